@@ -1,0 +1,252 @@
+"""CPU oracle for the per-decode-step token sampler -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the ``cpu_baseline`` leg of
+``bench.py`` may import this package.  The HIP library never loads it and
+shares no code with it: the arithmetic lives in ``sampler_oracle.c`` (plain
+scalar C, fp32 steps rounded one at a time, fp64 after the temperature
+division); this module only marshals numpy arrays through ctypes.
+
+What each part follows (page titles; the C file names the sections):
+  [A] "SGLang's +75% sampler speedup skips Qwen3 chat requests"
+  [B] the SGLang 101 operations manual ("Logprobs are temperature-scaled",
+      "What the flag switches")
+  [C] "采样参数对解码开销的影响：temperature、top_p 与采样核路径"
+
+Parity unpinned: the penalty formula (the pages name the three penalties and
+their defaults but print no formula); only its identity at the defaults,
+its locality and a hand-worked example are pinned.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "sampler_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_sampler_oracle.so")
+_lock = threading.Lock()
+_lib = None
+
+TOP_K_ALL = 1 << 30
+PATH_GREEDY, PATH_GUMBEL, PATH_FILTERED, PATH_DETERMINISTIC = 0, 1, 2, 3
+PATH_NAMES = {0: "greedy", 1: "gumbel", 2: "filtered", 3: "deterministic"}
+FLAG_GUMBEL_NEAR_TIE, FLAG_TOPP_MARGIN, FLAG_MINP_MARGIN, FLAG_SPELLING_MISMATCH = 1, 2, 4, 8
+
+GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11", "-pthread"]
+
+
+def build(force: bool = False) -> str:
+    """Compile the oracle with gcc (scalar, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+        tmp = _LIB_PATH + f".tmp{os.getpid()}"
+        subprocess.check_call(["gcc", *GCC_FLAGS, _SRC, "-o", tmp, "-lm"])
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+class _Args(ctypes.Structure):
+    _fields_ = [
+        ("logits", ctypes.c_void_p),
+        ("dtype", ctypes.c_int32),
+        ("n_rows", ctypes.c_int32),
+        ("vocab", ctypes.c_int32),
+        ("row_stride", ctypes.c_int64),
+        ("temperature", ctypes.c_void_p),
+        ("top_p", ctypes.c_void_p),
+        ("min_p", ctypes.c_void_p),
+        ("repetition_penalty", ctypes.c_void_p),
+        ("presence_penalty", ctypes.c_void_p),
+        ("frequency_penalty", ctypes.c_void_p),
+        ("top_k", ctypes.c_void_p),
+        ("history_ids", ctypes.c_void_p),
+        ("history_start", ctypes.c_void_p),
+        ("history_len", ctypes.c_void_p),
+        ("seed", ctypes.c_uint64),
+        ("offset", ctypes.c_uint64),
+        ("row_seed", ctypes.c_void_p),
+        ("row_offset", ctypes.c_void_p),
+        ("row_stream", ctypes.c_void_p),
+        ("deterministic", ctypes.c_int32),
+        ("n_threads", ctypes.c_int32),
+        ("token_ids", ctypes.c_void_p),
+        ("probs", ctypes.c_void_p),
+        ("logprobs", ctypes.c_void_p),
+        ("top_logprobs", ctypes.c_int32),
+        ("top_logprob_vals", ctypes.c_void_p),
+        ("top_logprob_ids", ctypes.c_void_p),
+        ("row_status", ctypes.c_void_p),
+        ("diag_flags", ctypes.c_void_p),
+        ("diag_gumbel_gap", ctypes.c_void_p),
+        ("diag_topp_margin", ctypes.c_void_p),
+        ("diag_kept", ctypes.c_void_p),
+    ]
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            path = build()
+            L = ctypes.CDLL(path)
+            L.orc_step.argtypes = [ctypes.POINTER(_Args)]
+            L.orc_step.restype = ctypes.c_int
+            L.orc_philox4x32_10.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+            L.orc_philox4x32_10.restype = None
+            L.orc_draw_word.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64]
+            L.orc_draw_word.restype = ctypes.c_uint32
+            L.orc_exp1_from_word.argtypes = [ctypes.c_uint32]
+            L.orc_exp1_from_word.restype = ctypes.c_double
+            L.orc_fill_exp1.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
+                                        ctypes.c_void_p]
+            L.orc_fill_exp1.restype = None
+            L.orc_select_path.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 4 + [ctypes.c_int32, ctypes.c_void_p]
+            L.orc_select_path.restype = ctypes.c_int
+            L.orc_do_penalties.argtypes = [ctypes.c_int32] + [ctypes.c_void_p] * 3
+            L.orc_do_penalties.restype = ctypes.c_int
+            L.orc_row_is_greedy.argtypes = [ctypes.c_float]
+            L.orc_row_is_greedy.restype = ctypes.c_int
+            L.orc_normalized_top_k.argtypes = [ctypes.c_float, ctypes.c_int32]
+            L.orc_normalized_top_k.restype = ctypes.c_int32
+            _lib = L
+    return _lib
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _arr(a, dtype, n=None):
+    if a is None:
+        return None
+    out = np.ascontiguousarray(np.asarray(a, dtype=dtype))
+    if n is not None and out.shape != (n,):
+        raise ValueError(f"expected shape ({n},), got {out.shape}")
+    return out
+
+
+def philox4x32_10(counter, key):
+    """Four 32-bit words of Philox4x32-10 for a 4-word counter and 2-word key."""
+    c = np.ascontiguousarray(np.asarray(counter, dtype=np.uint32).reshape(4))
+    k = np.ascontiguousarray(np.asarray(key, dtype=np.uint32).reshape(2))
+    out = np.zeros(4, dtype=np.uint32)
+    lib().orc_philox4x32_10(c.ctypes.data, k.ctypes.data, out.ctypes.data)
+    return out
+
+
+def draw_word(seed: int, stream: int, offset: int, index: int) -> int:
+    return int(lib().orc_draw_word(seed, stream, offset, index))
+
+
+def exp1_from_word(x: int) -> float:
+    return float(lib().orc_exp1_from_word(x))
+
+
+def exp1_draws(seed: int, stream: int, offset: int, n: int) -> np.ndarray:
+    """Exp(1) variates the oracle uses for vocabulary entries 0..n-1 of a row."""
+    out = np.empty(n, dtype=np.float64)
+    lib().orc_fill_exp1(seed, stream, offset, n, out.ctypes.data)
+    return out
+
+
+def select_path(temperature, top_k=None, top_p=None, min_p=None, deterministic=False):
+    """Batch predicate; returns a path name, raises ValueError on an empty batch."""
+    t = _arr(temperature, np.float32)
+    n = 0 if t is None else t.shape[0]
+    k = _arr(top_k, np.int32, n)
+    p = _arr(top_p, np.float32, n)
+    mp = _arr(min_p, np.float32, n)
+    out = ctypes.c_int32(-1)
+    rc = lib().orc_select_path(n, _ptr(t), _ptr(k), _ptr(p), _ptr(mp), int(deterministic), ctypes.addressof(out))
+    if rc != 0:
+        raise ValueError("a batch needs at least one row")
+    return PATH_NAMES[out.value]
+
+
+def do_penalties(repetition=None, presence=None, frequency=None, n=None):
+    arrs = [_arr(x, np.float32) for x in (repetition, presence, frequency)]
+    if n is None:
+        n = next((a.shape[0] for a in arrs if a is not None), 0)
+    return bool(lib().orc_do_penalties(n, *[_ptr(a) for a in arrs]))
+
+
+def normalized_top_k(temperature: float, top_k: int) -> int:
+    return int(lib().orc_normalized_top_k(temperature, top_k))
+
+
+def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k=None, min_p=None,
+         repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
+         history_ids=None, history_start=None, history_len=None,
+         seed=0, offset=0, row_seed=None, row_offset=None, row_stream=None, deterministic=False,
+         want_probs=True, want_logprobs=True, top_logprobs=0, n_threads=1):
+    """Run the oracle on host arrays.
+
+    ``logits`` is a 2-D array: float32, or uint16 holding bf16 bits when
+    ``dtype == "bf16"``; its row stride is its second dimension unless
+    ``vocab`` is smaller.  Returns a dict of numpy outputs and diagnostics.
+    """
+    if dtype not in ("f32", "bf16"):
+        raise ValueError("dtype must be 'f32' or 'bf16'")
+    L = np.ascontiguousarray(logits, dtype=np.uint16 if dtype == "bf16" else np.float32)
+    if L.ndim != 2:
+        raise ValueError("logits must be 2-D")
+    n, stride = L.shape
+    V = stride if vocab is None else int(vocab)
+    T = _arr(temperature, np.float32, n)
+    P = _arr(top_p, np.float32, n)
+    K = _arr(top_k, np.int32, n)
+    MP = _arr(min_p, np.float32, n)
+    RP = _arr(repetition_penalty, np.float32, n)
+    PP = _arr(presence_penalty, np.float32, n)
+    FP = _arr(frequency_penalty, np.float32, n)
+    H = _arr(history_ids, np.int32)
+    HS = _arr(history_start, np.int64, n)
+    HL = _arr(history_len, np.int32, n)
+    RS = _arr(row_seed, np.uint64, n)
+    RO = _arr(row_offset, np.uint64, n)
+    RST = _arr(row_stream, np.uint32, n)
+    out = {
+        "token_ids": np.full(n, -7, dtype=np.int32),
+        "probs": np.zeros((n, V), dtype=np.float32) if want_probs else None,
+        "logprobs": np.zeros((n, V), dtype=np.float32) if want_logprobs else None,
+        "top_logprob_vals": np.zeros((n, top_logprobs), dtype=np.float32) if top_logprobs else None,
+        "top_logprob_ids": np.zeros((n, top_logprobs), dtype=np.int32) if top_logprobs else None,
+        "row_status": np.zeros(n, dtype=np.int32),
+        "flags": np.zeros(n, dtype=np.int32),
+        "gumbel_gap": np.zeros(n, dtype=np.float64),
+        "topp_margin": np.zeros(n, dtype=np.float64),
+        "kept": np.zeros(n, dtype=np.int32),
+    }
+    a = _Args()
+    a.logits = L.ctypes.data
+    a.dtype = 1 if dtype == "bf16" else 0
+    a.n_rows, a.vocab, a.row_stride = n, V, stride
+    a.temperature, a.top_p, a.min_p = _ptr(T), _ptr(P), _ptr(MP)
+    a.repetition_penalty, a.presence_penalty, a.frequency_penalty = _ptr(RP), _ptr(PP), _ptr(FP)
+    a.top_k = _ptr(K)
+    a.history_ids, a.history_start, a.history_len = _ptr(H), _ptr(HS), _ptr(HL)
+    a.seed, a.offset = int(seed) & (2**64 - 1), int(offset) & (2**64 - 1)
+    a.row_seed, a.row_offset, a.row_stream = _ptr(RS), _ptr(RO), _ptr(RST)
+    a.deterministic = int(bool(deterministic))
+    a.n_threads = int(n_threads)
+    a.token_ids = out["token_ids"].ctypes.data
+    a.probs = _ptr(out["probs"])
+    a.logprobs = _ptr(out["logprobs"])
+    a.top_logprobs = int(top_logprobs)
+    a.top_logprob_vals = _ptr(out["top_logprob_vals"])
+    a.top_logprob_ids = _ptr(out["top_logprob_ids"])
+    a.row_status = out["row_status"].ctypes.data
+    a.diag_flags = out["flags"].ctypes.data
+    a.diag_gumbel_gap = out["gumbel_gap"].ctypes.data
+    a.diag_topp_margin = out["topp_margin"].ctypes.data
+    a.diag_kept = out["kept"].ctypes.data
+    if HS is not None and H is not None and HL is not None:
+        if np.any(HS < 0) or np.any(HS + HL > H.shape[0]):
+            raise ValueError("history span outside the id buffer")
+    rc = lib().orc_step(ctypes.byref(a))
+    if rc != 0:
+        raise RuntimeError(f"oracle step failed ({rc})")
+    return out

@@ -1,0 +1,522 @@
+/*
+ * sampler_oracle.c -- plain, slow CPU oracle for the per-decode-step token
+ * sampler.  TEST INFRASTRUCTURE ONLY: it exists to check the HIP library
+ * against a transparent implementation.  Only tests, the smoke check and the
+ * CPU-baseline leg of the benchmark may load it; the product never does.
+ *
+ * It shares no code, header, table or constant generator with the HIP
+ * library.  Build: gcc -O2 -ffp-contract=off -fno-fast-math -shared -fPIC
+ * (scalar code; fp32 steps are rounded one operation at a time, everything
+ * after the temperature division is fp64).
+ *
+ * Sources (the pages this follows; each function cites the passage):
+ *   [A] "SGLang's +75% sampler speedup skips Qwen3 chat requests" (dev.to)
+ *   [B] the SGLang 101 operations manual (aiengineeringfromscratch.com),
+ *       sections "Logprobs are temperature-scaled" and "What the flag switches"
+ *   [C] "采样参数对解码开销的影响：temperature、top_p 与采样核路径"
+ *       (xbrilliance.ai note on sampling-parameter decode cost)
+ *   Philox4x32-10: Salmon, Moraes, Dror, Shaw, "Parallel random numbers:
+ *       as easy as 1, 2, 3", SC'11.
+ *
+ * Readings where the pages are silent (each is listed with its reason in the
+ * design notes of the repository):
+ *   - penalties: repetition (divide positive / multiply non-positive logits),
+ *     then frequency (minus f*count), then presence (minus p), only where the
+ *     token occurs in the row's history; each op rounded to fp32.
+ *   - truncation order top-k -> top-p (on the top-k renormalised mass) ->
+ *     min-p (relative to the row maximum); thresholds keep ties.
+ *   - probs/logprobs are those of the distribution sampled from (after
+ *     truncation); greedy rows are untruncated at temperature 1.
+ *   - Gumbel-max over the kept set with Philox4x32-10 draws, counter
+ *     (i>>2, stream, off_lo, off_hi), key (seed_lo, seed_hi), word i&3.
+ *   - top-k logprobs list the K largest kept values by (z desc, index asc);
+ *     entries with z = -inf are never listed; padding is (-inf, -1).
+ *
+ * Parity pins: see tests/test_oracle_*.py.  The penalty formula itself is
+ * not fixed by the pages ("parity unpinned" for that formula; only its
+ * identity at the defaults and its locality are pinned).
+ */
+#include <float.h>
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORC_TOP_K_ALL (1 << 30)   /* [A] "One request with top_p ..." : -1 becomes 1<<30 */
+#define ORC_GREEDY_EPS 1e-6       /* [A] same section: temperature below 1e-6 is greedy */
+#define ORC_NEAR_TIE 1e-6         /* relative gap under which a Gumbel row is flagged */
+#define ORC_TOPP_MARGIN 1e-6      /* relative top-p margin under which a row is flagged */
+#define ORC_MINP_MARGIN 1e-9      /* relative min-p boundary margin (flag) */
+
+/* path codes */
+#define ORC_PATH_GREEDY 0
+#define ORC_PATH_GUMBEL 1
+#define ORC_PATH_FILTERED 2
+#define ORC_PATH_DETERMINISTIC 3
+
+/* per-row diagnostic flags */
+#define ORC_FLAG_GUMBEL_NEAR_TIE 1
+#define ORC_FLAG_TOPP_MARGIN 2
+#define ORC_FLAG_MINP_MARGIN 4
+#define ORC_FLAG_SPELLING_MISMATCH 8
+
+typedef struct {
+  const void *logits;       /* [n_rows, row_stride] fp32 or bf16 bits (host) */
+  int32_t dtype;            /* 0 = fp32, 1 = bf16 */
+  int32_t n_rows;
+  int32_t vocab;
+  int64_t row_stride;       /* elements */
+  const float *temperature; /* each array: n_rows entries, NULL = default */
+  const float *top_p;
+  const float *min_p;
+  const float *repetition_penalty;
+  const float *presence_penalty;
+  const float *frequency_penalty;
+  const int32_t *top_k;
+  const int32_t *history_ids;   /* host copy of the id buffer */
+  const int64_t *history_start; /* per row */
+  const int32_t *history_len;   /* per row */
+  uint64_t seed;
+  uint64_t offset;
+  const uint64_t *row_seed;
+  const uint64_t *row_offset;
+  const uint32_t *row_stream;
+  int32_t deterministic;
+  int32_t n_threads;
+  /* outputs (host) */
+  int32_t *token_ids;
+  float *probs;             /* [n_rows, vocab] or NULL */
+  float *logprobs;          /* [n_rows, vocab] or NULL */
+  int32_t top_logprobs;
+  float *top_logprob_vals;  /* [n_rows, top_logprobs] */
+  int32_t *top_logprob_ids;
+  int32_t *row_status;
+  /* diagnostics, each [n_rows] or NULL */
+  int32_t *diag_flags;
+  double *diag_gumbel_gap;  /* (s1 - s2) / s1 of the Gumbel scores */
+  double *diag_topp_margin; /* relative distance of the top-p crossing */
+  int32_t *diag_kept;       /* |K| */
+} orc_args;
+
+/* ------------------------------------------------------------------ */
+/* Philox4x32-10 (Salmon et al., SC'11): ten rounds of the multiply /  */
+/* xor round function; the key is bumped by the Weyl constants between */
+/* rounds.                                                             */
+/* ------------------------------------------------------------------ */
+void orc_philox4x32_10(const uint32_t ctr_in[4], const uint32_t key_in[2], uint32_t out[4]) {
+  const uint32_t MUL_A = 0xD2511F53u, MUL_B = 0xCD9E8D57u;
+  const uint32_t WEYL_A = 0x9E3779B9u, WEYL_B = 0xBB67AE85u;
+  uint32_t c0 = ctr_in[0], c1 = ctr_in[1], c2 = ctr_in[2], c3 = ctr_in[3];
+  uint32_t k0 = key_in[0], k1 = key_in[1];
+  for (int round = 0; round < 10; ++round) {
+    if (round > 0) {
+      k0 += WEYL_A;
+      k1 += WEYL_B;
+    }
+    uint64_t prod_a = (uint64_t)MUL_A * (uint64_t)c0;
+    uint64_t prod_b = (uint64_t)MUL_B * (uint64_t)c2;
+    uint32_t n0 = (uint32_t)(prod_b >> 32) ^ c1 ^ k0;
+    uint32_t n1 = (uint32_t)prod_b;
+    uint32_t n2 = (uint32_t)(prod_a >> 32) ^ c3 ^ k1;
+    uint32_t n3 = (uint32_t)prod_a;
+    c0 = n0; c1 = n1; c2 = n2; c3 = n3;
+  }
+  out[0] = c0; out[1] = c1; out[2] = c2; out[3] = c3;
+}
+
+/* The 32-bit word that vocabulary entry `i` of a row draws. */
+uint32_t orc_draw_word(uint64_t seed, uint32_t stream, uint64_t offset, int64_t i) {
+  uint32_t ctr[4] = {(uint32_t)((uint64_t)i >> 2), stream, (uint32_t)offset, (uint32_t)(offset >> 32)};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  return out[i & 3];
+}
+
+/* Exp(1) variate from one 32-bit word, as [A] "Nine lines..." draws it with
+ * exponential_(1.0) followed by a clamp at the smallest normal float:
+ * w = (x + 1/2) 2^-32 is uniform on (0,1); E = -ln(1 - w). */
+double orc_exp1_from_word(uint32_t x) {
+  double w = ((double)x + 0.5) * 0x1p-32;
+  double e = -log1p(-w);
+  if (e < (double)FLT_MIN) e = (double)FLT_MIN;
+  return e;
+}
+
+/* Exp(1) variates of vocabulary entries 0..n-1 of one row (test helper). */
+void orc_fill_exp1(uint64_t seed, uint32_t stream, uint64_t offset, int64_t n, double *out) {
+  for (int64_t i = 0; i < n; ++i) out[i] = orc_exp1_from_word(orc_draw_word(seed, stream, offset, i));
+}
+
+/* bf16 -> fp32: the bf16 bits are the high half of the fp32 bits. */
+static float orc_bf16_to_f32(uint16_t b) {
+  uint32_t u = (uint32_t)b << 16;
+  float f;
+  memcpy(&f, &u, 4);
+  return f;
+}
+
+/* ------------------------------------------------------------------ */
+/* Normalisation and the batch predicate: [A] "One request with top_p  */
+/* takes the whole batch off the fast path" (normalize and              */
+/* path_for_batch, and the four-row path table).                        */
+/* ------------------------------------------------------------------ */
+int orc_row_is_greedy(float temperature) {
+  return temperature >= 0.0f && (double)temperature < ORC_GREEDY_EPS;
+}
+
+int32_t orc_normalized_top_k(float temperature, int32_t top_k) {
+  if (orc_row_is_greedy(temperature)) return 1;
+  if (top_k == -1) return ORC_TOP_K_ALL;
+  return top_k;
+}
+
+/* Returns 0 and writes the path, or -1 for an empty batch. */
+int orc_select_path(int32_t n, const float *temperature, const int32_t *top_k, const float *top_p,
+                    const float *min_p, int32_t deterministic, int32_t *path_out) {
+  if (n <= 0) return -1;
+  int all_greedy = 1, need_top_p = 0, need_top_k = 0, need_min_p = 0;
+  for (int32_t r = 0; r < n; ++r) {
+    float t = temperature ? temperature[r] : 1.0f;
+    int32_t k = orc_normalized_top_k(t, top_k ? top_k[r] : -1);
+    float p = top_p ? top_p[r] : 1.0f;
+    float mp = min_p ? min_p[r] : 0.0f;
+    if (!(k <= 1)) all_greedy = 0;
+    if (p != 1.0f) need_top_p = 1;
+    if (k != ORC_TOP_K_ALL) need_top_k = 1;
+    if (mp > 0.0f) need_min_p = 1;
+  }
+  if (all_greedy) *path_out = ORC_PATH_GREEDY;
+  else if (!(need_top_p || need_top_k || need_min_p))
+    *path_out = deterministic ? ORC_PATH_DETERMINISTIC : ORC_PATH_GUMBEL;
+  else
+    *path_out = ORC_PATH_FILTERED;
+  return 0;
+}
+
+/* [C] "哪些参数会额外打开一趟全词表计算": do_penalties is raised by any row
+ * whose presence, frequency or repetition penalty differs from its default
+ * (compared exactly here). */
+int orc_do_penalties(int32_t n, const float *rep, const float *pres, const float *freq) {
+  for (int32_t r = 0; r < n; ++r) {
+    if ((rep && rep[r] != 1.0f) || (pres && pres[r] != 0.0f) || (freq && freq[r] != 0.0f)) return 1;
+  }
+  return 0;
+}
+
+/* ------------------------------------------------------------------ */
+/* One row.                                                            */
+/* ------------------------------------------------------------------ */
+typedef struct {
+  float z;
+  int32_t idx;
+} orc_zi;
+
+static int orc_cmp_desc(const void *pa, const void *pb) {
+  const orc_zi *a = (const orc_zi *)pa, *b = (const orc_zi *)pb;
+  if (a->z > b->z) return -1;
+  if (a->z < b->z) return 1;
+  return (a->idx < b->idx) ? -1 : (a->idx > b->idx);
+}
+
+/* Neumaier-compensated sum (accuracy of the normaliser; order is index). */
+typedef struct {
+  double s, c;
+} orc_ksum;
+static void orc_kadd(orc_ksum *k, double v) {
+  double t = k->s + v;
+  if (fabs(k->s) >= fabs(v)) k->c += (k->s - t) + v;
+  else k->c += (v - t) + k->s;
+  k->s = t;
+}
+static double orc_kval(const orc_ksum *k) { return k->s + k->c; }
+
+static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double *q, int32_t *cnt,
+                    unsigned char *kept) {
+  const int32_t V = a->vocab;
+  float T = a->temperature ? a->temperature[r] : 1.0f;
+  const int greedy = orc_row_is_greedy(T);
+  const float T_eff = greedy ? 1.0f : T;
+  const int32_t k_eff = orc_normalized_top_k(T, a->top_k ? a->top_k[r] : -1);
+  const float top_p = a->top_p ? a->top_p[r] : 1.0f;
+  const float min_p = a->min_p ? a->min_p[r] : 0.0f;
+  const float rep = a->repetition_penalty ? a->repetition_penalty[r] : 1.0f;
+  const float pres = a->presence_penalty ? a->presence_penalty[r] : 0.0f;
+  const float freq = a->frequency_penalty ? a->frequency_penalty[r] : 0.0f;
+  int32_t flags = 0;
+  double gumbel_gap = INFINITY, topp_margin = INFINITY;
+
+  /* 1. load; NaN becomes -inf ([B] "On Apple silicon" lists NaN
+   *    sanitisation among the sampler options; here it is always on). */
+  for (int32_t i = 0; i < V; ++i) {
+    float x;
+    if (a->dtype == 1) x = orc_bf16_to_f32(((const uint16_t *)a->logits)[(int64_t)r * a->row_stride + i]);
+    else x = ((const float *)a->logits)[(int64_t)r * a->row_stride + i];
+    if (isnan(x)) x = -INFINITY;
+    z[i] = x;
+  }
+
+  /* 2. penalties ([C] "解码一步里采样做什么", step _apply_penalties):
+   *    counts of each token in the row's history, then the three penalties
+   *    on the tokens that occur.  Ids outside [0, V) are ignored. */
+  if (a->history_len && a->history_len[r] > 0 && a->history_ids && a->history_start) {
+    memset(cnt, 0, sizeof(int32_t) * (size_t)V);
+    const int32_t *h = a->history_ids + a->history_start[r];
+    for (int32_t j = 0; j < a->history_len[r]; ++j) {
+      int32_t id = h[j];
+      if (id >= 0 && id < V) cnt[id] += 1;
+    }
+    for (int32_t i = 0; i < V; ++i) {
+      if (cnt[i] > 0) {
+        float x = z[i];
+        float t1 = (x > 0.0f) ? (x / rep) : (x * rep);
+        float fc = freq * (float)cnt[i];
+        float t2 = t1 - fc;
+        float t3 = t2 - pres;
+        z[i] = t3;
+      }
+    }
+  }
+
+  /* 3. temperature ([C] same section: logits.div_(temperatures)) */
+  for (int32_t i = 0; i < V; ++i) z[i] = z[i] / T_eff;
+
+  /* 4. row maximum */
+  float m = -INFINITY;
+  for (int32_t i = 0; i < V; ++i)
+    if (z[i] > m) m = z[i];
+
+  const int want_topk_out = a->top_logprobs > 0 && a->top_logprob_vals && a->top_logprob_ids;
+  if (!(m > -INFINITY) || m == INFINITY) {
+    if (a->row_status) a->row_status[r] = (m == INFINITY) ? 2 : 1;
+    a->token_ids[r] = -1;
+    for (int32_t i = 0; i < V; ++i) {
+      if (a->probs) a->probs[(int64_t)r * V + i] = 0.0f;
+      if (a->logprobs) a->logprobs[(int64_t)r * V + i] = -INFINITY;
+    }
+    if (want_topk_out)
+      for (int32_t j = 0; j < a->top_logprobs; ++j) {
+        a->top_logprob_vals[(int64_t)r * a->top_logprobs + j] = -INFINITY;
+        a->top_logprob_ids[(int64_t)r * a->top_logprobs + j] = -1;
+      }
+    if (a->diag_flags) a->diag_flags[r] = 0;
+    if (a->diag_gumbel_gap) a->diag_gumbel_gap[r] = INFINITY;
+    if (a->diag_topp_margin) a->diag_topp_margin[r] = INFINITY;
+    if (a->diag_kept) a->diag_kept[r] = 0;
+    return;
+  }
+  if (a->row_status) a->row_status[r] = 0;
+
+  const double dm = (double)m;
+  for (int32_t i = 0; i < V; ++i) q[i] = exp((double)z[i] - dm);
+
+  /* 5. truncation ([C] same section: _apply_top_k_top_p then _apply_min_p).
+   *    Greedy rows keep every token (distribution at temperature 1). */
+  for (int32_t i = 0; i < V; ++i) kept[i] = 1;
+  if (!greedy) {
+    for (int32_t i = 0; i < V; ++i) {
+      ord[i].z = z[i];
+      ord[i].idx = i;
+    }
+    qsort(ord, (size_t)V, sizeof(orc_zi), orc_cmp_desc);
+
+    /* top-k: keep every token whose value is >= the k-th largest value */
+    int32_t n_k = V;
+    if (k_eff < V) {
+      float t_k = ord[k_eff - 1].z;
+      n_k = k_eff;
+      while (n_k < V && ord[n_k].z == t_k) ++n_k;
+    }
+    /* top-p over the top-k set: smallest tie-closed prefix (by value) whose
+     * mass reaches top_p times the top-k mass. */
+    int32_t n_p = n_k;
+    if (top_p < 1.0f) {
+      double c_tot = 0.0;
+      for (int32_t j = 0; j < n_k; ++j) c_tot += q[ord[j].idx];
+      const double target = (double)top_p * c_tot;
+      double c = 0.0, c_prev = -1.0;
+      int32_t j = 0;
+      while (j < n_k) {
+        int32_t j2 = j;
+        const float v = ord[j].z;
+        double c_new = c;
+        while (j2 < n_k && ord[j2].z == v) c_new += q[ord[j2++].idx];
+        if (c_new >= target) {
+          n_p = j2;
+          double lo = (c_new - target) / c_tot;
+          double hi = (c_prev >= 0.0) ? (target - c) / c_tot : INFINITY;
+          topp_margin = lo < hi ? lo : hi;
+          break;
+        }
+        c_prev = c;
+        c = c_new;
+        j = j2;
+      }
+      if (topp_margin < ORC_TOPP_MARGIN) flags |= ORC_FLAG_TOPP_MARGIN;
+    }
+    /* kept by top-k/top-p: the first n_p entries of the order */
+    for (int32_t i = 0; i < V; ++i) kept[i] = 0;
+    for (int32_t j = 0; j < n_p; ++j) kept[ord[j].idx] = 1;
+    /* min-p: keep tokens whose probability is at least min_p times the
+     * largest probability, i.e. exp(z - m) >= min_p. */
+    if (min_p > 0.0f) {
+      for (int32_t i = 0; i < V; ++i) {
+        if (!(q[i] >= (double)min_p)) kept[i] = 0;
+        if (q[i] > 0.0 && fabs(q[i] / (double)min_p - 1.0) < ORC_MINP_MARGIN) flags |= ORC_FLAG_MINP_MARGIN;
+      }
+    }
+  }
+
+  /* 6. normaliser over the kept set, probs and logprobs
+   *    ([C] softmax/log_softmax in fp32 of the processed logits). */
+  orc_ksum ks = {0.0, 0.0};
+  int32_t n_kept = 0;
+  for (int32_t i = 0; i < V; ++i)
+    if (kept[i]) {
+      orc_kadd(&ks, q[i]);
+      ++n_kept;
+    }
+  const double S = orc_kval(&ks);
+  const double lnS = log(S);
+  for (int32_t i = 0; i < V; ++i) {
+    if (a->probs) a->probs[(int64_t)r * V + i] = kept[i] ? (float)(q[i] / S) : 0.0f;
+    if (a->logprobs)
+      a->logprobs[(int64_t)r * V + i] = kept[i] ? (float)(((double)z[i] - dm) - lnS) : -INFINITY;
+  }
+
+  /* 7. token selection.  Rows with top_k = 1 (greedy rows included) take
+   *    the first index of the maximum ([C] "采样类型与选路": argmax); the
+   *    others draw by Gumbel-max over the kept set ([A] "Nine lines, and
+   *    exactly one call site": probs divided by Exp(1) draws, then argmax). */
+  int32_t token = -1;
+  if (k_eff == 1) {
+    for (int32_t i = 0; i < V; ++i)
+      if (z[i] == m) {
+        token = i;
+        break;
+      }
+  } else {
+    uint64_t seed = a->row_seed ? a->row_seed[r] : (a->deterministic ? 42u : a->seed);
+    uint32_t stream = a->row_stream ? a->row_stream[r] : (a->deterministic ? 0u : (uint32_t)r);
+    uint64_t off = a->row_offset ? a->row_offset[r] : a->offset;
+    double s1 = -1.0, s2 = -1.0;
+    double g_best = -INFINITY;
+    int32_t tok_g = -1;
+    for (int32_t i = 0; i < V; ++i) {
+      if (!kept[i]) continue;
+      double E = orc_exp1_from_word(orc_draw_word(seed, stream, off, i));
+      double s = (q[i] / S) / E;
+      if (s > s1) {
+        s2 = s1;
+        s1 = s;
+        token = i;
+      } else if (s > s2) {
+        s2 = s;
+      }
+      /* second spelling (log domain), for the self-check */
+      double g = (((double)z[i] - dm) - lnS) - log(E);
+      if (g > g_best) {
+        g_best = g;
+        tok_g = i;
+      }
+    }
+    gumbel_gap = (s2 >= 0.0 && s1 > 0.0) ? (s1 - s2) / s1 : INFINITY;
+    if (gumbel_gap < ORC_NEAR_TIE) flags |= ORC_FLAG_GUMBEL_NEAR_TIE;
+    else if (tok_g != token) flags |= ORC_FLAG_SPELLING_MISMATCH;
+  }
+  a->token_ids[r] = token;
+
+  /* 8. top logprobs: the largest kept values by (z desc, index asc) */
+  if (want_topk_out) {
+    const int32_t K = a->top_logprobs;
+    int32_t nfill = 0;
+    /* simple selection by repeated scans (K is small) */
+    float last_z = INFINITY;
+    int32_t last_i = -1;
+    for (; nfill < K; ++nfill) {
+      int32_t best = -1;
+      for (int32_t i = 0; i < V; ++i) {
+        if (!kept[i] || z[i] == -INFINITY) continue;
+        /* strictly after (last_z, last_i) in the (z desc, idx asc) order */
+        if (z[i] > last_z || (z[i] == last_z && i <= last_i)) continue;
+        if (best < 0 || z[i] > z[best]) best = i; /* index ascending keeps the first */
+      }
+      if (best < 0) break;
+      a->top_logprob_vals[(int64_t)r * K + nfill] = (float)(((double)z[best] - dm) - lnS);
+      a->top_logprob_ids[(int64_t)r * K + nfill] = best;
+      last_z = z[best];
+      last_i = best;
+    }
+    for (; nfill < K; ++nfill) {
+      a->top_logprob_vals[(int64_t)r * K + nfill] = -INFINITY;
+      a->top_logprob_ids[(int64_t)r * K + nfill] = -1;
+    }
+  }
+
+  if (a->diag_flags) a->diag_flags[r] = flags;
+  if (a->diag_gumbel_gap) a->diag_gumbel_gap[r] = gumbel_gap;
+  if (a->diag_topp_margin) a->diag_topp_margin[r] = topp_margin;
+  if (a->diag_kept) a->diag_kept[r] = n_kept;
+}
+
+typedef struct {
+  const orc_args *a;
+  int32_t r0, r1;
+  int status;
+} orc_job;
+
+static void *orc_worker(void *p) {
+  orc_job *job = (orc_job *)p;
+  const int32_t V = job->a->vocab;
+  float *z = (float *)malloc(sizeof(float) * (size_t)V);
+  orc_zi *ord = (orc_zi *)malloc(sizeof(orc_zi) * (size_t)V);
+  double *q = (double *)malloc(sizeof(double) * (size_t)V);
+  int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)V);
+  unsigned char *kept = (unsigned char *)malloc((size_t)V);
+  if (!z || !ord || !q || !cnt || !kept) {
+    job->status = -2;
+  } else {
+    for (int32_t r = job->r0; r < job->r1; ++r) orc_row(job->a, r, z, ord, q, cnt, kept);
+    job->status = 0;
+  }
+  free(z);
+  free(ord);
+  free(q);
+  free(cnt);
+  free(kept);
+  return NULL;
+}
+
+/* Runs every row; returns 0, -1 for invalid sizes, -2 for allocation failure. */
+int orc_step(const orc_args *a) {
+  if (!a || a->n_rows <= 0 || a->vocab <= 0 || a->row_stride < a->vocab || !a->logits || !a->token_ids)
+    return -1;
+  int nt = a->n_threads > 0 ? a->n_threads : 1;
+  if (nt > a->n_rows) nt = a->n_rows;
+  if (nt > 256) nt = 256;
+  orc_job jobs[256];
+  pthread_t th[256];
+  int32_t per = (a->n_rows + nt - 1) / nt;
+  int started = 0;
+  for (int t = 0; t < nt; ++t) {
+    jobs[t].a = a;
+    jobs[t].r0 = t * per;
+    jobs[t].r1 = (t + 1) * per < a->n_rows ? (t + 1) * per : a->n_rows;
+    jobs[t].status = 0;
+    if (jobs[t].r0 >= jobs[t].r1) continue;
+    if (nt == 1) {
+      orc_worker(&jobs[t]);
+    } else {
+      pthread_create(&th[t], NULL, orc_worker, &jobs[t]);
+      ++started;
+    }
+  }
+  int rc = 0;
+  for (int t = 0; t < nt; ++t) {
+    if (jobs[t].r0 >= jobs[t].r1) continue;
+    if (nt > 1) pthread_join(th[t], NULL);
+    if (jobs[t].status != 0) rc = jobs[t].status;
+  }
+  return rc;
+}
