@@ -1,0 +1,118 @@
+// sampler_internal.h -- records shared by the host runtime and the HIP
+// kernels of the decode-step sampler (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsts {
+
+// [A] "One request with top_p takes the whole batch off the fast path":
+// top_k = -1 (whole vocabulary) is carried as 1 << 30.
+constexpr int32_t kTopKAll = 1 << 30;
+// Largest number of workgroups that cooperate on one row.
+constexpr int kMaxG = 32;
+// Largest top-logprob list per row.
+constexpr int kMaxTopLogprobs = 32;
+// Largest history of one row.  Its counts live in an LDS hash table of
+// next_pow2(2 * max_history_per_row) slots, each packing a slice-local index
+// (15 bits) and a count (13 bits) into one word.
+constexpr int kMaxHistPerRow = 4096;
+constexpr int kMaxHashSlots = 8192;
+// Largest vocabulary (masses are summed as 2^-44 fixed point in 64 bits).
+constexpr int32_t kMaxVocab = 1 << 20;
+
+// Workgroup shape of the row kernel: 1024 threads (16 wave64s).  Each
+// workgroup keeps its slice of the processed logits in LDS; the slice is at
+// most 32768 values (the hash packs 15-bit slice-local indices) and is also
+// bounded by the LDS left after the fixed part and the hash table.
+constexpr int kBlock = 1024;
+constexpr int kMaxSlice = 32768;
+
+// Per-row flags, decided on the host from the row's parameters.
+enum : uint32_t {
+  RF_GREEDY = 1u << 0,  // greedy row: keep every token at T = 1; token = first argmax
+  RF_TOP1 = 1u << 1,    // top_k == 1 after normalisation: token = first argmax
+  RF_PEN = 1u << 2,     // a penalty differs from its default and the row has history
+  RF_TOPK = 1u << 3,    // 2 <= top_k < vocab
+  RF_TOPP = 1u << 4,    // top_p < 1
+  RF_MINP = 1u << 5,    // min_p > 0
+};
+
+// One row's parameters as the kernel reads them (64 bytes).
+struct alignas(16) RowParam {
+  float temperature;  // effective temperature (1 for greedy rows)
+  float top_p;
+  float min_p;
+  float rep;
+  float pres;
+  float freq;
+  int32_t top_k;      // meaningful with RF_TOPK
+  uint32_t flags;
+  uint64_t seed;
+  uint64_t offset;
+  int64_t hist_start;
+  int32_t hist_len;
+  uint32_t stream;
+};
+static_assert(sizeof(RowParam) == 64, "RowParam layout");
+
+// Barrier words of one row group, each on its own 128-byte line.
+struct alignas(128) GroupSync {
+  uint32_t count;
+  uint32_t pad0[31];
+  uint32_t gen;
+  uint32_t pad1[31];
+  uint32_t fin;
+  uint32_t pad2[31];
+};
+
+// Exchange slots owned by one workgroup (indexed by its block id), double
+// buffered by the parity of the exchange sequence.
+struct alignas(128) WgSlots {
+  double small[2][4];                             // (max, sum, argmax key) / kept-set sum
+  uint32_t hcnt[2][256];                          // radix-select counts
+  unsigned long long hmass[2][256];               // radix-select masses (2^-44 fixed point)
+  double fin[2][2];                               // best Gumbel score and its index
+  unsigned long long toplist[2][kMaxTopLogprobs]; // local top-logprob candidates
+};
+
+enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINISTIC = 3 };
+
+struct KernelParams {
+  const void *logits;
+  int64_t row_stride;
+  int32_t n_rows;
+  int32_t vocab;
+  const RowParam *rows;
+  const int32_t *history_ids;
+  int32_t *token_ids;
+  float *probs;
+  float *logprobs;
+  float *top_lp_vals;
+  int32_t *top_lp_ids;
+  int32_t *row_status;
+  int32_t top_lp;
+  int32_t G;          // workgroups per row
+  int32_t n_groups;   // row groups (rows are strided over groups)
+  int32_t slice;      // elements per workgroup slice (multiple of 4)
+  int32_t hash_slots; // LDS hash slots (power of two) when penalties are on
+  int32_t vec_ok;     // bit 0: logits rows aligned for vector loads; bit 1: outputs for vector stores
+  int32_t path;
+  GroupSync *sync;    // [n_groups]
+  WgSlots *slots;     // [n_groups * G]
+  uint32_t *abort_word;  // equals epoch once a barrier wait of this launch expired
+  uint32_t epoch;        // launch counter of the handle (never 0)
+};
+
+// Launch one step (cooperative: every workgroup of the grid is resident).
+hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, hipStream_t stream);
+// Workgroups of the row kernel that fit on the device at once for a given
+// dynamic LDS size.
+hipError_t resident_blocks(int device, size_t lds_bytes, int *out);
+// Fixed LDS bytes of one workgroup (reductions, histograms, bitmap).
+size_t kernel_lds_fixed();
+// Dynamic LDS bytes of one workgroup for a slice and hash size.
+size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties);
+
+}  // namespace dsts

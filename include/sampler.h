@@ -1,0 +1,196 @@
+/*
+ * sampler.h -- C ABI of the MI355X (gfx950) per-decode-step token sampler.
+ *
+ * One call samples one decode step for a batch of N rows over a V-entry
+ * vocabulary: penalties from each row's token history, temperature,
+ * top-k / top-p / min-p truncation, fp32 softmax and log_softmax of the
+ * distribution sampled from, and token selection by greedy argmax or by
+ * Gumbel-max (probabilities divided by Exp(1) draws, then argmax).  A batch
+ * predicate picks the greedy, Gumbel or filtered kernel.  Everything runs in
+ * HIP kernels on the caller's stream; nothing is read back to the host.
+ *
+ * Pages the behaviour follows (cited by title and section below):
+ *   [A] "SGLang's +75% sampler speedup skips Qwen3 chat requests"
+ *   [B] the SGLang 101 operations manual ("Logprobs are temperature-scaled",
+ *       "What the flag switches")
+ *   [C] "采样参数对解码开销的影响：temperature、top_p 与采样核路径"
+ *       (vLLM 0.5.0 sampling-parameter decode-cost note)
+ *
+ * Conventions for every entry point:
+ *   - No C++ exception crosses this ABI; errors are negative status codes
+ *     and a per-handle message (sampler_last_error).
+ *   - Pointers documented "device" must point to device memory of the
+ *     handle's GPU; "host" pointers are read before the call returns, so
+ *     the caller may reuse them immediately.
+ *   - The caller owns every buffer it passes.  The handle owns only its
+ *     device workspace and its pinned host staging ring.
+ *   - A handle serves one stream at a time and is not thread-safe.
+ */
+#ifndef DSTS_SAMPLER_H
+#define DSTS_SAMPLER_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum sampler_status {
+  SAMPLER_OK = 0,
+  SAMPLER_EINVAL = -1,    /* an argument breaks the contract below */
+  SAMPLER_ECAPACITY = -2, /* a size exceeds what the handle was created for */
+  SAMPLER_EHIP = -3,      /* a HIP runtime call failed (no device, launch error) */
+  SAMPLER_ENOTSUP = -4    /* a valid request this build does not support */
+} sampler_status;
+
+/* [A] "One request with top_p takes the whole batch off the fast path":
+ * the four outcomes of the batch predicate. */
+typedef enum sampler_path {
+  SAMPLER_PATH_GREEDY = 0,       /* every row greedy (top_k <= 1 after normalisation) */
+  SAMPLER_PATH_GUMBEL = 1,       /* no row truncates: Gumbel-max over the whole vocabulary */
+  SAMPLER_PATH_FILTERED = 2,     /* some row uses top_k, top_p or min_p */
+  SAMPLER_PATH_DETERMINISTIC = 3 /* as GUMBEL, on a handle created with SAMPLER_DETERMINISTIC */
+} sampler_path;
+
+typedef enum sampler_dtype {
+  SAMPLER_DTYPE_F32 = 0,
+  SAMPLER_DTYPE_BF16 = 1
+} sampler_dtype;
+
+/* sampler_config.flags */
+/* [B] "What the flag switches": deterministic inference.  Rows without a
+ * row_seed use seed 42 and (without row_stream) stream 0, so a row's draw
+ * depends only on its own parameters; each row's reduction order depends
+ * only on V, so a row gives bit-identical results at any batch position and
+ * batch size. */
+#define SAMPLER_DETERMINISTIC (1u << 0)
+/* Run the general (filtered) kernel whatever the predicate says.  The
+ * outputs are identical by construction; this is the A/B switch for the
+ * specialised kernels. */
+#define SAMPLER_FORCE_FILTERED (1u << 1)
+
+typedef struct sampler_config {
+  int32_t max_rows;            /* largest n_rows a step may pass (>= 1) */
+  int32_t max_vocab;           /* largest vocab (>= 1, <= 1,048,576) */
+  int32_t max_history_per_row; /* largest history_len of one row (0..4096) */
+  int32_t max_top_logprobs;    /* largest top_logprobs (0..32) */
+  int32_t device;              /* HIP device ordinal */
+  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED */
+} sampler_config;
+
+typedef struct sampler_handle sampler_handle;
+
+typedef struct sampler_step_args {
+  /* Logits: device, [n_rows, row_stride] elements of `dtype`, row-major.
+   * Never written.  row_stride >= vocab. */
+  const void *logits;
+  int32_t dtype;               /* sampler_dtype */
+  int32_t n_rows;              /* 1 .. max_rows; 0 is an error ([A]: an empty batch has no path) */
+  int32_t vocab;               /* 1 .. max_vocab */
+  int64_t row_stride;          /* in elements */
+
+  /* Per-row sampling parameters: host arrays of n_rows entries.  NULL means
+   * the default for every row, as in [C] "哪些参数会额外打开一趟全词表计算":
+   * temperature 1, top_p 1, top_k -1, min_p 0, repetition 1, presence 0,
+   * frequency 0.
+   *   temperature >= 0 (0 <= T < 1e-6 is a greedy row: T := 1, top_k := 1,
+   *                     [A] normalisation);
+   *   top_p in (0, 1];  top_k = -1 (whole vocabulary) or >= 1;
+   *   min_p in [0, 1];  repetition_penalty > 0;  presence/frequency finite. */
+  const float *temperature;
+  const float *top_p;
+  const float *min_p;
+  const float *repetition_penalty;
+  const float *presence_penalty;
+  const float *frequency_penalty;
+  const int32_t *top_k;
+
+  /* Token history for the penalties ([C] "解码一步里采样做什么",
+   * _apply_penalties): history_ids is device memory; row r's history is
+   * history_ids[history_start[r] .. history_start[r] + history_len[r]).
+   * history_start / history_len are host arrays of n_rows entries.  Spans
+   * may overlap or alias (forked rows share their parent's history).  Ids
+   * outside [0, vocab) are ignored.  All three may be NULL when no row uses
+   * a penalty.  history_len[r] <= max_history_per_row. */
+  const int32_t *history_ids;
+  const int64_t *history_start;
+  const int32_t *history_len;
+
+  /* Randomness (Philox4x32-10, Salmon et al. SC'11).  Vocabulary entry i of
+   * row r draws word (i & 3) of the block at counter
+   * (i >> 2, stream_r, offset_r lo, offset_r hi) under key (seed_r lo, seed_r hi);
+   * E = -ln(1 - (x + 1/2) 2^-32), clamped below at FLT_MIN ([A] "Nine lines,
+   * and exactly one call site").  Defaults: seed_r = seed, offset_r = offset,
+   * stream_r = r; on a deterministic handle seed_r = 42 and stream_r = 0.
+   * The library keeps no random state: replaying the same arguments
+   * replays the same tokens. */
+  uint64_t seed;
+  uint64_t offset;
+  const uint64_t *row_seed;    /* host, n_rows entries, or NULL */
+  const uint64_t *row_offset;  /* host, n_rows entries, or NULL */
+  const uint32_t *row_stream;  /* host, n_rows entries, or NULL */
+
+  /* Outputs (device).  token_ids is required: int32 [n_rows]; -1 for a row
+   * with row_status != 0.  probs / logprobs: fp32 [n_rows, vocab] (stride
+   * vocab) or NULL; they are the distribution sampled from ([B] "Logprobs
+   * are temperature-scaled"): after temperature and truncation, 0 and -inf
+   * outside the kept set; greedy rows report the untruncated distribution
+   * at temperature 1.  top_logprobs (0 .. max_top_logprobs) largest kept
+   * logprobs per row with their ids, ordered by (logit desc, id asc), padded
+   * with (-inf, -1): fp32 / int32 [n_rows, top_logprobs].  row_status: int32
+   * [n_rows] or NULL; 0 ok, 1 no finite logit (all -inf/NaN after
+   * sanitising NaN to -inf), 2 a +inf value after temperature. */
+  int32_t *token_ids;
+  float *probs;
+  float *logprobs;
+  int32_t top_logprobs;
+  float *top_logprob_vals;
+  int32_t *top_logprob_ids;
+  int32_t *row_status;
+
+  /* Output (host, may be NULL): the path the predicate chose. */
+  int32_t *path_out;
+} sampler_step_args;
+
+/* Create a handle on cfg->device: checks the device, allocates the device
+ * workspace (exchange areas, barrier words, parameter ring) and a pinned
+ * host staging ring of depth 4.  Returns SAMPLER_EHIP when no usable HIP
+ * device exists (and *out = NULL), SAMPLER_EINVAL for a bad config.
+ * Ownership: the caller owns *out and must call sampler_destroy. */
+sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out);
+
+/* Enqueue one decode step on `stream` (a hipStream_t; NULL is the default
+ * stream).  Validates every host-side argument before any launch and returns
+ * a negative status without launching if one is wrong.  Allocates nothing,
+ * never synchronises the device and never reads device memory back; waits on
+ * the host only when the 4-slot staging ring wraps onto a slot whose copy is
+ * still in flight.  Outputs are valid when the stream reaches this point. */
+sampler_status sampler_step(sampler_handle *h, const sampler_step_args *args, void *stream);
+
+/* The batch predicate alone ([A] "One request with top_p takes the whole
+ * batch off the fast path": normalize, then is_all_greedy / need_top_p /
+ * need_top_k / need_min_p).  Pure host code: works without a GPU.  `flags`
+ * takes SAMPLER_DETERMINISTIC.  Reads only n_rows and the parameter arrays
+ * of args.  SAMPLER_EINVAL for an empty batch or invalid parameters. */
+sampler_status sampler_select_path(const sampler_step_args *args, uint32_t flags, int32_t *path_out);
+
+/* Check a step's host-side arguments against a config without a device
+ * (the same checks sampler_step performs before launching).  Writes a
+ * message into msg (when non-NULL, msg_len > 0). */
+sampler_status sampler_validate(const sampler_config *cfg, const sampler_step_args *args, char *msg,
+                                int32_t msg_len);
+
+/* Free the handle's device workspace and pinned ring after waiting for its
+ * in-flight staging copies.  NULL is a no-op. */
+void sampler_destroy(sampler_handle *h);
+
+/* Message of the last failed call on h ("" when none); with h == NULL, the
+ * message of the last sampler_create failure on this thread.  The string
+ * stays valid until the next call on the handle. */
+const char *sampler_last_error(const sampler_handle *h);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSTS_SAMPLER_H */

@@ -1,0 +1,154 @@
+"""C-ABI checks that need no GPU: the library loads and exports every entry
+point the header declares; the batch predicate and the host-side argument
+validation behave as documented; sampler_create fails cleanly without a
+device."""
+import ctypes
+import json
+import os
+import re
+
+import numpy as np
+import pytest
+
+import decode_step_token_sampler_amd as dsts
+from decode_step_token_sampler_amd import build as dbuild
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+GOLDEN = os.path.join(ROOT, "tests", "golden")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    dbuild.ensure_built()
+    return dsts.load_library()
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "sampler.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sampler_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(dsts.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+    # nm agrees: defined, global, text symbols
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--defined-only", dsts.LIB_PATH], capture_output=True, text=True).stdout
+    defined = {l.split()[-1] for l in out.splitlines() if " T " in l}
+    for n in names:
+        assert n in defined, n
+
+
+def test_predicate_matches_page_table(lib):
+    spec = json.load(open(os.path.join(GOLDEN, "path_table.json")))
+    for case in spec["cases"]:
+        rows = case["rows"]
+        got = dsts.select_path([r["temperature"] for r in rows], [r["top_k"] for r in rows],
+                               [r["top_p"] for r in rows], [r["min_p"] for r in rows],
+                               deterministic=case["deterministic"])
+        assert got == case["expected"], case["name"]
+
+
+def test_predicate_agrees_with_oracle_on_random_batches(lib):
+    import oracle
+    rng = np.random.default_rng(0)
+    for _ in range(300):
+        n = int(rng.integers(1, 9))
+        T = rng.choice(np.array([0.0, 5e-7, 0.5, 1.0, 1.3], np.float32), n)
+        k = rng.choice(np.array([-1, -1, -1, 1, 5, 50], np.int32), n)
+        p = rng.choice(np.array([1.0, 1.0, 0.9], np.float32), n)
+        mp = rng.choice(np.array([0.0, 0.0, 0.05], np.float32), n)
+        det = bool(rng.integers(0, 2))
+        assert dsts.select_path(T, k, p, mp, deterministic=det) == oracle.select_path(T, k, p, mp, det)
+
+
+def test_empty_batch_rejected(lib):
+    with pytest.raises(dsts.SamplerError) as e:
+        dsts.select_path([], [], [], [], n_rows=0)
+    assert e.value.status == dsts.SAMPLER_EINVAL
+
+
+def _args(n=2, V=16, **kw):
+    keep = []
+    a = dsts.StepArgs()
+    a.logits = 0x1000
+    a.dtype = dsts.DTYPE_F32
+    a.n_rows = n
+    a.vocab = V
+    a.row_stride = V
+    a.token_ids = 0x2000
+    for k, v in kw.items():
+        if isinstance(v, np.ndarray):
+            keep.append(v)
+            setattr(a, k, v.ctypes.data)
+        else:
+            setattr(a, k, v)
+    return a, keep
+
+
+CFG = dsts.Config(max_rows=8, max_vocab=1024, max_history_per_row=64, max_top_logprobs=20, device=0, flags=0)
+
+
+@pytest.mark.parametrize("change,status", [
+    (dict(n_rows=0), dsts.SAMPLER_EINVAL),
+    (dict(n_rows=9), dsts.SAMPLER_ECAPACITY),
+    (dict(vocab=0), dsts.SAMPLER_EINVAL),
+    (dict(vocab=2048, row_stride=2048), dsts.SAMPLER_ECAPACITY),
+    (dict(row_stride=8), dsts.SAMPLER_EINVAL),
+    (dict(logits=None), dsts.SAMPLER_EINVAL),
+    (dict(token_ids=None), dsts.SAMPLER_EINVAL),
+    (dict(dtype=7), dsts.SAMPLER_EINVAL),
+    (dict(temperature=np.array([1.0, -0.5], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(temperature=np.array([1.0, np.nan], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(temperature=np.array([1.0, np.inf], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(top_p=np.array([0.0, 1.0], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(top_p=np.array([1.5, 1.0], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(top_k=np.array([0, 5], np.int32)), dsts.SAMPLER_EINVAL),
+    (dict(top_k=np.array([-2, 5], np.int32)), dsts.SAMPLER_EINVAL),
+    (dict(min_p=np.array([-0.1, 0.0], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(min_p=np.array([1.1, 0.0], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(repetition_penalty=np.array([0.0, 1.0], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(presence_penalty=np.array([np.inf, 0.0], np.float32)), dsts.SAMPLER_EINVAL),
+    (dict(history_len=np.array([65, 0], np.int32), history_start=np.zeros(2, np.int64), history_ids=0x3000),
+     dsts.SAMPLER_ECAPACITY),
+    (dict(history_len=np.array([4, 0], np.int32), history_start=np.zeros(2, np.int64)), dsts.SAMPLER_EINVAL),
+    (dict(history_len=np.array([4, 0], np.int32), history_ids=0x3000), dsts.SAMPLER_EINVAL),
+    (dict(history_len=np.array([-1, 0], np.int32), history_start=np.zeros(2, np.int64), history_ids=0x3000),
+     dsts.SAMPLER_EINVAL),
+    (dict(top_logprobs=21, top_logprob_vals=0x4000, top_logprob_ids=0x5000), dsts.SAMPLER_ECAPACITY),
+    (dict(top_logprobs=5), dsts.SAMPLER_EINVAL),
+])
+def test_validation_errors(lib, change, status):
+    a, keep = _args(**change)
+    st, msg = dsts.validate(CFG, a)
+    assert st == status, msg
+    assert msg
+
+
+def test_validation_accepts_good_args(lib):
+    a, keep = _args(temperature=np.array([0.0, 0.7], np.float32), top_k=np.array([-1, 20], np.int32),
+                    top_p=np.array([1.0, 0.9], np.float32), min_p=np.array([0.0, 0.05], np.float32),
+                    history_len=np.array([4, 0], np.int32), history_start=np.zeros(2, np.int64),
+                    history_ids=0x3000, top_logprobs=20, top_logprob_vals=0x4000, top_logprob_ids=0x5000)
+    st, msg = dsts.validate(CFG, a)
+    assert st == dsts.SAMPLER_OK, msg
+
+
+def test_create_without_gpu_reports_ehip(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    with pytest.raises(dsts.SamplerError) as e:
+        dsts.Sampler(4, 1024)
+    assert e.value.status == dsts.SAMPLER_EHIP
+    assert "device" in str(e.value)
+
+
+def test_create_rejects_bad_config(lib):
+    h = ctypes.c_void_p()
+    bad = dsts.Config(max_rows=0, max_vocab=1024, max_history_per_row=0, max_top_logprobs=0, device=0, flags=0)
+    assert lib.sampler_create(ctypes.byref(bad), ctypes.byref(h)) in (dsts.SAMPLER_EINVAL, dsts.SAMPLER_EHIP)
+    assert not h.value
