@@ -32,7 +32,7 @@ FLAG_FORCE_FILTERED = 1 << 1
 
 # symbols the header declares
 EXPORTS = ("sampler_create", "sampler_step", "sampler_select_path", "sampler_validate", "sampler_destroy",
-           "sampler_last_error")
+           "sampler_last_error", "sampler_profile_start", "sampler_profile_stop")
 
 
 class SamplerError(RuntimeError):
@@ -107,6 +107,11 @@ def load_library(path: str = LIB_PATH):
     L.sampler_validate.restype = ctypes.c_int
     L.sampler_destroy.argtypes = [ctypes.c_void_p]
     L.sampler_destroy.restype = None
+    L.sampler_profile_start.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    L.sampler_profile_start.restype = ctypes.c_int
+    L.sampler_profile_stop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
+                                       ctypes.POINTER(ctypes.c_int32)]
+    L.sampler_profile_stop.restype = ctypes.c_int
     L.sampler_last_error.argtypes = [ctypes.c_void_p]
     L.sampler_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -207,6 +212,22 @@ class Sampler:
 
     def last_error(self) -> str:
         return self._L.sampler_last_error(self._h).decode()
+
+    def profile_start(self, capacity: int):
+        """Record kernel durations of the next `capacity` steps (HIP events)."""
+        st = self._L.sampler_profile_start(self._h, int(capacity))
+        if st != SAMPLER_OK:
+            raise SamplerError(st, self.last_error())
+
+    def profile_stop(self) -> np.ndarray:
+        """Kernel durations (ms) of the recorded steps, in launch order."""
+        cap = 1 << 20
+        buf = np.zeros(cap, dtype=np.float32)
+        n = ctypes.c_int32(0)
+        st = self._L.sampler_profile_stop(self._h, buf.ctypes.data, cap, ctypes.byref(n))
+        if st != SAMPLER_OK:
+            raise SamplerError(st, self.last_error())
+        return buf[:n.value].copy()
 
     def step_raw(self, args: StepArgs, stream: int = 0) -> int:
         """Enqueue with a filled StepArgs (pointers already set); returns the status."""

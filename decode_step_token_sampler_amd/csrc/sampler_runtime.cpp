@@ -16,6 +16,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <vector>
 
 #include "../../include/sampler.h"
 #include "sampler_internal.h"
@@ -60,6 +61,9 @@ struct sampler_handle {
   WgSlots *slots = nullptr;
   uint32_t *abort_word = nullptr;  // device word: epoch of an aborted launch
   uint32_t epoch = 0;
+  std::vector<hipEvent_t> prof;  // 2 per recorded step
+  int prof_cap = 0;
+  int prof_n = 0;
   std::string err;
 };
 
@@ -225,8 +229,15 @@ struct DeviceGuard {
   }
 };
 
+void free_profile(sampler_handle *h) {
+  for (hipEvent_t e : h->prof) (void)hipEventDestroy(e);
+  h->prof.clear();
+  h->prof_cap = h->prof_n = 0;
+}
+
 void free_handle(sampler_handle *h) {
   if (!h) return;
+  free_profile(h);
   for (int s = 0; s < kRing; ++s)
     if (h->slot_done[s]) {
       (void)hipEventSynchronize(h->slot_done[s]);
@@ -481,8 +492,50 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.abort_word = h->abort_word;
   if (++h->epoch == 0) h->epoch = 1;
   kp.epoch = h->epoch;
+  const bool prof = h->prof_n < h->prof_cap;
+  if (prof && (e = hipEventRecord(h->prof[2 * h->prof_n], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
   e = launch_step(kp, a->dtype, any_pen, stream);
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
+  if (prof) {
+    if ((e = hipEventRecord(h->prof[2 * h->prof_n + 1], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    ++h->prof_n;
+  }
+  return SAMPLER_OK;
+}
+
+sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity) {
+  if (!h || capacity < 1) return SAMPLER_EINVAL;
+  DeviceGuard guard(h->device);
+  free_profile(h);
+  h->prof.resize(2 * (size_t)capacity);
+  for (auto &ev : h->prof) {
+    hipError_t e = hipEventCreate(&ev);
+    if (e != hipSuccess) {
+      ev = nullptr;
+      free_profile(h);
+      return hip_fail(h, e, "hipEventCreate");
+    }
+  }
+  h->prof_cap = capacity;
+  h->prof_n = 0;
+  return SAMPLER_OK;
+}
+
+sampler_status sampler_profile_stop(sampler_handle *h, float *ms, int32_t cap, int32_t *n) {
+  if (!h || !n || (cap > 0 && !ms)) return SAMPLER_EINVAL;
+  DeviceGuard guard(h->device);
+  int k = 0;
+  for (int i = 0; i < h->prof_n && i < cap; ++i) {
+    hipError_t e = hipEventSynchronize(h->prof[2 * i + 1]);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms[k], h->prof[2 * i], h->prof[2 * i + 1]);
+    if (e != hipSuccess) {
+      free_profile(h);
+      return hip_fail(h, e, "hipEventElapsedTime");
+    }
+    ++k;
+  }
+  *n = k;
+  free_profile(h);
   return SAMPLER_OK;
 }
 

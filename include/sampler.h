@@ -180,6 +180,18 @@ sampler_status sampler_select_path(const sampler_step_args *args, uint32_t flags
 sampler_status sampler_validate(const sampler_config *cfg, const sampler_step_args *args, char *msg,
                                 int32_t msg_len);
 
+/* Profiling: from now on each sampler_step records a HIP event pair right
+ * before and right after its kernel on the step's stream, for up to
+ * `capacity` steps.  This call creates the events (it may allocate); the
+ * steps themselves allocate nothing.  SAMPLER_EINVAL for capacity < 1. */
+sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity);
+
+/* Stop recording, wait for the recorded kernels, and write the kernel
+ * durations in milliseconds (one per recorded step, in launch order) to
+ * ms[0 .. min(n_recorded, cap)); *n receives the number written.  Releases
+ * the events. */
+sampler_status sampler_profile_stop(sampler_handle *h, float *ms, int32_t cap, int32_t *n);
+
 /* Free the handle's device workspace and pinned ring after waiting for its
  * in-flight staging copies.  NULL is a no-op. */
 void sampler_destroy(sampler_handle *h);

@@ -1,0 +1,258 @@
+"""Parity of the HIP library (through the C ABI) with the CPU oracle on a
+real MI355X, plus invariants: replay, run-to-run stability, path invariance,
+deterministic batch invariance and the Gumbel-max distribution.
+
+Parity rules (also in parity.py): token ids bit-exact except oracle-flagged
+near-tie / boundary rows; probs within 1e-6; logprobs within 1e-5 with an
+identical -inf pattern; top logprobs ids identical and values within 1e-5.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from parity import PROB_TOL, LOGPROB_TOL, compare, run_gpu, run_oracle, to_device
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+
+
+@pytest.fixture(scope="module")
+def sampler():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(512, 262_144, max_history_per_row=2048, max_top_logprobs=32)
+    yield s
+    s.close()
+
+
+def check(batch, sampler, rows=None, **over):
+    g = run_gpu(sampler, batch, **over)
+    sub = batch if rows is None else batch.subset(rows)
+    o = run_oracle(sub, **{k: v for k, v in over.items() if k == "deterministic"})
+    r = compare(g, o, rows)
+    print(batch.name, r)
+    assert r.ok(), r
+    return g, o, r
+
+
+# ------------------------------------------------------------ the five workloads
+def test_workload1_gumbel_only(sampler):
+    g, o, r = check(workloads.config(1), sampler)
+    assert g["path"] == "gumbel"
+
+
+def test_workload2_batch1_gumbel_and_greedy(sampler):
+    sets = [workloads.config(2, set_id=s) for s in range(4)]
+    for step in range(48):
+        b = sets[step % 4]
+        b.offset = step
+        check(b, sampler)
+    greedy = workloads.config(2, temperature=0.0)
+    g, o, r = check(greedy, sampler)
+    assert g["path"] == "greedy"
+    x = workloads.bf16_bits_to_f32(greedy.logits)
+    assert g["token_ids"][0] == int(np.argmax(x[0]))
+
+
+def test_workload3_mixed_filtered(sampler):
+    b = workloads.config(3)
+    g, o, r = check(b, sampler)
+    assert g["path"] == "filtered"   # the greedy row forces it
+
+
+def test_workload4_full_chain(sampler):
+    for step in range(2):
+        b = workloads.config(4, set_id=step, step=step)
+        g, o, r = check(b, sampler)
+        assert g["path"] == "filtered"
+
+
+def test_workload5_large_vocab_forks(sampler):
+    b = workloads.config(5)
+    g, o, r = check(b, sampler)
+    # forks share parameters and history but draw independently
+    tok = g["token_ids"].reshape(-1, 4)
+    assert np.mean(tok[:, 0] == tok[:, 1]) < 0.9
+
+
+# ------------------------------------------------------------ randomised shapes
+@pytest.mark.parametrize("seed,n,V,dtype,ties", [
+    (0, 1, 1, "f32", False), (1, 3, 2, "f32", False), (2, 5, 3, "bf16", True), (3, 17, 63, "f32", True),
+    (4, 16, 64, "bf16", False), (5, 9, 65, "f32", False), (6, 11, 1000, "bf16", True), (7, 13, 4097, "f32", False),
+    (8, 4, 50_001, "bf16", False), (9, 2, 131_071, "f32", True), (10, 6, 40_000, "f32", False),
+])
+def test_random_small(sampler, seed, n, V, dtype, ties):
+    check(workloads.random_small(seed, n, V, dtype, ties=ties), sampler)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_unaligned_stride_and_outputs(sampler, dtype):
+    b = workloads.random_small(20, 6, 1001, dtype)
+    L, H = to_device(b)
+    wide = torch.full((b.n_rows, 1003), float("nan"), dtype=L.dtype, device=L.device)
+    wide[:, 1:1002] = L
+    view = wide[:, 1:1002]            # odd base offset and odd row stride
+    g = run_gpu(sampler, b, logits=view, history=H)
+    o = run_oracle(b)
+    r = compare(g, o)
+    assert r.ok(), r
+
+
+def test_edge_rows(sampler):
+    V = 300
+    x = np.random.default_rng(3).standard_normal((6, V)).astype(np.float32)
+    x[0, :] = -np.inf                 # no finite logit
+    x[1, :] = np.nan                  # NaN reads as -inf
+    x[2, 5] = np.inf                  # +inf
+    x[3, :] = -np.inf
+    x[3, 17] = 1.0                    # one finite value
+    x[4, ::2] = np.nan                # half NaN
+    b = workloads.Batch("edge rows", "f32", x, temperature=np.array([1, 1, 1, 0.5, 0.8, 1e-7], np.float32),
+                        top_k=np.array([-1, 5, -1, 3, 2, -1], np.int32), top_p=np.array([1, 1, 1, 0.5, 0.9, 1], np.float32),
+                        min_p=np.zeros(6, np.float32), want_probs=True, want_logprobs=True, top_logprobs=4)
+    g, o, r = check(b, sampler)
+    assert g["row_status"].tolist() == [1, 1, 2, 0, 0, 0]
+    assert g["token_ids"][:3].tolist() == [-1, -1, -1]
+    assert g["token_ids"][3] == 17
+
+
+def test_history_edges(sampler):
+    b = workloads.random_small(30, 8, 777, "f32", penalties=True, history_len=40)
+    b.history_ids[::7] = -5           # ids outside [0, V) are ignored
+    b.history_ids[3::11] = 777 + 9
+    b.history_start[5] = b.history_start[2]   # aliased spans
+    b.history_len[6] = 0
+    check(b, sampler)
+
+
+def test_max_vocab():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(4, 1 << 20, max_history_per_row=1024, max_top_logprobs=8)
+    b = workloads.random_small(40, 2, 1 << 20, "bf16", history_len=1024)
+    b.top_logprobs = 8
+    check(b, s)
+    s.close()
+
+
+# ------------------------------------------------------------ invariants
+def test_replay_and_run_to_run_stability(sampler):
+    b = workloads.config(4, n_rows=16, vocab=50_000, history_len=512)
+    L, H = to_device(b)
+    first = run_gpu(sampler, b, logits=L, history=H)
+    for _ in range(20):
+        again = run_gpu(sampler, b, logits=L, history=H)
+        for k in ("token_ids", "probs", "logprobs", "row_status"):
+            np.testing.assert_array_equal(first[k], again[k])
+
+
+def test_forced_filtered_path_is_identical():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    a = dsts.Sampler(64, 20_000, max_history_per_row=64)
+    f = dsts.Sampler(64, 20_000, max_history_per_row=64, force_filtered=True)
+    plain = workloads.random_small(50, 12, 9_999, "bf16", penalties=True, mix="plain")
+    plain.temperature = np.full(12, 0.9, np.float32)   # no greedy row: Gumbel path
+    for b in (workloads.config(1, n_rows=9, vocab=20_000), plain):
+        b.want_logprobs = True
+        for T in (None, 0.0):
+            if T is not None:
+                b.temperature = np.zeros(b.n_rows, np.float32)
+            ga = run_gpu(a, b)
+            gf = run_gpu(f, b)
+            assert ga["path"] in ("gumbel", "greedy")
+            for k in ("token_ids", "probs", "logprobs"):
+                np.testing.assert_array_equal(ga[k], gf[k])
+    a.close()
+    f.close()
+
+
+def test_one_greedy_row_changes_path_not_results(sampler):
+    # [A] worked case: a temperature-0 request moves the batch to filtered
+    b = workloads.config(1, n_rows=6, vocab=30_000)
+    b.want_logprobs = True
+    b.row_stream = np.arange(6, dtype=np.uint32)
+    plain = run_gpu(sampler, b)
+    x = np.concatenate([b.logits, b.logits[:1]])
+    b2 = workloads.Batch("plus greedy", "f32", x, temperature=np.append(b.temperature, 0.0).astype(np.float32),
+                         top_k=np.full(7, -1, np.int32), top_p=np.ones(7, np.float32), min_p=np.zeros(7, np.float32),
+                         row_stream=np.arange(7, dtype=np.uint32), want_probs=True, want_logprobs=True)
+    mixed = run_gpu(sampler, b2)
+    assert plain["path"] == "gumbel" and mixed["path"] == "filtered"
+    for k in ("token_ids", "probs", "logprobs"):
+        np.testing.assert_array_equal(plain[k], mixed[k][:6])
+
+
+def test_deterministic_batch_invariance():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(32, 100_000, max_history_per_row=256, deterministic=True)
+    big = workloads.random_small(60, 12, 70_000, "f32", penalties=True, history_len=256)
+    big.row_seed = None
+    big.row_stream = None
+    ref = run_gpu(s, big)
+    o = run_oracle(big, deterministic=True)
+    r = compare(ref, o)
+    assert r.ok(), r
+    for r_ in (0, 5, 11):
+        for n_before in (0, 3):
+            rows = list(range(n_before)) + [r_]
+            sub = big.subset(rows)
+            sub.row_seed = None
+            sub.row_stream = None
+            sub.row_offset = None
+            g = run_gpu(s, sub)
+            for k in ("token_ids", "probs", "logprobs"):
+                np.testing.assert_array_equal(g[k][-1], ref[k][r_])
+    s.close()
+
+
+def test_gumbel_distribution_chi2_and_exact_tokens():
+    _need_gpu()
+    import scipy.special
+    import scipy.stats
+    import decode_step_token_sampler_amd as dsts
+    n_chunk, chunks, V = 100_000, 10, 64
+    s = dsts.Sampler(n_chunk, V, max_history_per_row=0, max_top_logprobs=0)
+    x = (1.5 * np.random.default_rng(8).standard_normal(V)).astype(np.float32)
+    for top_k, top_p in ((-1, 1.0), (10, 0.8)):
+        counts = np.zeros(V, np.int64)
+        for c in range(chunks):
+            L = np.ascontiguousarray(np.broadcast_to(x, (n_chunk, V)))
+            b = workloads.Batch("chi2", "f32", L, temperature=np.full(n_chunk, 0.9, np.float32),
+                                top_k=np.full(n_chunk, top_k, np.int32), top_p=np.full(n_chunk, top_p, np.float32),
+                                min_p=np.zeros(n_chunk, np.float32), row_seed=np.full(n_chunk, 99, np.uint64),
+                                row_stream=np.zeros(n_chunk, np.uint32),
+                                row_offset=np.arange(c * n_chunk, (c + 1) * n_chunk, dtype=np.uint64))
+            g = run_gpu(s, b, want_status=True)
+            if c < 2:   # exact token parity on a fifth of the draws
+                o = run_oracle(b)
+                r = compare(g, o)
+                assert r.ok(), r
+            counts += np.bincount(g["token_ids"], minlength=V)
+        z = (x / np.float32(0.9)).astype(np.float64)
+        if top_k == -1:
+            probs = scipy.special.softmax(z)
+        else:
+            order = np.lexsort((np.arange(V), -z))
+            top = order[:top_k]
+            q = np.exp(z[top] - z.max())
+            cum = np.cumsum(q)
+            keep = top[:int(np.searchsorted(cum, top_p * cum[-1])) + 1]
+            probs = np.zeros(V)
+            probs[keep] = np.exp(z[keep] - z.max())
+            probs /= probs.sum()
+            assert counts[probs == 0].sum() == 0
+        exp = probs * counts.sum()
+        m = exp >= 5
+        obs, ex = counts[m], exp[m]
+        if exp[~m].sum() > 0:
+            obs, ex = np.append(obs, counts[~m].sum()), np.append(ex, exp[~m].sum())
+        p = scipy.stats.chisquare(obs, ex * (obs.sum() / ex.sum())).pvalue
+        assert p > 1e-3, (top_k, p)
+    s.close()
