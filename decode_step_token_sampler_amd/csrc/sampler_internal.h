@@ -22,19 +22,32 @@ constexpr int kMaxHashSlots = 8192;
 // Largest vocabulary (masses are summed as 2^-44 fixed point in 64 bits).
 constexpr int32_t kMaxVocab = 1 << 20;
 
-// Workgroup shape of the row kernel: 1024 threads (16 wave64s).  Each
+// Workgroup shape of the row kernel: 512 threads (8 wave64s; LDS allows one
+// workgroup per CU, so each thread may use 256 VGPRs).  Each
 // workgroup keeps its slice of the processed logits in LDS; the slice is at
 // most 32768 values (the hash packs 15-bit slice-local indices) and is also
-// bounded by the LDS left after the fixed part and the hash table.
-constexpr int kBlock = 1024;
+// bounded by the LDS left after the fixed part and the shared region.
+constexpr int kBlock = 512;
 constexpr int kMaxSlice = 32768;
+
+// Threshold window: values within 32 nats of the row max are counted in
+// 1/16-nat bins of their distance d = max - z (bin kWinBins counts the
+// rest).  Masses exp(-d) are binned for d < 16 nats (kMassBins bins); deeper
+// values only add to a per-workgroup total, kept in registers.
+constexpr int kWinBins = 512;
+constexpr float kBinsPerNat = 16.0f;
+constexpr int kMassBins = 256;
+// Candidates (values in the bins that hold a threshold or the top logprobs)
+// gathered per row for exact selection; more sends the row to the general
+// radix-select path.
+constexpr int kCandCap = 1024;
 
 // Per-row flags, decided on the host from the row's parameters.
 enum : uint32_t {
   RF_GREEDY = 1u << 0,  // greedy row: keep every token at T = 1; token = first argmax
   RF_TOP1 = 1u << 1,    // top_k == 1 after normalisation: token = first argmax
   RF_PEN = 1u << 2,     // a penalty differs from its default and the row has history
-  RF_TOPK = 1u << 3,    // 2 <= top_k < vocab
+  RF_TOPK = 1u << 3,    // 1 <= top_k < vocab (set for non-greedy top_k == 1 rows too)
   RF_TOPP = 1u << 4,    // top_p < 1
   RF_MINP = 1u << 5,    // min_p > 0
 };
@@ -67,14 +80,31 @@ struct alignas(128) GroupSync {
   uint32_t pad2[31];
 };
 
-// Exchange slots owned by one workgroup (indexed by its block id), double
-// buffered by the parity of the exchange sequence.
+// Per-group record written by the workgroup that merges an exchange (the
+// last to arrive) and read by the others.
+struct alignas(128) GroupRec {
+  uint32_t cum_cnt[kWinBins + 1];          // inclusive prefix counts over the bins (last: all values)
+  unsigned long long cum_mass[kMassBins + 1];  // inclusive prefix masses, 2^-44 fixed point (last: all)
+  uint32_t dec[16];                        // decisions (see the kernel)
+  double dd[8];
+  uint32_t cand_n;                         // candidates gathered
+  uint32_t pad[31];
+  float cz[kCandCap];                      // candidate values
+  int32_t ci[kCandCap];                    // candidate indices
+};
+
+// Exchange slots owned by one workgroup (indexed by its block id).
 struct alignas(128) WgSlots {
-  double small[2][4];                             // (max, sum, argmax key) / kept-set sum
-  uint32_t hcnt[2][256];                          // radix-select counts
-  unsigned long long hmass[2][256];               // radix-select masses (2^-44 fixed point)
-  double fin[2][2];                               // best Gumbel score and its index
-  unsigned long long toplist[2][kMaxTopLogprobs]; // local top-logprob candidates
+  double small[2][4];                             // exchange 1 (max, argmax key), by row parity
+  double fin[2][2];                               // best Gumbel score and its index, by row parity
+  double spart;                                   // sum of exp(z - m) over the slice (whole rows)
+  double pad0[3];
+  uint32_t wcnt[kWinBins + 1];                    // window counts (last: deeper values)
+  unsigned long long wmass[kMassBins + 1];        // window masses (last: deeper values)
+  uint32_t hcnt[2][256];                          // general path: radix counts
+  unsigned long long hmass[2][256];               // general path: radix masses
+  unsigned long long toplist[2][kMaxTopLogprobs]; // general path: local top-logprob candidates
+  double ssum[2];                                 // general path: kept-set sum
 };
 
 enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINISTIC = 3 };
@@ -100,6 +130,7 @@ struct KernelParams {
   int32_t vec_ok;     // bit 0: logits rows aligned for vector loads; bit 1: outputs for vector stores
   int32_t path;
   GroupSync *sync;    // [n_groups]
+  GroupRec *recs;     // [n_groups]
   WgSlots *slots;     // [n_groups * G]
   uint32_t *abort_word;  // equals epoch once a barrier wait of this launch expired
   uint32_t epoch;        // launch counter of the handle (never 0)
@@ -110,8 +141,11 @@ hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, hipStr
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);
-// Fixed LDS bytes of one workgroup (reductions, histograms, bitmap).
+// Fixed LDS bytes of one workgroup.
 size_t kernel_lds_fixed();
+// LDS bytes of the shared region (penalty hash + bitmap, window histogram,
+// candidate ranking, general-path histograms: used one at a time).
+size_t kernel_lds_region(int slice, int hash_slots, bool penalties);
 // Dynamic LDS bytes of one workgroup for a slice and hash size.
 size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties);
 

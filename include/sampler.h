@@ -139,7 +139,9 @@ typedef struct sampler_step_args {
    * logprobs per row with their ids, ordered by (logit desc, id asc), padded
    * with (-inf, -1): fp32 / int32 [n_rows, top_logprobs].  row_status: int32
    * [n_rows] or NULL; 0 ok, 1 no finite logit (all -inf/NaN after
-   * sanitising NaN to -inf), 2 a +inf value after temperature. */
+   * sanitising NaN to -inf), 2 a +inf value after temperature, 3 the
+   * step's cross-workgroup wait timed out (an internal error; the row's
+   * outputs are not valid). */
   int32_t *token_ids;
   float *probs;
   float *logprobs;
