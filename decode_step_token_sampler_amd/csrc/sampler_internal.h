@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <stddef.h>
 #include <stdint.h>
 
 namespace dsts {
@@ -30,13 +31,14 @@ constexpr int32_t kMaxVocab = 1 << 20;
 constexpr int kBlock = 512;
 constexpr int kMaxSlice = 32768;
 
-// Threshold window: values within 32 nats of the row max are counted in
-// 1/16-nat bins of their distance d = max - z (bin kWinBins counts the
-// rest).  Masses exp(-d) are binned for d < 16 nats (kMassBins bins); deeper
-// values only add to a per-workgroup total, kept in registers.
+// Threshold window: values whose distance d = max - z, times min(1, T), is
+// below 16 are counted, and their masses exp(-d) summed in 2^-31 units, in
+// bins of 1/32 of that scaled distance; deeper values only add to a
+// per-workgroup mass total.  kWinBins equals kBlock: the merge gives each
+// thread one bin.
 constexpr int kWinBins = 512;
-constexpr float kBinsPerNat = 16.0f;
-constexpr int kMassBins = 256;
+constexpr float kWinNats = 16.0f;
+constexpr float kBinsPerNat = 32.0f;
 // Candidates (values in the bins that hold a threshold or the top logprobs)
 // gathered per row for exact selection; more sends the row to the general
 // radix-select path.
@@ -81,31 +83,35 @@ struct alignas(128) GroupSync {
 };
 
 // Per-group record written by the workgroup that merges an exchange (the
-// last to arrive) and read by the others.
+// last to arrive) and read by the others.  Every array starts on a 16-byte
+// boundary: the readers fetch it in 16-byte pieces.
 struct alignas(128) GroupRec {
-  uint32_t cum_cnt[kWinBins + 1];          // inclusive prefix counts over the bins (last: all values)
-  unsigned long long cum_mass[kMassBins + 1];  // inclusive prefix masses, 2^-44 fixed point (last: all)
-  uint32_t dec[16];                        // decisions (see the kernel)
+  uint32_t dec[32];                            // decisions (see the kernel)
   double dd[8];
-  uint32_t cand_n;                         // candidates gathered
-  uint32_t pad[31];
-  float cz[kCandCap];                      // candidate values
-  int32_t ci[kCandCap];                    // candidate indices
+  uint32_t cum_cnt[kWinBins];                  // inclusive prefix counts over the window bins
+  unsigned long long cum_mass[kWinBins + 2];   // inclusive prefix masses, 2^-31 units ([kWinBins]: all values)
 };
 
-// Exchange slots owned by one workgroup (indexed by its block id).
+// Exchange slots owned by one workgroup (indexed by its block id), laid out
+// like GroupRec for 16-byte reads.
 struct alignas(128) WgSlots {
-  double small[2][4];                             // exchange 1 (max, argmax key), by row parity
+  unsigned long long e1[2][2];                    // exchange 1: (max key << 32 | ~argmax), by row parity
   double fin[2][2];                               // best Gumbel score and its index, by row parity
-  double spart;                                   // sum of exp(z - m) over the slice (whole rows)
-  double pad0[3];
-  uint32_t wcnt[kWinBins + 1];                    // window counts (last: deeper values)
-  unsigned long long wmass[kMassBins + 1];        // window masses (last: deeper values)
+  double spart[2];                                // exact sum of exp(z - m) over the slice, by row parity
+  uint32_t cand_n;                                // candidates gathered by this workgroup
+  uint32_t pad0[11];
+  unsigned long long whist[kWinBins];             // window bins: count << 48 | mass (2^-31 units)
+  unsigned long long wdeep[2];                    // mass of the deeper values (2^-31 units)
+  unsigned long long cand[kCandCap];              // candidate keys: order key << 32 | ~index
   uint32_t hcnt[2][256];                          // general path: radix counts
   unsigned long long hmass[2][256];               // general path: radix masses
   unsigned long long toplist[2][kMaxTopLogprobs]; // general path: local top-logprob candidates
   double ssum[2];                                 // general path: kept-set sum
 };
+static_assert(offsetof(GroupRec, cum_cnt) % 16 == 0 && offsetof(GroupRec, cum_mass) % 16 == 0, "GroupRec layout");
+static_assert(offsetof(WgSlots, fin) % 16 == 0 && offsetof(WgSlots, whist) % 16 == 0 &&
+                  offsetof(WgSlots, cand) % 16 == 0,
+              "WgSlots layout");
 
 enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINISTIC = 3 };
 
@@ -136,15 +142,18 @@ struct KernelParams {
   uint32_t epoch;        // launch counter of the handle (never 0)
 };
 
-// Launch one step (cooperative: every workgroup of the grid is resident).
-hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, hipStream_t stream);
+// Launch one step.  The grid never exceeds the workgroups the device holds at
+// once; `cooperative` launches through hipLaunchCooperativeKernel, which
+// also has the runtime check that they are all resident.
+hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, bool cooperative, hipStream_t stream);
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);
 // Fixed LDS bytes of one workgroup.
 size_t kernel_lds_fixed();
-// LDS bytes of the shared region (penalty hash + bitmap, window histogram,
-// candidate ranking, general-path histograms: used one at a time).
+// LDS bytes of the shared region (penalty hash + bitmap; merged prefix
+// arrays with the local histogram, candidate staging or sorting after them;
+// general-path histograms: used one at a time).
 size_t kernel_lds_region(int slice, int hash_slots, bool penalties);
 // Dynamic LDS bytes of one workgroup for a slice and hash size.
 size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties);

@@ -7,31 +7,30 @@
 //   Philox4x32-10: Salmon, Moraes, Dror, Shaw, SC'11.
 //
 // One launch samples a whole batch.  A row is split into G contiguous slices;
-// G workgroups of 1024 threads (a "row group") own one slice each and keep
+// G workgroups of 512 threads (a "row group") own one slice each and keep
 // their slice's processed logits z = penalised(x) / T in LDS, so the logits
-// are read from HBM once.  The G workgroups of a group cooperate
-// through per-group barrier words and exchange slots in device memory (the
-// launch is cooperative, so all workgroups are resident).  A group walks
-// rows group, group + n_groups, ...
+// are read from HBM once.  The G workgroups of a group cooperate through
+// per-group barrier words and exchange slots in device memory (the launch
+// is cooperative, so all workgroups are resident).  A group walks rows
+// group, group + n_groups, ...
 //
 // Per row:
-//   1. load, NaN -> -inf, penalties (LDS hash of history counts, each
-//      distinct id applied once), z = x / T
-//   2. exchange 1: row max and first argmax
-//   3. exchange 2: a histogram of d = max - z in 1/16-nat bins (counts over
-//      32 nats, 2^-44 fixed-point masses over 16 nats, deeper values summed
-//      in registers), merged by the last workgroup to arrive, which picks the
-//      bins holding each threshold; min-p's fp64 test bounds an upper set of
-//      keys, found by bisection
-//   4. exchange 3: the values of those bins are gathered, ranked exactly by
-//      the last workgroup to arrive, which fixes top-k, top-p, the kept-set
-//      sum and the top logprobs (rows whose thresholds fall outside the
+//   1. load, NaN -> -inf, z = x / T as the loads land; penalties from an LDS
+//      hash of history counts, applied once per distinct id
+//   2. exchange 1: row max and first argmax; min-p's boundary key
+//   3. exchange 2: a histogram of d = max - z in 1/32-nat bins over 16 nats
+//      (counts, 2^-44 fixed-point masses; deeper masses summed per
+//      workgroup), merged by the last workgroup to arrive, which picks in
+//      parallel the bins holding each threshold
+//   4. exchange 3: the values of those bins are gathered, sorted by the last
+//      workgroup to arrive, which fixes top-k, top-p, the kept-set sum and
+//      the top logprobs exactly (rows whose thresholds fall outside the
 //      window take the general path: a radix select with one exchange per
 //      8-bit digit)
 //   5. emit probs / logprobs of the kept set; Gumbel-max with an in-kernel
-//      Philox draw, an fp32 log-domain filter and an fp64 check of every
-//      element that can still win
-//   6. the last workgroup to arrive merges the Gumbel candidates and writes
+//      Philox draw, a linear-domain bound that skips elements which cannot
+//      win, and an fp64 score for every element that still can
+//   6. the last workgroup to arrive merges the Gumbel winners and writes
 //      the token and status
 #include <float.h>
 #include <hip/hip_runtime.h>
@@ -50,24 +49,47 @@ constexpr int kWaves = kBlock / 64;
 // the worst score of the max, m - ln(22.874) (E at its largest, 33 ln 2).
 // 22.874 + 3.130 = 26.004; the margin covers fp32 rounding of m - z.
 constexpr float kPruneNats = 26.25f;
-// fp32 log-domain Gumbel scores are within ~1e-5 of the exact ones; any
-// element whose fp32 score is within this margin of the running best is
-// rescored in fp64.
-constexpr float kVerifyMargin = 1e-3f;
-constexpr double kMassScale = 17592186044416.0;  // 2^44
+// Relative slack of the linear-domain Gumbel bound (covers the fp32
+// rounding of the probability and of the uniform, ~1e-6).
+constexpr float kSlack = 1.0009765625f;
+constexpr double kMassScale = 17592186044416.0;  // 2^44 (general-path radix masses)
+constexpr double kWinScale = 2147483648.0;        // 2^31 (window masses)
+constexpr float kLog2e = 1.44269504088896341f;
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
+constexpr uint32_t kNone = 0xFFFFFFFFu;
+
+// LDS region layout after the penalty phase (byte offsets):
+//   A: merged inclusive prefix counts lc[kWinBins] (u32) and masses
+//      lm[kWinBins + 1] (u64), filled by a merging workgroup;
+//   B: the local histogram wh[kWinBins] (packed u64); later the
+//      per-wave candidate staging; later the merger's sorted candidate keys
+//      sk[kCandCap] (u64) and prefix masses sq[kCandCap] (f64).
+constexpr size_t kRegionLm = 4 * kWinBins;
+constexpr size_t kRegionB = (kRegionLm + 8 * (kWinBins + 1) + 15) & ~(size_t)15;
+constexpr size_t kRegionBBytes = 16 * (size_t)kCandCap;
+constexpr int kStagePerWave = (int)(kRegionBBytes / 8) / kWaves;
+static_assert(kWinBins == kBlock, "the merge gives each thread one bin");
+static_assert(2 * 256 * 12 <= kRegionBBytes, "radix histograms fit the region");
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 struct alignas(16) SmemBase {
+  double exp_tab[64];  // 2^(j/64)
   float red_f[kWaves];
   double red_d[kWaves];
   unsigned long long red_u[kWaves];
   int red_i[kWaves];
   uint32_t red_c[kWaves];
-  uint32_t bu[16];
+  uint32_t bu[40];
   double bd[16];
+  uint32_t dec[32];              // decision words of the group record
+  double gd[kMaxG];              // per-workgroup values read by a merger
+  int gi[kMaxG];
+  uint32_t gcnt[kMaxG];          // merger: candidates per workgroup
+  uint32_t gpo[kMaxG + 1];       // merger: 16-byte pair offsets per workgroup
+  uint32_t goff[kMaxG + 1];      // merger: candidate offsets per workgroup
+  uint32_t wo[kWaves + 1];       // gather: offsets per wave
   unsigned long long tl[kMaxTopLogprobs];
 };
 
@@ -90,40 +112,120 @@ DEV void atomic_st(T *p, T v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-DEV float wave_max_f(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
-  return v;
-}
-DEV double wave_sum_d(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
-}
-DEV unsigned long long wave_max_u(unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    unsigned long long w = __shfl_xor(v, o, 64);
-    v = w > v ? w : v;
-  }
-  return v;
+// The thread index behind an opaque copy: values derived from it are
+// recomputed where used instead of being hoisted out of the row loop (where
+// they would stay live across every phase).
+DEV int tidx() {
+  int t = threadIdx.x;
+  asm volatile("" : "+v"(t));
+  return t;
 }
 
-// Workgroup reductions (every thread gets the result).
-DEV float wg_max_f(SmemBase &sm, float v) {
-  v = wave_max_f(v);
-  if ((threadIdx.x & 63) == 0) sm.red_f[threadIdx.x >> 6] = v;
-  __syncthreads();
-  float r = sm.red_f[0];
-#pragma unroll
-  for (int w = 1; w < kWaves; ++w) r = fmaxf(r, sm.red_f[w]);
-  __syncthreads();
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+// One 16-byte read (16-byte aligned) at the point of coherence: the same
+// access an agent-scope atomic load makes (sc1), issued as one instruction,
+// so a thread fetches four exchange words in one round trip.  (The compiler
+// waits after every atomic load, so a sequence of them costs one round trip
+// each.)
+DEV u32x4 coh_load16(const void *p) {
+  u32x4 r;
+  asm volatile("global_load_dwordx4 %0, %1, off sc1\n\ts_waitcnt vmcnt(0)" : "=v"(r) : "v"(p) : "memory");
   return r;
 }
-// Fixed order: lanes by xor tree, waves in index order (deterministic).
+// Two such reads sharing one wait.
+DEV void coh_load16x2(const void *p0, const void *p1, u32x4 &a, u32x4 &b) {
+  asm volatile(
+      "global_load_dwordx4 %0, %2, off sc1\n\t"
+      "global_load_dwordx4 %1, %3, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(a), "=&v"(b)
+      : "v"(p0), "v"(p1)
+      : "memory");
+}
+// Three such reads sharing one wait.
+DEV void coh_load16x3(const void *p0, const void *p1, const void *p2, u32x4 &a, u32x4 &b, u32x4 &c) {
+  asm volatile(
+      "global_load_dwordx4 %0, %3, off sc1\n\t"
+      "global_load_dwordx4 %1, %4, off sc1\n\t"
+      "global_load_dwordx4 %2, %5, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c)
+      : "v"(p0), "v"(p1), "v"(p2)
+      : "memory");
+}
+DEV unsigned long long u64_of(uint32_t lo, uint32_t hi) { return ((unsigned long long)hi << 32) | lo; }
+DEV double f64_of(uint32_t lo, uint32_t hi) { return __longlong_as_double((long long)u64_of(lo, hi)); }
+
+// Wave-wide inclusive scans by DPP: row_shr:1,2,4,8 (Hillis-Steele within
+// each 16-lane row, lanes shifted in from outside the row read 0), then
+// row_bcast:15 into rows 1 and 3 and row_bcast:31 into rows 2 and 3.  The
+// combining order is fixed, so results are deterministic.
+template <int CTRL, int ROWS>
+DEV uint32_t dpp_mov(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, ROWS, 0xF, false);
+}
+#define DSTS_DPP_SCAN_STEPS(X) X(0x111, 0xF) X(0x112, 0xF) X(0x114, 0xF) X(0x118, 0xF) X(0x142, 0xA) X(0x143, 0xC)
+
+DEV uint32_t wave_scan_u32(uint32_t v) {
+#define X(C, R) v += dpp_mov<C, R>(v);
+  DSTS_DPP_SCAN_STEPS(X)
+#undef X
+  return v;
+}
+DEV unsigned long long wave_scan_u64(unsigned long long v) {
+#define X(C, R) v += u64_of(dpp_mov<C, R>((uint32_t)v), dpp_mov<C, R>((uint32_t)(v >> 32)));
+  DSTS_DPP_SCAN_STEPS(X)
+#undef X
+  return v;
+}
+DEV double wave_scan_f64(double v) {
+#define X(C, R)                                                                                              \
+  {                                                                                                          \
+    const unsigned long long b = (unsigned long long)__double_as_longlong(v);                                \
+    v += __longlong_as_double((long long)u64_of(dpp_mov<C, R>((uint32_t)b), dpp_mov<C, R>((uint32_t)(b >> 32)))); \
+  }
+  DSTS_DPP_SCAN_STEPS(X)
+#undef X
+  return v;
+}
+// running maximum (0 is the identity: unsigned keys)
+DEV unsigned long long wave_scanmax_u64(unsigned long long v) {
+#define X(C, R)                                                                        \
+  {                                                                                    \
+    const unsigned long long t = u64_of(dpp_mov<C, R>((uint32_t)v), dpp_mov<C, R>((uint32_t)(v >> 32))); \
+    v = t > v ? t : v;                                                                 \
+  }
+  DSTS_DPP_SCAN_STEPS(X)
+#undef X
+  return v;
+}
+DEV uint32_t wave_scanmax_u32(uint32_t v) {
+#define X(C, R)                              \
+  {                                          \
+    const uint32_t t = dpp_mov<C, R>(v);     \
+    v = t > v ? t : v;                       \
+  }
+  DSTS_DPP_SCAN_STEPS(X)
+#undef X
+  return v;
+}
+DEV uint32_t lane63_u32(uint32_t v) { return __builtin_amdgcn_readlane(v, 63); }
+DEV unsigned long long lane63_u64(unsigned long long v) {
+  return u64_of(__builtin_amdgcn_readlane((uint32_t)v, 63), __builtin_amdgcn_readlane((uint32_t)(v >> 32), 63));
+}
+DEV double wave_sum_d(double v) {
+  const unsigned long long b = (unsigned long long)__double_as_longlong(wave_scan_f64(v));
+  return __longlong_as_double((long long)lane63_u64(b));
+}
+DEV unsigned long long wave_max_u(unsigned long long v) { return lane63_u64(wave_scanmax_u64(v)); }
+// maximum of non-negative floats (their bit patterns order as integers)
+DEV float wave_max_nonneg_f(float v) { return __uint_as_float(lane63_u32(wave_scanmax_u32(__float_as_uint(v)))); }
+
+// Workgroup reductions (every thread gets the result).
+// Fixed order: lanes by the DPP scan, waves in index order (deterministic).
 DEV double wg_sum_d(SmemBase &sm, double v) {
   v = wave_sum_d(v);
-  if ((threadIdx.x & 63) == 0) sm.red_d[threadIdx.x >> 6] = v;
+  if ((tidx() & 63) == 0) sm.red_d[tidx() >> 6] = v;
   __syncthreads();
   double r = sm.red_d[0];
 #pragma unroll
@@ -133,11 +235,22 @@ DEV double wg_sum_d(SmemBase &sm, double v) {
 }
 DEV unsigned long long wg_max_u(SmemBase &sm, unsigned long long v) {
   v = wave_max_u(v);
-  if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
+  if ((tidx() & 63) == 0) sm.red_u[tidx() >> 6] = v;
   __syncthreads();
   unsigned long long r = sm.red_u[0];
 #pragma unroll
   for (int w = 1; w < kWaves; ++w) r = sm.red_u[w] > r ? sm.red_u[w] : r;
+  __syncthreads();
+  return r;
+}
+// Sum of one u64 per thread over the workgroup (exact).
+DEV unsigned long long wg_sum_u(SmemBase &sm, unsigned long long v) {
+  v = lane63_u64(wave_scan_u64(v));
+  if ((tidx() & 63) == 0) sm.red_u[tidx() >> 6] = v;
+  __syncthreads();
+  unsigned long long r = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) r += sm.red_u[w];
   __syncthreads();
   return r;
 }
@@ -152,9 +265,9 @@ DEV void wg_best(SmemBase &sm, double &g, int &idx) {
       idx = i2;
     }
   }
-  if ((threadIdx.x & 63) == 0) {
-    sm.red_d[threadIdx.x >> 6] = g;
-    sm.red_i[threadIdx.x >> 6] = idx;
+  if ((tidx() & 63) == 0) {
+    sm.red_d[tidx() >> 6] = g;
+    sm.red_i[tidx() >> 6] = idx;
   }
   __syncthreads();
   g = sm.red_d[0];
@@ -169,19 +282,36 @@ DEV void wg_best(SmemBase &sm, double &g, int &idx) {
   __syncthreads();
 }
 
-// Philox4x32-10 block for counter (c0..c3) and key (k0, k1).
+// Inclusive scan of one value per thread over the workgroup (fixed order).
+DEV uint32_t wave_scan(uint32_t v) { return wave_scan_u32(v); }
+DEV unsigned long long wave_scan(unsigned long long v) { return wave_scan_u64(v); }
+DEV double wave_scan(double v) { return wave_scan_f64(v); }
+template <typename T>
+DEV T block_scan_incl(T v, T *wave_tot) {
+  const int lane = tidx() & 63, w = tidx() >> 6;
+  v = wave_scan(v);
+  if (lane == 63) wave_tot[w] = v;
+  __syncthreads();
+  T base = 0;
+  for (int i = 0; i < w; ++i) base += wave_tot[i];
+  __syncthreads();
+  return v + base;
+}
+
+// Philox4x32-10 block for counter (c0..c3) and key (k0, k1); each round
+// takes both halves of the two 32x32-bit products.
 DEV void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1,
                        uint32_t out[4]) {
 #pragma unroll
   for (int r = 0; r < 10; ++r) {
-    const uint32_t lo_a = c0 * 0xD2511F53u, hi_a = __umulhi(c0, 0xD2511F53u);
-    const uint32_t lo_b = c2 * 0xCD9E8D57u, hi_b = __umulhi(c2, 0xCD9E8D57u);
-    const uint32_t n0 = hi_b ^ c1 ^ k0;
-    const uint32_t n2 = hi_a ^ c3 ^ k1;
+    const uint64_t pa = (uint64_t)c0 * 0xD2511F53u;
+    const uint64_t pb = (uint64_t)c2 * 0xCD9E8D57u;
+    const uint32_t n0 = (uint32_t)(pb >> 32) ^ c1 ^ k0;
+    const uint32_t n2 = (uint32_t)(pa >> 32) ^ c3 ^ k1;
     c0 = n0;
-    c1 = lo_b;
+    c1 = (uint32_t)pb;
     c2 = n2;
-    c3 = lo_a;
+    c3 = (uint32_t)pa;
     k0 += 0x9E3779B9u;
     k1 += 0xBB67AE85u;
   }
@@ -191,7 +321,6 @@ DEV void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint3
   out[3] = c3;
 }
 
-
 // Exp(1) from a 32-bit word, fp64: w = (x + 1/2) 2^-32, E = -ln(1 - w),
 // clamped below at FLT_MIN ([A] "Nine lines, and exactly one call site").
 DEV double exp1_f64(uint32_t x) {
@@ -199,18 +328,24 @@ DEV double exp1_f64(uint32_t x) {
   double e = -log1p(-w);
   return e < (double)FLT_MIN ? (double)FLT_MIN : e;
 }
-// ln E in fp32 (filter only).  For x >= 2^31 use 1 - w = (~x + 1/2) 2^-32,
-// which is exact in the integer complement.
-DEV float ln_exp1_f32(uint32_t x) {
-  float e;
-  if (x < 0x80000000u) {
-    const float w = ((float)x + 0.5f) * 0x1p-32f;
-    e = -log1pf(-w);
-  } else {
-    const float u = ((float)(~x) + 0.5f) * 0x1p-32f;
-    e = -logf(u);
-  }
-  return logf(e);
+
+// exp(y) for y <= 0 in fp64: y = k ln2/64 + r with |r| <= ln2/128 (ln2/64 in
+// two parts, the first exact in k * c), exp(r) by its degree-6 Taylor
+// polynomial (truncation below 3e-20 relative), times 2^(k mod 64 / 64)
+// from the table and 2^(k div 64).  y below -800 gives 0.
+DEV double exp_nonpos(const double *tab, double y) {
+  y = y < -800.0 ? -800.0 : y;
+  const double kd = rint(y * 92.332482616893656);
+  const double r = fma(-kd, -0x1.718432a1b0e26p-41, fma(-kd, 0x1.62e42ffp-7, y));
+  double p = 1.0 / 720.0;
+  p = fma(p, r, 1.0 / 120.0);
+  p = fma(p, r, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  const int k = (int)kd;
+  return ldexp(tab[k & 63] * p, k >> 6);
 }
 
 // Penalties on one logit ([C] "解码一步里采样做什么", _apply_penalties):
@@ -222,6 +357,20 @@ DEV float apply_penalty(float x, uint32_t cnt, const RowParam &P) {
   const float fc = P.freq * (float)cnt;
   const float t2 = t1 - fc;
   return t2 - P.pres;
+}
+
+// z = x / T, correctly rounded: q = x (1/T), then one FMA correction with
+// the exact remainder (Markstein), valid while |q| lies in [2^-100, 2^100];
+// elsewhere (and for infinities and zeros) the IEEE division.  -0 -> +0, so
+// equal values share one key.  (The transform loop inlines the same
+// computation with the out-of-range branch taken per group of four.)
+DEV float div_temp(float x, float T, float rT) {
+  const float q = x * rT;
+  const float aq = fabsf(q);
+  float z;
+  if (__builtin_expect(aq >= 0x1p-100f && aq <= 0x1p100f, 1)) z = __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q);
+  else z = x / T;
+  return z + 0.0f;
 }
 
 template <typename TIn>
@@ -259,27 +408,39 @@ struct Loader<uint16_t> {
 };
 
 // ---------------------------------------------------------------- group sync
-// Exchange data is written with agent-scope stores; every wave drains its
-// memory counters before the workgroup barrier, then one thread fences
-// (agent-scope release, once per workgroup) and arrives.  Waiters poll the
-// generation word with relaxed loads and take one acquire fence when it
-// moves.  The last arrival resets the count, so the words are reusable
-// without clearing.
+// Every word that workgroups exchange (slots, group records, barrier words)
+// is read and written only with relaxed agent-scope atomics, which on gfx950
+// go to the point of coherence instead of a per-XCD cache.  Ordering between
+// them therefore needs no cache maintenance: a signalling workgroup waits
+// for its own stores to complete (vmcnt 0 in every wave, then a workgroup
+// barrier) before its signal, and a waiting workgroup issues its data loads
+// only after the signal load has returned.  Agent-scope fences would also
+// write back and invalidate the whole L2 (several microseconds per barrier)
+// and are not used.
 DEV void mem_quiesce() { __builtin_amdgcn_s_waitcnt(0); }
+DEV void order_release() {
+  mem_quiesce();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+}
+DEV void order_acquire() {
+  mem_quiesce();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+}
 
 // Returns true in exactly one workgroup, the last to arrive, which merges
 // the exchange and then calls group_release; the others call group_wait.
+// The last arrival resets the count, so the words are reusable without
+// clearing.
 DEV bool group_arrive(SmemBase &sm, GroupSync *s, int G) {
-  mem_quiesce();
+  order_release();
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (tidx() == 0) {
     const uint32_t g0 = __hip_atomic_load(&s->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const uint32_t old = __hip_atomic_fetch_add(&s->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const bool last = old == (uint32_t)G - 1u;
     if (last) {
       __hip_atomic_store(&s->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      order_acquire();
     }
     sm.bu[14] = g0;
     sm.bu[15] = last ? 1u : 0u;
@@ -291,12 +452,9 @@ DEV bool group_arrive(SmemBase &sm, GroupSync *s, int G) {
 }
 
 DEV void group_release(GroupSync *s) {
-  mem_quiesce();
+  order_release();
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-    __hip_atomic_fetch_add(&s->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tidx() == 0) __hip_atomic_fetch_add(&s->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The wait is bounded (~2 s): on expiry the launch is marked aborted (the
@@ -305,7 +463,7 @@ DEV void group_release(GroupSync *s) {
 // the device.
 constexpr uint32_t kSpinLimit = 1u << 26;
 DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t epoch) {
-  if (threadIdx.x == 0) {
+  if (tidx() == 0) {
     const uint32_t g0 = sm.bu[14];
     uint32_t spins = 0;
     while (__hip_atomic_load(&s->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
@@ -316,7 +474,7 @@ DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t e
       }
       __builtin_amdgcn_s_sleep(1);
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    order_acquire();
   }
   __syncthreads();
 }
@@ -325,37 +483,6 @@ DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t e
 DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch) {
   if (group_arrive(sm, s, G)) group_release(s);
   else group_wait(sm, s, abort_word, epoch);
-}
-
-// ---------------------------------------------------------------- block scans
-// Inclusive scan of one value per thread over the workgroup (fixed order).
-template <typename T>
-DEV T block_scan_incl(T v, T *wave_tot) {
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const T t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
-  if (lane == 63) wave_tot[w] = v;
-  __syncthreads();
-  T base = 0;
-  for (int i = 0; i < w; ++i) base += wave_tot[i];
-  __syncthreads();
-  return v + base;
-}
-
-// Sum of one u64 per thread over the workgroup (exact).
-DEV unsigned long long wg_sum_u(SmemBase &sm, unsigned long long v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
-  if ((threadIdx.x & 63) == 0) sm.red_u[threadIdx.x >> 6] = v;
-  __syncthreads();
-  unsigned long long r = 0;
-#pragma unroll
-  for (int w = 0; w < kWaves; ++w) r += sm.red_u[w];
-  __syncthreads();
-  return r;
 }
 
 // Per-row context shared by the phases.
@@ -372,21 +499,32 @@ struct RowCtx {
 
 DEV void row_barrier(SmemBase &sm, RowCtx &rc) { group_barrier(sm, rc.gsync, rc.G, rc.abort_word, rc.epoch); }
 
-// Window bin of a value: d = max - z in 1/16-nat steps, kWinBins past 32
-// nats.  Monotone in z, so the bins partition the value axis in order.
-DEV int win_bin(float mf, float z) {
-  const float d = mf - z;
-  return d < 32.0f ? (int)(d * kBinsPerNat) : kWinBins;
+// Window bin of a value: its distance d = max - z, scaled by wsc =
+// min(1, T) (so the window spans at least 16 nats of the logits themselves,
+// whatever the temperature), in 1/32 steps; kWinBins from 16 on.  Monotone
+// in z, so the bins partition the value axis in order.  Every bin of the
+// kernel is computed by this expression.
+DEV float win_dist(float mf, float z, float wsc) { return (mf - z) * wsc; }
+DEV int win_bin(float mf, float z, float wsc) {
+  const float dd = win_dist(mf, z, wsc);
+  return dd < kWinNats ? (int)(dd * kBinsPerNat) : kWinBins;
 }
 
-// exp(-d) for d >= 0 as 2^-44 fixed point (fp32 exp; exact scaling by 2^12
-// and 2^32, truncating conversions).
-DEV unsigned long long mass_fixed(float d) {
-  const float q = expf(-d);
-  const float a = q * 4096.0f;
-  const uint32_t hi = (uint32_t)a;
-  const uint32_t lo = (uint32_t)((a - (float)hi) * 4294967296.0f);
-  return ((unsigned long long)hi << 32) | lo;
+// Window histogram entry of one value at distance d = max - z: a count of
+// one in bits 48.. and the mass exp(-d) in 2^-31 units (2^(31 - d log2 e)
+// by the hardware exp2, relative error ~1e-6, rounded to an integer) below;
+// a workgroup's bin holds at most 2^15 values, so neither field overflows.
+// These masses only place thresholds in bins and sum the bins above a
+// threshold.
+DEV float mass_scaled(float d) { return __builtin_amdgcn_exp2f(__builtin_fmaf(-d, kLog2e, 31.0f)); }
+DEV unsigned long long hist_entry(float a) {
+  return (1ull << 48) | (unsigned long long)(uint32_t)__builtin_rintf(a);
+}
+
+// Candidate order key: value key << 32 | ~index (descending key order is
+// (value desc, index asc); 0 never occurs for a real value).
+DEV unsigned long long cand_key(float z, int idx) {
+  return ((unsigned long long)fkey(z) << 32) | (uint32_t)(~(uint32_t)idx);
 }
 
 // ---------------------------------------------------------------- general path
@@ -398,26 +536,27 @@ DEV unsigned long long mass_fixed(float d) {
 //   MASS:  the largest key t whose cumulative mass C(t) = sum_{key >= t}
 //          exp(z - m) reaches p * C(lower), in 2^-44 fixed point.
 // Padding values are -inf: lowest bin, zero mass, so they never move a
-// threshold above -inf.
+// threshold above -inf.  The digit is found in parallel over the 256 bins
+// (thread t holds bin 255 - t, so an inclusive scan runs from the top).
 template <bool MASS>
 DEV uint32_t radix_select(SmemBase &sm, RowCtx &rc, const float *zs, unsigned char *region, uint32_t lower,
                           uint32_t k, double p, double m) {
   uint32_t *hcnt = reinterpret_cast<uint32_t *>(region);
-  uint32_t *mcnt = hcnt + 256;
-  unsigned long long *hmass = reinterpret_cast<unsigned long long *>(mcnt + 256);
-  unsigned long long *mmass = hmass + 256;
+  unsigned long long *hmass = reinterpret_cast<unsigned long long *>(region + 1024);
+  unsigned long long *cum = reinterpret_cast<unsigned long long *>(region + 3072);
+  const int tid = tidx();
   uint32_t prefix = 0, mask = 0;
-  uint32_t rem_cnt = k;
+  uint32_t rem = k;
   unsigned long long above = 0;
   double target = 0.0;
   for (int round = 0; round < 4; ++round) {
     const int shift = 24 - 8 * round;
-    for (int b = threadIdx.x; b < 256; b += kBlock) {
+    for (int b = tid; b < 256; b += kBlock) {
       hcnt[b] = 0;
       hmass[b] = 0;
     }
     __syncthreads();
-    for (int l = 4 * threadIdx.x; l < rc.n4; l += 4 * kBlock) {
+    for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
       const f32x4 v = *reinterpret_cast<const f32x4 *>(zs + l);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
@@ -425,72 +564,40 @@ DEV uint32_t radix_select(SmemBase &sm, RowCtx &rc, const float *zs, unsigned ch
         const uint32_t key = fkey(zz);
         if (key >= lower && (key & mask) == prefix) {
           const uint32_t bin = (key >> shift) & 0xFFu;
-          if (MASS) atomicAdd(&hmass[bin], (unsigned long long)(exp((double)zz - m) * kMassScale));
+          if (MASS) atomicAdd(&hmass[bin], (unsigned long long)(exp_nonpos(sm.exp_tab, (double)zz - m) * kMassScale));
           else atomicAdd(&hcnt[bin], 1u);
         }
       }
     }
     __syncthreads();
     const unsigned par = (*rc.xseq)++ & 1u;
-    for (int b = threadIdx.x; b < 256; b += kBlock) {
+    for (int b = tid; b < 256; b += kBlock) {
       if (MASS) atomic_st(&rc.my->hmass[par][b], hmass[b]);
       else atomic_st(&rc.my->hcnt[par][b], hcnt[b]);
     }
     row_barrier(sm, rc);
-    for (int b = threadIdx.x; b < 256; b += kBlock) {
-      if (MASS) {
-        unsigned long long t = 0;
-        for (int g = 0; g < rc.G; ++g) t += atomic_ld(&rc.peers[g].hmass[par][b]);
-        mmass[b] = t;
-      } else {
-        uint32_t t = 0;
-        for (int g = 0; g < rc.G; ++g) t += atomic_ld(&rc.peers[g].hcnt[par][b]);
-        mcnt[b] = t;
-      }
+    unsigned long long v = 0;
+    if (tid < 256)
+      for (int g = 0; g < rc.G; ++g)
+        v += MASS ? atomic_ld(&rc.peers[g].hmass[par][255 - tid]) : (unsigned long long)atomic_ld(&rc.peers[g].hcnt[par][255 - tid]);
+    const unsigned long long incl = block_scan_incl<unsigned long long>(v, sm.red_u);
+    if (tid < 256) cum[tid] = incl;
+    if (MASS && round == 0 && tid == 255) sm.bd[0] = p * (double)incl;
+    if (tid == 0) sm.bu[0] = 255;
+    __syncthreads();
+    if (MASS && round == 0) target = sm.bd[0];
+    if (tid < 256) {
+      auto pred = [&](int t) {
+        return t == 255 || (MASS ? ((double)(above + cum[t]) >= target) : (cum[t] >= (unsigned long long)rem));
+      };
+      if (pred(tid) && (tid == 0 || !pred(tid - 1))) sm.bu[0] = (uint32_t)tid;
     }
     __syncthreads();
-    if (threadIdx.x == 0) {
-      uint32_t digit = 0;
-      if (MASS) {
-        if (round == 0) {
-          unsigned long long tot = 0;
-          for (int b = 0; b < 256; ++b) tot += mmass[b];
-          target = p * (double)tot;
-        }
-        unsigned long long acc = above;
-        for (int b = 255; b >= 0; --b) {
-          const unsigned long long nxt = acc + mmass[b];
-          if ((double)nxt >= target || b == 0) {
-            digit = (uint32_t)b;
-            break;
-          }
-          acc = nxt;
-        }
-        sm.bd[0] = target;
-        sm.bu[1] = (uint32_t)(acc & 0xFFFFFFFFu);
-        sm.bu[2] = (uint32_t)(acc >> 32);
-      } else {
-        uint32_t acc = 0;
-        for (int b = 255; b >= 0; --b) {
-          if (acc + mcnt[b] >= rem_cnt || b == 0) {
-            digit = (uint32_t)b;
-            break;
-          }
-          acc += mcnt[b];
-        }
-        sm.bu[1] = rem_cnt - acc;
-      }
-      sm.bu[0] = digit;
-    }
-    __syncthreads();
-    const uint32_t digit = sm.bu[0];
-    if (MASS) {
-      target = sm.bd[0];
-      above = ((unsigned long long)sm.bu[2] << 32) | sm.bu[1];
-    } else {
-      rem_cnt = sm.bu[1];
-    }
-    prefix |= digit << shift;
+    const int t = (int)sm.bu[0];
+    const unsigned long long before = t > 0 ? cum[t - 1] : 0ull;
+    if (MASS) above += before;
+    else rem -= (uint32_t)before;
+    prefix |= (uint32_t)(255 - t) << shift;
     mask |= 0xFFu << shift;
     __syncthreads();
   }
@@ -500,10 +607,11 @@ DEV uint32_t radix_select(SmemBase &sm, RowCtx &rc, const float *zs, unsigned ch
 // Packed hash entry: slice-local index << 13 | count.
 DEV uint32_t hash_slot(uint32_t local, uint32_t slots) { return (local * 2654435761u) & (slots - 1u); }
 
-// min-p keeps exp(z - m) >= min_p (fp64).  That set is an upper set of keys;
-// its boundary key is the smallest key passing the same test, found from the
-// closed-form guess m + ln(min_p) by bracketing and bisection.
-DEV uint32_t min_p_key(double m, float min_p) {
+// min-p keeps exp(z - m) >= min_p (fp64).  That set is an upper set of keys
+// (keys above the max's count as passing); its boundary is the smallest
+// passing key.  Serial form: from the closed-form guess m + ln(min_p),
+// bracket and bisect.
+DEV uint32_t min_p_key_serial(double m, float min_p) {
   const double mp = (double)min_p;
   auto pass = [&](uint32_t k) { return exp((double)key_to_float(k) - m) >= mp; };
   const uint32_t top = fkey((float)m);  // passes: exp(0) = 1 >= min_p
@@ -540,107 +648,54 @@ DEV uint32_t min_p_key(double m, float min_p) {
   return hi;
 }
 
+// Parallel form: the boundary lies within a few keys of the guess, so 128
+// threads test the keys around it; outside that span, the serial search.
+DEV uint32_t min_p_key(SmemBase &sm, double m, float min_p) {
+  constexpr int kSpan = 128;
+  const int tid = tidx();
+  const double mp = (double)min_p;
+  const uint32_t top = fkey((float)m);
+  uint32_t g = fkey((float)(m + log(mp)));
+  if (g > top) g = top;
+  const int64_t k0 = (int64_t)g - kSpan / 2;
+  auto pass = [&](int64_t k) {
+    if (k > (int64_t)top) return true;
+    if (k < 0) return false;
+    return exp((double)key_to_float((uint32_t)k) - m) >= mp;
+  };
+  if (tid == 0) sm.bu[20] = kNone;
+  __syncthreads();
+  if (tid < kSpan) {
+    const int64_t k = k0 + tid;
+    if (tid > 0 && pass(k) && !pass(k - 1)) sm.bu[20] = (uint32_t)k;
+  }
+  __syncthreads();
+  uint32_t r = sm.bu[20];
+  __syncthreads();
+  if (r == kNone) {  // boundary outside the span (or at its first key)
+    if (tid == 0) sm.bu[20] = min_p_key_serial(m, min_p);
+    __syncthreads();
+    r = sm.bu[20];
+    __syncthreads();
+  }
+  return r;
+}
+
 // Decision words of GroupRec::dec
 enum : int {
-  D_FLAGS = 0,  // bit 0: general path; bit 1: [0, RKHI] gathered whole (top-k prefix)
-  D_R0HI = 1,   // gathered bins: [0, R0HI] (top logprobs), [R1LO, R1HI] (top-p crossing),
-  D_R1LO = 2,   //   [RKLO, RKHI] (top-k crossing bin, or the whole top-k prefix), BM (min-p boundary)
-  D_R1HI = 3,
-  D_RKLO = 4,
-  D_RKHI = 5,
-  D_BM = 6,
-  D_TAU = 7,
+  D_FLAGS = 0,  // bit 0: general path; bit 1: [0, RKHI] gathered whole (top-k prefix);
+                //   bit 2: the k-th value lies deeper than min-p's boundary (top-k has no effect)
+  D_TAU = 1,
+  D_LNS = 2,    // 2 words: ln of the kept-set sum (fp64 bits)
+  D_R0HI = 4,   // gathered bins: [0, R0HI] (top logprobs), [R1LO, R1HI] (top-p crossing),
+  D_R1LO = 5,   //   [RKLO, RKHI] (top-k crossing bin, or the whole top-k prefix), BM (min-p boundary)
+  D_R1HI = 6,
+  D_RKLO = 7,
+  D_RKHI = 8,
+  D_BM = 9,
+  D_MASK = 16,  // 16 words: bitmask of the gathered bins
 };
-
-// Ranges of window bins whose values are gathered (hi < lo: empty).
-struct CandRanges {
-  int r0hi, r1lo, r1hi, rklo, rkhi, bm;
-  DEV bool has(int b) const {
-    return b <= r0hi || (b >= r1lo && b <= r1hi) || (b >= rklo && b <= rkhi) || b == bm;
-  }
-};
-
-// Exchange-2 decisions, by one thread of the merging workgroup, from the
-// merged inclusive prefix counts lc[0..kWinBins] and masses lm[0..kMassBins]
-// (LDS; the last entry of each includes the values deeper than the window).
-DEV void decide_window(GroupRec *rec, const uint32_t *lc, const unsigned long long *lm, const RowParam &P,
-                       bool topk, bool topp, bool minp, bool need_thr, int K, float mf, uint32_t t_m, double S_all) {
-  uint32_t flags = 0;
-  auto cc = [&](int b) { return b < 0 ? 0u : lc[b < kWinBins ? b : kWinBins]; };
-  auto cm = [&](int b) { return b < 0 ? 0.0 : (double)lm[b < kMassBins ? b : kMassBins]; };
-  auto bin_for_count = [&](uint32_t want) {  // first bin reaching `want`; kWinBins + 1 if none
-    if (lc[kWinBins] < want) return kWinBins + 1;
-    int lo = 0, hi = kWinBins;
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if (lc[mid] >= want) hi = mid;
-      else lo = mid + 1;
-    }
-    return lo;
-  };
-  auto bin_for_mass = [&](double want) {  // first mass bin reaching `want`; kMassBins: the deep values
-    int lo = 0, hi = kMassBins;
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if ((double)lm[mid] >= want) hi = mid;
-      else lo = mid + 1;
-    }
-    return lo;
-  };
-  int r0hi = -1, r1lo = 1, r1hi = 0, rklo = 1, rkhi = 0, bm = -1;
-  if (K > 0) r0hi = min(bin_for_count((uint32_t)K), kWinBins);
-  int bk = -1;
-  if (topk) {
-    bk = bin_for_count((uint32_t)P.top_k);
-    if (cc(bk) <= (uint32_t)kCandCap) {  // the whole top-k prefix fits: gather it
-      flags |= 2u;
-      rklo = 0;
-      rkhi = bk;
-    } else if (bk < kMassBins) {
-      rklo = rkhi = bk;
-    } else {
-      flags |= 1u;
-    }
-  }
-  if (topp && !(flags & 1u)) {
-    double clo, chi;
-    if (topk) {
-      clo = cm(min(bk, kMassBins) - 1);
-      chi = bk < kMassBins ? cm(bk) : cm(kMassBins);
-    } else {
-      clo = chi = cm(kMassBins);
-    }
-    r1lo = bin_for_mass((double)P.top_p * clo);
-    r1hi = bin_for_mass((double)P.top_p * chi);
-    if (r1hi >= kMassBins) flags |= 1u;
-    if (topk) {
-      r1lo = min(r1lo, bk);
-      r1hi = min(r1hi, bk);
-    }
-  }
-  if (minp && !(flags & 1u)) {
-    bm = win_bin(mf, key_to_float(t_m));
-    if (bm >= kMassBins && !((flags & 2u) && bm <= rkhi)) flags |= 1u;
-  }
-  if (!(flags & 1u) && need_thr) {
-    // values to gather: the union of the ranges, counted bin by bin
-    uint32_t n = 0;
-    for (int b = 0; b <= kWinBins; ++b) {
-      const bool in = b <= r0hi || (b >= r1lo && b <= r1hi) || (b >= rklo && b <= rkhi) || b == bm;
-      if (in) n += cc(b) - cc(b - 1);
-    }
-    if (n > (uint32_t)kCandCap) flags |= 1u;
-  }
-  atomic_st(&rec->dec[D_FLAGS], flags);
-  atomic_st(&rec->dec[D_R0HI], (uint32_t)r0hi);
-  atomic_st(&rec->dec[D_R1LO], (uint32_t)r1lo);
-  atomic_st(&rec->dec[D_R1HI], (uint32_t)r1hi);
-  atomic_st(&rec->dec[D_RKLO], (uint32_t)rklo);
-  atomic_st(&rec->dec[D_RKHI], (uint32_t)rkhi);
-  atomic_st(&rec->dec[D_BM], (uint32_t)bm);
-  atomic_st(&rec->dd[0], S_all);
-  atomic_st(&rec->cand_n, 0u);
-}
+static_assert(D_MASK + kWinBins / 32 <= (int)(sizeof(GroupRec::dec) / sizeof(uint32_t)), "decision words");
 
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
@@ -650,18 +705,17 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   static_assert(sizeof(SmemBase) % 16 == 0, "the LDS slice must be 16-byte aligned");
   float *zs = reinterpret_cast<float *>(lds_raw + sizeof(SmemBase));
   unsigned char *region = reinterpret_cast<unsigned char *>(zs + kp.slice);
-  // region views (used one at a time)
+  // region views (see the layout above)
   uint32_t *hash = reinterpret_cast<uint32_t *>(region);
   uint32_t *bitmap = hash + kp.hash_slots;
-  unsigned long long *wm = reinterpret_cast<unsigned long long *>(region);              // [kMassBins + 1]
-  uint32_t *wc = reinterpret_cast<uint32_t *>(wm + (kMassBins + 1));                     // [kWinBins + 1]
-  float *cz = reinterpret_cast<float *>(wc + (kWinBins + 4));                            // leader: candidates
-  int32_t *ci = reinterpret_cast<int32_t *>(cz + kCandCap);
-  float *sz = reinterpret_cast<float *>(ci + kCandCap);
-  int32_t *si = reinterpret_cast<int32_t *>(sz + kCandCap);
-  double *sq = reinterpret_cast<double *>(si + kCandCap);
+  uint32_t *lc = reinterpret_cast<uint32_t *>(region);
+  unsigned long long *lm = reinterpret_cast<unsigned long long *>(region + kRegionLm);
+  unsigned char *regB = region + kRegionB;
+  unsigned long long *wh = reinterpret_cast<unsigned long long *>(regB);
+  unsigned long long *stage = reinterpret_cast<unsigned long long *>(regB);
+  unsigned long long *sk = reinterpret_cast<unsigned long long *>(regB);
+  double *sq = reinterpret_cast<double *>(regB + 8 * kCandCap);
 
-  const int tid = threadIdx.x;
   const int G = kp.G;
   const int gid = blockIdx.x % G;
   const int group = blockIdx.x / G;
@@ -687,6 +741,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   rc.s0 = s0;
   rc.n = s1 - s0;
   rc.n4 = (rc.n + 3) & ~3;
+  for (int j = tidx(); j < 64; j += kBlock) sm.exp_tab[j] = exp2((double)j * (1.0 / 64.0));
+  __syncthreads();
 
   unsigned it = 0;
   for (int row = group; row < kp.n_rows; row += kp.n_groups, ++it) {
@@ -699,13 +755,24 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const bool topp = !greedy && (P.flags & RF_TOPP);
     const bool minp = !greedy && (P.flags & RF_MINP);
     const bool truncated = topk || topp || minp;
+    // the slice bounds, opaque per row: keeps per-element offsets and
+    // compares from being hoisted out of the row loop (they would stay
+    // live across it)
+    int ln = __builtin_amdgcn_readfirstlane(rc.n);
+    asm volatile("" : "+s"(ln));
+    const int ln4 = (ln + 3) & ~3;
+    // the thread index, opaque per row for the same reason (addresses
+    // derived from it are recomputed per row)
+    const int tid = tidx();
+    const int lane = tid & 63, wave = tid >> 6;
 
     // ---- 1. issue the history and logit loads, build the penalty counts
-    // while they are in flight, then sanitise, penalise and divide by the
-    // temperature into the LDS slice.  Loads use clamped in-bounds
-    // addresses; with vector loads the row stride is a multiple of 4, so a
-    // group starting below s1 lies inside the row.
+    // while they are in flight, then sanitise and divide by the temperature
+    // as each batch lands.  Loads use clamped in-bounds addresses; with
+    // vector loads the row stride is a multiple of 4, so a group starting
+    // below s1 lies inside the row.
     int32_t hv[kMaxHistPerRow / kBlock];
+    int32_t osl[kMaxHistPerRow / kBlock];  // hash slot of an entry this thread created, else -1
     if (pen) {
       const int32_t *hist = kp.history_ids + P.hist_start;
 #pragma unroll
@@ -716,126 +783,145 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     }
     constexpr int kBatch = kMaxSlice / (4 * kBlock);
     float v[kBatch][4];
-    {
-      // opaque per row: keeps the per-load offsets from being hoisted out of
-      // the row loop (they would stay live across it and spill)
-      int ln = __builtin_amdgcn_readfirstlane(rc.n);
-      asm volatile("" : "+s"(ln));
-      const int64_t rbase = (int64_t)row * kp.row_stride + s0;
-      const int lastg = (ln - 1) & ~3;
-#pragma unroll
-      for (int b = 0; b < kBatch; ++b) {
-        const int l = 4 * tid + 4 * kBlock * b;
-        if (kp.vec_ok & 1) {
-          Loader<TIn>::load4(kp.logits, rbase + min(l, lastg), v[b]);
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) v[b][c] = Loader<TIn>::load1(kp.logits, rbase + min(l + c, ln - 1));
-        }
-      }
-    }
-    if (pen) {
-      for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
-      for (int t = tid; t < (rc.n4 + 31) / 32; t += kBlock) bitmap[t] = 0;
-      __syncthreads();
-#pragma unroll
-      for (int q = 0; q < kMaxHistPerRow / kBlock; ++q) {
-        const int32_t id = hv[q];
-        if (id >= s0 && id < s1) {
-          const uint32_t local = (uint32_t)(id - s0);
-          uint32_t sl = hash_slot(local, hslots);
-          while (true) {
-            const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
-            if (prev == kEmpty) break;
-            if ((prev >> 13) == local) {
-              atomicAdd(&hash[sl], 1u);
-              break;
-            }
-            sl = (sl + 1u) & (hslots - 1u);
-          }
-          atomicOr(&bitmap[local >> 5], 1u << (local & 31));
-        }
-      }
-    }
-    // raw values -> LDS (slots past the slice end: -inf)
-#pragma unroll
-    for (int b = 0; b < kBatch; ++b) {
-      const int l = 4 * tid + 4 * kBlock * b;
-      if (l < rc.n4) {
-        f32x4 o;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) o[c] = (l + c < rc.n) ? v[b][c] : -INFINITY;
-        *reinterpret_cast<f32x4 *>(zs + l) = o;
-      }
-    }
-    __syncthreads();
-    // z = x / T, correctly rounded: q = x (1/T), then one FMA correction
-    // with the exact remainder (Markstein), valid while q stays in the
-    // normal range; elsewhere (and for infinities) the IEEE division.
+    const int64_t rbase = (int64_t)row * kp.row_stride + s0;
+    const bool vec = kp.vec_ok & 1;
     const float T = P.temperature;
     const float rT = 1.0f / T;
     float lmax = -INFINITY;
-    int lidx = 0x7FFFFFFF;  // first index of the local max (slots are visited in index order)
-    for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
-      f32x4 o = *reinterpret_cast<const f32x4 *>(zs + l);
-      const uint32_t pb = pen ? (bitmap[l >> 5] >> (l & 31)) & 0xFu : 0u;
+    int lidx = 0x7FFFFFFF;  // first index of the local max (visited in index order)
+    // the penalty counts are built while the loads are in flight; each path
+    // below is straight-line code from its loads to their uses
+    auto build_and_transform = [&]() {
+      if (pen) {
+        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+        for (int t = tid; t < (ln4 + 31) / 32; t += kBlock) bitmap[t] = 0;
+        __syncthreads();
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        float x = o[c];
-        x = (x == x) ? x : -INFINITY;
-        if ((pb >> c) & 1u) {
-          const uint32_t local = (uint32_t)(l + c);
-          uint32_t sl = hash_slot(local, hslots);
-          while ((hash[sl] >> 13) != local) sl = (sl + 1u) & (hslots - 1u);
-          x = apply_penalty(x, hash[sl] & 0x1FFFu, P);
+        for (int q = 0; q < kMaxHistPerRow / kBlock; ++q) {
+          const int32_t id = hv[q];
+          osl[q] = -1;
+          if (id >= s0 && id < s1) {
+            const uint32_t local = (uint32_t)(id - s0);
+            uint32_t sl = hash_slot(local, hslots);
+            while (true) {
+              const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
+              if (prev == kEmpty) {
+                osl[q] = (int32_t)sl;
+                break;
+              }
+              if ((prev >> 13) == local) {
+                atomicAdd(&hash[sl], 1u);
+                break;
+              }
+              sl = (sl + 1u) & (hslots - 1u);
+            }
+            atomicOr(&bitmap[local >> 5], 1u << (local & 31));
+          }
         }
-        const float q = x * rT;
-        const float aq = fabsf(q);
-        float zz;
-        if (aq >= 0x1p-100f && aq <= 0x1p100f) zz = __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q);
-        else zz = x / T;
-        zz = zz + 0.0f;  // -0 -> +0: equal values share one key
-        o[c] = zz;
-        if (zz > lmax) {
-          lmax = zz;
-          lidx = s0 + l + c;
+        __syncthreads();
+      }
+      // z = x / T as each batch lands, into the LDS slice (slots past the
+      // slice end: -inf); a penalised element keeps its raw value until the
+      // penalty pass
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int l = 4 * tid + 4 * kBlock * b;
+        if (l < ln4) {
+          const uint32_t pb = pen ? (bitmap[l >> 5] >> (l & 31)) & 0xFu : 0u;
+          float xs[4], zq[4];
+          bool slow = false;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float xv = v[b][c];
+            const float x = (xv == xv && l + c < ln) ? xv : -INFINITY;
+            xs[c] = x;
+            const float q = x * rT;
+            const bool fine = fabsf(q) >= 0x1p-100f && fabsf(q) <= 0x1p100f;
+            // outside that range infinities and zeros divide to themselves; a
+            // finite nonzero x goes to the IEEE division below (rare)
+            slow |= !fine && __builtin_amdgcn_classf(x, 0x198);
+            zq[c] = fine ? __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q) : x;
+          }
+          if (slow) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) zq[c] = xs[c] / T;
+          }
+          f32x4 o;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float zz = zq[c] + 0.0f;  // -0 -> +0: equal values share one key
+            const bool raw = (pb >> c) & 1u;
+            o[c] = raw ? xs[c] : zz;
+            if (!raw && zz > lmax) {
+              lmax = zz;
+              lidx = s0 + l + c;
+            }
+          }
+          *reinterpret_cast<f32x4 *>(zs + l) = o;
         }
       }
-      *reinterpret_cast<f32x4 *>(zs + l) = o;
+    };
+    // vector loads in issue order (batch b is later waited for with the
+    // batches behind it still in flight), or scalar loads for unaligned rows
+    if (vec) {
+      const int lastg = (ln - 1) & ~3;
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        Loader<TIn>::load4(kp.logits, rbase + min(4 * tid + 4 * kBlock * b, lastg), v[b]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      build_and_transform();
+    } else {
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b)
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[b][c] = Loader<TIn>::load1(kp.logits, rbase + min(4 * tid + 4 * kBlock * b + c, ln - 1));
+      build_and_transform();
+    }
+    if (pen) {
+      __syncthreads();
+      // the thread that created a history id's entry penalises that value
+      // once, with the final count
+#pragma unroll
+      for (int q = 0; q < kMaxHistPerRow / kBlock; ++q) {
+        if (osl[q] >= 0) {
+          const uint32_t e = hash[osl[q]];
+          const uint32_t local = e >> 13;
+          const float x = apply_penalty(zs[local], e & 0x1FFFu, P);
+          const float zz = div_temp(x, T, rT);
+          zs[local] = zz;
+          const int idx = s0 + (int)local;
+          if (zz > lmax || (zz == lmax && idx < lidx)) {
+            lmax = zz;
+            lidx = idx;
+          }
+        }
+      }
     }
 
-    // ---- 2. exchange 1: row max and first argmax
-    const float wmax = wg_max_f(sm, lmax);
-    const unsigned long long wam =
-        wg_max_u(sm, lmax == wmax && lmax > -INFINITY ? ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx) : 0ull);
+    // ---- 2. exchange 1: row max and first argmax, as one order key
+    // (value key << 32 | ~index: the largest key is the first argmax)
+    const unsigned long long wam = wg_max_u(sm, ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx));
     const unsigned par = it & 1u;
-    if (tid == 0) {
-      atomic_st(&rc.my->small[par][0], (double)wmax);
-      atomic_st(&rc.my->small[par][1], __longlong_as_double((long long)wam));
-    }
+    if (tid == 0) atomic_st(&rc.my->e1[par][0], wam);
     row_barrier(sm, rc);
-    if (tid == 0) {
-      double gm = -INFINITY;
-      unsigned long long am = 0;
-      for (int g = 0; g < G; ++g) {
-        gm = fmax(gm, atomic_ld(&rc.peers[g].small[par][0]));
-        const unsigned long long a = (unsigned long long)__double_as_longlong(atomic_ld(&rc.peers[g].small[par][1]));
-        am = a > am ? a : am;
+    if (wave == 0) {
+      unsigned long long a = lane < G ? atomic_ld(&rc.peers[lane].e1[par][0]) : 0ull;
+      a = wave_max_u(a);
+      if (lane == 0) {
+        sm.bd[0] = (double)key_to_float((uint32_t)(a >> 32));
+        sm.bu[0] = 0xFFFFFFFFu - (uint32_t)(a & 0xFFFFFFFFu);
       }
-      sm.bd[0] = gm;
-      sm.bu[0] = 0xFFFFFFFFu - (uint32_t)(am & 0xFFFFFFFFu);
-      if (minp && gm > -INFINITY && gm < INFINITY) sm.bu[3] = min_p_key(gm, P.min_p);
     }
     __syncthreads();
     const double m = sm.bd[0];
     const int argmax_idx = (int)sm.bu[0];
-    const uint32_t t_m = minp ? sm.bu[3] : 0u;
     __syncthreads();
 
     // ---- rows with no finite logit (status 1) or a +inf value (status 2)
     if (!(m > -INFINITY) || m == INFINITY) {
       if (want_out) {
-        for (int l = tid; l < rc.n; l += kBlock) {
+        for (int l = tid; l < ln; l += kBlock) {
           if (kp.probs) kp.probs[(int64_t)row * V + s0 + l] = 0.0f;
           if (kp.logprobs) kp.logprobs[(int64_t)row * V + s0 + l] = -INFINITY;
         }
@@ -852,179 +938,408 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       continue;
     }
     const float mf = (float)m;
+    const float wsc = T < 1.0f ? T : 1.0f;  // window scale (see win_bin)
+    const uint32_t t_m = minp ? min_p_key(sm, m, P.min_p) : 0u;
 
     // ---- 3. window histogram (exchange 2, merged by the last workgroup to
-    // arrive): counts for top-k and the top logprobs, masses for top-p and
-    // the kept-set sum, and the exact fp64 sum when every token is kept.
-    const bool need_cnt = topk || K > 0;
-    const bool need_mass = truncated && (topp || want_S);
+    // arrive): counts for top-k and the gather, masses for top-p and the
+    // kept-set sum, and the exact fp64 sum when every token is kept.
+    const bool need_sel = topk || topp || K > 0 || (truncated && want_S);  // window + candidates
+    const bool need_mass = topp || (truncated && want_S);
+    const bool need_deep = topp && !topk;  // top-p's total includes the deep values
     const bool need_exact = !truncated && want_S;
-    const bool need_thr = truncated || K > 0;  // thresholds / candidates needed
     bool general = false;
     bool full_k = false;
-    uint32_t tau = 0;
+    bool topk_on = topk;  // top-k decides (part of) the kept set
+    uint32_t tau = truncated && !need_sel ? t_m : 0u;  // min-p alone without outputs: closed form
     double lnS = 0.0;
-    CandRanges cr = {-1, 1, 0, 1, 0, -1};
-    if (need_cnt || need_mass || need_exact) {
-      if (need_cnt || need_mass) {
-        for (int b = tid; b < kWinBins + 1; b += kBlock) wc[b] = 0;
-        for (int b = tid; b < kMassBins + 1; b += kBlock) wm[b] = 0;
+    int r0hi = -1, r1lo = 1, r1hi = 0, rklo = 1, rkhi = 0, bm = -1;
+    if (need_sel || need_exact) {
+      if (need_sel) {
+        wh[tid] = 0;
         __syncthreads();
       }
-      uint32_t deep_n = 0;
-      unsigned long long deep_m = 0;
+      double deep_a = 0.0;  // deeper masses, 2^-31 units
       double sx = 0.0;
-      for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
+      for (int l = 4 * tid; l < ln4; l += 4 * kBlock) {
         const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const float zz = zv[c];
-          const float d = mf - zz;
-          if (need_cnt && l + c < rc.n) {
-            if (d < 32.0f) atomicAdd(&wc[(int)(d * kBinsPerNat)], 1u);
-            else ++deep_n;
+          const float d = mf - zz;  // padding: +inf
+          if (need_sel) {
+            const float dd = win_dist(mf, zz, wsc);
+            const bool near = dd < kWinNats;
+            const float a = mass_scaled(d);
+            if (near) atomicAdd(&wh[(int)(dd * kBinsPerNat)], hist_entry(a));
+            if (need_deep) deep_a += near ? 0.0 : (double)a;
           }
-          if (need_mass) {
-            if (d < 16.0f) atomicAdd(&wm[(int)(d * kBinsPerNat)], mass_fixed(d));
-            else deep_m += mass_fixed(d);
-          }
-          if (need_exact) sx += d < 40.0f ? exp((double)zz - m) : (double)expf(-d);
+          if (need_exact) sx += exp_nonpos(sm.exp_tab, (double)zz - m);
         }
       }
-      const uint32_t wdn = need_cnt ? (uint32_t)wg_sum_u(sm, deep_n) : 0u;
-      const unsigned long long wdm = need_mass ? wg_sum_u(sm, deep_m) : 0ull;
+      const double wdm = need_deep ? wg_sum_d(sm, deep_a) : 0.0;
       const double wsx = need_exact ? wg_sum_d(sm, sx) : 0.0;
       __syncthreads();
       // this workgroup's histogram -> its exchange slot
-      if (need_cnt)
-        for (int b = tid; b < kWinBins; b += kBlock) atomic_st(&rc.my->wcnt[b], wc[b]);
-      if (need_mass)
-        for (int b = tid; b < kMassBins; b += kBlock) atomic_st(&rc.my->wmass[b], wm[b]);
+      if (need_sel) atomic_st(&rc.my->whist[tid], wh[tid]);
       if (tid == 0) {
-        atomic_st(&rc.my->wcnt[kWinBins], wdn);
-        atomic_st(&rc.my->wmass[kMassBins], wdm);
-        atomic_st(&rc.my->spart, wsx);
+        atomic_st(&rc.my->wdeep[0], (unsigned long long)__double2ll_rn(wdm));
+        atomic_st(&rc.my->spart[par], wsx);
       }
       if (group_arrive(sm, rc.gsync, G)) {
-        // ---- merge (last arrival): inclusive prefix sums over the bins,
-        // kept in LDS for the decisions and published for exchange 3
-        static_assert(kWinBins == kBlock && kMassBins <= kBlock, "one bin per thread");
-        {
-          uint32_t c = 0;
-          if (need_cnt)
-            for (int g = 0; g < G; ++g) c += atomic_ld(&rc.peers[g].wcnt[tid]);
-          const uint32_t run = block_scan_incl<uint32_t>(c, sm.red_c);
-          wc[tid] = run;
-          if (tid == kBlock - 1) {
-            uint32_t o = 0;
-            if (need_cnt)
-              for (int g = 0; g < G; ++g) o += atomic_ld(&rc.peers[g].wcnt[kWinBins]);
-            wc[kWinBins] = run + o;
+        // ---- merge (last arrival): sum the G histograms (16-byte reads,
+        // integer LDS adds: order-free), inclusive prefix sums over the bins
+        // (thread b owns bin b), then every decision in parallel
+        if (need_sel) {
+          const int b = tid;
+          lc[b] = 0;
+          lm[b] = 0;
+          if (tid == 0) lm[kWinBins] = 0;
+          __syncthreads();
+          // two bins per 16-byte read, two reads per pass (the second
+          // repeats the first when out of range and is then ignored)
+          constexpr int kPairs = kWinBins / 2;
+          for (int pi = tid; pi < G * kPairs; pi += 2 * kBlock) {
+            const int pj = pi + kBlock < G * kPairs ? pi + kBlock : pi;
+            u32x4 ra, rb;
+            coh_load16x2(&rc.peers[pi / kPairs].whist[2 * (pi % kPairs)], &rc.peers[pj / kPairs].whist[2 * (pj % kPairs)], ra, rb);
+            const unsigned long long h[4] = {u64_of(ra.x, ra.y), u64_of(ra.z, ra.w), u64_of(rb.x, rb.y), u64_of(rb.z, rb.w)};
+            const int b0[2] = {2 * (pi % kPairs), 2 * (pj % kPairs)};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              if (i >= 2 && pj == pi) break;
+              const unsigned long long e = h[i];
+              if (e) {
+                const int bin = b0[i >> 1] + (i & 1);
+                atomicAdd(&lc[bin], (uint32_t)(e >> 48));
+                if (need_mass) atomicAdd(&lm[bin], e & 0xFFFFFFFFFFFFull);
+              }
+            }
+          }
+          if (need_deep && tid < G) atomicAdd(&lm[kWinBins], atomic_ld(&rc.peers[tid].wdeep[0]));
+          __syncthreads();
+          const uint32_t cb = lc[b];
+          const unsigned long long mb = lm[b], deep = lm[kWinBins];
+          const uint32_t runc = block_scan_incl<uint32_t>(cb, sm.red_c);
+          const unsigned long long runm = block_scan_incl<unsigned long long>(mb, sm.red_u);
+          lc[b] = runc;
+          lm[b] = runm;
+          if (b == kWinBins - 1) lm[kWinBins] = runm + deep;
+          if (tid == 0) {
+            sm.bu[16] = kNone;
+            sm.bu[17] = kNone;
+            sm.bu[18] = kNone;
+            sm.bu[19] = kNone;
+          }
+          __syncthreads();
+          atomic_st(&rec->cum_cnt[b], runc);
+          atomic_st(&rec->cum_mass[b], runm);
+          if (b == kWinBins - 1) atomic_st(&rec->cum_mass[kWinBins], runm + deep);
+          // bins of the k-th and the K-th value
+          const uint32_t cprev = b > 0 ? lc[b - 1] : 0u;
+          if (topk && cprev < (uint32_t)P.top_k && runc >= (uint32_t)P.top_k) sm.bu[16] = (uint32_t)b;
+          if (K > 0 && cprev < (uint32_t)K && runc >= (uint32_t)K) sm.bu[17] = (uint32_t)b;
+          __syncthreads();
+          const uint32_t bk = sm.bu[16], r0 = sm.bu[17];
+          bool gen = false;
+          bool fk = false;
+          bool k_off = false;
+          int e_r0hi = -1, e_r1lo = 1, e_r1hi = 0, e_rklo = 1, e_rkhi = 0, e_bm = -1;
+          const int bmin = minp ? win_bin(mf, key_to_float(t_m), wsc) : kWinBins;
+          if (K > 0) {
+            if (r0 != kNone) e_r0hi = (int)r0;
+            else if (truncated) e_r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
+            else gen = true;
+          }
+          if (topk) {
+            if (bk != kNone) {
+              if (lc[bk] <= (uint32_t)kCandCap) {
+                fk = true;
+                e_rklo = 0;
+                e_rkhi = (int)bk;
+              } else {
+                e_rklo = e_rkhi = (int)bk;
+              }
+            } else if (topp || !(minp && bmin < kWinBins)) {
+              gen = true;  // the k-th value is deeper than the window and decides the kept set
+            } else {
+              k_off = true;
+            }
+          }
+          // top-p: the bins where the cumulative mass crosses p times the
+          // total mass of the top-k set (bounded below and above)
+          double tlo = 0.0, thi = 0.0;
+          if (topp && !gen) {
+            if (topk) {
+              tlo = (double)P.top_p * (bk > 0 ? (double)lm[bk - 1] : 0.0);
+              thi = (double)P.top_p * (double)lm[bk];
+            } else {
+              tlo = thi = (double)P.top_p * (double)lm[kWinBins];
+            }
+            const double mprev = b > 0 ? (double)lm[b - 1] : 0.0, mcur = (double)lm[b];
+            if (mprev < tlo && mcur >= tlo) sm.bu[18] = (uint32_t)b;
+            if (mprev < thi && mcur >= thi) sm.bu[19] = (uint32_t)b;
+          }
+          __syncthreads();
+          if (topp && !gen) {
+            const uint32_t lo = tlo <= 0.0 ? 0u : sm.bu[18], hi = sm.bu[19];
+            if (hi == kNone) {
+              gen = true;  // the crossing lies deeper than the window
+            } else {
+              e_r1lo = (int)(lo == kNone ? hi : lo);
+              e_r1hi = (int)hi;
+              if (topk) {
+                e_r1lo = min(e_r1lo, (int)bk);
+                e_r1hi = min(e_r1hi, (int)bk);
+              }
+            }
+          }
+          if (minp && !gen) {
+            if (bmin < kWinBins) e_bm = bmin;
+            else if (!topk && !topp) gen = true;  // min-p alone keeps values deeper than the window
+          }
+          // gathered bins and their total count
+          const bool in = !gen && (b <= e_r0hi || (b >= e_r1lo && b <= e_r1hi) || (b >= e_rklo && b <= e_rkhi) || b == e_bm);
+          const unsigned long long bal = __ballot(in);
+          if (lane == 0) {
+            atomic_st(&rec->dec[D_MASK + 2 * wave], (uint32_t)bal);
+            atomic_st(&rec->dec[D_MASK + 2 * wave + 1], (uint32_t)(bal >> 32));
+          }
+          const uint32_t ncand = (uint32_t)wg_sum_u(sm, in ? (unsigned long long)cb : 0ull);
+          if (ncand > (uint32_t)kCandCap) gen = true;
+          if (tid == 0) {
+            atomic_st(&rec->dec[D_FLAGS], (gen ? 1u : 0u) | (fk ? 2u : 0u) | (k_off ? 4u : 0u));
+            atomic_st(&rec->dec[D_R0HI], (uint32_t)e_r0hi);
+            atomic_st(&rec->dec[D_R1LO], (uint32_t)e_r1lo);
+            atomic_st(&rec->dec[D_R1HI], (uint32_t)e_r1hi);
+            atomic_st(&rec->dec[D_RKLO], (uint32_t)e_rklo);
+            atomic_st(&rec->dec[D_RKHI], (uint32_t)e_rkhi);
+            atomic_st(&rec->dec[D_BM], (uint32_t)e_bm);
           }
         }
-        {
-          unsigned long long mm = 0;
-          if (need_mass && tid < kMassBins)
-            for (int g = 0; g < G; ++g) mm += atomic_ld(&rc.peers[g].wmass[tid]);
-          const unsigned long long run = block_scan_incl<unsigned long long>(mm, sm.red_u);
-          if (tid < kMassBins) wm[tid] = run;
-          if (tid == kMassBins - 1) {
-            unsigned long long o = 0;
-            if (need_mass)
-              for (int g = 0; g < G; ++g) o += atomic_ld(&rc.peers[g].wmass[kMassBins]);
-            wm[kMassBins] = run + o;
+        if (need_exact) {
+          if (tid < G) sm.gd[tid] = atomic_ld(&rc.peers[tid].spart[par]);
+          __syncthreads();
+          if (tid == 0) {
+            double S_all = 0.0;
+            for (int g = 0; g < G; ++g) S_all += sm.gd[g];
+            atomic_st(&rec->dd[0], S_all);
           }
-        }
-        __syncthreads();
-        for (int b = tid; b <= kWinBins; b += kBlock) atomic_st(&rec->cum_cnt[b], wc[b]);
-        for (int b = tid; b <= kMassBins; b += kBlock) atomic_st(&rec->cum_mass[b], wm[b]);
-        if (tid == 0) {
-          double S_all = 0.0;
-          if (need_exact)
-            for (int g = 0; g < G; ++g) S_all += atomic_ld(&rc.peers[g].spart);
-          decide_window(rec, wc, wm, P, topk, topp, minp, need_thr, K, mf, t_m, S_all);
         }
         group_release(rc.gsync);
       } else {
         group_wait(sm, rc.gsync, rc.abort_word, rc.epoch);
       }
-      if (tid == 0) {
-        sm.bu[4] = atomic_ld(&rec->dec[D_FLAGS]);
-        sm.bu[5] = atomic_ld(&rec->dec[D_R0HI]);
-        sm.bu[6] = atomic_ld(&rec->dec[D_R1LO]);
-        sm.bu[7] = atomic_ld(&rec->dec[D_R1HI]);
-        sm.bu[8] = atomic_ld(&rec->dec[D_RKLO]);
-        sm.bu[9] = atomic_ld(&rec->dec[D_RKHI]);
-        sm.bu[10] = atomic_ld(&rec->dec[D_BM]);
-        sm.bd[1] = atomic_ld(&rec->dd[0]);
+      // decisions (32 words) and the exact sum: 16-byte reads in parallel
+      if (need_sel && tid < 8) {
+        const u32x4 r = coh_load16(&rec->dec[4 * tid]);
+        sm.dec[4 * tid] = r.x;
+        sm.dec[4 * tid + 1] = r.y;
+        sm.dec[4 * tid + 2] = r.z;
+        sm.dec[4 * tid + 3] = r.w;
+      } else if (need_exact && tid == 8) {
+        const u32x4 r = coh_load16(&rec->dd[0]);
+        sm.bd[1] = f64_of(r.x, r.y);
       }
       __syncthreads();
-      general = sm.bu[4] & 1u;
-      full_k = sm.bu[4] & 2u;
-      cr.r0hi = (int)sm.bu[5];
-      cr.r1lo = (int)sm.bu[6];
-      cr.r1hi = (int)sm.bu[7];
-      cr.rklo = (int)sm.bu[8];
-      cr.rkhi = (int)sm.bu[9];
-      cr.bm = (int)sm.bu[10];
+      if (need_sel) {
+        general = sm.dec[D_FLAGS] & 1u;
+        full_k = sm.dec[D_FLAGS] & 2u;
+        topk_on = topk && !(sm.dec[D_FLAGS] & 4u);
+        r0hi = (int)sm.dec[D_R0HI];
+        r1lo = (int)sm.dec[D_R1LO];
+        r1hi = (int)sm.dec[D_R1HI];
+        rklo = (int)sm.dec[D_RKLO];
+        rkhi = (int)sm.dec[D_RKHI];
+        bm = (int)sm.dec[D_BM];
+      }
       if (need_exact) lnS = log(sm.bd[1]);
-      __syncthreads();
     }
 
     // ---- 4. exact thresholds from the gathered candidates (exchange 3,
-    // ranked and decided by the last workgroup to arrive)
-    if (need_thr && !general) {
-      // count, reserve, then write this slice's candidates
-      uint32_t mine = 0;
-      for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
-        const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+    // sorted and decided by the last workgroup to arrive)
+    if (need_sel && !general) {
+      // compact this slice's candidates into per-wave LDS staging (ballot
+      // order: deterministic), then copy them to this workgroup's slot
+      uint32_t cnt = 0;  // wave-uniform
+      unsigned long long *wst = stage + wave * kStagePerWave;
+      // the gathered bins as runs, from the (up to four) ranges the merge
+      // chose: sorted by start and joined where they touch; the first two
+      // runs are tested by value, any further bins through the mask
+      int run_lo[2] = {1, 1}, run_hi[2] = {0, 0};
+      bool more = false;
+      {
+        int lo[4] = {0, r1lo, rklo, bm}, hi[4] = {r0hi, r1hi, rkhi, bm};
+        if (bm < 0) hi[3] = -1;
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
-          if (l + c < rc.n && cr.has(win_bin(mf, zv[c]))) ++mine;
-      }
-      const uint32_t incl = block_scan_incl<uint32_t>(mine, sm.red_c);
-      if (tid == kBlock - 1) sm.bu[11] = atomicAdd(&rec->cand_n, incl);
-      __syncthreads();
-      uint32_t pos = sm.bu[11] + incl - mine;
-      if (mine > 0) {
-        for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
-          const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+        for (int i = 1; i < 4; ++i)  // insertion sort by start (empty ranges have hi < lo)
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (l + c < rc.n && cr.has(win_bin(mf, zv[c]))) {
-              if (pos < (uint32_t)kCandCap) {
-                atomic_st(&rec->cz[pos], zv[c]);
-                atomic_st(&rec->ci[pos], s0 + l + c);
-              }
-              ++pos;
+          for (int j = i; j > 0; --j)
+            if (lo[j] < lo[j - 1]) {
+              const int tl = lo[j], th = hi[j];
+              lo[j] = lo[j - 1];
+              hi[j] = hi[j - 1];
+              lo[j - 1] = tl;
+              hi[j - 1] = th;
             }
+        int nrun = 0, clo = 0, chi = -1;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          if (hi[i] < lo[i]) continue;
+          if (chi >= clo && lo[i] <= chi + 1) {
+            chi = max(chi, hi[i]);
+          } else {
+            if (chi >= clo) {
+              if (nrun < 2) {
+                run_lo[nrun] = clo;
+                run_hi[nrun] = chi;
+              } else {
+                more = true;
+              }
+              ++nrun;
+            }
+            clo = lo[i];
+            chi = hi[i];
+          }
+        }
+        if (chi >= clo) {
+          if (nrun < 2) {
+            run_lo[nrun] = clo;
+            run_hi[nrun] = chi;
+          } else {
+            more = true;
           }
         }
       }
+      // value bounds of the runs: bin(d) in [lo, hi]  <=>  lo / 32 <= d < (hi + 1) / 32
+      const float d0lo = (float)run_lo[0] / kBinsPerNat, d0hi = (float)(run_hi[0] + 1) / kBinsPerNat;
+      const float d1lo = (float)run_lo[1] / kBinsPerNat, d1hi = (float)(run_hi[1] + 1) / kBinsPerNat;
+      const float d_cut = more ? kWinNats : max(d0hi, d1hi);
+      // branch-free membership: the two runs by value, or (more than two
+      // runs, rare) the bin mask
+      auto is_cand = [&](float d) -> bool {
+        if (more) {
+          const int bb = min((int)(d * kBinsPerNat), kWinBins - 1);
+          return (d < d_cut) & (bool)((sm.dec[D_MASK + (bb >> 5)] >> (bb & 31)) & 1u);
+        }
+        return ((d >= d0lo) & (d < d0hi)) | ((d >= d1lo) & (d < d1hi));
+      };
+      const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);
+      for (int q = 0; q < iters; ++q) {
+        const int l = 4 * tid + 4 * kBlock * q;
+        f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (l < ln4) zv = *reinterpret_cast<const f32x4 *>(zs + l);
+        bool isc[4];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) isc[c] = is_cand(win_dist(mf, zv[c], wsc));
+        if (!__ballot(isc[0] || isc[1] || isc[2] || isc[3])) continue;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const unsigned long long bal = __ballot(isc[c]);
+          if (bal) {
+            const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (isc[c] && cnt + off < (uint32_t)kStagePerWave) wst[cnt + off] = cand_key(zv[c], s0 + l + c);
+            cnt += (uint32_t)__popcll(bal);
+          }
+        }
+      }
+      if (lane == 0) sm.red_c[wave] = cnt;
+      __syncthreads();
+      if (tid == 0) {
+        uint32_t acc = 0;
+        bool ovf = false;
+        for (int w = 0; w < kWaves; ++w) {
+          sm.wo[w] = acc;
+          ovf |= sm.red_c[w] > (uint32_t)kStagePerWave;
+          acc += sm.red_c[w];
+        }
+        ovf |= acc > (uint32_t)kCandCap;
+        sm.wo[kWaves] = ovf ? (uint32_t)kCandCap + 1u : acc;
+      }
+      __syncthreads();
+      const uint32_t my_n = sm.wo[kWaves];
+      if (my_n <= (uint32_t)kCandCap) {
+        for (int w = 0; w < kWaves; ++w) {
+          const int cw = (int)sm.red_c[w];
+          for (int j = tid; j < cw; j += kBlock) atomic_st(&rc.my->cand[sm.wo[w] + j], stage[w * kStagePerWave + j]);
+        }
+      }
+      if (tid == 0) atomic_st(&rc.my->cand_n, my_n);
       if (group_arrive(sm, rc.gsync, G)) {
-        if (tid == 0) sm.bu[12] = atomic_ld(&rec->cand_n);
+        // ---- merge: gather the G lists, sort, decide
+        if (tid < G) sm.gcnt[tid] = atomic_ld(&rc.peers[tid].cand_n);
         __syncthreads();
-        const uint32_t n_all = sm.bu[12];
-        const int n = (int)min(n_all, (uint32_t)kCandCap);
-        // merged prefix arrays and candidates -> LDS
-        for (int b = tid; b <= kWinBins; b += kBlock) wc[b] = atomic_ld(&rec->cum_cnt[b]);
-        for (int b = tid; b <= kMassBins; b += kBlock) wm[b] = atomic_ld(&rec->cum_mass[b]);
-        for (int t = tid; t < n; t += kBlock) {
-          cz[t] = atomic_ld(&rec->cz[t]);
-          ci[t] = atomic_ld(&rec->ci[t]);
+        if (tid == 0) {
+          uint32_t acc = 0, pairs = 0;
+          bool ovf = false;
+          for (int g = 0; g < G; ++g) {
+            const uint32_t c = sm.gcnt[g];
+            ovf |= c > (uint32_t)kCandCap;
+            const uint32_t cc = c > (uint32_t)kCandCap ? 0u : c;
+            sm.gcnt[g] = cc;
+            sm.goff[g] = acc;
+            sm.gpo[g] = pairs;
+            acc += cc;
+            pairs += (cc + 1u) / 2u;
+          }
+          ovf |= acc > (uint32_t)kCandCap;
+          sm.goff[G] = acc;
+          sm.gpo[G] = pairs;
+          sm.bu[12] = ovf ? 1u : 0u;
         }
         __syncthreads();
-        // rank by (value desc, index asc): a total order, so the sorted list
-        // (and every sum over it) does not depend on the gather order
-        for (int t = tid; t < n; t += kBlock) {
-          const float zt = cz[t];
-          const int it_ = ci[t];
-          int r = 0;
-          for (int j = 0; j < n; ++j) r += (cz[j] > zt || (cz[j] == zt && ci[j] < it_)) ? 1 : 0;
-          sz[r] = zt;
-          si[r] = it_;
+        const bool ovf = sm.bu[12] != 0u;
+        const int n = ovf ? 0 : (int)sm.goff[G];
+        if (!ovf) {
+          // candidates in 16-byte pairs (a slot's array has room past an odd count)
+          for (int pi = tid; pi < (int)sm.gpo[G]; pi += kBlock) {
+            int g = 0;
+            while ((int)sm.gpo[g + 1] <= pi) ++g;
+            const int j = 2 * (pi - (int)sm.gpo[g]);
+            const u32x4 r = coh_load16(&rc.peers[g].cand[j]);
+            sk[sm.goff[g] + j] = u64_of(r.x, r.y);
+            if (j + 1 < (int)sm.gcnt[g]) sk[sm.goff[g] + j + 1] = u64_of(r.z, r.w);
+          }
         }
+        // merged prefix arrays, 16 bytes per thread
+        if (tid < kWinBins / 4) {
+          const u32x4 r = coh_load16(&rec->cum_cnt[4 * tid]);
+          lc[4 * tid] = r.x;
+          lc[4 * tid + 1] = r.y;
+          lc[4 * tid + 2] = r.z;
+          lc[4 * tid + 3] = r.w;
+        } else if (tid < kWinBins / 4 + kWinBins / 2 + 1) {
+          const int j = 2 * (tid - kWinBins / 4);
+          const u32x4 r = coh_load16(&rec->cum_mass[j]);
+          lm[j] = u64_of(r.x, r.y);
+          if (j + 1 <= kWinBins) lm[j + 1] = u64_of(r.z, r.w);
+        }
+        if (tid == 0) sk[n] = 0ull;  // pads an odd count for the pairwise reads below
         __syncthreads();
+        // rank each candidate by counting the larger keys (keys are distinct:
+        // each holds its index), two candidates per thread, keys read in
+        // 16-byte pairs by every thread at once; the ranks place the list in
+        // (value desc, index asc) order, a total order, so the list and every
+        // sum over it do not depend on the gather order
+        {
+          const unsigned long long c0 = tid < n ? sk[tid] : ~0ull;
+          const unsigned long long c1 = tid + kBlock < n ? sk[tid + kBlock] : ~0ull;
+          uint32_t r0 = 0, r1 = 0;
+#pragma unroll 4
+          for (int j = 0; j < n; j += 2) {
+            const unsigned long long ka = sk[j], kb = sk[j + 1];
+            r0 += (ka > c0 ? 1u : 0u) + (kb > c0 ? 1u : 0u);
+            r1 += (ka > c1 ? 1u : 0u) + (kb > c1 ? 1u : 0u);
+          }
+          __syncthreads();
+          if (tid < n) sk[r0] = c0;
+          if (tid + kBlock < n) sk[r1] = c1;
+          __syncthreads();
+        }
+        auto keyof = [&](int j) { return (uint32_t)(sk[j] >> 32); };
+        auto zof = [&](int j) { return key_to_float(keyof(j)); };
+        auto idxof = [&](int j) { return (int)(~(uint32_t)sk[j]); };
+        auto binof = [&](int j) { return win_bin(mf, zof(j), wsc); };
         // inclusive prefix of exact masses exp(z - m) along the sorted list;
         // each thread owns kCandCap / kBlock consecutive positions
         {
@@ -1035,7 +1350,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
 #pragma unroll
           for (int u = 0; u < kPerC; ++u) {
             const int j = tid * kPerC + u;
-            qv[u] = j < n ? exp((double)sz[j] - m) : 0.0;
+            qv[u] = j < n ? exp_nonpos(sm.exp_tab, (double)zof(j) - m) : 0.0;
             own += qv[u];
           }
           double run = block_scan_incl<double>(own, sm.red_d) - own;
@@ -1046,122 +1361,110 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             if (j < n) sq[j] = run;
           }
         }
-        __syncthreads();
-        // exact decisions; the sorted list holds every value of the gathered
-        // bins, so the values of one bin are a contiguous run
-        auto binof = [&](int j) { return win_bin(mf, sz[j]); };
-        auto first_pos_bin = [&](int b) {  // first position whose bin is >= b
-          int lo = 0, hi = n;
-          while (lo < hi) {
-            const int mid = (lo + hi) / 2;
-            if (binof(mid) >= b) hi = mid;
-            else lo = mid + 1;
-          }
-          return lo;
-        };
-        auto last_pos_ge = [&](uint32_t key) {  // last position with key >= `key` (-1: none)
-          int lo = 0, hi = n;
-          while (lo < hi) {
-            const int mid = (lo + hi) / 2;
-            if (fkey(sz[mid]) >= key) lo = mid + 1;
-            else hi = mid;
-          }
-          return lo - 1;
-        };
         auto qsum = [&](int a, int e) { return (e < a) ? 0.0 : sq[e] - (a > 0 ? sq[a - 1] : 0.0); };
-        auto cmass = [&](int b) { return b < 0 ? 0.0 : (double)wm[b < kMassBins ? b : kMassBins] / kMassScale; };
-        auto ccnt = [&](int b) { return b < 0 ? 0u : wc[b < kWinBins ? b : kWinBins]; };
+        auto cmass = [&](int b) { return b < 0 ? 0.0 : (double)lm[b < kWinBins ? b : kWinBins] / kWinScale; };
+        auto ccnt = [&](int b) { return b < 0 ? 0u : lc[b < kWinBins ? b : kWinBins - 1]; };
+        // first positions of the bins that bound the ranges (the values of
+        // one bin are a contiguous run of the sorted list)
         if (tid == 0) {
-          uint32_t flags = n_all > (uint32_t)kCandCap ? 1u : 0u;
-          uint32_t t = 0;
-          double ctot = cmass(kMassBins);
-          if (!flags && topk) {
-            int j;
-            if (full_k) {
-              j = P.top_k - 1;
-            } else {
-              j = first_pos_bin(cr.rklo) + (P.top_k - (int)ccnt(cr.rklo - 1)) - 1;
-            }
-            if (j < 0 || j >= n) {
-              flags |= 1u;
-            } else {
-              t = fkey(sz[j]);
-              const int e = last_pos_ge(t);
-              ctot = full_k ? qsum(0, e) : cmass(cr.rklo - 1) + qsum(first_pos_bin(cr.rklo), e);
-            }
-          }
-          sm.bd[4] = ctot;
-          sm.bu[0] = flags;
-          sm.bu[1] = t;
-          // top-p search range: positions of bins [r1lo, r1hi]
-          const int p0 = first_pos_bin(cr.r1lo);
-          sm.bu[2] = (uint32_t)p0;
-          sm.bu[3] = (uint32_t)(first_pos_bin(cr.r1hi + 1) - 1);
-          sm.bd[5] = (full_k ? 0.0 : cmass(cr.r1lo - 1)) - (p0 > 0 ? (full_k ? 0.0 : sq[p0 - 1]) : 0.0);
-          sm.bd[6] = (double)P.top_p * ctot;
-          sm.bu[5] = 0x7FFFFFFF;
+          sm.bu[20] = (uint32_t)n;
+          sm.bu[21] = (uint32_t)n;
+          sm.bu[22] = (uint32_t)n;
         }
         __syncthreads();
-        // top-p crossing: the first tie-group end e in range whose
-        // cumulative mass reaches p * C_tot (parallel over positions)
-        if (topp && !(sm.bu[0] & 1u)) {
-          const int p0 = (int)sm.bu[2], p1 = (int)sm.bu[3];
-          const double base = sm.bd[5], target = sm.bd[6];
-          for (int e = p0 + tid; e <= p1; e += kBlock) {
-            const bool end = (e == n - 1) || (sz[e + 1] != sz[e]);
-            if (end && base + sq[e] >= target) atomicMin(&sm.bu[5], (uint32_t)e);
-          }
+        for (int j = tid; j < n; j += kBlock) {
+          const int bj = binof(j), bp = j > 0 ? binof(j - 1) : -1;
+          if (bj >= rklo && bp < rklo) sm.bu[20] = (uint32_t)j;
+          if (bj >= r1lo && bp < r1lo) sm.bu[21] = (uint32_t)j;
+          if (bj >= r1hi + 1 && bp < r1hi + 1) sm.bu[22] = (uint32_t)j;
         }
         __syncthreads();
+        const int fp_k = (int)sm.bu[20], fp_p0 = (int)sm.bu[21], fp_p1 = (int)sm.bu[22];
+        // top-k: the value of rank k, and the end of its tie group
+        uint32_t flags = ovf ? 1u : 0u;
+        uint32_t tk = 0;
+        if (!flags && topk_on) {
+          const int jk = full_k ? P.top_k - 1 : fp_k + (P.top_k - (int)ccnt(rklo - 1)) - 1;
+          if (jk < 0 || jk >= n) flags |= 1u;
+          else tk = keyof(jk);
+        }
+        if (tid == 0) sm.bu[23] = (uint32_t)n;
+        __syncthreads();
+        if (!flags && topk_on)
+          for (int j = tid; j < n; j += kBlock)
+            if (keyof(j) < tk && (j == 0 || keyof(j - 1) >= tk)) sm.bu[23] = (uint32_t)j;
+        __syncthreads();
+        const int ek = (int)sm.bu[23] - 1;
+        // top-p: the first tie-group end whose cumulative mass reaches p
+        // times the top-k set's mass (parallel over the crossing range)
+        uint32_t t = tk;
+        if (!flags && topp) {
+          const double ctot = topk_on ? (full_k ? qsum(0, ek) : cmass(rklo - 1) + qsum(fp_k, ek)) : cmass(kWinBins);
+          const double target = (double)P.top_p * ctot;
+          const double base = full_k ? 0.0 : cmass(r1lo - 1) - (fp_p0 > 0 ? sq[fp_p0 - 1] : 0.0);
+          if (tid == 0) sm.bu[24] = 0x7FFFFFFFu;
+          __syncthreads();
+          for (int e = fp_p0 + tid; e < fp_p1; e += kBlock) {
+            const bool end = (e == n - 1) || (keyof(e + 1) != keyof(e));
+            if (end && base + sq[e] >= target) atomicMin(&sm.bu[24], (uint32_t)e);
+          }
+          __syncthreads();
+          const uint32_t e = sm.bu[24];
+          if (e == 0x7FFFFFFFu) flags |= 1u;
+          else t = max(t, keyof((int)e));
+        }
+        if (minp) t = max(t, t_m);
+        // the kept set: positions [0, et); its sum and the top logprobs
+        const int bt = t ? win_bin(mf, key_to_float(t), wsc) : kWinBins;
         if (tid == 0) {
-          uint32_t flags = sm.bu[0];
-          uint32_t t = sm.bu[1];
-          if (topp && !flags) {
-            const uint32_t e = sm.bu[5];
-            if (e == 0x7FFFFFFFu) flags |= 1u;
-            else t = max(t, fkey(sz[e]));
+          sm.bu[25] = (uint32_t)n;
+          sm.bu[26] = (uint32_t)n;
+        }
+        __syncthreads();
+        if (t)
+          for (int j = tid; j < n; j += kBlock) {
+            if (keyof(j) < t && (j == 0 || keyof(j - 1) >= t)) sm.bu[25] = (uint32_t)j;
+            const int bj = binof(j), bp = j > 0 ? binof(j - 1) : -1;
+            if (bj >= bt && bp < bt) sm.bu[26] = (uint32_t)j;
           }
-          if (minp) t = max(t, t_m);
-          double S_K = atomic_ld(&rec->dd[0]);
-          if (!flags && truncated && want_S) {
-            const int e = last_pos_ge(t);
-            const int bt = win_bin(mf, key_to_float(t));
-            if (full_k && bt <= cr.rkhi) {
-              S_K = qsum(0, e);
-            } else if (bt < kMassBins) {
-              S_K = cmass(bt - 1) + qsum(first_pos_bin(bt), e);
+        __syncthreads();
+        const int et = (int)sm.bu[25], fp_bt = (int)sm.bu[26];
+        double S_K = atomic_ld(&rec->dd[0]);
+        if (!flags && truncated && want_S) {
+          if (full_k && bt <= rkhi) S_K = qsum(0, et - 1);
+          else if (bt < kWinBins) S_K = cmass(bt - 1) + qsum(fp_bt, et - 1);
+          else flags |= 1u;
+        }
+        const double lns = log(S_K);
+        if (!flags && K > 0) {
+          const int kept_n = truncated ? et : n;
+          for (int q = tid; q < K; q += kBlock) {
+            const int64_t o = (int64_t)row * K + q;
+            if (q < kept_n) {
+              kp.top_lp_vals[o] = (float)(((double)zof(q) - m) - lns);
+              kp.top_lp_ids[o] = idxof(q);
             } else {
-              flags |= 1u;
+              kp.top_lp_vals[o] = -INFINITY;
+              kp.top_lp_ids[o] = -1;
             }
           }
-          const double lns = log(S_K);
-          if (!flags && K > 0) {
-            const int kept_n = truncated ? last_pos_ge(t) + 1 : n;
-            int w = 0;
-            for (int j = 0; j < kept_n && w < K; ++j) {
-              if (sz[j] > -INFINITY) {
-                kp.top_lp_vals[(int64_t)row * K + w] = (float)(((double)sz[j] - m) - lns);
-                kp.top_lp_ids[(int64_t)row * K + w] = si[j];
-                ++w;
-              }
-            }
-            for (; w < K; ++w) {
-              kp.top_lp_vals[(int64_t)row * K + w] = -INFINITY;
-              kp.top_lp_ids[(int64_t)row * K + w] = -1;
-            }
-          }
+        }
+        if (tid == 0) {
           atomic_st(&rec->dec[D_FLAGS], flags);
           atomic_st(&rec->dec[D_TAU], t);
-          atomic_st(&rec->dd[1], lns);
+          const unsigned long long lb = (unsigned long long)__double_as_longlong(lns);
+          atomic_st(&rec->dec[D_LNS], (uint32_t)lb);
+          atomic_st(&rec->dec[D_LNS + 1], (uint32_t)(lb >> 32));
         }
         group_release(rc.gsync);
       } else {
         group_wait(sm, rc.gsync, rc.abort_word, rc.epoch);
       }
       if (tid == 0) {
-        sm.bu[4] = atomic_ld(&rec->dec[D_FLAGS]);
-        sm.bu[13] = atomic_ld(&rec->dec[D_TAU]);
-        sm.bd[2] = atomic_ld(&rec->dd[1]);
+        const u32x4 r = coh_load16(&rec->dec[0]);
+        sm.bu[4] = r[D_FLAGS];
+        sm.bu[13] = r[D_TAU];
+        sm.bd[2] = f64_of(r[D_LNS], r[D_LNS + 1]);
       }
       __syncthreads();
       general = sm.bu[4] & 1u;
@@ -1180,11 +1483,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
       if (minp) tau = t_m > tau ? t_m : tau;
       double ls = 0.0;
-      for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
+      for (int l = 4 * tid; l < ln4; l += 4 * kBlock) {
         const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
 #pragma unroll
         for (int c = 0; c < 4; ++c)
-          if (fkey(zv[c]) >= tau) ls += exp((double)zv[c] - m);
+          if (fkey(zv[c]) >= tau) ls += exp_nonpos(sm.exp_tab, (double)zv[c] - m);
       }
       const double ws = wg_sum_d(sm, ls);
       const unsigned p2 = xseq++ & 1u;
@@ -1203,7 +1506,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         unsigned long long last = ~0ull;
         for (int t = 0; t < K; ++t) {
           unsigned long long cand = 0;
-          for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
+          for (int l = 4 * tid; l < ln4; l += 4 * kBlock) {
             const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -1228,32 +1531,50 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     }
 
     // ---- 5. emit probs / logprobs, Gumbel-max candidates
+    // Linear scores s_i = q_i / E_i with q_i = exp(z_i - m).  bound is a
+    // lower bound of the best exact score (shared by the wave): an element
+    // with w_i bound > q_i cannot reach it, because E_i >= w_i.
     const bool gumbel = !top1 && kp.path != PATH_GREEDY;
+    const float tauf = tau == 0 ? -INFINITY : key_to_float(tau);
     double best_g = -INFINITY;
-    float best_a = -INFINITY;
     int best_i = 0x7FFFFFFF;
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
-    for (int l = 4 * tid; l < rc.n4; l += 4 * kBlock) {
-      const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+    float bound = 0.0f;
+    const float inv_s = (float)exp(-lnS) * 0.99999f;  // bound in probability units
+    if (gumbel) {
+      // the argmax is always kept; its score is 1 / E
+      uint32_t w4[4];
+      philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
+      bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
+    }
+    const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);  // wave-uniform trip count
+    for (int q = 0; q < iters; ++q) {
+      const int l = 4 * tid + 4 * kBlock * q;
+      const bool act = l < ln4;
+      f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      if (act) zv = *reinterpret_cast<const f32x4 *>(zs + l);
       const int i0 = s0 + l;
       bool kk[4];
       bool any_cand = false;
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        kk[c] = fkey(zv[c]) >= tau;
+        kk[c] = act && zv[c] >= tauf;
         any_cand |= kk[c] && (mf - zv[c] <= kPruneNats);
       }
-      if (want_out) {
-        float pv[4], lv[4];
+      float pv[4];
+      if (want_out && act) {
+        float lv[4];
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
+          // logprob: one rounding of the fp64 value; prob = 2^(lp log2 e) by
+          // the hardware exp2 (absolute error below 2e-7)
           const float lp = kk[c] ? (float)(((double)zv[c] - m) - lnS) : -INFINITY;
           lv[c] = lp;
-          pv[c] = kk[c] ? expf(lp) : 0.0f;
+          pv[c] = kk[c] ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
         }
         const int64_t o = (int64_t)row * V + i0;
-        if ((kp.vec_ok & 2) && l + 3 < rc.n) {
+        if ((kp.vec_ok & 2) && l + 3 < ln) {
           if (kp.probs) {
             const f32x4 t = {pv[0], pv[1], pv[2], pv[3]};
             __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.probs + o));
@@ -1265,29 +1586,40 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         } else {
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            if (l + c < rc.n) {
+            if (l + c < ln) {
               if (kp.probs) kp.probs[o + c] = pv[c];
               if (kp.logprobs) kp.logprobs[o + c] = lv[c];
             }
           }
         }
       }
-      if (gumbel && any_cand) {
-        uint32_t w[4];
-        philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
+      if (gumbel) {
+        bool improved = false;
+        if (any_cand) {
+          uint32_t w[4];
+          philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
+          const float lim = want_out ? bound * inv_s : bound;
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          if (kk[c] && (mf - zv[c] <= kPruneNats)) {
-            const float ga = (zv[c] - mf) - ln_exp1_f32(w[c]);
-            if (ga > best_a - kVerifyMargin) {
-              const double ge = (double)zv[c] - log(exp1_f64(w[c]));
-              if (ge > best_g) {
-                best_g = ge;
-                best_i = i0 + c;
-                best_a = ga;
+          for (int c = 0; c < 4; ++c) {
+            if (kk[c] && (mf - zv[c] <= kPruneNats)) {
+              // lower bound of w: (float)x rounds to nearest
+              const float wl = (float)w[c] * 0x1.fffffcp-33f;
+              const float qv = want_out ? pv[c] : __builtin_amdgcn_exp2f((zv[c] - mf) * kLog2e);
+              if (wl * lim <= qv * kSlack) {
+                const double ge = (double)zv[c] - log(exp1_f64(w[c]));
+                if (ge > best_g) {
+                  best_g = ge;
+                  best_i = i0 + c;
+                  improved = true;
+                }
               }
             }
           }
+        }
+        if (__ballot(improved)) {
+          float mb = improved ? (float)exp(best_g - m) * 0.99999f : 0.0f;
+          mb = wave_max_nonneg_f(mb);
+          bound = fmaxf(bound, mb);
         }
       }
     }
@@ -1301,25 +1633,34 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     }
     if (general)
       for (int t = tid; t < K; t += kBlock) atomic_st(&rc.my->toplist[fpar][t], sm.tl[t]);
-    mem_quiesce();
+    order_release();
     __syncthreads();
     if (tid == 0) {
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
       const uint32_t old = __hip_atomic_fetch_add(&rc.gsync->fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       const bool last = old == (uint32_t)G - 1u;
       if (last) {
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
         __hip_atomic_store(&rc.gsync->fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        order_acquire();
+      }
+      sm.bu[15] = last ? 1u : 0u;
+    }
+    __syncthreads();
+    if (sm.bu[15]) {
+      if (gumbel && tid < G) {
+        const u32x4 r = coh_load16(&rc.peers[tid].fin[fpar][0]);
+        sm.gd[tid] = f64_of(r.x, r.y);
+        sm.gi[tid] = (int)f64_of(r.z, r.w);
+      }
+      __syncthreads();
+      if (tid == 0) {
         int token = argmax_idx;
         if (gumbel) {
           double bg = -INFINITY;
           int bi = 0x7FFFFFFF;
           for (int g = 0; g < G; ++g) {
-            const double gg = atomic_ld(&rc.peers[g].fin[fpar][0]);
-            const int gi = (int)atomic_ld(&rc.peers[g].fin[fpar][1]);
-            if (gg > bg || (gg == bg && gi < bi)) {
-              bg = gg;
-              bi = gi;
+            if (sm.gd[g] > bg || (sm.gd[g] == bg && sm.gi[g] < bi)) {
+              bg = sm.gd[g];
+              bi = sm.gi[g];
             }
           }
           if (bi != 0x7FFFFFFF) token = bi;
@@ -1327,28 +1668,33 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         const bool aborted = atomic_ld(kp.abort_word) == kp.epoch;
         kp.token_ids[row] = aborted ? -1 : token;
         if (kp.row_status) kp.row_status[row] = aborted ? 3 : 0;
-        if (general && K > 0) {
-          // merge the G local lists: K rounds of a max below the previous pick
-          unsigned long long lastk = ~0ull;
-          for (int t = 0; t < K; ++t) {
-            unsigned long long best = 0;
-            for (int g = 0; g < G; ++g)
-              for (int u = 0; u < K; ++u) {
-                const unsigned long long c = atomic_ld(&rc.peers[g].toplist[fpar][u]);
-                if (c < lastk && c > best) best = c;
-              }
-            lastk = best;
-            const int64_t o = (int64_t)row * K + t;
-            if (best == 0) {
-              kp.top_lp_vals[o] = -INFINITY;
-              kp.top_lp_ids[o] = -1;
-            } else {
-              const float zz = key_to_float((uint32_t)(best >> 32));
-              kp.top_lp_vals[o] = (float)(((double)zz - m) - lnS);
-              kp.top_lp_ids[o] = (int)(0xFFFFFFFFu - (uint32_t)(best & 0xFFFFFFFFu));
-            }
-          }
+      }
+    }
+    if (general && K > 0 && sm.bu[15]) {
+      // merge the G local top-logprob lists (keys are distinct: each holds
+      // its index): an entry's rank among all entries is its output slot
+      unsigned long long *ent = reinterpret_cast<unsigned long long *>(region);
+      const int ne = G * K;
+      for (int e = tid; e < ne; e += kBlock) ent[e] = atomic_ld(&rc.peers[e / K].toplist[fpar][e % K]);
+      __syncthreads();
+      uint32_t nz = 0;
+      for (int e = tid; e < ne; e += kBlock) {
+        const unsigned long long key = ent[e];
+        if (key == 0) continue;
+        ++nz;
+        int r = 0;
+        for (int j = 0; j < ne; ++j) r += ent[j] > key ? 1 : 0;
+        if (r < K) {
+          const int64_t o = (int64_t)row * K + r;
+          const float zz = key_to_float((uint32_t)(key >> 32));
+          kp.top_lp_vals[o] = (float)(((double)zz - m) - lnS);
+          kp.top_lp_ids[o] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
         }
+      }
+      const uint32_t nzt = (uint32_t)wg_sum_u(sm, nz);
+      for (int r = (int)nzt + tid; r < K; r += kBlock) {
+        kp.top_lp_vals[(int64_t)row * K + r] = -INFINITY;
+        kp.top_lp_ids[(int64_t)row * K + r] = -1;
       }
     }
     __syncthreads();
@@ -1356,11 +1702,16 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
 }
 
 template <typename TIn, bool PEN>
-hipError_t launch_t(const KernelParams &kp, hipStream_t stream) {
-  void *args[] = {const_cast<KernelParams *>(&kp)};
+hipError_t launch_t(const KernelParams &kp, bool cooperative, hipStream_t stream) {
   const size_t lds = kernel_lds_bytes(kp.slice, kp.hash_slots, PEN);
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&row_kernel<TIn, PEN>),
-                                    dim3(kp.n_groups * kp.G), dim3(kBlock), args, (unsigned)lds, stream);
+  const dim3 grid(kp.n_groups * kp.G), block(kBlock);
+  if (cooperative) {
+    void *args[] = {const_cast<KernelParams *>(&kp)};
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&row_kernel<TIn, PEN>), grid, block, args,
+                                      (unsigned)lds, stream);
+  }
+  hipLaunchKernelGGL((row_kernel<TIn, PEN>), grid, block, (unsigned)lds, stream, kp);
+  return hipGetLastError();
 }
 
 template <typename TIn, bool PEN>
@@ -1374,12 +1725,11 @@ hipError_t set_lds_attr(size_t lds) {
 size_t kernel_lds_fixed() { return sizeof(SmemBase); }
 
 size_t kernel_lds_region(int slice, int hash_slots, bool penalties) {
-  // window histogram (masses first, 8-byte aligned), then the leader's
-  // candidate arrays after it
-  const size_t hist = sizeof(unsigned long long) * (kMassBins + 1) + sizeof(uint32_t) * (kWinBins + 4);
-  size_t r = hist + (sizeof(float) + sizeof(int32_t)) * 2 * (size_t)kCandCap + sizeof(double) * kCandCap;
-  const size_t radix = 2 * 256 * sizeof(uint32_t) + 2 * 256 * sizeof(unsigned long long);
+  size_t r = kRegionB + kRegionBBytes;
+  const size_t radix = 3072 + 8 * 256;
   r = r > radix ? r : radix;
+  const size_t merge = 8 * (size_t)kMaxG * kMaxTopLogprobs;
+  r = r > merge ? r : merge;
   if (penalties) {
     const size_t pen = sizeof(uint32_t) * ((size_t)hash_slots + ((size_t)slice + 31) / 32 + 1);
     r = r > pen ? r : pen;
@@ -1391,9 +1741,10 @@ size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties) {
   return kernel_lds_fixed() + sizeof(float) * (size_t)slice + kernel_lds_region(slice, hash_slots, penalties);
 }
 
-hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, hipStream_t stream) {
-  if (dtype == 0) return penalties ? launch_t<float, true>(kp, stream) : launch_t<float, false>(kp, stream);
-  return penalties ? launch_t<uint16_t, true>(kp, stream) : launch_t<uint16_t, false>(kp, stream);
+hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, bool cooperative, hipStream_t stream) {
+  if (dtype == 0)
+    return penalties ? launch_t<float, true>(kp, cooperative, stream) : launch_t<float, false>(kp, cooperative, stream);
+  return penalties ? launch_t<uint16_t, true>(kp, cooperative, stream) : launch_t<uint16_t, false>(kp, cooperative, stream);
 }
 
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out) {

@@ -269,7 +269,7 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
   }
   if (cfg->max_rows < 1 || cfg->max_vocab < 1 || cfg->max_vocab > kMaxVocab || cfg->max_history_per_row < 0 ||
       cfg->max_history_per_row > kMaxHistPerRow || cfg->max_top_logprobs < 0 ||
-      cfg->max_top_logprobs > kMaxTopLogprobs || (cfg->flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED))) {
+      cfg->max_top_logprobs > kMaxTopLogprobs || (cfg->flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH))) {
     set_msg(g_create_error,
             "bad config: need max_rows >= 1, 1 <= max_vocab <= %d, 0 <= max_history_per_row <= %d, "
             "0 <= max_top_logprobs <= %d and known flags",
@@ -499,7 +499,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.epoch = h->epoch;
   const bool prof = h->prof_n < h->prof_cap;
   if (prof && (e = hipEventRecord(h->prof[2 * h->prof_n], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  e = launch_step(kp, a->dtype, any_pen, stream);
+  e = launch_step(kp, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream);
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   if (prof) {
     if ((e = hipEventRecord(h->prof[2 * h->prof_n + 1], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");

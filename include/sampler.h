@@ -68,6 +68,15 @@ typedef enum sampler_dtype {
  * outputs are identical by construction; this is the A/B switch for the
  * specialised kernels. */
 #define SAMPLER_FORCE_FILTERED (1u << 1)
+/* Launch through hipLaunchCooperativeKernel, so the runtime itself checks
+ * that every workgroup of a step is resident at once (the workgroups of a
+ * row wait on one another).  Without the flag the step is a plain launch
+ * whose grid never exceeds what the device holds at once, which makes all
+ * workgroups resident whenever no other kernel occupies the compute units
+ * at the same time (cooperative launches cost ~12 us more per step on
+ * MI355X).  Either way every wait is bounded: a wait that expires marks the
+ * step's rows with row_status 3. */
+#define SAMPLER_COOPERATIVE_LAUNCH (1u << 2)
 
 typedef struct sampler_config {
   int32_t max_rows;            /* largest n_rows a step may pass (>= 1) */
@@ -75,7 +84,7 @@ typedef struct sampler_config {
   int32_t max_history_per_row; /* largest history_len of one row (0..4096) */
   int32_t max_top_logprobs;    /* largest top_logprobs (0..32) */
   int32_t device;              /* HIP device ordinal */
-  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED */
+  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH */
 } sampler_config;
 
 typedef struct sampler_handle sampler_handle;

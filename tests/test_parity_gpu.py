@@ -256,3 +256,18 @@ def test_gumbel_distribution_chi2_and_exact_tokens():
         p = scipy.stats.chisquare(obs, ex * (obs.sum() / ex.sum())).pvalue
         assert p > 1e-3, (top_k, p)
     s.close()
+
+
+def test_cooperative_launch_is_identical():
+    # the plain launch (default) and the cooperative one run the same kernel
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    a = dsts.Sampler(64, 128_000, max_history_per_row=2048)
+    c = dsts.Sampler(64, 128_000, max_history_per_row=2048, cooperative_launch=True)
+    b = workloads.config(4, n_rows=24)
+    ga, gc = run_gpu(a, b), run_gpu(c, b)
+    for k in ("token_ids", "probs", "logprobs", "row_status"):
+        np.testing.assert_array_equal(ga[k], gc[k])
+    assert np.all(ga["row_status"] == 0)
+    a.close()
+    c.close()
