@@ -31,13 +31,12 @@ constexpr int32_t kMaxVocab = 1 << 20;
 constexpr int kBlock = 512;
 constexpr int kMaxSlice = 32768;
 
-// Threshold window: values whose distance d = max - z, times min(1, T), is
-// below 16 are counted, and their masses exp(-d) summed in 2^-31 units, in
-// bins of 1/32 of that scaled distance; deeper values only add to a
-// per-workgroup mass total.  kWinBins equals kBlock: the merge gives each
-// thread one bin.
+// Threshold window: values are binned on an absolute grid, bin(z) =
+// floor(z min(1, T) 32), counted down from the bin of the row max (so the
+// window spans 16 nats of z / max(1, 1/T)); kWinBins bins hold counts and
+// masses exp(z - max) in 2^-31 units, the deeper values only a mass total.
+// kWinBins equals kBlock: the merge gives each thread one bin.
 constexpr int kWinBins = 512;
-constexpr float kWinNats = 16.0f;
 constexpr float kBinsPerNat = 32.0f;
 // Candidates (values in the bins that hold a threshold or the top logprobs)
 // gathered per row for exact selection; more sends the row to the general
@@ -95,13 +94,16 @@ struct alignas(128) GroupRec {
 // Exchange slots owned by one workgroup (indexed by its block id), laid out
 // like GroupRec for 16-byte reads.
 struct alignas(128) WgSlots {
-  unsigned long long e1[2][2];                    // exchange 1: (max key << 32 | ~argmax), by row parity
-  double fin[2][2];                               // best Gumbel score and its index, by row parity
-  double spart[2];                                // exact sum of exp(z - m) over the slice, by row parity
+  // exchange 2, by row parity: the order key of this slice's max, the
+  // slice's bin anchor (float bits), and relative to the slice's max the
+  // mass of the values deeper than the window and the exact sum (fp64 bits)
+  unsigned long long x1[2][4];
+  // final exchange, by row parity: best Gumbel score (fp64 bits), its
+  // index, this slice's max order key
+  unsigned long long fin[2][4];
   uint32_t cand_n;                                // candidates gathered by this workgroup
-  uint32_t pad0[11];
+  uint32_t pad0[31];
   unsigned long long whist[kWinBins];             // window bins: count << 48 | mass (2^-31 units)
-  unsigned long long wdeep[2];                    // mass of the deeper values (2^-31 units)
   unsigned long long cand[kCandCap];              // candidate keys: order key << 32 | ~index
   uint32_t hcnt[2][256];                          // general path: radix counts
   unsigned long long hmass[2][256];               // general path: radix masses
@@ -109,7 +111,7 @@ struct alignas(128) WgSlots {
   double ssum[2];                                 // general path: kept-set sum
 };
 static_assert(offsetof(GroupRec, cum_cnt) % 16 == 0 && offsetof(GroupRec, cum_mass) % 16 == 0, "GroupRec layout");
-static_assert(offsetof(WgSlots, fin) % 16 == 0 && offsetof(WgSlots, whist) % 16 == 0 &&
+static_assert(offsetof(WgSlots, x1) % 16 == 0 && offsetof(WgSlots, fin) % 16 == 0 && offsetof(WgSlots, whist) % 16 == 0 &&
                   offsetof(WgSlots, cand) % 16 == 0,
               "WgSlots layout");
 

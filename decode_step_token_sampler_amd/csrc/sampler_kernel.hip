@@ -85,6 +85,10 @@ struct alignas(16) SmemBase {
   double bd[16];
   uint32_t dec[32];              // decision words of the group record
   double gd[kMaxG];              // per-workgroup values read by a merger
+  double gf[kMaxG];
+  double gs[kMaxG];
+  unsigned long long gk[kMaxG];
+  float ga[kMaxG];
   int gi[kMaxG];
   uint32_t gcnt[kMaxG];          // merger: candidates per workgroup
   uint32_t gpo[kMaxG + 1];       // merger: 16-byte pair offsets per workgroup
@@ -499,15 +503,18 @@ struct RowCtx {
 
 DEV void row_barrier(SmemBase &sm, RowCtx &rc) { group_barrier(sm, rc.gsync, rc.G, rc.abort_word, rc.epoch); }
 
-// Window bin of a value: its distance d = max - z, scaled by wsc =
-// min(1, T) (so the window spans at least 16 nats of the logits themselves,
-// whatever the temperature), in 1/32 steps; kWinBins from 16 on.  Monotone
-// in z, so the bins partition the value axis in order.  Every bin of the
-// kernel is computed by this expression.
-DEV float win_dist(float mf, float z, float wsc) { return (mf - z) * wsc; }
-DEV int win_bin(float mf, float z, float wsc) {
-  const float dd = win_dist(mf, z, wsc);
-  return dd < kWinNats ? (int)(dd * kBinsPerNat) : kWinBins;
+// Bins on an absolute grid: abin(z) = floor(z wsc 32) with wsc = min(1, T),
+// so a bin is 1/32 nat of the logits x = z T below T = 1 and of z above it.
+// A value's window bin is A - abin(z), counted down from the anchor A =
+// abin(row max); bins from kWinBins on are deep.  Every bin of the kernel is
+// computed by these two expressions (float operations: monotone in z, so
+// the bins partition the value axis in order, and an anchor shift between
+// two slices is a whole number of bins while |z wsc 32| < 2^24).
+DEV float abin(float z, float wsc) { return floorf((z * wsc) * kBinsPerNat); }
+DEV float win_pos(float A, float z, float wsc) { return A - abin(z, wsc); }
+DEV int win_bin(float A, float z, float wsc) {
+  const float lb = win_pos(A, z, wsc);
+  return lb < (float)kWinBins ? (int)lb : kWinBins;
 }
 
 // Window histogram entry of one value at distance d = max - z: a count of
@@ -693,7 +700,10 @@ enum : int {
   D_RKLO = 7,
   D_RKHI = 8,
   D_BM = 9,
-  D_MASK = 16,  // 16 words: bitmask of the gathered bins
+  D_STATUS = 10,  // row status (1: no finite logit, 2: +inf after temperature)
+  D_ARGMAX = 11,  // first argmax of the row
+  D_TM = 12,      // min-p's boundary key
+  D_MASK = 16,    // 16 words: bitmask of the gathered bins
 };
 static_assert(D_MASK + kWinBins / 32 <= (int)(sizeof(GroupRec::dec) / sizeof(uint32_t)), "decision words");
 
@@ -899,249 +909,302 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
     }
 
-    // ---- 2. exchange 1: row max and first argmax, as one order key
-    // (value key << 32 | ~index: the largest key is the first argmax)
-    const unsigned long long wam = wg_max_u(sm, ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx));
+    // ---- 2. this slice's max and first argmax as one order key (value key
+    // << 32 | ~index: the largest key is the first argmax)
+    const unsigned long long lkey = wg_max_u(sm, ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx));
+    const float mg = key_to_float((uint32_t)(lkey >> 32));  // -inf: no finite value in this slice
     const unsigned par = it & 1u;
-    if (tid == 0) atomic_st(&rc.my->e1[par][0], wam);
-    row_barrier(sm, rc);
-    if (wave == 0) {
-      unsigned long long a = lane < G ? atomic_ld(&rc.peers[lane].e1[par][0]) : 0ull;
-      a = wave_max_u(a);
-      if (lane == 0) {
-        sm.bd[0] = (double)key_to_float((uint32_t)(a >> 32));
-        sm.bu[0] = 0xFFFFFFFFu - (uint32_t)(a & 0xFFFFFFFFu);
-      }
-    }
-    __syncthreads();
-    const double m = sm.bd[0];
-    const int argmax_idx = (int)sm.bu[0];
-    __syncthreads();
-
-    // ---- rows with no finite logit (status 1) or a +inf value (status 2)
-    if (!(m > -INFINITY) || m == INFINITY) {
-      if (want_out) {
-        for (int l = tid; l < ln; l += kBlock) {
-          if (kp.probs) kp.probs[(int64_t)row * V + s0 + l] = 0.0f;
-          if (kp.logprobs) kp.logprobs[(int64_t)row * V + s0 + l] = -INFINITY;
-        }
-      }
-      if (gid == 0 && tid == 0) {
-        kp.token_ids[row] = -1;
-        if (kp.row_status) kp.row_status[row] = (m == INFINITY) ? 2 : 1;
-        for (int t = 0; t < K; ++t) {
-          kp.top_lp_vals[(int64_t)row * K + t] = -INFINITY;
-          kp.top_lp_ids[(int64_t)row * K + t] = -1;
-        }
-      }
-      __syncthreads();
-      continue;
-    }
-    const float mf = (float)m;
-    const float wsc = T < 1.0f ? T : 1.0f;  // window scale (see win_bin)
-    const uint32_t t_m = minp ? min_p_key(sm, m, P.min_p) : 0u;
-
-    // ---- 3. window histogram (exchange 2, merged by the last workgroup to
-    // arrive): counts for top-k and the gather, masses for top-p and the
-    // kept-set sum, and the exact fp64 sum when every token is kept.
+    const float wsc = T < 1.0f ? T : 1.0f;  // bin scale (see abin)
     const bool need_sel = topk || topp || K > 0 || (truncated && want_S);  // window + candidates
     const bool need_mass = topp || (truncated && want_S);
     const bool need_deep = topp && !topk;  // top-p's total includes the deep values
     const bool need_exact = !truncated && want_S;
+    // rows that need the merged max: thresholds, sums or min-p's boundary.
+    // The rest (no truncation, no outputs) prune against their own slice's
+    // max and settle argmax and status in the final exchange.
+    const bool need_x = need_sel || need_exact || minp;
+    double m = (double)mg;
+    int argmax_idx = (int)(0xFFFFFFFFu - (uint32_t)lkey);
+    uint32_t t_m = 0;
+    float Af = 0.0f;  // window anchor abin(row max)
     bool general = false;
     bool full_k = false;
     bool topk_on = topk;  // top-k decides (part of) the kept set
-    uint32_t tau = truncated && !need_sel ? t_m : 0u;  // min-p alone without outputs: closed form
+    uint32_t tau = 0;
     double lnS = 0.0;
     int r0hi = -1, r1lo = 1, r1hi = 0, rklo = 1, rkhi = 0, bm = -1;
-    if (need_sel || need_exact) {
+    if (need_x) {
+      // ---- 3. window histogram of this slice on the absolute bin grid,
+      // anchored at its own max, masses relative to its own max; the exact
+      // fp64 sum when every token is kept.  Exchange 2: the last workgroup
+      // to arrive finds the row max, shifts each histogram by whole bins,
+      // rescales its masses and decides in parallel.
+      const bool finite_g = mg > -INFINITY && mg < INFINITY;
+      const float Ag = finite_g ? abin(mg, wsc) : 0.0f;
       if (need_sel) {
         wh[tid] = 0;
         __syncthreads();
       }
       double deep_a = 0.0;  // deeper masses, 2^-31 units
       double sx = 0.0;
-      for (int l = 4 * tid; l < ln4; l += 4 * kBlock) {
-        const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+      if (finite_g && (need_sel || need_exact)) {
+        for (int l = 4 * tid; l < ln4; l += 4 * kBlock) {
+          const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const float zz = zv[c];
-          const float d = mf - zz;  // padding: +inf
-          if (need_sel) {
-            const float dd = win_dist(mf, zz, wsc);
-            const bool near = dd < kWinNats;
-            const float a = mass_scaled(d);
-            if (near) atomicAdd(&wh[(int)(dd * kBinsPerNat)], hist_entry(a));
-            if (need_deep) deep_a += near ? 0.0 : (double)a;
+          for (int c = 0; c < 4; ++c) {
+            const float zz = zv[c];
+            if (need_sel) {
+              const float lb = win_pos(Ag, zz, wsc);  // padding: +inf
+              const bool near = lb < (float)kWinBins;
+              const float a = mass_scaled(mg - zz);
+              if (near) atomicAdd(&wh[(int)lb], hist_entry(a));
+              if (need_deep) deep_a += near ? 0.0 : (double)a;
+            }
+            if (need_exact) sx += exp_nonpos(sm.exp_tab, (double)zz - (double)mg);
           }
-          if (need_exact) sx += exp_nonpos(sm.exp_tab, (double)zz - m);
         }
       }
       const double wdm = need_deep ? wg_sum_d(sm, deep_a) : 0.0;
       const double wsx = need_exact ? wg_sum_d(sm, sx) : 0.0;
       __syncthreads();
-      // this workgroup's histogram -> its exchange slot
+      // this workgroup's record and histogram -> its exchange slot
       if (need_sel) atomic_st(&rc.my->whist[tid], wh[tid]);
       if (tid == 0) {
-        atomic_st(&rc.my->wdeep[0], (unsigned long long)__double2ll_rn(wdm));
-        atomic_st(&rc.my->spart[par], wsx);
+        atomic_st(&rc.my->x1[par][0], lkey);
+        atomic_st(&rc.my->x1[par][1], (unsigned long long)__float_as_uint(Ag));
+        atomic_st(&rc.my->x1[par][2], (unsigned long long)__double_as_longlong(wdm));
+        atomic_st(&rc.my->x1[par][3], (unsigned long long)__double_as_longlong(wsx));
       }
       if (group_arrive(sm, rc.gsync, G)) {
-        // ---- merge (last arrival): sum the G histograms (16-byte reads,
-        // integer LDS adds: order-free), inclusive prefix sums over the bins
-        // (thread b owns bin b), then every decision in parallel
-        if (need_sel) {
-          const int b = tid;
-          lc[b] = 0;
-          lm[b] = 0;
-          if (tid == 0) lm[kWinBins] = 0;
+        // ---- merge (last arrival)
+        if (tid < G) {
+          u32x4 r0, r1;
+          coh_load16x2(&rc.peers[tid].x1[par][0], &rc.peers[tid].x1[par][2], r0, r1);
+          sm.gk[tid] = u64_of(r0.x, r0.y);
+          sm.ga[tid] = __uint_as_float(r0.z);
+          sm.gd[tid] = f64_of(r1.z, r1.w);                        // exact sum
+          sm.gf[tid] = f64_of(r1.x, r1.y);                        // deep mass (scaled below)
+        }
+        __syncthreads();
+        unsigned long long mk = 0;
+        for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
+        const float mfx = key_to_float((uint32_t)(mk >> 32));
+        const double mx = (double)mfx;
+        const uint32_t status = (mfx > -INFINITY && mfx < INFINITY) ? 0u : (mfx == INFINITY ? 2u : 1u);
+        uint32_t tmx = 0;
+        uint32_t flags = 0;
+        if (status == 0) {
+          const float A = abin(mfx, wsc);
+          if (minp) tmx = min_p_key(sm, mx, P.min_p);
+          // per-workgroup mass scale exp(m_g - m) and bin shift A - A_g
+          double deep_x = 0.0;  // window bins of a slice that fall past the row's window
+          if (tid < G) {
+            const float mgg = key_to_float((uint32_t)(sm.gk[tid] >> 32));
+            const double f = mgg > -INFINITY ? exp_nonpos(sm.exp_tab, (double)mgg - mx) : 0.0;
+            const float sh = A - sm.ga[tid];  // whole bins, >= 0
+            sm.gi[tid] = (mgg > -INFINITY && sh < (float)kWinBins) ? (int)sh : kWinBins;
+            sm.gd[tid] *= f;  // exact sums, rescaled
+            sm.gf[tid] *= f;  // deep masses, rescaled
+            sm.gs[tid] = f;
+          }
           __syncthreads();
-          // two bins per 16-byte read, two reads per pass (the second
-          // repeats the first when out of range and is then ignored)
-          constexpr int kPairs = kWinBins / 2;
-          for (int pi = tid; pi < G * kPairs; pi += 2 * kBlock) {
-            const int pj = pi + kBlock < G * kPairs ? pi + kBlock : pi;
-            u32x4 ra, rb;
-            coh_load16x2(&rc.peers[pi / kPairs].whist[2 * (pi % kPairs)], &rc.peers[pj / kPairs].whist[2 * (pj % kPairs)], ra, rb);
-            const unsigned long long h[4] = {u64_of(ra.x, ra.y), u64_of(ra.z, ra.w), u64_of(rb.x, rb.y), u64_of(rb.z, rb.w)};
-            const int b0[2] = {2 * (pi % kPairs), 2 * (pj % kPairs)};
+          if (need_sel) {
+            const int b = tid;
+            lc[b] = 0;
+            lm[b] = 0;
+            if (tid == 0) lm[kWinBins] = 0;
+            __syncthreads();
+            // two bins per 16-byte read, two reads per pass (the second
+            // repeats the first when out of range and is then ignored);
+            // integer LDS adds of each slice's rescaled, rounded masses:
+            // order-free
+            constexpr int kPairs = kWinBins / 2;
+            for (int pi = tid; pi < G * kPairs; pi += 2 * kBlock) {
+              const int pj = pi + kBlock < G * kPairs ? pi + kBlock : pi;
+              u32x4 ra, rb;
+              coh_load16x2(&rc.peers[pi / kPairs].whist[2 * (pi % kPairs)], &rc.peers[pj / kPairs].whist[2 * (pj % kPairs)], ra, rb);
+              const unsigned long long h[4] = {u64_of(ra.x, ra.y), u64_of(ra.z, ra.w), u64_of(rb.x, rb.y), u64_of(rb.z, rb.w)};
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              if (i >= 2 && pj == pi) break;
-              const unsigned long long e = h[i];
-              if (e) {
-                const int bin = b0[i >> 1] + (i & 1);
-                atomicAdd(&lc[bin], (uint32_t)(e >> 48));
-                if (need_mass) atomicAdd(&lm[bin], e & 0xFFFFFFFFFFFFull);
+              for (int i = 0; i < 4; ++i) {
+                if (i >= 2 && pj == pi) break;
+                const unsigned long long e = h[i];
+                if (e) {
+                  const int p = (i < 2) ? pi : pj;
+                  const int g = p / kPairs;
+                  const int bin = 2 * (p % kPairs) + (i & 1) + sm.gi[g];
+                  const double ms = (double)(e & 0xFFFFFFFFFFFFull) * sm.gs[g];
+                  if (bin < kWinBins) {
+                    atomicAdd(&lc[bin], (uint32_t)(e >> 48));
+                    if (need_mass) atomicAdd(&lm[bin], (unsigned long long)__double2ll_rn(ms));
+                  } else {
+                    deep_x += ms;
+                  }
+                }
               }
             }
-          }
-          if (need_deep && tid < G) atomicAdd(&lm[kWinBins], atomic_ld(&rc.peers[tid].wdeep[0]));
-          __syncthreads();
-          const uint32_t cb = lc[b];
-          const unsigned long long mb = lm[b], deep = lm[kWinBins];
-          const uint32_t runc = block_scan_incl<uint32_t>(cb, sm.red_c);
-          const unsigned long long runm = block_scan_incl<unsigned long long>(mb, sm.red_u);
-          lc[b] = runc;
-          lm[b] = runm;
-          if (b == kWinBins - 1) lm[kWinBins] = runm + deep;
-          if (tid == 0) {
-            sm.bu[16] = kNone;
-            sm.bu[17] = kNone;
-            sm.bu[18] = kNone;
-            sm.bu[19] = kNone;
-          }
-          __syncthreads();
-          atomic_st(&rec->cum_cnt[b], runc);
-          atomic_st(&rec->cum_mass[b], runm);
-          if (b == kWinBins - 1) atomic_st(&rec->cum_mass[kWinBins], runm + deep);
-          // bins of the k-th and the K-th value
-          const uint32_t cprev = b > 0 ? lc[b - 1] : 0u;
-          if (topk && cprev < (uint32_t)P.top_k && runc >= (uint32_t)P.top_k) sm.bu[16] = (uint32_t)b;
-          if (K > 0 && cprev < (uint32_t)K && runc >= (uint32_t)K) sm.bu[17] = (uint32_t)b;
-          __syncthreads();
-          const uint32_t bk = sm.bu[16], r0 = sm.bu[17];
-          bool gen = false;
-          bool fk = false;
-          bool k_off = false;
-          int e_r0hi = -1, e_r1lo = 1, e_r1hi = 0, e_rklo = 1, e_rkhi = 0, e_bm = -1;
-          const int bmin = minp ? win_bin(mf, key_to_float(t_m), wsc) : kWinBins;
-          if (K > 0) {
-            if (r0 != kNone) e_r0hi = (int)r0;
-            else if (truncated) e_r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
-            else gen = true;
-          }
-          if (topk) {
-            if (bk != kNone) {
-              if (lc[bk] <= (uint32_t)kCandCap) {
-                fk = true;
-                e_rklo = 0;
-                e_rkhi = (int)bk;
-              } else {
-                e_rklo = e_rkhi = (int)bk;
-              }
-            } else if (topp || !(minp && bmin < kWinBins)) {
-              gen = true;  // the k-th value is deeper than the window and decides the kept set
-            } else {
-              k_off = true;
+            const double deep_w = need_deep ? wg_sum_d(sm, deep_x) : 0.0;
+            __syncthreads();
+            const uint32_t cb = lc[b];
+            const unsigned long long mb = lm[b];
+            unsigned long long deep = 0;
+            if (need_deep) {
+              double dt = deep_w;
+              for (int g = 0; g < G; ++g) dt += sm.gf[g];
+              deep = (unsigned long long)__double2ll_rn(dt);
             }
-          }
-          // top-p: the bins where the cumulative mass crosses p times the
-          // total mass of the top-k set (bounded below and above)
-          double tlo = 0.0, thi = 0.0;
-          if (topp && !gen) {
+            const uint32_t runc = block_scan_incl<uint32_t>(cb, sm.red_c);
+            const unsigned long long runm = block_scan_incl<unsigned long long>(mb, sm.red_u);
+            lc[b] = runc;
+            lm[b] = runm;
+            if (b == kWinBins - 1) lm[kWinBins] = runm + deep;
+            if (tid == 0) {
+              sm.bu[16] = kNone;
+              sm.bu[17] = kNone;
+              sm.bu[18] = kNone;
+              sm.bu[19] = kNone;
+            }
+            __syncthreads();
+            atomic_st(&rec->cum_cnt[b], runc);
+            atomic_st(&rec->cum_mass[b], runm);
+            if (b == kWinBins - 1) atomic_st(&rec->cum_mass[kWinBins], runm + deep);
+            // bins of the k-th and the K-th value
+            const uint32_t cprev = b > 0 ? lc[b - 1] : 0u;
+            if (topk && cprev < (uint32_t)P.top_k && runc >= (uint32_t)P.top_k) sm.bu[16] = (uint32_t)b;
+            if (K > 0 && cprev < (uint32_t)K && runc >= (uint32_t)K) sm.bu[17] = (uint32_t)b;
+            __syncthreads();
+            const uint32_t bk = sm.bu[16], r0 = sm.bu[17];
+            bool gen = false;
+            bool fk = false;
+            bool k_off = false;
+            int e_r0hi = -1, e_r1lo = 1, e_r1hi = 0, e_rklo = 1, e_rkhi = 0, e_bm = -1;
+            const int bmin = minp ? win_bin(A, key_to_float(tmx), wsc) : kWinBins;
+            if (K > 0) {
+              if (r0 != kNone) e_r0hi = (int)r0;
+              else if (truncated) e_r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
+              else gen = true;
+            }
             if (topk) {
-              tlo = (double)P.top_p * (bk > 0 ? (double)lm[bk - 1] : 0.0);
-              thi = (double)P.top_p * (double)lm[bk];
-            } else {
-              tlo = thi = (double)P.top_p * (double)lm[kWinBins];
-            }
-            const double mprev = b > 0 ? (double)lm[b - 1] : 0.0, mcur = (double)lm[b];
-            if (mprev < tlo && mcur >= tlo) sm.bu[18] = (uint32_t)b;
-            if (mprev < thi && mcur >= thi) sm.bu[19] = (uint32_t)b;
-          }
-          __syncthreads();
-          if (topp && !gen) {
-            const uint32_t lo = tlo <= 0.0 ? 0u : sm.bu[18], hi = sm.bu[19];
-            if (hi == kNone) {
-              gen = true;  // the crossing lies deeper than the window
-            } else {
-              e_r1lo = (int)(lo == kNone ? hi : lo);
-              e_r1hi = (int)hi;
-              if (topk) {
-                e_r1lo = min(e_r1lo, (int)bk);
-                e_r1hi = min(e_r1hi, (int)bk);
+              if (bk != kNone) {
+                if (lc[bk] <= (uint32_t)kCandCap) {
+                  fk = true;
+                  e_rklo = 0;
+                  e_rkhi = (int)bk;
+                } else {
+                  e_rklo = e_rkhi = (int)bk;
+                }
+              } else if (topp || !(minp && bmin < kWinBins)) {
+                gen = true;  // the k-th value is deeper than the window and decides the kept set
+              } else {
+                k_off = true;
               }
             }
-          }
-          if (minp && !gen) {
-            if (bmin < kWinBins) e_bm = bmin;
-            else if (!topk && !topp) gen = true;  // min-p alone keeps values deeper than the window
-          }
-          // gathered bins and their total count
-          const bool in = !gen && (b <= e_r0hi || (b >= e_r1lo && b <= e_r1hi) || (b >= e_rklo && b <= e_rkhi) || b == e_bm);
-          const unsigned long long bal = __ballot(in);
-          if (lane == 0) {
-            atomic_st(&rec->dec[D_MASK + 2 * wave], (uint32_t)bal);
-            atomic_st(&rec->dec[D_MASK + 2 * wave + 1], (uint32_t)(bal >> 32));
-          }
-          const uint32_t ncand = (uint32_t)wg_sum_u(sm, in ? (unsigned long long)cb : 0ull);
-          if (ncand > (uint32_t)kCandCap) gen = true;
-          if (tid == 0) {
-            atomic_st(&rec->dec[D_FLAGS], (gen ? 1u : 0u) | (fk ? 2u : 0u) | (k_off ? 4u : 0u));
-            atomic_st(&rec->dec[D_R0HI], (uint32_t)e_r0hi);
-            atomic_st(&rec->dec[D_R1LO], (uint32_t)e_r1lo);
-            atomic_st(&rec->dec[D_R1HI], (uint32_t)e_r1hi);
-            atomic_st(&rec->dec[D_RKLO], (uint32_t)e_rklo);
-            atomic_st(&rec->dec[D_RKHI], (uint32_t)e_rkhi);
-            atomic_st(&rec->dec[D_BM], (uint32_t)e_bm);
+            // top-p: the bins where the cumulative mass crosses p times the
+            // total mass of the top-k set (bounded below and above)
+            double tlo = 0.0, thi = 0.0;
+            if (topp && !gen) {
+              if (topk) {
+                tlo = (double)P.top_p * (bk > 0 ? (double)lm[bk - 1] : 0.0);
+                thi = (double)P.top_p * (double)lm[bk];
+              } else {
+                tlo = thi = (double)P.top_p * (double)lm[kWinBins];
+              }
+              const double mprev = b > 0 ? (double)lm[b - 1] : 0.0, mcur = (double)lm[b];
+              if (mprev < tlo && mcur >= tlo) sm.bu[18] = (uint32_t)b;
+              if (mprev < thi && mcur >= thi) sm.bu[19] = (uint32_t)b;
+            }
+            __syncthreads();
+            if (topp && !gen) {
+              const uint32_t lo = tlo <= 0.0 ? 0u : sm.bu[18], hi = sm.bu[19];
+              if (hi == kNone) {
+                gen = true;  // the crossing lies deeper than the window
+              } else {
+                e_r1lo = (int)(lo == kNone ? hi : lo);
+                e_r1hi = (int)hi;
+                if (topk) {
+                  e_r1lo = min(e_r1lo, (int)bk);
+                  e_r1hi = min(e_r1hi, (int)bk);
+                }
+              }
+            }
+            if (minp && !gen) {
+              if (bmin < kWinBins) e_bm = bmin;
+              else if (!topk && !topp) gen = true;  // min-p alone keeps values deeper than the window
+            }
+            // the bin grid overflows for |m / T| beyond ~1e37: exact path
+            if (!(A > -INFINITY && A < INFINITY)) gen = true;
+            // gathered bins and their total count
+            const bool in = !gen && (b <= e_r0hi || (b >= e_r1lo && b <= e_r1hi) || (b >= e_rklo && b <= e_rkhi) || b == e_bm);
+            const unsigned long long bal = __ballot(in);
+            if (lane == 0) {
+              atomic_st(&rec->dec[D_MASK + 2 * wave], (uint32_t)bal);
+              atomic_st(&rec->dec[D_MASK + 2 * wave + 1], (uint32_t)(bal >> 32));
+            }
+            const uint32_t ncand = (uint32_t)wg_sum_u(sm, in ? (unsigned long long)cb : 0ull);
+            if (ncand > (uint32_t)kCandCap) gen = true;
+            flags = (gen ? 1u : 0u) | (fk ? 2u : 0u) | (k_off ? 4u : 0u);
+            if (tid == 0) {
+              atomic_st(&rec->dec[D_R0HI], (uint32_t)e_r0hi);
+              atomic_st(&rec->dec[D_R1LO], (uint32_t)e_r1lo);
+              atomic_st(&rec->dec[D_R1HI], (uint32_t)e_r1hi);
+              atomic_st(&rec->dec[D_RKLO], (uint32_t)e_rklo);
+              atomic_st(&rec->dec[D_RKHI], (uint32_t)e_rkhi);
+              atomic_st(&rec->dec[D_BM], (uint32_t)e_bm);
+            }
           }
         }
-        if (need_exact) {
-          if (tid < G) sm.gd[tid] = atomic_ld(&rc.peers[tid].spart[par]);
-          __syncthreads();
-          if (tid == 0) {
-            double S_all = 0.0;
+        if (tid == 0) {
+          double S_all = 0.0;
+          if (status == 0 && need_exact)
             for (int g = 0; g < G; ++g) S_all += sm.gd[g];
-            atomic_st(&rec->dd[0], S_all);
-          }
+          atomic_st(&rec->dd[0], S_all);
+          atomic_st(&rec->dd[1], mx);
+          atomic_st(&rec->dec[D_FLAGS], flags);
+          atomic_st(&rec->dec[D_STATUS], status);
+          atomic_st(&rec->dec[D_ARGMAX], 0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
+          atomic_st(&rec->dec[D_TM], tmx);
         }
         group_release(rc.gsync);
       } else {
         group_wait(sm, rc.gsync, rc.abort_word, rc.epoch);
       }
-      // decisions (32 words) and the exact sum: 16-byte reads in parallel
-      if (need_sel && tid < 8) {
+      // decisions (32 words), the exact sum and the row max: 16-byte reads
+      // in parallel
+      if (tid < 8) {
         const u32x4 r = coh_load16(&rec->dec[4 * tid]);
         sm.dec[4 * tid] = r.x;
         sm.dec[4 * tid + 1] = r.y;
         sm.dec[4 * tid + 2] = r.z;
         sm.dec[4 * tid + 3] = r.w;
-      } else if (need_exact && tid == 8) {
+      } else if (tid == 8) {
         const u32x4 r = coh_load16(&rec->dd[0]);
         sm.bd[1] = f64_of(r.x, r.y);
+        sm.bd[0] = f64_of(r.z, r.w);
       }
       __syncthreads();
+      m = sm.bd[0];
+      argmax_idx = (int)sm.dec[D_ARGMAX];
+      t_m = sm.dec[D_TM];
+      const uint32_t status = sm.dec[D_STATUS];
+      if (status != 0) {
+        // ---- no finite logit (status 1) or a +inf value (status 2)
+        if (want_out) {
+          for (int l = tid; l < ln; l += kBlock) {
+            if (kp.probs) kp.probs[(int64_t)row * V + s0 + l] = 0.0f;
+            if (kp.logprobs) kp.logprobs[(int64_t)row * V + s0 + l] = -INFINITY;
+          }
+        }
+        if (gid == 0 && tid == 0) {
+          kp.token_ids[row] = -1;
+          if (kp.row_status) kp.row_status[row] = (int)status;
+          for (int t = 0; t < K; ++t) {
+            kp.top_lp_vals[(int64_t)row * K + t] = -INFINITY;
+            kp.top_lp_ids[(int64_t)row * K + t] = -1;
+          }
+        }
+        __syncthreads();
+        continue;
+      }
+      Af = abin((float)m, wsc);
       if (need_sel) {
         general = sm.dec[D_FLAGS] & 1u;
         full_k = sm.dec[D_FLAGS] & 2u;
@@ -1152,9 +1215,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         rklo = (int)sm.dec[D_RKLO];
         rkhi = (int)sm.dec[D_RKHI];
         bm = (int)sm.dec[D_BM];
+      } else if (minp) {
+        tau = t_m;  // min-p alone without outputs: the closed-form boundary
       }
       if (need_exact) lnS = log(sm.bd[1]);
+      __syncthreads();
     }
+    const float mf = (float)m;
 
     // ---- 4. exact thresholds from the gathered candidates (exchange 3,
     // sorted and decided by the last workgroup to arrive)
@@ -1211,18 +1278,17 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           }
         }
       }
-      // value bounds of the runs: bin(d) in [lo, hi]  <=>  lo / 32 <= d < (hi + 1) / 32
-      const float d0lo = (float)run_lo[0] / kBinsPerNat, d0hi = (float)(run_hi[0] + 1) / kBinsPerNat;
-      const float d1lo = (float)run_lo[1] / kBinsPerNat, d1hi = (float)(run_hi[1] + 1) / kBinsPerNat;
-      const float d_cut = more ? kWinNats : max(d0hi, d1hi);
-      // branch-free membership: the two runs by value, or (more than two
-      // runs, rare) the bin mask
-      auto is_cand = [&](float d) -> bool {
+      // the run bounds as window positions (integer-valued floats)
+      const float p0lo = (float)run_lo[0], p0hi = (float)run_hi[0];
+      const float p1lo = (float)run_lo[1], p1hi = (float)run_hi[1];
+      // branch-free membership of window position lb: the two runs by
+      // value, or (more than two runs, rare) the bin mask
+      auto is_cand = [&](float lb) -> bool {
         if (more) {
-          const int bb = min((int)(d * kBinsPerNat), kWinBins - 1);
-          return (d < d_cut) & (bool)((sm.dec[D_MASK + (bb >> 5)] >> (bb & 31)) & 1u);
+          const int bb = min((int)lb, kWinBins - 1);
+          return (lb < (float)kWinBins) & (bool)((sm.dec[D_MASK + (bb >> 5)] >> (bb & 31)) & 1u);
         }
-        return ((d >= d0lo) & (d < d0hi)) | ((d >= d1lo) & (d < d1hi));
+        return ((lb >= p0lo) & (lb <= p0hi)) | ((lb >= p1lo) & (lb <= p1hi));
       };
       const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);
       for (int q = 0; q < iters; ++q) {
@@ -1231,7 +1297,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         if (l < ln4) zv = *reinterpret_cast<const f32x4 *>(zs + l);
         bool isc[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) isc[c] = is_cand(win_dist(mf, zv[c], wsc));
+        for (int c = 0; c < 4; ++c) isc[c] = is_cand(win_pos(Af, zv[c], wsc));
         if (!__ballot(isc[0] || isc[1] || isc[2] || isc[3])) continue;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
@@ -1339,7 +1405,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         auto keyof = [&](int j) { return (uint32_t)(sk[j] >> 32); };
         auto zof = [&](int j) { return key_to_float(keyof(j)); };
         auto idxof = [&](int j) { return (int)(~(uint32_t)sk[j]); };
-        auto binof = [&](int j) { return win_bin(mf, zof(j), wsc); };
+        auto binof = [&](int j) { return win_bin(Af, zof(j), wsc); };
         // inclusive prefix of exact masses exp(z - m) along the sorted list;
         // each thread owns kCandCap / kBlock consecutive positions
         {
@@ -1415,7 +1481,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         }
         if (minp) t = max(t, t_m);
         // the kept set: positions [0, et); its sum and the top logprobs
-        const int bt = t ? win_bin(mf, key_to_float(t), wsc) : kWinBins;
+        const int bt = t ? win_bin(Af, key_to_float(t), wsc) : kWinBins;
         if (tid == 0) {
           sm.bu[25] = (uint32_t)n;
           sm.bu[26] = (uint32_t)n;
@@ -1628,8 +1694,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     // ---- 6. final exchange: the last workgroup to arrive writes the row
     const unsigned fpar = it & 1u;
     if (tid == 0) {
-      atomic_st(&rc.my->fin[fpar][0], best_g);
-      atomic_st(&rc.my->fin[fpar][1], (double)best_i);
+      atomic_st(&rc.my->fin[fpar][0], (unsigned long long)__double_as_longlong(best_g));
+      atomic_st(&rc.my->fin[fpar][1], (unsigned long long)(uint32_t)best_i);
+      atomic_st(&rc.my->fin[fpar][2], lkey);
     }
     if (general)
       for (int t = tid; t < K; t += kBlock) atomic_st(&rc.my->toplist[fpar][t], sm.tl[t]);
@@ -1646,14 +1713,22 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     }
     __syncthreads();
     if (sm.bu[15]) {
-      if (gumbel && tid < G) {
-        const u32x4 r = coh_load16(&rc.peers[tid].fin[fpar][0]);
-        sm.gd[tid] = f64_of(r.x, r.y);
-        sm.gi[tid] = (int)f64_of(r.z, r.w);
+      if (tid < G) {
+        u32x4 r0, r1;
+        coh_load16x2(&rc.peers[tid].fin[fpar][0], &rc.peers[tid].fin[fpar][2], r0, r1);
+        sm.gd[tid] = f64_of(r0.x, r0.y);
+        sm.gi[tid] = (int)r0.z;
+        sm.gk[tid] = u64_of(r1.x, r1.y);
       }
       __syncthreads();
       if (tid == 0) {
-        int token = argmax_idx;
+        // the row max and first argmax over the slices' keys; rows that
+        // skipped exchange 2 get their status here
+        unsigned long long mk = 0;
+        for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
+        const float mx = key_to_float((uint32_t)(mk >> 32));
+        const int status = (mx > -INFINITY && mx < INFINITY) ? 0 : (mx == INFINITY ? 2 : 1);
+        int token = (int)(0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
         if (gumbel) {
           double bg = -INFINITY;
           int bi = 0x7FFFFFFF;
@@ -1666,8 +1741,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           if (bi != 0x7FFFFFFF) token = bi;
         }
         const bool aborted = atomic_ld(kp.abort_word) == kp.epoch;
-        kp.token_ids[row] = aborted ? -1 : token;
-        if (kp.row_status) kp.row_status[row] = aborted ? 3 : 0;
+        kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
+        if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
       }
     }
     if (general && K > 0 && sm.bu[15]) {
