@@ -71,46 +71,39 @@ struct alignas(16) RowParam {
 };
 static_assert(sizeof(RowParam) == 64, "RowParam layout");
 
-// Barrier words of one row group, each on its own 128-byte line.
+// Barrier words of one row group, each on its own 128-byte line: the
+// barrier word (generation << 8 | arrival count) and the final-exchange
+// arrival count.
 struct alignas(128) GroupSync {
-  uint32_t count;
+  uint32_t word;
   uint32_t pad0[31];
-  uint32_t gen;
-  uint32_t pad1[31];
   uint32_t fin;
-  uint32_t pad2[31];
+  uint32_t pad1[31];
 };
 
-// Per-group record written by the workgroup that merges an exchange (the
-// last to arrive) and read by the others.  Every array starts on a 16-byte
-// boundary: the readers fetch it in 16-byte pieces.
-struct alignas(128) GroupRec {
-  uint32_t dec[32];                            // decisions (see the kernel)
-  double dd[8];
-  uint32_t cum_cnt[kWinBins];                  // inclusive prefix counts over the window bins
-  unsigned long long cum_mass[kWinBins + 2];   // inclusive prefix masses, 2^-31 units ([kWinBins]: all values)
-};
 
-// Exchange slots owned by one workgroup (indexed by its block id), laid out
-// like GroupRec for 16-byte reads.
+// Exchange slots owned by one workgroup (indexed by its block id); every
+// array starts on a 16-byte boundary, since readers fetch 16-byte pieces.
 struct alignas(128) WgSlots {
-  // exchange 2, by row parity: the order key of this slice's max, the
-  // slice's bin anchor (float bits), and relative to the slice's max the
-  // mass of the values deeper than the window and the exact sum (fp64 bits)
+  // Arrays read by every workgroup of the row after a group barrier are
+  // double buffered by the group's exchange count, so a workgroup rewrites
+  // one only after all readers have passed the next barrier.
+  // exchange 2: the order key of this slice's max, the slice's bin anchor
+  // (float bits), and relative to the slice's max the mass of the values
+  // deeper than the window and the exact sum (fp64 bits)
   unsigned long long x1[2][4];
   // final exchange, by row parity: best Gumbel score (fp64 bits), its
   // index, this slice's max order key
   unsigned long long fin[2][4];
-  uint32_t cand_n;                                // candidates gathered by this workgroup
-  uint32_t pad0[31];
-  unsigned long long whist[kWinBins];             // window bins: count << 48 | mass (2^-31 units)
-  unsigned long long cand[kCandCap];              // candidate keys: order key << 32 | ~index
+  uint32_t cand_n[2][4];                          // candidates gathered by this workgroup (word 0)
+  uint32_t pad0[24];
+  unsigned long long whist[2][kWinBins];          // window bins: count << 48 | mass (2^-31 units)
+  unsigned long long cand[2][kCandCap];           // candidate keys: order key << 32 | ~index
   uint32_t hcnt[2][256];                          // general path: radix counts
   unsigned long long hmass[2][256];               // general path: radix masses
   unsigned long long toplist[2][kMaxTopLogprobs]; // general path: local top-logprob candidates
   double ssum[2];                                 // general path: kept-set sum
 };
-static_assert(offsetof(GroupRec, cum_cnt) % 16 == 0 && offsetof(GroupRec, cum_mass) % 16 == 0, "GroupRec layout");
 static_assert(offsetof(WgSlots, x1) % 16 == 0 && offsetof(WgSlots, fin) % 16 == 0 && offsetof(WgSlots, whist) % 16 == 0 &&
                   offsetof(WgSlots, cand) % 16 == 0,
               "WgSlots layout");
@@ -138,7 +131,6 @@ struct KernelParams {
   int32_t vec_ok;     // bit 0: logits rows aligned for vector loads; bit 1: outputs for vector stores
   int32_t path;
   GroupSync *sync;    // [n_groups]
-  GroupRec *recs;     // [n_groups]
   WgSlots *slots;     // [n_groups * G]
   uint32_t *abort_word;  // equals epoch once a barrier wait of this launch expired
   uint32_t epoch;        // launch counter of the handle (never 0)

@@ -83,7 +83,7 @@ struct alignas(16) SmemBase {
   uint32_t red_c[kWaves];
   uint32_t bu[40];
   double bd[16];
-  uint32_t dec[32];              // decision words of the group record
+  uint32_t binmask[kWinBins / 32]; // the bins the gather collects
   double gd[kMaxG];              // per-workgroup values read by a merger
   double gf[kMaxG];
   double gs[kMaxG];
@@ -155,6 +155,33 @@ DEV void coh_load16x3(const void *p0, const void *p1, const void *p2, u32x4 &a, 
       "s_waitcnt vmcnt(0)"
       : "=&v"(a), "=&v"(b), "=&v"(c)
       : "v"(p0), "v"(p1), "v"(p2)
+      : "memory");
+}
+// Four and six such reads sharing one wait.
+DEV void coh_load16x4(const void *p0, const void *p1, const void *p2, const void *p3, u32x4 &a, u32x4 &b, u32x4 &c,
+                      u32x4 &d) {
+  asm volatile(
+      "global_load_dwordx4 %0, %4, off sc1\n\t"
+      "global_load_dwordx4 %1, %5, off sc1\n\t"
+      "global_load_dwordx4 %2, %6, off sc1\n\t"
+      "global_load_dwordx4 %3, %7, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3)
+      : "memory");
+}
+DEV void coh_load16x6(const void *p0, const void *p1, const void *p2, const void *p3, const void *p4, const void *p5,
+                      u32x4 &a, u32x4 &b, u32x4 &c, u32x4 &d, u32x4 &e, u32x4 &f) {
+  asm volatile(
+      "global_load_dwordx4 %0, %6, off sc1\n\t"
+      "global_load_dwordx4 %1, %7, off sc1\n\t"
+      "global_load_dwordx4 %2, %8, off sc1\n\t"
+      "global_load_dwordx4 %3, %9, off sc1\n\t"
+      "global_load_dwordx4 %4, %10, off sc1\n\t"
+      "global_load_dwordx4 %5, %11, off sc1\n\t"
+      "s_waitcnt vmcnt(0)"
+      : "=&v"(a), "=&v"(b), "=&v"(c), "=&v"(d), "=&v"(e), "=&v"(f)
+      : "v"(p0), "v"(p1), "v"(p2), "v"(p3), "v"(p4), "v"(p5)
       : "memory");
 }
 DEV unsigned long long u64_of(uint32_t lo, uint32_t hi) { return ((unsigned long long)hi << 32) | lo; }
@@ -431,19 +458,23 @@ DEV void order_acquire() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// Returns true in exactly one workgroup, the last to arrive, which merges
-// the exchange and then calls group_release; the others call group_wait.
-// The last arrival resets the count, so the words are reusable without
-// clearing.
+// A group's barrier word holds a generation in bits 8.. and the arrival
+// count in bits 0..7, so one atomic add both arrives and reads the
+// generation.  The last arrival resets the count (and, to release, advances
+// the generation); the others wait for the generation to change.  The word
+// is reusable without clearing.
+//
+// group_arrive returns true in exactly one workgroup, the last to arrive,
+// which then calls group_release; the others call group_wait.
 DEV bool group_arrive(SmemBase &sm, GroupSync *s, int G) {
   order_release();
   __syncthreads();
   if (tidx() == 0) {
-    const uint32_t g0 = __hip_atomic_load(&s->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t old = __hip_atomic_fetch_add(&s->count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const bool last = old == (uint32_t)G - 1u;
+    const uint32_t old = __hip_atomic_fetch_add(&s->word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t g0 = old >> 8;
+    const bool last = (old & 0xFFu) == (uint32_t)G - 1u;
     if (last) {
-      __hip_atomic_store(&s->count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&s->word, g0 << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       order_acquire();
     }
     sm.bu[14] = g0;
@@ -455,10 +486,10 @@ DEV bool group_arrive(SmemBase &sm, GroupSync *s, int G) {
   return last;
 }
 
-DEV void group_release(GroupSync *s) {
+DEV void group_release(SmemBase &sm, GroupSync *s) {
   order_release();
   __syncthreads();
-  if (tidx() == 0) __hip_atomic_fetch_add(&s->gen, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tidx() == 0) __hip_atomic_store(&s->word, (sm.bu[14] + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The wait is bounded (~2 s): on expiry the launch is marked aborted (the
@@ -466,34 +497,44 @@ DEV void group_release(GroupSync *s) {
 // returns at once and the rows report status 3, so a logic error cannot hang
 // the device.
 constexpr uint32_t kSpinLimit = 1u << 26;
+DEV void spin_gen(GroupSync *s, uint32_t g0, uint32_t *abort_word, uint32_t epoch) {
+  uint32_t spins = 0;
+  while ((__hip_atomic_load(&s->word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 8) == g0) {
+    if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
+    if (++spins > kSpinLimit) {
+      __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      break;
+    }
+    __builtin_amdgcn_s_sleep(1);
+  }
+}
 DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t epoch) {
   if (tidx() == 0) {
-    const uint32_t g0 = sm.bu[14];
-    uint32_t spins = 0;
-    while (__hip_atomic_load(&s->gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g0) {
-      if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
-      if (++spins > kSpinLimit) {
-        __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-    }
+    spin_gen(s, sm.bu[14], abort_word, epoch);
     order_acquire();
   }
   __syncthreads();
 }
 
-// Plain barrier: arrive, and the last arrival releases at once.
+// Barrier: one atomic add; the last arrival resets the count and advances
+// the generation in one store, the others wait for it.
 DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch) {
-  if (group_arrive(sm, s, G)) group_release(s);
-  else group_wait(sm, s, abort_word, epoch);
+  order_release();
+  __syncthreads();
+  if (tidx() == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(&s->word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t g0 = old >> 8;
+    if ((old & 0xFFu) == (uint32_t)G - 1u) __hip_atomic_store(&s->word, (g0 + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else spin_gen(s, g0, abort_word, epoch);
+    order_acquire();
+  }
+  __syncthreads();
 }
 
 // Per-row context shared by the phases.
 struct RowCtx {
   int row, gid, G, n, n4, s0;
   GroupSync *gsync;
-  GroupRec *rec;
   uint32_t *abort_word;
   uint32_t epoch;
   WgSlots *my;
@@ -515,6 +556,33 @@ DEV float win_pos(float A, float z, float wsc) { return A - abin(z, wsc); }
 DEV int win_bin(float A, float z, float wsc) {
   const float lb = win_pos(A, z, wsc);
   return lb < (float)kWinBins ? (int)lb : kWinBins;
+}
+
+// The smallest value z whose window position A - abin(z) is at most h (a
+// whole number): the values at or above it are exactly those in bins 0..h.
+// Found on the order keys of the floats with the same expressions the bins
+// use: a guess from the inverse of abin, settled within a few key steps,
+// else a bisection.
+DEV float win_floor_z(float A, float h, float wsc) {
+  auto in = [&](uint32_t k) { return win_pos(A, key_to_float(k), wsc) <= h; };
+  const uint32_t kninf = fkey(-INFINITY), kinf = fkey(INFINITY);  // in(kninf) false, in(kinf) true
+  uint32_t k = fkey(((A - h) * (1.0f / kBinsPerNat)) / wsc);
+  k = k < kninf ? kninf : (k > kinf ? kinf : k);
+  for (int s = 0; s < 4; ++s) {
+    if (in(k)) {
+      if (!in(k - 1u)) return key_to_float(k);
+      --k;
+    } else {
+      ++k;
+    }
+  }
+  uint32_t lo = kninf, hi = kinf;
+  while (hi - lo > 1u) {
+    const uint32_t mid = lo + (hi - lo) / 2u;
+    if (in(mid)) hi = mid;
+    else lo = mid;
+  }
+  return key_to_float(hi);
 }
 
 // Window histogram entry of one value at distance d = max - z: a count of
@@ -688,24 +756,7 @@ DEV uint32_t min_p_key(SmemBase &sm, double m, float min_p) {
   return r;
 }
 
-// Decision words of GroupRec::dec
-enum : int {
-  D_FLAGS = 0,  // bit 0: general path; bit 1: [0, RKHI] gathered whole (top-k prefix);
-                //   bit 2: the k-th value lies deeper than min-p's boundary (top-k has no effect)
-  D_TAU = 1,
-  D_LNS = 2,    // 2 words: ln of the kept-set sum (fp64 bits)
-  D_R0HI = 4,   // gathered bins: [0, R0HI] (top logprobs), [R1LO, R1HI] (top-p crossing),
-  D_R1LO = 5,   //   [RKLO, RKHI] (top-k crossing bin, or the whole top-k prefix), BM (min-p boundary)
-  D_R1HI = 6,
-  D_RKLO = 7,
-  D_RKHI = 8,
-  D_BM = 9,
-  D_STATUS = 10,  // row status (1: no finite logit, 2: +inf after temperature)
-  D_ARGMAX = 11,  // first argmax of the row
-  D_TM = 12,      // min-p's boundary key
-  D_MASK = 16,    // 16 words: bitmask of the gathered bins
-};
-static_assert(D_MASK + kWinBins / 32 <= (int)(sizeof(GroupRec::dec) / sizeof(uint32_t)), "decision words");
+
 
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
@@ -717,7 +768,6 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   unsigned char *region = reinterpret_cast<unsigned char *>(zs + kp.slice);
   // region views (see the layout above)
   uint32_t *hash = reinterpret_cast<uint32_t *>(region);
-  uint32_t *bitmap = hash + kp.hash_slots;
   uint32_t *lc = reinterpret_cast<uint32_t *>(region);
   unsigned long long *lm = reinterpret_cast<unsigned long long *>(region + kRegionLm);
   unsigned char *regB = region + kRegionB;
@@ -736,13 +786,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   rc.gid = gid;
   rc.G = G;
   rc.gsync = kp.sync + group;
-  rc.rec = kp.recs + group;
   rc.abort_word = kp.abort_word;
   rc.epoch = kp.epoch;
   rc.my = kp.slots + blockIdx.x;
   rc.peers = kp.slots + (size_t)group * G;
   rc.xseq = &xseq;
-  GroupRec *rec = rc.rec;
   const bool want_out = kp.probs != nullptr || kp.logprobs != nullptr;
   const int K = kp.top_lp;
   const bool want_S = want_out || K > 0;
@@ -776,17 +824,17 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const int tid = tidx();
     const int lane = tid & 63, wave = tid >> 6;
 
-    // ---- 1. issue the history and logit loads, build the penalty counts
-    // while they are in flight, then sanitise and divide by the temperature
-    // as each batch lands.  Loads use clamped in-bounds addresses; with
-    // vector loads the row stride is a multiple of 4, so a group starting
-    // below s1 lies inside the row.
-    int32_t hv[kMaxHistPerRow / kBlock];
-    int32_t osl[kMaxHistPerRow / kBlock];  // hash slot of an entry this thread created, else -1
+    // ---- 1. issue the history and logit loads; z = x / T into the LDS
+    // slice as each batch lands.  Loads use clamped in-bounds addresses;
+    // with vector loads the row stride is a multiple of 4, so a group
+    // starting below s1 lies inside the row.
+    constexpr int kHistPer = kMaxHistPerRow / kBlock;
+    int32_t hv[kHistPer];
+    float xr[kHistPer];  // raw logit of each in-slice history entry
     if (pen) {
       const int32_t *hist = kp.history_ids + P.hist_start;
 #pragma unroll
-      for (int q = 0; q < kMaxHistPerRow / kBlock; ++q) {
+      for (int q = 0; q < kHistPer; ++q) {
         const int h = tid + q * kBlock;
         hv[q] = h < P.hist_len ? hist[h] : -1;
       }
@@ -797,82 +845,61 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const bool vec = kp.vec_ok & 1;
     const float T = P.temperature;
     const float rT = 1.0f / T;
-    float lmax = -INFINITY;
-    int lidx = 0x7FFFFFFF;  // first index of the local max (visited in index order)
-    // the penalty counts are built while the loads are in flight; each path
-    // below is straight-line code from its loads to their uses
-    auto build_and_transform = [&]() {
-      if (pen) {
-        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
-        for (int t = tid; t < (ln4 + 31) / 32; t += kBlock) bitmap[t] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int q = 0; q < kMaxHistPerRow / kBlock; ++q) {
-          const int32_t id = hv[q];
-          osl[q] = -1;
-          if (id >= s0 && id < s1) {
-            const uint32_t local = (uint32_t)(id - s0);
-            uint32_t sl = hash_slot(local, hslots);
-            while (true) {
-              const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
-              if (prev == kEmpty) {
-                osl[q] = (int32_t)sl;
-                break;
-              }
-              if ((prev >> 13) == local) {
-                atomicAdd(&hash[sl], 1u);
-                break;
-              }
-              sl = (sl + 1u) & (hslots - 1u);
-            }
-            atomicOr(&bitmap[local >> 5], 1u << (local & 31));
-          }
-        }
-        __syncthreads();
-      }
-      // z = x / T as each batch lands, into the LDS slice (slots past the
-      // slice end: -inf); a penalised element keeps its raw value until the
-      // penalty pass
+    // |x| in [xlo, xhi] keeps q = x (1/T) within [2^-100, 2^100], where one
+    // FMA correction of q gives the correctly rounded quotient (Markstein).
+    // The test runs on the bits of |x| (NaN compares above every finite
+    // value); other groups of four (NaN, zeros, infinities, extreme values)
+    // take the IEEE division.
+    const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
+    const uint32_t xhi_b = min(__float_as_uint(T * 0x1p99f), 0x7F7FFFFFu);
+    auto transform = [&]() {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int l = 4 * tid + 4 * kBlock * b;
         if (l < ln4) {
-          const uint32_t pb = pen ? (bitmap[l >> 5] >> (l & 31)) & 0xFu : 0u;
-          float xs[4], zq[4];
-          bool slow = false;
+          uint32_t a[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float xv = v[b][c];
-            const float x = (xv == xv && l + c < ln) ? xv : -INFINITY;
-            xs[c] = x;
-            const float q = x * rT;
-            const bool fine = fabsf(q) >= 0x1p-100f && fabsf(q) <= 0x1p100f;
-            // outside that range infinities and zeros divide to themselves; a
-            // finite nonzero x goes to the IEEE division below (rare)
-            slow |= !fine && __builtin_amdgcn_classf(x, 0x198);
-            zq[c] = fine ? __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q) : x;
-          }
-          if (slow) {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) zq[c] = xs[c] / T;
-          }
+          for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(v[b][c]) & 0x7FFFFFFFu;
+          const uint32_t amax = max(max(a[0], a[1]), max(a[2], a[3]));
+          const uint32_t amin = min(min(a[0], a[1]), min(a[2], a[3]));
           f32x4 o;
+          if ((amax <= xhi_b) & (amin >= xlo_b)) {
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float zz = zq[c] + 0.0f;  // -0 -> +0: equal values share one key
-            const bool raw = (pb >> c) & 1u;
-            o[c] = raw ? xs[c] : zz;
-            if (!raw && zz > lmax) {
-              lmax = zz;
-              lidx = s0 + l + c;
+            for (int c = 0; c < 4; ++c) {
+              const float q = v[b][c] * rT;
+              o[c] = __builtin_fmaf(__builtin_fmaf(-q, T, v[b][c]), rT, q);
             }
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float x = v[b][c] == v[b][c] ? v[b][c] : -INFINITY;
+              o[c] = x / T + 0.0f;  // -0 -> +0: equal values share one key
+            }
+          }
+          if (l + 4 > ln) {  // the slice's last group: slots past its end hold -inf
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+              if (l + c >= ln) o[c] = -INFINITY;
           }
           *reinterpret_cast<f32x4 *>(zs + l) = o;
         }
       }
     };
     // vector loads in issue order (batch b is later waited for with the
-    // batches behind it still in flight), or scalar loads for unaligned rows
+    // batches behind it still in flight), or scalar loads for unaligned
+    // rows; then the raw logits of the slice's history entries, read again
+    // from the input since the transform overwrites the slice (each path is
+    // straight-line code from its loads to their uses)
+    auto load_raw = [&]() {
+      if (pen) {
+#pragma unroll
+        for (int q = 0; q < kHistPer; ++q) {
+          const int32_t id = hv[q];
+          xr[q] = 0.0f;
+          if (id >= s0 && id < s1) xr[q] = Loader<TIn>::load1(kp.logits, rbase + (id - s0));
+        }
+      }
+    };
     if (vec) {
       const int lastg = (ln - 1) & ~3;
 #pragma unroll
@@ -880,33 +907,74 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         Loader<TIn>::load4(kp.logits, rbase + min(4 * tid + 4 * kBlock * b, lastg), v[b]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      build_and_transform();
+      load_raw();
+      transform();
     } else {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[b][c] = Loader<TIn>::load1(kp.logits, rbase + min(4 * tid + 4 * kBlock * b + c, ln - 1));
-      build_and_transform();
+      load_raw();
+      transform();
     }
     if (pen) {
+      // history counts in an LDS hash (id -> count); the thread that creates
+      // an id's entry penalises that value once, with the final count
+      for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
       __syncthreads();
-      // the thread that created a history id's entry penalises that value
-      // once, with the final count
+      int32_t osl[kHistPer];  // hash slot of an entry this thread created, else -1
 #pragma unroll
-      for (int q = 0; q < kMaxHistPerRow / kBlock; ++q) {
-        if (osl[q] >= 0) {
-          const uint32_t e = hash[osl[q]];
-          const uint32_t local = e >> 13;
-          const float x = apply_penalty(zs[local], e & 0x1FFFu, P);
-          const float zz = div_temp(x, T, rT);
-          zs[local] = zz;
-          const int idx = s0 + (int)local;
-          if (zz > lmax || (zz == lmax && idx < lidx)) {
-            lmax = zz;
-            lidx = idx;
+      for (int q = 0; q < kHistPer; ++q) {
+        const int32_t id = hv[q];
+        osl[q] = -1;
+        if (id >= s0 && id < s1) {
+          const uint32_t local = (uint32_t)(id - s0);
+          uint32_t sl = hash_slot(local, hslots);
+          while (true) {
+            const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
+            if (prev == kEmpty) {
+              osl[q] = (int32_t)sl;
+              break;
+            }
+            if ((prev >> 13) == local) {
+              atomicAdd(&hash[sl], 1u);
+              break;
+            }
+            sl = (sl + 1u) & (hslots - 1u);
           }
         }
       }
+      __syncthreads();
+#pragma unroll
+      for (int q = 0; q < kHistPer; ++q) {
+        if (osl[q] >= 0) {
+          const uint32_t e = hash[osl[q]];
+          const float x = xr[q] == xr[q] ? xr[q] : -INFINITY;
+          zs[e >> 13] = div_temp(apply_penalty(x, e & 0x1FFFu, P), T, rT);
+        }
+      }
+    }
+    __syncthreads();
+    // this thread's max and first argmax: the best group of four by a
+    // strict compare (groups in index order), then the first match in it
+    float lmax = -INFINITY;
+    int lgrp = -1;
+#pragma unroll
+    for (int b = 0; b < kBatch; ++b) {
+      const int l = 4 * tid + 4 * kBlock * b;
+      if (l < ln4) {
+        const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+        const float gm = fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3]));
+        if (gm > lmax) {
+          lmax = gm;
+          lgrp = l;
+        }
+      }
+    }
+    int lidx = 0x7FFFFFFF;
+    if (lgrp >= 0) {
+      const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + lgrp);
+      lidx = s0 + lgrp + (zv[0] == lmax ? 0 : zv[1] == lmax ? 1 : zv[2] == lmax ? 2 : 3);
     }
 
     // ---- 2. this slice's max and first argmax as one order key (value key
@@ -932,6 +1000,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     bool topk_on = topk;  // top-k decides (part of) the kept set
     uint32_t tau = 0;
     double lnS = 0.0;
+    double s_all = 0.0;  // the exact sum of every value's mass, when needed
     int r0hi = -1, r1lo = 1, r1hi = 0, rklo = 1, rkhi = 0, bm = -1;
     if (need_x) {
       // ---- 3. window histogram of this slice on the absolute bin grid,
@@ -968,223 +1037,52 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       const double wsx = need_exact ? wg_sum_d(sm, sx) : 0.0;
       __syncthreads();
       // this workgroup's record and histogram -> its exchange slot
-      if (need_sel) atomic_st(&rc.my->whist[tid], wh[tid]);
+      const unsigned xp = xseq++ & 1u;
+      if (need_sel) atomic_st(&rc.my->whist[xp][tid], wh[tid]);
       if (tid == 0) {
-        atomic_st(&rc.my->x1[par][0], lkey);
-        atomic_st(&rc.my->x1[par][1], (unsigned long long)__float_as_uint(Ag));
-        atomic_st(&rc.my->x1[par][2], (unsigned long long)__double_as_longlong(wdm));
-        atomic_st(&rc.my->x1[par][3], (unsigned long long)__double_as_longlong(wsx));
+        atomic_st(&rc.my->x1[xp][0], lkey);
+        atomic_st(&rc.my->x1[xp][1], (unsigned long long)__float_as_uint(Ag));
+        atomic_st(&rc.my->x1[xp][2], (unsigned long long)__double_as_longlong(wdm));
+        atomic_st(&rc.my->x1[xp][3], (unsigned long long)__double_as_longlong(wsx));
       }
-      if (group_arrive(sm, rc.gsync, G)) {
-        // ---- merge (last arrival)
+      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
+      // ---- exchange 2, merged by every workgroup of the row alike: the
+      // records and the first histogram pairs in one batch of 16-byte reads,
+      // the row max, each slice's bin shift and mass scale, integer LDS adds
+      // (order-free), prefix sums and decisions.  Every workgroup reads the
+      // same words and runs the same code, so all take the same decisions.
+      constexpr int kPairs = kWinBins / 2;
+      const int npairs = need_sel ? G * kPairs : 0;
+      u32x4 hr[4];
+      {
+        const int g1 = tid < G ? tid : G - 1;
+        u32x4 r0, r1;
+        if (npairs > 0) {
+          const void *ph[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const int pk = min(tid + k * kBlock, npairs - 1);
+            ph[k] = &rc.peers[pk / kPairs].whist[xp][2 * (pk % kPairs)];
+          }
+          coh_load16x6(&rc.peers[g1].x1[xp][0], &rc.peers[g1].x1[xp][2], ph[0], ph[1], ph[2], ph[3], r0, r1, hr[0], hr[1],
+                       hr[2], hr[3]);
+        } else {
+          coh_load16x2(&rc.peers[g1].x1[xp][0], &rc.peers[g1].x1[xp][2], r0, r1);
+        }
         if (tid < G) {
-          u32x4 r0, r1;
-          coh_load16x2(&rc.peers[tid].x1[par][0], &rc.peers[tid].x1[par][2], r0, r1);
           sm.gk[tid] = u64_of(r0.x, r0.y);
           sm.ga[tid] = __uint_as_float(r0.z);
-          sm.gd[tid] = f64_of(r1.z, r1.w);                        // exact sum
-          sm.gf[tid] = f64_of(r1.x, r1.y);                        // deep mass (scaled below)
+          sm.gf[tid] = f64_of(r1.x, r1.y);  // deep mass (scaled below)
+          sm.gd[tid] = f64_of(r1.z, r1.w);  // exact sum (scaled below)
         }
-        __syncthreads();
-        unsigned long long mk = 0;
-        for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
-        const float mfx = key_to_float((uint32_t)(mk >> 32));
-        const double mx = (double)mfx;
-        const uint32_t status = (mfx > -INFINITY && mfx < INFINITY) ? 0u : (mfx == INFINITY ? 2u : 1u);
-        uint32_t tmx = 0;
-        uint32_t flags = 0;
-        if (status == 0) {
-          const float A = abin(mfx, wsc);
-          if (minp) tmx = min_p_key(sm, mx, P.min_p);
-          // per-workgroup mass scale exp(m_g - m) and bin shift A - A_g
-          double deep_x = 0.0;  // window bins of a slice that fall past the row's window
-          if (tid < G) {
-            const float mgg = key_to_float((uint32_t)(sm.gk[tid] >> 32));
-            const double f = mgg > -INFINITY ? exp_nonpos(sm.exp_tab, (double)mgg - mx) : 0.0;
-            const float sh = A - sm.ga[tid];  // whole bins, >= 0
-            sm.gi[tid] = (mgg > -INFINITY && sh < (float)kWinBins) ? (int)sh : kWinBins;
-            sm.gd[tid] *= f;  // exact sums, rescaled
-            sm.gf[tid] *= f;  // deep masses, rescaled
-            sm.gs[tid] = f;
-          }
-          __syncthreads();
-          if (need_sel) {
-            const int b = tid;
-            lc[b] = 0;
-            lm[b] = 0;
-            if (tid == 0) lm[kWinBins] = 0;
-            __syncthreads();
-            // two bins per 16-byte read, two reads per pass (the second
-            // repeats the first when out of range and is then ignored);
-            // integer LDS adds of each slice's rescaled, rounded masses:
-            // order-free
-            constexpr int kPairs = kWinBins / 2;
-            for (int pi = tid; pi < G * kPairs; pi += 2 * kBlock) {
-              const int pj = pi + kBlock < G * kPairs ? pi + kBlock : pi;
-              u32x4 ra, rb;
-              coh_load16x2(&rc.peers[pi / kPairs].whist[2 * (pi % kPairs)], &rc.peers[pj / kPairs].whist[2 * (pj % kPairs)], ra, rb);
-              const unsigned long long h[4] = {u64_of(ra.x, ra.y), u64_of(ra.z, ra.w), u64_of(rb.x, rb.y), u64_of(rb.z, rb.w)};
-#pragma unroll
-              for (int i = 0; i < 4; ++i) {
-                if (i >= 2 && pj == pi) break;
-                const unsigned long long e = h[i];
-                if (e) {
-                  const int p = (i < 2) ? pi : pj;
-                  const int g = p / kPairs;
-                  const int bin = 2 * (p % kPairs) + (i & 1) + sm.gi[g];
-                  const double ms = (double)(e & 0xFFFFFFFFFFFFull) * sm.gs[g];
-                  if (bin < kWinBins) {
-                    atomicAdd(&lc[bin], (uint32_t)(e >> 48));
-                    if (need_mass) atomicAdd(&lm[bin], (unsigned long long)__double2ll_rn(ms));
-                  } else {
-                    deep_x += ms;
-                  }
-                }
-              }
-            }
-            const double deep_w = need_deep ? wg_sum_d(sm, deep_x) : 0.0;
-            __syncthreads();
-            const uint32_t cb = lc[b];
-            const unsigned long long mb = lm[b];
-            unsigned long long deep = 0;
-            if (need_deep) {
-              double dt = deep_w;
-              for (int g = 0; g < G; ++g) dt += sm.gf[g];
-              deep = (unsigned long long)__double2ll_rn(dt);
-            }
-            const uint32_t runc = block_scan_incl<uint32_t>(cb, sm.red_c);
-            const unsigned long long runm = block_scan_incl<unsigned long long>(mb, sm.red_u);
-            lc[b] = runc;
-            lm[b] = runm;
-            if (b == kWinBins - 1) lm[kWinBins] = runm + deep;
-            if (tid == 0) {
-              sm.bu[16] = kNone;
-              sm.bu[17] = kNone;
-              sm.bu[18] = kNone;
-              sm.bu[19] = kNone;
-            }
-            __syncthreads();
-            atomic_st(&rec->cum_cnt[b], runc);
-            atomic_st(&rec->cum_mass[b], runm);
-            if (b == kWinBins - 1) atomic_st(&rec->cum_mass[kWinBins], runm + deep);
-            // bins of the k-th and the K-th value
-            const uint32_t cprev = b > 0 ? lc[b - 1] : 0u;
-            if (topk && cprev < (uint32_t)P.top_k && runc >= (uint32_t)P.top_k) sm.bu[16] = (uint32_t)b;
-            if (K > 0 && cprev < (uint32_t)K && runc >= (uint32_t)K) sm.bu[17] = (uint32_t)b;
-            __syncthreads();
-            const uint32_t bk = sm.bu[16], r0 = sm.bu[17];
-            bool gen = false;
-            bool fk = false;
-            bool k_off = false;
-            int e_r0hi = -1, e_r1lo = 1, e_r1hi = 0, e_rklo = 1, e_rkhi = 0, e_bm = -1;
-            const int bmin = minp ? win_bin(A, key_to_float(tmx), wsc) : kWinBins;
-            if (K > 0) {
-              if (r0 != kNone) e_r0hi = (int)r0;
-              else if (truncated) e_r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
-              else gen = true;
-            }
-            if (topk) {
-              if (bk != kNone) {
-                if (lc[bk] <= (uint32_t)kCandCap) {
-                  fk = true;
-                  e_rklo = 0;
-                  e_rkhi = (int)bk;
-                } else {
-                  e_rklo = e_rkhi = (int)bk;
-                }
-              } else if (topp || !(minp && bmin < kWinBins)) {
-                gen = true;  // the k-th value is deeper than the window and decides the kept set
-              } else {
-                k_off = true;
-              }
-            }
-            // top-p: the bins where the cumulative mass crosses p times the
-            // total mass of the top-k set (bounded below and above)
-            double tlo = 0.0, thi = 0.0;
-            if (topp && !gen) {
-              if (topk) {
-                tlo = (double)P.top_p * (bk > 0 ? (double)lm[bk - 1] : 0.0);
-                thi = (double)P.top_p * (double)lm[bk];
-              } else {
-                tlo = thi = (double)P.top_p * (double)lm[kWinBins];
-              }
-              const double mprev = b > 0 ? (double)lm[b - 1] : 0.0, mcur = (double)lm[b];
-              if (mprev < tlo && mcur >= tlo) sm.bu[18] = (uint32_t)b;
-              if (mprev < thi && mcur >= thi) sm.bu[19] = (uint32_t)b;
-            }
-            __syncthreads();
-            if (topp && !gen) {
-              const uint32_t lo = tlo <= 0.0 ? 0u : sm.bu[18], hi = sm.bu[19];
-              if (hi == kNone) {
-                gen = true;  // the crossing lies deeper than the window
-              } else {
-                e_r1lo = (int)(lo == kNone ? hi : lo);
-                e_r1hi = (int)hi;
-                if (topk) {
-                  e_r1lo = min(e_r1lo, (int)bk);
-                  e_r1hi = min(e_r1hi, (int)bk);
-                }
-              }
-            }
-            if (minp && !gen) {
-              if (bmin < kWinBins) e_bm = bmin;
-              else if (!topk && !topp) gen = true;  // min-p alone keeps values deeper than the window
-            }
-            // the bin grid overflows for |m / T| beyond ~1e37: exact path
-            if (!(A > -INFINITY && A < INFINITY)) gen = true;
-            // gathered bins and their total count
-            const bool in = !gen && (b <= e_r0hi || (b >= e_r1lo && b <= e_r1hi) || (b >= e_rklo && b <= e_rkhi) || b == e_bm);
-            const unsigned long long bal = __ballot(in);
-            if (lane == 0) {
-              atomic_st(&rec->dec[D_MASK + 2 * wave], (uint32_t)bal);
-              atomic_st(&rec->dec[D_MASK + 2 * wave + 1], (uint32_t)(bal >> 32));
-            }
-            const uint32_t ncand = (uint32_t)wg_sum_u(sm, in ? (unsigned long long)cb : 0ull);
-            if (ncand > (uint32_t)kCandCap) gen = true;
-            flags = (gen ? 1u : 0u) | (fk ? 2u : 0u) | (k_off ? 4u : 0u);
-            if (tid == 0) {
-              atomic_st(&rec->dec[D_R0HI], (uint32_t)e_r0hi);
-              atomic_st(&rec->dec[D_R1LO], (uint32_t)e_r1lo);
-              atomic_st(&rec->dec[D_R1HI], (uint32_t)e_r1hi);
-              atomic_st(&rec->dec[D_RKLO], (uint32_t)e_rklo);
-              atomic_st(&rec->dec[D_RKHI], (uint32_t)e_rkhi);
-              atomic_st(&rec->dec[D_BM], (uint32_t)e_bm);
-            }
-          }
-        }
-        if (tid == 0) {
-          double S_all = 0.0;
-          if (status == 0 && need_exact)
-            for (int g = 0; g < G; ++g) S_all += sm.gd[g];
-          atomic_st(&rec->dd[0], S_all);
-          atomic_st(&rec->dd[1], mx);
-          atomic_st(&rec->dec[D_FLAGS], flags);
-          atomic_st(&rec->dec[D_STATUS], status);
-          atomic_st(&rec->dec[D_ARGMAX], 0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
-          atomic_st(&rec->dec[D_TM], tmx);
-        }
-        group_release(rc.gsync);
-      } else {
-        group_wait(sm, rc.gsync, rc.abort_word, rc.epoch);
-      }
-      // decisions (32 words), the exact sum and the row max: 16-byte reads
-      // in parallel
-      if (tid < 8) {
-        const u32x4 r = coh_load16(&rec->dec[4 * tid]);
-        sm.dec[4 * tid] = r.x;
-        sm.dec[4 * tid + 1] = r.y;
-        sm.dec[4 * tid + 2] = r.z;
-        sm.dec[4 * tid + 3] = r.w;
-      } else if (tid == 8) {
-        const u32x4 r = coh_load16(&rec->dd[0]);
-        sm.bd[1] = f64_of(r.x, r.y);
-        sm.bd[0] = f64_of(r.z, r.w);
       }
       __syncthreads();
-      m = sm.bd[0];
-      argmax_idx = (int)sm.dec[D_ARGMAX];
-      t_m = sm.dec[D_TM];
-      const uint32_t status = sm.dec[D_STATUS];
+      unsigned long long mk = 0;
+      for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
+      const float mfx = key_to_float((uint32_t)(mk >> 32));
+      m = (double)mfx;
+      argmax_idx = (int)(0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
+      const uint32_t status = (mfx > -INFINITY && mfx < INFINITY) ? 0u : (mfx == INFINITY ? 2u : 1u);
       if (status != 0) {
         // ---- no finite logit (status 1) or a +inf value (status 2)
         if (want_out) {
@@ -1204,21 +1102,160 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         __syncthreads();
         continue;
       }
-      Af = abin((float)m, wsc);
+      const float A = abin(mfx, wsc);
+      Af = A;
+      if (minp) t_m = min_p_key(sm, m, P.min_p);
+      // per-workgroup mass scale exp(m_g - m) and bin shift A - A_g
+      if (tid < G) {
+        const float mgg = key_to_float((uint32_t)(sm.gk[tid] >> 32));
+        const double f = mgg > -INFINITY ? exp_nonpos(sm.exp_tab, (double)mgg - m) : 0.0;
+        const float sh = A - sm.ga[tid];  // whole bins, >= 0
+        sm.gi[tid] = (mgg > -INFINITY && sh < (float)kWinBins) ? (int)sh : kWinBins;
+        sm.gd[tid] *= f;
+        sm.gf[tid] *= f;
+        sm.gs[tid] = f;
+      }
+      __syncthreads();
+      if (need_exact) {
+        for (int g = 0; g < G; ++g) s_all += sm.gd[g];
+        lnS = log(s_all);
+      }
       if (need_sel) {
-        general = sm.dec[D_FLAGS] & 1u;
-        full_k = sm.dec[D_FLAGS] & 2u;
-        topk_on = topk && !(sm.dec[D_FLAGS] & 4u);
-        r0hi = (int)sm.dec[D_R0HI];
-        r1lo = (int)sm.dec[D_R1LO];
-        r1hi = (int)sm.dec[D_R1HI];
-        rklo = (int)sm.dec[D_RKLO];
-        rkhi = (int)sm.dec[D_RKHI];
-        bm = (int)sm.dec[D_BM];
+        const int b = tid;
+        lc[b] = 0;
+        lm[b] = 0;
+        if (tid == 0) lm[kWinBins] = 0;
+        __syncthreads();
+        double deep_x = 0.0;  // window bins of a slice that fall past the row's window
+        // two bins per 16-byte pair; integer LDS adds of each slice's
+        // rescaled, rounded masses: order-free
+        auto add_pair = [&](int p, const u32x4 &r) {
+          const int g = p / kPairs;
+          const unsigned long long e2[2] = {u64_of(r.x, r.y), u64_of(r.z, r.w)};
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const unsigned long long e = e2[i];
+            if (e) {
+              const int bin = 2 * (p % kPairs) + i + sm.gi[g];
+              const double ms = (double)(e & 0xFFFFFFFFFFFFull) * sm.gs[g];
+              if (bin < kWinBins) {
+                atomicAdd(&lc[bin], (uint32_t)(e >> 48));
+                if (need_mass) atomicAdd(&lm[bin], (unsigned long long)__double2ll_rn(ms));
+              } else {
+                deep_x += ms;
+              }
+            }
+          }
+        };
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          if (tid + k * kBlock < npairs) add_pair(tid + k * kBlock, hr[k]);
+        // more than eight slices: the remaining pairs, two reads per pass
+        for (int pi = tid + 4 * kBlock; pi < npairs; pi += 2 * kBlock) {
+          const int pj = pi + kBlock < npairs ? pi + kBlock : pi;
+          u32x4 ra, rb;
+          coh_load16x2(&rc.peers[pi / kPairs].whist[xp][2 * (pi % kPairs)], &rc.peers[pj / kPairs].whist[xp][2 * (pj % kPairs)],
+                       ra, rb);
+          add_pair(pi, ra);
+          if (pj != pi) add_pair(pj, rb);
+        }
+        const double deep_w = need_deep ? wg_sum_d(sm, deep_x) : 0.0;
+        __syncthreads();
+        const uint32_t cb = lc[b];
+        const unsigned long long mb = lm[b];
+        unsigned long long deep = 0;
+        if (need_deep) {
+          double dt = deep_w;
+          for (int g = 0; g < G; ++g) dt += sm.gf[g];
+          deep = (unsigned long long)__double2ll_rn(dt);
+        }
+        const uint32_t runc = block_scan_incl<uint32_t>(cb, sm.red_c);
+        const unsigned long long runm = block_scan_incl<unsigned long long>(mb, sm.red_u);
+        lc[b] = runc;
+        lm[b] = runm;
+        if (b == kWinBins - 1) lm[kWinBins] = runm + deep;
+        if (tid == 0) {
+          sm.bu[16] = kNone;
+          sm.bu[17] = kNone;
+          sm.bu[18] = kNone;
+          sm.bu[19] = kNone;
+        }
+        __syncthreads();
+        // bins of the k-th and the K-th value
+        const uint32_t cprev = b > 0 ? lc[b - 1] : 0u;
+        if (topk && cprev < (uint32_t)P.top_k && runc >= (uint32_t)P.top_k) sm.bu[16] = (uint32_t)b;
+        if (K > 0 && cprev < (uint32_t)K && runc >= (uint32_t)K) sm.bu[17] = (uint32_t)b;
+        __syncthreads();
+        const uint32_t bk = sm.bu[16], r0 = sm.bu[17];
+        bool gen = false;
+        const int bmin = minp ? win_bin(A, key_to_float(t_m), wsc) : kWinBins;
+        if (K > 0) {
+          if (r0 != kNone) r0hi = (int)r0;
+          else if (truncated) r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
+          else gen = true;
+        }
+        if (topk) {
+          if (bk != kNone) {
+            if (lc[bk] <= (uint32_t)kCandCap) {
+              full_k = true;
+              rklo = 0;
+              rkhi = (int)bk;
+            } else {
+              rklo = rkhi = (int)bk;
+            }
+          } else if (topp || !(minp && bmin < kWinBins)) {
+            gen = true;  // the k-th value is deeper than the window and decides the kept set
+          } else {
+            topk_on = false;
+          }
+        }
+        // top-p: the bins where the cumulative mass crosses p times the
+        // total mass of the top-k set (bounded below and above)
+        double tlo = 0.0, thi = 0.0;
+        if (topp && !gen) {
+          if (topk) {
+            tlo = (double)P.top_p * (bk > 0 ? (double)lm[bk - 1] : 0.0);
+            thi = (double)P.top_p * (double)lm[bk];
+          } else {
+            tlo = thi = (double)P.top_p * (double)lm[kWinBins];
+          }
+          const double mprev = b > 0 ? (double)lm[b - 1] : 0.0, mcur = (double)lm[b];
+          if (mprev < tlo && mcur >= tlo) sm.bu[18] = (uint32_t)b;
+          if (mprev < thi && mcur >= thi) sm.bu[19] = (uint32_t)b;
+        }
+        __syncthreads();
+        if (topp && !gen) {
+          const uint32_t lo = tlo <= 0.0 ? 0u : sm.bu[18], hi = sm.bu[19];
+          if (hi == kNone) {
+            gen = true;  // the crossing lies deeper than the window
+          } else {
+            r1lo = (int)(lo == kNone ? hi : lo);
+            r1hi = (int)hi;
+            if (topk) {
+              r1lo = min(r1lo, (int)bk);
+              r1hi = min(r1hi, (int)bk);
+            }
+          }
+        }
+        if (minp && !gen) {
+          if (bmin < kWinBins) bm = bmin;
+          else if (!topk && !topp) gen = true;  // min-p alone keeps values deeper than the window
+        }
+        // the bin grid overflows for |m / T| beyond ~1e37: exact path
+        if (!(A > -INFINITY && A < INFINITY)) gen = true;
+        // gathered bins (mask for the gather) and their total count
+        const bool in = !gen && (b <= r0hi || (b >= r1lo && b <= r1hi) || (b >= rklo && b <= rkhi) || b == bm);
+        const unsigned long long bal = __ballot(in);
+        if (lane == 0) {
+          sm.binmask[2 * wave] = (uint32_t)bal;
+          sm.binmask[2 * wave + 1] = (uint32_t)(bal >> 32);
+        }
+        const uint32_t ncand = (uint32_t)wg_sum_u(sm, in ? (unsigned long long)cb : 0ull);
+        if (ncand > (uint32_t)kCandCap) gen = true;
+        general = gen;
       } else if (minp) {
         tau = t_m;  // min-p alone without outputs: the closed-form boundary
       }
-      if (need_exact) lnS = log(sm.bd[1]);
       __syncthreads();
     }
     const float mf = (float)m;
@@ -1278,36 +1315,56 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           }
         }
       }
-      // the run bounds as window positions (integer-valued floats)
-      const float p0lo = (float)run_lo[0], p0hi = (float)run_hi[0];
-      const float p1lo = (float)run_lo[1], p1hi = (float)run_hi[1];
-      // branch-free membership of window position lb: the two runs by
-      // value, or (more than two runs, rare) the bin mask
-      auto is_cand = [&](float lb) -> bool {
-        if (more) {
-          const int bb = min((int)lb, kWinBins - 1);
-          return (lb < (float)kWinBins) & (bool)((sm.dec[D_MASK + (bb >> 5)] >> (bb & 31)) & 1u);
-        }
-        return ((lb >= p0lo) & (lb <= p0hi)) | ((lb >= p1lo) & (lb <= p1hi));
-      };
-      const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);
-      for (int q = 0; q < iters; ++q) {
-        const int l = 4 * tid + 4 * kBlock * q;
-        f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (l < ln4) zv = *reinterpret_cast<const f32x4 *>(zs + l);
-        bool isc[4];
+      // each run [lo, hi] as a value range [zlo, zhi): bins lo..hi hold
+      // exactly the values with zmin(hi) <= z < zmin(lo - 1)
+      if (tid < 4) {
+        const int r = tid >> 1;
+        const bool upper = tid & 1;
+        float zb;
+        if (run_hi[r] < run_lo[r]) zb = upper ? -INFINITY : INFINITY;  // empty run
+        else if (!upper) zb = win_floor_z(Af, (float)run_hi[r], wsc);
+        else zb = run_lo[r] > 0 ? win_floor_z(Af, (float)(run_lo[r] - 1), wsc) : INFINITY;
+        sm.bu[28 + tid] = __float_as_uint(zb);
+      }
+      __syncthreads();
+      const float z0lo = __uint_as_float(sm.bu[28]), z0hi = __uint_as_float(sm.bu[29]);
+      const float z1lo = __uint_as_float(sm.bu[30]), z1hi = __uint_as_float(sm.bu[31]);
+      // membership by value (one or two runs), or (more than two runs,
+      // rare) by the bin mask; groups of four in a fixed, unrolled order so
+      // the LDS reads overlap; the staging branch runs only for the waves
+      // that hold a candidate
+      auto gather = [&](auto is_cand) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) isc[c] = is_cand(win_pos(Af, zv[c], wsc));
-        if (!__ballot(isc[0] || isc[1] || isc[2] || isc[3])) continue;
+        for (int q = 0; q < kBatch; ++q) {
+          const int l = 4 * tid + 4 * kBlock * q;
+          f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          if (l < ln4) zv = *reinterpret_cast<const f32x4 *>(zs + l);
+          bool isc[4];
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          const unsigned long long bal = __ballot(isc[c]);
-          if (bal) {
-            const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (isc[c] && cnt + off < (uint32_t)kStagePerWave) wst[cnt + off] = cand_key(zv[c], s0 + l + c);
-            cnt += (uint32_t)__popcll(bal);
+          for (int c = 0; c < 4; ++c) isc[c] = is_cand(zv[c]);
+          if (__ballot(isc[0] | isc[1] | isc[2] | isc[3])) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const unsigned long long bal = __ballot(isc[c]);
+              if (bal) {
+                const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+                if (isc[c] && cnt + off < (uint32_t)kStagePerWave) wst[cnt + off] = cand_key(zv[c], s0 + l + c);
+                cnt += (uint32_t)__popcll(bal);
+              }
+            }
           }
         }
+      };
+      if (more) {
+        gather([&](float z) -> bool {
+          const float lb = win_pos(Af, z, wsc);
+          const int bb = min((int)lb, kWinBins - 1);
+          return (lb < (float)kWinBins) & (bool)((sm.binmask[bb >> 5] >> (bb & 31)) & 1u);
+        });
+      } else if (run_hi[1] < run_lo[1]) {
+        gather([&](float z) -> bool { return (z >= z0lo) & (z < z0hi); });
+      } else {
+        gather([&](float z) -> bool { return ((z >= z0lo) & (z < z0hi)) | ((z >= z1lo) & (z < z1hi)); });
       }
       if (lane == 0) sm.red_c[wave] = cnt;
       __syncthreads();
@@ -1324,19 +1381,30 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
       __syncthreads();
       const uint32_t my_n = sm.wo[kWaves];
+      const unsigned xq = xseq++ & 1u;
       if (my_n <= (uint32_t)kCandCap) {
         for (int w = 0; w < kWaves; ++w) {
           const int cw = (int)sm.red_c[w];
-          for (int j = tid; j < cw; j += kBlock) atomic_st(&rc.my->cand[sm.wo[w] + j], stage[w * kStagePerWave + j]);
+          for (int j = tid; j < cw; j += kBlock) atomic_st(&rc.my->cand[xq][sm.wo[w] + j], stage[w * kStagePerWave + j]);
         }
       }
-      if (tid == 0) atomic_st(&rc.my->cand_n, my_n);
-      if (group_arrive(sm, rc.gsync, G)) {
-        // ---- merge: gather the G lists, sort, decide
-        if (tid < G) sm.gcnt[tid] = atomic_ld(&rc.peers[tid].cand_n);
+      if (tid == 0) atomic_st(&rc.my->cand_n[xq][0], my_n);
+      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
+      // ---- exchange 3, in every workgroup alike: the counts and the first
+      // candidates of every slice in one batch of 16-byte reads (pairs of
+      // keys; a slot's array has room past an odd count), the rest only
+      // when a slice gathered more
+      {
+        const int pps = min(2 * kBlock / G, kCandCap / 2);  // pairs read at first per slice
+        const int g1 = tid < G ? tid : G - 1;
+        const int pa = tid, pb = tid + kBlock;
+        u32x4 rn, ra, rb;
+        coh_load16x3(&rc.peers[g1].cand_n[xq][0], &rc.peers[pa / pps].cand[xq][2 * (pa % pps)],
+                     &rc.peers[min(pb / pps, G - 1)].cand[xq][2 * (pb % pps)], rn, ra, rb);
+        if (tid < G) sm.gcnt[tid] = rn.x;
         __syncthreads();
         if (tid == 0) {
-          uint32_t acc = 0, pairs = 0;
+          uint32_t acc = 0;
           bool ovf = false;
           for (int g = 0; g < G; ++g) {
             const uint32_t c = sm.gcnt[g];
@@ -1344,42 +1412,31 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             const uint32_t cc = c > (uint32_t)kCandCap ? 0u : c;
             sm.gcnt[g] = cc;
             sm.goff[g] = acc;
-            sm.gpo[g] = pairs;
             acc += cc;
-            pairs += (cc + 1u) / 2u;
           }
           ovf |= acc > (uint32_t)kCandCap;
           sm.goff[G] = acc;
-          sm.gpo[G] = pairs;
           sm.bu[12] = ovf ? 1u : 0u;
         }
         __syncthreads();
-        const bool ovf = sm.bu[12] != 0u;
-        const int n = ovf ? 0 : (int)sm.goff[G];
-        if (!ovf) {
-          // candidates in 16-byte pairs (a slot's array has room past an odd count)
-          for (int pi = tid; pi < (int)sm.gpo[G]; pi += kBlock) {
-            int g = 0;
-            while ((int)sm.gpo[g + 1] <= pi) ++g;
-            const int j = 2 * (pi - (int)sm.gpo[g]);
-            const u32x4 r = coh_load16(&rc.peers[g].cand[j]);
-            sk[sm.goff[g] + j] = u64_of(r.x, r.y);
-            if (j + 1 < (int)sm.gcnt[g]) sk[sm.goff[g] + j + 1] = u64_of(r.z, r.w);
+        if (sm.bu[12] == 0u) {
+          auto put = [&](int g, int j, const u32x4 &r) {
+            const int c = (int)sm.gcnt[g];
+            if (j < c) sk[sm.goff[g] + j] = u64_of(r.x, r.y);
+            if (j + 1 < c) sk[sm.goff[g] + j + 1] = u64_of(r.z, r.w);
+          };
+          put(pa / pps, 2 * (pa % pps), ra);
+          if (pb / pps < G) put(pb / pps, 2 * (pb % pps), rb);
+          // slices with more than 2 pps candidates: the rest
+          for (int g = 0; g < G; ++g) {
+            const int c = (int)sm.gcnt[g];
+            for (int j = 2 * pps + 2 * tid; j < c; j += 2 * kBlock) put(g, j, coh_load16(&rc.peers[g].cand[xq][j]));
           }
         }
-        // merged prefix arrays, 16 bytes per thread
-        if (tid < kWinBins / 4) {
-          const u32x4 r = coh_load16(&rec->cum_cnt[4 * tid]);
-          lc[4 * tid] = r.x;
-          lc[4 * tid + 1] = r.y;
-          lc[4 * tid + 2] = r.z;
-          lc[4 * tid + 3] = r.w;
-        } else if (tid < kWinBins / 4 + kWinBins / 2 + 1) {
-          const int j = 2 * (tid - kWinBins / 4);
-          const u32x4 r = coh_load16(&rec->cum_mass[j]);
-          lm[j] = u64_of(r.x, r.y);
-          if (j + 1 <= kWinBins) lm[j + 1] = u64_of(r.z, r.w);
-        }
+      }
+      {
+        const bool ovf = sm.bu[12] != 0u;
+        const int n = ovf ? 0 : (int)sm.goff[G];
         if (tid == 0) sk[n] = 0ull;  // pads an odd count for the pairwise reads below
         __syncthreads();
         // rank each candidate by counting the larger keys (keys are distinct:
@@ -1495,14 +1552,14 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           }
         __syncthreads();
         const int et = (int)sm.bu[25], fp_bt = (int)sm.bu[26];
-        double S_K = atomic_ld(&rec->dd[0]);
+        double S_K = s_all;
         if (!flags && truncated && want_S) {
           if (full_k && bt <= rkhi) S_K = qsum(0, et - 1);
           else if (bt < kWinBins) S_K = cmass(bt - 1) + qsum(fp_bt, et - 1);
           else flags |= 1u;
         }
         const double lns = log(S_K);
-        if (!flags && K > 0) {
+        if (!flags && K > 0 && gid == 0) {
           const int kept_n = truncated ? et : n;
           for (int q = tid; q < K; q += kBlock) {
             const int64_t o = (int64_t)row * K + q;
@@ -1515,27 +1572,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             }
           }
         }
-        if (tid == 0) {
-          atomic_st(&rec->dec[D_FLAGS], flags);
-          atomic_st(&rec->dec[D_TAU], t);
-          const unsigned long long lb = (unsigned long long)__double_as_longlong(lns);
-          atomic_st(&rec->dec[D_LNS], (uint32_t)lb);
-          atomic_st(&rec->dec[D_LNS + 1], (uint32_t)(lb >> 32));
-        }
-        group_release(rc.gsync);
-      } else {
-        group_wait(sm, rc.gsync, rc.abort_word, rc.epoch);
+        general = flags & 1u;
+        tau = t;
+        lnS = lns;
       }
-      if (tid == 0) {
-        const u32x4 r = coh_load16(&rec->dec[0]);
-        sm.bu[4] = r[D_FLAGS];
-        sm.bu[13] = r[D_TAU];
-        sm.bd[2] = f64_of(r[D_LNS], r[D_LNS + 1]);
-      }
-      __syncthreads();
-      general = sm.bu[4] & 1u;
-      tau = sm.bu[13];
-      lnS = sm.bd[2];
       __syncthreads();
     }
 
@@ -1599,7 +1639,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     // ---- 5. emit probs / logprobs, Gumbel-max candidates
     // Linear scores s_i = q_i / E_i with q_i = exp(z_i - m).  bound is a
     // lower bound of the best exact score (shared by the wave): an element
-    // with w_i bound > q_i cannot reach it, because E_i >= w_i.
+    // with w_i bound > q_i cannot reach it, because E_i >= w_i.  Groups of
+    // four that hold a candidate (kept, and within kPruneNats of the max)
+    // join a per-wave ring in LDS; Philox runs on full waves of such groups.
     const bool gumbel = !top1 && kp.path != PATH_GREEDY;
     const float tauf = tau == 0 ? -INFINITY : key_to_float(tau);
     double best_g = -INFINITY;
@@ -1607,88 +1649,106 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
     float bound = 0.0f;
-    const float inv_s = (float)exp(-lnS) * 0.99999f;  // bound in probability units
     if (gumbel) {
       // the argmax is always kept; its score is 1 / E
       uint32_t w4[4];
       philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
       bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
     }
-    const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);  // wave-uniform trip count
-    for (int q = 0; q < iters; ++q) {
-      const int l = 4 * tid + 4 * kBlock * q;
-      const bool act = l < ln4;
-      f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      if (act) zv = *reinterpret_cast<const f32x4 *>(zs + l);
-      const int i0 = s0 + l;
-      bool kk[4];
-      bool any_cand = false;
-#pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        kk[c] = act && zv[c] >= tauf;
-        any_cand |= kk[c] && (mf - zv[c] <= kPruneNats);
-      }
-      float pv[4];
-      if (want_out && act) {
-        float lv[4];
+    constexpr uint32_t kRing = 512;  // per wave; at most 63 + 4 * 64 entries pending
+    static_assert(kWaves * kRing * sizeof(int) <= kRegionBBytes, "Gumbel rings fit the region");
+    int *ring = reinterpret_cast<int *>(regB) + wave * kRing;
+    uint32_t qh = 0, qt = 0;  // wave-uniform head and tail
+    auto gumbel_batch = [&](uint32_t cnt) {  // one queued group per lane, cnt <= 64
+      bool improved = false;
+      if ((uint32_t)lane < cnt) {
+        const int l = ring[(qh + lane) & (kRing - 1)];
+        const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+        const int i0 = s0 + l;
+        uint32_t w[4];
+        philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          // logprob: one rounding of the fp64 value; prob = 2^(lp log2 e) by
-          // the hardware exp2 (absolute error below 2e-7)
-          const float lp = kk[c] ? (float)(((double)zv[c] - m) - lnS) : -INFINITY;
-          lv[c] = lp;
-          pv[c] = kk[c] ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
-        }
-        const int64_t o = (int64_t)row * V + i0;
-        if ((kp.vec_ok & 2) && l + 3 < ln) {
-          if (kp.probs) {
-            const f32x4 t = {pv[0], pv[1], pv[2], pv[3]};
-            __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.probs + o));
-          }
-          if (kp.logprobs) {
-            const f32x4 t = {lv[0], lv[1], lv[2], lv[3]};
-            __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.logprobs + o));
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (l + c < ln) {
-              if (kp.probs) kp.probs[o + c] = pv[c];
-              if (kp.logprobs) kp.logprobs[o + c] = lv[c];
-            }
-          }
-        }
-      }
-      if (gumbel) {
-        bool improved = false;
-        if (any_cand) {
-          uint32_t w[4];
-          philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
-          const float lim = want_out ? bound * inv_s : bound;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            if (kk[c] && (mf - zv[c] <= kPruneNats)) {
-              // lower bound of w: (float)x rounds to nearest
-              const float wl = (float)w[c] * 0x1.fffffcp-33f;
-              const float qv = want_out ? pv[c] : __builtin_amdgcn_exp2f((zv[c] - mf) * kLog2e);
-              if (wl * lim <= qv * kSlack) {
-                const double ge = (double)zv[c] - log(exp1_f64(w[c]));
-                if (ge > best_g) {
-                  best_g = ge;
-                  best_i = i0 + c;
-                  improved = true;
-                }
+          if (zv[c] >= tauf && (mf - zv[c] <= kPruneNats)) {
+            // lower bound of w: (float)x rounds to nearest
+            const float wl = (float)w[c] * 0x1.fffffcp-33f;
+            const float qv = __builtin_amdgcn_exp2f((zv[c] - mf) * kLog2e);
+            if (wl * bound <= qv * kSlack) {
+              const double ge = (double)zv[c] - log(exp1_f64(w[c]));
+              if (ge > best_g || (ge == best_g && i0 + c < best_i)) {
+                best_g = ge;
+                best_i = i0 + c;
+                improved = true;
               }
             }
           }
         }
-        if (__ballot(improved)) {
-          float mb = improved ? (float)exp(best_g - m) * 0.99999f : 0.0f;
-          mb = wave_max_nonneg_f(mb);
-          bound = fmaxf(bound, mb);
+      }
+      qh += cnt;
+      if (__ballot(improved)) {
+        float mb = improved ? (float)exp(best_g - m) * 0.99999f : 0.0f;
+        mb = wave_max_nonneg_f(mb);
+        bound = fmaxf(bound, mb);
+      }
+    };
+    const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);  // wave-uniform trip count
+    for (int q0 = 0; q0 < iters; q0 += 4) {
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int l = 4 * tid + 4 * kBlock * (q0 + u);
+        const bool act = l < ln4;
+        f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+        if (act) zv = *reinterpret_cast<const f32x4 *>(zs + l);
+        bool kk[4];
+        bool any_cand = false;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kk[c] = act && zv[c] >= tauf;
+          any_cand |= kk[c] && (mf - zv[c] <= kPruneNats);
+        }
+        if (want_out && act) {
+          float lv[4], pv[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            // logprob: one rounding of the fp64 value; prob = 2^(lp log2 e) by
+            // the hardware exp2 (absolute error below 2e-7)
+            const float lp = kk[c] ? (float)(((double)zv[c] - m) - lnS) : -INFINITY;
+            lv[c] = lp;
+            pv[c] = kk[c] ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
+          }
+          const int64_t o = (int64_t)row * V + s0 + l;
+          if ((kp.vec_ok & 2) && l + 3 < ln) {
+            if (kp.probs) {
+              const f32x4 t = {pv[0], pv[1], pv[2], pv[3]};
+              __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.probs + o));
+            }
+            if (kp.logprobs) {
+              const f32x4 t = {lv[0], lv[1], lv[2], lv[3]};
+              __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.logprobs + o));
+            }
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              if (l + c < ln) {
+                if (kp.probs) kp.probs[o + c] = pv[c];
+                if (kp.logprobs) kp.logprobs[o + c] = lv[c];
+              }
+            }
+          }
+        }
+        if (gumbel) {
+          const unsigned long long bal = __ballot(any_cand);
+          if (bal) {
+            const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (any_cand) ring[(qt + off) & (kRing - 1)] = l;
+            qt += (uint32_t)__popcll(bal);
+          }
         }
       }
+      if (gumbel)
+        while (qt - qh >= 64u) gumbel_batch(64u);
     }
+    if (gumbel && qt != qh) gumbel_batch(qt - qh);
     if (gumbel) wg_best(sm, best_g, best_i);
 
     // ---- 6. final exchange: the last workgroup to arrive writes the row
@@ -1806,7 +1866,7 @@ size_t kernel_lds_region(int slice, int hash_slots, bool penalties) {
   const size_t merge = 8 * (size_t)kMaxG * kMaxTopLogprobs;
   r = r > merge ? r : merge;
   if (penalties) {
-    const size_t pen = sizeof(uint32_t) * ((size_t)hash_slots + ((size_t)slice + 31) / 32 + 1);
+    const size_t pen = sizeof(uint32_t) * (size_t)hash_slots;
     r = r > pen ? r : pen;
   }
   return (r + 15) & ~(size_t)15;

@@ -58,7 +58,6 @@ struct sampler_handle {
   bool slot_used[kRing] = {};
   int next_slot = 0;
   GroupSync *sync = nullptr;
-  GroupRec *recs = nullptr;
   WgSlots *slots = nullptr;
   uint32_t *abort_word = nullptr;  // device word: epoch of an aborted launch
   uint32_t epoch = 0;
@@ -247,7 +246,6 @@ void free_handle(sampler_handle *h) {
   if (h->host_ring) (void)hipHostFree(h->host_ring);
   if (h->dev_ring) (void)hipFree(h->dev_ring);
   if (h->sync) (void)hipFree(h->sync);
-  if (h->recs) (void)hipFree(h->recs);
   if (h->slots) (void)hipFree(h->slots);
   if (h->abort_word) (void)hipFree(h->abort_word);
   delete h;
@@ -339,8 +337,6 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     const size_t n_groups_max = (size_t)h->resident;  // one group per resident workgroup at most
     if ((e = hipMalloc((void **)&h->sync, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
     if ((e = hipMemset(h->sync, 0, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
-    if ((e = hipMalloc((void **)&h->recs, sizeof(GroupRec) * n_groups_max)) != hipSuccess) goto fail;
-    if ((e = hipMemset(h->recs, 0, sizeof(GroupRec) * n_groups_max)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&h->slots, sizeof(WgSlots) * (size_t)h->resident)) != hipSuccess) goto fail;
     if ((e = hipMemset(h->slots, 0, sizeof(WgSlots) * (size_t)h->resident)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&h->abort_word, 256)) != hipSuccess) goto fail;
@@ -492,7 +488,6 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0);
   kp.path = path;
   kp.sync = h->sync;
-  kp.recs = h->recs;
   kp.slots = h->slots;
   kp.abort_word = h->abort_word;
   if (++h->epoch == 0) h->epoch = 1;
