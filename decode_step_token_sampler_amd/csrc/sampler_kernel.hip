@@ -36,6 +36,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "sampler_internal.h"
 
 namespace dsts {
@@ -852,11 +854,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     // take the IEEE division.
     const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
     const uint32_t xhi_b = min(__float_as_uint(T * 0x1p99f), 0x7F7FFFFFu);
-    auto transform = [&]() {
+    auto transform = [&](int b0, int b1) {  // batches [b0, b1) (constants after inlining)
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
         const int l = 4 * tid + 4 * kBlock * b;
-        if (l < ln4) {
+        if (b >= b0 && b < b1 && l < ln4) {
           uint32_t a[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(v[b][c]) & 0x7FFFFFFFu;
@@ -885,13 +887,37 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         }
       }
     };
-    // vector loads in issue order (batch b is later waited for with the
-    // batches behind it still in flight), or scalar loads for unaligned
-    // rows; then the raw logits of the slice's history entries, read again
-    // from the input since the transform overwrites the slice (each path is
-    // straight-line code from its loads to their uses)
-    auto load_raw = [&]() {
+    // History counts live in an LDS hash (id -> count), built between the
+    // two halves of the transform while the second half of the logits is
+    // still arriving: cleared right after the loads are issued, filled
+    // once the history ids have landed.  The raw logits of the slice's
+    // history entries are then read again from the input (the transform
+    // overwrites the slice).
+    int32_t osl[kHistPer];  // hash slot of an entry this thread created, else -1
+    auto build_hash = [&]() {
       if (pen) {
+        __syncthreads();
+#pragma unroll
+        for (int q = 0; q < kHistPer; ++q) {
+          const int32_t id = hv[q];
+          osl[q] = -1;
+          if (id >= s0 && id < s1) {
+            const uint32_t local = (uint32_t)(id - s0);
+            uint32_t sl = hash_slot(local, hslots);
+            while (true) {
+              const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
+              if (prev == kEmpty) {
+                osl[q] = (int32_t)sl;
+                break;
+              }
+              if ((prev >> 13) == local) {
+                atomicAdd(&hash[sl], 1u);
+                break;
+              }
+              sl = (sl + 1u) & (hslots - 1u);
+            }
+          }
+        }
 #pragma unroll
         for (int q = 0; q < kHistPer; ++q) {
           const int32_t id = hv[q];
@@ -900,6 +926,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         }
       }
     };
+    // vector loads in issue order (batch b is later waited for with the
+    // batches behind it still in flight), or scalar loads for unaligned
+    // rows (each path is straight-line code from its loads to their uses)
     if (vec) {
       const int lastg = (ln - 1) & ~3;
 #pragma unroll
@@ -907,43 +936,25 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         Loader<TIn>::load4(kp.logits, rbase + min(4 * tid + 4 * kBlock * b, lastg), v[b]);
         __builtin_amdgcn_sched_barrier(0);
       }
-      load_raw();
-      transform();
+      if (pen)
+        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+      transform(0, kBatch / 2);
+      build_hash();
+      transform(kBatch / 2, kBatch);
     } else {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[b][c] = Loader<TIn>::load1(kp.logits, rbase + min(4 * tid + 4 * kBlock * b + c, ln - 1));
-      load_raw();
-      transform();
+      if (pen)
+        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+      transform(0, kBatch / 2);
+      build_hash();
+      transform(kBatch / 2, kBatch);
     }
     if (pen) {
-      // history counts in an LDS hash (id -> count); the thread that creates
-      // an id's entry penalises that value once, with the final count
-      for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
-      __syncthreads();
-      int32_t osl[kHistPer];  // hash slot of an entry this thread created, else -1
-#pragma unroll
-      for (int q = 0; q < kHistPer; ++q) {
-        const int32_t id = hv[q];
-        osl[q] = -1;
-        if (id >= s0 && id < s1) {
-          const uint32_t local = (uint32_t)(id - s0);
-          uint32_t sl = hash_slot(local, hslots);
-          while (true) {
-            const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
-            if (prev == kEmpty) {
-              osl[q] = (int32_t)sl;
-              break;
-            }
-            if ((prev >> 13) == local) {
-              atomicAdd(&hash[sl], 1u);
-              break;
-            }
-            sl = (sl + 1u) & (hslots - 1u);
-          }
-        }
-      }
+      // the thread that created an id's entry penalises that value once,
+      // with the final count
       __syncthreads();
 #pragma unroll
       for (int q = 0; q < kHistPer; ++q) {
@@ -1017,19 +1028,34 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       double deep_a = 0.0;  // deeper masses, 2^-31 units
       double sx = 0.0;
       if (finite_g && (need_sel || need_exact)) {
-        for (int l = 4 * tid; l < ln4; l += 4 * kBlock) {
-          const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
+        // eight groups of four per step: all reads first, then the bins
+        // (LDS operations complete in order, so a read issued after the
+        // previous step's atomics would wait for them)
+        constexpr int kStep = 8;
+        for (int b0 = 0; b0 < kBatch; b0 += kStep) {
+          f32x4 zr[kStep];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float zz = zv[c];
-            if (need_sel) {
-              const float lb = win_pos(Ag, zz, wsc);  // padding: +inf
-              const bool near = lb < (float)kWinBins;
-              const float a = mass_scaled(mg - zz);
-              if (near) atomicAdd(&wh[(int)lb], hist_entry(a));
-              if (need_deep) deep_a += near ? 0.0 : (double)a;
+          for (int u = 0; u < kStep; ++u) {
+            const int l = 4 * tid + 4 * kBlock * (b0 + u);
+            zr[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+            if (l < ln4) zr[u] = *reinterpret_cast<const f32x4 *>(zs + l);
+          }
+#pragma unroll
+          for (int u = 0; u < kStep; ++u) {
+            float dsum = 0.0f;  // deep masses of the group (each below 2^8 units)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float zz = zr[u][c];
+              if (need_sel) {
+                const float lb = win_pos(Ag, zz, wsc);  // padding: +inf
+                const bool near = lb < (float)kWinBins;
+                const float a = mass_scaled(mg - zz);
+                if (near) atomicAdd(&wh[(int)lb], hist_entry(a));
+                dsum += near ? 0.0f : a;
+              }
+              if (need_exact) sx += exp_nonpos(sm.exp_tab, (double)zz - (double)mg);
             }
-            if (need_exact) sx += exp_nonpos(sm.exp_tab, (double)zz - (double)mg);
+            if (need_deep) deep_a += (double)dsum;
           }
         }
       }
@@ -1270,7 +1296,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       // the gathered bins as runs, from the (up to four) ranges the merge
       // chose: sorted by start and joined where they touch; the first two
       // runs are tested by value, any further bins through the mask
-      int run_lo[2] = {1, 1}, run_hi[2] = {0, 0};
+      int rl0 = 1, rh0 = 0, rl1 = 1, rh1 = 0;  // the first two runs (empty: hi < lo)
       bool more = false;
       {
         int lo[4] = {0, r1lo, rklo, bm}, hi[4] = {r0hi, r1hi, rkhi, bm};
@@ -1286,44 +1312,45 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
               lo[j - 1] = tl;
               hi[j - 1] = th;
             }
+        // join touching ranges; scalars only (a run index would put the
+        // runs in scratch memory)
         int nrun = 0, clo = 0, chi = -1;
+        auto close_run = [&]() {
+          if (chi >= clo) {
+            if (nrun == 0) {
+              rl0 = clo;
+              rh0 = chi;
+            } else if (nrun == 1) {
+              rl1 = clo;
+              rh1 = chi;
+            } else {
+              more = true;
+            }
+            ++nrun;
+          }
+        };
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           if (hi[i] < lo[i]) continue;
           if (chi >= clo && lo[i] <= chi + 1) {
             chi = max(chi, hi[i]);
           } else {
-            if (chi >= clo) {
-              if (nrun < 2) {
-                run_lo[nrun] = clo;
-                run_hi[nrun] = chi;
-              } else {
-                more = true;
-              }
-              ++nrun;
-            }
+            close_run();
             clo = lo[i];
             chi = hi[i];
           }
         }
-        if (chi >= clo) {
-          if (nrun < 2) {
-            run_lo[nrun] = clo;
-            run_hi[nrun] = chi;
-          } else {
-            more = true;
-          }
-        }
+        close_run();
       }
       // each run [lo, hi] as a value range [zlo, zhi): bins lo..hi hold
       // exactly the values with zmin(hi) <= z < zmin(lo - 1)
       if (tid < 4) {
-        const int r = tid >> 1;
+        const int rlo = (tid >> 1) ? rl1 : rl0, rhi = (tid >> 1) ? rh1 : rh0;
         const bool upper = tid & 1;
         float zb;
-        if (run_hi[r] < run_lo[r]) zb = upper ? -INFINITY : INFINITY;  // empty run
-        else if (!upper) zb = win_floor_z(Af, (float)run_hi[r], wsc);
-        else zb = run_lo[r] > 0 ? win_floor_z(Af, (float)(run_lo[r] - 1), wsc) : INFINITY;
+        if (rhi < rlo) zb = upper ? -INFINITY : INFINITY;  // empty run
+        else if (!upper) zb = win_floor_z(Af, (float)rhi, wsc);
+        else zb = rlo > 0 ? win_floor_z(Af, (float)(rlo - 1), wsc) : INFINITY;
         sm.bu[28 + tid] = __float_as_uint(zb);
       }
       __syncthreads();
@@ -1361,7 +1388,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           const int bb = min((int)lb, kWinBins - 1);
           return (lb < (float)kWinBins) & (bool)((sm.binmask[bb >> 5] >> (bb & 31)) & 1u);
         });
-      } else if (run_hi[1] < run_lo[1]) {
+      } else if (rh1 < rl1) {
         gather([&](float z) -> bool { return (z >= z0lo) & (z < z0hi); });
       } else {
         gather([&](float z) -> bool { return ((z >= z0lo) & (z < z0hi)) | ((z >= z1lo) & (z < z1hi)); });
@@ -1659,7 +1686,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     static_assert(kWaves * kRing * sizeof(int) <= kRegionBBytes, "Gumbel rings fit the region");
     int *ring = reinterpret_cast<int *>(regB) + wave * kRing;
     uint32_t qh = 0, qt = 0;  // wave-uniform head and tail
-    auto gumbel_batch = [&](uint32_t cnt) {  // one queued group per lane, cnt <= 64
+    auto gumbel_batch = [&](uint32_t cnt) __attribute__((always_inline)) {  // one queued group per lane, cnt <= 64
       bool improved = false;
       if ((uint32_t)lane < cnt) {
         const int l = ring[(qh + lane) & (kRing - 1)];
@@ -1691,64 +1718,84 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         bound = fmaxf(bound, mb);
       }
     };
+    // The loop is specialised on the output mode (none; both outputs with
+    // 16-byte stores; anything else, element by element) and on Gumbel-max,
+    // with the per-row constants it uses held in vector registers.
     const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);  // wave-uniform trip count
-    for (int q0 = 0; q0 < iters; q0 += 4) {
+    auto emit_loop = [&](auto MODE, auto GUMBEL) __attribute__((always_inline)) {
+      constexpr int mode = decltype(MODE)::value;
+      constexpr bool gum = decltype(GUMBEL)::value;
+      double mv = m, lnsv = lnS;
+      float tv = tauf, mfv = mf;
+      int64_t ob = (int64_t)row * V + s0;  // output offset of the slice
+      asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(mfv), "+v"(ob));
+      for (int q0 = 0; q0 < iters; q0 += 4) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int l = 4 * tid + 4 * kBlock * (q0 + u);
-        const bool act = l < ln4;
-        f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-        if (act) zv = *reinterpret_cast<const f32x4 *>(zs + l);
-        bool kk[4];
-        bool any_cand = false;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          kk[c] = act && zv[c] >= tauf;
-          any_cand |= kk[c] && (mf - zv[c] <= kPruneNats);
-        }
-        if (want_out && act) {
-          float lv[4], pv[4];
+        for (int u = 0; u < 4; ++u) {
+          const int l = 4 * tid + 4 * kBlock * (q0 + u);
+          const bool act = l < ln4;
+          f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+          if (act) zv = *reinterpret_cast<const f32x4 *>(zs + l);
+          bool kk[4];
+          bool any_cand = false;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
-            // logprob: one rounding of the fp64 value; prob = 2^(lp log2 e) by
-            // the hardware exp2 (absolute error below 2e-7)
-            const float lp = kk[c] ? (float)(((double)zv[c] - m) - lnS) : -INFINITY;
-            lv[c] = lp;
-            pv[c] = kk[c] ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
+            kk[c] = zv[c] >= tv;  // padding (-inf) only passes when tau is 0
+            any_cand |= kk[c] && (mfv - zv[c] <= kPruneNats);
           }
-          const int64_t o = (int64_t)row * V + s0 + l;
-          if ((kp.vec_ok & 2) && l + 3 < ln) {
-            if (kp.probs) {
-              const f32x4 t = {pv[0], pv[1], pv[2], pv[3]};
-              __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.probs + o));
-            }
-            if (kp.logprobs) {
-              const f32x4 t = {lv[0], lv[1], lv[2], lv[3]};
-              __builtin_nontemporal_store(t, reinterpret_cast<f32x4 *>(kp.logprobs + o));
-            }
-          } else {
+          if (mode != 0 && act) {
+            float lv[4], pv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              if (l + c < ln) {
-                if (kp.probs) kp.probs[o + c] = pv[c];
-                if (kp.logprobs) kp.logprobs[o + c] = lv[c];
+              // logprob: one rounding of the fp64 value; prob = 2^(lp log2 e)
+              // by the hardware exp2 (absolute error below 2e-7)
+              const float lp = kk[c] ? (float)(((double)zv[c] - mv) - lnsv) : -INFINITY;
+              lv[c] = lp;
+              pv[c] = kk[c] ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
+            }
+            const int64_t o = ob + l;
+            if (mode == 1 && l + 3 < ln) {
+              __builtin_nontemporal_store(f32x4{pv[0], pv[1], pv[2], pv[3]}, reinterpret_cast<f32x4 *>(kp.probs + o));
+              __builtin_nontemporal_store(f32x4{lv[0], lv[1], lv[2], lv[3]}, reinterpret_cast<f32x4 *>(kp.logprobs + o));
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                if (l + c < ln) {
+                  if (kp.probs) kp.probs[o + c] = pv[c];
+                  if (kp.logprobs) kp.logprobs[o + c] = lv[c];
+                }
               }
             }
           }
-        }
-        if (gumbel) {
-          const unsigned long long bal = __ballot(any_cand);
-          if (bal) {
-            const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-            if (any_cand) ring[(qt + off) & (kRing - 1)] = l;
-            qt += (uint32_t)__popcll(bal);
+          if (gum) {
+            const unsigned long long bal = __ballot(act && any_cand);
+            if (bal) {
+              const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+              if (act && any_cand) ring[(qt + off) & (kRing - 1)] = l;
+              qt += (uint32_t)__popcll(bal);
+            }
           }
         }
+        if (gum)
+          while (qt - qh >= 64u) gumbel_batch(64u);
       }
-      if (gumbel)
-        while (qt - qh >= 64u) gumbel_batch(64u);
+      if (gum && qt != qh) gumbel_batch(qt - qh);
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    using BT = std::integral_constant<bool, true>;
+    using BF = std::integral_constant<bool, false>;
+    const int omode = !want_out ? 0 : (((kp.vec_ok & 2) && kp.probs && kp.logprobs) ? 1 : 2);
+    if (gumbel) {
+      if (omode == 0) emit_loop(I0{}, BT{});
+      else if (omode == 1) emit_loop(I1{}, BT{});
+      else emit_loop(I2{}, BT{});
+    } else {
+      if (omode == 0) emit_loop(I0{}, BF{});
+      else if (omode == 1) emit_loop(I1{}, BF{});
+      else emit_loop(I2{}, BF{});
     }
-    if (gumbel && qt != qh) gumbel_batch(qt - qh);
     if (gumbel) wg_best(sm, best_g, best_i);
 
     // ---- 6. final exchange: the last workgroup to arrive writes the row
