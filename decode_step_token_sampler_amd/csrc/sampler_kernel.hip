@@ -1462,34 +1462,63 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         }
       }
       {
-        const bool ovf = sm.bu[12] != 0u;
+        bool ovf = sm.bu[12] != 0u;
         const int n = ovf ? 0 : (int)sm.goff[G];
-        if (tid == 0) sk[n] = 0ull;  // pads an odd count for the pairwise reads below
-        __syncthreads();
-        // rank each candidate by counting the larger keys (keys are distinct:
-        // each holds its index), two candidates per thread, keys read in
-        // 16-byte pairs by every thread at once; the ranks place the list in
-        // (value desc, index asc) order, a total order, so the list and every
-        // sum over it do not depend on the gather order
+        // sort by rank counting: a candidate's position is the number of
+        // larger keys (keys are distinct: each holds its index), so the list
+        // is in (value desc, index asc) order, a total order, and it and
+        // every sum over it do not depend on the gather order.  Only the
+        // waves holding candidates count, eight keys per step.
+        // The gathered bins are complete, so a masked scan of the merged
+        // histogram's counts gives each bin's first position in the list
+        // (lc becomes those positions), checked against the sorted keys.
+        const uint32_t c_rk = rklo > 0 ? lc[min(rklo - 1, kWinBins - 1)] : 0u;  // values above the top-k bin
+        unsigned long long *srt = reinterpret_cast<unsigned long long *>(sq);  // the sorted keys
+        double *pre = reinterpret_cast<double *>(sk);                          // then their prefix masses
         {
-          const unsigned long long c0 = tid < n ? sk[tid] : ~0ull;
-          const unsigned long long c1 = tid + kBlock < n ? sk[tid + kBlock] : ~0ull;
-          uint32_t r0 = 0, r1 = 0;
-#pragma unroll 4
-          for (int j = 0; j < n; j += 2) {
-            const unsigned long long ka = sk[j], kb = sk[j + 1];
-            r0 += (ka > c0 ? 1u : 0u) + (kb > c0 ? 1u : 0u);
-            r1 += (ka > c1 ? 1u : 0u) + (kb > c1 ? 1u : 0u);
+          const int b = tid;
+          const bool gb = (sm.binmask[b >> 5] >> (b & 31)) & 1u;
+          const uint32_t cb = gb ? lc[b] - (b > 0 ? lc[b - 1] : 0u) : 0u;
+          const uint32_t incl = block_scan_incl<uint32_t>(cb, sm.red_c);
+          lc[b] = incl - cb;
+          auto rank_of = [&](unsigned long long c) {
+            uint32_t r = 0;
+            int j = 0;
+            for (; j + 8 <= n; j += 8) {  // eight keys read before any compare
+              unsigned long long kk[8];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) kk[u] = sk[j + u];
+#pragma unroll
+              for (int u = 0; u < 8; ++u) r += kk[u] > c ? 1u : 0u;
+            }
+            for (; j < n; ++j) r += sk[j] > c ? 1u : 0u;
+            return r;
+          };
+          if (wave * 64 < n) {
+            const unsigned long long c0 = tid < n ? sk[tid] : ~0ull;
+            const uint32_t r0 = rank_of(c0);
+            if (tid < n) srt[r0] = c0;
+          }
+          if (kBlock + wave * 64 < n) {
+            const unsigned long long c1 = tid + kBlock < n ? sk[tid + kBlock] : ~0ull;
+            const uint32_t r1 = rank_of(c1);
+            if (tid + kBlock < n) srt[r1] = c1;
           }
           __syncthreads();
-          if (tid < n) sk[r0] = c0;
-          if (tid + kBlock < n) sk[r1] = c1;
-          __syncthreads();
+          // each gathered bin's first and last positions hold keys of that
+          // bin (else the exact path)
+          bool bad = false;
+          if (cb > 0) {
+            const int f = (int)(incl - cb), e = (int)incl - 1;
+            bad = e >= n || win_bin(Af, key_to_float((uint32_t)(srt[f] >> 32)), wsc) != b ||
+                  win_bin(Af, key_to_float((uint32_t)(srt[e] >> 32)), wsc) != b;
+          }
+          if (__syncthreads_or(bad)) ovf = true;
         }
-        auto keyof = [&](int j) { return (uint32_t)(sk[j] >> 32); };
+        auto keyof = [&](int j) { return (uint32_t)(srt[j] >> 32); };
         auto zof = [&](int j) { return key_to_float(keyof(j)); };
-        auto idxof = [&](int j) { return (int)(~(uint32_t)sk[j]); };
-        auto binof = [&](int j) { return win_bin(Af, zof(j), wsc); };
+        auto idxof = [&](int j) { return (int)(~(uint32_t)srt[j]); };
+        auto fpos = [&](int b) { return b >= kWinBins ? n : (int)lc[b]; };  // first position of bin b
         // inclusive prefix of exact masses exp(z - m) along the sorted list;
         // each thread owns kCandCap / kBlock consecutive positions
         {
@@ -1508,33 +1537,17 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           for (int u = 0; u < kPerC; ++u) {
             const int j = tid * kPerC + u;
             run += qv[u];
-            if (j < n) sq[j] = run;
+            if (j < n) pre[j] = run;
           }
         }
-        auto qsum = [&](int a, int e) { return (e < a) ? 0.0 : sq[e] - (a > 0 ? sq[a - 1] : 0.0); };
+        auto qsum = [&](int a, int e) { return (e < a) ? 0.0 : pre[e] - (a > 0 ? pre[a - 1] : 0.0); };
         auto cmass = [&](int b) { return b < 0 ? 0.0 : (double)lm[b < kWinBins ? b : kWinBins] / kWinScale; };
-        auto ccnt = [&](int b) { return b < 0 ? 0u : lc[b < kWinBins ? b : kWinBins - 1]; };
-        // first positions of the bins that bound the ranges (the values of
-        // one bin are a contiguous run of the sorted list)
-        if (tid == 0) {
-          sm.bu[20] = (uint32_t)n;
-          sm.bu[21] = (uint32_t)n;
-          sm.bu[22] = (uint32_t)n;
-        }
-        __syncthreads();
-        for (int j = tid; j < n; j += kBlock) {
-          const int bj = binof(j), bp = j > 0 ? binof(j - 1) : -1;
-          if (bj >= rklo && bp < rklo) sm.bu[20] = (uint32_t)j;
-          if (bj >= r1lo && bp < r1lo) sm.bu[21] = (uint32_t)j;
-          if (bj >= r1hi + 1 && bp < r1hi + 1) sm.bu[22] = (uint32_t)j;
-        }
-        __syncthreads();
-        const int fp_k = (int)sm.bu[20], fp_p0 = (int)sm.bu[21], fp_p1 = (int)sm.bu[22];
+        const int fp_k = fpos(rklo), fp_p0 = fpos(r1lo), fp_p1 = fpos(r1hi + 1);
         // top-k: the value of rank k, and the end of its tie group
         uint32_t flags = ovf ? 1u : 0u;
         uint32_t tk = 0;
         if (!flags && topk_on) {
-          const int jk = full_k ? P.top_k - 1 : fp_k + (P.top_k - (int)ccnt(rklo - 1)) - 1;
+          const int jk = full_k ? P.top_k - 1 : fp_k + (P.top_k - (int)c_rk) - 1;
           if (jk < 0 || jk >= n) flags |= 1u;
           else tk = keyof(jk);
         }
@@ -1551,12 +1564,15 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         if (!flags && topp) {
           const double ctot = topk_on ? (full_k ? qsum(0, ek) : cmass(rklo - 1) + qsum(fp_k, ek)) : cmass(kWinBins);
           const double target = (double)P.top_p * ctot;
-          const double base = full_k ? 0.0 : cmass(r1lo - 1) - (fp_p0 > 0 ? sq[fp_p0 - 1] : 0.0);
+          const double base = full_k ? 0.0 : cmass(r1lo - 1) - (fp_p0 > 0 ? pre[fp_p0 - 1] : 0.0);
           if (tid == 0) sm.bu[24] = 0x7FFFFFFFu;
           __syncthreads();
           for (int e = fp_p0 + tid; e < fp_p1; e += kBlock) {
             const bool end = (e == n - 1) || (keyof(e + 1) != keyof(e));
-            if (end && base + sq[e] >= target) atomicMin(&sm.bu[24], (uint32_t)e);
+            // positions rise with the lane: the wave's first passing lane
+            // holds its smallest passing position
+            const unsigned long long bal = __ballot(end && base + pre[e] >= target);
+            if (bal && lane == __ffsll((long long)bal) - 1) atomicMin(&sm.bu[24], (uint32_t)e);
           }
           __syncthreads();
           const uint32_t e = sm.bu[24];
@@ -1566,19 +1582,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         if (minp) t = max(t, t_m);
         // the kept set: positions [0, et); its sum and the top logprobs
         const int bt = t ? win_bin(Af, key_to_float(t), wsc) : kWinBins;
-        if (tid == 0) {
-          sm.bu[25] = (uint32_t)n;
-          sm.bu[26] = (uint32_t)n;
-        }
+        if (tid == 0) sm.bu[25] = (uint32_t)n;
         __syncthreads();
         if (t)
-          for (int j = tid; j < n; j += kBlock) {
+          for (int j = tid; j < n; j += kBlock)
             if (keyof(j) < t && (j == 0 || keyof(j - 1) >= t)) sm.bu[25] = (uint32_t)j;
-            const int bj = binof(j), bp = j > 0 ? binof(j - 1) : -1;
-            if (bj >= bt && bp < bt) sm.bu[26] = (uint32_t)j;
-          }
         __syncthreads();
-        const int et = (int)sm.bu[25], fp_bt = (int)sm.bu[26];
+        const int et = (int)sm.bu[25], fp_bt = fpos(bt);
         double S_K = s_all;
         if (!flags && truncated && want_S) {
           if (full_k && bt <= rkhi) S_K = qsum(0, et - 1);
@@ -1728,7 +1738,14 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       double mv = m, lnsv = lnS;
       float tv = tauf, mfv = mf;
       int64_t ob = (int64_t)row * V + s0;  // output offset of the slice
-      asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(mfv), "+v"(ob));
+      // the slice's output rows, as global pointers held in vector registers
+      typedef __attribute__((address_space(1))) f32x4 gf32x4;
+      gf32x4 *pq = nullptr, *lq = nullptr;
+      if (mode == 1) {
+        pq = (gf32x4 *)(kp.probs + ob);
+        lq = (gf32x4 *)(kp.logprobs + ob);
+      }
+      asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(mfv), "+v"(ob), "+v"(pq), "+v"(lq));
       for (int q0 = 0; q0 < iters; q0 += 4) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
@@ -1755,8 +1772,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             }
             const int64_t o = ob + l;
             if (mode == 1 && l + 3 < ln) {
-              __builtin_nontemporal_store(f32x4{pv[0], pv[1], pv[2], pv[3]}, reinterpret_cast<f32x4 *>(kp.probs + o));
-              __builtin_nontemporal_store(f32x4{lv[0], lv[1], lv[2], lv[3]}, reinterpret_cast<f32x4 *>(kp.logprobs + o));
+              __builtin_nontemporal_store(f32x4{pv[0], pv[1], pv[2], pv[3]}, pq + (l >> 2));
+              __builtin_nontemporal_store(f32x4{lv[0], lv[1], lv[2], lv[3]}, lq + (l >> 2));
             } else {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
