@@ -1360,12 +1360,21 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       // rare) by the bin mask; groups of four in a fixed, unrolled order so
       // the LDS reads overlap; the staging branch runs only for the waves
       // that hold a candidate
-      auto gather = [&](auto is_cand) {
+      auto gather = [&](auto is_cand) __attribute__((always_inline)) {
+        constexpr int kStep = 8;  // groups read before any is tested
+        f32x4 zr[kStep];
 #pragma unroll
         for (int q = 0; q < kBatch; ++q) {
           const int l = 4 * tid + 4 * kBlock * q;
-          f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          if (l < ln4) zv = *reinterpret_cast<const f32x4 *>(zs + l);
+          if (q % kStep == 0) {
+#pragma unroll
+            for (int u = 0; u < kStep; ++u) {
+              const int lu = l + 4 * kBlock * u;
+              zr[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+              if (lu < ln4) zr[u] = *reinterpret_cast<const f32x4 *>(zs + lu);
+            }
+          }
+          const f32x4 zv = zr[q % kStep];
           bool isc[4];
 #pragma unroll
           for (int c = 0; c < 4; ++c) isc[c] = is_cand(zv[c]);
