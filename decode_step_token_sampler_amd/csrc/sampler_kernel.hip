@@ -779,8 +779,26 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   double *sq = reinterpret_cast<double *>(regB + 8 * kCandCap);
 
   const int G = kp.G;
-  const int gid = blockIdx.x % G;
-  const int group = blockIdx.x / G;
+  // Block b runs on XCD b % 8 (the dispatcher deals blocks round-robin over
+  // the eight XCDs), so the G workgroups of a group are taken from one
+  // residue class: their exchanges then stay on one XCD (a group barrier
+  // measures ~0.86 us there against ~1.16 us across XCDs).  Only speed
+  // depends on this; every exchange is coherent device-wide either way.
+  // Groups beyond a multiple of 8 take consecutive blocks.
+  int group, gid;
+  {
+    const int b = blockIdx.x;
+    const int gpx = kp.n_groups / 8;  // groups per XCD in the XCD-aware part
+    const int nbx = gpx * 8 * G;
+    if (b < nbx) {
+      const int q = b / 8;
+      group = (b % 8) * gpx + q / G;
+      gid = q % G;
+    } else {
+      group = gpx * 8 + (b - nbx) / G;
+      gid = (b - nbx) % G;
+    }
+  }
   const int V = kp.vocab;
   const uint32_t hslots = (uint32_t)kp.hash_slots;
   unsigned xseq = 0;
@@ -790,7 +808,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   rc.gsync = kp.sync + group;
   rc.abort_word = kp.abort_word;
   rc.epoch = kp.epoch;
-  rc.my = kp.slots + blockIdx.x;
+  rc.my = kp.slots + (size_t)group * G + gid;
   rc.peers = kp.slots + (size_t)group * G;
   rc.xseq = &xseq;
   const bool want_out = kp.probs != nullptr || kp.logprobs != nullptr;
