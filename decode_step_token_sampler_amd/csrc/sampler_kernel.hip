@@ -546,14 +546,14 @@ struct RowCtx {
 
 DEV void row_barrier(SmemBase &sm, RowCtx &rc) { group_barrier(sm, rc.gsync, rc.G, rc.abort_word, rc.epoch); }
 
-// Bins on an absolute grid: abin(z) = floor(z wsc 32) with wsc = min(1, T),
+// Bins on an absolute grid: abin(z) = floor(z (32 wsc)) with wsc = min(1, T),
 // so a bin is 1/32 nat of the logits x = z T below T = 1 and of z above it.
 // A value's window bin is A - abin(z), counted down from the anchor A =
 // abin(row max); bins from kWinBins on are deep.  Every bin of the kernel is
 // computed by these two expressions (float operations: monotone in z, so
 // the bins partition the value axis in order, and an anchor shift between
 // two slices is a whole number of bins while |z wsc 32| < 2^24).
-DEV float abin(float z, float wsc) { return floorf((z * wsc) * kBinsPerNat); }
+DEV float abin(float z, float wsc) { return floorf(z * (wsc * (float)kBinsPerNat)); }
 DEV float win_pos(float A, float z, float wsc) { return A - abin(z, wsc); }
 DEV int win_bin(float A, float z, float wsc) {
   const float lb = win_pos(A, z, wsc);
@@ -1046,35 +1046,48 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       double deep_a = 0.0;  // deeper masses, 2^-31 units
       double sx = 0.0;
       if (finite_g && (need_sel || need_exact)) {
-        // eight groups of four per step: all reads first, then the bins
+        // Specialised on what the row needs (window bins, their deeper mass,
+        // the exact sum).  Eight groups of four per step: all reads first
+        // (from clamped addresses; only the work is guarded), then the bins
         // (LDS operations complete in order, so a read issued after the
-        // previous step's atomics would wait for them)
-        constexpr int kStep = 8;
-        for (int b0 = 0; b0 < kBatch; b0 += kStep) {
-          f32x4 zr[kStep];
+        // previous step's atomics would wait for them).
+        auto hist_pass = [&](auto SEL, auto DEEP, auto EXACT) __attribute__((always_inline)) {
+          constexpr bool sel = decltype(SEL)::value, deep = decltype(DEEP)::value, exact = decltype(EXACT)::value;
+          constexpr int kStep = 8;
+          for (int b0 = 0; b0 < kBatch; b0 += kStep) {
+            f32x4 zr[kStep];
 #pragma unroll
-          for (int u = 0; u < kStep; ++u) {
-            const int l = 4 * tid + 4 * kBlock * (b0 + u);
-            zr[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-            if (l < ln4) zr[u] = *reinterpret_cast<const f32x4 *>(zs + l);
-          }
+            for (int u = 0; u < kStep; ++u)
+              zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * kBlock * (b0 + u), ln4 - 4));
 #pragma unroll
-          for (int u = 0; u < kStep; ++u) {
-            float dsum = 0.0f;  // deep masses of the group (each below 2^8 units)
+            for (int u = 0; u < kStep; ++u) {
+              if (4 * tid + 4 * kBlock * (b0 + u) < ln4) {
+                float dsum = 0.0f;  // deep masses of the group (each below 2^8 units)
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float zz = zr[u][c];
-              if (need_sel) {
-                const float lb = win_pos(Ag, zz, wsc);  // padding: +inf
-                const bool near = lb < (float)kWinBins;
-                const float a = mass_scaled(mg - zz);
-                if (near) atomicAdd(&wh[(int)lb], hist_entry(a));
-                dsum += near ? 0.0f : a;
+                for (int c = 0; c < 4; ++c) {
+                  const float zz = zr[u][c];
+                  if (sel) {
+                    const float lb = win_pos(Ag, zz, wsc);  // padding: +inf
+                    const bool near = lb < (float)kWinBins;
+                    const float a = mass_scaled(mg - zz);
+                    if (near) atomicAdd(&wh[(int)lb], hist_entry(a));
+                    if (deep) dsum += near ? 0.0f : a;
+                  }
+                  if (exact) sx += exp_nonpos(sm.exp_tab, (double)zz - (double)mg);
+                }
+                if (deep) deep_a += (double)dsum;
               }
-              if (need_exact) sx += exp_nonpos(sm.exp_tab, (double)zz - (double)mg);
             }
-            if (need_deep) deep_a += (double)dsum;
           }
+        };
+        using T1 = std::integral_constant<bool, true>;
+        using F1 = std::integral_constant<bool, false>;
+        if (need_sel) {
+          if (need_deep) hist_pass(T1{}, T1{}, F1{});
+          else if (need_exact) hist_pass(T1{}, F1{}, T1{});
+          else hist_pass(T1{}, F1{}, F1{});
+        } else {
+          hist_pass(F1{}, F1{}, T1{});
         }
       }
       const double wdm = need_deep ? wg_sum_d(sm, deep_a) : 0.0;
@@ -1386,16 +1399,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           const int l = 4 * tid + 4 * kBlock * q;
           if (q % kStep == 0) {
 #pragma unroll
-            for (int u = 0; u < kStep; ++u) {
-              const int lu = l + 4 * kBlock * u;
-              zr[u] = f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-              if (lu < ln4) zr[u] = *reinterpret_cast<const f32x4 *>(zs + lu);
-            }
+            for (int u = 0; u < kStep; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(l + 4 * kBlock * u, ln4 - 4));
           }
           const f32x4 zv = zr[q % kStep];
+          const bool in_slice = l < ln4;  // (a clamped read repeats the last group)
           bool isc[4];
 #pragma unroll
-          for (int c = 0; c < 4; ++c) isc[c] = is_cand(zv[c]);
+          for (int c = 0; c < 4; ++c) isc[c] = in_slice && is_cand(zv[c]);
           if (__ballot(isc[0] | isc[1] | isc[2] | isc[3])) {
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
