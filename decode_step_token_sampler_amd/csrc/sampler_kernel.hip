@@ -1723,20 +1723,18 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
     float bound = 0.0f;
-    if (gumbel) {
-      // the argmax is always kept; its score is 1 / E
-      uint32_t w4[4];
-      philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
-      bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
-    }
-    constexpr uint32_t kRing = 512;  // per wave; at most 63 + 4 * 64 entries pending
-    static_assert(kWaves * kRing * sizeof(int) <= kRegionBBytes, "Gumbel rings fit the region");
-    int *ring = reinterpret_cast<int *>(regB) + wave * kRing;
+    // Groups of four that hold a Gumbel candidate (kept, and within
+    // kPruneNats of the max) are listed per wave in LDS while the outputs
+    // are written (16-bit group numbers; every group the wave visits fits),
+    // then finished on full waves: Philox and the filter.
+    constexpr uint32_t kRing = kMaxSlice / 4 / kWaves;  // groups one wave visits at most
+    static_assert(kWaves * kRing * sizeof(uint16_t) <= kRegionBBytes, "candidate lists fit the region");
+    uint16_t *ring = reinterpret_cast<uint16_t *>(regB) + wave * kRing;
     uint32_t qh = 0, qt = 0;  // wave-uniform head and tail
     auto gumbel_batch = [&](uint32_t cnt) __attribute__((always_inline)) {  // one queued group per lane, cnt <= 64
       bool improved = false;
       if ((uint32_t)lane < cnt) {
-        const int l = ring[(qh + lane) & (kRing - 1)];
+        const int l = 4 * (int)ring[qh + lane];
         const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
         const int i0 = s0 + l;
         uint32_t w[4];
@@ -1784,20 +1782,37 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
       asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(mfv), "+v"(ob), "+v"(pq), "+v"(lq));
       for (int q0 = 0; q0 < iters; q0 += 4) {
+        f32x4 zr[4];  // the chunk's four groups, read first (clamped addresses)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * kBlock * (q0 + u), ln4 - 4));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int l = 4 * tid + 4 * kBlock * (q0 + u);
           const bool act = l < ln4;
-          f32x4 zv = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-          if (act) zv = *reinterpret_cast<const f32x4 *>(zs + l);
+          const f32x4 zv = zr[u];
           bool kk[4];
-          bool any_cand = false;
+          bool anyk = false, any_cand = false;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             kk[c] = zv[c] >= tv;  // padding (-inf) only passes when tau is 0
+            anyk |= kk[c];
             any_cand |= kk[c] && (mfv - zv[c] <= kPruneNats);
           }
-          if (mode != 0 && act) {
+          // a wave whose groups keep nothing stores 0 / -inf without the math
+          if (mode != 0 && act && !__ballot(act && anyk)) {
+            if (mode == 1 && l + 3 < ln) {
+              __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pq + (l >> 2));
+              __builtin_nontemporal_store(f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lq + (l >> 2));
+            } else {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                if (l + c < ln) {
+                  if (kp.probs) kp.probs[ob + l + c] = 0.0f;
+                  if (kp.logprobs) kp.logprobs[ob + l + c] = -INFINITY;
+                }
+              }
+            }
+          } else if (mode != 0 && act) {
             float lv[4], pv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -1825,15 +1840,20 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             const unsigned long long bal = __ballot(act && any_cand);
             if (bal) {
               const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-              if (act && any_cand) ring[(qt + off) & (kRing - 1)] = l;
+              if (act && any_cand) ring[qt + off] = (uint16_t)(l >> 2);
               qt += (uint32_t)__popcll(bal);
             }
           }
         }
-        if (gum)
-          while (qt - qh >= 64u) gumbel_batch(64u);
       }
-      if (gum && qt != qh) gumbel_batch(qt - qh);
+      if (gum) {
+        // the bound starts at the argmax's own score 1 / E (the argmax is
+        // always kept)
+        uint32_t w4[4];
+        philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
+        bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
+        for (; qh < qt;) gumbel_batch(min(qt - qh, 64u));
+      }
     };
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
