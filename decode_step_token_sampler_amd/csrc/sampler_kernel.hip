@@ -331,6 +331,28 @@ DEV T block_scan_incl(T v, T *wave_tot) {
   return v + base;
 }
 
+// Inclusive scans of a count and a mass per thread over the workgroup,
+// sharing one barrier; the caller passes another barrier before it writes
+// the wave totals again.
+DEV void block_scan_incl2(uint32_t &c, unsigned long long &v, uint32_t *ctot, unsigned long long *vtot) {
+  const int lane = tidx() & 63, w = tidx() >> 6;
+  c = wave_scan(c);
+  v = wave_scan(v);
+  if (lane == 63) {
+    ctot[w] = c;
+    vtot[w] = v;
+  }
+  __syncthreads();
+  uint32_t cb = 0;
+  unsigned long long vb = 0;
+  for (int i = 0; i < w; ++i) {
+    cb += ctot[i];
+    vb += vtot[i];
+  }
+  c += cb;
+  v += vb;
+}
+
 // Philox4x32-10 block for counter (c0..c3) and key (k0, k1); each round
 // takes both halves of the two 32x32-bit products.
 DEV void philox4x32_10(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0, uint32_t k1,
@@ -519,9 +541,11 @@ DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t e
 }
 
 // Barrier: one atomic add; the last arrival resets the count and advances
-// the generation in one store, the others wait for it.
-DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch) {
-  order_release();
+// the generation in one store, the others wait for it.  all_waves = false:
+// only wave 0 wrote data the other workgroups read, so only it waits for
+// its stores.
+DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch, bool all_waves = true) {
+  if (all_waves || tidx() < 64) order_release();
   __syncthreads();
   if (tidx() == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&s->word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -531,6 +555,14 @@ DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, 
     order_acquire();
   }
   __syncthreads();
+}
+
+// An exchange slot's address, computed where it is used from an opaque
+// index (a slot pointer kept live across the row would be spilled).
+DEV WgSlots *slot_at(const KernelParams &kp, int i) {
+  i = __builtin_amdgcn_readfirstlane(i);
+  asm volatile("" : "+s"(i));
+  return kp.slots + i;
 }
 
 // Per-row context shared by the phases.
@@ -725,40 +757,188 @@ DEV uint32_t min_p_key_serial(double m, float min_p) {
   return hi;
 }
 
-// Parallel form: the boundary lies within a few keys of the guess, so 128
-// threads test the keys around it; outside that span, the serial search.
-DEV uint32_t min_p_key(SmemBase &sm, double m, float min_p) {
+// Parallel form: the boundary lies within a few keys of the guess, so two
+// waves test the 128 keys around it, one key per lane, and the boundary is
+// the lowest passing key of their ballots (pass is monotone in the key).
+// Outside that span, the serial search.  lmp = ln(min_p), taken by the
+// caller ahead of the exchange so its latency hides in the wait.  The
+// ballots go to bu[32..35], read after one barrier; the caller passes
+// other barriers before this function runs again.
+DEV uint32_t min_p_key(SmemBase &sm, double m, double lmp, float min_p) {
   constexpr int kSpan = 128;
   const int tid = tidx();
   const double mp = (double)min_p;
   const uint32_t top = fkey((float)m);
-  uint32_t g = fkey((float)(m + log(mp)));
+  uint32_t g = fkey((float)(m + lmp));
   if (g > top) g = top;
   const int64_t k0 = (int64_t)g - kSpan / 2;
-  auto pass = [&](int64_t k) {
-    if (k > (int64_t)top) return true;
-    if (k < 0) return false;
-    return exp((double)key_to_float((uint32_t)k) - m) >= mp;
-  };
-  if (tid == 0) sm.bu[20] = kNone;
-  __syncthreads();
   if (tid < kSpan) {
     const int64_t k = k0 + tid;
-    if (tid > 0 && pass(k) && !pass(k - 1)) sm.bu[20] = (uint32_t)k;
+    bool p;
+    if (k > (int64_t)top) {
+      p = true;
+    } else if (k < 0) {
+      p = false;
+    } else {
+      const double x = (double)key_to_float((uint32_t)k) - m;  // <= 0, or NaN below -inf's key
+      p = x == x && exp_nonpos(sm.exp_tab, x) >= mp;
+    }
+    const unsigned long long bal = __ballot(p);
+    if ((tid & 63) == 0) {
+      sm.bu[32 + 2 * (tid >> 6)] = (uint32_t)bal;
+      sm.bu[33 + 2 * (tid >> 6)] = (uint32_t)(bal >> 32);
+    }
   }
   __syncthreads();
-  uint32_t r = sm.bu[20];
-  __syncthreads();
-  if (r == kNone) {  // boundary outside the span (or at its first key)
-    if (tid == 0) sm.bu[20] = min_p_key_serial(m, min_p);
-    __syncthreads();
-    r = sm.bu[20];
-    __syncthreads();
-  }
-  return r;
+  const unsigned long long b0 = u64_of(sm.bu[32], sm.bu[33]), b1 = u64_of(sm.bu[34], sm.bu[35]);
+  const int first = b0 ? __ffsll((long long)b0) - 1 : b1 ? 64 + __ffsll((long long)b1) - 1 : -1;
+  if (first <= 0) return min_p_key_serial(m, min_p);  // the boundary lies outside the span
+  return (uint32_t)(k0 + first);
 }
 
-
+// Exchange 3 for at most 64 candidates, by one wave with one candidate per
+// lane and no workgroup barrier: the same list, checks and decisions as the
+// workgroup form in the kernel (sorted candidates, each gathered bin's
+// first position and a check of the list against the merged counts,
+// prefix masses, the end of the top-k tie group, the top-p crossing, the
+// kept-set sum and the top logprobs), with ballots in place of the
+// searches.  The sorted keys go to sq (sk holds the unsorted ones), and lc
+// becomes the bins' first positions.
+struct E3In {
+  int top_k;
+  float top_p;
+  double m, s_all;
+  float Af, wsc;
+  uint32_t t_m;
+  int rklo, rkhi, r1lo, r1hi, K, row, gid;
+  bool full_k, topk_on, topp, minp, truncated, want_S;
+};
+struct E3Out {
+  bool general;
+  uint32_t tau;
+  double lnS;
+};
+DEV E3Out e3_wave(SmemBase &sm, const int n, const unsigned long long *sk, double *sq, uint32_t *lc, const unsigned long long *lm,
+                  const E3In &in, const KernelParams &kp) {
+  const int lane = tidx() & 63;
+  unsigned long long *srt = reinterpret_cast<unsigned long long *>(sq);
+  const bool has = lane < n;
+  // position = the number of larger keys (keys are distinct: each holds
+  // its index), eight keys read before any compare
+  {
+    const unsigned long long ck = has ? sk[lane] : 0ull;
+    uint32_t r = 0;
+    for (int j = 0; j < n; j += 8) {
+      unsigned long long kk[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) kk[u] = sk[min(j + u, n - 1)];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) r += (j + u < n && kk[u] > ck) ? 1u : 0u;
+    }
+    __builtin_amdgcn_wave_barrier();
+    if (has) srt[r] = ck;
+  }
+  // values above the top-k bin (merged inclusive counts, read before lc
+  // becomes positions)
+  const uint32_t c_rk = in.rklo > 0 ? lc[min(in.rklo - 1, kWinBins - 1)] : 0u;
+  // the gathered bins' first positions: a masked scan of the merged counts,
+  // eight bins per lane
+  uint32_t tot;
+  {
+    uint32_t cbs[8], sum = 0;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int b = 8 * lane + u;
+      const bool gb = (sm.binmask[b >> 5] >> (b & 31)) & 1u;
+      cbs[u] = gb ? lc[b] - (b > 0 ? lc[b - 1] : 0u) : 0u;
+      sum += cbs[u];
+    }
+    const uint32_t incl = wave_scan_u32(sum);
+    tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+    uint32_t run = incl - sum;
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      lc[8 * lane + u] = run;
+      run += cbs[u];
+    }
+  }
+  __builtin_amdgcn_wave_barrier();
+  const unsigned long long sj = has ? srt[lane] : 0ull;  // the key at position lane
+  const uint32_t kj = (uint32_t)(sj >> 32);
+  // the list against the merged counts: as many candidates as the gathered
+  // bins hold, each at a position inside its bin's range (else the exact
+  // path)
+  bool bad = false;
+  if (has) {
+    const int bj = win_bin(in.Af, key_to_float(kj), in.wsc);
+    bad = bj < 0 || bj >= kWinBins || !((sm.binmask[bj >> 5] >> (bj & 31)) & 1u) || lane < (int)lc[bj] ||
+          lane >= (bj + 1 < kWinBins ? (int)lc[bj + 1] : (int)tot);
+  }
+  uint32_t flags = (__ballot(bad) || tot != (uint32_t)n) ? 1u : 0u;
+  // inclusive prefix of the exact masses exp(z - m) along the list
+  const double pj = wave_scan_f64(has ? exp_nonpos(sm.exp_tab, (double)key_to_float(kj) - in.m) : 0.0);
+  auto keyof = [&](int j) { return (uint32_t)__builtin_amdgcn_readlane((int)kj, j); };
+  auto fpos = [&](int b) { return b >= kWinBins ? n : (int)lc[b]; };
+  auto pre_at = [&](int j) { return __shfl(pj, j); };
+  auto qsum = [&](int a, int e) { return (e < a) ? 0.0 : pre_at(e) - (a > 0 ? pre_at(a - 1) : 0.0); };
+  auto cmass = [&](int b) { return b < 0 ? 0.0 : (double)lm[b < kWinBins ? b : kWinBins] / kWinScale; };
+  // the number of positions whose key is at least t (a prefix of the list)
+  auto count_ge = [&](uint32_t t) { return __popcll(__ballot(has && kj >= t)); };
+  const int fp_k = fpos(in.rklo), fp_p0 = fpos(in.r1lo), fp_p1 = fpos(in.r1hi + 1);
+  // top-k: the value of rank k, and the end of its tie group
+  uint32_t tk = 0;
+  int ek = n - 1;
+  if (!flags && in.topk_on) {
+    const int jk = in.full_k ? in.top_k - 1 : fp_k + (in.top_k - (int)c_rk) - 1;
+    if (jk < 0 || jk >= n) {
+      flags |= 1u;
+    } else {
+      tk = keyof(jk);
+      ek = count_ge(tk) - 1;
+    }
+  }
+  // top-p: the first tie-group end in the crossing range whose cumulative
+  // mass reaches p times the top-k set's mass
+  uint32_t t = tk;
+  if (!flags && in.topp) {
+    const double ctot = in.topk_on ? (in.full_k ? qsum(0, ek) : cmass(in.rklo - 1) + qsum(fp_k, ek)) : cmass(kWinBins);
+    const double target = (double)in.top_p * ctot;
+    const double base = in.full_k ? 0.0 : cmass(in.r1lo - 1) - (fp_p0 > 0 ? pre_at(fp_p0 - 1) : 0.0);
+    const uint32_t knext = (uint32_t)__shfl_down((int)kj, 1);
+    const bool end = lane == n - 1 || knext != kj;
+    const unsigned long long bal = __ballot(has && lane >= fp_p0 && lane < fp_p1 && end && base + pj >= target);
+    if (!bal) flags |= 1u;
+    else t = max(t, keyof(__ffsll((long long)bal) - 1));
+  }
+  if (in.minp) t = max(t, in.t_m);
+  // the kept set: positions [0, et); its sum and the top logprobs
+  const int bt = t ? win_bin(in.Af, key_to_float(t), in.wsc) : kWinBins;
+  const int et = t ? count_ge(t) : n;
+  const int fp_bt = fpos(bt);
+  double S_K = in.s_all;
+  if (!flags && in.truncated && in.want_S) {
+    if (in.full_k && bt <= in.rkhi) S_K = qsum(0, et - 1);
+    else if (bt < kWinBins) S_K = cmass(bt - 1) + qsum(fp_bt, et - 1);
+    else flags |= 1u;
+  }
+  const double lns = log(S_K);
+  if (!flags && in.K > 0 && in.gid == 0) {
+    const int kept_n = in.truncated ? et : n;
+    for (int q = lane; q < in.K; q += 64) {
+      const int64_t o = (int64_t)in.row * in.K + q;
+      if (q < kept_n) {
+        const unsigned long long sq_ = srt[q];
+        kp.top_lp_vals[o] = (float)(((double)key_to_float((uint32_t)(sq_ >> 32)) - in.m) - lns);
+        kp.top_lp_ids[o] = (int)(~(uint32_t)sq_);
+      } else {
+        kp.top_lp_vals[o] = -INFINITY;
+        kp.top_lp_ids[o] = -1;
+      }
+    }
+  }
+  return E3Out{(flags & 1u) != 0u, t, lns};
+}
 
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
@@ -812,6 +992,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
   rc.peers = kp.slots + (size_t)group * G;
   rc.xseq = &xseq;
   const bool want_out = kp.probs != nullptr || kp.logprobs != nullptr;
+  // output mode: none; both outputs with 16-byte stores; anything else,
+  // element by element
+  const int omode = !want_out ? 0 : (((kp.vec_ok & 2) && kp.probs && kp.logprobs) ? 1 : 2);
   const int K = kp.top_lp;
   const bool want_S = want_out || K > 0;
   const int s0 = gid * kp.slice;
@@ -1040,7 +1223,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       const bool finite_g = mg > -INFINITY && mg < INFINITY;
       const float Ag = finite_g ? abin(mg, wsc) : 0.0f;
       if (need_sel) {
+        // this slice's histogram, and the row's merged bins (exchange 2)
         wh[tid] = 0;
+        lc[tid] = 0;
+        lm[tid] = 0;
+        if (tid == 0) lm[kWinBins] = 0;
         __syncthreads();
       }
       double deep_a = 0.0;  // deeper masses, 2^-31 units
@@ -1102,6 +1289,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         atomic_st(&rc.my->x1[xp][2], (unsigned long long)__double_as_longlong(wdm));
         atomic_st(&rc.my->x1[xp][3], (unsigned long long)__double_as_longlong(wsx));
       }
+      const double lmp = minp ? log((double)P.min_p) : 0.0;  // min-p's guess, taken before the wait
       group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
       // ---- exchange 2, merged by every workgroup of the row alike: the
       // records and the first histogram pairs in one batch of 16-byte reads,
@@ -1161,7 +1349,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
       const float A = abin(mfx, wsc);
       Af = A;
-      if (minp) t_m = min_p_key(sm, m, P.min_p);
+      if (minp) t_m = min_p_key(sm, m, lmp, P.min_p);
       // per-workgroup mass scale exp(m_g - m) and bin shift A - A_g
       if (tid < G) {
         const float mgg = key_to_float((uint32_t)(sm.gk[tid] >> 32));
@@ -1179,10 +1367,6 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
       if (need_sel) {
         const int b = tid;
-        lc[b] = 0;
-        lm[b] = 0;
-        if (tid == 0) lm[kWinBins] = 0;
-        __syncthreads();
         double deep_x = 0.0;  // window bins of a slice that fall past the row's window
         // two bins per 16-byte pair; integer LDS adds of each slice's
         // rescaled, rounded masses: order-free
@@ -1226,8 +1410,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           for (int g = 0; g < G; ++g) dt += sm.gf[g];
           deep = (unsigned long long)__double2ll_rn(dt);
         }
-        const uint32_t runc = block_scan_incl<uint32_t>(cb, sm.red_c);
-        const unsigned long long runm = block_scan_incl<unsigned long long>(mb, sm.red_u);
+        uint32_t runc = cb;
+        unsigned long long runm = mb;
+        block_scan_incl2(runc, runm, sm.red_c, sm.red_u);
         lc[b] = runc;
         lm[b] = runm;
         if (b == kWinBins - 1) lm[kWinBins] = runm + deep;
@@ -1446,59 +1631,108 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       __syncthreads();
       const uint32_t my_n = sm.wo[kWaves];
       const unsigned xq = xseq++ & 1u;
-      if (my_n <= (uint32_t)kCandCap) {
-        for (int w = 0; w < kWaves; ++w) {
-          const int cw = (int)sm.red_c[w];
-          for (int j = tid; j < cw; j += kBlock) atomic_st(&rc.my->cand[xq][sm.wo[w] + j], stage[w * kStagePerWave + j]);
-        }
-      }
-      if (tid == 0) atomic_st(&rc.my->cand_n[xq][0], my_n);
-      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
-      // ---- exchange 3, in every workgroup alike: the counts and the first
-      // candidates of every slice in one batch of 16-byte reads (pairs of
-      // keys; a slot's array has room past an odd count), the rest only
-      // when a slice gathered more
-      {
-        const int pps = min(2 * kBlock / G, kCandCap / 2);  // pairs read at first per slice
-        const int g1 = tid < G ? tid : G - 1;
-        const int pa = tid, pb = tid + kBlock;
-        u32x4 rn, ra, rb;
-        coh_load16x3(&rc.peers[g1].cand_n[xq][0], &rc.peers[pa / pps].cand[xq][2 * (pa % pps)],
-                     &rc.peers[min(pb / pps, G - 1)].cand[xq][2 * (pb % pps)], rn, ra, rb);
-        if (tid < G) sm.gcnt[tid] = rn.x;
-        __syncthreads();
-        if (tid == 0) {
-          uint32_t acc = 0;
-          bool ovf = false;
-          for (int g = 0; g < G; ++g) {
-            const uint32_t c = sm.gcnt[g];
-            ovf |= c > (uint32_t)kCandCap;
-            const uint32_t cc = c > (uint32_t)kCandCap ? 0u : c;
-            sm.gcnt[g] = cc;
-            sm.goff[g] = acc;
-            acc += cc;
+      if (wave == 0) {
+        WgSlots *my = slot_at(kp, group * G + gid);
+        if (my_n <= (uint32_t)kCandCap) {
+          for (int w = 0; w < kWaves; ++w) {
+            const int cw = (int)sm.red_c[w];
+            for (int j = lane; j < cw; j += 64) atomic_st(&my->cand[xq][sm.wo[w] + j], stage[w * kStagePerWave + j]);
           }
-          ovf |= acc > (uint32_t)kCandCap;
-          sm.goff[G] = acc;
+        }
+        if (lane == 0) atomic_st(&my->cand_n[xq][0], my_n);
+      }
+      // the addresses wave 0 reads in exchange 3 (below), taken before the wait
+      constexpr int kPL = 5;
+      const int pps = min(64 * kPL / G, kCandCap / 2);  // pairs read at first per slice
+      WgSlots *peers = slot_at(kp, group * G);
+      const void *pp[kPL];
+#pragma unroll
+      for (int j = 0; j < kPL; ++j) {
+        const int pj = lane + 64 * j;
+        pp[j] = &peers[min(pj / pps, G - 1)].cand[xq][2 * (pj % pps)];
+      }
+      // only wave 0 wrote exchange data, so only it waits for its stores
+      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch, false);
+      // ---- exchange 3, in every workgroup alike: wave 0 reads the counts and
+      // the first candidates of every slice in one batch (pairs of keys; a
+      // slot's array has room past an odd count), places them in the list
+      // by the slices' offsets (a scan of the counts within the wave), and
+      // reads the rest only when a slice gathered more
+      if (wave == 0) {
+        const int g1 = lane < G ? lane : G - 1;
+        u32x4 rn, rp[kPL];
+        coh_load16x6(&peers[g1].cand_n[xq][0], pp[0], pp[1], pp[2], pp[3], pp[4], rn, rp[0], rp[1], rp[2], rp[3], rp[4]);
+        const bool bad = lane < G && rn.x > (uint32_t)kCandCap;
+        const uint32_t cc = (lane < G && !bad) ? rn.x : 0u;
+        const uint32_t incl = wave_scan(cc);
+        const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, G - 1);
+        const bool ovf = __ballot(bad) != 0ull || tot > (uint32_t)kCandCap;
+        if (lane < G) {
+          sm.gcnt[lane] = cc;
+          sm.goff[lane] = incl - cc;
+        }
+        if (lane == 0) {
+          sm.goff[G] = tot;
           sm.bu[12] = ovf ? 1u : 0u;
         }
-        __syncthreads();
-        if (sm.bu[12] == 0u) {
+        __builtin_amdgcn_wave_barrier();
+        bool fast = false;
+        if (!ovf) {
           auto put = [&](int g, int j, const u32x4 &r) {
             const int c = (int)sm.gcnt[g];
             if (j < c) sk[sm.goff[g] + j] = u64_of(r.x, r.y);
             if (j + 1 < c) sk[sm.goff[g] + j + 1] = u64_of(r.z, r.w);
           };
-          put(pa / pps, 2 * (pa % pps), ra);
-          if (pb / pps < G) put(pb / pps, 2 * (pb % pps), rb);
+#pragma unroll
+          for (int j = 0; j < kPL; ++j) {
+            const int pj = lane + 64 * j;
+            if (pj / pps < G) put(pj / pps, 2 * (pj % pps), rp[j]);
+          }
           // slices with more than 2 pps candidates: the rest
           for (int g = 0; g < G; ++g) {
             const int c = (int)sm.gcnt[g];
-            for (int j = 2 * pps + 2 * tid; j < c; j += 2 * kBlock) put(g, j, coh_load16(&rc.peers[g].cand[xq][j]));
+            for (int j = 2 * pps + 2 * lane; j < c; j += 128) put(g, j, coh_load16(&peers[g].cand[xq][j]));
+          }
+          fast = tot <= 64u;
+          if (fast) {
+            __builtin_amdgcn_wave_barrier();
+            E3In in;
+            in.top_k = P.top_k;
+            in.top_p = P.top_p;
+            in.m = m;
+            in.s_all = s_all;
+            in.Af = Af;
+            in.wsc = wsc;
+            in.t_m = t_m;
+            in.rklo = rklo;
+            in.rkhi = rkhi;
+            in.r1lo = r1lo;
+            in.r1hi = r1hi;
+            in.K = K;
+            in.row = row;
+            in.gid = gid;
+            in.full_k = full_k;
+            in.topk_on = topk_on;
+            in.topp = topp;
+            in.minp = minp;
+            in.truncated = truncated;
+            in.want_S = want_S;
+            const E3Out o = e3_wave(sm, (int)tot, sk, sq, lc, lm, in, kp);
+            if (lane == 0) {
+              sm.bu[26] = o.general ? 1u : 0u;
+              sm.bu[27] = o.tau;
+              sm.bd[5] = o.lnS;
+            }
           }
         }
+        if (lane == 0) sm.bu[13] = fast ? 1u : 0u;
       }
-      {
+      __syncthreads();
+      if (sm.bu[13] != 0u) {
+        general = sm.bu[26] != 0u;
+        tau = sm.bu[27];
+        lnS = sm.bd[5];
+      } else {
         bool ovf = sm.bu[12] != 0u;
         const int n = ovf ? 0 : (int)sm.goff[G];
         // sort by rank counting: a candidate's position is the number of
@@ -1860,7 +2094,6 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     using I2 = std::integral_constant<int, 2>;
     using BT = std::integral_constant<bool, true>;
     using BF = std::integral_constant<bool, false>;
-    const int omode = !want_out ? 0 : (((kp.vec_ok & 2) && kp.probs && kp.logprobs) ? 1 : 2);
     if (gumbel) {
       if (omode == 0) emit_loop(I0{}, BT{});
       else if (omode == 1) emit_loop(I1{}, BT{});

@@ -121,6 +121,22 @@ def test_edge_rows(sampler):
     assert g["token_ids"][3] == 17
 
 
+def test_exchange3_list_sizes(sampler):
+    """Top-k rows whose candidate lists span one value per lane, up to four
+    per lane (the single-wave form of the exact selection: boundaries at 64
+    and 256) and beyond (the workgroup form); half with top-p as well."""
+    V = 60_000
+    ks = np.array([30, 63, 64, 65, 129, 200, 255, 256, 257, 300, 600, 900], np.int32)
+    n = len(ks)
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal((n, V)) * 2.0).astype(np.float32)
+    x[1::3] = np.round(x[1::3] * 16.0) / 16.0  # tie groups
+    top_p = np.where(np.arange(n) % 2 == 0, 1.0, 0.97).astype(np.float32)
+    b = workloads.Batch("exchange-3 list sizes", "f32", x, temperature=np.full(n, 1.0, np.float32), top_k=ks,
+                        top_p=top_p, min_p=np.zeros(n, np.float32), want_probs=True, want_logprobs=True, top_logprobs=20)
+    check(b, sampler)
+
+
 def test_history_edges(sampler):
     b = workloads.random_small(30, 8, 777, "f32", penalties=True, history_len=40)
     b.history_ids[::7] = -5           # ids outside [0, V) are ignored
