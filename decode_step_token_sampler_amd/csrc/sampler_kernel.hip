@@ -288,7 +288,7 @@ DEV unsigned long long wg_sum_u(SmemBase &sm, unsigned long long v) {
   return r;
 }
 // Best (score desc, index asc) pair over the workgroup.
-DEV void wg_best(SmemBase &sm, double &g, int &idx) {
+DEV void wave_best(double &g, int &idx) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) {
     double g2 = __shfl_xor(g, o, 64);
@@ -298,6 +298,9 @@ DEV void wg_best(SmemBase &sm, double &g, int &idx) {
       idx = i2;
     }
   }
+}
+DEV void wg_best(SmemBase &sm, double &g, int &idx) {
+  wave_best(g, idx);
   if ((tidx() & 63) == 0) {
     sm.red_d[tidx() >> 6] = g;
     sm.red_i[tidx() >> 6] = idx;
@@ -940,6 +943,32 @@ DEV E3Out e3_wave(SmemBase &sm, const int n, const unsigned long long *sk, doubl
   return E3Out{(flags & 1u) != 0u, t, lns};
 }
 
+// The last workgroup of a row writes it: the row max and first argmax over
+// the slices' max keys (sm.gk; rows that skipped exchange 2 get their
+// status here) and, with Gumbel-max, the best of the slices' best scores
+// (sm.gd) and their indices (sm.gi), ties to the lower index.
+DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, bool gumbel) {
+  unsigned long long mk = 0;
+  for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
+  const float mx = key_to_float((uint32_t)(mk >> 32));
+  const int status = (mx > -INFINITY && mx < INFINITY) ? 0 : (mx == INFINITY ? 2 : 1);
+  int token = (int)(0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
+  if (gumbel) {
+    double bg = -INFINITY;
+    int bi = 0x7FFFFFFF;
+    for (int g = 0; g < G; ++g) {
+      if (sm.gd[g] > bg || (sm.gd[g] == bg && sm.gi[g] < bi)) {
+        bg = sm.gd[g];
+        bi = sm.gi[g];
+      }
+    }
+    if (bi != 0x7FFFFFFF) token = bi;
+  }
+  const bool aborted = atomic_ld(kp.abort_word) == kp.epoch;
+  kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
+  if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
+}
+
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
 __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
@@ -1026,6 +1055,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     // derived from it are recomputed per row)
     const int tid = tidx();
     const int lane = tid & 63, wave = tid >> 6;
+    if (tid == 0) sm.bu[37] = 0u;  // waves done with Gumbel-max (end of the row)
 
     // ---- 1. issue the history and logit loads; z = x / T into the LDS
     // slice as each batch lands.  Loads use clamped in-bounds addresses;
@@ -1944,7 +1974,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
     }
 
-    // ---- 5. emit probs / logprobs, Gumbel-max candidates
+    // ---- 5. Gumbel-max over the kept set, before any output store
     // Linear scores s_i = q_i / E_i with q_i = exp(z_i - m).  bound is a
     // lower bound of the best exact score (shared by the wave): an element
     // with w_i bound > q_i cannot reach it, because E_i >= w_i.  Groups of
@@ -1958,12 +1988,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
     float bound = 0.0f;
     // Groups of four that hold a Gumbel candidate (kept, and within
-    // kPruneNats of the max) are listed per wave in LDS while the outputs
-    // are written (16-bit group numbers; every group the wave visits fits),
-    // then finished on full waves: Philox and the filter.
-    constexpr uint32_t kRing = kMaxSlice / 4 / kWaves;  // groups one wave visits at most
-    static_assert(kWaves * kRing * sizeof(uint16_t) <= kRegionBBytes, "candidate lists fit the region");
-    uint16_t *ring = reinterpret_cast<uint16_t *>(regB) + wave * kRing;
+    // kPruneNats of the max) are listed per wave in LDS (16-bit group
+    // numbers; every group the wave visits fits), then finished on full
+    // waves: Philox and the filter.
+    uint16_t *ring = reinterpret_cast<uint16_t *>(regB);  // this wave's list (set by the pass)
     uint32_t qh = 0, qt = 0;  // wave-uniform head and tail
     auto gumbel_batch = [&](uint32_t cnt) __attribute__((always_inline)) {  // one queued group per lane, cnt <= 64
       bool improved = false;
@@ -1997,15 +2025,88 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         bound = fmaxf(bound, mb);
       }
     };
-    // The loop is specialised on the output mode (none; both outputs with
-    // 16-byte stores; anything else, element by element) and on Gumbel-max,
-    // with the per-row constants it uses held in vector registers.
-    const int iters = (ln4 + 4 * kBlock - 1) / (4 * kBlock);  // wave-uniform trip count
-    auto emit_loop = [&](auto MODE, auto GUMBEL) __attribute__((always_inline)) {
+    // Gumbel candidates of the slice, NT threads from thread 0 (a list per
+    // wave), then Philox on full waves of listed groups.
+    auto gumbel_pass = [&](auto NTC) __attribute__((always_inline)) {
+      constexpr int NT = decltype(NTC)::value;
+      constexpr uint32_t kRingW = kMaxSlice / 4 / (NT / 64);  // groups one wave visits at most
+      static_assert((NT / 64) * kRingW * sizeof(uint16_t) <= kRegionBBytes, "candidate lists fit the region");
+      ring = reinterpret_cast<uint16_t *>(regB) + wave * kRingW;
+      const int its = (ln4 + 4 * NT - 1) / (4 * NT);
+      for (int q0 = 0; q0 < its; q0 += 4) {
+        f32x4 zr[4];  // four groups, read first (clamped addresses)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * NT * (q0 + u), ln4 - 4));
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int l = 4 * tid + 4 * NT * (q0 + u);
+          const bool act = l < ln4;
+          bool any_cand = false;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) any_cand |= zr[u][c] >= tauf && (mf - zr[u][c] <= kPruneNats);  // padding: never
+          const unsigned long long bal = __ballot(act && any_cand);
+          if (bal) {
+            const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+            if (act && any_cand) ring[qt + off] = (uint16_t)(l >> 2);
+            qt += (uint32_t)__popcll(bal);
+          }
+        }
+      }
+      // the bound starts at the argmax's own score 1 / E (the argmax is
+      // always kept)
+      uint32_t w4[4];
+      philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
+      bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
+      for (; qh < qt;) gumbel_batch(min(qt - qh, 64u));
+    };
+
+    // ---- 6. final exchange: the last workgroup to arrive writes the row.
+    // One wave arrives before it issues any output store, so its wait for
+    // its own stores covers only the exchange data, and the exchange runs
+    // while the outputs are written.  Rows that merge top-logprob lists
+    // (general path) need every thread and exchange after the emit.
+    const unsigned fpar = it & 1u;
+    const bool late_fin = general && K > 0;
+    auto final_exchange = [&]() __attribute__((always_inline)) {  // one wave
+      if (lane == 0) {
+        atomic_st(&rc.my->fin[fpar][0], (unsigned long long)__double_as_longlong(best_g));
+        atomic_st(&rc.my->fin[fpar][1], (unsigned long long)(uint32_t)best_i);
+        atomic_st(&rc.my->fin[fpar][2], lkey);
+      }
+      order_release();
+      uint32_t last = 0;
+      if (lane == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&rc.gsync->fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        last = old == (uint32_t)G - 1u ? 1u : 0u;
+        if (last) {
+          __hip_atomic_store(&rc.gsync->fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          order_acquire();
+        }
+      }
+      if (__builtin_amdgcn_readfirstlane(last)) {
+        if (lane < G) {
+          u32x4 r0, r1;
+          coh_load16x2(&rc.peers[lane].fin[fpar][0], &rc.peers[lane].fin[fpar][2], r0, r1);
+          sm.gd[lane] = f64_of(r0.x, r0.y);
+          sm.gi[lane] = (int)r0.z;
+          sm.gk[lane] = u64_of(r1.x, r1.y);
+        }
+        __builtin_amdgcn_wave_barrier();
+        if (lane == 0) finish_row(sm, kp, row, G, gumbel);
+      }
+    };
+
+    // Outputs: the loop is specialised on the output mode (both outputs
+    // with 16-byte stores; anything else, element by element) and on the
+    // number of storing threads, with the per-row constants it uses held in
+    // vector registers.
+    auto emit_loop = [&](auto MODE, auto NTC) __attribute__((always_inline)) {
       constexpr int mode = decltype(MODE)::value;
-      constexpr bool gum = decltype(GUMBEL)::value;
+      constexpr int NT = decltype(NTC)::value;  // the last NT threads store
+      const int et = tid - (kBlock - NT);
+      const int its = (ln4 + 4 * NT - 1) / (4 * NT);
       double mv = m, lnsv = lnS;
-      float tv = tauf, mfv = mf;
+      float tv = tauf;
       int64_t ob = (int64_t)row * V + s0;  // output offset of the slice
       // the slice's output rows, as global pointers held in vector registers
       typedef __attribute__((address_space(1))) f32x4 gf32x4;
@@ -2014,26 +2115,25 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         pq = (gf32x4 *)(kp.probs + ob);
         lq = (gf32x4 *)(kp.logprobs + ob);
       }
-      asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(mfv), "+v"(ob), "+v"(pq), "+v"(lq));
-      for (int q0 = 0; q0 < iters; q0 += 4) {
+      asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(ob), "+v"(pq), "+v"(lq));
+      for (int q0 = 0; q0 < its; q0 += 4) {
         f32x4 zr[4];  // the chunk's four groups, read first (clamped addresses)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * kBlock * (q0 + u), ln4 - 4));
+        for (int u = 0; u < 4; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * et + 4 * NT * (q0 + u), ln4 - 4));
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const int l = 4 * tid + 4 * kBlock * (q0 + u);
+          const int l = 4 * et + 4 * NT * (q0 + u);
           const bool act = l < ln4;
           const f32x4 zv = zr[u];
           bool kk[4];
-          bool anyk = false, any_cand = false;
+          bool anyk = false;
 #pragma unroll
           for (int c = 0; c < 4; ++c) {
             kk[c] = zv[c] >= tv;  // padding (-inf) only passes when tau is 0
             anyk |= kk[c];
-            any_cand |= kk[c] && (mfv - zv[c] <= kPruneNats);
           }
           // a wave whose groups keep nothing stores 0 / -inf without the math
-          if (mode != 0 && act && !__ballot(act && anyk)) {
+          if (act && !__ballot(act && anyk)) {
             if (mode == 1 && l + 3 < ln) {
               __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pq + (l >> 2));
               __builtin_nontemporal_store(f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lq + (l >> 2));
@@ -2046,7 +2146,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
                 }
               }
             }
-          } else if (mode != 0 && act) {
+          } else if (act) {
             float lv[4], pv[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
@@ -2070,120 +2170,111 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
               }
             }
           }
-          if (gum) {
-            const unsigned long long bal = __ballot(act && any_cand);
-            if (bal) {
-              const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
-              if (act && any_cand) ring[qt + off] = (uint16_t)(l >> 2);
-              qt += (uint32_t)__popcll(bal);
-            }
-          }
         }
-      }
-      if (gum) {
-        // the bound starts at the argmax's own score 1 / E (the argmax is
-        // always kept)
-        uint32_t w4[4];
-        philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
-        bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
-        for (; qh < qt;) gumbel_batch(min(qt - qh, 64u));
       }
     };
-    using I0 = std::integral_constant<int, 0>;
+    using NT256 = std::integral_constant<int, 256>;
+    using NT512 = std::integral_constant<int, kBlock>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    using BT = std::integral_constant<bool, true>;
-    using BF = std::integral_constant<bool, false>;
-    if (gumbel) {
-      if (omode == 0) emit_loop(I0{}, BT{});
-      else if (omode == 1) emit_loop(I1{}, BT{});
-      else emit_loop(I2{}, BT{});
-    } else {
-      if (omode == 0) emit_loop(I0{}, BF{});
-      else if (omode == 1) emit_loop(I1{}, BF{});
-      else emit_loop(I2{}, BF{});
-    }
-    if (gumbel) wg_best(sm, best_g, best_i);
-
-    // ---- 6. final exchange: the last workgroup to arrive writes the row
-    const unsigned fpar = it & 1u;
-    if (tid == 0) {
-      atomic_st(&rc.my->fin[fpar][0], (unsigned long long)__double_as_longlong(best_g));
-      atomic_st(&rc.my->fin[fpar][1], (unsigned long long)(uint32_t)best_i);
-      atomic_st(&rc.my->fin[fpar][2], lkey);
-    }
-    if (general)
-      for (int t = tid; t < K; t += kBlock) atomic_st(&rc.my->toplist[fpar][t], sm.tl[t]);
-    order_release();
-    __syncthreads();
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&rc.gsync->fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      const bool last = old == (uint32_t)G - 1u;
-      if (last) {
-        __hip_atomic_store(&rc.gsync->fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        order_acquire();
-      }
-      sm.bu[15] = last ? 1u : 0u;
-    }
-    __syncthreads();
-    if (sm.bu[15]) {
-      if (tid < G) {
-        u32x4 r0, r1;
-        coh_load16x2(&rc.peers[tid].fin[fpar][0], &rc.peers[tid].fin[fpar][2], r0, r1);
-        sm.gd[tid] = f64_of(r0.x, r0.y);
-        sm.gi[tid] = (int)r0.z;
-        sm.gk[tid] = u64_of(r1.x, r1.y);
-      }
-      __syncthreads();
-      if (tid == 0) {
-        // the row max and first argmax over the slices' keys; rows that
-        // skipped exchange 2 get their status here
-        unsigned long long mk = 0;
-        for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
-        const float mx = key_to_float((uint32_t)(mk >> 32));
-        const int status = (mx > -INFINITY && mx < INFINITY) ? 0 : (mx == INFINITY ? 2 : 1);
-        int token = (int)(0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
+    if (omode != 0 && !late_fin) {
+      // Waves 4..7 write the outputs from the start; waves 0..3 run
+      // Gumbel-max over the whole slice meanwhile, and the last of them to
+      // finish (an LDS counter, cleared at the row start) merges the four
+      // bests and runs the final exchange.
+      static_assert(kBlock == 512, "four Gumbel waves and four storing waves");
+      if (wave < 4) {
         if (gumbel) {
-          double bg = -INFINITY;
-          int bi = 0x7FFFFFFF;
-          for (int g = 0; g < G; ++g) {
-            if (sm.gd[g] > bg || (sm.gd[g] == bg && sm.gi[g] < bi)) {
-              bg = sm.gd[g];
-              bi = sm.gi[g];
+          gumbel_pass(NT256{});
+          wave_best(best_g, best_i);
+        }
+        if (lane == 0) {
+          sm.red_d[wave] = best_g;
+          sm.red_i[wave] = best_i;
+        }
+        uint32_t old = 0;
+        if (lane == 0) old = __hip_atomic_fetch_add(&sm.bu[37], 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+        if (__builtin_amdgcn_readfirstlane(old) == 3u) {
+          best_g = sm.red_d[0];
+          best_i = sm.red_i[0];
+#pragma unroll
+          for (int w = 1; w < 4; ++w) {
+            if (sm.red_d[w] > best_g || (sm.red_d[w] == best_g && sm.red_i[w] < best_i)) {
+              best_g = sm.red_d[w];
+              best_i = sm.red_i[w];
             }
           }
-          if (bi != 0x7FFFFFFF) token = bi;
+          final_exchange();
         }
-        const bool aborted = atomic_ld(kp.abort_word) == kp.epoch;
-        kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
-        if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
+      } else if (omode == 1) {
+        emit_loop(I1{}, NT256{});
+      } else {
+        emit_loop(I2{}, NT256{});
       }
+    } else {
+      if (gumbel) {
+        gumbel_pass(NT512{});
+        wg_best(sm, best_g, best_i);
+      }
+      if (!late_fin && wave == 0) final_exchange();
+      if (omode == 1) emit_loop(I1{}, NT512{});
+      else if (omode == 2) emit_loop(I2{}, NT512{});
     }
-    if (general && K > 0 && sm.bu[15]) {
-      // merge the G local top-logprob lists (keys are distinct: each holds
-      // its index): an entry's rank among all entries is its output slot
-      unsigned long long *ent = reinterpret_cast<unsigned long long *>(region);
-      const int ne = G * K;
-      for (int e = tid; e < ne; e += kBlock) ent[e] = atomic_ld(&rc.peers[e / K].toplist[fpar][e % K]);
-      __syncthreads();
-      uint32_t nz = 0;
-      for (int e = tid; e < ne; e += kBlock) {
-        const unsigned long long key = ent[e];
-        if (key == 0) continue;
-        ++nz;
-        int r = 0;
-        for (int j = 0; j < ne; ++j) r += ent[j] > key ? 1 : 0;
-        if (r < K) {
-          const int64_t o = (int64_t)row * K + r;
-          const float zz = key_to_float((uint32_t)(key >> 32));
-          kp.top_lp_vals[o] = (float)(((double)zz - m) - lnS);
-          kp.top_lp_ids[o] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
-        }
+
+    if (late_fin) {
+      if (tid == 0) {
+        atomic_st(&rc.my->fin[fpar][0], (unsigned long long)__double_as_longlong(best_g));
+        atomic_st(&rc.my->fin[fpar][1], (unsigned long long)(uint32_t)best_i);
+        atomic_st(&rc.my->fin[fpar][2], lkey);
       }
-      const uint32_t nzt = (uint32_t)wg_sum_u(sm, nz);
-      for (int r = (int)nzt + tid; r < K; r += kBlock) {
-        kp.top_lp_vals[(int64_t)row * K + r] = -INFINITY;
-        kp.top_lp_ids[(int64_t)row * K + r] = -1;
+      for (int t = tid; t < K; t += kBlock) atomic_st(&rc.my->toplist[fpar][t], sm.tl[t]);
+      order_release();
+      __syncthreads();
+      if (tid == 0) {
+        const uint32_t old = __hip_atomic_fetch_add(&rc.gsync->fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const bool last = old == (uint32_t)G - 1u;
+        if (last) {
+          __hip_atomic_store(&rc.gsync->fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          order_acquire();
+        }
+        sm.bu[15] = last ? 1u : 0u;
+      }
+      __syncthreads();
+      if (sm.bu[15]) {
+        if (tid < G) {
+          u32x4 r0, r1;
+          coh_load16x2(&rc.peers[tid].fin[fpar][0], &rc.peers[tid].fin[fpar][2], r0, r1);
+          sm.gd[tid] = f64_of(r0.x, r0.y);
+          sm.gi[tid] = (int)r0.z;
+          sm.gk[tid] = u64_of(r1.x, r1.y);
+        }
+        __syncthreads();
+        if (tid == 0) finish_row(sm, kp, row, G, gumbel);
+        // merge the G local top-logprob lists (keys are distinct: each holds
+        // its index): an entry's rank among all entries is its output slot
+        unsigned long long *ent = reinterpret_cast<unsigned long long *>(region);
+        const int ne = G * K;
+        for (int e = tid; e < ne; e += kBlock) ent[e] = atomic_ld(&rc.peers[e / K].toplist[fpar][e % K]);
+        __syncthreads();
+        uint32_t nz = 0;
+        for (int e = tid; e < ne; e += kBlock) {
+          const unsigned long long key = ent[e];
+          if (key == 0) continue;
+          ++nz;
+          int r = 0;
+          for (int j = 0; j < ne; ++j) r += ent[j] > key ? 1 : 0;
+          if (r < K) {
+            const int64_t o = (int64_t)row * K + r;
+            const float zz = key_to_float((uint32_t)(key >> 32));
+            kp.top_lp_vals[o] = (float)(((double)zz - m) - lnS);
+            kp.top_lp_ids[o] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
+          }
+        }
+        const uint32_t nzt = (uint32_t)wg_sum_u(sm, nz);
+        for (int r = (int)nzt + tid; r < K; r += kBlock) {
+          kp.top_lp_vals[(int64_t)row * K + r] = -INFINITY;
+          kp.top_lp_ids[(int64_t)row * K + r] = -1;
+        }
       }
     }
     __syncthreads();
