@@ -2033,17 +2033,20 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       static_assert((NT / 64) * kRingW * sizeof(uint16_t) <= kRegionBBytes, "candidate lists fit the region");
       ring = reinterpret_cast<uint16_t *>(regB) + wave * kRingW;
       const int its = (ln4 + 4 * NT - 1) / (4 * NT);
-      for (int q0 = 0; q0 < its; q0 += 4) {
-        f32x4 zr[4];  // four groups, read first (clamped addresses)
+      constexpr int kStep = 8;  // groups read before any is tested
+      for (int q0 = 0; q0 < its; q0 += kStep) {
+        f32x4 zr[kStep];  // (clamped addresses)
 #pragma unroll
-        for (int u = 0; u < 4; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * NT * (q0 + u), ln4 - 4));
+        for (int u = 0; u < kStep; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * NT * (q0 + u), ln4 - 4));
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
+        for (int u = 0; u < kStep; ++u) {
           const int l = 4 * tid + 4 * NT * (q0 + u);
           const bool act = l < ln4;
-          bool any_cand = false;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) any_cand |= zr[u][c] >= tauf && (mf - zr[u][c] <= kPruneNats);  // padding: never
+          // both tests are monotone in z (float subtraction rounds
+          // monotonically), so a group holds a candidate exactly when its
+          // largest value passes them; padding (-inf) never does
+          const float zmax = fmaxf(fmaxf(zr[u][0], zr[u][1]), fmaxf(zr[u][2], zr[u][3]));
+          const bool any_cand = zmax >= tauf && (mf - zmax <= kPruneNats);
           const unsigned long long bal = __ballot(act && any_cand);
           if (bal) {
             const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
@@ -2125,13 +2128,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           const int l = 4 * et + 4 * NT * (q0 + u);
           const bool act = l < ln4;
           const f32x4 zv = zr[u];
-          bool kk[4];
-          bool anyk = false;
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            kk[c] = zv[c] >= tv;  // padding (-inf) only passes when tau is 0
-            anyk |= kk[c];
-          }
+          // padding (-inf) only passes when tau is 0
+          const bool anyk = fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])) >= tv;
           // a wave whose groups keep nothing stores 0 / -inf without the math
           if (act && !__ballot(act && anyk)) {
             if (mode == 1 && l + 3 < ln) {
@@ -2152,9 +2150,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             for (int c = 0; c < 4; ++c) {
               // logprob: one rounding of the fp64 value; prob = 2^(lp log2 e)
               // by the hardware exp2 (absolute error below 2e-7)
-              const float lp = kk[c] ? (float)(((double)zv[c] - mv) - lnsv) : -INFINITY;
+              const bool kk = zv[c] >= tv;
+              const float lp = kk ? (float)(((double)zv[c] - mv) - lnsv) : -INFINITY;
               lv[c] = lp;
-              pv[c] = kk[c] ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
+              pv[c] = kk ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
             }
             const int64_t o = ob + l;
             if (mode == 1 && l + 3 < ln) {
