@@ -1795,15 +1795,42 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             for (; j < n; ++j) r += sk[j] > c ? 1u : 0u;
             return r;
           };
-          if (wave * 64 < n) {
-            const unsigned long long c0 = tid < n ? sk[tid] : ~0ull;
-            const uint32_t r0 = rank_of(c0);
-            if (tid < n) srt[r0] = c0;
-          }
-          if (kBlock + wave * 64 < n) {
-            const unsigned long long c1 = tid + kBlock < n ? sk[tid + kBlock] : ~0ull;
-            const uint32_t r1 = rank_of(c1);
-            if (tid + kBlock < n) srt[r1] = c1;
+          // S adjacent lanes share a key when the list is short (S a power
+          // of two, S keys' worth of threads at most the workgroup): each
+          // counts over its own part of the list, and the parts add up
+          // within the wave
+          int S = 1;
+          while (S < 8 && 2 * S * ((n + 63) & ~63) <= kBlock) S *= 2;
+          if (S > 1) {
+            const int k = tid / S, p = tid & (S - 1);
+            const int j0 = (p * n) / S, j1 = ((p + 1) * n) / S;
+            uint32_t r = 0;
+            unsigned long long c = ~0ull;
+            if (k < n) {
+              c = sk[k];
+              int j = j0;
+              for (; j + 8 <= j1; j += 8) {  // eight keys read before any compare
+                unsigned long long kk[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) kk[u] = sk[j + u];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) r += kk[u] > c ? 1u : 0u;
+              }
+              for (; j < j1; ++j) r += sk[j] > c ? 1u : 0u;
+            }
+            for (int o = 1; o < S; o <<= 1) r += (uint32_t)__shfl_xor((int)r, o);
+            if (k < n && p == 0) srt[r] = c;
+          } else {
+            if (wave * 64 < n) {
+              const unsigned long long c0 = tid < n ? sk[tid] : ~0ull;
+              const uint32_t r0 = rank_of(c0);
+              if (tid < n) srt[r0] = c0;
+            }
+            if (kBlock + wave * 64 < n) {
+              const unsigned long long c1 = tid + kBlock < n ? sk[tid + kBlock] : ~0ull;
+              const uint32_t r1 = rank_of(c1);
+              if (tid + kBlock < n) srt[r1] = c1;
+            }
           }
           __syncthreads();
           // each gathered bin's first and last positions hold keys of that
@@ -2176,11 +2203,12 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     using NT512 = std::integral_constant<int, kBlock>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
-    if (omode != 0 && !late_fin) {
-      // Waves 4..7 write the outputs from the start; waves 0..3 run
-      // Gumbel-max over the whole slice meanwhile, and the last of them to
-      // finish (an LDS counter, cleared at the row start) merges the four
-      // bests and runs the final exchange.
+    if (omode != 0 && !late_fin && tau != 0) {
+      // A truncated row: waves 4..7 write the outputs from the start; waves
+      // 0..3 run Gumbel-max over the whole slice meanwhile (the kept set is
+      // small), and the last of them to finish (an LDS counter, cleared at
+      // the row start) merges the four bests and runs the final exchange.
+      // Rows that keep every value need all waves for Philox (below).
       static_assert(kBlock == 512, "four Gumbel waves and four storing waves");
       if (wave < 4) {
         if (gumbel) {
