@@ -799,14 +799,15 @@ DEV uint32_t min_p_key(SmemBase &sm, double m, double lmp, float min_p) {
   return (uint32_t)(k0 + first);
 }
 
-// Exchange 3 for at most 64 candidates, by one wave with one candidate per
-// lane and no workgroup barrier: the same list, checks and decisions as the
-// workgroup form in the kernel (sorted candidates, each gathered bin's
-// first position and a check of the list against the merged counts,
-// prefix masses, the end of the top-k tie group, the top-p crossing, the
-// kept-set sum and the top logprobs), with ballots in place of the
-// searches.  The sorted keys go to sq (sk holds the unsorted ones), and lc
-// becomes the bins' first positions.
+// Exchange 3 for at most 256 candidates: the waves have placed the sorted
+// keys in sq; one wave then decides (position p = lane + 64 s in slot s of
+// a lane) with no workgroup barrier: the same decisions as the workgroup
+// form in the kernel (each gathered bin's first position and a check of
+// the list against the merged counts, prefix masses, the end of the top-k
+// tie group, the top-p crossing, the kept-set sum and the top logprobs),
+// with wave scans and ballots in place of the searches.  lc becomes the
+// bins' first positions.
+constexpr int kE3Slots = 4;
 struct E3In {
   int top_k;
   float top_p;
@@ -821,25 +822,16 @@ struct E3Out {
   uint32_t tau;
   double lnS;
 };
-DEV E3Out e3_wave(SmemBase &sm, const int n, const unsigned long long *sk, double *sq, uint32_t *lc, const unsigned long long *lm,
-                  const E3In &in, const KernelParams &kp) {
+DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, const unsigned long long *lm, const E3In &in,
+                    const KernelParams &kp) {
   const int lane = tidx() & 63;
-  unsigned long long *srt = reinterpret_cast<unsigned long long *>(sq);
-  const bool has = lane < n;
-  // position = the number of larger keys (keys are distinct: each holds
-  // its index), eight keys read before any compare
-  {
-    const unsigned long long ck = has ? sk[lane] : 0ull;
-    uint32_t r = 0;
-    for (int j = 0; j < n; j += 8) {
-      unsigned long long kk[8];
+  const unsigned long long *srt = reinterpret_cast<const unsigned long long *>(sq);
+  bool has[kE3Slots];
+  uint32_t kj[kE3Slots];  // the key at each of the lane's positions
 #pragma unroll
-      for (int u = 0; u < 8; ++u) kk[u] = sk[min(j + u, n - 1)];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) r += (j + u < n && kk[u] > ck) ? 1u : 0u;
-    }
-    __builtin_amdgcn_wave_barrier();
-    if (has) srt[r] = ck;
+  for (int s = 0; s < kE3Slots; ++s) {
+    has[s] = lane + 64 * s < n;
+    kj[s] = has[s] ? (uint32_t)(srt[lane + 64 * s] >> 32) : 0u;
   }
   // values above the top-k bin (merged inclusive counts, read before lc
   // becomes positions)
@@ -867,27 +859,54 @@ DEV E3Out e3_wave(SmemBase &sm, const int n, const unsigned long long *sk, doubl
     }
   }
   __builtin_amdgcn_wave_barrier();
-  const unsigned long long sj = has ? srt[lane] : 0ull;  // the key at position lane
-  const uint32_t kj = (uint32_t)(sj >> 32);
   // the list against the merged counts: as many candidates as the gathered
   // bins hold, each at a position inside its bin's range (else the exact
   // path)
   bool bad = false;
-  if (has) {
-    const int bj = win_bin(in.Af, key_to_float(kj), in.wsc);
-    bad = bj < 0 || bj >= kWinBins || !((sm.binmask[bj >> 5] >> (bj & 31)) & 1u) || lane < (int)lc[bj] ||
-          lane >= (bj + 1 < kWinBins ? (int)lc[bj + 1] : (int)tot);
+#pragma unroll
+  for (int s = 0; s < kE3Slots; ++s) {
+    if (has[s]) {
+      const int p = lane + 64 * s;
+      const int bj = win_bin(in.Af, key_to_float(kj[s]), in.wsc);
+      bad |= bj < 0 || bj >= kWinBins || !((sm.binmask[bj >> 5] >> (bj & 31)) & 1u) || p < (int)lc[bj] ||
+             p >= (bj + 1 < kWinBins ? (int)lc[bj + 1] : (int)tot);
+    }
   }
   uint32_t flags = (__ballot(bad) || tot != (uint32_t)n) ? 1u : 0u;
-  // inclusive prefix of the exact masses exp(z - m) along the list
-  const double pj = wave_scan_f64(has ? exp_nonpos(sm.exp_tab, (double)key_to_float(kj) - in.m) : 0.0);
-  auto keyof = [&](int j) { return (uint32_t)__builtin_amdgcn_readlane((int)kj, j); };
+  // inclusive prefix of the exact masses exp(z - m) along the list, slot by
+  // slot
+  double pj[kE3Slots];
+  {
+    double carry = 0.0;
+#pragma unroll
+    for (int s = 0; s < kE3Slots; ++s) {
+      pj[s] = carry + wave_scan_f64(has[s] ? exp_nonpos(sm.exp_tab, (double)key_to_float(kj[s]) - in.m) : 0.0);
+      carry = __shfl(pj[s], 63);
+    }
+  }
+  // a position's key and prefix mass (j wave-uniform, 0 <= j < n)
+  auto keyof = [&](int j) {
+    const int s = j >> 6, l = j & 63;
+    const uint32_t v = s == 0 ? kj[0] : s == 1 ? kj[1] : s == 2 ? kj[2] : kj[3];
+    return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+  };
+  auto pre_at = [&](int j) {
+    const int s = j >> 6, l = j & 63;
+    const double v = s == 0 ? pj[0] : s == 1 ? pj[1] : s == 2 ? pj[2] : pj[3];
+    const unsigned long long u = (unsigned long long)__double_as_longlong(v);
+    return __longlong_as_double((long long)u64_of((uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l),
+                                                  (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l)));
+  };
   auto fpos = [&](int b) { return b >= kWinBins ? n : (int)lc[b]; };
-  auto pre_at = [&](int j) { return __shfl(pj, j); };
   auto qsum = [&](int a, int e) { return (e < a) ? 0.0 : pre_at(e) - (a > 0 ? pre_at(a - 1) : 0.0); };
   auto cmass = [&](int b) { return b < 0 ? 0.0 : (double)lm[b < kWinBins ? b : kWinBins] / kWinScale; };
   // the number of positions whose key is at least t (a prefix of the list)
-  auto count_ge = [&](uint32_t t) { return __popcll(__ballot(has && kj >= t)); };
+  auto count_ge = [&](uint32_t t) {
+    int c = 0;
+#pragma unroll
+    for (int s = 0; s < kE3Slots; ++s) c += __popcll(__ballot(has[s] && kj[s] >= t));
+    return c;
+  };
   const int fp_k = fpos(in.rklo), fp_p0 = fpos(in.r1lo), fp_p1 = fpos(in.r1hi + 1);
   // top-k: the value of rank k, and the end of its tie group
   uint32_t tk = 0;
@@ -908,11 +927,20 @@ DEV E3Out e3_wave(SmemBase &sm, const int n, const unsigned long long *sk, doubl
     const double ctot = in.topk_on ? (in.full_k ? qsum(0, ek) : cmass(in.rklo - 1) + qsum(fp_k, ek)) : cmass(kWinBins);
     const double target = (double)in.top_p * ctot;
     const double base = in.full_k ? 0.0 : cmass(in.r1lo - 1) - (fp_p0 > 0 ? pre_at(fp_p0 - 1) : 0.0);
-    const uint32_t knext = (uint32_t)__shfl_down((int)kj, 1);
-    const bool end = lane == n - 1 || knext != kj;
-    const unsigned long long bal = __ballot(has && lane >= fp_p0 && lane < fp_p1 && end && base + pj >= target);
-    if (!bal) flags |= 1u;
-    else t = max(t, keyof(__ffsll((long long)bal) - 1));
+    int e = -1;
+#pragma unroll
+    for (int s = 0; s < kE3Slots; ++s) {
+      // the key one position on: the next lane, or the next slot's lane 0
+      const uint32_t nx = s + 1 < kE3Slots ? (uint32_t)__builtin_amdgcn_readlane((int)kj[s + 1 < kE3Slots ? s + 1 : s], 0) : 0u;
+      const uint32_t dn = (uint32_t)__shfl_down((int)kj[s], 1);
+      const uint32_t knext = lane == 63 ? nx : dn;
+      const int p = lane + 64 * s;
+      const bool end = p == n - 1 || knext != kj[s];
+      const unsigned long long bal = __ballot(has[s] && p >= fp_p0 && p < fp_p1 && end && base + pj[s] >= target);
+      if (e < 0 && bal) e = 64 * s + __ffsll((long long)bal) - 1;
+    }
+    if (e < 0) flags |= 1u;
+    else t = max(t, keyof(e));
   }
   if (in.minp) t = max(t, in.t_m);
   // the kept set: positions [0, et); its sum and the top logprobs
@@ -1723,42 +1751,74 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             const int c = (int)sm.gcnt[g];
             for (int j = 2 * pps + 2 * lane; j < c; j += 128) put(g, j, coh_load16(&peers[g].cand[xq][j]));
           }
-          fast = tot <= 64u;
-          if (fast) {
-            __builtin_amdgcn_wave_barrier();
-            E3In in;
-            in.top_k = P.top_k;
-            in.top_p = P.top_p;
-            in.m = m;
-            in.s_all = s_all;
-            in.Af = Af;
-            in.wsc = wsc;
-            in.t_m = t_m;
-            in.rklo = rklo;
-            in.rkhi = rkhi;
-            in.r1lo = r1lo;
-            in.r1hi = r1hi;
-            in.K = K;
-            in.row = row;
-            in.gid = gid;
-            in.full_k = full_k;
-            in.topk_on = topk_on;
-            in.topp = topp;
-            in.minp = minp;
-            in.truncated = truncated;
-            in.want_S = want_S;
-            const E3Out o = e3_wave(sm, (int)tot, sk, sq, lc, lm, in, kp);
-            if (lane == 0) {
-              sm.bu[26] = o.general ? 1u : 0u;
-              sm.bu[27] = o.tau;
-              sm.bd[5] = o.lnS;
-            }
-          }
+          fast = tot <= (uint32_t)(64 * kE3Slots);
         }
         if (lane == 0) sm.bu[13] = fast ? 1u : 0u;
       }
       __syncthreads();
+      // rank of each key: the number of larger keys (keys are distinct:
+      // each holds its index), so the list is in (value desc, index asc)
+      // order, a total order.  On a short list S adjacent lanes share a key
+      // (S a power of two; at most the workgroup): each counts over its own
+      // part of the list, eight keys read before any compare, and the parts
+      // add up within the wave.
+      auto rank_place = [&](int n, unsigned long long *srt) __attribute__((always_inline)) {
+        int S = 1;
+        while (S < 8 && 2 * S * ((n + 63) & ~63) <= kBlock) S *= 2;
+        const int k = tid / S, p = tid & (S - 1);
+        const int j0 = (p * n) / S, j1 = ((p + 1) * n) / S;
+        uint32_t r = 0;
+        unsigned long long c = ~0ull;
+        if (k < n) {
+          c = sk[k];
+          int j = j0;
+          for (; j + 8 <= j1; j += 8) {
+            unsigned long long kk[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kk[u] = sk[j + u];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) r += kk[u] > c ? 1u : 0u;
+          }
+          for (; j < j1; ++j) r += sk[j] > c ? 1u : 0u;
+        }
+        for (int o = 1; o < S; o <<= 1) r += (uint32_t)__shfl_xor((int)r, o);
+        if (k < n && p == 0) srt[r] = c;
+      };
       if (sm.bu[13] != 0u) {
+        // a list of at most 256: sorted by every wave, decided by wave 0
+        const int n = (int)sm.goff[G];
+        rank_place(n, reinterpret_cast<unsigned long long *>(sq));
+        __syncthreads();
+        if (wave == 0) {
+          E3In in;
+          in.top_k = P.top_k;
+          in.top_p = P.top_p;
+          in.m = m;
+          in.s_all = s_all;
+          in.Af = Af;
+          in.wsc = wsc;
+          in.t_m = t_m;
+          in.rklo = rklo;
+          in.rkhi = rkhi;
+          in.r1lo = r1lo;
+          in.r1hi = r1hi;
+          in.K = K;
+          in.row = row;
+          in.gid = gid;
+          in.full_k = full_k;
+          in.topk_on = topk_on;
+          in.topp = topp;
+          in.minp = minp;
+          in.truncated = truncated;
+          in.want_S = want_S;
+          const E3Out o = e3_decide(sm, n, sq, lc, lm, in, kp);
+          if (lane == 0) {
+            sm.bu[26] = o.general ? 1u : 0u;
+            sm.bu[27] = o.tau;
+            sm.bd[5] = o.lnS;
+          }
+        }
+        __syncthreads();
         general = sm.bu[26] != 0u;
         tau = sm.bu[27];
         lnS = sm.bd[5];
@@ -1795,31 +1855,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
             for (; j < n; ++j) r += sk[j] > c ? 1u : 0u;
             return r;
           };
-          // S adjacent lanes share a key when the list is short (S a power
-          // of two, S keys' worth of threads at most the workgroup): each
-          // counts over its own part of the list, and the parts add up
-          // within the wave
-          int S = 1;
-          while (S < 8 && 2 * S * ((n + 63) & ~63) <= kBlock) S *= 2;
-          if (S > 1) {
-            const int k = tid / S, p = tid & (S - 1);
-            const int j0 = (p * n) / S, j1 = ((p + 1) * n) / S;
-            uint32_t r = 0;
-            unsigned long long c = ~0ull;
-            if (k < n) {
-              c = sk[k];
-              int j = j0;
-              for (; j + 8 <= j1; j += 8) {  // eight keys read before any compare
-                unsigned long long kk[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) kk[u] = sk[j + u];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) r += kk[u] > c ? 1u : 0u;
-              }
-              for (; j < j1; ++j) r += sk[j] > c ? 1u : 0u;
-            }
-            for (int o = 1; o < S; o <<= 1) r += (uint32_t)__shfl_xor((int)r, o);
-            if (k < n && p == 0) srt[r] = c;
+          if (n <= kBlock) {
+            rank_place(n, srt);
           } else {
             if (wave * 64 < n) {
               const unsigned long long c0 = tid < n ? sk[tid] : ~0ull;
