@@ -1704,10 +1704,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       const int pps = min(64 * kPL / G, kCandCap / 2);  // pairs read at first per slice
       WgSlots *peers = slot_at(kp, group * G);
       const void *pp[kPL];
+      int pg[kPL], po[kPL];  // each pair's slice (G: none) and key offset in it
 #pragma unroll
       for (int j = 0; j < kPL; ++j) {
         const int pj = lane + 64 * j;
-        pp[j] = &peers[min(pj / pps, G - 1)].cand[xq][2 * (pj % pps)];
+        pg[j] = min(pj / pps, G);
+        po[j] = 2 * (pj - pg[j] * pps);
+        pp[j] = &peers[min(pg[j], G - 1)].cand[xq][pg[j] < G ? po[j] : 0];
       }
       // only wave 0 wrote exchange data, so only it waits for its stores
       group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch, false);
@@ -1720,36 +1723,34 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
         const int g1 = lane < G ? lane : G - 1;
         u32x4 rn, rp[kPL];
         coh_load16x6(&peers[g1].cand_n[xq][0], pp[0], pp[1], pp[2], pp[3], pp[4], rn, rp[0], rp[1], rp[2], rp[3], rp[4]);
+        // slice g's count and offset sit in lane g
         const bool bad = lane < G && rn.x > (uint32_t)kCandCap;
         const uint32_t cc = (lane < G && !bad) ? rn.x : 0u;
         const uint32_t incl = wave_scan(cc);
         const uint32_t tot = (uint32_t)__builtin_amdgcn_readlane((int)incl, G - 1);
         const bool ovf = __ballot(bad) != 0ull || tot > (uint32_t)kCandCap;
-        if (lane < G) {
-          sm.gcnt[lane] = cc;
-          sm.goff[lane] = incl - cc;
-        }
+        const uint32_t goff = incl - cc;
         if (lane == 0) {
           sm.goff[G] = tot;
           sm.bu[12] = ovf ? 1u : 0u;
         }
-        __builtin_amdgcn_wave_barrier();
         bool fast = false;
         if (!ovf) {
-          auto put = [&](int g, int j, const u32x4 &r) {
-            const int c = (int)sm.gcnt[g];
-            if (j < c) sk[sm.goff[g] + j] = u64_of(r.x, r.y);
-            if (j + 1 < c) sk[sm.goff[g] + j + 1] = u64_of(r.z, r.w);
-          };
 #pragma unroll
           for (int j = 0; j < kPL; ++j) {
-            const int pj = lane + 64 * j;
-            if (pj / pps < G) put(pj / pps, 2 * (pj % pps), rp[j]);
+            const int g = min(pg[j], G - 1);
+            const int c = pg[j] < G ? __shfl((int)cc, g) : 0, o = __shfl((int)goff, g);
+            if (po[j] < c) sk[o + po[j]] = u64_of(rp[j].x, rp[j].y);
+            if (po[j] + 1 < c) sk[o + po[j] + 1] = u64_of(rp[j].z, rp[j].w);
           }
           // slices with more than 2 pps candidates: the rest
           for (int g = 0; g < G; ++g) {
-            const int c = (int)sm.gcnt[g];
-            for (int j = 2 * pps + 2 * lane; j < c; j += 128) put(g, j, coh_load16(&peers[g].cand[xq][j]));
+            const int c = __builtin_amdgcn_readlane((int)cc, g), o = __builtin_amdgcn_readlane((int)goff, g);
+            for (int j = 2 * pps + 2 * lane; j < c; j += 128) {
+              const u32x4 r = coh_load16(&peers[g].cand[xq][j]);
+              sk[o + j] = u64_of(r.x, r.y);
+              if (j + 1 < c) sk[o + j + 1] = u64_of(r.z, r.w);
+            }
           }
           fast = tot <= (uint32_t)(64 * kE3Slots);
         }
