@@ -1636,15 +1636,14 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       // that hold a candidate
       auto gather = [&](auto is_cand) __attribute__((always_inline)) {
         constexpr int kStep = 8;  // groups read before any is tested
-        f32x4 zr[kStep];
+        for (int q0 = 0; q0 < kBatch; q0 += kStep) {  // (a loop: the body's code is large)
+          f32x4 zr[kStep];
 #pragma unroll
-        for (int q = 0; q < kBatch; ++q) {
-          const int l = 4 * tid + 4 * kBlock * q;
-          if (q % kStep == 0) {
+          for (int u = 0; u < kStep; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(4 * tid + 4 * kBlock * (q0 + u), ln4 - 4));
 #pragma unroll
-            for (int u = 0; u < kStep; ++u) zr[u] = *reinterpret_cast<const f32x4 *>(zs + min(l + 4 * kBlock * u, ln4 - 4));
-          }
-          const f32x4 zv = zr[q % kStep];
+          for (int u = 0; u < kStep; ++u) {
+          const int l = 4 * tid + 4 * kBlock * (q0 + u);
+          const f32x4 zv = zr[u];
           const bool in_slice = l < ln4;  // (a clamped read repeats the last group)
           bool isc[4];
 #pragma unroll
@@ -1659,6 +1658,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
                 cnt += (uint32_t)__popcll(bal);
               }
             }
+          }
           }
         }
       };
