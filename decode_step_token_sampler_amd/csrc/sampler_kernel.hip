@@ -1101,6 +1101,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       }
     }
     constexpr int kBatch = kMaxSlice / (4 * kBlock);
+    static_assert(kBatch <= 32, "one bit per batch");
     float v[kBatch][4];
     const int64_t rbase = (int64_t)row * kp.row_stride + s0;
     const bool vec = kp.vec_ok & 1;
@@ -1113,6 +1114,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     // take the IEEE division.
     const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
     const uint32_t xhi_b = min(__float_as_uint(T * 0x1p99f), 0x7F7FFFFFu);
+    // Groups outside the Markstein range keep their raw values in the slice
+    // and a bit in slow_b; one loop after the transform divides them (the
+    // division's code then appears once, not once per unrolled batch).
+    uint32_t slow_b = 0;
     auto transform = [&](int b0, int b1) {  // batches [b0, b1) (constants after inlining)
 #pragma unroll
       for (int b = 0; b < kBatch; ++b) {
@@ -1124,19 +1129,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           const uint32_t amax = max(max(a[0], a[1]), max(a[2], a[3]));
           const uint32_t amin = min(min(a[0], a[1]), min(a[2], a[3]));
           f32x4 o;
-          if ((amax <= xhi_b) & (amin >= xlo_b)) {
+          const bool fast = (amax <= xhi_b) & (amin >= xlo_b);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float q = v[b][c] * rT;
-              o[c] = __builtin_fmaf(__builtin_fmaf(-q, T, v[b][c]), rT, q);
-            }
-          } else {
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const float x = v[b][c] == v[b][c] ? v[b][c] : -INFINITY;
-              o[c] = x / T + 0.0f;  // -0 -> +0: equal values share one key
-            }
+          for (int c = 0; c < 4; ++c) {
+            const float q = v[b][c] * rT;
+            o[c] = fast ? __builtin_fmaf(__builtin_fmaf(-q, T, v[b][c]), rT, q) : v[b][c];
           }
+          slow_b |= fast ? 0u : 1u << b;
           if (l + 4 > ln) {  // the slice's last group: slots past its end hold -inf
 #pragma unroll
             for (int c = 0; c < 4; ++c)
@@ -1144,6 +1143,23 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
           }
           *reinterpret_cast<f32x4 *>(zs + l) = o;
         }
+      }
+    };
+    // the groups outside the Markstein range (NaN, zeros, infinities,
+    // extreme values): IEEE division, NaN -> -inf, -0 -> +0 (equal values
+    // share one key); slots past the slice's end stay -inf
+    auto transform_slow = [&]() {
+      while (slow_b) {
+        const int b = __builtin_ctz(slow_b);
+        slow_b &= slow_b - 1u;
+        const int l = 4 * tid + 4 * kBlock * b;
+        f32x4 o = *reinterpret_cast<const f32x4 *>(zs + l);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float x = o[c] == o[c] ? o[c] : -INFINITY;
+          o[c] = l + c < ln ? x / T + 0.0f : -INFINITY;
+        }
+        *reinterpret_cast<f32x4 *>(zs + l) = o;
       }
     };
     // History counts live in an LDS hash (id -> count), built between the
@@ -1200,6 +1216,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       transform(0, kBatch / 2);
       build_hash();
       transform(kBatch / 2, kBatch);
+      transform_slow();
     } else {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
@@ -1210,6 +1227,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
       transform(0, kBatch / 2);
       build_hash();
       transform(kBatch / 2, kBatch);
+      transform_slow();
     }
     if (pen) {
       // the thread that created an id's entry penalises that value once,
