@@ -7,8 +7,8 @@ Gumbel-max / argmax.  Inputs are seeded synthetic Zipf-biased Gaussian
 logits (workloads.py); six buffer sets (593 MB) rotate so every step reads
 its logits from HBM rather than the 256 MB Infinity Cache.
 
-A step is one sampler_step call: the per-row record copy and the one
-cooperative kernel.  W warm-up steps, then K timed steps between two
+A step is one sampler_step call: one kernel launch, with the per-row
+records carried in its arguments.  W warm-up steps, then K timed steps between two
 device synchronisations.  The kernel's own duration is taken per launch
 with HIP events recorded by the library around the launch on its stream.
 

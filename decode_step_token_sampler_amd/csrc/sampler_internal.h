@@ -115,7 +115,7 @@ struct KernelParams {
   int64_t row_stride;
   int32_t n_rows;
   int32_t vocab;
-  const RowParam *rows;
+  const RowParam *rows;  // device records, or null: KernelArgs::rows
   const int32_t *history_ids;
   int32_t *token_ids;
   float *probs;
@@ -136,10 +136,19 @@ struct KernelParams {
   uint32_t epoch;        // launch counter of the handle (never 0)
 };
 
+// Batches of up to kArgRows rows carry their per-row records in the kernel
+// arguments (no copy ahead of the launch); larger ones are copied to a
+// device ring first and KernelParams::rows points there.
+constexpr int kArgRows = 96;
+struct KernelArgs {
+  KernelParams kp;
+  RowParam rows[kArgRows];  // used when kp.rows is null
+};
+
 // Launch one step.  The grid never exceeds the workgroups the device holds at
 // once; `cooperative` launches through hipLaunchCooperativeKernel, which
 // also has the runtime check that they are all resident.
-hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, bool cooperative, hipStream_t stream);
+hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream);
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);

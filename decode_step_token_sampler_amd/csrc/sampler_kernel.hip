@@ -999,7 +999,8 @@ DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, 
 
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
-__global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
+__global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
+  const KernelParams &kp = ka.kp;
   extern __shared__ __align__(16) unsigned char lds_raw[];
   SmemBase &sm = *reinterpret_cast<SmemBase *>(lds_raw);
   static_assert(sizeof(SmemBase) % 16 == 0, "the LDS slice must be 16-byte aligned");
@@ -1064,15 +1065,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
 
   unsigned it = 0;
   for (int row = group; row < kp.n_rows; row += kp.n_groups, ++it) {
-    const RowParam P = kp.rows[row];
     rc.row = row;
-    const bool greedy = P.flags & RF_GREEDY;
-    const bool top1 = P.flags & RF_TOP1;
-    const bool pen = PEN && (P.flags & RF_PEN);
-    const bool topk = !greedy && (P.flags & RF_TOPK);
-    const bool topp = !greedy && (P.flags & RF_TOPP);
-    const bool minp = !greedy && (P.flags & RF_MINP);
-    const bool truncated = topk || topp || minp;
     // the slice bounds, opaque per row: keeps per-element offsets and
     // compares from being hoisted out of the row loop (they would stay
     // live across it)
@@ -1084,6 +1077,15 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
     const int tid = tidx();
     const int lane = tid & 63, wave = tid >> 6;
     if (tid == 0) sm.bu[37] = 0u;  // waves done with Gumbel-max (end of the row)
+
+    const RowParam P = kp.rows ? kp.rows[row] : ka.rows[row];
+    const bool greedy = P.flags & RF_GREEDY;
+    const bool top1 = P.flags & RF_TOP1;
+    const bool pen = PEN && (P.flags & RF_PEN);
+    const bool topk = !greedy && (P.flags & RF_TOPK);
+    const bool topp = !greedy && (P.flags & RF_TOPP);
+    const bool minp = !greedy && (P.flags & RF_MINP);
+    const bool truncated = topk || topp || minp;
 
     // ---- 1. issue the history and logit loads; z = x / T into the LDS
     // slice as each batch lands.  Loads use clamped in-bounds addresses;
@@ -2365,15 +2367,16 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelParams kp) {
 }
 
 template <typename TIn, bool PEN>
-hipError_t launch_t(const KernelParams &kp, bool cooperative, hipStream_t stream) {
+hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream) {
+  const KernelParams &kp = ka.kp;
   const size_t lds = kernel_lds_bytes(kp.slice, kp.hash_slots, PEN);
   const dim3 grid(kp.n_groups * kp.G), block(kBlock);
   if (cooperative) {
-    void *args[] = {const_cast<KernelParams *>(&kp)};
+    void *args[] = {const_cast<KernelArgs *>(&ka)};
     return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&row_kernel<TIn, PEN>), grid, block, args,
                                       (unsigned)lds, stream);
   }
-  hipLaunchKernelGGL((row_kernel<TIn, PEN>), grid, block, (unsigned)lds, stream, kp);
+  hipLaunchKernelGGL((row_kernel<TIn, PEN>), grid, block, (unsigned)lds, stream, ka);
   return hipGetLastError();
 }
 
@@ -2404,10 +2407,10 @@ size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties) {
   return kernel_lds_fixed() + sizeof(float) * (size_t)slice + kernel_lds_region(slice, hash_slots, penalties);
 }
 
-hipError_t launch_step(const KernelParams &kp, int dtype, bool penalties, bool cooperative, hipStream_t stream) {
+hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream) {
   if (dtype == 0)
-    return penalties ? launch_t<float, true>(kp, cooperative, stream) : launch_t<float, false>(kp, cooperative, stream);
-  return penalties ? launch_t<uint16_t, true>(kp, cooperative, stream) : launch_t<uint16_t, false>(kp, cooperative, stream);
+    return penalties ? launch_t<float, true>(ka, cooperative, stream) : launch_t<float, false>(ka, cooperative, stream);
+  return penalties ? launch_t<uint16_t, true>(ka, cooperative, stream) : launch_t<uint16_t, false>(ka, cooperative, stream);
 }
 
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out) {

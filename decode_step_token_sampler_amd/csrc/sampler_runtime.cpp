@@ -1,8 +1,10 @@
 // sampler_runtime.cpp -- host side of the decode-step sampler's C ABI.
 //
-// Validation, per-row normalisation, the batch predicate, the pinned
-// staging ring that carries the per-row records to the device in one copy,
-// launch planning (workgroups per row) and the cooperative launch.
+// Validation, per-row normalisation, the batch predicate, the per-row
+// records (in the kernel arguments for batches of up to kArgRows rows, so a
+// step is one launch and no copy; otherwise through a pinned staging ring
+// and one copy), launch planning (workgroups per row) and the cooperative
+// launch.
 //
 // Sources (page titles; sections named where used):
 //   [A] "SGLang's +75% sampler speedup skips Qwen3 chat requests"
@@ -54,6 +56,7 @@ struct sampler_handle {
   int hash_slots = 0; // LDS hash slots for history counts
   RowParam *host_ring = nullptr;   // pinned, kRing slots of max_rows records
   RowParam *dev_ring = nullptr;    // device, kRing slots
+  KernelArgs *args = nullptr;      // host: the launch's argument block
   hipEvent_t slot_done[kRing] = {};
   bool slot_used[kRing] = {};
   int next_slot = 0;
@@ -245,6 +248,7 @@ void free_handle(sampler_handle *h) {
     }
   if (h->host_ring) (void)hipHostFree(h->host_ring);
   if (h->dev_ring) (void)hipFree(h->dev_ring);
+  delete h->args;
   if (h->sync) (void)hipFree(h->sync);
   if (h->slots) (void)hipFree(h->slots);
   if (h->abort_word) (void)hipFree(h->abort_word);
@@ -334,6 +338,12 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     const size_t ring_bytes = sizeof(RowParam) * (size_t)cfg->max_rows * kRing;
     if ((e = hipHostMalloc((void **)&h->host_ring, ring_bytes, hipHostMallocDefault)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&h->dev_ring, ring_bytes)) != hipSuccess) goto fail;
+    h->args = new (std::nothrow) KernelArgs();
+    if (!h->args) {
+      g_create_error = "out of host memory";
+      free_handle(h);
+      return SAMPLER_EHIP;
+    }
     const size_t n_groups_max = (size_t)h->resident;  // one group per resident workgroup at most
     if ((e = hipMalloc((void **)&h->sync, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
     if ((e = hipMemset(h->sync, 0, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
@@ -391,15 +401,22 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   if (a->path_out) *a->path_out = path;
   if (h->cfg.flags & SAMPLER_FORCE_FILTERED) path = PATH_FILTERED;
 
-  // ---- staging slot (waits only when the ring wraps onto a busy slot)
-  const int slot = h->next_slot;
-  h->next_slot = (slot + 1) % kRing;
-  if (h->slot_used[slot]) {
-    hipError_t e = hipEventSynchronize(h->slot_done[slot]);
-    if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
+  // ---- per-row records: in the kernel arguments, or in a staging slot
+  // (waits only when the ring wraps onto a slot whose copy is in flight)
+  const bool inline_rows = n <= kArgRows;
+  KernelArgs &ka = *h->args;
+  int slot = -1;
+  RowParam *rp = ka.rows, *dp = nullptr;
+  if (!inline_rows) {
+    slot = h->next_slot;
+    h->next_slot = (slot + 1) % kRing;
+    if (h->slot_used[slot]) {
+      hipError_t e = hipEventSynchronize(h->slot_done[slot]);
+      if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
+    }
+    rp = h->host_ring + (size_t)slot * h->cfg.max_rows;
+    dp = h->dev_ring + (size_t)slot * h->cfg.max_rows;
   }
-  RowParam *rp = h->host_ring + (size_t)slot * h->cfg.max_rows;
-  RowParam *dp = h->dev_ring + (size_t)slot * h->cfg.max_rows;
   bool any_pen = false;
   for (int r = 0; r < n; ++r) {
     RowParam &p = rp[r];
@@ -436,11 +453,14 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
     p.stream = a->row_stream ? a->row_stream[r] : (det ? 0u : (uint32_t)r);
     p.offset = a->row_offset ? a->row_offset[r] : a->offset;
   }
-  hipError_t e = hipMemcpyAsync(dp, rp, sizeof(RowParam) * (size_t)n, hipMemcpyHostToDevice, stream);
-  if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
-  e = hipEventRecord(h->slot_done[slot], stream);
-  if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  h->slot_used[slot] = true;
+  hipError_t e;
+  if (!inline_rows) {
+    e = hipMemcpyAsync(dp, rp, sizeof(RowParam) * (size_t)n, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+    e = hipEventRecord(h->slot_done[slot], stream);
+    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    h->slot_used[slot] = true;
+  }
 
   // ---- launch plan: G workgroups per row, rows strided over groups
   const int g_min = (V + h->slice_cap - 1) / h->slice_cap;
@@ -463,7 +483,8 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   int slice = (V + G - 1) / G;
   slice = (slice + 3) & ~3;
   G = (V + slice - 1) / slice;  // every workgroup gets a non-empty slice
-  KernelParams kp{};
+  KernelParams &kp = ka.kp;
+  kp = KernelParams{};
   kp.logits = a->logits;
   kp.row_stride = a->row_stride;
   kp.n_rows = n;
@@ -494,7 +515,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.epoch = h->epoch;
   const bool prof = h->prof_n < h->prof_cap;
   if (prof && (e = hipEventRecord(h->prof[2 * h->prof_n], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  e = launch_step(kp, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream);
+  e = launch_step(ka, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream);
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
   if (prof) {
     if ((e = hipEventRecord(h->prof[2 * h->prof_n + 1], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");

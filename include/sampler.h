@@ -175,7 +175,8 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out);
  * a negative status without launching if one is wrong.  Allocates nothing,
  * never synchronises the device and never reads device memory back; waits on
  * the host only when the 4-slot staging ring wraps onto a slot whose copy is
- * still in flight.  Outputs are valid when the stream reaches this point. */
+ * still in flight (batches of up to 96 rows pass their per-row records in
+ * the kernel arguments and use no staging slot).  Outputs are valid when the stream reaches this point. */
 sampler_status sampler_step(sampler_handle *h, const sampler_step_args *args, void *stream);
 
 /* The batch predicate alone ([A] "One request with top_p takes the whole
