@@ -83,7 +83,22 @@ class _Args(ctypes.Structure):
         ("diag_gumbel_gap", ctypes.c_void_p),
         ("diag_topp_margin", ctypes.c_void_p),
         ("diag_kept", ctypes.c_void_p),
+        ("vocab_mask", ctypes.c_void_p),
+        ("mask_stride", ctypes.c_int64),
+        ("bias_ids", ctypes.c_void_p),
+        ("bias_vals", ctypes.c_void_p),
+        ("bias_start", ctypes.c_void_p),
+        ("bias_len", ctypes.c_void_p),
+        ("stop_ids", ctypes.c_void_p),
+        ("stop_start", ctypes.c_void_p),
+        ("stop_len", ctypes.c_void_p),
+        ("min_tokens", ctypes.c_void_p),
+        ("output_len", ctypes.c_void_p),
+        ("logprob_mode", ctypes.c_int32),
     ]
+
+
+LOGPROB_MODES = {"processed": 0, "temperature": 1, "raw": 2}
 
 
 def lib():
@@ -181,12 +196,17 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
          repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
          history_ids=None, history_start=None, history_len=None,
          seed=0, offset=0, row_seed=None, row_offset=None, row_stream=None, deterministic=False,
-         want_probs=True, want_logprobs=True, top_logprobs=0, n_threads=1):
+         want_probs=True, want_logprobs=True, top_logprobs=0, n_threads=1,
+         vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None,
+         stop_ids=None, stop_start=None, stop_len=None, min_tokens=None, output_len=None,
+         logprob_mode="processed"):
     """Run the oracle on host arrays.
 
     ``logits`` is a 2-D array: float32, or uint16 holding bf16 bits when
     ``dtype == "bf16"``; its row stride is its second dimension unless
-    ``vocab`` is smaller.  Returns a dict of numpy outputs and diagnostics.
+    ``vocab`` is smaller.  ``vocab_mask`` is a 2-D uint32 array of allowed
+    bits (bit i & 31 of word i >> 5; its row stride is its second
+    dimension).  Returns a dict of numpy outputs and diagnostics.
     """
     if dtype not in ("f32", "bf16"):
         raise ValueError("dtype must be 'f32' or 'bf16'")
@@ -208,6 +228,16 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
     RS = _arr(row_seed, np.uint64, n)
     RO = _arr(row_offset, np.uint64, n)
     RST = _arr(row_stream, np.uint32, n)
+    M = None if vocab_mask is None else np.ascontiguousarray(vocab_mask, dtype=np.uint32)
+    if M is not None and (M.ndim != 2 or M.shape[0] != n or M.shape[1] < (V + 31) // 32):
+        raise ValueError("vocab_mask must be [n_rows, >= ceil(vocab / 32)] uint32")
+    BI, BV = _arr(bias_ids, np.int32), _arr(bias_vals, np.float32)
+    BS, BL = _arr(bias_start, np.int64, n), _arr(bias_len, np.int32, n)
+    SI = _arr(stop_ids, np.int32)
+    SS, SL = _arr(stop_start, np.int64, n), _arr(stop_len, np.int32, n)
+    MT, OL = _arr(min_tokens, np.int32, n), _arr(output_len, np.int32, n)
+    if logprob_mode not in LOGPROB_MODES:
+        raise ValueError("logprob_mode must be one of %s" % sorted(LOGPROB_MODES))
     out = {
         "token_ids": np.full(n, -7, dtype=np.int32),
         "probs": np.zeros((n, V), dtype=np.float32) if want_probs else None,
@@ -243,6 +273,18 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
     a.diag_gumbel_gap = out["gumbel_gap"].ctypes.data
     a.diag_topp_margin = out["topp_margin"].ctypes.data
     a.diag_kept = out["kept"].ctypes.data
+    a.vocab_mask = _ptr(M)
+    a.mask_stride = 0 if M is None else M.shape[1]
+    a.bias_ids, a.bias_vals, a.bias_start, a.bias_len = _ptr(BI), _ptr(BV), _ptr(BS), _ptr(BL)
+    a.stop_ids, a.stop_start, a.stop_len = _ptr(SI), _ptr(SS), _ptr(SL)
+    a.min_tokens, a.output_len = _ptr(MT), _ptr(OL)
+    a.logprob_mode = LOGPROB_MODES[logprob_mode]
+    for ids, st, ln, what in ((BI, BS, BL, "bias"), (SI, SS, SL, "stop")):
+        if ids is not None and st is not None and ln is not None:
+            if np.any(st < 0) or np.any(st + ln > ids.shape[0]):
+                raise ValueError(f"{what} span outside the id buffer")
+    if BI is not None and BV is not None and BV.shape != BI.shape:
+        raise ValueError("bias_vals must match bias_ids")
     if HS is not None and H is not None and HL is not None:
         if np.any(HS < 0) or np.any(HS + HL > H.shape[0]):
             raise ValueError("history span outside the id buffer")

@@ -31,6 +31,12 @@
  *     (i>>2, stream, off_lo, off_hi), key (seed_lo, seed_hi), word i&3.
  *   - top-k logprobs list the K largest kept values by (z desc, index asc);
  *     entries with z = -inf are never listed; padding is (-inf, -1).
+ *   - logits processors run first, in this order: grammar bitmask (cleared
+ *     bit -> -inf), logit_bias (a token's entries summed, then added once;
+ *     NaN -> -inf), min_tokens (stop ids -> -inf while fewer than min_tokens
+ *     tokens were produced); then penalties and temperature.
+ *   - logprob modes: processed (after truncation, the default), temperature
+ *     (untruncated log_softmax(z)), raw (untruncated, before temperature).
  *
  * Parity pins: see tests/test_oracle_*.py.  The penalty formula itself is
  * not fixed by the pages ("parity unpinned" for that formula; only its
@@ -97,6 +103,19 @@ typedef struct {
   double *diag_gumbel_gap;  /* (s1 - s2) / s1 of the Gumbel scores */
   double *diag_topp_margin; /* relative distance of the top-p crossing */
   int32_t *diag_kept;       /* |K| */
+  /* logits processors, applied before the penalties (NULL = none) */
+  const uint32_t *vocab_mask; /* [n_rows, mask_stride] words; bit i&31 of word i>>5: 1 = allowed */
+  int64_t mask_stride;        /* words */
+  const int32_t *bias_ids;    /* host copy of the bias id buffer */
+  const float *bias_vals;     /* same length */
+  const int64_t *bias_start;  /* per row */
+  const int32_t *bias_len;    /* per row */
+  const int32_t *stop_ids;    /* host copy of the stop id buffer */
+  const int64_t *stop_start;  /* per row */
+  const int32_t *stop_len;    /* per row */
+  const int32_t *min_tokens;  /* per row */
+  const int32_t *output_len;  /* per row: tokens generated so far */
+  int32_t logprob_mode;       /* 0 processed, 1 temperature-scaled, 2 raw */
 } orc_args;
 
 /* ------------------------------------------------------------------ */
@@ -232,7 +251,7 @@ static void orc_kadd(orc_ksum *k, double v) {
 }
 static double orc_kval(const orc_ksum *k) { return k->s + k->c; }
 
-static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double *q, int32_t *cnt,
+static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *ord, double *q, int32_t *cnt,
                     unsigned char *kept) {
   const int32_t V = a->vocab;
   float T = a->temperature ? a->temperature[r] : 1.0f;
@@ -257,6 +276,47 @@ static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double 
     z[i] = x;
   }
 
+  /* 1b. logits processors, before the sampler's own steps.
+   *    Grammar mask ([B] "Constrained decoding", step 4 "Mask": the grammar
+   *    fills a vocabulary bitmask that is applied to the logits before
+   *    sampling): a cleared bit makes the logit -inf.
+   *    logit_bias (listed among the sampler options in [B] "On Apple
+   *    silicon"): every entry of the row's list adds its value to its
+   *    token's logit; entries of one token are summed first (in list
+   *    order), then added once.  A NaN result becomes -inf.
+   *    min_tokens ([C] "解码一步里采样做什么", step _apply_min_tokens_penalty):
+   *    while the row has produced fewer than min_tokens tokens, each of
+   *    its stop ids is made -inf.  Ids outside [0, V) are ignored. */
+  if (a->vocab_mask) {
+    const uint32_t *mw = a->vocab_mask + (int64_t)r * a->mask_stride;
+    for (int32_t i = 0; i < V; ++i)
+      if (((mw[i >> 5] >> (i & 31)) & 1u) == 0u) z[i] = -INFINITY;
+  }
+  if (a->bias_len && a->bias_len[r] > 0 && a->bias_ids && a->bias_vals && a->bias_start) {
+    const int32_t *bi = a->bias_ids + a->bias_start[r];
+    const float *bv = a->bias_vals + a->bias_start[r];
+    const int32_t nb = a->bias_len[r];
+    for (int32_t j = 0; j < nb; ++j) {
+      const int32_t id = bi[j];
+      if (id < 0 || id >= V) continue;
+      int first = 1;
+      for (int32_t j2 = 0; j2 < j; ++j2)
+        if (bi[j2] == id) first = 0;
+      if (!first) continue; /* this token's total was added at its first entry */
+      float total = bv[j];
+      for (int32_t j2 = j + 1; j2 < nb; ++j2)
+        if (bi[j2] == id) total = total + bv[j2];
+      float x = z[id] + total;
+      z[id] = isnan(x) ? -INFINITY : x;
+    }
+  }
+  if (a->min_tokens && a->output_len && a->output_len[r] < a->min_tokens[r] && a->stop_ids && a->stop_start &&
+      a->stop_len) {
+    const int32_t *st = a->stop_ids + a->stop_start[r];
+    for (int32_t j = 0; j < a->stop_len[r]; ++j)
+      if (st[j] >= 0 && st[j] < V) z[st[j]] = -INFINITY;
+  }
+
   /* 2. penalties ([C] "解码一步里采样做什么", step _apply_penalties):
    *    counts of each token in the row's history, then the three penalties
    *    on the tokens that occur.  Ids outside [0, V) are ignored. */
@@ -278,6 +338,9 @@ static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double 
       }
     }
   }
+
+  /* the processed logits before temperature, for the raw logprob mode */
+  if (a->logprob_mode == 2) memcpy(xp, z, sizeof(float) * (size_t)V);
 
   /* 3. temperature ([C] same section: logits.div_(temperatures)) */
   for (int32_t i = 0; i < V; ++i) z[i] = z[i] / T_eff;
@@ -379,10 +442,33 @@ static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double 
     }
   const double S = orc_kval(&ks);
   const double lnS = log(S);
+  /* Returned logprobs ([B] "Logprobs are temperature-scaled"): mode 0 (the
+   * default) reports the distribution sampled from, after truncation; mode
+   * 1 the untruncated log_softmax(logits / temperature); mode 2 the
+   * untruncated log_softmax of the processed logits without temperature
+   * (the page's original-logprob switch).  Greedy rows are untruncated at
+   * temperature 1, so the three modes agree on them. */
+  double lp_m = dm, lp_lnS = lnS;
+  if (a->logprob_mode == 1) {
+    orc_ksum ka = {0.0, 0.0};
+    for (int32_t i = 0; i < V; ++i) orc_kadd(&ka, q[i]);
+    lp_lnS = log(orc_kval(&ka));
+  } else if (a->logprob_mode == 2) {
+    float mr = -INFINITY;
+    for (int32_t i = 0; i < V; ++i)
+      if (xp[i] > mr) mr = xp[i];
+    lp_m = (double)mr;
+    orc_ksum ka = {0.0, 0.0};
+    for (int32_t i = 0; i < V; ++i) orc_kadd(&ka, exp((double)xp[i] - lp_m));
+    lp_lnS = log(orc_kval(&ka));
+  }
+  const float *lp_x = a->logprob_mode == 2 ? xp : z;
+  const int lp_all = a->logprob_mode != 0;
   for (int32_t i = 0; i < V; ++i) {
     if (a->probs) a->probs[(int64_t)r * V + i] = kept[i] ? (float)(q[i] / S) : 0.0f;
     if (a->logprobs)
-      a->logprobs[(int64_t)r * V + i] = kept[i] ? (float)(((double)z[i] - dm) - lnS) : -INFINITY;
+      a->logprobs[(int64_t)r * V + i] =
+          (kept[i] || lp_all) ? (float)(((double)lp_x[i] - lp_m) - lp_lnS) : -INFINITY;
   }
 
   /* 7. token selection.  Rows with top_k = 1 (greedy rows included) take
@@ -427,7 +513,9 @@ static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double 
   }
   a->token_ids[r] = token;
 
-  /* 8. top logprobs: the largest kept values by (z desc, index asc) */
+  /* 8. top logprobs: the largest listed values by (z desc, index asc),
+   *    with the logprob mode's values; mode 0 lists kept tokens only,
+   *    modes 1 and 2 every token with a finite value. */
   if (want_topk_out) {
     const int32_t K = a->top_logprobs;
     int32_t nfill = 0;
@@ -437,13 +525,13 @@ static void orc_row(const orc_args *a, int32_t r, float *z, orc_zi *ord, double 
     for (; nfill < K; ++nfill) {
       int32_t best = -1;
       for (int32_t i = 0; i < V; ++i) {
-        if (!kept[i] || z[i] == -INFINITY) continue;
+        if ((!kept[i] && !lp_all) || z[i] == -INFINITY) continue;
         /* strictly after (last_z, last_i) in the (z desc, idx asc) order */
         if (z[i] > last_z || (z[i] == last_z && i <= last_i)) continue;
         if (best < 0 || z[i] > z[best]) best = i; /* index ascending keeps the first */
       }
       if (best < 0) break;
-      a->top_logprob_vals[(int64_t)r * K + nfill] = (float)(((double)z[best] - dm) - lnS);
+      a->top_logprob_vals[(int64_t)r * K + nfill] = (float)(((double)lp_x[best] - lp_m) - lp_lnS);
       a->top_logprob_ids[(int64_t)r * K + nfill] = best;
       last_z = z[best];
       last_i = best;
@@ -470,17 +558,19 @@ static void *orc_worker(void *p) {
   orc_job *job = (orc_job *)p;
   const int32_t V = job->a->vocab;
   float *z = (float *)malloc(sizeof(float) * (size_t)V);
+  float *xp = (float *)malloc(sizeof(float) * (size_t)V);
   orc_zi *ord = (orc_zi *)malloc(sizeof(orc_zi) * (size_t)V);
   double *q = (double *)malloc(sizeof(double) * (size_t)V);
   int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)V);
   unsigned char *kept = (unsigned char *)malloc((size_t)V);
-  if (!z || !ord || !q || !cnt || !kept) {
+  if (!z || !xp || !ord || !q || !cnt || !kept) {
     job->status = -2;
   } else {
-    for (int32_t r = job->r0; r < job->r1; ++r) orc_row(job->a, r, z, ord, q, cnt, kept);
+    for (int32_t r = job->r0; r < job->r1; ++r) orc_row(job->a, r, z, xp, ord, q, cnt, kept);
     job->status = 0;
   }
   free(z);
+  free(xp);
   free(ord);
   free(q);
   free(cnt);
@@ -490,7 +580,8 @@ static void *orc_worker(void *p) {
 
 /* Runs every row; returns 0, -1 for invalid sizes, -2 for allocation failure. */
 int orc_step(const orc_args *a) {
-  if (!a || a->n_rows <= 0 || a->vocab <= 0 || a->row_stride < a->vocab || !a->logits || !a->token_ids)
+  if (!a || a->n_rows <= 0 || a->vocab <= 0 || a->row_stride < a->vocab || !a->logits || !a->token_ids ||
+      a->logprob_mode < 0 || a->logprob_mode > 2 || (a->vocab_mask && a->mask_stride < (a->vocab + 31) / 32))
     return -1;
   int nt = a->n_threads > 0 ? a->n_threads : 1;
   if (nt > a->n_rows) nt = a->n_rows;

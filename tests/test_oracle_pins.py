@@ -382,3 +382,132 @@ def test_top_logprobs_match_sort():
         np.testing.assert_array_equal(np.sort(got[:n]), np.sort(order[:n]))
         np.testing.assert_array_equal(o["top_logprob_vals"][r, :n], lp[got[:n]])
         assert np.all(got[n:] == -1) and np.all(np.isneginf(o["top_logprob_vals"][r, n:]))
+
+
+# ---------------------------------------------------------------- logits processors
+def test_grammar_mask_matches_scipy_on_allowed_set():
+    # [B] "Constrained decoding": the bitmask removes tokens before sampling;
+    # the kept distribution is the softmax over the allowed tokens only.
+    rng = np.random.default_rng(21)
+    n, V = 5, 203
+    x = (3 * rng.standard_normal((n, V))).astype(np.float32)
+    T = np.array([1.0, 0.7, 1.3, 1.0, 0.5], np.float32)
+    allowed = rng.random((n, V)) < 0.3
+    allowed[3] = False
+    allowed[3, [7, 150]] = True                       # two tokens left
+    words = np.zeros((n, (V + 31) // 32 + 1), np.uint32)   # one spare word of stride
+    for r in range(n):
+        for i in np.flatnonzero(allowed[r]):
+            words[r, i >> 5] |= np.uint32(1 << (i & 31))
+    o = run(x, temperature=T, vocab_mask=words)
+    z = np.where(allowed, (x / T[:, None]).astype(np.float32), -np.inf).astype(np.float64)
+    np.testing.assert_allclose(o["probs"], scipy.special.softmax(z, axis=1), rtol=0, atol=1e-7)
+    lp = scipy.special.log_softmax(z, axis=1)
+    assert np.array_equal(np.isneginf(o["logprobs"]), np.isneginf(lp))
+    fin = np.isfinite(lp)
+    np.testing.assert_allclose(o["logprobs"][fin], lp[fin], rtol=2e-7, atol=1e-6)
+    assert np.all(allowed[np.arange(n), o["token_ids"]])
+    # greedy over the allowed set is numpy's first argmax there
+    g = run(x, temperature=np.zeros(n, np.float32), vocab_mask=words)
+    np.testing.assert_array_equal(g["token_ids"], np.argmax(np.where(allowed, x, -np.inf), axis=1))
+    # nothing allowed: no finite logit
+    e = run(x[:1], vocab_mask=np.zeros((1, 7), np.uint32))
+    assert e["row_status"][0] == 1 and e["token_ids"][0] == -1
+
+
+def test_logit_bias_matches_numpy_float32_sums():
+    # logit_bias ([B] sampler options): each token's entries are summed, then
+    # added to its logit in fp32, before the temperature division.
+    rng = np.random.default_rng(22)
+    n, V = 3, 150
+    x = (2 * rng.standard_normal((n, V))).astype(np.float32)
+    T = np.array([0.8, 1.0, 1.7], np.float32)
+    ids = np.array([5, 9, 5, 149, 0, 3, 3, 70, -1, 150], np.int32)   # -1 and 150 are ignored
+    vals = np.array([1.5, -2.25, 0.375, 4.0, -100.0, 0.1, 0.2, 7.0, 9.0, 9.0], np.float32)
+    start = np.array([0, 4, 0], np.int64)
+    length = np.array([4, 6, 0], np.int32)
+    o = run(x, temperature=T, bias_ids=ids, bias_vals=vals, bias_start=start, bias_len=length)
+    xb = x.copy()
+    for r in range(n):
+        tot = {}
+        for j in range(start[r], start[r] + length[r]):
+            i = int(ids[j])
+            if 0 <= i < V:
+                tot[i] = vals[j] if i not in tot else np.float32(tot[i] + vals[j])
+        for i, b in tot.items():
+            xb[r, i] = np.float32(xb[r, i] + b)
+    z = (xb / T[:, None]).astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(o["probs"], scipy.special.softmax(z, axis=1), rtol=0, atol=1e-7)
+    np.testing.assert_allclose(o["logprobs"], scipy.special.log_softmax(z, axis=1), rtol=2e-7, atol=1e-6)
+    # the probability ratio of a biased token to an unbiased one moves by exp(b / T)
+    r, i, j = 0, 149, 1
+    ratio = (o["probs"][r, i] / o["probs"][r, j]) / math.exp((float(x[r, i]) - float(x[r, j])) / float(T[r]))
+    assert ratio == pytest.approx(math.exp(4.0 / 0.8), rel=1e-5)
+    # a +inf bias makes +inf (status 2); a NaN sum becomes -inf
+    s = run(x[:1], bias_ids=np.array([3], np.int32), bias_vals=np.array([np.inf], np.float32),
+            bias_start=[0], bias_len=[1])
+    assert s["row_status"][0] == 2
+    q = run(np.array([[-np.inf, 0.0, 1.0]], np.float32), bias_ids=np.array([0], np.int32),
+            bias_vals=np.array([np.inf], np.float32), bias_start=[0], bias_len=[1])
+    assert q["row_status"][0] == 0 and q["probs"][0, 0] == 0.0
+
+
+def test_min_tokens_masks_stop_ids_only_while_active():
+    # [C] step _apply_min_tokens_penalty: stop ids are -inf until the row has
+    # produced min_tokens tokens.
+    rng = np.random.default_rng(23)
+    n, V = 4, 64
+    x = (2 * rng.standard_normal((n, V))).astype(np.float32)
+    x[:, 11] = 10.0                                   # a stop token that would dominate
+    stops = np.array([11, 40, 11, 63], np.int32)
+    kw = dict(stop_ids=stops, stop_start=[0, 0, 2, 0], stop_len=[2, 2, 2, 0],
+              min_tokens=[5, 5, 1, 9], output_len=[0, 5, 0, 0])
+    base = run(x)
+    active = [True, False, True, False]               # row 3 has no stop ids
+    for seed in range(40):
+        o = run(x, seed=seed, **kw)
+        b = run(x, seed=seed)
+        for r in range(n):
+            if active[r]:
+                assert o["token_ids"][r] not in (11, 40, 63)
+                assert o["probs"][r, 11] == 0.0
+            else:
+                assert o["token_ids"][r] == b["token_ids"][r]
+    o = run(x, **kw)
+    z = x.astype(np.float64).copy()
+    z[0, [11, 40]] = -np.inf
+    np.testing.assert_allclose(o["probs"][0], scipy.special.softmax(z[0]), rtol=0, atol=1e-7)
+    np.testing.assert_array_equal(o["probs"][1], base["probs"][1])
+
+
+# ---------------------------------------------------------------- logprob modes
+def test_logprob_modes_match_scipy():
+    # [B] "Logprobs are temperature-scaled": the temperature mode is the
+    # untruncated log_softmax(logits / T); the raw mode log_softmax(logits).
+    rng = np.random.default_rng(24)
+    n, V = 6, 300
+    x = (3 * rng.standard_normal((n, V))).astype(np.float32)
+    T = np.array([0.5, 1.0, 1.4, 0.0, 0.9, 2.0], np.float32)     # row 3 greedy
+    kw = dict(temperature=T, top_k=[5, -1, 40, -1, -1, 3], top_p=[1.0, 0.8, 0.9, 1.0, 1.0, 1.0],
+              min_p=[0.0, 0.0, 0.0, 0.0, 0.1, 0.0], top_logprobs=4)
+    proc = run(x, **kw)
+    tmp = run(x, logprob_mode="temperature", **kw)
+    raw = run(x, logprob_mode="raw", **kw)
+    Te = np.where(T < 1e-6, 1.0, T).astype(np.float32)
+    z = (x / Te[:, None]).astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(tmp["logprobs"], scipy.special.log_softmax(z, axis=1), rtol=2e-7, atol=1e-6)
+    np.testing.assert_allclose(raw["logprobs"], scipy.special.log_softmax(x.astype(np.float64), axis=1),
+                               rtol=2e-7, atol=1e-6)
+    # tokens and probs do not depend on the mode; greedy rows agree in all modes
+    for o in (tmp, raw):
+        np.testing.assert_array_equal(o["token_ids"], proc["token_ids"])
+        np.testing.assert_array_equal(o["probs"], proc["probs"])
+    np.testing.assert_array_equal(tmp["logprobs"][3], proc["logprobs"][3])
+    np.testing.assert_array_equal(raw["logprobs"][3], proc["logprobs"][3])
+    # top logprobs list the largest values over every token (numpy sort)
+    for o in (tmp, raw):
+        for r in range(n):
+            lp = o["logprobs"][r].astype(np.float64)
+            order = np.lexsort((np.arange(V), -z[r]))[:4]
+            np.testing.assert_array_equal(o["top_logprob_ids"][r], order)
+            np.testing.assert_array_equal(o["top_logprob_vals"][r], lp[order].astype(np.float32))
