@@ -50,6 +50,7 @@ class Config(ctypes.Structure):
         ("max_top_logprobs", ctypes.c_int32),
         ("device", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
+        ("max_bias_per_row", ctypes.c_int32),
     ]
 
 
@@ -83,6 +84,17 @@ class StepArgs(ctypes.Structure):
         ("top_logprob_ids", ctypes.c_void_p),
         ("row_status", ctypes.c_void_p),
         ("path_out", ctypes.c_void_p),
+        ("vocab_mask", ctypes.c_void_p),
+        ("mask_stride", ctypes.c_int64),
+        ("bias_ids", ctypes.c_void_p),
+        ("bias_vals", ctypes.c_void_p),
+        ("bias_start", ctypes.c_void_p),
+        ("bias_len", ctypes.c_void_p),
+        ("stop_ids", ctypes.c_void_p),
+        ("stop_start", ctypes.c_void_p),
+        ("stop_len", ctypes.c_void_p),
+        ("min_tokens", ctypes.c_void_p),
+        ("output_len", ctypes.c_void_p),
     ]
 
 
@@ -142,7 +154,9 @@ class _Marshalled:
 
     def __init__(self, n_rows, vocab, temperature=None, top_p=None, top_k=None, min_p=None,
                  repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
-                 history_start=None, history_len=None, row_seed=None, row_offset=None, row_stream=None):
+                 history_start=None, history_len=None, row_seed=None, row_offset=None, row_stream=None,
+                 bias_start=None, bias_len=None, stop_start=None, stop_len=None, min_tokens=None,
+                 output_len=None):
         n = int(n_rows)
         self.keep = dict(
             temperature=_host(temperature, np.float32, n), top_p=_host(top_p, np.float32, n),
@@ -151,7 +165,10 @@ class _Marshalled:
             frequency_penalty=_host(frequency_penalty, np.float32, n), top_k=_host(top_k, np.int32, n),
             history_start=_host(history_start, np.int64, n), history_len=_host(history_len, np.int32, n),
             row_seed=_host(row_seed, np.uint64, n), row_offset=_host(row_offset, np.uint64, n),
-            row_stream=_host(row_stream, np.uint32, n))
+            row_stream=_host(row_stream, np.uint32, n),
+            bias_start=_host(bias_start, np.int64, n), bias_len=_host(bias_len, np.int32, n),
+            stop_start=_host(stop_start, np.int64, n), stop_len=_host(stop_len, np.int32, n),
+            min_tokens=_host(min_tokens, np.int32, n), output_len=_host(output_len, np.int32, n))
         a = StepArgs()
         a.n_rows = n
         a.vocab = int(vocab)
@@ -186,11 +203,11 @@ class Sampler:
 
     def __init__(self, max_rows: int, max_vocab: int, *, max_history_per_row: int = 4096,
                  max_top_logprobs: int = 32, device: int = 0, deterministic: bool = False,
-                 force_filtered: bool = False, cooperative_launch: bool = False):
+                 force_filtered: bool = False, cooperative_launch: bool = False, max_bias_per_row: int = 0):
         L = load_library()
         self._L = L
         cfg = Config(max_rows=max_rows, max_vocab=max_vocab, max_history_per_row=max_history_per_row,
-                     max_top_logprobs=max_top_logprobs, device=device,
+                     max_top_logprobs=max_top_logprobs, device=device, max_bias_per_row=max_bias_per_row,
                      flags=(FLAG_DETERMINISTIC if deterministic else 0) | (FLAG_FORCE_FILTERED if force_filtered else 0)
                            | (FLAG_COOPERATIVE_LAUNCH if cooperative_launch else 0))
         self.config = cfg
@@ -239,12 +256,16 @@ class Sampler:
              repetition_penalty=None, presence_penalty=None, frequency_penalty=None, history_ids=None,
              history_start=None, history_len=None, seed: int = 0, offset: int = 0, row_seed=None,
              row_offset=None, row_stream=None, want_probs: bool = False, want_logprobs: bool = False,
-             top_logprobs: int = 0, want_status: bool = True, out: Optional[dict] = None, stream=None) -> dict:
+             top_logprobs: int = 0, want_status: bool = True, out: Optional[dict] = None, stream=None,
+             vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None, stop_ids=None,
+             stop_start=None, stop_len=None, min_tokens=None, output_len=None) -> dict:
         """Enqueue one decode step on the current torch stream; returns the output tensors.
 
         ``logits``: a CUDA tensor [N, row_stride] of float32 or bfloat16 with unit
         column stride.  Per-row parameters: host sequences / numpy arrays.
-        ``history_ids``: a CUDA int32 tensor.  Outputs are allocated with torch
+        ``history_ids``, ``bias_ids``, ``bias_vals``, ``stop_ids``: CUDA tensors
+        (int32 / float32); ``vocab_mask``: a CUDA int32 or uint32-bits tensor
+        [N, words] with unit column stride.  Outputs are allocated with torch
         on the logits' device unless ``out`` supplies them.
         """
         import torch
@@ -274,12 +295,22 @@ class Sampler:
         m = _Marshalled(n, V, temperature=temperature, top_p=top_p, top_k=top_k, min_p=min_p,
                         repetition_penalty=repetition_penalty, presence_penalty=presence_penalty,
                         frequency_penalty=frequency_penalty, history_start=history_start,
-                        history_len=history_len, row_seed=row_seed, row_offset=row_offset, row_stream=row_stream)
+                        history_len=history_len, row_seed=row_seed, row_offset=row_offset, row_stream=row_stream,
+                        bias_start=bias_start, bias_len=bias_len, stop_start=stop_start, stop_len=stop_len,
+                        min_tokens=min_tokens, output_len=output_len)
         a = m.args
         a.logits = logits.data_ptr()
         a.dtype = dt
         a.row_stride = logits.stride(0)
         a.history_ids = None if history_ids is None else history_ids.data_ptr()
+        a.bias_ids = None if bias_ids is None else bias_ids.data_ptr()
+        a.bias_vals = None if bias_vals is None else bias_vals.data_ptr()
+        a.stop_ids = None if stop_ids is None else stop_ids.data_ptr()
+        if vocab_mask is not None:
+            if vocab_mask.dim() != 2 or vocab_mask.stride(1) != 1 or vocab_mask.element_size() != 4:
+                raise ValueError("vocab_mask must be a 2-D 32-bit tensor with unit column stride")
+            a.vocab_mask = vocab_mask.data_ptr()
+            a.mask_stride = vocab_mask.stride(0)
         a.seed = int(seed) & (2**64 - 1)
         a.offset = int(offset) & (2**64 - 1)
         a.token_ids = o["token_ids"].data_ptr()

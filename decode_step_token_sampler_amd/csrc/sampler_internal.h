@@ -20,6 +20,10 @@ constexpr int kMaxTopLogprobs = 32;
 // (15 bits) and a count (13 bits) into one word.
 constexpr int kMaxHistPerRow = 4096;
 constexpr int kMaxHashSlots = 8192;
+// Largest list of logit_bias plus active stop entries of one row: one per
+// thread.  They live in a second LDS hash of next_pow2(2 * max) 8-byte
+// slots (slice-local index, summed bias).
+constexpr int kMaxBiasPerRow = 512;
 // Largest vocabulary (masses are summed as 2^-44 fixed point in 64 bits).
 constexpr int32_t kMaxVocab = 1 << 20;
 
@@ -51,9 +55,10 @@ enum : uint32_t {
   RF_TOPK = 1u << 3,    // 1 <= top_k < vocab (set for non-greedy top_k == 1 rows too)
   RF_TOPP = 1u << 4,    // top_p < 1
   RF_MINP = 1u << 5,    // min_p > 0
+  RF_SPEC = 1u << 6,    // the row has logit_bias entries or active stop ids
 };
 
-// One row's parameters as the kernel reads them (64 bytes).
+// One row's parameters as the kernel reads them (96 bytes).
 struct alignas(16) RowParam {
   float temperature;  // effective temperature (1 for greedy rows)
   float top_p;
@@ -68,8 +73,13 @@ struct alignas(16) RowParam {
   int64_t hist_start;
   int32_t hist_len;
   uint32_t stream;
+  int64_t bias_start;  // logit_bias span (RF_SPEC)
+  int64_t stop_start;  // stop-id span, counted only while min_tokens is active
+  int32_t bias_len;
+  int32_t stop_len;    // 0 when min_tokens is not active
+  uint32_t pad[2];
 };
-static_assert(sizeof(RowParam) == 64, "RowParam layout");
+static_assert(sizeof(RowParam) == 96, "RowParam layout");
 
 // Barrier words of one row group, each on its own 128-byte line: the
 // barrier word (generation << 8 | arrival count) and the final-exchange
@@ -134,12 +144,19 @@ struct KernelParams {
   WgSlots *slots;     // [n_groups * G]
   uint32_t *abort_word;  // equals epoch once a barrier wait of this launch expired
   uint32_t epoch;        // launch counter of the handle (never 0)
+  // logits processors
+  const uint32_t *vocab_mask;  // [n_rows, mask_stride] allowed bits, or null
+  int64_t mask_stride;         // words
+  const int32_t *bias_ids;
+  const float *bias_vals;
+  const int32_t *stop_ids;
+  int32_t bias_slots;          // LDS bias-hash slots (power of two), 0 without bias
 };
 
 // Batches of up to kArgRows rows carry their per-row records in the kernel
 // arguments (no copy ahead of the launch); larger ones are copied to a
 // device ring first and KernelParams::rows points there.
-constexpr int kArgRows = 96;
+constexpr int kArgRows = 72;
 struct KernelArgs {
   KernelParams kp;
   RowParam rows[kArgRows];  // used when kp.rows is null
@@ -154,11 +171,11 @@ hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool coo
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);
 // Fixed LDS bytes of one workgroup.
 size_t kernel_lds_fixed();
-// LDS bytes of the shared region (penalty hash + bitmap; merged prefix
+// LDS bytes of the shared region (history hash and bias hash; merged prefix
 // arrays with the local histogram, candidate staging or sorting after them;
 // general-path histograms: used one at a time).
-size_t kernel_lds_region(int slice, int hash_slots, bool penalties);
-// Dynamic LDS bytes of one workgroup for a slice and hash size.
-size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties);
+size_t kernel_lds_region(int slice, int hash_slots, int bias_slots, bool penalties);
+// Dynamic LDS bytes of one workgroup for a slice and hash sizes.
+size_t kernel_lds_bytes(int slice, int hash_slots, int bias_slots, bool penalties);
 
 }  // namespace dsts

@@ -417,6 +417,12 @@ DEV float apply_penalty(float x, uint32_t cnt, const RowParam &P) {
   return t2 - P.pres;
 }
 
+// A token's summed logit_bias added to its (sanitised) logit; NaN -> -inf.
+DEV float add_bias(float x, float b) {
+  const float y = x + b;
+  return y == y ? y : -INFINITY;
+}
+
 // z = x / T, correctly rounded: q = x (1/T), then one FMA correction with
 // the exact remainder (Markstein), valid while |q| lies in [2^-100, 2^100];
 // elsewhere (and for infinities and zeros) the IEEE division.  -0 -> +0, so
@@ -719,6 +725,31 @@ DEV uint32_t radix_select(SmemBase &sm, RowCtx &rc, const float *zs, unsigned ch
 // Packed hash entry: slice-local index << 13 | count.
 DEV uint32_t hash_slot(uint32_t local, uint32_t slots) { return (local * 2654435761u) & (slots - 1u); }
 
+// The summed bias of slice-local token `local`, if the row lists one.
+DEV bool bias_lookup(const unsigned long long *bhash, uint32_t slots, uint32_t local, float &b) {
+  uint32_t sl = hash_slot(local, slots);
+  while (true) {
+    const unsigned long long e = bhash[sl];
+    if ((uint32_t)e == local) {
+      b = __uint_as_float((uint32_t)(e >> 32));
+      return true;
+    }
+    if ((uint32_t)e == 0xFFFFFFFFu) return false;
+    sl = (sl + 1u) & (slots - 1u);
+  }
+}
+
+// Whether slice-local token `local` has a history entry.
+DEV bool hist_contains(const uint32_t *hash, uint32_t slots, uint32_t local) {
+  uint32_t sl = hash_slot(local, slots);
+  while (true) {
+    const uint32_t e = hash[sl];
+    if (e == 0xFFFFFFFFu) return false;
+    if ((e >> 13) == local) return true;
+    sl = (sl + 1u) & (slots - 1u);
+  }
+}
+
 // min-p keeps exp(z - m) >= min_p (fp64).  That set is an upper set of keys
 // (keys above the max's count as passing); its boundary is the smallest
 // passing key.  Serial form: from the closed-form guess m + ln(min_p),
@@ -1008,6 +1039,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   unsigned char *region = reinterpret_cast<unsigned char *>(zs + kp.slice);
   // region views (see the layout above)
   uint32_t *hash = reinterpret_cast<uint32_t *>(region);
+  // logit_bias / stop entries: slice-local index (low word, kEmpty = free)
+  // and the token's summed bias (high word, fp32 bits)
+  unsigned long long *bhash = reinterpret_cast<unsigned long long *>(region + 4 * (size_t)kp.hash_slots);
   uint32_t *lc = reinterpret_cast<uint32_t *>(region);
   unsigned long long *lm = reinterpret_cast<unsigned long long *>(region + kRegionLm);
   unsigned char *regB = region + kRegionB;
@@ -1039,6 +1073,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   }
   const int V = kp.vocab;
   const uint32_t hslots = (uint32_t)kp.hash_slots;
+  const uint32_t bslots = (uint32_t)kp.bias_slots;
   unsigned xseq = 0;
   RowCtx rc;
   rc.gid = gid;
@@ -1082,6 +1117,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const bool greedy = P.flags & RF_GREEDY;
     const bool top1 = P.flags & RF_TOP1;
     const bool pen = PEN && (P.flags & RF_PEN);
+    const bool spec = PEN && (P.flags & RF_SPEC);
     const bool topk = !greedy && (P.flags & RF_TOPK);
     const bool topp = !greedy && (P.flags & RF_TOPP);
     const bool minp = !greedy && (P.flags & RF_MINP);
@@ -1100,6 +1136,19 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       for (int q = 0; q < kHistPer; ++q) {
         const int h = tid + q * kBlock;
         hv[q] = h < P.hist_len ? hist[h] : -1;
+      }
+    }
+    // this thread's logit_bias or stop entry (one per thread): the bias
+    // list first, then the stop ids with bias -inf
+    int32_t bid = -1;
+    float bval = 0.0f;
+    if (spec) {
+      if (tid < P.bias_len) {
+        bid = kp.bias_ids[P.bias_start + tid];
+        bval = kp.bias_vals[P.bias_start + tid];
+      } else if (tid < P.bias_len + P.stop_len) {
+        bid = kp.stop_ids[P.stop_start + (tid - P.bias_len)];
+        bval = -INFINITY;
       }
     }
     constexpr int kBatch = kMaxSlice / (4 * kBlock);
@@ -1171,9 +1220,30 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // history entries are then read again from the input (the transform
     // overwrites the slice).
     int32_t osl[kHistPer];  // hash slot of an entry this thread created, else -1
+    int32_t bsl = -1;       // bias-hash slot this thread created, else -1
+    float xbr = 0.0f;       // raw logit of that slot's token
     auto build_hash = [&]() {
+      if (pen || spec) __syncthreads();
+      if (spec) {
+        // logit_bias and stop entries of this slice: a token's entries sum
+        // into one slot (LDS float adds)
+        if (bid >= s0 && bid < s1) {
+          const uint32_t local = (uint32_t)(bid - s0);
+          uint32_t sl = hash_slot(local, bslots);
+          uint32_t *lo = reinterpret_cast<uint32_t *>(bhash);
+          while (true) {
+            const uint32_t prev = atomicCAS(&lo[2 * sl], kEmpty, local);
+            if (prev == kEmpty || prev == local) {
+              if (prev == kEmpty) bsl = (int32_t)sl;
+              atomicAdd(reinterpret_cast<float *>(&lo[2 * sl + 1]), bval);
+              break;
+            }
+            sl = (sl + 1u) & (bslots - 1u);
+          }
+        }
+        if (bsl >= 0) xbr = Loader<TIn>::load1(kp.logits, rbase + (bid - s0));
+      }
       if (pen) {
-        __syncthreads();
 #pragma unroll
         for (int q = 0; q < kHistPer; ++q) {
           const int32_t id = hv[q];
@@ -1215,6 +1285,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       }
       if (pen)
         for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+      if (spec)
+        for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;  // free, bias +0
       transform(0, kBatch / 2);
       build_hash();
       transform(kBatch / 2, kBatch);
@@ -1226,25 +1298,67 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         for (int c = 0; c < 4; ++c) v[b][c] = Loader<TIn>::load1(kp.logits, rbase + min(4 * tid + 4 * kBlock * b + c, ln - 1));
       if (pen)
         for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+      if (spec)
+        for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;  // free, bias +0
       transform(0, kBatch / 2);
       build_hash();
       transform(kBatch / 2, kBatch);
       transform_slow();
     }
-    if (pen) {
-      // the thread that created an id's entry penalises that value once,
-      // with the final count
+    if (pen || spec) {
+      // The thread that created a history entry recomputes that token once
+      // from its raw logit: its bias (if any), then the penalties with the
+      // final count.  A bias entry whose token has no history entry is
+      // recomputed by the thread that created it.
       __syncthreads();
+      if (pen) {
 #pragma unroll
-      for (int q = 0; q < kHistPer; ++q) {
-        if (osl[q] >= 0) {
-          const uint32_t e = hash[osl[q]];
-          const float x = xr[q] == xr[q] ? xr[q] : -INFINITY;
-          zs[e >> 13] = div_temp(apply_penalty(x, e & 0x1FFFu, P), T, rT);
+        for (int q = 0; q < kHistPer; ++q) {
+          if (osl[q] >= 0) {
+            const uint32_t e = hash[osl[q]];
+            float x = xr[q] == xr[q] ? xr[q] : -INFINITY;
+            if (spec) {
+              float b;
+              if (bias_lookup(bhash, bslots, e >> 13, b)) x = add_bias(x, b);
+            }
+            zs[e >> 13] = div_temp(apply_penalty(x, e & 0x1FFFu, P), T, rT);
+          }
+        }
+      }
+      if (spec && bsl >= 0) {
+        const unsigned long long e = bhash[bsl];
+        const uint32_t local = (uint32_t)e;
+        if (!(pen && hist_contains(hash, hslots, local))) {
+          const float x = xbr == xbr ? xbr : -INFINITY;
+          zs[local] = div_temp(add_bias(x, __uint_as_float((uint32_t)(e >> 32))), T, rT);
         }
       }
     }
     __syncthreads();
+    if (kp.vocab_mask) {
+      // grammar bitmask: a cleared bit makes the value -inf.  Groups of four
+      // start at multiples of 4 of the row, so their bits share one word.
+      const uint32_t *mrow = kp.vocab_mask + (int64_t)row * kp.mask_stride;
+      uint32_t mw[kBatch];
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int l = 4 * tid + 4 * kBlock * b;
+        mw[b] = l < ln4 ? mrow[(s0 + l) >> 5] : 0xFFFFFFFFu;
+      }
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        const int l = 4 * tid + 4 * kBlock * b;
+        const uint32_t bits = (mw[b] >> ((s0 + l) & 31)) & 0xFu;
+        if (l < ln4 && bits != 0xFu) {
+          f32x4 o = *reinterpret_cast<const f32x4 *>(zs + l);
+#pragma unroll
+          for (int c = 0; c < 4; ++c)
+            if (!((bits >> c) & 1u)) o[c] = -INFINITY;
+          *reinterpret_cast<f32x4 *>(zs + l) = o;
+        }
+      }
+      __syncthreads();
+    }
     // this thread's max and first argmax: the best group of four by a
     // strict compare (groups in index order), then the first match in it
     float lmax = -INFINITY;
@@ -2369,7 +2483,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
 template <typename TIn, bool PEN>
 hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream) {
   const KernelParams &kp = ka.kp;
-  const size_t lds = kernel_lds_bytes(kp.slice, kp.hash_slots, PEN);
+  const size_t lds = kernel_lds_bytes(kp.slice, kp.hash_slots, kp.bias_slots, PEN);
   const dim3 grid(kp.n_groups * kp.G), block(kBlock);
   if (cooperative) {
     void *args[] = {const_cast<KernelArgs *>(&ka)};
@@ -2390,21 +2504,22 @@ hipError_t set_lds_attr(size_t lds) {
 
 size_t kernel_lds_fixed() { return sizeof(SmemBase); }
 
-size_t kernel_lds_region(int slice, int hash_slots, bool penalties) {
+size_t kernel_lds_region(int slice, int hash_slots, int bias_slots, bool penalties) {
   size_t r = kRegionB + kRegionBBytes;
   const size_t radix = 3072 + 8 * 256;
   r = r > radix ? r : radix;
   const size_t merge = 8 * (size_t)kMaxG * kMaxTopLogprobs;
   r = r > merge ? r : merge;
   if (penalties) {
-    const size_t pen = sizeof(uint32_t) * (size_t)hash_slots;
+    const size_t pen = sizeof(uint32_t) * (size_t)hash_slots + 8 * (size_t)bias_slots;
     r = r > pen ? r : pen;
   }
   return (r + 15) & ~(size_t)15;
 }
 
-size_t kernel_lds_bytes(int slice, int hash_slots, bool penalties) {
-  return kernel_lds_fixed() + sizeof(float) * (size_t)slice + kernel_lds_region(slice, hash_slots, penalties);
+size_t kernel_lds_bytes(int slice, int hash_slots, int bias_slots, bool penalties) {
+  return kernel_lds_fixed() + sizeof(float) * (size_t)slice +
+         kernel_lds_region(slice, hash_slots, bias_slots, penalties);
 }
 
 hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream) {

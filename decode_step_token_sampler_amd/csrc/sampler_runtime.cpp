@@ -54,6 +54,7 @@ struct sampler_handle {
   int resident = 0;  // workgroups of the row kernel that fit at once
   int slice_cap = 0;  // largest slice a workgroup holds in LDS
   int hash_slots = 0; // LDS hash slots for history counts
+  int bias_slots = 0; // LDS hash slots for logit_bias / stop entries (0: none)
   RowParam *host_ring = nullptr;   // pinned, kRing slots of max_rows records
   RowParam *dev_ring = nullptr;    // device, kRing slots
   KernelArgs *args = nullptr;      // host: the launch's argument block
@@ -124,6 +125,37 @@ sampler_status validate(const sampler_config *cfg, const sampler_step_args *a, s
   if (a->top_logprobs > 0 && (!a->top_logprob_vals || !a->top_logprob_ids)) {
     msg = "top_logprobs > 0 needs top_logprob_vals and top_logprob_ids";
     return SAMPLER_EINVAL;
+  }
+  if (a->vocab_mask && a->mask_stride < ((int64_t)a->vocab + 31) / 32) {
+    set_msg(msg, "mask_stride %lld is smaller than ceil(vocab / 32) = %d words", (long long)a->mask_stride,
+            (a->vocab + 31) / 32);
+    return SAMPLER_EINVAL;
+  }
+  if ((a->min_tokens != nullptr) != (a->output_len != nullptr)) {
+    msg = "min_tokens and output_len go together";
+    return SAMPLER_EINVAL;
+  }
+  const int32_t bias_cap = cfg ? cfg->max_bias_per_row : kMaxBiasPerRow;
+  for (int r = 0; r < a->n_rows; ++r) {
+    const int32_t bl = a->bias_len ? a->bias_len[r] : 0;
+    const bool stop_on = a->min_tokens && a->output_len[r] < a->min_tokens[r];
+    const int32_t sl = (stop_on && a->stop_len) ? a->stop_len[r] : 0;
+    if (bl < 0 || sl < 0) {
+      set_msg(msg, "row %d: bias_len and stop_len must be >= 0", r);
+      return SAMPLER_EINVAL;
+    }
+    if (bl > 0 && (!a->bias_ids || !a->bias_vals || !a->bias_start || a->bias_start[r] < 0)) {
+      set_msg(msg, "row %d: bias_len > 0 needs bias_ids, bias_vals and a bias_start >= 0", r);
+      return SAMPLER_EINVAL;
+    }
+    if (sl > 0 && (!a->stop_ids || !a->stop_start || a->stop_start[r] < 0)) {
+      set_msg(msg, "row %d: an active stop list needs stop_ids and a stop_start >= 0", r);
+      return SAMPLER_EINVAL;
+    }
+    if ((int64_t)bl + sl > bias_cap) {
+      set_msg(msg, "row %d: %d bias and %d active stop entries exceed max_bias_per_row %d", r, bl, sl, bias_cap);
+      return SAMPLER_ECAPACITY;
+    }
   }
   return validate_params(cfg, a, msg);
 }
@@ -271,11 +303,13 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
   }
   if (cfg->max_rows < 1 || cfg->max_vocab < 1 || cfg->max_vocab > kMaxVocab || cfg->max_history_per_row < 0 ||
       cfg->max_history_per_row > kMaxHistPerRow || cfg->max_top_logprobs < 0 ||
-      cfg->max_top_logprobs > kMaxTopLogprobs || (cfg->flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH))) {
+      cfg->max_top_logprobs > kMaxTopLogprobs || cfg->max_bias_per_row < 0 ||
+      cfg->max_bias_per_row > kMaxBiasPerRow ||
+      (cfg->flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH))) {
     set_msg(g_create_error,
             "bad config: need max_rows >= 1, 1 <= max_vocab <= %d, 0 <= max_history_per_row <= %d, "
-            "0 <= max_top_logprobs <= %d and known flags",
-            kMaxVocab, kMaxHistPerRow, kMaxTopLogprobs);
+            "0 <= max_top_logprobs <= %d, 0 <= max_bias_per_row <= %d and known flags",
+            kMaxVocab, kMaxHistPerRow, kMaxTopLogprobs, kMaxBiasPerRow);
     return SAMPLER_EINVAL;
   }
   int n_dev = 0;
@@ -309,8 +343,14 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     int slots = 64;
     while (slots < 2 * cfg->max_history_per_row) slots *= 2;
     h->hash_slots = slots;
+    int bslots = 0;
+    if (cfg->max_bias_per_row > 0) {
+      bslots = 64;
+      while (bslots < 2 * cfg->max_bias_per_row) bslots *= 2;
+    }
+    h->bias_slots = bslots;
     const size_t lds_max = prop.sharedMemPerBlock;
-    const size_t fixed = kernel_lds_fixed() + kernel_lds_region(kMaxSlice, slots, true);
+    const size_t fixed = kernel_lds_fixed() + kernel_lds_region(kMaxSlice, slots, bslots, true);
     if (lds_max <= fixed + 16 * kBlock) {
       set_msg(g_create_error, "device LDS per workgroup (%zu B) too small", lds_max);
       free_handle(h);
@@ -326,7 +366,8 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
       return SAMPLER_ECAPACITY;
     }
   }
-  if ((e = resident_blocks(cfg->device, kernel_lds_bytes(h->slice_cap, h->hash_slots, true), &h->resident)) !=
+  if ((e = resident_blocks(cfg->device, kernel_lds_bytes(h->slice_cap, h->hash_slots, h->bias_slots, true),
+                           &h->resident)) !=
       hipSuccess)
     goto fail;
   if (h->resident < 1) {
@@ -448,6 +489,22 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
       p.hist_len = a->history_len[r];
       any_pen = true;
     }
+    p.bias_start = 0;
+    p.bias_len = 0;
+    p.stop_start = 0;
+    p.stop_len = 0;
+    if (a->bias_len && a->bias_len[r] > 0) {
+      p.bias_start = a->bias_start[r];
+      p.bias_len = a->bias_len[r];
+    }
+    if (a->min_tokens && a->output_len[r] < a->min_tokens[r] && a->stop_len && a->stop_len[r] > 0) {
+      p.stop_start = a->stop_start[r];
+      p.stop_len = a->stop_len[r];
+    }
+    if (p.bias_len + p.stop_len > 0) {
+      f |= RF_SPEC;
+      any_pen = true;  // the launch needs the hash machinery
+    }
     p.flags = f;
     p.seed = a->row_seed ? a->row_seed[r] : (det ? kDeterministicSeed : a->seed);
     p.stream = a->row_stream ? a->row_stream[r] : (det ? 0u : (uint32_t)r);
@@ -503,6 +560,12 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.n_groups = groups < n ? groups : n;
   kp.slice = slice;
   kp.hash_slots = h->hash_slots;
+  kp.bias_slots = h->bias_slots;
+  kp.vocab_mask = a->vocab_mask;
+  kp.mask_stride = a->mask_stride;
+  kp.bias_ids = a->bias_ids;
+  kp.bias_vals = a->bias_vals;
+  kp.stop_ids = a->stop_ids;
   const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
   const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
   const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);

@@ -85,6 +85,7 @@ typedef struct sampler_config {
   int32_t max_top_logprobs;    /* largest top_logprobs (0..32) */
   int32_t device;              /* HIP device ordinal */
   uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH */
+  int32_t max_bias_per_row;    /* largest bias_len + active stop_len of one row (0..512) */
 } sampler_config;
 
 typedef struct sampler_handle sampler_handle;
@@ -161,6 +162,38 @@ typedef struct sampler_step_args {
 
   /* Output (host, may be NULL): the path the predicate chose. */
   int32_t *path_out;
+
+  /* Logits processors, applied to the logits before the penalties, in this
+   * order (each may be absent: NULL pointers):
+   *   1. grammar bitmask ([B] "Constrained decoding", step 4 "Mask": the
+   *      grammar fills a vocabulary bitmask that is applied to the logits
+   *      before sampling).  vocab_mask is device memory, uint32
+   *      [n_rows, mask_stride] (mask_stride >= ceil(vocab / 32) words); bit
+   *      (i & 31) of word (i >> 5) set = token i allowed, cleared = its
+   *      logit becomes -inf.
+   *   2. logit_bias (a sampler option in [B] "On Apple silicon"): row r's
+   *      entries are bias_ids / bias_vals[bias_start[r] .. + bias_len[r])
+   *      (ids and values in device memory, spans host arrays); entries of
+   *      one token are summed (order unspecified beyond two), then added to
+   *      its logit once; a NaN result becomes -inf.  Ids outside [0, vocab)
+   *      are ignored.
+   *   3. min_tokens ([C] "解码一步里采样做什么", _apply_min_tokens_penalty):
+   *      while output_len[r] < min_tokens[r] (host arrays), every id of row
+   *      r's stop list stop_ids[stop_start[r] .. + stop_len[r]) (ids in
+   *      device memory, spans host arrays) gets logit -inf.
+   * bias_len[r] plus stop_len[r] (counted only while the row's min_tokens
+   * is active) must not exceed max_bias_per_row. */
+  const uint32_t *vocab_mask;
+  int64_t mask_stride;
+  const int32_t *bias_ids;
+  const float *bias_vals;
+  const int64_t *bias_start;
+  const int32_t *bias_len;
+  const int32_t *stop_ids;
+  const int64_t *stop_start;
+  const int32_t *stop_len;
+  const int32_t *min_tokens;
+  const int32_t *output_len;
 } sampler_step_args;
 
 /* Create a handle on cfg->device: checks the device, allocates the device

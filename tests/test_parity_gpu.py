@@ -156,6 +156,61 @@ def test_max_vocab():
     s.close()
 
 
+# ------------------------------------------------------------ logits processors
+@pytest.fixture(scope="module")
+def sampler_proc():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(64, 131_072, max_history_per_row=2048, max_top_logprobs=32, max_bias_per_row=512)
+    yield s
+    s.close()
+
+
+def _processors_on_device(p):
+    def dev(a):
+        return torch.from_numpy(a).to("cuda:0")
+    return dict(vocab_mask=dev(p.vocab_mask.view(np.int32)), bias_ids=dev(p.bias_ids), bias_vals=dev(p.bias_vals),
+                stop_ids=dev(p.stop_ids), bias_start=p.bias_start, bias_len=p.bias_len, stop_start=p.stop_start,
+                stop_len=p.stop_len, min_tokens=p.min_tokens, output_len=p.output_len)
+
+
+@pytest.mark.parametrize("seed,n,V,dtype", [(31, 12, 4000, "f32"), (32, 10, 40_000, "bf16"), (33, 7, 129, "f32"),
+                                            (34, 15, 90_001, "f32")])
+def test_logits_processors(sampler_proc, seed, n, V, dtype):
+    """Grammar bitmask, logit_bias (repeats, ignored ids, -inf and large
+    values, tokens with and without history) and min_tokens stop lists, with
+    penalties and every truncation, against the oracle."""
+    b = workloads.random_small(seed, n, V, dtype, penalties=True, history_len=300)
+    p = workloads.processors(seed, b)
+    g = run_gpu(sampler_proc, b, **_processors_on_device(p))
+    o = run_oracle(b, **p.kwargs())
+    r = compare(g, o)
+    print(b.name, r)
+    assert r.ok(), r
+    assert np.all(g["row_status"][np.arange(n) % 10 == 9] == 1)      # nothing allowed
+
+
+def test_logits_processors_full_chain(sampler_proc):
+    """The full-chain workload (N=64, V=128,000) with processors on every row."""
+    b = workloads.config(4)
+    p = workloads.processors(35, b)
+    g = run_gpu(sampler_proc, b, **_processors_on_device(p))
+    o = run_oracle(b, **p.kwargs())
+    r = compare(g, o)
+    print(b.name, r)
+    assert r.ok(), r
+
+
+def test_logits_processors_absent_is_identity(sampler_proc, sampler):
+    """A handle with a bias table and no processor inputs gives the same
+    results as one without."""
+    b = workloads.random_small(36, 9, 5000, "f32", penalties=True)
+    g1 = run_gpu(sampler_proc, b)
+    g2 = run_gpu(sampler, b)
+    for k in ("token_ids", "probs", "logprobs", "top_logprob_ids", "top_logprob_vals", "row_status"):
+        np.testing.assert_array_equal(g1[k], g2[k])
+
+
 # ------------------------------------------------------------ invariants
 def test_replay_and_run_to_run_stability(sampler):
     b = workloads.config(4, n_rows=16, vocab=50_000, history_len=512)

@@ -264,3 +264,93 @@ def random_small(seed: int, n: int, V: int, dtype: str = "f32", *, ties: bool = 
         b.history_start = np.arange(n, dtype=np.int64) * history_len
         b.history_len = r.integers(0, history_len + 1, size=n).astype(np.int32)
     return b
+
+
+@dataclasses.dataclass
+class Processors:
+    """Logits-processor inputs of one batch (grammar bitmask, logit_bias,
+    min_tokens stop lists), as host arrays."""
+    vocab_mask: np.ndarray       # uint32 [n, words + 1] (one spare word of stride)
+    bias_ids: np.ndarray         # int32
+    bias_vals: np.ndarray        # float32
+    bias_start: np.ndarray       # int64 [n]
+    bias_len: np.ndarray         # int32 [n]
+    stop_ids: np.ndarray         # int32
+    stop_start: np.ndarray       # int64 [n]
+    stop_len: np.ndarray         # int32 [n]
+    min_tokens: np.ndarray       # int32 [n]
+    output_len: np.ndarray       # int32 [n]
+
+    def kwargs(self) -> dict:
+        return dict(vocab_mask=self.vocab_mask, bias_ids=self.bias_ids, bias_vals=self.bias_vals,
+                    bias_start=self.bias_start, bias_len=self.bias_len, stop_ids=self.stop_ids,
+                    stop_start=self.stop_start, stop_len=self.stop_len, min_tokens=self.min_tokens,
+                    output_len=self.output_len)
+
+
+def processors(seed: int, batch: Batch, max_entries: int = 512) -> Processors:
+    """Seeded grammar masks, logit_bias lists and stop lists for `batch`.
+
+    Masks per row cycle through: everything allowed, ~half allowed, ~5%
+    allowed, two tokens allowed, nothing allowed.  Bias lists mix ids from the
+    row's history (where there is one) with random ids, a few repeated ids
+    (a token's entries are summed) and out-of-range ids, with values in
+    [-5, 5]; one row biases its top token by -inf (a banned word) and one by
+    a large positive value.  Stop lists of 1-8 ids are active on every other
+    row (output_len < min_tokens)."""
+    n, V = batch.n_rows, batch.vocab
+    g = _rng(9001, seed, n, V)
+    words = (V + 31) // 32
+    allowed = np.ones((n, V), dtype=bool)
+    for r in range(n):
+        kind = r % 5
+        if kind == 1:
+            allowed[r] = g.random(V) < 0.5
+        elif kind == 2:
+            allowed[r] = g.random(V) < 0.05
+        elif kind == 3:
+            allowed[r] = False
+            allowed[r, g.choice(V, size=min(2, V), replace=False)] = True
+        elif kind == 4 and r % 10 == 9:
+            allowed[r] = False
+    bits = np.zeros((n, words * 32), dtype=np.uint64)
+    bits[:, :V] = allowed
+    packed = (bits.reshape(n, words, 32) << np.arange(32, dtype=np.uint64)).sum(axis=2).astype(np.uint32)
+    mask = np.zeros((n, words + 1), dtype=np.uint32)
+    mask[:, :words] = packed
+    ids, vals, bstart, blen = [], [], [], []
+    sids, sstart, slen = [], [], []
+    for r in range(n):
+        nb = int(g.integers(0, max_entries // 2 + 1)) if r % 4 != 3 else 0
+        row_ids = []
+        if batch.history_ids is not None and batch.history_len is not None and batch.history_len[r] > 0:
+            h = batch.history_ids[batch.history_start[r]:batch.history_start[r] + batch.history_len[r]]
+            row_ids += list(g.choice(h, size=min(nb // 2, len(h))))
+        row_ids += list(g.integers(0, V, size=nb - len(row_ids)))
+        if row_ids:
+            row_ids[:2] = [-1, V][:len(row_ids[:2])]               # ignored ids
+            if len(row_ids) > 6:
+                row_ids[3] = row_ids[4]                            # a repeated id
+        rv = list(g.uniform(-5.0, 5.0, size=len(row_ids)).astype(np.float32))
+        if r % 7 == 5 and len(row_ids) > 8:
+            row_ids[8] = int(np.argmax(batch.logits[r].view(np.float32) if batch.dtype == "f32"
+                                       else bf16_bits_to_f32(batch.logits[r])))
+            rv[8] = np.float32(-np.inf)
+        if r % 7 == 6 and len(row_ids) > 8:
+            rv[8] = np.float32(25.0)
+        bstart.append(len(ids))
+        blen.append(len(row_ids))
+        ids += [int(x) for x in row_ids]
+        vals += rv
+        ns = int(g.integers(1, 9))
+        sstart.append(len(sids))
+        slen.append(ns)
+        sids += [int(x) for x in g.integers(0, V, size=ns)]
+        # stop lists must fit beside the bias list when active
+        if blen[-1] + ns > max_entries:
+            blen[-1] = max_entries - ns
+    min_tokens = np.full(n, 4, dtype=np.int32)
+    output_len = np.array([2 if r % 2 == 0 else 6 for r in range(n)], dtype=np.int32)
+    return Processors(mask, np.array(ids, np.int32), np.array(vals, np.float32), np.array(bstart, np.int64),
+                      np.array(blen, np.int32), np.array(sids, np.int32), np.array(sstart, np.int64),
+                      np.array(slen, np.int32), min_tokens, output_len)
