@@ -95,7 +95,11 @@ class StepArgs(ctypes.Structure):
         ("stop_len", ctypes.c_void_p),
         ("min_tokens", ctypes.c_void_p),
         ("output_len", ctypes.c_void_p),
+        ("logprob_mode", ctypes.c_int32),
     ]
+
+
+LOGPROB_MODES = {"processed": 0, "temperature": 1, "raw": 2}
 
 
 _lib = None
@@ -258,7 +262,8 @@ class Sampler:
              row_offset=None, row_stream=None, want_probs: bool = False, want_logprobs: bool = False,
              top_logprobs: int = 0, want_status: bool = True, out: Optional[dict] = None, stream=None,
              vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None, stop_ids=None,
-             stop_start=None, stop_len=None, min_tokens=None, output_len=None) -> dict:
+             stop_start=None, stop_len=None, min_tokens=None, output_len=None,
+             logprob_mode: str = "processed") -> dict:
         """Enqueue one decode step on the current torch stream; returns the output tensors.
 
         ``logits``: a CUDA tensor [N, row_stride] of float32 or bfloat16 with unit
@@ -306,6 +311,9 @@ class Sampler:
         a.bias_ids = None if bias_ids is None else bias_ids.data_ptr()
         a.bias_vals = None if bias_vals is None else bias_vals.data_ptr()
         a.stop_ids = None if stop_ids is None else stop_ids.data_ptr()
+        if logprob_mode not in LOGPROB_MODES:
+            raise ValueError("logprob_mode must be one of %s" % sorted(LOGPROB_MODES))
+        a.logprob_mode = LOGPROB_MODES[logprob_mode]
         if vocab_mask is not None:
             if vocab_mask.dim() != 2 or vocab_mask.stride(1) != 1 or vocab_mask.element_size() != 4:
                 raise ValueError("vocab_mask must be a 2-D 32-bit tensor with unit column stride")

@@ -847,6 +847,8 @@ struct E3In {
   uint32_t t_m;
   int rklo, rkhi, r1lo, r1hi, K, row, gid;
   bool full_k, topk_on, topp, minp, truncated, want_S;
+  bool lp_all;  // top logprobs list every token, valued with ln of the full sum
+  double lnA;   // ln of the full sum (with lp_all)
 };
 struct E3Out {
   bool general;
@@ -986,12 +988,13 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
   }
   const double lns = log(S_K);
   if (!flags && in.K > 0 && in.gid == 0) {
-    const int kept_n = in.truncated ? et : n;
+    const int kept_n = (in.truncated && !in.lp_all) ? et : n;
+    const double lnl = in.lp_all ? in.lnA : lns;
     for (int q = lane; q < in.K; q += 64) {
       const int64_t o = (int64_t)in.row * in.K + q;
       if (q < kept_n) {
         const unsigned long long sq_ = srt[q];
-        kp.top_lp_vals[o] = (float)(((double)key_to_float((uint32_t)(sq_ >> 32)) - in.m) - lns);
+        kp.top_lp_vals[o] = (float)(((double)key_to_float((uint32_t)(sq_ >> 32)) - in.m) - lnl);
         kp.top_lp_ids[o] = (int)(~(uint32_t)sq_);
       } else {
         kp.top_lp_vals[o] = -INFINITY;
@@ -1090,6 +1093,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   const int omode = !want_out ? 0 : (((kp.vec_ok & 2) && kp.probs && kp.logprobs) ? 1 : 2);
   const int K = kp.top_lp;
   const bool want_S = want_out || K > 0;
+  // [B] "Logprobs are temperature-scaled": returned logprobs (and top
+  // logprobs) of every token under the untruncated distribution at the
+  // row's temperature, instead of the distribution sampled from
+  const bool lp_all = kp.lp_mode != 0 && (kp.logprobs != nullptr || K > 0);
   const int s0 = gid * kp.slice;
   const int s1 = min(V, s0 + kp.slice);
   rc.s0 = s0;
@@ -1390,7 +1397,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const bool need_sel = topk || topp || K > 0 || (truncated && want_S);  // window + candidates
     const bool need_mass = topp || (truncated && want_S);
     const bool need_deep = topp && !topk;  // top-p's total includes the deep values
-    const bool need_exact = !truncated && want_S;
+    const bool need_exact = want_S && (!truncated || lp_all);
     // rows that need the merged max: thresholds, sums or min-p's boundary.
     // The rest (no truncation, no outputs) prune against their own slice's
     // max and settle argmax and status in the final exchange.
@@ -1405,6 +1412,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     uint32_t tau = 0;
     double lnS = 0.0;
     double s_all = 0.0;  // the exact sum of every value's mass, when needed
+    double lnA = 0.0;    // its log (the logprob normaliser with lp_all)
     int r0hi = -1, r1lo = 1, r1hi = 0, rklo = 1, rkhi = 0, bm = -1;
     if (need_x) {
       // ---- 3. window histogram of this slice on the absolute bin grid,
@@ -1462,8 +1470,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         using T1 = std::integral_constant<bool, true>;
         using F1 = std::integral_constant<bool, false>;
         if (need_sel) {
-          if (need_deep) hist_pass(T1{}, T1{}, F1{});
-          else if (need_exact) hist_pass(T1{}, F1{}, T1{});
+          if (need_deep) {
+            if (need_exact) hist_pass(T1{}, T1{}, T1{});
+            else hist_pass(T1{}, T1{}, F1{});
+          } else if (need_exact) hist_pass(T1{}, F1{}, T1{});
           else hist_pass(T1{}, F1{}, F1{});
         } else {
           hist_pass(F1{}, F1{}, T1{});
@@ -1556,6 +1566,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       if (need_exact) {
         for (int g = 0; g < G; ++g) s_all += sm.gd[g];
         lnS = log(s_all);
+        lnA = lnS;
       }
       if (need_sel) {
         const int b = tid;
@@ -1625,7 +1636,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         const int bmin = minp ? win_bin(A, key_to_float(t_m), wsc) : kWinBins;
         if (K > 0) {
           if (r0 != kNone) r0hi = (int)r0;
-          else if (truncated) r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
+          else if (truncated && !lp_all) r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
           else gen = true;
         }
         if (topk) {
@@ -1946,6 +1957,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           in.minp = minp;
           in.truncated = truncated;
           in.want_S = want_S;
+          in.lp_all = lp_all;
+          in.lnA = lnA;
           const E3Out o = e3_decide(sm, n, sq, lc, lm, in, kp);
           if (lane == 0) {
             sm.bu[26] = o.general ? 1u : 0u;
@@ -2097,11 +2110,12 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         }
         const double lns = log(S_K);
         if (!flags && K > 0 && gid == 0) {
-          const int kept_n = truncated ? et : n;
+          const int kept_n = (truncated && !lp_all) ? et : n;
+          const double lnl = lp_all ? lnA : lns;
           for (int q = tid; q < K; q += kBlock) {
             const int64_t o = (int64_t)row * K + q;
             if (q < kept_n) {
-              kp.top_lp_vals[o] = (float)(((double)zof(q) - m) - lns);
+              kp.top_lp_vals[o] = (float)(((double)zof(q) - m) - lnl);
               kp.top_lp_ids[o] = idxof(q);
             } else {
               kp.top_lp_vals[o] = -INFINITY;
@@ -2153,7 +2167,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
             const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              if (zv[c] > -INFINITY && fkey(zv[c]) >= tau) {
+              if (zv[c] > -INFINITY && (lp_all || fkey(zv[c]) >= tau)) {
                 const unsigned long long ck =
                     ((unsigned long long)fkey(zv[c]) << 32) | (0xFFFFFFFFu - (uint32_t)(s0 + l + c));
                 if (ck < last && ck > cand) cand = ck;
@@ -2302,12 +2316,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // with 16-byte stores; anything else, element by element) and on the
     // number of storing threads, with the per-row constants it uses held in
     // vector registers.
-    auto emit_loop = [&](auto MODE, auto NTC) __attribute__((always_inline)) {
+    auto emit_loop = [&](auto MODE, auto NTC, auto LPA) __attribute__((always_inline)) {
       constexpr int mode = decltype(MODE)::value;
       constexpr int NT = decltype(NTC)::value;  // the last NT threads store
+      constexpr bool lpa = decltype(LPA)::value;  // logprobs of every token (ln S_all)
       const int et = tid - (kBlock - NT);
       const int its = (ln4 + 4 * NT - 1) / (4 * NT);
-      double mv = m, lnsv = lnS;
+      double mv = m, lnsv = lnS, lnav = lnA;
       float tv = tauf;
       int64_t ob = (int64_t)row * V + s0;  // output offset of the slice
       // the slice's output rows, as global pointers held in vector registers
@@ -2318,6 +2333,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         lq = (gf32x4 *)(kp.logprobs + ob);
       }
       asm volatile("" : "+v"(mv), "+v"(lnsv), "+v"(tv), "+v"(ob), "+v"(pq), "+v"(lq));
+      if (lpa) asm volatile("" : "+v"(lnav));
       for (int q0 = 0; q0 < its; q0 += 4) {
         f32x4 zr[4];  // the chunk's four groups, read first (clamped addresses)
 #pragma unroll
@@ -2330,7 +2346,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           // padding (-inf) only passes when tau is 0
           const bool anyk = fmaxf(fmaxf(zv[0], zv[1]), fmaxf(zv[2], zv[3])) >= tv;
           // a wave whose groups keep nothing stores 0 / -inf without the math
-          if (act && !__ballot(act && anyk)) {
+          if (!lpa && act && !__ballot(act && anyk)) {
             if (mode == 1 && l + 3 < ln) {
               __builtin_nontemporal_store(f32x4{0.0f, 0.0f, 0.0f, 0.0f}, pq + (l >> 2));
               __builtin_nontemporal_store(f32x4{-INFINITY, -INFINITY, -INFINITY, -INFINITY}, lq + (l >> 2));
@@ -2351,7 +2367,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
               // by the hardware exp2 (absolute error below 2e-7)
               const bool kk = zv[c] >= tv;
               const float lp = kk ? (float)(((double)zv[c] - mv) - lnsv) : -INFINITY;
-              lv[c] = lp;
+              lv[c] = lpa ? (float)(((double)zv[c] - mv) - lnav) : lp;
               pv[c] = kk ? __builtin_amdgcn_exp2f(lp * kLog2e) : 0.0f;
             }
             const int64_t o = ob + l;
@@ -2375,6 +2391,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     using NT512 = std::integral_constant<int, kBlock>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
+    using B0 = std::integral_constant<bool, false>;
+    using B1 = std::integral_constant<bool, true>;
     if (omode != 0 && !late_fin && tau != 0) {
       // A truncated row: waves 4..7 write the outputs from the start; waves
       // 0..3 run Gumbel-max over the whole slice meanwhile (the kept set is
@@ -2405,10 +2423,13 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           }
           final_exchange();
         }
+      } else if (lp_all) {
+        if (omode == 1) emit_loop(I1{}, NT256{}, B1{});
+        else emit_loop(I2{}, NT256{}, B1{});
       } else if (omode == 1) {
-        emit_loop(I1{}, NT256{});
+        emit_loop(I1{}, NT256{}, B0{});
       } else {
-        emit_loop(I2{}, NT256{});
+        emit_loop(I2{}, NT256{}, B0{});
       }
     } else {
       if (gumbel) {
@@ -2416,8 +2437,14 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         wg_best(sm, best_g, best_i);
       }
       if (!late_fin && wave == 0) final_exchange();
-      if (omode == 1) emit_loop(I1{}, NT512{});
-      else if (omode == 2) emit_loop(I2{}, NT512{});
+      if (lp_all) {
+        if (omode == 1) emit_loop(I1{}, NT512{}, B1{});
+        else if (omode == 2) emit_loop(I2{}, NT512{}, B1{});
+      } else if (omode == 1) {
+        emit_loop(I1{}, NT512{}, B0{});
+      } else if (omode == 2) {
+        emit_loop(I2{}, NT512{}, B0{});
+      }
     }
 
     if (late_fin) {
@@ -2465,7 +2492,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           if (r < K) {
             const int64_t o = (int64_t)row * K + r;
             const float zz = key_to_float((uint32_t)(key >> 32));
-            kp.top_lp_vals[o] = (float)(((double)zz - m) - lnS);
+            kp.top_lp_vals[o] = (float)(((double)zz - m) - (lp_all ? lnA : lnS));
             kp.top_lp_ids[o] = (int)(0xFFFFFFFFu - (uint32_t)(key & 0xFFFFFFFFu));
           }
         }

@@ -131,6 +131,20 @@ sampler_status validate(const sampler_config *cfg, const sampler_step_args *a, s
             (a->vocab + 31) / 32);
     return SAMPLER_EINVAL;
   }
+  if (a->logprob_mode < SAMPLER_LOGPROB_PROCESSED || a->logprob_mode > SAMPLER_LOGPROB_RAW) {
+    set_msg(msg, "unknown logprob_mode %d", a->logprob_mode);
+    return SAMPLER_EINVAL;
+  }
+  if (a->logprob_mode == SAMPLER_LOGPROB_RAW) {
+    for (int r = 0; r < a->n_rows; ++r) {
+      const float t = a->temperature ? a->temperature[r] : 1.0f;
+      if (!(row_is_greedy(t) || t == 1.0f)) {
+        set_msg(msg, "row %d: the raw logprob mode is supported only at effective temperature 1 (got %g)", r,
+                (double)t);
+        return SAMPLER_ENOTSUP;
+      }
+    }
+  }
   if ((a->min_tokens != nullptr) != (a->output_len != nullptr)) {
     msg = "min_tokens and output_len go together";
     return SAMPLER_EINVAL;
@@ -566,6 +580,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.bias_ids = a->bias_ids;
   kp.bias_vals = a->bias_vals;
   kp.stop_ids = a->stop_ids;
+  kp.lp_mode = a->logprob_mode != SAMPLER_LOGPROB_PROCESSED ? 1 : 0;
   const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
   const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
   const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);

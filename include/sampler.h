@@ -194,7 +194,26 @@ typedef struct sampler_step_args {
   const int32_t *stop_len;
   const int32_t *min_tokens;
   const int32_t *output_len;
+
+  /* Which logprobs (and top logprobs) are returned ([B] "Logprobs are
+   * temperature-scaled"):
+   *   SAMPLER_LOGPROB_PROCESSED (0, default): the distribution sampled
+   *     from, after truncation (0 / -inf outside the kept set);
+   *   SAMPLER_LOGPROB_TEMPERATURE (1): log_softmax(logits / temperature)
+   *     of the processed logits, untruncated: every token gets a value and
+   *     top logprobs list the largest over all tokens;
+   *   SAMPLER_LOGPROB_RAW (2): log_softmax of the processed logits without
+   *     temperature (the page's original-logprob switch).  This build
+   *     supports it when every row's effective temperature is 1 (greedy
+   *     rows and T = 1), where it equals mode 1; otherwise the step returns
+   *     SAMPLER_ENOTSUP without launching.
+   * probs and the sampled tokens do not depend on the mode. */
+  int32_t logprob_mode;
 } sampler_step_args;
+
+#define SAMPLER_LOGPROB_PROCESSED 0
+#define SAMPLER_LOGPROB_TEMPERATURE 1
+#define SAMPLER_LOGPROB_RAW 2
 
 /* Create a handle on cfg->device: checks the device, allocates the device
  * workspace (exchange areas, barrier words, parameter ring) and a pinned

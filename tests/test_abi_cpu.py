@@ -89,7 +89,8 @@ def _args(n=2, V=16, **kw):
     return a, keep
 
 
-CFG = dsts.Config(max_rows=8, max_vocab=1024, max_history_per_row=64, max_top_logprobs=20, device=0, flags=0)
+CFG = dsts.Config(max_rows=8, max_vocab=1024, max_history_per_row=64, max_top_logprobs=20, device=0, flags=0,
+                  max_bias_per_row=16)
 
 
 @pytest.mark.parametrize("change,status", [
@@ -120,6 +121,23 @@ CFG = dsts.Config(max_rows=8, max_vocab=1024, max_history_per_row=64, max_top_lo
      dsts.SAMPLER_EINVAL),
     (dict(top_logprobs=21, top_logprob_vals=0x4000, top_logprob_ids=0x5000), dsts.SAMPLER_ECAPACITY),
     (dict(top_logprobs=5), dsts.SAMPLER_EINVAL),
+    # logits processors
+    (dict(vocab_mask=0x6000, mask_stride=0), dsts.SAMPLER_EINVAL),          # needs ceil(16 / 32) = 1 word
+    (dict(bias_len=np.array([2, 0], np.int32), bias_start=np.zeros(2, np.int64)), dsts.SAMPLER_EINVAL),
+    (dict(bias_len=np.array([17, 0], np.int32), bias_start=np.zeros(2, np.int64), bias_ids=0x7000,
+          bias_vals=0x8000), dsts.SAMPLER_ECAPACITY),
+    (dict(bias_len=np.array([-1, 0], np.int32), bias_start=np.zeros(2, np.int64), bias_ids=0x7000,
+          bias_vals=0x8000), dsts.SAMPLER_EINVAL),
+    (dict(bias_len=np.array([10, 0], np.int32), bias_start=np.zeros(2, np.int64), bias_ids=0x7000,
+          bias_vals=0x8000, stop_len=np.array([7, 0], np.int32), stop_start=np.zeros(2, np.int64),
+          stop_ids=0x9000, min_tokens=np.array([3, 3], np.int32), output_len=np.array([0, 0], np.int32)),
+     dsts.SAMPLER_ECAPACITY),                                                # 10 + 7 active stop ids > 16
+    (dict(stop_len=np.array([2, 0], np.int32), stop_start=np.zeros(2, np.int64),
+          min_tokens=np.array([3, 3], np.int32), output_len=np.array([0, 0], np.int32)), dsts.SAMPLER_EINVAL),
+    (dict(min_tokens=np.array([3, 3], np.int32)), dsts.SAMPLER_EINVAL),      # without output_len
+    # logprob modes
+    (dict(logprob_mode=3), dsts.SAMPLER_EINVAL),
+    (dict(logprob_mode=2, temperature=np.array([1.0, 0.7], np.float32)), dsts.SAMPLER_ENOTSUP),
 ])
 def test_validation_errors(lib, change, status):
     a, keep = _args(**change)
@@ -135,6 +153,21 @@ def test_validation_accepts_good_args(lib):
                     history_ids=0x3000, top_logprobs=20, top_logprob_vals=0x4000, top_logprob_ids=0x5000)
     st, msg = dsts.validate(CFG, a)
     assert st == dsts.SAMPLER_OK, msg
+
+
+def test_validation_accepts_processors_and_modes(lib):
+    # a mask of exactly ceil(V / 32) words; stop lists count only while min_tokens is active
+    a, keep = _args(vocab_mask=0x6000, mask_stride=1, bias_len=np.array([10, 16], np.int32),
+                    bias_start=np.array([0, 10], np.int64), bias_ids=0x7000, bias_vals=0x8000,
+                    stop_len=np.array([7, 7], np.int32), stop_start=np.zeros(2, np.int64), stop_ids=0x9000,
+                    min_tokens=np.array([3, 3], np.int32), output_len=np.array([3, 5], np.int32),
+                    logprob_mode=1)
+    st, msg = dsts.validate(CFG, a)
+    assert st == dsts.SAMPLER_OK, msg
+    for t in ([0.0, 1.0], [1.0, 1.0], [1e-7, 0.0]):
+        a, keep = _args(logprob_mode=2, temperature=np.array(t, np.float32))
+        st, msg = dsts.validate(CFG, a)
+        assert st == dsts.SAMPLER_OK, msg
 
 
 def test_create_without_gpu_reports_ehip(lib):

@@ -211,6 +211,62 @@ def test_logits_processors_absent_is_identity(sampler_proc, sampler):
         np.testing.assert_array_equal(g1[k], g2[k])
 
 
+# ------------------------------------------------------------ logprob modes
+@pytest.mark.parametrize("seed,n,V,dtype", [(41, 12, 3000, "f32"), (42, 9, 70_000, "bf16"), (43, 16, 257, "f32")])
+def test_logprob_mode_temperature(sampler, seed, n, V, dtype):
+    """Untruncated logprobs at the row's temperature for every token; top
+    logprobs over all tokens."""
+    b = workloads.random_small(seed, n, V, dtype, penalties=True)
+    b.top_logprobs = 7
+    g = run_gpu(sampler, b, logprob_mode="temperature")
+    o = run_oracle(b, logprob_mode="temperature")
+    r = compare(g, o)
+    print(b.name, r)
+    assert r.ok(), r
+    assert np.all(np.isfinite(g["logprobs"][g["row_status"] == 0]))
+
+
+def test_logprob_mode_temperature_workloads(sampler):
+    for b in (workloads.config(3), workloads.config(4)):
+        g = run_gpu(sampler, b, logprob_mode="temperature")
+        o = run_oracle(b, logprob_mode="temperature")
+        r = compare(g, o)
+        print(b.name, r)
+        assert r.ok(), r
+
+
+def test_logprob_mode_top_list_below_the_window(sampler):
+    """Truncated rows whose top-logprob list must reach values far below the
+    row max (deeper than the threshold window): the general path."""
+    V = 5000
+    x = np.full((3, V), -60.0, np.float32) - np.arange(V, dtype=np.float32) * 1e-3
+    x[:, :3] = [0.0, -0.5, -1.0]
+    b = workloads.Batch("deep top list", "f32", x, temperature=np.array([1.0, 0.8, 1.0], np.float32),
+                        top_k=np.array([2, -1, 3], np.int32), top_p=np.array([1.0, 0.5, 1.0], np.float32),
+                        min_p=np.array([0.0, 0.0, 0.2], np.float32), want_probs=True, want_logprobs=True,
+                        top_logprobs=6)
+    for mode in ("processed", "temperature"):
+        g = run_gpu(sampler, b, logprob_mode=mode)
+        o = run_oracle(b, logprob_mode=mode)
+        r = compare(g, o)
+        print(mode, r)
+        assert r.ok(), r
+    assert np.all(g["top_logprob_ids"] >= 0)          # six listed in the temperature mode
+
+
+def test_logprob_mode_raw_at_unit_temperature(sampler):
+    b = workloads.random_small(44, 10, 9000, "bf16", penalties=True)
+    b.temperature = np.where(np.arange(10) % 3 == 0, 0.0, 1.0).astype(np.float32)
+    g = run_gpu(sampler, b, logprob_mode="raw")
+    o = run_oracle(b, logprob_mode="raw")
+    r = compare(g, o)
+    assert r.ok(), r
+    import decode_step_token_sampler_amd as dsts
+    b.temperature[1] = 0.7
+    with pytest.raises(dsts.SamplerError):
+        run_gpu(sampler, b, logprob_mode="raw")
+
+
 # ------------------------------------------------------------ invariants
 def test_replay_and_run_to_run_stability(sampler):
     b = workloads.config(4, n_rows=16, vocab=50_000, history_len=512)
