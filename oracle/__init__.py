@@ -35,6 +35,7 @@ TOP_K_ALL = 1 << 30
 PATH_GREEDY, PATH_GUMBEL, PATH_FILTERED, PATH_DETERMINISTIC = 0, 1, 2, 3
 PATH_NAMES = {0: "greedy", 1: "gumbel", 2: "filtered", 3: "deterministic"}
 FLAG_GUMBEL_NEAR_TIE, FLAG_TOPP_MARGIN, FLAG_MINP_MARGIN, FLAG_SPELLING_MISMATCH = 1, 2, 4, 8
+FLAG_ICDF_MARGIN = 16
 
 GCC_FLAGS = ["-O2", "-ffp-contract=off", "-fno-fast-math", "-fPIC", "-shared", "-std=c11", "-pthread"]
 
@@ -95,6 +96,7 @@ class _Args(ctypes.Structure):
         ("min_tokens", ctypes.c_void_p),
         ("output_len", ctypes.c_void_p),
         ("logprob_mode", ctypes.c_int32),
+        ("inverse_cdf", ctypes.c_int32),
     ]
 
 
@@ -115,6 +117,8 @@ def lib():
             L.orc_draw_word.restype = ctypes.c_uint32
             L.orc_exp1_from_word.argtypes = [ctypes.c_uint32]
             L.orc_exp1_from_word.restype = ctypes.c_double
+            L.orc_icdf_uniform.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64]
+            L.orc_icdf_uniform.restype = ctypes.c_double
             L.orc_fill_exp1.argtypes = [ctypes.c_uint64, ctypes.c_uint32, ctypes.c_uint64, ctypes.c_int64,
                                         ctypes.c_void_p]
             L.orc_fill_exp1.restype = None
@@ -160,6 +164,11 @@ def exp1_from_word(x: int) -> float:
     return float(lib().orc_exp1_from_word(x))
 
 
+def icdf_uniform(seed: int, stream: int, offset: int) -> float:
+    """The row's uniform for inverse-CDF selection."""
+    return float(lib().orc_icdf_uniform(seed, stream, offset))
+
+
 def exp1_draws(seed: int, stream: int, offset: int, n: int) -> np.ndarray:
     """Exp(1) variates the oracle uses for vocabulary entries 0..n-1 of a row."""
     out = np.empty(n, dtype=np.float64)
@@ -199,7 +208,7 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
          want_probs=True, want_logprobs=True, top_logprobs=0, n_threads=1,
          vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None,
          stop_ids=None, stop_start=None, stop_len=None, min_tokens=None, output_len=None,
-         logprob_mode="processed"):
+         logprob_mode="processed", inverse_cdf=False):
     """Run the oracle on host arrays.
 
     ``logits`` is a 2-D array: float32, or uint16 holding bf16 bits when
@@ -279,6 +288,7 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
     a.stop_ids, a.stop_start, a.stop_len = _ptr(SI), _ptr(SS), _ptr(SL)
     a.min_tokens, a.output_len = _ptr(MT), _ptr(OL)
     a.logprob_mode = LOGPROB_MODES[logprob_mode]
+    a.inverse_cdf = int(bool(inverse_cdf))
     for ids, st, ln, what in ((BI, BS, BL, "bias"), (SI, SS, SL, "stop")):
         if ids is not None and st is not None and ln is not None:
             if np.any(st < 0) or np.any(st + ln > ids.shape[0]):

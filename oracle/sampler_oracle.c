@@ -37,6 +37,10 @@
  *     tokens were produced); then penalties and temperature.
  *   - logprob modes: processed (after truncation, the default), temperature
  *     (untruncated log_softmax(z)), raw (untruncated, before temperature).
+ *   - inverse-CDF selection (the seeded multinomial): u from the Philox
+ *     block at counter (0xFFFFFFFF, stream, off_lo, off_hi), 53 bits; the
+ *     first kept token in index order whose running kept mass exceeds u
+ *     times the kept total.
  *
  * Parity pins: see tests/test_oracle_*.py.  The penalty formula itself is
  * not fixed by the pages ("parity unpinned" for that formula; only its
@@ -66,6 +70,8 @@
 #define ORC_FLAG_TOPP_MARGIN 2
 #define ORC_FLAG_MINP_MARGIN 4
 #define ORC_FLAG_SPELLING_MISMATCH 8
+#define ORC_FLAG_ICDF_MARGIN 16
+#define ORC_ICDF_MARGIN 1e-10       /* relative distance of u*S from a CDF step (flag) */
 
 typedef struct {
   const void *logits;       /* [n_rows, row_stride] fp32 or bf16 bits (host) */
@@ -116,6 +122,7 @@ typedef struct {
   const int32_t *min_tokens;  /* per row */
   const int32_t *output_len;  /* per row: tokens generated so far */
   int32_t logprob_mode;       /* 0 processed, 1 temperature-scaled, 2 raw */
+  int32_t inverse_cdf;        /* select by the seeded inverse CDF instead of Gumbel-max */
 } orc_args;
 
 /* ------------------------------------------------------------------ */
@@ -161,6 +168,19 @@ double orc_exp1_from_word(uint32_t x) {
   double e = -log1p(-w);
   if (e < (double)FLT_MIN) e = (double)FLT_MIN;
   return e;
+}
+
+/* The row's uniform for inverse-CDF selection: the Philox block at counter
+ * (0xFFFFFFFF, stream, off_lo, off_hi) -- a counter no vocabulary entry
+ * uses (entries use i >> 2 < 2^30) -- words 0 and 1 as a 64-bit integer,
+ * its top 53 bits scaled to [0, 1). */
+double orc_icdf_uniform(uint64_t seed, uint32_t stream, uint64_t offset) {
+  uint32_t ctr[4] = {0xFFFFFFFFu, stream, (uint32_t)offset, (uint32_t)(offset >> 32)};
+  uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+  uint32_t out[4];
+  orc_philox4x32_10(ctr, key, out);
+  uint64_t x = ((uint64_t)out[1] << 32) | out[0];
+  return (double)(x >> 11) * 0x1p-53;
 }
 
 /* Exp(1) variates of vocabulary entries 0..n-1 of one row (test helper). */
@@ -482,6 +502,30 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
         token = i;
         break;
       }
+  } else if (a->inverse_cdf) {
+    /* The seeded multinomial ([A] "One request with top_p ...", the
+     * deterministic path's seeded multinomial; [B] "What the flag
+     * switches"): one uniform u per row, then the first token (in index
+     * order) whose cumulative kept mass exceeds u times the kept total.
+     * Masses are summed one at a time in index order. */
+    uint64_t seed = a->row_seed ? a->row_seed[r] : (a->deterministic ? 42u : a->seed);
+    uint32_t stream = a->row_stream ? a->row_stream[r] : (a->deterministic ? 0u : (uint32_t)r);
+    uint64_t off = a->row_offset ? a->row_offset[r] : a->offset;
+    const double u = orc_icdf_uniform(seed, stream, off);
+    double tot = 0.0;
+    for (int32_t i = 0; i < V; ++i)
+      if (kept[i]) tot += q[i];
+    const double t = u * tot;
+    double c = 0.0, c_prev = 0.0;
+    for (int32_t i = 0; i < V; ++i) {
+      if (!kept[i]) continue;
+      c_prev = c;
+      c += q[i];
+      token = i;
+      if (c > t) break;
+    }
+    const double gap = fmin(fabs(c - t), fabs(t - c_prev)) / tot;
+    if (gap < ORC_ICDF_MARGIN) flags |= ORC_FLAG_ICDF_MARGIN;
   } else {
     uint64_t seed = a->row_seed ? a->row_seed[r] : (a->deterministic ? 42u : a->seed);
     uint32_t stream = a->row_stream ? a->row_stream[r] : (a->deterministic ? 0u : (uint32_t)r);

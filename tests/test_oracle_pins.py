@@ -225,7 +225,7 @@ def test_topp_margin_flag_on_exact_crossing():
 
 
 # ---------------------------------------------------------------- Gumbel-max distribution
-def _draw_tokens(x, n_draws, chunk=100_000, **kw):
+def _draw_tokens(x, n_draws, chunk=100_000, inverse_cdf=False, **kw):
     V = x.shape[-1]
     counts = np.zeros(V, np.int64)
     for start in range(0, n_draws, chunk):
@@ -234,6 +234,7 @@ def _draw_tokens(x, n_draws, chunk=100_000, **kw):
         o = oracle.step(np.ascontiguousarray(L), want_probs=False, want_logprobs=False,
                         row_seed=np.full(n, 99, np.uint64), row_stream=np.zeros(n, np.uint32),
                         row_offset=np.arange(start, start + n, dtype=np.uint64), n_threads=8,
+                        inverse_cdf=inverse_cdf,
                         **{k: np.broadcast_to(np.asarray(v), (n,)).copy() for k, v in kw.items()})
         assert np.all(o["row_status"] == 0)
         counts += np.bincount(o["token_ids"], minlength=V)
@@ -511,3 +512,61 @@ def test_logprob_modes_match_scipy():
             order = np.lexsort((np.arange(V), -z[r]))[:4]
             np.testing.assert_array_equal(o["top_logprob_ids"][r], order)
             np.testing.assert_array_equal(o["top_logprob_vals"][r], lp[order].astype(np.float32))
+
+
+# ---------------------------------------------------------------- inverse-CDF selection (seeded multinomial)
+def test_icdf_uniform_is_uniform():
+    u = np.array([oracle.icdf_uniform(3, 0, off) for off in range(200_000)])
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert scipy.stats.kstest(u, "uniform").pvalue > 1e-3
+    # 53 bits: the Philox words 0 and 1 of block (0xFFFFFFFF, stream, off_lo, off_hi)
+    w = oracle.philox4x32_10([0xFFFFFFFF, 5, 7, 0], [11, 0])
+    x = (int(w[1]) << 32) | int(w[0])
+    assert oracle.icdf_uniform(11, 5, 7) == (x >> 11) * 2.0 ** -53
+
+
+def test_icdf_token_is_numpy_searchsorted():
+    # the first kept token whose running mass exceeds u * total: numpy's
+    # cumsum and searchsorted over the kept set in index order
+    b = workloads.random_small(50, 24, 700, penalties=False)
+    o = oracle.step(b.logits, temperature=b.temperature, top_k=b.top_k, top_p=b.top_p, min_p=b.min_p,
+                    seed=b.seed, offset=b.offset, inverse_cdf=True)
+    for r in range(24):
+        p = o["probs"][r].astype(np.float64)
+        if o["row_status"][r] != 0 or oracle.normalized_top_k(b.temperature[r], b.top_k[r]) == 1:
+            continue
+        kept = np.flatnonzero(p > 0)
+        z = (b.logits[r] / b.temperature[r]).astype(np.float32).astype(np.float64)
+        q = np.exp(z[kept] - z.max())
+        c = np.cumsum(q)
+        u = oracle.icdf_uniform(b.seed, r, b.offset)
+        j = int(np.searchsorted(c, u * c[-1], side="right"))
+        assert o["token_ids"][r] == kept[j]
+
+
+def test_icdf_matches_categorical_chi2():
+    rng = np.random.default_rng(51)
+    x = (1.5 * rng.standard_normal(40)).astype(np.float32)
+    counts = _draw_tokens(x, 400_000, inverse_cdf=True, temperature=np.float32(1.1))
+    z = (x / np.float32(1.1)).astype(np.float32).astype(np.float64)
+    assert _chi2_pvalue(counts, scipy.special.softmax(z)) > 1e-3
+    counts = _draw_tokens(x, 400_000, inverse_cdf=True, top_k=np.int32(6))
+    order = np.lexsort((np.arange(40), -x.astype(np.float64)))[:6]
+    probs = np.zeros(40)
+    probs[order] = scipy.special.softmax(x[order].astype(np.float64))
+    assert counts[probs == 0].sum() == 0
+    assert _chi2_pvalue(counts, probs) > 1e-3
+
+
+def test_icdf_keeps_argmax_rows_and_outputs():
+    b = workloads.random_small(52, 16, 300, penalties=True)
+    kw = dict(temperature=b.temperature, top_k=b.top_k, top_p=b.top_p, min_p=b.min_p, seed=b.seed,
+              offset=b.offset, repetition_penalty=b.repetition_penalty, presence_penalty=b.presence_penalty,
+              frequency_penalty=b.frequency_penalty, history_ids=b.history_ids, history_start=b.history_start,
+              history_len=b.history_len)
+    g = oracle.step(b.logits, **kw)
+    i = oracle.step(b.logits, inverse_cdf=True, **kw)
+    np.testing.assert_array_equal(g["probs"], i["probs"])
+    np.testing.assert_array_equal(g["logprobs"], i["logprobs"])
+    top1 = np.array([oracle.normalized_top_k(t, k) == 1 for t, k in zip(b.temperature, b.top_k)])
+    np.testing.assert_array_equal(g["token_ids"][top1], i["token_ids"][top1])
