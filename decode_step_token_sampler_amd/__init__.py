@@ -30,6 +30,7 @@ DTYPE_F32, DTYPE_BF16 = 0, 1
 FLAG_DETERMINISTIC = 1 << 0
 FLAG_FORCE_FILTERED = 1 << 1
 FLAG_COOPERATIVE_LAUNCH = 1 << 2
+FLAG_INVERSE_CDF = 1 << 3
 
 # symbols the header declares
 EXPORTS = ("sampler_create", "sampler_step", "sampler_select_path", "sampler_validate", "sampler_destroy",
@@ -207,13 +208,15 @@ class Sampler:
 
     def __init__(self, max_rows: int, max_vocab: int, *, max_history_per_row: int = 4096,
                  max_top_logprobs: int = 32, device: int = 0, deterministic: bool = False,
-                 force_filtered: bool = False, cooperative_launch: bool = False, max_bias_per_row: int = 0):
+                 force_filtered: bool = False, cooperative_launch: bool = False, max_bias_per_row: int = 0,
+                 inverse_cdf: bool = False):
         L = load_library()
         self._L = L
         cfg = Config(max_rows=max_rows, max_vocab=max_vocab, max_history_per_row=max_history_per_row,
                      max_top_logprobs=max_top_logprobs, device=device, max_bias_per_row=max_bias_per_row,
                      flags=(FLAG_DETERMINISTIC if deterministic else 0) | (FLAG_FORCE_FILTERED if force_filtered else 0)
-                           | (FLAG_COOPERATIVE_LAUNCH if cooperative_launch else 0))
+                           | (FLAG_COOPERATIVE_LAUNCH if cooperative_launch else 0)
+                           | (FLAG_INVERSE_CDF if inverse_cdf else 0))
         self.config = cfg
         h = ctypes.c_void_p()
         st = L.sampler_create(ctypes.byref(cfg), ctypes.byref(h))

@@ -152,6 +152,7 @@ struct KernelParams {
   const int32_t *stop_ids;
   int32_t bias_slots;          // LDS bias-hash slots (power of two), 0 without bias
   int32_t lp_mode;             // 0: logprobs of the sampled distribution; 1: untruncated at the row's temperature
+  int32_t icdf;                // select by the seeded inverse CDF instead of Gumbel-max
 };
 
 // Batches of up to kArgRows rows carry their per-row records in the kernel

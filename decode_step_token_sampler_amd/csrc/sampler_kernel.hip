@@ -1009,7 +1009,7 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
 // the slices' max keys (sm.gk; rows that skipped exchange 2 get their
 // status here) and, with Gumbel-max, the best of the slices' best scores
 // (sm.gd) and their indices (sm.gi), ties to the lower index.
-DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, bool gumbel) {
+DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, bool gumbel, bool token_set) {
   unsigned long long mk = 0;
   for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
   const float mx = key_to_float((uint32_t)(mk >> 32));
@@ -1027,7 +1027,8 @@ DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, 
     if (bi != 0x7FFFFFFF) token = bi;
   }
   const bool aborted = atomic_ld(kp.abort_word) == kp.epoch;
-  kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
+  // token_set: the inverse-CDF selection already wrote the token
+  if (!token_set || aborted || status != 0) kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
   if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
 }
 
@@ -1401,7 +1402,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // rows that need the merged max: thresholds, sums or min-p's boundary.
     // The rest (no truncation, no outputs) prune against their own slice's
     // max and settle argmax and status in the final exchange.
-    const bool need_x = need_sel || need_exact || minp;
+    const bool icdf = kp.icdf && !top1 && kp.path != PATH_GREEDY;  // inverse-CDF selection
+    const bool need_x = need_sel || need_exact || minp || icdf;
     double m = (double)mg;
     int argmax_idx = (int)(0xFFFFFFFFu - (uint32_t)lkey);
     uint32_t t_m = 0;
@@ -2193,12 +2195,91 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // with w_i bound > q_i cannot reach it, because E_i >= w_i.  Groups of
     // four that hold a candidate (kept, and within kPruneNats of the max)
     // join a per-wave ring in LDS; Philox runs on full waves of such groups.
-    const bool gumbel = !top1 && kp.path != PATH_GREEDY;
+    const bool gumbel = !top1 && kp.path != PATH_GREEDY && !icdf;
     const float tauf = tau == 0 ? -INFINITY : key_to_float(tau);
     double best_g = -INFINITY;
     int best_i = 0x7FFFFFFF;
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
+
+    // ---- 4b. inverse-CDF selection (the seeded multinomial of [A] "One
+    // request with top_p takes the whole batch off the fast path" and [B]
+    // "What the flag switches"): the first kept token, in index order,
+    // whose running kept mass q = exp(z - m) exceeds u times the kept total.
+    // Each thread sums a contiguous segment of the slice in index order, a
+    // fixed-order scan over threads and one exchange over the slices place
+    // every segment on the row's cumulative axis, and the workgroup whose
+    // range holds u S walks its segments.  (Summation order differs from a
+    // single running sum only by rounding.)
+    if (icdf) {
+      double *cum = reinterpret_cast<double *>(regB);
+      const int segl = (ln + kBlock - 1) / kBlock;
+      const int a0 = min(tid * segl, ln), a1 = min(a0 + segl, ln);
+      double ms = 0.0;
+      int lastk = -1;
+      for (int l = a0; l < a1; ++l) {
+        const float zz = zs[l];
+        if (zz >= tauf && zz > -INFINITY) {
+          ms += exp_nonpos(sm.exp_tab, (double)zz - m);
+          lastk = l;
+        }
+      }
+      const double incl = block_scan_incl(ms, sm.red_d);
+      cum[tid] = incl;
+      if (tid == 0) {
+        sm.bu[38] = 0xFFFFFFFFu;  // first slice position past u S
+        sm.bu[39] = 0u;           // 1 + the slice's last kept position
+      }
+      __syncthreads();
+      const double excl = tid > 0 ? cum[tid - 1] : 0.0;
+      const double Mg = cum[kBlock - 1];
+      if (lastk >= 0) atomicMax(&sm.bu[39], (uint32_t)lastk + 1u);
+      const unsigned p2 = xseq++ & 1u;
+      if (tid == 0) atomic_st(&rc.my->ssum[p2], Mg);
+      row_barrier(sm, rc);
+      if (tid == 0) {
+        // the slices in index order: this slice's range [P_g, P_g+1) and
+        // the total; the last slice with mass also takes u S >= the total
+        double acc = 0.0, pg = 0.0, pg1 = 0.0;
+        int lastg = -1;
+        for (int g = 0; g < G; ++g) {
+          const double mg_ = atomic_ld(&rc.peers[g].ssum[p2]);
+          if (g == gid) pg = acc;
+          acc += mg_;
+          if (g == gid) pg1 = acc;
+          if (mg_ > 0.0) lastg = g;
+        }
+        uint32_t w[4];
+        philox4x32_10(0xFFFFFFFFu, P.stream, off0, off1, key0, key1, w);
+        const double u = (double)((((unsigned long long)w[1] << 32) | w[0]) >> 11) * 0x1p-53;
+        const double t = u * acc;
+        sm.bd[6] = pg;
+        sm.bd[7] = t;
+        sm.bu[36] = (Mg > 0.0 && pg <= t && (t < pg1 || gid == lastg)) ? 1u : 0u;
+      }
+      __syncthreads();
+      if (sm.bu[36]) {
+        const double t = sm.bd[7];
+        double c = sm.bd[6] + excl;
+        if (c <= t) {
+          for (int l = a0; l < a1; ++l) {
+            const float zz = zs[l];
+            if (zz >= tauf && zz > -INFINITY) {
+              c += exp_nonpos(sm.exp_tab, (double)zz - m);
+              if (c > t) {
+                atomicMin(&sm.bu[38], (uint32_t)l);
+                break;
+              }
+            }
+          }
+        }
+        __syncthreads();
+        if (tid == 0) {
+          const uint32_t f = sm.bu[38];
+          kp.token_ids[row] = s0 + (int)(f != 0xFFFFFFFFu ? f : sm.bu[39] - 1u);
+        }
+      }
+    }
     float bound = 0.0f;
     // Groups of four that hold a Gumbel candidate (kept, and within
     // kPruneNats of the max) are listed per wave in LDS (16-bit group
@@ -2308,7 +2389,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           sm.gk[lane] = u64_of(r1.x, r1.y);
         }
         __builtin_amdgcn_wave_barrier();
-        if (lane == 0) finish_row(sm, kp, row, G, gumbel);
+        if (lane == 0) finish_row(sm, kp, row, G, gumbel, icdf);
       }
     };
 
@@ -2475,7 +2556,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           sm.gk[tid] = u64_of(r1.x, r1.y);
         }
         __syncthreads();
-        if (tid == 0) finish_row(sm, kp, row, G, gumbel);
+        if (tid == 0) finish_row(sm, kp, row, G, gumbel, icdf);
         // merge the G local top-logprob lists (keys are distinct: each holds
         // its index): an entry's rank among all entries is its output slot
         unsigned long long *ent = reinterpret_cast<unsigned long long *>(region);

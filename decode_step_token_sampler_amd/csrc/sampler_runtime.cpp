@@ -319,7 +319,8 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
       cfg->max_history_per_row > kMaxHistPerRow || cfg->max_top_logprobs < 0 ||
       cfg->max_top_logprobs > kMaxTopLogprobs || cfg->max_bias_per_row < 0 ||
       cfg->max_bias_per_row > kMaxBiasPerRow ||
-      (cfg->flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH))) {
+      (cfg->flags &
+       ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH | SAMPLER_INVERSE_CDF))) {
     set_msg(g_create_error,
             "bad config: need max_rows >= 1, 1 <= max_vocab <= %d, 0 <= max_history_per_row <= %d, "
             "0 <= max_top_logprobs <= %d, 0 <= max_bias_per_row <= %d and known flags",
@@ -581,6 +582,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   kp.bias_vals = a->bias_vals;
   kp.stop_ids = a->stop_ids;
   kp.lp_mode = a->logprob_mode != SAMPLER_LOGPROB_PROCESSED ? 1 : 0;
+  kp.icdf = (h->cfg.flags & SAMPLER_INVERSE_CDF) ? 1 : 0;
   const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
   const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
   const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);

@@ -77,6 +77,17 @@ typedef enum sampler_dtype {
  * MI355X).  Either way every wait is bounded: a wait that expires marks the
  * step's rows with row_status 3. */
 #define SAMPLER_COOPERATIVE_LAUNCH (1u << 2)
+/* Select tokens by the seeded inverse CDF instead of Gumbel-max (the
+ * "seeded multinomial" of [A] "One request with top_p takes the whole batch
+ * off the fast path", used by the deterministic path of [B] "What the flag
+ * switches"): row r draws one uniform u in [0, 1) (53 bits of the Philox
+ * block at counter (0xFFFFFFFF, stream_r, offset_r lo, offset_r hi) under
+ * key seed_r, words 0 and 1) and takes the first kept token, in index
+ * order, whose running kept mass exceeds u times the kept total.  Rows with
+ * top_k == 1 still take the first argmax; probs and logprobs are
+ * unchanged.  With SAMPLER_DETERMINISTIC the result of a row does not
+ * depend on its batch. */
+#define SAMPLER_INVERSE_CDF (1u << 3)
 
 typedef struct sampler_config {
   int32_t max_rows;            /* largest n_rows a step may pass (>= 1) */
@@ -84,7 +95,8 @@ typedef struct sampler_config {
   int32_t max_history_per_row; /* largest history_len of one row (0..4096) */
   int32_t max_top_logprobs;    /* largest top_logprobs (0..32) */
   int32_t device;              /* HIP device ordinal */
-  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH */
+  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH |
+                                  SAMPLER_INVERSE_CDF */
   int32_t max_bias_per_row;    /* largest bias_len + active stop_len of one row (0..512) */
 } sampler_config;
 

@@ -3,8 +3,9 @@ oracle, and compare them under the parity rules:
 
   token ids     bit-exact, except rows the oracle flags (Gumbel near-tie
                 below 1e-6 relative, top-p crossing within 1e-6 relative of
-                the target mass, min-p boundary within 1e-9): counted and
-                reported, not compared
+                the target mass, min-p boundary within 1e-9, inverse-CDF
+                target within 1e-10 relative of a step of the CDF): counted
+                and reported, not compared
   probs         |gpu - oracle| <= 1e-6 (absolute)
   logprobs      the -inf pattern identical; finite values within 1e-5
   top logprobs  ids identical, values within 1e-5
@@ -20,7 +21,7 @@ import oracle
 
 PROB_TOL = 1e-6
 LOGPROB_TOL = 1e-5
-FLAG_MASK = oracle.FLAG_GUMBEL_NEAR_TIE | oracle.FLAG_TOPP_MARGIN | oracle.FLAG_MINP_MARGIN
+FLAG_MASK = oracle.FLAG_GUMBEL_NEAR_TIE | oracle.FLAG_TOPP_MARGIN | oracle.FLAG_MINP_MARGIN | oracle.FLAG_ICDF_MARGIN
 
 
 def to_device(batch, device="cuda:0"):

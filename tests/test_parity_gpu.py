@@ -339,6 +339,81 @@ def test_deterministic_batch_invariance():
     s.close()
 
 
+# ------------------------------------------------------------ inverse-CDF selection
+@pytest.fixture(scope="module")
+def sampler_icdf():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(512, 262_144, max_history_per_row=2048, max_top_logprobs=32, inverse_cdf=True)
+    yield s
+    s.close()
+
+
+@pytest.mark.parametrize("seed,n,V,dtype", [(61, 12, 3000, "f32"), (62, 9, 70_000, "bf16"), (63, 16, 257, "f32"),
+                                            (64, 5, 131_071, "f32")])
+def test_inverse_cdf_random(sampler_icdf, seed, n, V, dtype):
+    b = workloads.random_small(seed, n, V, dtype, penalties=True)
+    g = run_gpu(sampler_icdf, b)
+    o = run_oracle(b, inverse_cdf=True)
+    r = compare(g, o)
+    print(b.name, r)
+    assert r.ok(), r
+
+
+def test_inverse_cdf_workloads(sampler_icdf):
+    for b in (workloads.config(1), workloads.config(3), workloads.config(4), workloads.config(5)):
+        g = run_gpu(sampler_icdf, b)
+        o = run_oracle(b, inverse_cdf=True)
+        r = compare(g, o)
+        print(b.name, r)
+        assert r.ok(), r
+
+
+def test_inverse_cdf_exact_tokens_over_offsets(sampler_icdf):
+    """10^5 draws of one V=64 row (offsets 0..), token for token against the
+    oracle (whose chi-square against the categorical is pinned)."""
+    import parity
+    rng = np.random.default_rng(65)
+    x = (1.5 * rng.standard_normal(64)).astype(np.float32)
+    n = 500
+    for start in range(0, 100_000, n):
+        L = np.ascontiguousarray(np.broadcast_to(x, (n, 64)))
+        b = workloads.Batch("icdf draws", "f32", L, temperature=np.full(n, 0.9, np.float32),
+                            top_k=np.full(n, -1, np.int32), top_p=np.full(n, 1.0, np.float32),
+                            min_p=np.zeros(n, np.float32), want_probs=False, want_logprobs=False, top_logprobs=0)
+        b.row_seed = np.full(n, 7, np.uint64)
+        b.row_stream = np.zeros(n, np.uint32)
+        b.row_offset = np.arange(start, start + n, dtype=np.uint64)
+        g = run_gpu(sampler_icdf, b)
+        o = run_oracle(b, inverse_cdf=True)
+        ok = (o["flags"] & parity.FLAG_MASK) == 0
+        assert np.array_equal(g["token_ids"][ok], o["token_ids"][ok]), start
+
+
+def test_inverse_cdf_deterministic_batch_invariance():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(32, 100_000, max_history_per_row=256, deterministic=True, inverse_cdf=True)
+    big = workloads.random_small(66, 12, 70_000, "f32", penalties=True, history_len=256)
+    big.row_seed = None
+    big.row_stream = None
+    ref = run_gpu(s, big)
+    o = run_oracle(big, deterministic=True, inverse_cdf=True)
+    r = compare(ref, o)
+    assert r.ok(), r
+    for r_ in (0, 5, 11):
+        for n_before in (0, 3, 7):
+            rows = list(range(n_before)) + [r_]
+            sub = big.subset(rows)
+            sub.row_seed = None
+            sub.row_stream = None
+            sub.row_offset = None
+            g = run_gpu(s, sub)
+            for k in ("token_ids", "probs", "logprobs"):
+                np.testing.assert_array_equal(g[k][-1], ref[k][r_])
+    s.close()
+
+
 def test_gumbel_distribution_chi2_and_exact_tokens():
     _need_gpu()
     import scipy.special
