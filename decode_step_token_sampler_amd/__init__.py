@@ -33,8 +33,8 @@ FLAG_COOPERATIVE_LAUNCH = 1 << 2
 FLAG_INVERSE_CDF = 1 << 3
 
 # symbols the header declares
-EXPORTS = ("sampler_create", "sampler_step", "sampler_select_path", "sampler_validate", "sampler_destroy",
-           "sampler_last_error", "sampler_profile_start", "sampler_profile_stop")
+EXPORTS = ("sampler_create", "sampler_step", "sampler_step_graph", "sampler_select_path", "sampler_validate",
+           "sampler_destroy", "sampler_last_error", "sampler_profile_start", "sampler_profile_stop")
 
 
 class SamplerError(RuntimeError):
@@ -103,6 +103,21 @@ class StepArgs(ctypes.Structure):
 LOGPROB_MODES = {"processed": 0, "temperature": 1, "raw": 2}
 
 
+class DeviceParams(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in (
+        "temperature", "top_p", "min_p", "repetition_penalty", "presence_penalty", "frequency_penalty", "top_k",
+        "history_start", "history_len", "row_seed", "row_offset", "row_stream", "bias_start", "bias_len",
+        "stop_start", "stop_len", "min_tokens", "output_len")]
+
+
+# dtype of each device array of DeviceParams
+DEVICE_PARAM_DTYPES = dict(
+    temperature="float32", top_p="float32", min_p="float32", repetition_penalty="float32",
+    presence_penalty="float32", frequency_penalty="float32", top_k="int32", history_start="int64",
+    history_len="int32", row_seed="int64", row_offset="int64", row_stream="int32", bias_start="int64",
+    bias_len="int32", stop_start="int64", stop_len="int32", min_tokens="int32", output_len="int32")
+
+
 _lib = None
 
 
@@ -119,6 +134,9 @@ def load_library(path: str = LIB_PATH):
     L.sampler_create.restype = ctypes.c_int
     L.sampler_step.argtypes = [ctypes.c_void_p, ctypes.POINTER(StepArgs), ctypes.c_void_p]
     L.sampler_step.restype = ctypes.c_int
+    L.sampler_step_graph.argtypes = [ctypes.c_void_p, ctypes.POINTER(StepArgs), ctypes.POINTER(DeviceParams),
+                                     ctypes.c_void_p]
+    L.sampler_step_graph.restype = ctypes.c_int
     L.sampler_select_path.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_uint32, ctypes.POINTER(ctypes.c_int32)]
     L.sampler_select_path.restype = ctypes.c_int
     L.sampler_validate.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(StepArgs), ctypes.c_char_p, ctypes.c_int32]
@@ -339,3 +357,56 @@ class Sampler:
             raise SamplerError(st, self.last_error())
         o["path"] = PATH_NAMES[path.value]
         return o
+
+    def step_graph(self, logits, params: dict, *, vocab: Optional[int] = None, history_ids=None, seed: int = 0,
+                   offset: int = 0, out: dict, top_logprobs: int = 0, vocab_mask=None, bias_ids=None,
+                   bias_vals=None, stop_ids=None, logprob_mode: str = "processed", stream=None) -> None:
+        """Enqueue one step whose per-row parameters are CUDA tensors (``params``:
+        names of DeviceParams -> tensors of DEVICE_PARAM_DTYPES, n_rows entries
+        each; missing names take the defaults).  Outputs go to the tensors of
+        ``out`` (token_ids required; probs, logprobs, top_logprob_vals /
+        top_logprob_ids, row_status optional), so the call can be captured
+        into a graph and replayed after the parameter tensors are updated in
+        place."""
+        import torch
+        if logits.dim() != 2 or logits.stride(1) != 1:
+            raise ValueError("logits must be 2-D with unit column stride")
+        dt = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16}.get(logits.dtype)
+        if dt is None:
+            raise ValueError("logits must be float32 or bfloat16")
+        n = logits.shape[0]
+        dp = DeviceParams()
+        for name, t in params.items():
+            if name not in DEVICE_PARAM_DTYPES:
+                raise ValueError(f"unknown device parameter {name}")
+            want = getattr(torch, DEVICE_PARAM_DTYPES[name])
+            if t.dtype != want or t.dim() != 1 or t.shape[0] != n or not t.is_contiguous() or not t.is_cuda:
+                raise ValueError(f"{name} must be a contiguous CUDA {want} tensor of {n} entries")
+            setattr(dp, name, t.data_ptr())
+        a = StepArgs()
+        a.logits = logits.data_ptr()
+        a.dtype = dt
+        a.n_rows = n
+        a.vocab = logits.shape[1] if vocab is None else int(vocab)
+        a.row_stride = logits.stride(0)
+        a.history_ids = None if history_ids is None else history_ids.data_ptr()
+        a.bias_ids = None if bias_ids is None else bias_ids.data_ptr()
+        a.bias_vals = None if bias_vals is None else bias_vals.data_ptr()
+        a.stop_ids = None if stop_ids is None else stop_ids.data_ptr()
+        if vocab_mask is not None:
+            a.vocab_mask = vocab_mask.data_ptr()
+            a.mask_stride = vocab_mask.stride(0)
+        a.seed = int(seed) & (2**64 - 1)
+        a.offset = int(offset) & (2**64 - 1)
+        a.token_ids = out["token_ids"].data_ptr()
+        a.probs = out["probs"].data_ptr() if "probs" in out else None
+        a.logprobs = out["logprobs"].data_ptr() if "logprobs" in out else None
+        a.top_logprobs = int(top_logprobs)
+        a.top_logprob_vals = out["top_logprob_vals"].data_ptr() if top_logprobs else None
+        a.top_logprob_ids = out["top_logprob_ids"].data_ptr() if top_logprobs else None
+        a.row_status = out["row_status"].data_ptr() if "row_status" in out else None
+        a.logprob_mode = LOGPROB_MODES[logprob_mode]
+        s = torch.cuda.current_stream(logits.device).cuda_stream if stream is None else int(stream)
+        st = self._L.sampler_step_graph(self._h, ctypes.byref(a), ctypes.byref(dp), ctypes.c_void_p(s))
+        if st != SAMPLER_OK:
+            raise SamplerError(st, self.last_error())

@@ -56,6 +56,7 @@ enum : uint32_t {
   RF_TOPP = 1u << 4,    // top_p < 1
   RF_MINP = 1u << 5,    // min_p > 0
   RF_SPEC = 1u << 6,    // the row has logit_bias entries or active stop ids
+  RF_BAD = 1u << 7,     // device-side parameters broke the rules (status 4); no other flag
 };
 
 // One row's parameters as the kernel reads them (96 bytes).
@@ -120,6 +121,22 @@ static_assert(offsetof(WgSlots, x1) % 16 == 0 && offsetof(WgSlots, fin) % 16 == 
 
 enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINISTIC = 3 };
 
+// Per-row parameters in device memory (one entry per row, or null for the
+// default), normalised by the kernel itself.
+struct DevRowArrays {
+  const float *temperature, *top_p, *min_p, *rep, *pres, *freq;
+  const int32_t *top_k;
+  const int64_t *hist_start;
+  const int32_t *hist_len;
+  const uint64_t *seed, *offset;
+  const uint32_t *stream;
+  const int64_t *bias_start;
+  const int32_t *bias_len;
+  const int64_t *stop_start;
+  const int32_t *stop_len;
+  const int32_t *min_tokens, *output_len;
+};
+
 struct KernelParams {
   const void *logits;
   int64_t row_stride;
@@ -153,6 +170,12 @@ struct KernelParams {
   int32_t bias_slots;          // LDS bias-hash slots (power of two), 0 without bias
   int32_t lp_mode;             // 0: logprobs of the sampled distribution; 1: untruncated at the row's temperature
   int32_t icdf;                // select by the seeded inverse CDF instead of Gumbel-max
+  // rows from device arrays (rows_kernel): the defaults and the limits they
+  // are checked against
+  int32_t det;                 // deterministic handle: default seed 42, stream 0
+  int32_t max_hist, max_bias;
+  uint64_t seed, offset;
+  DevRowArrays dev;
 };
 
 // Batches of up to kArgRows rows carry their per-row records in the kernel
@@ -164,6 +187,9 @@ struct KernelArgs {
   RowParam rows[kArgRows];  // used when kp.rows is null
 };
 
+// Normalise the per-row device arrays of kp.dev into records at `out`
+// (one thread per row).
+hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream);
 // Launch one step.  The grid never exceeds the workgroups the device holds at
 // once; `cooperative` launches through hipLaunchCooperativeKernel, which
 // also has the runtime check that they are all resident.

@@ -1032,6 +1032,79 @@ DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, 
   if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
 }
 
+// A row's record from per-row arrays in device memory, normalised and
+// checked with the rules the host applies to host arrays ([A] "One request
+// with top_p takes the whole batch off the fast path": 0 <= T < 1e-6 is
+// greedy, T := 1, top_k := 1; -1 means the whole vocabulary).  bad is set
+// when a value breaks them.
+DEV RowParam row_from_device(const KernelParams &kp, int r) {
+  const DevRowArrays &d = kp.dev;
+  const int V = kp.vocab;
+  const float t = d.temperature ? d.temperature[r] : 1.0f;
+  const float top_p = d.top_p ? d.top_p[r] : 1.0f;
+  const float min_p = d.min_p ? d.min_p[r] : 0.0f;
+  const float rep = d.rep ? d.rep[r] : 1.0f;
+  const float pres = d.pres ? d.pres[r] : 0.0f;
+  const float freq = d.freq ? d.freq[r] : 0.0f;
+  int32_t k = d.top_k ? d.top_k[r] : -1;
+  const int32_t hl = d.hist_len ? d.hist_len[r] : 0;
+  const int64_t hs = d.hist_start ? d.hist_start[r] : 0;
+  const int32_t bl = d.bias_len ? d.bias_len[r] : 0;
+  const int64_t bs = d.bias_start ? d.bias_start[r] : 0;
+  const bool stop_on = d.min_tokens && d.output_len && d.output_len[r] < d.min_tokens[r];
+  const int32_t sl = (stop_on && d.stop_len) ? d.stop_len[r] : 0;
+  const int64_t ss = d.stop_start ? d.stop_start[r] : 0;
+  const bool bad = !(t >= 0.0f && __builtin_isfinite(t)) || !(top_p > 0.0f && top_p <= 1.0f) || !(k == -1 || k >= 1) ||
+        !(min_p >= 0.0f && min_p <= 1.0f) || !(rep > 0.0f && __builtin_isfinite(rep)) ||
+        !__builtin_isfinite(pres) || !__builtin_isfinite(freq) || hl < 0 || hl > kp.max_hist ||
+        (hl > 0 && (hs < 0 || !kp.history_ids)) || bl < 0 || sl < 0 ||
+        (bl > 0 && (bs < 0 || !kp.bias_ids || !kp.bias_vals)) || (sl > 0 && (ss < 0 || !kp.stop_ids)) ||
+        (int64_t)bl + sl > kp.max_bias;
+  const bool greedy = t >= 0.0f && (double)t < 1e-6;
+  if (greedy) k = 1;
+  RowParam p;
+  p.temperature = greedy ? 1.0f : t;
+  p.top_p = top_p;
+  p.min_p = min_p;
+  p.rep = rep;
+  p.pres = pres;
+  p.freq = freq;
+  p.top_k = (k == -1 || k >= V) ? V : k;
+  uint32_t f = 0;
+  if (greedy) f |= RF_GREEDY | RF_TOP1;
+  else {
+    if (k == 1) f |= RF_TOP1 | RF_TOPK;
+    else if (k != -1 && k < V) f |= RF_TOPK;
+    if (top_p < 1.0f) f |= RF_TOPP;
+    if (min_p > 0.0f) f |= RF_MINP;
+  }
+  p.hist_start = 0;
+  p.hist_len = 0;
+  if ((rep != 1.0f || pres != 0.0f || freq != 0.0f) && hl > 0) {
+    f |= RF_PEN;
+    p.hist_start = hs;
+    p.hist_len = hl;
+  }
+  p.bias_start = bl > 0 ? bs : 0;
+  p.bias_len = bl > 0 ? bl : 0;
+  p.stop_start = sl > 0 ? ss : 0;
+  p.stop_len = sl > 0 ? sl : 0;
+  if (p.bias_len + p.stop_len > 0) f |= RF_SPEC;
+  p.flags = bad ? RF_BAD : f;
+  p.seed = d.seed ? d.seed[r] : (kp.det ? 42ull : kp.seed);
+  p.stream = d.stream ? d.stream[r] : (kp.det ? 0u : (uint32_t)r);
+  p.offset = d.offset ? d.offset[r] : kp.offset;
+  p.pad[0] = p.pad[1] = 0;
+  return p;
+}
+
+// One thread per row: the records of a step whose per-row parameters live
+// in device memory (the row kernel then reads them like copied records).
+__global__ __launch_bounds__(256) void rows_kernel(KernelParams kp, RowParam *out) {
+  const int r = blockIdx.x * blockDim.x + threadIdx.x;
+  if (r < kp.n_rows) out[r] = row_from_device(kp, r);
+}
+
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
 __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
@@ -1122,6 +1195,24 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     if (tid == 0) sm.bu[37] = 0u;  // waves done with Gumbel-max (end of the row)
 
     const RowParam P = kp.rows ? kp.rows[row] : ka.rows[row];
+    if (P.flags & RF_BAD) {
+      // device-side parameters that break the rules: status 4
+      if (want_out)
+        for (int l = tid; l < ln; l += kBlock) {
+          if (kp.probs) kp.probs[(int64_t)row * V + s0 + l] = 0.0f;
+          if (kp.logprobs) kp.logprobs[(int64_t)row * V + s0 + l] = -INFINITY;
+        }
+      if (gid == 0 && tid == 0) {
+        kp.token_ids[row] = -1;
+        if (kp.row_status) kp.row_status[row] = 4;
+        for (int t = 0; t < K; ++t) {
+          kp.top_lp_vals[(int64_t)row * K + t] = -INFINITY;
+          kp.top_lp_ids[(int64_t)row * K + t] = -1;
+        }
+      }
+      __syncthreads();
+      continue;
+    }
     const bool greedy = P.flags & RF_GREEDY;
     const bool top1 = P.flags & RF_TOP1;
     const bool pen = PEN && (P.flags & RF_PEN);
@@ -2628,6 +2719,11 @@ size_t kernel_lds_region(int slice, int hash_slots, int bias_slots, bool penalti
 size_t kernel_lds_bytes(int slice, int hash_slots, int bias_slots, bool penalties) {
   return kernel_lds_fixed() + sizeof(float) * (size_t)slice +
          kernel_lds_region(slice, hash_slots, bias_slots, penalties);
+}
+
+hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream) {
+  hipLaunchKernelGGL(rows_kernel, dim3((kp.n_rows + 255) / 256), dim3(256), 0, stream, kp, out);
+  return hipGetLastError();
 }
 
 hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream) {

@@ -58,6 +58,7 @@ struct sampler_handle {
   RowParam *host_ring = nullptr;   // pinned, kRing slots of max_rows records
   RowParam *dev_ring = nullptr;    // device, kRing slots
   KernelArgs *args = nullptr;      // host: the launch's argument block
+  RowParam *graph_rows = nullptr;  // device, max_rows records written by sampler_step_graph's first kernel
   hipEvent_t slot_done[kRing] = {};
   bool slot_used[kRing] = {};
   int next_slot = 0;
@@ -294,11 +295,104 @@ void free_handle(sampler_handle *h) {
     }
   if (h->host_ring) (void)hipHostFree(h->host_ring);
   if (h->dev_ring) (void)hipFree(h->dev_ring);
+  if (h->graph_rows) (void)hipFree(h->graph_rows);
   delete h->args;
   if (h->sync) (void)hipFree(h->sync);
   if (h->slots) (void)hipFree(h->slots);
   if (h->abort_word) (void)hipFree(h->abort_word);
   delete h;
+}
+
+}  // namespace
+
+namespace {
+
+// Launch plan (G workgroups per row, rows strided over groups), the kernel
+// parameters and the launch, shared by both step entry points.  `dp`: the
+// device records, or null (records in ka.rows); `dev`: per-row arrays in
+// device memory that the kernel normalises itself (sampler_step_graph).
+sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, KernelArgs &ka, const RowParam *dp,
+                               bool any_pen, int path, hipStream_t stream, const DevRowArrays *dev = nullptr) {
+  const int n = a->n_rows, V = a->vocab;
+  const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
+  hipError_t e;
+  const int g_min = (V + h->slice_cap - 1) / h->slice_cap;
+  if (g_min > kMaxG || g_min > h->resident) {
+    set_msg(h->err, "vocab %d needs %d workgroups per row (max %d)", V, g_min,
+            kMaxG < h->resident ? kMaxG : h->resident);
+    return SAMPLER_ECAPACITY;
+  }
+  int G;
+  if (det) {
+    G = g_min;  // depends on V only: a row's reduction order is batch invariant
+  } else {
+    const int fill = h->resident / n;
+    const int by_work = (V + 4 * kBlock - 1) / (4 * kBlock);  // at least ~4 values per thread
+    G = fill < by_work ? fill : by_work;
+    if (G > kMaxG) G = kMaxG;
+    if (G > h->resident) G = h->resident;
+    if (G < g_min) G = g_min;
+  }
+  int slice = (V + G - 1) / G;
+  slice = (slice + 3) & ~3;
+  G = (V + slice - 1) / slice;  // every workgroup gets a non-empty slice
+  KernelParams &kp = ka.kp;
+  kp = KernelParams{};
+  kp.logits = a->logits;
+  kp.row_stride = a->row_stride;
+  kp.n_rows = n;
+  kp.vocab = V;
+  kp.rows = dp;
+  kp.history_ids = a->history_ids;
+  kp.token_ids = a->token_ids;
+  kp.probs = a->probs;
+  kp.logprobs = a->logprobs;
+  kp.top_lp = a->top_logprobs;
+  kp.top_lp_vals = a->top_logprob_vals;
+  kp.top_lp_ids = a->top_logprob_ids;
+  kp.row_status = a->row_status;
+  kp.G = G;
+  const int groups = h->resident / G;
+  kp.n_groups = groups < n ? groups : n;
+  kp.slice = slice;
+  kp.hash_slots = h->hash_slots;
+  kp.bias_slots = h->bias_slots;
+  kp.vocab_mask = a->vocab_mask;
+  kp.mask_stride = a->mask_stride;
+  kp.bias_ids = a->bias_ids;
+  kp.bias_vals = a->bias_vals;
+  kp.stop_ids = a->stop_ids;
+  kp.lp_mode = a->logprob_mode != SAMPLER_LOGPROB_PROCESSED ? 1 : 0;
+  kp.icdf = (h->cfg.flags & SAMPLER_INVERSE_CDF) ? 1 : 0;
+  if (dev) {
+    kp.dev = *dev;
+    kp.rows = h->graph_rows;
+  }
+  kp.det = det ? 1 : 0;
+  kp.max_hist = h->cfg.max_history_per_row;
+  kp.max_bias = h->cfg.max_bias_per_row;
+  kp.seed = a->seed;
+  kp.offset = a->offset;
+  const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
+  const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
+  const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);
+  kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0);
+  kp.path = path;
+  kp.sync = h->sync;
+  kp.slots = h->slots;
+  kp.abort_word = h->abort_word;
+  if (++h->epoch == 0) h->epoch = 1;
+  kp.epoch = h->epoch;
+  if (dev && (e = launch_rows(kp, h->graph_rows, stream)) != hipSuccess) return hip_fail(h, e, "rows kernel launch");
+  const bool prof = h->prof_n < h->prof_cap;
+  if (prof && (e = hipEventRecord(h->prof[2 * h->prof_n], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+  e = launch_step(ka, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream);
+  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
+  if (prof) {
+    if ((e = hipEventRecord(h->prof[2 * h->prof_n + 1], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    ++h->prof_n;
+  }
+  return SAMPLER_OK;
 }
 
 }  // namespace
@@ -394,6 +488,7 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     const size_t ring_bytes = sizeof(RowParam) * (size_t)cfg->max_rows * kRing;
     if ((e = hipHostMalloc((void **)&h->host_ring, ring_bytes, hipHostMallocDefault)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&h->dev_ring, ring_bytes)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&h->graph_rows, sizeof(RowParam) * (size_t)cfg->max_rows)) != hipSuccess) goto fail;
     h->args = new (std::nothrow) KernelArgs();
     if (!h->args) {
       g_create_error = "out of host memory";
@@ -534,74 +629,66 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
     h->slot_used[slot] = true;
   }
 
-  // ---- launch plan: G workgroups per row, rows strided over groups
-  const int g_min = (V + h->slice_cap - 1) / h->slice_cap;
-  if (g_min > kMaxG || g_min > h->resident) {
-    set_msg(h->err, "vocab %d needs %d workgroups per row (max %d)", V, g_min,
-            kMaxG < h->resident ? kMaxG : h->resident);
-    return SAMPLER_ECAPACITY;
+  return plan_and_launch(h, a, ka, dp, any_pen, path, stream);
+}
+
+sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a, const sampler_device_params *dp,
+                                  void *stream_ptr) {
+  if (!h) return SAMPLER_EINVAL;
+  h->err.clear();
+  if (!a || !dp) {
+    h->err = !a ? "args is NULL" : "device params are NULL";
+    return SAMPLER_EINVAL;
   }
-  int G;
-  if (det) {
-    G = g_min;  // depends on V only: a row's reduction order is batch invariant
-  } else {
-    const int fill = h->resident / n;
-    const int by_work = (V + 4 * kBlock - 1) / (4 * kBlock);  // at least ~4 values per thread
-    G = fill < by_work ? fill : by_work;
-    if (G > kMaxG) G = kMaxG;
-    if (G > h->resident) G = h->resident;
-    if (G < g_min) G = g_min;
+  if (a->temperature || a->top_p || a->min_p || a->repetition_penalty || a->presence_penalty ||
+      a->frequency_penalty || a->top_k || a->history_start || a->history_len || a->row_seed || a->row_offset ||
+      a->row_stream || a->bias_start || a->bias_len || a->stop_start || a->stop_len || a->min_tokens ||
+      a->output_len) {
+    h->err = "sampler_step_graph takes its per-row parameters from the device params: the host arrays of args "
+             "must be NULL";
+    return SAMPLER_EINVAL;
   }
-  int slice = (V + G - 1) / G;
-  slice = (slice + 3) & ~3;
-  G = (V + slice - 1) / slice;  // every workgroup gets a non-empty slice
-  KernelParams &kp = ka.kp;
-  kp = KernelParams{};
-  kp.logits = a->logits;
-  kp.row_stride = a->row_stride;
-  kp.n_rows = n;
-  kp.vocab = V;
-  kp.rows = dp;
-  kp.history_ids = a->history_ids;
-  kp.token_ids = a->token_ids;
-  kp.probs = a->probs;
-  kp.logprobs = a->logprobs;
-  kp.top_lp = a->top_logprobs;
-  kp.top_lp_vals = a->top_logprob_vals;
-  kp.top_lp_ids = a->top_logprob_ids;
-  kp.row_status = a->row_status;
-  kp.G = G;
-  const int groups = h->resident / G;
-  kp.n_groups = groups < n ? groups : n;
-  kp.slice = slice;
-  kp.hash_slots = h->hash_slots;
-  kp.bias_slots = h->bias_slots;
-  kp.vocab_mask = a->vocab_mask;
-  kp.mask_stride = a->mask_stride;
-  kp.bias_ids = a->bias_ids;
-  kp.bias_vals = a->bias_vals;
-  kp.stop_ids = a->stop_ids;
-  kp.lp_mode = a->logprob_mode != SAMPLER_LOGPROB_PROCESSED ? 1 : 0;
-  kp.icdf = (h->cfg.flags & SAMPLER_INVERSE_CDF) ? 1 : 0;
-  const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
-  const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
-  const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);
-  kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0);
-  kp.path = path;
-  kp.sync = h->sync;
-  kp.slots = h->slots;
-  kp.abort_word = h->abort_word;
-  if (++h->epoch == 0) h->epoch = 1;
-  kp.epoch = h->epoch;
-  const bool prof = h->prof_n < h->prof_cap;
-  if (prof && (e = hipEventRecord(h->prof[2 * h->prof_n], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  e = launch_step(ka, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream);
-  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
-  if (prof) {
-    if ((e = hipEventRecord(h->prof[2 * h->prof_n + 1], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-    ++h->prof_n;
+  if ((dp->min_tokens != nullptr) != (dp->output_len != nullptr)) {
+    h->err = "min_tokens and output_len go together";
+    return SAMPLER_EINVAL;
   }
-  return SAMPLER_OK;
+  if (a->logprob_mode == SAMPLER_LOGPROB_RAW) {
+    h->err = "the raw logprob mode needs host temperatures (sampler_step)";
+    return SAMPLER_ENOTSUP;
+  }
+  // the host checks of sizes, pointers and modes (per-row values are
+  // checked on the device)
+  sampler_status st = validate(&h->cfg, a, h->err);
+  if (st != SAMPLER_OK) return st;
+  DeviceGuard guard(h->device);
+  if (!guard.ok) {
+    h->err = "hipSetDevice failed";
+    return SAMPLER_EHIP;
+  }
+  if (a->path_out) *a->path_out = PATH_FILTERED;
+  DevRowArrays dev;
+  dev.temperature = dp->temperature;
+  dev.top_p = dp->top_p;
+  dev.min_p = dp->min_p;
+  dev.rep = dp->repetition_penalty;
+  dev.pres = dp->presence_penalty;
+  dev.freq = dp->frequency_penalty;
+  dev.top_k = dp->top_k;
+  dev.hist_start = dp->history_start;
+  dev.hist_len = dp->history_len;
+  dev.seed = dp->row_seed;
+  dev.offset = dp->row_offset;
+  dev.stream = dp->row_stream;
+  dev.bias_start = dp->bias_start;
+  dev.bias_len = dp->bias_len;
+  dev.stop_start = dp->stop_start;
+  dev.stop_len = dp->stop_len;
+  dev.min_tokens = dp->min_tokens;
+  dev.output_len = dp->output_len;
+  // the penalty / bias machinery whenever a row could use it
+  const bool any_pen = (dp->history_len && a->history_ids) || dp->bias_len || (dp->min_tokens && dp->stop_len);
+  return plan_and_launch(h, a, *h->args, nullptr, any_pen, PATH_FILTERED, reinterpret_cast<hipStream_t>(stream_ptr),
+                         &dev);
 }
 
 sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity) {

@@ -163,7 +163,8 @@ typedef struct sampler_step_args {
    * [n_rows] or NULL; 0 ok, 1 no finite logit (all -inf/NaN after
    * sanitising NaN to -inf), 2 a +inf value after temperature, 3 the
    * step's cross-workgroup wait timed out (an internal error; the row's
-   * outputs are not valid). */
+   * outputs are not valid), 4 the row's device-side parameters broke the
+   * rules (sampler_step_graph only). */
   int32_t *token_ids;
   float *probs;
   float *logprobs;
@@ -242,6 +243,58 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out);
  * still in flight (batches of up to 96 rows pass their per-row records in
  * the kernel arguments and use no staging slot).  Outputs are valid when the stream reaches this point. */
 sampler_status sampler_step(sampler_handle *h, const sampler_step_args *args, void *stream);
+
+/* Per-row parameters in device memory, for sampler_step_graph.  Each array
+ * has n_rows entries in device memory of the handle's GPU, or is NULL (the
+ * default for every row, as in sampler_step_args).  Their meaning is that of
+ * the host arrays of the same names in sampler_step_args. */
+typedef struct sampler_device_params {
+  const float *temperature;
+  const float *top_p;
+  const float *min_p;
+  const float *repetition_penalty;
+  const float *presence_penalty;
+  const float *frequency_penalty;
+  const int32_t *top_k;
+  const int64_t *history_start;
+  const int32_t *history_len;
+  const uint64_t *row_seed;
+  const uint64_t *row_offset;
+  const uint32_t *row_stream;
+  const int64_t *bias_start;
+  const int32_t *bias_len;
+  const int64_t *stop_start;
+  const int32_t *stop_len;
+  const int32_t *min_tokens;
+  const int32_t *output_len;
+} sampler_device_params;
+
+/* One decode step whose per-row parameters live in device memory, so that a
+ * caller can capture the call into a HIP graph once per (n_rows, vocab)
+ * bucket and replay it after updating those arrays (offsets, temperatures,
+ * histories...) in place -- the launch-bound batch-1 decode loop ([A] "What
+ * a free T4 can and cannot tell you": the sampler's host overhead is the
+ * cost at batch 1).  The call enqueues two kernels and nothing else (one
+ * normalises the rows' parameters into a record buffer of the handle, the
+ * other samples; no copy, no memset, no event unless profiling is on); it
+ * allocates nothing; the workspace addresses are fixed by the handle.
+ *   args: as for sampler_step, except that its per-row host arrays
+ *     (temperature .. top_k, history_start / history_len, row_seed /
+ *     row_offset / row_stream, bias_start / bias_len, stop_start / stop_len,
+ *     min_tokens / output_len) must be NULL: dp carries them.  args->seed
+ *     and args->offset are the defaults of rows without row_seed /
+ *     row_offset (and are frozen into a captured graph).  path_out, when
+ *     given, receives SAMPLER_PATH_FILTERED: the kernel decides each row's
+ *     treatment from its parameters on the device.
+ *   dp: device pointers (the struct itself is read before the call
+ *     returns).
+ * Each row's parameters are normalised and checked on the device with the
+ * rules of sampler_step; a row that breaks them gets row_status 4, token -1,
+ * probs 0 and logprobs -inf, and the other rows are unaffected.  Results
+ * equal those of sampler_step with the same values.  Replays of one
+ * captured step must not overlap each other or other steps of the handle. */
+sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *args, const sampler_device_params *dp,
+                                  void *stream);
 
 /* The batch predicate alone ([A] "One request with top_p takes the whole
  * batch off the fast path": normalize, then is_all_greedy / need_top_p /

@@ -414,6 +414,113 @@ def test_inverse_cdf_deterministic_batch_invariance():
     s.close()
 
 
+# ------------------------------------------------------------ device parameters and graph capture
+def _device_params(b):
+    def dev(a, dt):
+        return torch.from_numpy(np.ascontiguousarray(a).view(dt)).to("cuda:0")
+    p = dict(temperature=dev(b.temperature, np.float32), top_p=dev(b.top_p, np.float32),
+             top_k=dev(b.top_k, np.int32), min_p=dev(b.min_p, np.float32))
+    if b.repetition_penalty is not None:
+        p.update(repetition_penalty=dev(b.repetition_penalty, np.float32),
+                 presence_penalty=dev(b.presence_penalty, np.float32),
+                 frequency_penalty=dev(b.frequency_penalty, np.float32),
+                 history_start=dev(b.history_start, np.int64), history_len=dev(b.history_len, np.int32))
+    n = b.n_rows
+    rs = b.row_seed if b.row_seed is not None else np.full(n, b.seed, np.uint64)
+    ro = b.row_offset if b.row_offset is not None else np.full(n, b.offset, np.uint64)
+    rst = b.row_stream if b.row_stream is not None else np.arange(n, dtype=np.uint32)
+    p.update(row_seed=dev(rs.astype(np.uint64), np.int64), row_offset=dev(ro.astype(np.uint64), np.int64),
+             row_stream=dev(rst.astype(np.uint32), np.int32))
+    return p
+
+
+def _outputs(n, V, K):
+    d = "cuda:0"
+    return dict(token_ids=torch.empty(n, dtype=torch.int32, device=d), probs=torch.empty(n, V, device=d),
+                logprobs=torch.empty(n, V, device=d), top_logprob_vals=torch.empty(n, K, device=d),
+                top_logprob_ids=torch.empty(n, K, dtype=torch.int32, device=d),
+                row_status=torch.empty(n, dtype=torch.int32, device=d))
+
+
+def _host(out):
+    return {k: v.cpu().numpy() for k, v in out.items()}
+
+
+def test_step_graph_eager_matches_host_step(sampler):
+    b = workloads.random_small(70, 14, 30_000, "bf16", penalties=True, history_len=200)
+    L, H = to_device(b)
+    out = _outputs(b.n_rows, b.vocab, b.top_logprobs)
+    sampler.step_graph(L, _device_params(b), history_ids=H, out=out, top_logprobs=b.top_logprobs)
+    torch.cuda.synchronize()
+    g = _host(out)
+    h = run_gpu(sampler, b, logits=L, history=H)
+    for k in ("token_ids", "probs", "logprobs", "top_logprob_ids", "top_logprob_vals", "row_status"):
+        np.testing.assert_array_equal(g[k], h[k])
+    r = compare(g, run_oracle(b))
+    assert r.ok(), r
+
+
+def test_step_graph_bad_rows_get_status_4(sampler):
+    b = workloads.random_small(71, 8, 4000, "f32", penalties=True)
+    b.temperature[1] = -1.0
+    b.top_p[3] = 0.0
+    b.top_k[5] = 0
+    b.history_len[6] = 4000             # beyond max_history_per_row
+    L, H = to_device(b)
+    out = _outputs(b.n_rows, b.vocab, b.top_logprobs)
+    sampler.step_graph(L, _device_params(b), history_ids=H, out=out, top_logprobs=b.top_logprobs)
+    torch.cuda.synchronize()
+    g = _host(out)
+    bad = [1, 3, 5, 6]
+    assert g["row_status"][bad].tolist() == [4, 4, 4, 4]
+    assert np.all(g["token_ids"][bad] == -1) and np.all(g["probs"][bad] == 0)
+    assert np.all(np.isneginf(g["logprobs"][bad])) and np.all(g["top_logprob_ids"][bad] == -1)
+    good = [0, 2, 4, 7]
+    r = compare(g, run_oracle(b.subset(good)), rows=good)
+    assert r.ok(), r
+
+
+def test_step_graph_capture_and_replay():
+    """Capture one step into a graph, then replay it after updating the
+    logits and the per-row parameters in place (a decode loop), with eager
+    steps and synchronisations between the replays; every replay equals the
+    eager host-path step on the same inputs and the oracle."""
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(32, 70_000, max_history_per_row=256, max_top_logprobs=8)
+    batches = [workloads.random_small(80 + i, 12, 60_000, "f32", penalties=True, history_len=256) for i in range(4)]
+    for bb in batches[1:]:                    # one history buffer layout for all replays
+        bb.history_ids = batches[0].history_ids
+        bb.history_start = batches[0].history_start
+    b0 = batches[0]
+    L, H = to_device(b0)
+    params = _device_params(b0)
+    out = _outputs(b0.n_rows, b0.vocab, b0.top_logprobs)
+    s.step_graph(L, params, history_ids=H, out=out, top_logprobs=b0.top_logprobs)   # warm-up
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s.step_graph(L, params, history_ids=H, out=out, top_logprobs=b0.top_logprobs)
+    torch.cuda.synchronize()
+    for step, b in enumerate(batches):
+        b.offset = 1000 + step
+        b.row_offset = None
+        Ln, _ = to_device(b)
+        L.copy_(Ln)
+        for k, v in _device_params(b).items():
+            params[k].copy_(v)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        g = _host(out)
+        e = run_gpu(s, b, logits=L, history=H)    # eager host path between replays
+        for k in ("token_ids", "probs", "logprobs", "top_logprob_ids", "top_logprob_vals", "row_status"):
+            np.testing.assert_array_equal(g[k], e[k], err_msg=f"replay {step} {k}")
+        r = compare(g, run_oracle(b))
+        assert r.ok(), (step, r)
+    s.close()
+
+
 def test_gumbel_distribution_chi2_and_exact_tokens():
     _need_gpu()
     import scipy.special
