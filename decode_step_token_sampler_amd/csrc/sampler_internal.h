@@ -78,7 +78,8 @@ struct alignas(16) RowParam {
   int64_t stop_start;  // stop-id span, counted only while min_tokens is active
   int32_t bias_len;
   int32_t stop_len;    // 0 when min_tokens is not active
-  uint32_t pad[2];
+  int32_t row;         // the batch row this record describes (records may be reordered)
+  uint32_t pad;
 };
 static_assert(sizeof(RowParam) == 96, "RowParam layout");
 

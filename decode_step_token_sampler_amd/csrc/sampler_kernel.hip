@@ -1094,7 +1094,8 @@ DEV RowParam row_from_device(const KernelParams &kp, int r) {
   p.seed = d.seed ? d.seed[r] : (kp.det ? 42ull : kp.seed);
   p.stream = d.stream ? d.stream[r] : (kp.det ? 0u : (uint32_t)r);
   p.offset = d.offset ? d.offset[r] : kp.offset;
-  p.pad[0] = p.pad[1] = 0;
+  p.row = r;
+  p.pad = 0;
   return p;
 }
 
@@ -1180,8 +1181,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   __syncthreads();
 
   unsigned it = 0;
-  for (int row = group; row < kp.n_rows; row += kp.n_groups, ++it) {
-    rc.row = row;
+  // Record ri describes batch row rows[ri].row: the host puts the rows it
+  // expects to take longest on the groups whose workgroups are dispatched
+  // first.
+  for (int ri = group; ri < kp.n_rows; ri += kp.n_groups, ++it) {
     // the slice bounds, opaque per row: keeps per-element offsets and
     // compares from being hoisted out of the row loop (they would stay
     // live across it)
@@ -1194,7 +1197,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const int lane = tid & 63, wave = tid >> 6;
     if (tid == 0) sm.bu[37] = 0u;  // waves done with Gumbel-max (end of the row)
 
-    const RowParam P = kp.rows ? kp.rows[row] : ka.rows[row];
+    const RowParam P = kp.rows ? kp.rows[ri] : ka.rows[ri];
+    const int row = P.row;
+    rc.row = row;
     if (P.flags & RF_BAD) {
       // device-side parameters that break the rules: status 4
       if (want_out)

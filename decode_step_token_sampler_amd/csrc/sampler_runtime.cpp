@@ -59,6 +59,8 @@ struct sampler_handle {
   RowParam *dev_ring = nullptr;    // device, kRing slots
   KernelArgs *args = nullptr;      // host: the launch's argument block
   RowParam *graph_rows = nullptr;  // device, max_rows records written by sampler_step_graph's first kernel
+  std::vector<RowParam> recs;      // host scratch: a step's records in row order (max_rows)
+  std::vector<int> rank, order;    // host scratch: group start order, rows by cost (max_rows)
   hipEvent_t slot_done[kRing] = {};
   bool slot_used[kRing] = {};
   int next_slot = 0;
@@ -311,11 +313,10 @@ namespace {
 // parameters and the launch, shared by both step entry points.  `dp`: the
 // device records, or null (records in ka.rows); `dev`: per-row arrays in
 // device memory that the kernel normalises itself (sampler_step_graph).
-sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, KernelArgs &ka, const RowParam *dp,
-                               bool any_pen, int path, hipStream_t stream, const DevRowArrays *dev = nullptr) {
-  const int n = a->n_rows, V = a->vocab;
+// The launch plan: G workgroups of `slice` values per row, `groups` row
+// groups (rows strided over them).
+sampler_status plan_groups(sampler_handle *h, int n, int V, int *G_out, int *slice_out, int *groups_out) {
   const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
-  hipError_t e;
   const int g_min = (V + h->slice_cap - 1) / h->slice_cap;
   if (g_min > kMaxG || g_min > h->resident) {
     set_msg(h->err, "vocab %d needs %d workgroups per row (max %d)", V, g_min,
@@ -336,6 +337,48 @@ sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, Ke
   int slice = (V + G - 1) / G;
   slice = (slice + 3) & ~3;
   G = (V + slice - 1) / slice;  // every workgroup gets a non-empty slice
+  const int groups = h->resident / G;
+  *G_out = G;
+  *slice_out = slice;
+  *groups_out = groups < n ? groups : n;
+  return SAMPLER_OK;
+}
+
+// The order in which the kernel's row groups start: block b of the grid is
+// dealt to XCD b % 8 and the kernel gives group x * gpx + j (gpx = groups /
+// 8) the blocks 8 (j G + gid) + x, so groups start in (j, x) order; groups
+// past 8 gpx take the last blocks.  rank[k] = the k-th group to start.
+void group_start_order(int groups, int *rank) {
+  const int gpx = groups / 8;
+  int k = 0;
+  for (int j = 0; j < gpx; ++j)
+    for (int x = 0; x < 8; ++x) rank[k++] = x * gpx + j;
+  for (int g = 8 * gpx; g < groups; ++g) rank[k++] = g;
+}
+
+// Expected cost class of a row (larger: longer): top-p without top-k keeps
+// the most candidates and values; rows that keep everything run Philox on
+// the whole slice; top-k rows decide from short lists; greedy rows draw
+// nothing.  Penalties and biases add a pass.
+int row_cost(const RowParam &p) {
+  int c;
+  if (p.flags & RF_GREEDY) c = 0;
+  else if (p.flags & RF_TOP1) c = 1;
+  else if ((p.flags & RF_TOPP) && !(p.flags & RF_TOPK)) c = 5;
+  else if (!(p.flags & (RF_TOPK | RF_TOPP | RF_MINP))) c = 4;
+  else if (p.flags & RF_TOPK) c = 3;
+  else c = 2;
+  return 2 * c + ((p.flags & (RF_PEN | RF_SPEC)) ? 1 : 0);
+}
+
+sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, KernelArgs &ka, const RowParam *dp,
+                               bool any_pen, int path, hipStream_t stream, const DevRowArrays *dev = nullptr) {
+  const int n = a->n_rows, V = a->vocab;
+  const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
+  hipError_t e;
+  int G, slice, groups;
+  sampler_status st = plan_groups(h, n, V, &G, &slice, &groups);
+  if (st != SAMPLER_OK) return st;
   KernelParams &kp = ka.kp;
   kp = KernelParams{};
   kp.logits = a->logits;
@@ -352,8 +395,7 @@ sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, Ke
   kp.top_lp_ids = a->top_logprob_ids;
   kp.row_status = a->row_status;
   kp.G = G;
-  const int groups = h->resident / G;
-  kp.n_groups = groups < n ? groups : n;
+  kp.n_groups = groups;
   kp.slice = slice;
   kp.hash_slots = h->hash_slots;
   kp.bias_slots = h->bias_slots;
@@ -489,6 +531,15 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     if ((e = hipHostMalloc((void **)&h->host_ring, ring_bytes, hipHostMallocDefault)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&h->dev_ring, ring_bytes)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&h->graph_rows, sizeof(RowParam) * (size_t)cfg->max_rows)) != hipSuccess) goto fail;
+    try {
+      h->recs.resize((size_t)cfg->max_rows);
+      h->rank.resize((size_t)cfg->max_rows);
+      h->order.resize((size_t)cfg->max_rows);
+    } catch (...) {
+      g_create_error = "out of host memory";
+      free_handle(h);
+      return SAMPLER_EHIP;
+    }
     h->args = new (std::nothrow) KernelArgs();
     if (!h->args) {
       g_create_error = "out of host memory";
@@ -568,9 +619,15 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
     rp = h->host_ring + (size_t)slot * h->cfg.max_rows;
     dp = h->dev_ring + (size_t)slot * h->cfg.max_rows;
   }
+  int G, slice, groups;
+  {
+    sampler_status pst = plan_groups(h, n, V, &G, &slice, &groups);
+    if (pst != SAMPLER_OK) return pst;
+  }
+  RowParam *recs = h->recs.data();  // records in row order, placed below
   bool any_pen = false;
   for (int r = 0; r < n; ++r) {
-    RowParam &p = rp[r];
+    RowParam &p = recs[r];
     const float t = a->temperature ? a->temperature[r] : 1.0f;
     const bool greedy = row_is_greedy(t);
     int32_t k = a->top_k ? a->top_k[r] : -1;
@@ -616,9 +673,28 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
       any_pen = true;  // the launch needs the hash machinery
     }
     p.flags = f;
+    p.row = r;
+    p.pad = 0;
     p.seed = a->row_seed ? a->row_seed[r] : (det ? kDeterministicSeed : a->seed);
     p.stream = a->row_stream ? a->row_stream[r] : (det ? 0u : (uint32_t)r);
     p.offset = a->row_offset ? a->row_offset[r] : a->offset;
+  }
+  // Place the records: the rows expected to take longest on the groups
+  // whose workgroups start first (a stable counting sort by cost class);
+  // rows past the first pass keep their order.
+  {
+    int *rank = h->rank.data(), *ord = h->order.data();
+    group_start_order(groups, rank);
+    constexpr int kClasses = 12;
+    int start[kClasses] = {};
+    for (int r = 0; r < n; ++r) ++start[row_cost(recs[r])];
+    for (int c = kClasses - 1, acc = 0; c >= 0; --c) {
+      const int cnt = start[c];
+      start[c] = acc;
+      acc += cnt;
+    }
+    for (int r = 0; r < n; ++r) ord[start[row_cost(recs[r])]++] = r;
+    for (int k = 0; k < n; ++k) rp[k < groups ? rank[k] : k] = recs[ord[k]];
   }
   hipError_t e;
   if (!inline_rows) {
