@@ -194,7 +194,9 @@ hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream
 // Launch one step.  The grid never exceeds the workgroups the device holds at
 // once; `cooperative` launches through hipLaunchCooperativeKernel, which
 // also has the runtime check that they are all resident.
-hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream);
+// ev0 / ev1 (or null): an event pair that brackets the kernel's execution.
+hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream,
+                       hipEvent_t ev0, hipEvent_t ev1);
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);

@@ -33,6 +33,7 @@
 //   6. the last workgroup to arrive merges the Gumbel winners and writes
 //      the token and status
 #include <float.h>
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -2685,17 +2686,22 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
 }
 
 template <typename TIn, bool PEN>
-hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream) {
+hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const KernelParams &kp = ka.kp;
   const size_t lds = kernel_lds_bytes(kp.slice, kp.hash_slots, kp.bias_slots, PEN);
   const dim3 grid(kp.n_groups * kp.G), block(kBlock);
+  void *args[] = {const_cast<KernelArgs *>(&ka)};
   if (cooperative) {
-    void *args[] = {const_cast<KernelArgs *>(&ka)};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&row_kernel<TIn, PEN>), grid, block, args,
-                                      (unsigned)lds, stream);
+    hipError_t e;
+    if (ev0 && (e = hipEventRecord(ev0, stream)) != hipSuccess) return e;
+    e = hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&row_kernel<TIn, PEN>), grid, block, args,
+                                   (unsigned)lds, stream);
+    if (e == hipSuccess && ev1) e = hipEventRecord(ev1, stream);
+    return e;
   }
-  hipLaunchKernelGGL((row_kernel<TIn, PEN>), grid, block, (unsigned)lds, stream, ka);
-  return hipGetLastError();
+  // the event pair (when given) brackets the kernel's own execution
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(&row_kernel<TIn, PEN>), grid, block, args, lds, stream,
+                            ev0, ev1, 0);
 }
 
 template <typename TIn, bool PEN>
@@ -2731,10 +2737,13 @@ hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream
   return hipGetLastError();
 }
 
-hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream) {
+hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream,
+                       hipEvent_t ev0, hipEvent_t ev1) {
   if (dtype == 0)
-    return penalties ? launch_t<float, true>(ka, cooperative, stream) : launch_t<float, false>(ka, cooperative, stream);
-  return penalties ? launch_t<uint16_t, true>(ka, cooperative, stream) : launch_t<uint16_t, false>(ka, cooperative, stream);
+    return penalties ? launch_t<float, true>(ka, cooperative, stream, ev0, ev1)
+                     : launch_t<float, false>(ka, cooperative, stream, ev0, ev1);
+  return penalties ? launch_t<uint16_t, true>(ka, cooperative, stream, ev0, ev1)
+                   : launch_t<uint16_t, false>(ka, cooperative, stream, ev0, ev1);
 }
 
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out) {

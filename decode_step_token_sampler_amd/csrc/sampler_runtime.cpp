@@ -427,13 +427,10 @@ sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, Ke
   kp.epoch = h->epoch;
   if (dev && (e = launch_rows(kp, h->graph_rows, stream)) != hipSuccess) return hip_fail(h, e, "rows kernel launch");
   const bool prof = h->prof_n < h->prof_cap;
-  if (prof && (e = hipEventRecord(h->prof[2 * h->prof_n], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-  e = launch_step(ka, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream);
+  e = launch_step(ka, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream,
+                  prof ? h->prof[2 * h->prof_n] : nullptr, prof ? h->prof[2 * h->prof_n + 1] : nullptr);
   if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
-  if (prof) {
-    if ((e = hipEventRecord(h->prof[2 * h->prof_n + 1], stream)) != hipSuccess) return hip_fail(h, e, "hipEventRecord");
-    ++h->prof_n;
-  }
+  if (prof) ++h->prof_n;
   return SAMPLER_OK;
 }
 

@@ -309,9 +309,10 @@ sampler_status sampler_select_path(const sampler_step_args *args, uint32_t flags
 sampler_status sampler_validate(const sampler_config *cfg, const sampler_step_args *args, char *msg,
                                 int32_t msg_len);
 
-/* Profiling: from now on each sampler_step records a HIP event pair right
- * before and right after its kernel on the step's stream, for up to
- * `capacity` steps.  This call creates the events (it may allocate); the
+/* Profiling: from now on each step records a HIP event pair that brackets
+ * its sampling kernel's execution on the step's stream (hipExtLaunchKernel's
+ * start and stop events; around the launch for cooperative launches), for
+ * up to `capacity` steps.  This call creates the events (it may allocate); the
  * steps themselves allocate nothing.  SAMPLER_EINVAL for capacity < 1. */
 sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity);
 
