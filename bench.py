@@ -30,6 +30,17 @@ sys.path.insert(0, ROOT)
 METRIC = "sampled rows/sec and achieved HBM GB/s (% peak) at N=64, V=128,000 filtered path"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 N_SETS = 6
+# buffer sets per workload: enough that one pass over them exceeds the 256 MB
+# Infinity Cache twice (workload 1 is latency-bound and fits anyway)
+SETS = {"1": 1, "2": 16, "2-greedy": 16, "3": 11, "4": N_SETS, "5": 2}
+WORKLOADS = {
+    "1": "Gumbel only N=4 V=1024 fp32, ids + probs",
+    "2": "batch-1 decode N=1 V=151936 bf16 T=1 (Gumbel), ids",
+    "2-greedy": "batch-1 decode N=1 V=151936 bf16 T=0 (greedy), ids",
+    "3": "mixed filtered N=32 V=151936 bf16, one greedy row, probs+logprobs",
+    "4": "full sampler chain N=64 V=128000 fp32, filtered path, probs+logprobs",
+    "5": "large vocab N=512 (128 x 4 forks) V=256000 bf16, top-20 logprobs",
+}
 
 
 def parse():
@@ -39,6 +50,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--workload", default="4", choices=["1", "2", "2-greedy", "3", "4", "5"],
+                    help="4 (default): the headline full-chain workload; the others time the remaining "
+                         "synthetic workloads (no CPU baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -120,32 +134,46 @@ def main():
     import workloads
 
     dev = torch.device("cuda:0")
-    batches = [workloads.config(4, set_id=s, step=s) for s in range(N_SETS)]
+    wl = args.workload
+    cfg = int(wl[0])
+    n_sets = SETS[wl]
+    temp = 0.0 if wl == "2-greedy" else None
+    batches = [workloads.config(cfg, set_id=s, step=s, temperature=temp) for s in range(n_sets)]
     b0 = batches[0]
     n, V = b0.n_rows, b0.vocab
+    K = b0.top_logprobs
     sets = []
     for b in batches:
-        sets.append(dict(
-            logits=torch.from_numpy(b.logits).to(dev),
-            hist=torch.from_numpy(b.history_ids).to(dev),
-            out=dict(token_ids=torch.empty(n, dtype=torch.int32, device=dev),
-                     probs=torch.empty(n, V, dtype=torch.float32, device=dev),
-                     logprobs=torch.empty(n, V, dtype=torch.float32, device=dev),
-                     row_status=torch.empty(n, dtype=torch.int32, device=dev))))
+        if b.dtype == "bf16":
+            L = torch.from_numpy(b.logits.view(np.int16)).view(torch.bfloat16).to(dev)
+        else:
+            L = torch.from_numpy(b.logits).to(dev)
+        out = dict(token_ids=torch.empty(n, dtype=torch.int32, device=dev),
+                   row_status=torch.empty(n, dtype=torch.int32, device=dev))
+        if b.want_probs:
+            out["probs"] = torch.empty(n, V, dtype=torch.float32, device=dev)
+        if b.want_logprobs:
+            out["logprobs"] = torch.empty(n, V, dtype=torch.float32, device=dev)
+        if K:
+            out["top_logprob_vals"] = torch.empty(n, K, dtype=torch.float32, device=dev)
+            out["top_logprob_ids"] = torch.empty(n, K, dtype=torch.int32, device=dev)
+        sets.append(dict(logits=L, out=out,
+                         hist=None if b.history_ids is None else torch.from_numpy(b.history_ids).to(dev)))
     torch.cuda.synchronize()
-    S = dsts.Sampler(n, V, max_history_per_row=2048, max_top_logprobs=0)
+    S = dsts.Sampler(n, V, max_history_per_row=2048, max_top_logprobs=K)
 
     def step(i):
-        b, t = batches[i % N_SETS], sets[i % N_SETS]
+        b, t = batches[i % n_sets], sets[i % n_sets]
         return S.step(t["logits"], temperature=b.temperature, top_p=b.top_p, top_k=b.top_k, min_p=b.min_p,
                       repetition_penalty=b.repetition_penalty, presence_penalty=b.presence_penalty,
                       frequency_penalty=b.frequency_penalty, history_ids=t["hist"], history_start=b.history_start,
-                      history_len=b.history_len, seed=0, offset=i, want_probs=True, want_logprobs=True,
-                      out=t["out"])
+                      history_len=b.history_len, row_stream=b.row_stream, seed=0, offset=i,
+                      want_probs=b.want_probs, want_logprobs=b.want_logprobs, top_logprobs=K, out=t["out"])
 
     for i in range(args.warmup):
         r = step(i)
-    assert r["path"] == "filtered"
+    if wl == "4":
+        assert r["path"] == "filtered"
     torch.cuda.synchronize()
     S.profile_start(args.steps)
     torch.cuda.synchronize()
@@ -169,6 +197,14 @@ def main():
         step(i)
         host_us.append((time.perf_counter() - t1) * 1e6)
     torch.cuda.synchronize()
+    # synchronised cost of one step (the call and its kernel, device idle before)
+    sync_us = []
+    for i in range(50):
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        step(i)
+        torch.cuda.synchronize()
+        sync_us.append((time.perf_counter() - t1) * 1e6)
 
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = n * args.steps / wall
@@ -176,7 +212,7 @@ def main():
     k_avg_ms = float(np.mean(kernel_ms))
     achieved = alg_bytes / (k_avg_ms * 1e-3) / 1e9
     line = {
-        "metric": METRIC,
+        "metric": METRIC if wl == "4" else "sampled rows/sec and achieved HBM GB/s (%% peak), workload %s" % wl,
         "value": rows_per_s,
         "unit": "rows/s",
         "n_gpus": 1,
@@ -186,20 +222,23 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
-        "data": "synthetic (seeded Zipf-biased Gaussian logits, Zipf(1.1) histories; 6 rotating sets, 593 MB)",
-        "config": {"workload": "full sampler chain N=64 V=128000 fp32, filtered path, probs+logprobs",
-                   "n_rows": n, "vocab": V, "history_per_row": 2048, "path": "filtered",
+        "dtype": b0.dtype,
+        "data": "synthetic (seeded Zipf-biased Gaussian logits%s; %d rotating sets, %d MB)" % (
+            ", Zipf(1.1) histories" if b0.history_ids is not None else "", n_sets,
+            sum(int(t["logits"].numel() * t["logits"].element_size()) for t in sets) // 10**6),
+        "config": {"workload": WORKLOADS[wl], "n_rows": n, "vocab": V,
+                   "history_per_row": 2048 if b0.history_ids is not None else 0, "path": r["path"],
                    "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic()},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if wl == "4" else None},
         "kernel_us": {"mean": k_avg_ms * 1e3, "median": float(np.median(kernel_ms)) * 1e3,
                       "p10": float(np.percentile(kernel_ms, 10)) * 1e3,
                       "p90": float(np.percentile(kernel_ms, 90)) * 1e3},
         "step_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "host_call_us_median": float(np.median(host_us)),
+        "sync_step_us_median": float(np.median(sync_us)),
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and wl == "4":
         line["cpu_baseline"] = cpu_baseline(batches, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     S.close()
