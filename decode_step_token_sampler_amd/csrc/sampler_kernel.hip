@@ -532,12 +532,16 @@ DEV void group_release(SmemBase &sm, GroupSync *s) {
 // the device.
 constexpr uint32_t kSpinLimit = 1u << 26;
 DEV void spin_gen(GroupSync *s, uint32_t g0, uint32_t *abort_word, uint32_t epoch) {
+  // one coherent load per iteration; the abort word (a peer's expired wait)
+  // and the bound are checked every 256 iterations
   uint32_t spins = 0;
   while ((__hip_atomic_load(&s->word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 8) == g0) {
-    if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
-    if (++spins > kSpinLimit) {
-      __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      break;
+    if ((++spins & 255u) == 0u) {
+      if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
+      if (spins > kSpinLimit) {
+        __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
     }
     __builtin_amdgcn_s_sleep(1);
   }
