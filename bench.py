@@ -33,16 +33,17 @@ sys.path.insert(0, ROOT)
 METRIC = "sampled rows/sec and achieved HBM GB/s (% peak) at N=64, V=128,000 filtered path"
 HBM_PEAK_GBS = 8000.0   # MI355X HBM3E, published
 N_SETS = 6
-# buffer sets per workload: enough that one pass over them exceeds the 256 MB
-# Infinity Cache twice (workload 1 is latency-bound and fits anyway)
-SETS = {"1": 1, "2": 16, "2-greedy": 16, "3": 11, "4": N_SETS, "5": 2}
+# name -> (generator index in workloads.config, temperature override, buffer
+# sets: enough that one pass over them exceeds the 256 MB Infinity Cache
+# twice; the small Gumbel-only workload is latency-bound and fits anyway,
+# description)
 WORKLOADS = {
-    "1": "Gumbel only N=4 V=1024 fp32, ids + probs",
-    "2": "batch-1 decode N=1 V=151936 bf16 T=1 (Gumbel), ids",
-    "2-greedy": "batch-1 decode N=1 V=151936 bf16 T=0 (greedy), ids",
-    "3": "mixed filtered N=32 V=151936 bf16, one greedy row, probs+logprobs",
-    "4": "full sampler chain N=64 V=128000 fp32, filtered path, probs+logprobs",
-    "5": "large vocab N=512 (128 x 4 forks) V=256000 bf16, top-20 logprobs",
+    "gumbel-small": (1, None, 1, "Gumbel only N=4 V=1024 fp32, ids + probs"),
+    "batch1": (2, None, 16, "batch-1 decode N=1 V=151936 bf16 T=1 (Gumbel), ids"),
+    "batch1-greedy": (2, 0.0, 16, "batch-1 decode N=1 V=151936 bf16 T=0 (greedy), ids"),
+    "mixed": (3, None, 11, "mixed filtered N=32 V=151936 bf16, one greedy row, probs+logprobs"),
+    "full-chain": (4, None, N_SETS, "full sampler chain N=64 V=128000 fp32, filtered path, probs+logprobs"),
+    "large-vocab": (5, None, 2, "large vocab N=512 (128 x 4 forks) V=256000 bf16, top-20 logprobs"),
 }
 
 
@@ -53,9 +54,9 @@ def parse():
     ap.add_argument("--warmup", type=int, default=30)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
-    ap.add_argument("--workload", default="4", choices=["1", "2", "2-greedy", "3", "4", "5"],
-                    help="4 (default): the headline full-chain workload; the others time the remaining "
-                         "synthetic workloads (no CPU baseline)")
+    ap.add_argument("--workload", default="full-chain", choices=sorted(WORKLOADS),
+                    help="full-chain (default): N=64, V=128,000 with every option; the others time the "
+                         "remaining synthetic workloads (no CPU baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -138,9 +139,8 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = args.workload
-    cfg = int(wl[0])
-    n_sets = SETS[wl]
-    temp = 0.0 if wl == "2-greedy" else None
+    cfg, temp, n_sets, desc = WORKLOADS[wl]
+    headline = wl == "full-chain"
     batches = [workloads.config(cfg, set_id=s, step=s, temperature=temp) for s in range(n_sets)]
     b0 = batches[0]
     n, V = b0.n_rows, b0.vocab
@@ -175,7 +175,7 @@ def main():
 
     for i in range(args.warmup):
         r = step(i)
-    if wl == "4":
+    if headline:
         assert r["path"] == "filtered"
     # the timed steps (no profiling events: they add a dependency per launch)
     torch.cuda.synchronize()
@@ -220,7 +220,7 @@ def main():
     k_avg_ms = float(np.mean(kernel_ms))
     achieved = alg_bytes / (k_avg_ms * 1e-3) / 1e9
     line = {
-        "metric": METRIC if wl == "4" else "sampled rows/sec and achieved HBM GB/s (%% peak), workload %s" % wl,
+        "metric": METRIC if headline else "sampled rows/sec and achieved HBM GB/s (%% peak), %s" % desc,
         "value": rows_per_s,
         "unit": "rows/s",
         "n_gpus": 1,
@@ -234,11 +234,11 @@ def main():
         "data": "synthetic (seeded Zipf-biased Gaussian logits%s; %d rotating sets, %d MB)" % (
             ", Zipf(1.1) histories" if b0.history_ids is not None else "", n_sets,
             sum(int(t["logits"].numel() * t["logits"].element_size()) for t in sets) // 10**6),
-        "config": {"workload": WORKLOADS[wl], "n_rows": n, "vocab": V,
+        "config": {"workload": desc, "n_rows": n, "vocab": V,
                    "history_per_row": 2048 if b0.history_ids is not None else 0, "path": r["path"],
                    "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if wl == "4" else None},
+                     "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if headline else None},
         "kernel_us": {"mean": k_avg_ms * 1e3, "median": float(np.median(kernel_ms)) * 1e3,
                       "p10": float(np.percentile(kernel_ms, 10)) * 1e3,
                       "p90": float(np.percentile(kernel_ms, 90)) * 1e3},
@@ -246,7 +246,7 @@ def main():
         "host_call_us_median": float(np.median(host_us)),
         "sync_step_us_median": float(np.median(sync_us)),
     }
-    if not args.no_cpu_baseline and wl == "4":
+    if not args.no_cpu_baseline and headline:
         line["cpu_baseline"] = cpu_baseline(batches, args.cpu_seconds)
     print(json.dumps(line), flush=True)
     S.close()
