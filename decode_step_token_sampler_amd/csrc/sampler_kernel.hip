@@ -903,7 +903,7 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
   bool bad = false;
 #pragma unroll
   for (int s = 0; s < kE3Slots; ++s) {
-    if (has[s]) {
+    if (64 * s < n && has[s]) {
       const int p = lane + 64 * s;
       const int bj = win_bin(in.Af, key_to_float(kj[s]), in.wsc);
       bad |= bj < 0 || bj >= kWinBins || !((sm.binmask[bj >> 5] >> (bj & 31)) & 1u) || p < (int)lc[bj] ||
@@ -913,13 +913,19 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
   uint32_t flags = (__ballot(bad) || tot != (uint32_t)n) ? 1u : 0u;
   // inclusive prefix of the exact masses exp(z - m) along the list, slot by
   // slot
+  // (slots past the list's end hold the running total; the test is
+  // wave-uniform, so short lists skip their fp64 work)
   double pj[kE3Slots];
   {
     double carry = 0.0;
 #pragma unroll
     for (int s = 0; s < kE3Slots; ++s) {
-      pj[s] = carry + wave_scan_f64(has[s] ? exp_nonpos(sm.exp_tab, (double)key_to_float(kj[s]) - in.m) : 0.0);
-      carry = __shfl(pj[s], 63);
+      if (64 * s < n) {
+        pj[s] = carry + wave_scan_f64(has[s] ? exp_nonpos(sm.exp_tab, (double)key_to_float(kj[s]) - in.m) : 0.0);
+        carry = __shfl(pj[s], 63);
+      } else {
+        pj[s] = carry;
+      }
     }
   }
   // a position's key and prefix mass (j wave-uniform, 0 <= j < n)
@@ -942,7 +948,8 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
   auto count_ge = [&](uint32_t t) {
     int c = 0;
 #pragma unroll
-    for (int s = 0; s < kE3Slots; ++s) c += __popcll(__ballot(has[s] && kj[s] >= t));
+    for (int s = 0; s < kE3Slots; ++s)
+      if (64 * s < n) c += __popcll(__ballot(has[s] && kj[s] >= t));
     return c;
   };
   const int fp_k = fpos(in.rklo), fp_p0 = fpos(in.r1lo), fp_p1 = fpos(in.r1hi + 1);
@@ -968,6 +975,7 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
     int e = -1;
 #pragma unroll
     for (int s = 0; s < kE3Slots; ++s) {
+      if (64 * s >= n) break;  // wave-uniform: past the list's end
       // the key one position on: the next lane, or the next slot's lane 0
       const uint32_t nx = s + 1 < kE3Slots ? (uint32_t)__builtin_amdgcn_readlane((int)kj[s + 1 < kE3Slots ? s + 1 : s], 0) : 0u;
       const uint32_t dn = (uint32_t)__shfl_down((int)kj[s], 1);
