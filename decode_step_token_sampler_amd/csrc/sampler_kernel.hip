@@ -96,7 +96,6 @@ struct alignas(16) SmemBase {
   uint32_t gcnt[kMaxG];          // merger: candidates per workgroup
   uint32_t gpo[kMaxG + 1];       // merger: 16-byte pair offsets per workgroup
   uint32_t goff[kMaxG + 1];      // merger: candidate offsets per workgroup
-  uint32_t wo[kWaves + 1];       // gather: offsets per wave
   unsigned long long tl[kMaxTopLogprobs];
 };
 
@@ -1931,29 +1930,24 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       }
       if (lane == 0) sm.red_c[wave] = cnt;
       __syncthreads();
-      if (tid == 0) {
-        uint32_t acc = 0;
-        bool ovf = false;
-        for (int w = 0; w < kWaves; ++w) {
-          sm.wo[w] = acc;
-          ovf |= sm.red_c[w] > (uint32_t)kStagePerWave;
-          acc += sm.red_c[w];
-        }
-        ovf |= acc > (uint32_t)kCandCap;
-        sm.wo[kWaves] = ovf ? (uint32_t)kCandCap + 1u : acc;
+      // every wave copies its own candidates to the slot, at its offset among
+      // the waves' counts (each wave sums the counts itself)
+      uint32_t acc = 0, woff = 0;
+      bool ovf = false;
+      for (int w = 0; w < kWaves; ++w) {
+        const uint32_t c = sm.red_c[w];
+        if (w == wave) woff = acc;
+        ovf |= c > (uint32_t)kStagePerWave;
+        acc += c;
       }
-      __syncthreads();
-      const uint32_t my_n = sm.wo[kWaves];
+      ovf |= acc > (uint32_t)kCandCap;
+      const uint32_t my_n = ovf ? (uint32_t)kCandCap + 1u : acc;
       const unsigned xq = xseq++ & 1u;
-      if (wave == 0) {
+      {
         WgSlots *my = slot_at(kp, group * G + gid);
-        if (my_n <= (uint32_t)kCandCap) {
-          for (int w = 0; w < kWaves; ++w) {
-            const int cw = (int)sm.red_c[w];
-            for (int j = lane; j < cw; j += 64) atomic_st(&my->cand[xq][sm.wo[w] + j], stage[w * kStagePerWave + j]);
-          }
-        }
-        if (lane == 0) atomic_st(&my->cand_n[xq][0], my_n);
+        if (my_n <= (uint32_t)kCandCap)
+          for (int j = lane; j < (int)cnt; j += 64) atomic_st(&my->cand[xq][woff + j], wst[j]);
+        if (tid == 0) atomic_st(&my->cand_n[xq][0], my_n);
       }
       // the addresses wave 0 reads in exchange 3 (below), taken before the wait
       constexpr int kPL = 5;
@@ -1968,8 +1962,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         po[j] = 2 * (pj - pg[j] * pps);
         pp[j] = &peers[min(pg[j], G - 1)].cand[xq][pg[j] < G ? po[j] : 0];
       }
-      // only wave 0 wrote exchange data, so only it waits for its stores
-      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch, false);
+      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
       // ---- exchange 3, in every workgroup alike: wave 0 reads the counts and
       // the first candidates of every slice in one batch (pairs of keys; a
       // slot's array has room past an odd count), places them in the list
