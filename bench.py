@@ -36,14 +36,23 @@ N_SETS = 6
 # name -> (generator index in workloads.config, temperature override, buffer
 # sets: enough that one pass over them exceeds the 256 MB Infinity Cache
 # twice; the small Gumbel-only workload is latency-bound and fits anyway,
-# description)
+# description, ablation stage of the full chain or None)
 WORKLOADS = {
-    "gumbel-small": (1, None, 1, "Gumbel only N=4 V=1024 fp32, ids + probs"),
-    "batch1": (2, None, 16, "batch-1 decode N=1 V=151936 bf16 T=1 (Gumbel), ids"),
-    "batch1-greedy": (2, 0.0, 16, "batch-1 decode N=1 V=151936 bf16 T=0 (greedy), ids"),
-    "mixed": (3, None, 11, "mixed filtered N=32 V=151936 bf16, one greedy row, probs+logprobs"),
-    "full-chain": (4, None, N_SETS, "full sampler chain N=64 V=128000 fp32, filtered path, probs+logprobs"),
-    "large-vocab": (5, None, 2, "large vocab N=512 (128 x 4 forks) V=256000 bf16, top-20 logprobs"),
+    "gumbel-small": (1, None, 1, "Gumbel only N=4 V=1024 fp32, ids + probs", None),
+    "batch1": (2, None, 16, "batch-1 decode N=1 V=151936 bf16 T=1 (Gumbel), ids", None),
+    "batch1-greedy": (2, 0.0, 16, "batch-1 decode N=1 V=151936 bf16 T=0 (greedy), ids", None),
+    "mixed": (3, None, 11, "mixed filtered N=32 V=151936 bf16, one greedy row, probs+logprobs", None),
+    "full-chain": (4, None, N_SETS, "full sampler chain N=64 V=128000 fp32, filtered path, probs+logprobs", None),
+    "large-vocab": (5, None, 2, "large vocab N=512 (128 x 4 forks) V=256000 bf16, top-20 logprobs", None),
+    # the per-feature ablation of the full chain: same logits, temperatures,
+    # outputs and RNG keys, features added one at a time (the last stage is
+    # full-chain itself)
+    "ablation-defaults": (4, None, N_SETS, "full-chain ablation N=64 V=128000 fp32: temperature only, "
+                          "probs+logprobs", "defaults"),
+    "ablation-penalties": (4, None, N_SETS, "full-chain ablation N=64 V=128000 fp32: + penalties, "
+                           "probs+logprobs", "penalties"),
+    "ablation-min_p": (4, None, N_SETS, "full-chain ablation N=64 V=128000 fp32: + penalties + min_p, "
+                       "probs+logprobs", "min_p"),
 }
 
 
@@ -56,7 +65,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--workload", default="full-chain", choices=sorted(WORKLOADS),
                     help="full-chain (default): N=64, V=128,000 with every option; the others time the "
-                         "remaining synthetic workloads (no CPU baseline)")
+                         "remaining synthetic workloads and the full chain's per-feature ablation "
+                         "(no CPU baseline)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -101,10 +111,12 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 10}))
 
 
-def cpu_baseline(batches, budget_s):
-    """The oracle, as it stands, on whole steps of the same workload."""
+def cpu_baseline(batches, budget_s, threads=None):
+    """The oracle, as it stands, on whole steps of the same workload (one
+    thread per host core, at most 16, unless threads is given)."""
     import oracle
-    threads = min(os.cpu_count() or 1, 16)
+    if threads is None:
+        threads = min(os.cpu_count() or 1, 16)
     rows = 0
     steps = 0
     t0 = time.perf_counter()
@@ -139,9 +151,11 @@ def main():
 
     dev = torch.device("cuda:0")
     wl = args.workload
-    cfg, temp, n_sets, desc = WORKLOADS[wl]
+    cfg, temp, n_sets, desc, stage = WORKLOADS[wl]
     headline = wl == "full-chain"
     batches = [workloads.config(cfg, set_id=s, step=s, temperature=temp) for s in range(n_sets)]
+    if stage is not None:
+        batches = [b.ablation(stage) for b in batches]
     b0 = batches[0]
     n, V = b0.n_rows, b0.vocab
     K = b0.top_logprobs
@@ -244,10 +258,17 @@ def main():
                       "p90": float(np.percentile(kernel_ms, 90)) * 1e3},
         "step_gbs": alg_bytes / (ms_per_step * 1e-3) / 1e9,
         "host_call_us_median": float(np.median(host_us)),
+        "host_call_us_iqr": [float(np.percentile(host_us, 25)), float(np.percentile(host_us, 75))],
         "sync_step_us_median": float(np.median(sync_us)),
+        "sync_step_us_iqr": [float(np.percentile(sync_us, 25)), float(np.percentile(sync_us, 75))],
     }
+    if stage is not None:
+        line["config"]["ablation_stage"] = stage
     if not args.no_cpu_baseline and headline:
         line["cpu_baseline"] = cpu_baseline(batches, args.cpu_seconds)
+        # the same oracle on one host thread (rows are independent, so this
+        # is the per-core rate)
+        line["cpu_baseline_1thread"] = cpu_baseline(batches, args.cpu_seconds / 3, threads=1)
     print(json.dumps(line), flush=True)
     S.close()
 

@@ -52,6 +52,7 @@ constexpr int kWaves = kBlock / 64;
 // the worst score of the max, m - ln(22.874) (E at its largest, 33 ln 2).
 // 22.874 + 3.130 = 26.004; the margin covers fp32 rounding of m - z.
 constexpr float kPruneNats = 26.25f;
+constexpr float kLnInvEmin = 22.8738570f;  // 33 ln 2 = -ln of the least E
 // Relative slack of the linear-domain Gumbel bound (covers the fp32
 // rounding of the probability and of the uniform, ~1e-6).
 constexpr float kSlack = 1.0009765625f;
@@ -2428,6 +2429,15 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       constexpr uint32_t kRingW = kMaxSlice / 4 / (NT / 64);  // groups one wave visits at most
       static_assert((NT / 64) * kRingW * sizeof(uint16_t) <= kRegionBBytes, "candidate lists fit the region");
       ring = reinterpret_cast<uint16_t *>(regB) + wave * kRingW;
+      // the bound starts at the argmax's own score 1 / E (the argmax is
+      // always kept).  A value's score is at most q 2^33 (E >= 2^-33), so
+      // one with m - z above 33 ln 2 - ln(bound) cannot beat the argmax:
+      // the listing cut, never looser than kPruneNats (1 / E >= 1 / (33
+      // ln 2)), with the same margin for the fp32 rounding of m - z.
+      uint32_t w4[4];
+      philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
+      bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
+      const float cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
       const int its = (ln4 + 4 * NT - 1) / (4 * NT);
       constexpr int kStep = 8;  // groups read before any is tested
       for (int q0 = 0; q0 < its; q0 += kStep) {
@@ -2442,7 +2452,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           // monotonically), so a group holds a candidate exactly when its
           // largest value passes them; padding (-inf) never does
           const float zmax = fmaxf(fmaxf(zr[u][0], zr[u][1]), fmaxf(zr[u][2], zr[u][3]));
-          const bool any_cand = zmax >= tauf && (mf - zmax <= kPruneNats);
+          const bool any_cand = zmax >= tauf && (mf - zmax <= cut);
           const unsigned long long bal = __ballot(act && any_cand);
           if (bal) {
             const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
@@ -2451,11 +2461,6 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           }
         }
       }
-      // the bound starts at the argmax's own score 1 / E (the argmax is
-      // always kept)
-      uint32_t w4[4];
-      philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
-      bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
       for (; qh < qt;) gumbel_batch(min(qt - qh, 64u));
     };
 

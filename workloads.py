@@ -131,6 +131,28 @@ class Batch:
             row_seed=np.ascontiguousarray(rs[rows]), row_offset=np.ascontiguousarray(ro[rows]),
             row_stream=np.ascontiguousarray(rst[rows]))
 
+    ABLATION_STAGES = ("defaults", "penalties", "min_p", "all")
+
+    def ablation(self, stage: str) -> "Batch":
+        """The per-feature ablation of a full-chain batch, one stage of it:
+        "defaults" keeps only the temperatures (no penalties and no history,
+        top_k = -1, top_p = 1, min_p = 0); "penalties" adds the batch's own
+        penalties and histories; "min_p" adds its min_p; "all" adds top-k and
+        top-p, which is the batch unchanged.  Logits, outputs and RNG keys
+        stay the same throughout."""
+        if stage not in self.ABLATION_STAGES:
+            raise ValueError("unknown ablation stage %r" % stage)
+        if stage == "all":
+            return self
+        n = self.n_rows
+        b = dataclasses.replace(self, top_k=np.full(n, -1, np.int32), top_p=np.ones(n, np.float32))
+        if stage != "min_p":
+            b = dataclasses.replace(b, min_p=np.zeros(n, np.float32))
+        if stage == "defaults":
+            b = dataclasses.replace(b, repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
+                                    history_ids=None, history_start=None, history_len=None)
+        return b
+
 
 def _logits(cfg: int, set_id: int, n: int, V: int, dtype: str):
     rows, ranks = [], []
