@@ -72,6 +72,16 @@ def test_workload4_full_chain(sampler):
         assert g["path"] == "filtered"
 
 
+@pytest.mark.parametrize("stage", ["defaults", "penalties", "min_p"])
+def test_workload4_ablation_stages(sampler, stage):
+    # the full chain with features added one at a time, at full size: without
+    # truncation every row keeps every value (Gumbel path, Philox and the
+    # listing cut on most of the vocabulary, exact sums for the outputs)
+    b = workloads.config(4, set_id=1, step=1).ablation(stage)
+    g, o, r = check(b, sampler)
+    assert g["path"] == ("filtered" if stage == "min_p" else "gumbel")
+
+
 def test_workload5_large_vocab_forks(sampler):
     b = workloads.config(5)
     g, o, r = check(b, sampler)
