@@ -554,12 +554,11 @@ DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t e
   __syncthreads();
 }
 
-// Barrier: one atomic add; the last arrival resets the count and advances
-// the generation in one store, the others wait for it.  all_waves = false:
-// only wave 0 wrote data the other workgroups read, so only it waits for
-// its stores.
-DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch, bool all_waves = true) {
-  if (all_waves || tidx() < 64) order_release();
+// Barrier: every wave waits for its own stores, then one atomic add; the
+// last arrival resets the count and advances the generation in one store,
+// the others wait for it.
+DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch) {
+  order_release();
   __syncthreads();
   if (tidx() == 0) {
     const uint32_t old = __hip_atomic_fetch_add(&s->word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -2384,6 +2383,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       }
     }
     float bound = 0.0f;
+    float cut = kPruneNats;  // listing cut in nats below the max (set by the pass)
     // Groups of four that hold a Gumbel candidate (kept, and within
     // kPruneNats of the max) are listed per wave in LDS (16-bit group
     // numbers; every group the wave visits fits), then finished on full
@@ -2400,7 +2400,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          if (zv[c] >= tauf && (mf - zv[c] <= kPruneNats)) {
+          if (zv[c] >= tauf && (mf - zv[c] <= cut)) {
             // lower bound of w: (float)x rounds to nearest
             const float wl = (float)w[c] * 0x1.fffffcp-33f;
             const float qv = __builtin_amdgcn_exp2f((zv[c] - mf) * kLog2e);
@@ -2437,7 +2437,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       uint32_t w4[4];
       philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
       bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
-      const float cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
+      cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
       const int its = (ln4 + 4 * NT - 1) / (4 * NT);
       constexpr int kStep = 8;  // groups read before any is tested
       for (int q0 = 0; q0 < its; q0 += kStep) {
