@@ -42,9 +42,11 @@
  *     first kept token in index order whose running kept mass exceeds u
  *     times the kept total.
  *
- * Parity pins: see tests/test_oracle_*.py.  The penalty formula itself is
- * not fixed by the pages ("parity unpinned" for that formula; only its
- * identity at the defaults and its locality are pinned).
+ * Parity pins: see tests/test_oracle_*.py.  The penalty formula is not
+ * fixed by the pages: its repetition term is pinned against the transformers
+ * library's repetition-penalty processor; the frequency and presence terms
+ * and the order of the three are "parity unpinned" (only their identity at
+ * the defaults, their locality and a hand-worked example are pinned).
  */
 #include <float.h>
 #include <math.h>

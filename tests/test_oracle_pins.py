@@ -315,6 +315,41 @@ def test_penalty_hand_worked_example():
     np.testing.assert_allclose(o["logprobs"][0], scipy.special.log_softmax(z), rtol=1e-7)
 
 
+def test_repetition_penalty_matches_transformers_processor():
+    # The repetition part of the reading is the CTRL rule as the transformers
+    # library applies it (RepetitionPenaltyLogitsProcessor): each token seen
+    # in the history has a negative logit multiplied and a positive one
+    # divided by the penalty, once, whatever its count; other tokens stay.
+    # Penalties above and below 1, zero logits and repeated ids included.
+    transformers = pytest.importorskip("transformers")
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    n, V, H = 6, 257, 48
+    x = rng.normal(0.0, 3.0, (n, V)).astype(np.float32)
+    x[:, :6] = 0.0
+    hist = rng.integers(0, V, (n, H)).astype(np.int32)
+    hist[:, :12] = np.arange(12)                  # zeros and repeats in every history
+    hist[:, 12:16] = hist[:, 16:20]
+    rep = np.array([1.3, 0.7, 2.0, 1.0, 1.05, 3.5], np.float32)
+    zeros = np.zeros(n, np.float32)
+    o = run(x, temperature=np.ones(n, np.float32), repetition_penalty=rep, presence_penalty=zeros,
+            frequency_penalty=zeros, history_ids=hist.ravel(), history_start=np.arange(n, dtype=np.int64) * H,
+            history_len=np.full(n, H, np.int32))
+    for r in range(n):
+        proc = transformers.RepetitionPenaltyLogitsProcessor(penalty=float(rep[r]))
+        z = proc(torch.from_numpy(hist[r:r + 1].astype(np.int64)), torch.from_numpy(x[r:r + 1].copy()))
+        z = z.numpy()[0].astype(np.float64)
+        # torch may divide by a scalar through its reciprocal: 1 fp32 ulp of a
+        # logit is below 1e-6 here
+        np.testing.assert_allclose(o["logprobs"][r], scipy.special.log_softmax(z), rtol=0, atol=2e-6)
+    # a planted sign slip (dividing negative logits instead) is caught
+    bad = np.where(x < 0, x / rep[:, None], x * rep[:, None]).astype(np.float64)
+    seen = np.zeros((n, V), bool)
+    seen[np.repeat(np.arange(n), H), hist.ravel()] = True
+    wrong = np.where(seen, bad, x)
+    assert np.abs(o["logprobs"] - scipy.special.log_softmax(wrong, axis=1)).max() > 1e-2
+
+
 def test_penalty_identity_at_defaults_and_locality():
     b = workloads.random_small(12, 8, 300, penalties=True, mix="plain")
     common = dict(temperature=b.temperature, top_k=b.top_k, top_p=b.top_p, min_p=b.min_p,
