@@ -3,7 +3,8 @@
 Each test checks the oracle against something other than itself: values the
 pages print (the path table), published known-answer vectors (Philox), closed
 forms, library routines (scipy's softmax, numpy's argmax and sort, torch's
-bf16 conversion), brute force over tiny vocabularies, and distribution tests
+bf16 conversion, the transformers library's repetition-penalty processor and
+top-k / top-p / min-p warpers), brute force over tiny vocabularies, and distribution tests
 of the Gumbel-max draw against the categorical distribution.
 """
 import json
@@ -222,6 +223,48 @@ def test_topp_margin_flag_on_exact_crossing():
     assert o["topp_margin"][0] < 1e-7
     o = run(np.array([[1.0, 0.0]], np.float32), top_p=[0.6])
     assert not (o["flags"][0] & oracle.FLAG_TOPP_MARGIN)
+
+
+def test_masks_match_transformers_warpers():
+    # top-k, top-p and min-p applied in that order by the transformers
+    # library's warpers, each on the previous one's output (so top-p sees
+    # the top-k set renormalised and min-p compares with the largest kept
+    # probability), give the reading's kept sets at vocabulary sizes brute
+    # force cannot reach.  Continuous values (no ties, which the library's
+    # sort would break arbitrarily); rows within 1e-4 of a top-p or 1e-5 of
+    # a min-p boundary are skipped: the library decides them from fp32
+    # cumulative sums and an fp32 softmax.
+    transformers = pytest.importorskip("transformers")
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(91)
+    n, V = 96, 2000
+    scale = rng.choice([0.7, 1.5, 2.5], n)[:, None]   # flat to peaked rows
+    x = (scale * rng.standard_normal((n, V))).astype(np.float32)
+    k = rng.choice([-1, 1, 5, 50, 400], n).astype(np.int32)
+    p = rng.choice([1.0, 0.95, 0.8, 0.5, 0.2], n).astype(np.float32)
+    mp = rng.choice([0.0, 0.01, 0.1, 0.5], n).astype(np.float32)
+    o = run(x, temperature=np.ones(n, np.float32), top_k=k, top_p=p, min_p=mp)
+    ids = torch.zeros((1, 1), dtype=torch.long)
+    checked = 0
+    for r in range(n):
+        q = np.exp(x[r].astype(np.float64) - float(x[r].max()))
+        if p[r] < 1.0 and o["topp_margin"][r] < 1e-4:
+            continue
+        if mp[r] > 0 and np.min(np.abs(q / float(mp[r]) - 1.0)) < 1e-5:
+            continue
+        s = torch.from_numpy(x[r:r + 1].copy())
+        if k[r] > 0:
+            s = transformers.TopKLogitsWarper(int(k[r]))(ids, s)
+        if p[r] < 1.0:
+            s = transformers.TopPLogitsWarper(float(p[r]))(ids, s)
+        if mp[r] > 0:
+            s = transformers.MinPLogitsWarper(float(mp[r]))(ids, s)
+        want = np.isfinite(s.numpy()[0])
+        assert np.array_equal(np.isfinite(o["logprobs"][r]), want), (r, k[r], p[r], mp[r])
+        np.testing.assert_allclose(o["probs"][r][want], scipy.special.softmax(x[r][want].astype(np.float64)),
+                                   rtol=0, atol=1e-7)
+        checked += 1
+    assert checked >= 80
 
 
 # ---------------------------------------------------------------- Gumbel-max distribution
