@@ -3,8 +3,8 @@
 Each test checks the oracle against something other than itself: values the
 pages print (the path table), published known-answer vectors (Philox), closed
 forms, library routines (scipy's softmax, numpy's argmax and sort, torch's
-bf16 conversion, the transformers library's repetition-penalty processor and
-top-k / top-p / min-p warpers), brute force over tiny vocabularies, and distribution tests
+bf16 conversion, the transformers library's repetition-penalty and min-length
+processors and its top-k / top-p / min-p warpers), brute force over tiny vocabularies, and distribution tests
 of the Gumbel-max draw against the categorical distribution.
 """
 import json
@@ -557,6 +557,28 @@ def test_min_tokens_masks_stop_ids_only_while_active():
     z[0, [11, 40]] = -np.inf
     np.testing.assert_allclose(o["probs"][0], scipy.special.softmax(z[0]), rtol=0, atol=1e-7)
     np.testing.assert_array_equal(o["probs"][1], base["probs"][1])
+
+
+def test_min_tokens_boundary_matches_transformers_processor():
+    # The activation rule (stop ids masked while output_len < min_tokens) at
+    # and around the boundary, against the transformers library's
+    # min-length processor over a sequence of output_len tokens, with the
+    # row's stop ids as its end-of-sequence ids.
+    transformers = pytest.importorskip("transformers")
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(29)
+    V = 50
+    stops = np.array([3, 17, 49], np.int32)
+    cases = [(m, L) for m in (0, 1, 4) for L in (0, max(m - 1, 0), m, m + 1)]
+    n = len(cases)
+    x = (2 * rng.standard_normal((n, V))).astype(np.float32)
+    o = run(x, stop_ids=stops, stop_start=np.zeros(n, np.int64), stop_len=np.full(n, 3, np.int32),
+            min_tokens=[m for m, _ in cases], output_len=[L for _, L in cases])
+    for r, (m, L) in enumerate(cases):
+        proc = transformers.MinLengthLogitsProcessor(m, [int(s) for s in stops])
+        s = proc(torch.zeros((1, L), dtype=torch.long), torch.from_numpy(x[r:r + 1].copy())).numpy()[0]
+        np.testing.assert_array_equal(np.isfinite(o["logprobs"][r]), np.isfinite(s), err_msg=str((m, L)))
+        np.testing.assert_allclose(o["probs"][r], scipy.special.softmax(s.astype(np.float64)), rtol=0, atol=1e-7)
 
 
 # ---------------------------------------------------------------- logprob modes
