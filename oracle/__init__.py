@@ -99,6 +99,7 @@ class _Args(ctypes.Structure):
         ("output_len", ctypes.c_void_p),
         ("logprob_mode", ctypes.c_int32),
         ("inverse_cdf", ctypes.c_int32),
+        ("diag_token_alt", ctypes.c_void_p),
     ]
 
 
@@ -132,6 +133,10 @@ def lib():
             L.orc_row_is_greedy.restype = ctypes.c_int
             L.orc_normalized_top_k.argtypes = [ctypes.c_float, ctypes.c_int32]
             L.orc_normalized_top_k.restype = ctypes.c_int32
+            L.orc_row_alternative.argtypes = [ctypes.POINTER(_Args), ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p]
+            L.orc_row_alternative.restype = ctypes.c_int
+            L.orc_row_with_kept.argtypes = [ctypes.POINTER(_Args), ctypes.c_int32, ctypes.c_void_p]
+            L.orc_row_with_kept.restype = ctypes.c_int
             _lib = L
     return _lib
 
@@ -203,22 +208,16 @@ def normalized_top_k(temperature: float, top_k: int) -> int:
     return int(lib().orc_normalized_top_k(temperature, top_k))
 
 
-def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k=None, min_p=None,
-         repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
-         history_ids=None, history_start=None, history_len=None,
-         seed=0, offset=0, row_seed=None, row_offset=None, row_stream=None, deterministic=False,
-         want_probs=True, want_logprobs=True, top_logprobs=0, n_threads=1,
-         vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None,
-         stop_ids=None, stop_start=None, stop_len=None, min_tokens=None, output_len=None,
-         logprob_mode="processed", inverse_cdf=False):
-    """Run the oracle on host arrays.
-
-    ``logits`` is a 2-D array: float32, or uint16 holding bf16 bits when
-    ``dtype == "bf16"``; its row stride is its second dimension unless
-    ``vocab`` is smaller.  ``vocab_mask`` is a 2-D uint32 array of allowed
-    bits (bit i & 31 of word i >> 5; its row stride is its second
-    dimension).  Returns a dict of numpy outputs and diagnostics.
-    """
+def _make_args(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k=None, min_p=None,
+               repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
+               history_ids=None, history_start=None, history_len=None,
+               seed=0, offset=0, row_seed=None, row_offset=None, row_stream=None, deterministic=False,
+               want_probs=True, want_logprobs=True, top_logprobs=0, n_threads=1,
+               vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None,
+               stop_ids=None, stop_start=None, stop_len=None, min_tokens=None, output_len=None,
+               logprob_mode="processed", inverse_cdf=False):
+    """The oracle's argument block for host arrays, the output arrays it
+    writes, and the converted inputs it points at (kept alive by the caller)."""
     if dtype not in ("f32", "bf16"):
         raise ValueError("dtype must be 'f32' or 'bf16'")
     L = np.ascontiguousarray(logits, dtype=np.uint16 if dtype == "bf16" else np.float32)
@@ -260,6 +259,7 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
         "gumbel_gap": np.zeros(n, dtype=np.float64),
         "topp_margin": np.zeros(n, dtype=np.float64),
         "kept": np.zeros(n, dtype=np.int32),
+        "token_alt": np.full(n, -1, dtype=np.int32),
     }
     a = _Args()
     a.logits = L.ctypes.data
@@ -284,6 +284,7 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
     a.diag_gumbel_gap = out["gumbel_gap"].ctypes.data
     a.diag_topp_margin = out["topp_margin"].ctypes.data
     a.diag_kept = out["kept"].ctypes.data
+    a.diag_token_alt = out["token_alt"].ctypes.data
     a.vocab_mask = _ptr(M)
     a.mask_stride = 0 if M is None else M.shape[1]
     a.bias_ids, a.bias_vals, a.bias_start, a.bias_len = _ptr(BI), _ptr(BV), _ptr(BS), _ptr(BL)
@@ -300,7 +301,60 @@ def step(logits, *, dtype="f32", vocab=None, temperature=None, top_p=None, top_k
     if HS is not None and H is not None and HL is not None:
         if np.any(HS < 0) or np.any(HS + HL > H.shape[0]):
             raise ValueError("history span outside the id buffer")
+    keep = (L, T, P, K, MP, RP, PP, FP, H, HS, HL, RS, RO, RST, M, BI, BV, BS, BL, SI, SS, SL, MT, OL)
+    return a, out, keep
+
+
+def step(logits, **kw):
+    """Run the oracle on host arrays.
+
+    ``logits`` is a 2-D array: float32, or uint16 holding bf16 bits when
+    ``dtype == "bf16"``; its row stride is its second dimension unless
+    ``vocab`` is smaller.  ``vocab_mask`` is a 2-D uint32 array of allowed
+    bits (bit i & 31 of word i >> 5; its row stride is its second
+    dimension).  Keyword arguments are those of the sampler step (see
+    ``_make_args``).  Returns a dict of numpy outputs and diagnostics.
+    """
+    a, out, keep = _make_args(logits, **kw)
     rc = lib().orc_step(ctypes.byref(a))
     if rc != 0:
         raise RuntimeError(f"oracle step failed ({rc})")
+    del keep
     return out
+
+
+def row_alternatives(logits, row: int, **kw):
+    """The kept sets (bool [V] arrays) row ``row`` allows: the oracle's own
+    first, then, where the row is flagged, each set a rounding of its top-p
+    crossing (one tie group earlier or later) or of its min-p boundary could
+    give.  Unflagged rows allow one set."""
+    a, out, keep = _make_args(logits, **kw)
+    V = a.vocab
+    sets = []
+    which = 0
+    while True:
+        k = np.zeros(V, dtype=np.uint8)
+        rc = lib().orc_row_alternative(ctypes.byref(a), int(row), which, k.ctypes.data)
+        if rc == -1:
+            break
+        if rc < 0:
+            raise RuntimeError(f"oracle row alternative failed ({rc})")
+        if rc == 1 and not any(np.array_equal(k, s) for s in sets):
+            sets.append(k.copy())
+        which += 1
+    del keep
+    return [s.astype(bool) for s in sets]
+
+
+def row_with_kept(logits, row: int, kept, **kw):
+    """Row ``row``'s outputs when ``kept`` (bool [V]) is its kept set: a
+    dict like ``step``'s, for that row alone (1-D arrays)."""
+    a, out, keep = _make_args(logits, **kw)
+    k = np.ascontiguousarray(np.asarray(kept, dtype=np.uint8))
+    if k.shape != (a.vocab,):
+        raise ValueError("kept must have one entry per vocabulary token")
+    rc = lib().orc_row_with_kept(ctypes.byref(a), int(row), k.ctypes.data)
+    if rc != 0:
+        raise RuntimeError(f"oracle row_with_kept failed ({rc})")
+    del keep
+    return {name: (None if v is None else v[row]) for name, v in out.items()}

@@ -125,6 +125,8 @@ typedef struct {
   const int32_t *output_len;  /* per row: tokens generated so far */
   int32_t logprob_mode;       /* 0 processed, 1 temperature-scaled, 2 raw */
   int32_t inverse_cdf;        /* select by the seeded inverse CDF instead of Gumbel-max */
+  int32_t *diag_token_alt;    /* [n_rows] or NULL: for a near-tie or inverse-CDF margin row, the token on
+                                 the other side of the tie or step, else -1 */
 } orc_args;
 
 /* ------------------------------------------------------------------ */
@@ -213,26 +215,34 @@ int32_t orc_normalized_top_k(float temperature, int32_t top_k) {
   return top_k;
 }
 
+/* The path table of [A] "One request with top_p takes the whole batch off
+ * the fast path", read as a function of the set of row classes present:
+ * a batch with no sampling row (every row has top_k <= 1 after
+ * normalisation) is greedy; one whose rows ask for no truncation at all
+ * takes Gumbel-max (deterministic on a deterministic handle); a single row
+ * with top-k (a greedy row counts: its top_k is 1), top-p or min-p makes
+ * the whole batch filtered. */
+enum { ORC_C_SAMPLING = 1, ORC_C_TOPK = 2, ORC_C_TOPP = 4, ORC_C_MINP = 8 };
+
+static unsigned orc_row_classes(float temperature, int32_t top_k, float top_p, float min_p) {
+  const int32_t k = orc_normalized_top_k(temperature, top_k);
+  return (k > 1 ? ORC_C_SAMPLING : 0u) | (k != ORC_TOP_K_ALL ? ORC_C_TOPK : 0u) |
+         (top_p != 1.0f ? ORC_C_TOPP : 0u) | (min_p > 0.0f ? ORC_C_MINP : 0u);
+}
+
 /* Returns 0 and writes the path, or -1 for an empty batch. */
 int orc_select_path(int32_t n, const float *temperature, const int32_t *top_k, const float *top_p,
                     const float *min_p, int32_t deterministic, int32_t *path_out) {
   if (n <= 0) return -1;
-  int all_greedy = 1, need_top_p = 0, need_top_k = 0, need_min_p = 0;
-  for (int32_t r = 0; r < n; ++r) {
-    float t = temperature ? temperature[r] : 1.0f;
-    int32_t k = orc_normalized_top_k(t, top_k ? top_k[r] : -1);
-    float p = top_p ? top_p[r] : 1.0f;
-    float mp = min_p ? min_p[r] : 0.0f;
-    if (!(k <= 1)) all_greedy = 0;
-    if (p != 1.0f) need_top_p = 1;
-    if (k != ORC_TOP_K_ALL) need_top_k = 1;
-    if (mp > 0.0f) need_min_p = 1;
-  }
-  if (all_greedy) *path_out = ORC_PATH_GREEDY;
-  else if (!(need_top_p || need_top_k || need_min_p))
-    *path_out = deterministic ? ORC_PATH_DETERMINISTIC : ORC_PATH_GUMBEL;
-  else
-    *path_out = ORC_PATH_FILTERED;
+  unsigned present = 0;
+  for (int32_t r = 0; r < n; ++r)
+    present |= orc_row_classes(temperature ? temperature[r] : 1.0f, top_k ? top_k[r] : -1,
+                               top_p ? top_p[r] : 1.0f, min_p ? min_p[r] : 0.0f);
+  const int32_t U = deterministic ? ORC_PATH_DETERMINISTIC : ORC_PATH_GUMBEL; /* untruncated sampling */
+  const int32_t F = ORC_PATH_FILTERED, G = ORC_PATH_GREEDY;
+  /* indexed by the classes present: bit 0 sampling, 1 top-k, 2 top-p, 3 min-p */
+  const int32_t table[16] = {G, U, G, F, G, F, G, F, G, F, G, F, G, F, G, F};
+  *path_out = table[present];
   return 0;
 }
 
@@ -273,20 +283,46 @@ static void orc_kadd(orc_ksum *k, double v) {
 }
 static double orc_kval(const orc_ksum *k) { return k->s + k->c; }
 
-static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *ord, double *q, int32_t *cnt,
-                    unsigned char *kept) {
+/* Working arrays of one row (one set per worker thread). */
+typedef struct {
+  float *z;              /* processed logits after temperature */
+  float *xp;             /* processed logits before temperature (raw logprob mode) */
+  orc_zi *ord;           /* the row in (z desc, index asc) order */
+  double *q;             /* exp(z - m) */
+  int32_t *cnt;          /* history counts */
+  unsigned char *kept;   /* the kept set K */
+} orc_work;
+
+/* What steps 1-5 found for a row. */
+#define ORC_MAX_NEAR 4
+typedef struct {
+  int status;            /* 0; 1: no finite value; 2: a +inf value */
+  int greedy;
+  int32_t k_eff;
+  float m;
+  int32_t n_p;           /* entries of the order that top-k and top-p keep */
+  int32_t n_p_alt[2];    /* that prefix with the top-p crossing one tie group earlier / later; -1: not reachable */
+  int32_t n_near;        /* values kept by top-k/top-p within the min-p margin of the boundary */
+  float near_z[ORC_MAX_NEAR];
+  double topp_margin;
+  int32_t flags;
+} orc_rowinfo;
+
+/* Steps 1-4 of a row: load, logits processors, penalties, temperature,
+ * row maximum and status. */
+static void orc_row_values(const orc_args *a, int32_t r, orc_work *w, orc_rowinfo *info) {
   const int32_t V = a->vocab;
-  float T = a->temperature ? a->temperature[r] : 1.0f;
-  const int greedy = orc_row_is_greedy(T);
-  const float T_eff = greedy ? 1.0f : T;
-  const int32_t k_eff = orc_normalized_top_k(T, a->top_k ? a->top_k[r] : -1);
-  const float top_p = a->top_p ? a->top_p[r] : 1.0f;
-  const float min_p = a->min_p ? a->min_p[r] : 0.0f;
+  float *z = w->z;
+  const float T = a->temperature ? a->temperature[r] : 1.0f;
   const float rep = a->repetition_penalty ? a->repetition_penalty[r] : 1.0f;
   const float pres = a->presence_penalty ? a->presence_penalty[r] : 0.0f;
   const float freq = a->frequency_penalty ? a->frequency_penalty[r] : 0.0f;
-  int32_t flags = 0;
-  double gumbel_gap = INFINITY, topp_margin = INFINITY;
+  memset(info, 0, sizeof(*info));
+  info->greedy = orc_row_is_greedy(T);
+  info->k_eff = orc_normalized_top_k(T, a->top_k ? a->top_k[r] : -1);
+  info->n_p_alt[0] = info->n_p_alt[1] = -1;
+  info->topp_margin = INFINITY;
+  const float T_eff = info->greedy ? 1.0f : T;
 
   /* 1. load; NaN becomes -inf ([B] "On Apple silicon" lists NaN
    *    sanitisation among the sampler options; here it is always on). */
@@ -343,6 +379,7 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
    *    counts of each token in the row's history, then the three penalties
    *    on the tokens that occur.  Ids outside [0, V) are ignored. */
   if (a->history_len && a->history_len[r] > 0 && a->history_ids && a->history_start) {
+    int32_t *cnt = w->cnt;
     memset(cnt, 0, sizeof(int32_t) * (size_t)V);
     const int32_t *h = a->history_ids + a->history_start[r];
     for (int32_t j = 0; j < a->history_len[r]; ++j) {
@@ -362,7 +399,7 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
   }
 
   /* the processed logits before temperature, for the raw logprob mode */
-  if (a->logprob_mode == 2) memcpy(xp, z, sizeof(float) * (size_t)V);
+  if (a->logprob_mode == 2) memcpy(w->xp, z, sizeof(float) * (size_t)V);
 
   /* 3. temperature ([C] same section: logits.div_(temperatures)) */
   for (int32_t i = 0; i < V; ++i) z[i] = z[i] / T_eff;
@@ -371,87 +408,126 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
   float m = -INFINITY;
   for (int32_t i = 0; i < V; ++i)
     if (z[i] > m) m = z[i];
+  info->m = m;
+  info->status = (m == INFINITY) ? 2 : (m > -INFINITY ? 0 : 1);
+}
 
-  const int want_topk_out = a->top_logprobs > 0 && a->top_logprob_vals && a->top_logprob_ids;
-  if (!(m > -INFINITY) || m == INFINITY) {
-    if (a->row_status) a->row_status[r] = (m == INFINITY) ? 2 : 1;
-    a->token_ids[r] = -1;
-    for (int32_t i = 0; i < V; ++i) {
-      if (a->probs) a->probs[(int64_t)r * V + i] = 0.0f;
-      if (a->logprobs) a->logprobs[(int64_t)r * V + i] = -INFINITY;
-    }
-    if (want_topk_out)
-      for (int32_t j = 0; j < a->top_logprobs; ++j) {
-        a->top_logprob_vals[(int64_t)r * a->top_logprobs + j] = -INFINITY;
-        a->top_logprob_ids[(int64_t)r * a->top_logprobs + j] = -1;
-      }
-    if (a->diag_flags) a->diag_flags[r] = 0;
-    if (a->diag_gumbel_gap) a->diag_gumbel_gap[r] = INFINITY;
-    if (a->diag_topp_margin) a->diag_topp_margin[r] = INFINITY;
-    if (a->diag_kept) a->diag_kept[r] = 0;
-    return;
-  }
-  if (a->row_status) a->row_status[r] = 0;
-
-  const double dm = (double)m;
+/* Step 5, truncation ([C] "解码一步里采样做什么": _apply_top_k_top_p, then
+ * _apply_min_p), for a row with status 0: q_i = exp(z_i - m), the order,
+ * the kept set K in w->kept, and the row's boundary diagnostics.  Greedy rows
+ * keep every token (their distribution is the one at temperature 1).
+ *
+ * The diagnostics mark a rule's boundary only where that rule decides K:
+ *   - top-p: the crossing's distance from the target mass, relative to the
+ *     top-k mass.  Within ORC_TOPP_MARGIN, rounding of the masses could
+ *     move the crossing one tie group earlier (hi side) or later (lo side);
+ *     the row is flagged when such a move changes K, i.e. when min-p keeps
+ *     the tie group that the move would add or drop.
+ *   - min-p: values kept by top-k and top-p whose q lies within
+ *     ORC_MINP_MARGIN (relative) of min_p. */
+static void orc_row_truncate(const orc_args *a, int32_t r, orc_work *w, orc_rowinfo *info) {
+  const int32_t V = a->vocab;
+  const float *z = w->z;
+  double *q = w->q;
+  orc_zi *ord = w->ord;
+  unsigned char *kept = w->kept;
+  const float top_p = a->top_p ? a->top_p[r] : 1.0f;
+  const float min_p = a->min_p ? a->min_p[r] : 0.0f;
+  const double dm = (double)info->m;
   for (int32_t i = 0; i < V; ++i) q[i] = exp((double)z[i] - dm);
-
-  /* 5. truncation ([C] same section: _apply_top_k_top_p then _apply_min_p).
-   *    Greedy rows keep every token (distribution at temperature 1). */
   for (int32_t i = 0; i < V; ++i) kept[i] = 1;
-  if (!greedy) {
-    for (int32_t i = 0; i < V; ++i) {
-      ord[i].z = z[i];
-      ord[i].idx = i;
-    }
-    qsort(ord, (size_t)V, sizeof(orc_zi), orc_cmp_desc);
+  info->n_p = V;
+  if (info->greedy) return;
+  for (int32_t i = 0; i < V; ++i) {
+    ord[i].z = z[i];
+    ord[i].idx = i;
+  }
+  qsort(ord, (size_t)V, sizeof(orc_zi), orc_cmp_desc);
+  /* min-p keeps exp(z - m) >= min_p, i.e. a probability of at least min_p
+   * times the largest one */
+  const int minp_on = min_p > 0.0f;
+#define ORC_MINP_KEEPS(zv) (!minp_on || exp((double)(zv) - dm) >= (double)min_p)
 
-    /* top-k: keep every token whose value is >= the k-th largest value */
-    int32_t n_k = V;
-    if (k_eff < V) {
-      float t_k = ord[k_eff - 1].z;
-      n_k = k_eff;
-      while (n_k < V && ord[n_k].z == t_k) ++n_k;
-    }
-    /* top-p over the top-k set: smallest tie-closed prefix (by value) whose
-     * mass reaches top_p times the top-k mass. */
-    int32_t n_p = n_k;
-    if (top_p < 1.0f) {
-      double c_tot = 0.0;
-      for (int32_t j = 0; j < n_k; ++j) c_tot += q[ord[j].idx];
-      const double target = (double)top_p * c_tot;
-      double c = 0.0, c_prev = -1.0;
-      int32_t j = 0;
-      while (j < n_k) {
-        int32_t j2 = j;
-        const float v = ord[j].z;
-        double c_new = c;
-        while (j2 < n_k && ord[j2].z == v) c_new += q[ord[j2++].idx];
-        if (c_new >= target) {
-          n_p = j2;
-          double lo = (c_new - target) / c_tot;
-          double hi = (c_prev >= 0.0) ? (target - c) / c_tot : INFINITY;
-          topp_margin = lo < hi ? lo : hi;
-          break;
+  /* top-k: keep every token whose value is >= the k-th largest value */
+  int32_t n_k = V;
+  if (info->k_eff < V) {
+    const float t_k = ord[info->k_eff - 1].z;
+    n_k = info->k_eff;
+    while (n_k < V && ord[n_k].z == t_k) ++n_k;
+  }
+  /* top-p over the top-k set: the smallest tie-closed prefix (by value)
+   * whose mass reaches top_p times the top-k mass */
+  int32_t n_p = n_k;
+  if (top_p < 1.0f) {
+    double c_tot = 0.0;
+    for (int32_t j = 0; j < n_k; ++j) c_tot += q[ord[j].idx];
+    const double target = (double)top_p * c_tot;
+    double c = 0.0;
+    int32_t j = 0;
+    while (j < n_k) {
+      int32_t j2 = j;
+      const float v = ord[j].z;
+      double c_new = c;
+      while (j2 < n_k && ord[j2].z == v) c_new += q[ord[j2++].idx];
+      if (c_new >= target) {
+        n_p = j2;
+        const double lo = (c_new - target) / c_tot;                /* distance to the lo side */
+        const double hi = j > 0 ? (target - c) / c_tot : INFINITY; /* distance to the hi side */
+        info->topp_margin = lo < hi ? lo : hi;
+        /* hi side: the crossing one group earlier drops this group */
+        if (hi < ORC_TOPP_MARGIN) {
+          info->n_p_alt[0] = j;
+          if (ORC_MINP_KEEPS(v)) info->flags |= ORC_FLAG_TOPP_MARGIN;
         }
-        c_prev = c;
-        c = c_new;
-        j = j2;
+        /* lo side: one group later adds the next group of the top-k set */
+        if (lo < ORC_TOPP_MARGIN && j2 < n_k) {
+          int32_t j3 = j2;
+          while (j3 < n_k && ord[j3].z == ord[j2].z) ++j3;
+          info->n_p_alt[1] = j3;
+          if (ORC_MINP_KEEPS(ord[j2].z)) info->flags |= ORC_FLAG_TOPP_MARGIN;
+        }
+        break;
       }
-      if (topp_margin < ORC_TOPP_MARGIN) flags |= ORC_FLAG_TOPP_MARGIN;
+      c = c_new;
+      j = j2;
     }
-    /* kept by top-k/top-p: the first n_p entries of the order */
-    for (int32_t i = 0; i < V; ++i) kept[i] = 0;
-    for (int32_t j = 0; j < n_p; ++j) kept[ord[j].idx] = 1;
-    /* min-p: keep tokens whose probability is at least min_p times the
-     * largest probability, i.e. exp(z - m) >= min_p. */
-    if (min_p > 0.0f) {
-      for (int32_t i = 0; i < V; ++i) {
-        if (!(q[i] >= (double)min_p)) kept[i] = 0;
-        if (q[i] > 0.0 && fabs(q[i] / (double)min_p - 1.0) < ORC_MINP_MARGIN) flags |= ORC_FLAG_MINP_MARGIN;
+  }
+  info->n_p = n_p;
+  /* kept by top-k/top-p: the first n_p entries of the order; then min-p */
+  for (int32_t i = 0; i < V; ++i) kept[i] = 0;
+  for (int32_t j = 0; j < n_p; ++j) kept[ord[j].idx] = 1;
+  if (minp_on) {
+    /* the widest prefix any top-p alternative keeps, for the margin test */
+    int32_t n_any = n_p;
+    if (info->n_p_alt[1] > n_any) n_any = info->n_p_alt[1];
+    for (int32_t j = 0; j < n_any; ++j) {
+      const int32_t i = ord[j].idx;
+      if (j < n_p && !ORC_MINP_KEEPS(z[i])) kept[i] = 0;
+      if (fabs(q[i] / (double)min_p - 1.0) < ORC_MINP_MARGIN) {
+        if (j < n_p) info->flags |= ORC_FLAG_MINP_MARGIN;
+        int seen = 0;
+        for (int32_t t = 0; t < info->n_near; ++t)
+          if (info->near_z[t] == z[i]) seen = 1;
+        if (!seen && info->n_near < ORC_MAX_NEAR) info->near_z[info->n_near++] = z[i];
       }
     }
   }
+#undef ORC_MINP_KEEPS
+}
+
+/* Steps 6-8 of a row with status 0 and the kept set in w->kept: probs,
+ * logprobs, the token and the top logprobs, written to row r of the
+ * outputs; the diagnostics of the selection are added to info->flags. */
+static void orc_row_emit(const orc_args *a, int32_t r, orc_work *w, orc_rowinfo *info) {
+  const int32_t V = a->vocab;
+  const float *z = w->z, *xp = w->xp;
+  const double *q = w->q;
+  const unsigned char *kept = w->kept;
+  const double dm = (double)info->m;
+  const int want_topk_out = a->top_logprobs > 0 && a->top_logprob_vals && a->top_logprob_ids;
+  int32_t flags = info->flags;
+  double gumbel_gap = INFINITY;
+  int32_t token_alt = -1;
 
   /* 6. normaliser over the kept set, probs and logprobs
    *    ([C] softmax/log_softmax in fp32 of the processed logits). */
@@ -498,9 +574,12 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
    *    others draw by Gumbel-max over the kept set ([A] "Nine lines, and
    *    exactly one call site": probs divided by Exp(1) draws, then argmax). */
   int32_t token = -1;
-  if (k_eff == 1) {
+  const uint64_t seed = a->row_seed ? a->row_seed[r] : (a->deterministic ? 42u : a->seed);
+  const uint32_t stream = a->row_stream ? a->row_stream[r] : (a->deterministic ? 0u : (uint32_t)r);
+  const uint64_t off = a->row_offset ? a->row_offset[r] : a->offset;
+  if (info->k_eff == 1) {
     for (int32_t i = 0; i < V; ++i)
-      if (z[i] == m) {
+      if (z[i] == info->m) {
         token = i;
         break;
       }
@@ -509,30 +588,40 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
      * deterministic path's seeded multinomial; [B] "What the flag
      * switches"): one uniform u per row, then the first token (in index
      * order) whose cumulative kept mass exceeds u times the kept total.
-     * Masses are summed one at a time in index order. */
-    uint64_t seed = a->row_seed ? a->row_seed[r] : (a->deterministic ? 42u : a->seed);
-    uint32_t stream = a->row_stream ? a->row_stream[r] : (a->deterministic ? 0u : (uint32_t)r);
-    uint64_t off = a->row_offset ? a->row_offset[r] : a->offset;
+     * Masses are summed one at a time in index order.  Where u S lies
+     * within ORC_ICDF_MARGIN of a step, the token on the step's other side
+     * is the row's alternative. */
     const double u = orc_icdf_uniform(seed, stream, off);
     double tot = 0.0;
     for (int32_t i = 0; i < V; ++i)
       if (kept[i]) tot += q[i];
     const double t = u * tot;
     double c = 0.0, c_prev = 0.0;
+    int32_t prev = -1;
     for (int32_t i = 0; i < V; ++i) {
       if (!kept[i]) continue;
       c_prev = c;
       c += q[i];
+      prev = token;
       token = i;
       if (c > t) break;
     }
-    const double gap = fmin(fabs(c - t), fabs(t - c_prev)) / tot;
-    if (gap < ORC_ICDF_MARGIN) flags |= ORC_FLAG_ICDF_MARGIN;
+    const double up = fabs(c - t) / tot, down = fabs(t - c_prev) / tot;
+    if (up < ORC_ICDF_MARGIN || down < ORC_ICDF_MARGIN) {
+      flags |= ORC_FLAG_ICDF_MARGIN;
+      if (down <= up) {
+        token_alt = prev;
+      } else {
+        for (int32_t i = token + 1; i < V; ++i)
+          if (kept[i]) {
+            token_alt = i;
+            break;
+          }
+      }
+    }
   } else {
-    uint64_t seed = a->row_seed ? a->row_seed[r] : (a->deterministic ? 42u : a->seed);
-    uint32_t stream = a->row_stream ? a->row_stream[r] : (a->deterministic ? 0u : (uint32_t)r);
-    uint64_t off = a->row_offset ? a->row_offset[r] : a->offset;
     double s1 = -1.0, s2 = -1.0;
+    int32_t tok2 = -1;
     double g_best = -INFINITY;
     int32_t tok_g = -1;
     for (int32_t i = 0; i < V; ++i) {
@@ -541,10 +630,12 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
       double s = (q[i] / S) / E;
       if (s > s1) {
         s2 = s1;
+        tok2 = token;
         s1 = s;
         token = i;
       } else if (s > s2) {
         s2 = s;
+        tok2 = i;
       }
       /* second spelling (log domain), for the self-check */
       double g = (((double)z[i] - dm) - lnS) - log(E);
@@ -554,8 +645,12 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
       }
     }
     gumbel_gap = (s2 >= 0.0 && s1 > 0.0) ? (s1 - s2) / s1 : INFINITY;
-    if (gumbel_gap < ORC_NEAR_TIE) flags |= ORC_FLAG_GUMBEL_NEAR_TIE;
-    else if (tok_g != token) flags |= ORC_FLAG_SPELLING_MISMATCH;
+    if (gumbel_gap < ORC_NEAR_TIE) {
+      flags |= ORC_FLAG_GUMBEL_NEAR_TIE;
+      token_alt = tok2;
+    } else if (tok_g != token) {
+      flags |= ORC_FLAG_SPELLING_MISMATCH;
+    }
   }
   a->token_ids[r] = token;
 
@@ -590,8 +685,61 @@ static void orc_row(const orc_args *a, int32_t r, float *z, float *xp, orc_zi *o
 
   if (a->diag_flags) a->diag_flags[r] = flags;
   if (a->diag_gumbel_gap) a->diag_gumbel_gap[r] = gumbel_gap;
-  if (a->diag_topp_margin) a->diag_topp_margin[r] = topp_margin;
+  if (a->diag_topp_margin) a->diag_topp_margin[r] = info->topp_margin;
   if (a->diag_kept) a->diag_kept[r] = n_kept;
+  if (a->diag_token_alt) a->diag_token_alt[r] = token_alt;
+}
+
+/* The outputs of a row whose status is not 0 (no finite value, or +inf). */
+static void orc_row_bad(const orc_args *a, int32_t r, int status) {
+  const int32_t V = a->vocab;
+  if (a->row_status) a->row_status[r] = status;
+  a->token_ids[r] = -1;
+  for (int32_t i = 0; i < V; ++i) {
+    if (a->probs) a->probs[(int64_t)r * V + i] = 0.0f;
+    if (a->logprobs) a->logprobs[(int64_t)r * V + i] = -INFINITY;
+  }
+  if (a->top_logprobs > 0 && a->top_logprob_vals && a->top_logprob_ids)
+    for (int32_t j = 0; j < a->top_logprobs; ++j) {
+      a->top_logprob_vals[(int64_t)r * a->top_logprobs + j] = -INFINITY;
+      a->top_logprob_ids[(int64_t)r * a->top_logprobs + j] = -1;
+    }
+  if (a->diag_flags) a->diag_flags[r] = 0;
+  if (a->diag_gumbel_gap) a->diag_gumbel_gap[r] = INFINITY;
+  if (a->diag_topp_margin) a->diag_topp_margin[r] = INFINITY;
+  if (a->diag_kept) a->diag_kept[r] = 0;
+  if (a->diag_token_alt) a->diag_token_alt[r] = -1;
+}
+
+static void orc_row(const orc_args *a, int32_t r, orc_work *w) {
+  orc_rowinfo info;
+  orc_row_values(a, r, w, &info);
+  if (info.status != 0) {
+    orc_row_bad(a, r, info.status);
+    return;
+  }
+  if (a->row_status) a->row_status[r] = 0;
+  orc_row_truncate(a, r, w, &info);
+  orc_row_emit(a, r, w, &info);
+}
+
+static int orc_work_alloc(orc_work *w, int32_t V) {
+  w->z = (float *)malloc(sizeof(float) * (size_t)V);
+  w->xp = (float *)malloc(sizeof(float) * (size_t)V);
+  w->ord = (orc_zi *)malloc(sizeof(orc_zi) * (size_t)V);
+  w->q = (double *)malloc(sizeof(double) * (size_t)V);
+  w->cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)V);
+  w->kept = (unsigned char *)malloc((size_t)V);
+  return (w->z && w->xp && w->ord && w->q && w->cnt && w->kept) ? 0 : -2;
+}
+
+static void orc_work_free(orc_work *w) {
+  free(w->z);
+  free(w->xp);
+  free(w->ord);
+  free(w->q);
+  free(w->cnt);
+  free(w->kept);
 }
 
 typedef struct {
@@ -602,52 +750,36 @@ typedef struct {
 
 static void *orc_worker(void *p) {
   orc_job *job = (orc_job *)p;
-  const int32_t V = job->a->vocab;
-  float *z = (float *)malloc(sizeof(float) * (size_t)V);
-  float *xp = (float *)malloc(sizeof(float) * (size_t)V);
-  orc_zi *ord = (orc_zi *)malloc(sizeof(orc_zi) * (size_t)V);
-  double *q = (double *)malloc(sizeof(double) * (size_t)V);
-  int32_t *cnt = (int32_t *)malloc(sizeof(int32_t) * (size_t)V);
-  unsigned char *kept = (unsigned char *)malloc((size_t)V);
-  if (!z || !xp || !ord || !q || !cnt || !kept) {
-    job->status = -2;
-  } else {
-    for (int32_t r = job->r0; r < job->r1; ++r) orc_row(job->a, r, z, xp, ord, q, cnt, kept);
-    job->status = 0;
-  }
-  free(z);
-  free(xp);
-  free(ord);
-  free(q);
-  free(cnt);
-  free(kept);
+  orc_work w;
+  job->status = orc_work_alloc(&w, job->a->vocab);
+  if (job->status == 0)
+    for (int32_t r = job->r0; r < job->r1; ++r) orc_row(job->a, r, &w);
+  orc_work_free(&w);
   return NULL;
+}
+
+static int orc_args_ok(const orc_args *a) {
+  return a && a->n_rows > 0 && a->vocab > 0 && a->row_stride >= a->vocab && a->logits && a->token_ids &&
+         a->logprob_mode >= 0 && a->logprob_mode <= 2 && !(a->vocab_mask && a->mask_stride < (a->vocab + 31) / 32);
 }
 
 /* Runs every row; returns 0, -1 for invalid sizes, -2 for allocation failure. */
 int orc_step(const orc_args *a) {
-  if (!a || a->n_rows <= 0 || a->vocab <= 0 || a->row_stride < a->vocab || !a->logits || !a->token_ids ||
-      a->logprob_mode < 0 || a->logprob_mode > 2 || (a->vocab_mask && a->mask_stride < (a->vocab + 31) / 32))
-    return -1;
+  if (!orc_args_ok(a)) return -1;
   int nt = a->n_threads > 0 ? a->n_threads : 1;
   if (nt > a->n_rows) nt = a->n_rows;
   if (nt > 256) nt = 256;
   orc_job jobs[256];
   pthread_t th[256];
   int32_t per = (a->n_rows + nt - 1) / nt;
-  int started = 0;
   for (int t = 0; t < nt; ++t) {
     jobs[t].a = a;
     jobs[t].r0 = t * per;
     jobs[t].r1 = (t + 1) * per < a->n_rows ? (t + 1) * per : a->n_rows;
     jobs[t].status = 0;
     if (jobs[t].r0 >= jobs[t].r1) continue;
-    if (nt == 1) {
-      orc_worker(&jobs[t]);
-    } else {
-      pthread_create(&th[t], NULL, orc_worker, &jobs[t]);
-      ++started;
-    }
+    if (nt == 1) orc_worker(&jobs[t]);
+    else pthread_create(&th[t], NULL, orc_worker, &jobs[t]);
   }
   int rc = 0;
   for (int t = 0; t < nt; ++t) {
@@ -655,5 +787,84 @@ int orc_step(const orc_args *a) {
     if (nt > 1) pthread_join(th[t], NULL);
     if (jobs[t].status != 0) rc = jobs[t].status;
   }
+  return rc;
+}
+
+/* ------------------------------------------------------------------ */
+/* Kept sets a flagged row allows, and a row's outputs for a given     */
+/* kept set (for checking rows whose boundary lies within a flag       */
+/* margin: such a row must match the outputs of one allowed set).      */
+/* ------------------------------------------------------------------ */
+
+/* Alternative `which` of row r's kept set, written to kept_out[V]:
+ *   which = c + 3 s, with c the top-p choice (0: the row's own crossing,
+ *   1: one tie group earlier, 2: one group later; only where the margin
+ *   reaches it) and s a subset of the near-boundary min-p values whose
+ *   decision is flipped (bit t flips near value t).
+ * Returns 1 when the alternative exists, 0 when it does not, -1 when
+ * `which` is past the last one (or r is invalid), -2 on allocation failure.
+ * Alternative 0 is the oracle's own kept set. */
+int orc_row_alternative(const orc_args *a, int32_t r, int32_t which, unsigned char *kept_out) {
+  if (!orc_args_ok(a) || r < 0 || r >= a->n_rows || which < 0 || which >= 3 << ORC_MAX_NEAR) return -1;
+  orc_work w;
+  int rc = orc_work_alloc(&w, a->vocab);
+  if (rc != 0) {
+    orc_work_free(&w);
+    return rc;
+  }
+  orc_rowinfo info;
+  orc_row_values(a, r, &w, &info);
+  rc = 0;
+  if (info.status == 0) {
+    orc_row_truncate(a, r, &w, &info);
+    const int c = which % 3, s = which / 3;
+    const int32_t n_pre = c == 0 ? info.n_p : info.n_p_alt[c - 1];
+    if (s >= (1 << info.n_near)) {
+      rc = c == 0 ? -1 : 0;
+    } else if (n_pre >= 0 && !info.greedy) {
+      const float min_p = a->min_p ? a->min_p[r] : 0.0f;
+      const int32_t V = a->vocab;
+      for (int32_t i = 0; i < V; ++i) kept_out[i] = 0;
+      for (int32_t j = 0; j < n_pre; ++j) {
+        const int32_t i = w.ord[j].idx;
+        int keep = !(min_p > 0.0f) || exp((double)w.z[i] - (double)info.m) >= (double)min_p;
+        for (int32_t t = 0; t < info.n_near; ++t)
+          if (((s >> t) & 1) && info.near_z[t] == w.z[i]) keep = !keep;
+        kept_out[i] = (unsigned char)keep;
+      }
+      rc = 1;
+    } else if (which == 0) {
+      memcpy(kept_out, w.kept, (size_t)a->vocab);
+      rc = 1;
+    }
+  } else {
+    rc = which == 0 ? 0 : -1;
+  }
+  orc_work_free(&w);
+  return rc;
+}
+
+/* Row r's outputs (token, probs, logprobs, top logprobs, diagnostics) for
+ * the kept set kept_in[V] instead of the row's own truncation.  Returns 0,
+ * -1 for invalid arguments or a row whose status is not 0, -2 on allocation
+ * failure. */
+int orc_row_with_kept(const orc_args *a, int32_t r, const unsigned char *kept_in) {
+  if (!orc_args_ok(a) || r < 0 || r >= a->n_rows || !kept_in) return -1;
+  orc_work w;
+  int rc = orc_work_alloc(&w, a->vocab);
+  if (rc == 0) {
+    orc_rowinfo info;
+    orc_row_values(a, r, &w, &info);
+    if (info.status != 0) {
+      rc = -1;
+    } else {
+      orc_row_truncate(a, r, &w, &info);
+      memcpy(w.kept, kept_in, (size_t)a->vocab);
+      info.flags = 0;
+      if (a->row_status) a->row_status[r] = 0;
+      orc_row_emit(a, r, &w, &info);
+    }
+  }
+  orc_work_free(&w);
   return rc;
 }

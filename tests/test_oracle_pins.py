@@ -205,6 +205,9 @@ def test_masks_brute_force(ties):
         want, tot, m = brute_force_kept(z, kk, np.float32(p), np.float32(mp))
         o = run(x, temperature=[T], top_k=[k], top_p=[p], min_p=[mp])
         if o["flags"][0] & (oracle.FLAG_TOPP_MARGIN | oracle.FLAG_MINP_MARGIN):
+            # a boundary within the margin: the exact set is one the flag allows
+            alts = oracle.row_alternatives(np.atleast_2d(x), 0, temperature=[T], top_k=[k], top_p=[p], min_p=[mp])
+            assert any(set(np.flatnonzero(a).tolist()) == want for a in alts), (x, k, p, mp, T)
             continue
         got = set(np.flatnonzero(np.isfinite(o["logprobs"][0])).tolist())
         assert got == want, (x, k, p, mp, T)
@@ -217,12 +220,103 @@ def test_masks_brute_force(ties):
 
 def test_topp_margin_flag_on_exact_crossing():
     # p equal (to fp32 precision) to the top token's share puts the crossing on the boundary
-    p = np.float32(1.0 / (1.0 + math.exp(-1.0)))
+    p = _share_top_of_two()
     o = run(np.array([[1.0, 0.0]], np.float32), top_p=[p])
     assert o["flags"][0] & oracle.FLAG_TOPP_MARGIN
     assert o["topp_margin"][0] < 1e-7
     o = run(np.array([[1.0, 0.0]], np.float32), top_p=[0.6])
     assert not (o["flags"][0] & oracle.FLAG_TOPP_MARGIN)
+
+
+# The diagnostic flags mark a row only where rounding at a rule's boundary
+# could change what the row returns; each has a case that must flag and one
+# that must not.
+def _share_top_of_two():
+    # the fp32 top_p nearest the exact share of the larger of two tokens
+    # one nat apart: the crossing lies on the boundary (to fp32 precision)
+    return np.float32(1.0 / (1.0 + math.exp(-1.0)))
+
+
+def test_topp_margin_flag_only_where_top_p_decides():
+    x = np.array([[1.0, 0.0]], np.float32)
+    p = _share_top_of_two()
+    # min-p 0.3 keeps the second token (ratio e^-1 = 0.37): the crossing's
+    # side decides whether it is kept
+    o = run(x, top_p=[p], min_p=[0.3])
+    assert o["flags"][0] & oracle.FLAG_TOPP_MARGIN
+    # min-p 0.5 drops it whatever top-p does: no flag
+    o = run(x, top_p=[p], min_p=[0.5])
+    assert not (o["flags"][0] & oracle.FLAG_TOPP_MARGIN)
+    assert o["topp_margin"][0] < 1e-7  # the margin itself is still reported
+    # top-k 1 keeps one token whatever top-p does: no flag
+    o = run(x, top_p=[p], top_k=[1])
+    assert not (o["flags"][0] & oracle.FLAG_TOPP_MARGIN)
+
+
+def test_topp_margin_alternatives_are_the_neighbouring_groups():
+    x = np.array([[1.0, 0.0, -3.0]], np.float32)
+    p = _share_top_of_two() * np.float32((1 + math.exp(-1.0)) / (1 + math.exp(-1.0) + math.exp(-4.0)))
+    alts = oracle.row_alternatives(x, 0, top_p=[p])
+    sets = [set(np.flatnonzero(a).tolist()) for a in alts]
+    own = set(np.flatnonzero(np.isfinite(run(x, top_p=[p])["logprobs"][0])).tolist())
+    assert sets[0] == own
+    assert sorted(map(sorted, sets)) == [[0], [0, 1]]
+    # an unflagged row allows its own set alone
+    assert len(oracle.row_alternatives(x, 0, top_p=[0.6])) == 1
+
+
+def test_minp_margin_flag():
+    # m = fl32(ln 2 + 1e-3) and z = fl32(m - ln 2) (a tiny value with a fine
+    # fp32 grid): exp(z - m) = 1/2 to ~1e-12, on min_p = 1/2's boundary
+    m = np.float32(math.log(2.0) + 1e-3)
+    zb = np.float32(float(m) - math.log(2.0))
+    assert abs(math.exp(float(zb) - float(m)) / 0.5 - 1.0) < 1e-9
+    x = np.array([[m, zb, -4.0]], np.float32)
+    o = run(x, min_p=[0.5])
+    assert o["flags"][0] & oracle.FLAG_MINP_MARGIN
+    assert len(oracle.row_alternatives(x, 0, min_p=[0.5])) == 2
+    # a value 1e-6 nat away is outside the margin
+    x2 = np.array([[m, np.float32(float(zb) - 1e-6), -4.0]], np.float32)
+    assert not (run(x2, min_p=[0.5])["flags"][0] & oracle.FLAG_MINP_MARGIN)
+    # top-k 1 drops the near-boundary value whatever min-p does: no flag
+    assert not (run(x, min_p=[0.5], top_k=[1])["flags"][0] & oracle.FLAG_MINP_MARGIN)
+
+
+def test_gumbel_near_tie_flag():
+    # tokens 0 and 1 get equal Gumbel scores (to fp32 precision of the
+    # logit): z_1 = ln(E_1 / E_0) with the row's own Exp(1) draws
+    seed, stream, off = 5, 0, 9
+    E = oracle.exp1_draws(seed, stream, off, 4)
+    a = np.float32(math.log(E[1] / E[0]))
+    x = np.array([[0.0, a, -6.0, -6.0]], np.float32)
+    kw = dict(seed=seed, offset=off, row_stream=[stream])
+    o = run(x, **kw)
+    assert o["flags"][0] & oracle.FLAG_GUMBEL_NEAR_TIE
+    assert o["gumbel_gap"][0] < 1e-6
+    assert sorted([int(o["token_ids"][0]), int(o["token_alt"][0])]) == [0, 1]
+    # the brute-force scores agree: the two best are tokens 0 and 1
+    q = np.exp(x[0].astype(np.float64) - x[0].max())
+    assert set(np.argsort(-(q / E))[:2].tolist()) == {0, 1}
+    o = run(np.array([[0.0, a - np.float32(1e-3), -6.0, -6.0]], np.float32), **kw)
+    assert not (o["flags"][0] & oracle.FLAG_GUMBEL_NEAR_TIE)
+    assert o["token_alt"][0] == -1
+
+
+def test_icdf_margin_flag():
+    # u for (seed 11, stream 0, offset 1803) lies within 5e-5 of 1/3; with
+    # masses (1, 1, e^z2) and e^z2 = 1/u - 2, u S falls on the step after
+    # token 0
+    seed, off = 11, 1803
+    u = oracle.icdf_uniform(seed, 0, off)
+    assert abs(u - 1.0 / 3.0) < 5e-5
+    z2 = np.float32(math.log(1.0 / u - 2.0))
+    x = np.array([[0.0, 0.0, z2]], np.float32)
+    kw = dict(seed=seed, offset=off, row_stream=[0], inverse_cdf=True)
+    o = run(x, **kw)
+    assert o["flags"][0] & oracle.FLAG_ICDF_MARGIN
+    assert sorted([int(o["token_ids"][0]), int(o["token_alt"][0])]) == [0, 1]
+    o = run(np.array([[0.0, 0.0, z2 + np.float32(0.01)]], np.float32), **kw)
+    assert not (o["flags"][0] & oracle.FLAG_ICDF_MARGIN)
 
 
 def test_masks_match_transformers_warpers():
