@@ -31,10 +31,13 @@ FLAG_DETERMINISTIC = 1 << 0
 FLAG_FORCE_FILTERED = 1 << 1
 FLAG_COOPERATIVE_LAUNCH = 1 << 2
 FLAG_INVERSE_CDF = 1 << 3
+FLAG_FORCE_PATH_GREEDY = 1 << 4
+FLAG_FORCE_PATH_GUMBEL = 1 << 5
 
 # symbols the header declares
 EXPORTS = ("sampler_create", "sampler_step", "sampler_step_graph", "sampler_select_path", "sampler_validate",
-           "sampler_destroy", "sampler_last_error", "sampler_profile_start", "sampler_profile_stop")
+           "sampler_destroy", "sampler_last_error", "sampler_profile_start", "sampler_profile_stop",
+           "sampler_set_wait_spin_limit")
 
 
 class SamplerError(RuntimeError):
@@ -52,6 +55,7 @@ class Config(ctypes.Structure):
         ("device", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("max_bias_per_row", ctypes.c_int32),
+        ("wait_spin_limit", ctypes.c_int32),
     ]
 
 
@@ -148,6 +152,8 @@ def load_library(path: str = LIB_PATH):
     L.sampler_profile_stop.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int32,
                                        ctypes.POINTER(ctypes.c_int32)]
     L.sampler_profile_stop.restype = ctypes.c_int
+    L.sampler_set_wait_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_int32]
+    L.sampler_set_wait_spin_limit.restype = ctypes.c_int
     L.sampler_last_error.argtypes = [ctypes.c_void_p]
     L.sampler_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -170,6 +176,28 @@ def _host(a, dtype, n):
 
 def _p(a):
     return None if a is None else a.ctypes.data
+
+
+def _check_tensor(t, name, dtype, device, shape=None):
+    """A device tensor the library reads or writes: CUDA, on the logits'
+    device, of the given dtype, contiguous (and of the given shape)."""
+    if not getattr(t, "is_cuda", False) or t.device != device:
+        raise ValueError(f"{name} must be a CUDA tensor on {device}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_spans(name, numel, start, length):
+    """Every span [start, start + length) of the rows lies inside a buffer of numel entries."""
+    if start is None or length is None:
+        return
+    live = length > 0
+    if np.any(start[live] < 0) or np.any(start[live] + length[live] > numel):
+        raise ValueError(f"a span of {name} lies outside its {numel} entries")
 
 
 class _Marshalled:
@@ -221,20 +249,123 @@ def validate(config: Config, args: StepArgs):
     return st, buf.value.decode()
 
 
+def _prepare_step(logits, *, vocab: Optional[int] = None, temperature=None, top_p=None, top_k=None,
+                  min_p=None, repetition_penalty=None, presence_penalty=None, frequency_penalty=None,
+                  history_ids=None, history_start=None, history_len=None, seed: int = 0, offset: int = 0,
+                  row_seed=None, row_offset=None, row_stream=None, want_probs: bool = False,
+                  want_logprobs: bool = False, top_logprobs: int = 0, want_status: bool = True,
+                  out: Optional[dict] = None, stream=None, vocab_mask=None, bias_ids=None, bias_vals=None,
+                  bias_start=None, bias_len=None, stop_ids=None, stop_start=None, stop_len=None, min_tokens=None,
+                  output_len=None, logprob_mode: str = "processed"):
+    """Marshal one decode step (argument checks only, no arithmetic): returns
+    the filled StepArgs, the output tensors, the path word, the host arrays
+    to keep alive until the call returns, and the stream handle."""
+    import torch
+    if logits.dim() != 2 or logits.stride(1) != 1:
+        raise ValueError("logits must be 2-D with unit column stride")
+    if logits.dtype == torch.float32:
+        dt = DTYPE_F32
+    elif logits.dtype == torch.bfloat16:
+        dt = DTYPE_BF16
+    else:
+        raise ValueError("logits must be float32 or bfloat16")
+    n = logits.shape[0]
+    V = logits.shape[1] if vocab is None else int(vocab)
+    dev = logits.device
+    if not logits.is_cuda:
+        raise ValueError("logits must be a CUDA tensor")
+    o = dict(out or {})
+    # caller-supplied outputs: the kernel writes exactly these shapes
+    for name, dtype, shape in (("token_ids", torch.int32, (n,)), ("probs", torch.float32, (n, V)),
+                               ("logprobs", torch.float32, (n, V)), ("row_status", torch.int32, (n,)),
+                               ("top_logprob_vals", torch.float32, (n, top_logprobs)),
+                               ("top_logprob_ids", torch.int32, (n, top_logprobs))):
+        if name in o:
+            _check_tensor(o[name], f"out['{name}']", dtype, dev, shape)
+    if "token_ids" not in o:
+        o["token_ids"] = torch.empty(n, dtype=torch.int32, device=dev)
+    if want_probs and "probs" not in o:
+        o["probs"] = torch.empty(n, V, dtype=torch.float32, device=dev)
+    if want_logprobs and "logprobs" not in o:
+        o["logprobs"] = torch.empty(n, V, dtype=torch.float32, device=dev)
+    if top_logprobs and "top_logprob_vals" not in o:
+        o["top_logprob_vals"] = torch.empty(n, top_logprobs, dtype=torch.float32, device=dev)
+        o["top_logprob_ids"] = torch.empty(n, top_logprobs, dtype=torch.int32, device=dev)
+    if want_status and "row_status" not in o:
+        o["row_status"] = torch.empty(n, dtype=torch.int32, device=dev)
+    m = _Marshalled(n, V, temperature=temperature, top_p=top_p, top_k=top_k, min_p=min_p,
+                    repetition_penalty=repetition_penalty, presence_penalty=presence_penalty,
+                    frequency_penalty=frequency_penalty, history_start=history_start,
+                    history_len=history_len, row_seed=row_seed, row_offset=row_offset, row_stream=row_stream,
+                    bias_start=bias_start, bias_len=bias_len, stop_start=stop_start, stop_len=stop_len,
+                    min_tokens=min_tokens, output_len=output_len)
+    a = m.args
+    k = m.keep
+    # the device id buffers: dtype, device, and every row's span inside them
+    if history_ids is not None:
+        _check_tensor(history_ids, "history_ids", torch.int32, dev)
+        _check_spans("history_ids", history_ids.numel(), k["history_start"], k["history_len"])
+    if bias_ids is not None or bias_vals is not None:
+        if bias_ids is None or bias_vals is None:
+            raise ValueError("bias_ids and bias_vals go together")
+        _check_tensor(bias_ids, "bias_ids", torch.int32, dev)
+        _check_tensor(bias_vals, "bias_vals", torch.float32, dev, tuple(bias_ids.shape))
+        _check_spans("bias_ids", bias_ids.numel(), k["bias_start"], k["bias_len"])
+    if stop_ids is not None:
+        _check_tensor(stop_ids, "stop_ids", torch.int32, dev)
+        _check_spans("stop_ids", stop_ids.numel(), k["stop_start"], k["stop_len"])
+    a.logits = logits.data_ptr()
+    a.dtype = dt
+    a.row_stride = logits.stride(0)
+    a.history_ids = None if history_ids is None else history_ids.data_ptr()
+    a.bias_ids = None if bias_ids is None else bias_ids.data_ptr()
+    a.bias_vals = None if bias_vals is None else bias_vals.data_ptr()
+    a.stop_ids = None if stop_ids is None else stop_ids.data_ptr()
+    if logprob_mode not in LOGPROB_MODES:
+        raise ValueError("logprob_mode must be one of %s" % sorted(LOGPROB_MODES))
+    a.logprob_mode = LOGPROB_MODES[logprob_mode]
+    if vocab_mask is not None:
+        if vocab_mask.dim() != 2 or vocab_mask.stride(1) != 1 or vocab_mask.element_size() != 4:
+            raise ValueError("vocab_mask must be a 2-D 32-bit tensor with unit column stride")
+        if not vocab_mask.is_cuda or vocab_mask.device != dev:
+            raise ValueError(f"vocab_mask must be a CUDA tensor on {dev}")
+        if vocab_mask.shape[0] != n or vocab_mask.shape[1] < (V + 31) // 32:
+            raise ValueError(f"vocab_mask must be [{n}, >= {(V + 31) // 32}] words")
+        a.vocab_mask = vocab_mask.data_ptr()
+        a.mask_stride = vocab_mask.stride(0)
+    a.seed = int(seed) & (2**64 - 1)
+    a.offset = int(offset) & (2**64 - 1)
+    a.token_ids = o["token_ids"].data_ptr()
+    a.probs = o["probs"].data_ptr() if "probs" in o else None
+    a.logprobs = o["logprobs"].data_ptr() if "logprobs" in o else None
+    a.top_logprobs = int(top_logprobs)
+    a.top_logprob_vals = o["top_logprob_vals"].data_ptr() if top_logprobs else None
+    a.top_logprob_ids = o["top_logprob_ids"].data_ptr() if top_logprobs else None
+    a.row_status = o["row_status"].data_ptr() if "row_status" in o else None
+    path = ctypes.c_int32(-1)
+    a.path_out = ctypes.addressof(path)
+    s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+    return a, o, path, (m, path), s
+
+
+
 class Sampler:
     """One handle (device workspace + pinned staging ring) on one GPU."""
 
     def __init__(self, max_rows: int, max_vocab: int, *, max_history_per_row: int = 4096,
                  max_top_logprobs: int = 32, device: int = 0, deterministic: bool = False,
                  force_filtered: bool = False, cooperative_launch: bool = False, max_bias_per_row: int = 0,
-                 inverse_cdf: bool = False):
+                 inverse_cdf: bool = False, wait_spin_limit: int = 0, force_path: Optional[str] = None):
         L = load_library()
         self._L = L
         cfg = Config(max_rows=max_rows, max_vocab=max_vocab, max_history_per_row=max_history_per_row,
                      max_top_logprobs=max_top_logprobs, device=device, max_bias_per_row=max_bias_per_row,
+                     wait_spin_limit=wait_spin_limit,
                      flags=(FLAG_DETERMINISTIC if deterministic else 0) | (FLAG_FORCE_FILTERED if force_filtered else 0)
                            | (FLAG_COOPERATIVE_LAUNCH if cooperative_launch else 0)
-                           | (FLAG_INVERSE_CDF if inverse_cdf else 0))
+                           | (FLAG_INVERSE_CDF if inverse_cdf else 0)
+                           | {None: 0, "greedy": FLAG_FORCE_PATH_GREEDY, "gumbel": FLAG_FORCE_PATH_GUMBEL,
+                              "filtered": FLAG_FORCE_FILTERED}[force_path])
         self.config = cfg
         h = ctypes.c_void_p()
         st = L.sampler_create(ctypes.byref(cfg), ctypes.byref(h))
@@ -257,6 +388,12 @@ class Sampler:
     def last_error(self) -> str:
         return self._L.sampler_last_error(self._h).decode()
 
+    def set_wait_spin_limit(self, limit: int):
+        """Bound of the cross-workgroup waits of later steps (0: the default)."""
+        st = self._L.sampler_set_wait_spin_limit(self._h, int(limit))
+        if st != SAMPLER_OK:
+            raise SamplerError(st, self.last_error())
+
     def profile_start(self, capacity: int):
         """Record kernel durations of the next `capacity` steps (HIP events)."""
         st = self._L.sampler_profile_start(self._h, int(capacity))
@@ -277,14 +414,7 @@ class Sampler:
         """Enqueue with a filled StepArgs (pointers already set); returns the status."""
         return self._L.sampler_step(self._h, ctypes.byref(args), ctypes.c_void_p(stream))
 
-    def step(self, logits, *, vocab: Optional[int] = None, temperature=None, top_p=None, top_k=None, min_p=None,
-             repetition_penalty=None, presence_penalty=None, frequency_penalty=None, history_ids=None,
-             history_start=None, history_len=None, seed: int = 0, offset: int = 0, row_seed=None,
-             row_offset=None, row_stream=None, want_probs: bool = False, want_logprobs: bool = False,
-             top_logprobs: int = 0, want_status: bool = True, out: Optional[dict] = None, stream=None,
-             vocab_mask=None, bias_ids=None, bias_vals=None, bias_start=None, bias_len=None, stop_ids=None,
-             stop_start=None, stop_len=None, min_tokens=None, output_len=None,
-             logprob_mode: str = "processed") -> dict:
+    def step(self, logits, **kw) -> dict:
         """Enqueue one decode step on the current torch stream; returns the output tensors.
 
         ``logits``: a CUDA tensor [N, row_stride] of float32 or bfloat16 with unit
@@ -292,70 +422,15 @@ class Sampler:
         ``history_ids``, ``bias_ids``, ``bias_vals``, ``stop_ids``: CUDA tensors
         (int32 / float32); ``vocab_mask``: a CUDA int32 or uint32-bits tensor
         [N, words] with unit column stride.  Outputs are allocated with torch
-        on the logits' device unless ``out`` supplies them.
+        on the logits' device unless ``out`` supplies them (each is checked
+        for dtype, device and shape).  Keywords: those of ``_prepare_step``.
         """
-        import torch
-        if logits.dim() != 2 or logits.stride(1) != 1:
-            raise ValueError("logits must be 2-D with unit column stride")
-        if logits.dtype == torch.float32:
-            dt = DTYPE_F32
-        elif logits.dtype == torch.bfloat16:
-            dt = DTYPE_BF16
-        else:
-            raise ValueError("logits must be float32 or bfloat16")
-        n = logits.shape[0]
-        V = logits.shape[1] if vocab is None else int(vocab)
-        dev = logits.device
-        o = dict(out or {})
-        if "token_ids" not in o:
-            o["token_ids"] = torch.empty(n, dtype=torch.int32, device=dev)
-        if want_probs and "probs" not in o:
-            o["probs"] = torch.empty(n, V, dtype=torch.float32, device=dev)
-        if want_logprobs and "logprobs" not in o:
-            o["logprobs"] = torch.empty(n, V, dtype=torch.float32, device=dev)
-        if top_logprobs and "top_logprob_vals" not in o:
-            o["top_logprob_vals"] = torch.empty(n, top_logprobs, dtype=torch.float32, device=dev)
-            o["top_logprob_ids"] = torch.empty(n, top_logprobs, dtype=torch.int32, device=dev)
-        if want_status and "row_status" not in o:
-            o["row_status"] = torch.empty(n, dtype=torch.int32, device=dev)
-        m = _Marshalled(n, V, temperature=temperature, top_p=top_p, top_k=top_k, min_p=min_p,
-                        repetition_penalty=repetition_penalty, presence_penalty=presence_penalty,
-                        frequency_penalty=frequency_penalty, history_start=history_start,
-                        history_len=history_len, row_seed=row_seed, row_offset=row_offset, row_stream=row_stream,
-                        bias_start=bias_start, bias_len=bias_len, stop_start=stop_start, stop_len=stop_len,
-                        min_tokens=min_tokens, output_len=output_len)
-        a = m.args
-        a.logits = logits.data_ptr()
-        a.dtype = dt
-        a.row_stride = logits.stride(0)
-        a.history_ids = None if history_ids is None else history_ids.data_ptr()
-        a.bias_ids = None if bias_ids is None else bias_ids.data_ptr()
-        a.bias_vals = None if bias_vals is None else bias_vals.data_ptr()
-        a.stop_ids = None if stop_ids is None else stop_ids.data_ptr()
-        if logprob_mode not in LOGPROB_MODES:
-            raise ValueError("logprob_mode must be one of %s" % sorted(LOGPROB_MODES))
-        a.logprob_mode = LOGPROB_MODES[logprob_mode]
-        if vocab_mask is not None:
-            if vocab_mask.dim() != 2 or vocab_mask.stride(1) != 1 or vocab_mask.element_size() != 4:
-                raise ValueError("vocab_mask must be a 2-D 32-bit tensor with unit column stride")
-            a.vocab_mask = vocab_mask.data_ptr()
-            a.mask_stride = vocab_mask.stride(0)
-        a.seed = int(seed) & (2**64 - 1)
-        a.offset = int(offset) & (2**64 - 1)
-        a.token_ids = o["token_ids"].data_ptr()
-        a.probs = o["probs"].data_ptr() if "probs" in o else None
-        a.logprobs = o["logprobs"].data_ptr() if "logprobs" in o else None
-        a.top_logprobs = int(top_logprobs)
-        a.top_logprob_vals = o["top_logprob_vals"].data_ptr() if top_logprobs else None
-        a.top_logprob_ids = o["top_logprob_ids"].data_ptr() if top_logprobs else None
-        a.row_status = o["row_status"].data_ptr() if "row_status" in o else None
-        path = ctypes.c_int32(-1)
-        a.path_out = ctypes.addressof(path)
-        s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
+        a, o, path, keep, s = _prepare_step(logits, **kw)
         st = self._L.sampler_step(self._h, ctypes.byref(a), ctypes.c_void_p(s))
         if st != SAMPLER_OK:
             raise SamplerError(st, self.last_error())
         o["path"] = PATH_NAMES[path.value]
+        del keep
         return o
 
     def step_graph(self, logits, params: dict, *, vocab: Optional[int] = None, history_ids=None, seed: int = 0,

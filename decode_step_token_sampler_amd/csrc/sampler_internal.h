@@ -83,14 +83,15 @@ struct alignas(16) RowParam {
 };
 static_assert(sizeof(RowParam) == 96, "RowParam layout");
 
-// Barrier words of one row group, each on its own 128-byte line: the
-// barrier word (generation << 8 | arrival count) and the final-exchange
-// arrival count.
+// Group words of one row group, each on its own 128-byte line: the barrier
+// word (epoch << 32 | generation << 8 | arrival count) and the
+// final-exchange word (epoch << 32 | arrival count); the epoch is that of
+// the launch that last used the word.
 struct alignas(128) GroupSync {
-  uint32_t word;
-  uint32_t pad0[31];
-  uint32_t fin;
-  uint32_t pad1[31];
+  unsigned long long word;
+  unsigned long long pad0[15];
+  unsigned long long fin;
+  unsigned long long pad1[15];
 };
 
 
@@ -160,8 +161,10 @@ struct KernelParams {
   int32_t path;
   GroupSync *sync;    // [n_groups]
   WgSlots *slots;     // [n_groups * G]
-  uint32_t *abort_word;  // equals epoch once a barrier wait of this launch expired
-  uint32_t epoch;        // launch counter of the handle (never 0)
+  uint32_t *abort_word;  // equals the epoch once a barrier wait of this launch expired
+  uint32_t epoch;        // the launch's epoch (host launches: 1 .. 2^31 - 1)
+  uint32_t *epoch_dev;   // or null; else the launch's epoch lives here (advanced by rows_kernel)
+  uint32_t spin_limit;   // bound of every cross-workgroup wait in spins (0: the default, ~2 s)
   // logits processors
   const uint32_t *vocab_mask;  // [n_rows, mask_stride] allowed bits, or null
   int64_t mask_stride;         // words
@@ -202,6 +205,9 @@ hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool coo
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);
+// Static LDS bytes of the row kernel (the compiler's own, besides the
+// dynamic request).
+hipError_t kernel_lds_static(size_t *out);
 // Fixed LDS bytes of one workgroup.
 size_t kernel_lds_fixed();
 // LDS bytes of the shared region (history hash and bias hash; merged prefix

@@ -492,82 +492,90 @@ DEV void order_acquire() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
 }
 
-// A group's barrier word holds a generation in bits 8.. and the arrival
-// count in bits 0..7, so one atomic add both arrives and reads the
-// generation.  The last arrival resets the count (and, to release, advances
-// the generation); the others wait for the generation to change.  The word
-// is reusable without clearing.
-//
-// group_arrive returns true in exactly one workgroup, the last to arrive,
-// which then calls group_release; the others call group_wait.
-DEV bool group_arrive(SmemBase &sm, GroupSync *s, int G) {
-  order_release();
-  __syncthreads();
-  if (tidx() == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&s->word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t g0 = old >> 8;
-    const bool last = (old & 0xFFu) == (uint32_t)G - 1u;
-    if (last) {
-      __hip_atomic_store(&s->word, g0 << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      order_acquire();
+// Group words (the barrier word and the final-exchange counter) carry, in
+// bits 32..63, the epoch of the launch that last used them; every launch has
+// its own epoch (host launches count up from 1, launches whose epoch lives
+// in device memory have bit 31 set).  A launch therefore never inherits an
+// earlier launch's count, also after that launch aborted mid-count: its
+// first arrival at a word claims the word by a compare-and-swap from the old
+// epoch, as if it were clear; later arrivals add one.
+//   barrier word: epoch << 32 | generation << 8 | arrivals
+//   final word:   epoch << 32 | arrivals
+// The last arrival at a barrier resets the count and advances the
+// generation in one store; the others wait for the generation to change.
+struct GroupCtx {
+  GroupSync *s;
+  uint32_t *abort_word;
+  uint32_t epoch;
+  uint32_t spin_limit;
+  int G;
+  bool claimed;  // this workgroup has seen its launch's epoch on the barrier word (thread 0 only)
+};
+
+// One arrival at a group word; returns the word's value before it (the
+// count of an older epoch reads as 0).
+DEV unsigned long long arrive_word(unsigned long long *w, uint32_t epoch, bool claimed) {
+  const unsigned long long mine = (unsigned long long)epoch << 32;
+  if (!claimed) {
+    unsigned long long cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    while ((uint32_t)(cur >> 32) != epoch) {
+      if (__hip_atomic_compare_exchange_strong(w, &cur, mine | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT))
+        return mine;
     }
-    sm.bu[14] = g0;
-    sm.bu[15] = last ? 1u : 0u;
   }
-  __syncthreads();
-  const bool last = sm.bu[15] != 0u;
-  __syncthreads();
-  return last;
+  return __hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-DEV void group_release(SmemBase &sm, GroupSync *s) {
-  order_release();
-  __syncthreads();
-  if (tidx() == 0) __hip_atomic_store(&s->word, (sm.bu[14] + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// The wait is bounded (~2 s): on expiry the launch is marked aborted (the
-// abort word takes this launch's epoch), every later wait of the launch
-// returns at once and the rows report status 3, so a logic error cannot hang
-// the device.
+// The wait is bounded (~2 s by default): on expiry the launch is marked
+// aborted (the abort word takes this launch's epoch), every later wait of
+// the launch returns at once and the rows report status 3, so a logic error
+// cannot hang the device.
 constexpr uint32_t kSpinLimit = 1u << 26;
-DEV void spin_gen(GroupSync *s, uint32_t g0, uint32_t *abort_word, uint32_t epoch) {
+DEV void spin_gen(const GroupCtx &gc, uint32_t g0) {
   // one coherent load per iteration; the abort word (a peer's expired wait)
-  // and the bound are checked every 256 iterations
+  // and the bound are checked every 256 iterations (every iteration under a
+  // bound below 256)
+  const uint32_t mask = gc.spin_limit < 256u ? 0u : 255u;
   uint32_t spins = 0;
-  while ((__hip_atomic_load(&s->word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 8) == g0) {
-    if ((++spins & 255u) == 0u) {
-      if (__hip_atomic_load(abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch) break;
-      if (spins > kSpinLimit) {
-        __hip_atomic_store(abort_word, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (((uint32_t)__hip_atomic_load(&gc.s->word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 8) == g0) {
+    if ((++spins & mask) == 0u) {
+      if (__hip_atomic_load(gc.abort_word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gc.epoch) break;
+      if (spins > gc.spin_limit) {
+        __hip_atomic_store(gc.abort_word, gc.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         break;
       }
     }
     __builtin_amdgcn_s_sleep(1);
   }
 }
-DEV void group_wait(SmemBase &sm, GroupSync *s, uint32_t *abort_word, uint32_t epoch) {
+
+// Barrier: every wave waits for its own stores, then one arrival; the last
+// arrival resets the count and advances the generation in one store, the
+// others wait for it.
+DEV void group_barrier(SmemBase &sm, GroupCtx &gc) {
+  order_release();
+  __syncthreads();
   if (tidx() == 0) {
-    spin_gen(s, sm.bu[14], abort_word, epoch);
+    const unsigned long long old = arrive_word(&gc.s->word, gc.epoch, gc.claimed);
+    gc.claimed = true;
+    const uint32_t g0 = ((uint32_t)old >> 8) & 0xFFFFFFu;
+    if ((old & 0xFFull) == (unsigned long long)gc.G - 1ull)
+      __hip_atomic_store(&gc.s->word, ((unsigned long long)gc.epoch << 32) | ((unsigned long long)((g0 + 1u) & 0xFFFFFFu) << 8),
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else spin_gen(gc, g0);
     order_acquire();
   }
   __syncthreads();
 }
 
-// Barrier: every wave waits for its own stores, then one atomic add; the
-// last arrival resets the count and advances the generation in one store,
-// the others wait for it.
-DEV void group_barrier(SmemBase &sm, GroupSync *s, int G, uint32_t *abort_word, uint32_t epoch) {
-  order_release();
-  __syncthreads();
-  if (tidx() == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(&s->word, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t g0 = old >> 8;
-    if ((old & 0xFFu) == (uint32_t)G - 1u) __hip_atomic_store(&s->word, (g0 + 1u) << 8, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    else spin_gen(s, g0, abort_word, epoch);
-    order_acquire();
-  }
-  __syncthreads();
+// Arrival at the final exchange of a row: true in the last workgroup to
+// arrive, which resets the count (one lane calls it).
+DEV bool final_arrive(const GroupCtx &gc) {
+  const unsigned long long old = arrive_word(&gc.s->fin, gc.epoch, false);
+  const bool last = (old & 0xFFull) == (unsigned long long)gc.G - 1ull;
+  if (last) __hip_atomic_store(&gc.s->fin, (unsigned long long)gc.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return last;
 }
 
 // An exchange slot's address, computed where it is used from an opaque
@@ -581,15 +589,13 @@ DEV WgSlots *slot_at(const KernelParams &kp, int i) {
 // Per-row context shared by the phases.
 struct RowCtx {
   int row, gid, G, n, n4, s0;
-  GroupSync *gsync;
-  uint32_t *abort_word;
-  uint32_t epoch;
+  GroupCtx gc;
   WgSlots *my;
   WgSlots *peers;
   unsigned *xseq;
 };
 
-DEV void row_barrier(SmemBase &sm, RowCtx &rc) { group_barrier(sm, rc.gsync, rc.G, rc.abort_word, rc.epoch); }
+DEV void row_barrier(SmemBase &sm, RowCtx &rc) { group_barrier(sm, rc.gc); }
 
 // Bins on an absolute grid: abin(z) = floor(z (32 wsc)) with wsc = min(1, T),
 // so a bin is 1/32 nat of the logits x = z T below T = 1 and of z above it.
@@ -1021,7 +1027,8 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
 // the slices' max keys (sm.gk; rows that skipped exchange 2 get their
 // status here) and, with Gumbel-max, the best of the slices' best scores
 // (sm.gd) and their indices (sm.gi), ties to the lower index.
-DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, bool gumbel, bool token_set) {
+DEV void finish_row(const SmemBase &sm, const KernelParams &kp, uint32_t epoch, int row, int G, bool gumbel,
+                    bool token_set) {
   unsigned long long mk = 0;
   for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
   const float mx = key_to_float((uint32_t)(mk >> 32));
@@ -1038,7 +1045,7 @@ DEV void finish_row(const SmemBase &sm, const KernelParams &kp, int row, int G, 
     }
     if (bi != 0x7FFFFFFF) token = bi;
   }
-  const bool aborted = atomic_ld(kp.abort_word) == kp.epoch;
+  const bool aborted = atomic_ld(kp.abort_word) == epoch;
   // token_set: the inverse-CDF selection already wrote the token
   if (!token_set || aborted || status != 0) kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
   if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
@@ -1113,9 +1120,16 @@ DEV RowParam row_from_device(const KernelParams &kp, int r) {
 
 // One thread per row: the records of a step whose per-row parameters live
 // in device memory (the row kernel then reads them like copied records).
+// Thread 0 also advances the device epoch word that the row kernel launched
+// after it reads (bit 31 set: never a host epoch), so that a captured graph's
+// replays are distinct launches.
 __global__ __launch_bounds__(256) void rows_kernel(KernelParams kp, RowParam *out) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r < kp.n_rows) out[r] = row_from_device(kp, r);
+  if (r == 0 && kp.epoch_dev) {
+    const uint32_t e = *kp.epoch_dev;
+    __hip_atomic_store(kp.epoch_dev, ((e + 1u) & 0x7FFFFFFFu) | 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 // ---------------------------------------------------------------- the kernel
@@ -1168,9 +1182,15 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   RowCtx rc;
   rc.gid = gid;
   rc.G = G;
-  rc.gsync = kp.sync + group;
-  rc.abort_word = kp.abort_word;
-  rc.epoch = kp.epoch;
+  // the launch's epoch: from the host, or from the device word that the
+  // records kernel ahead of this launch advanced
+  const uint32_t epoch = kp.epoch_dev ? atomic_ld(kp.epoch_dev) : kp.epoch;
+  rc.gc.s = kp.sync + group;
+  rc.gc.abort_word = kp.abort_word;
+  rc.gc.epoch = epoch;
+  rc.gc.spin_limit = kp.spin_limit ? kp.spin_limit : kSpinLimit;
+  rc.gc.G = G;
+  rc.gc.claimed = false;
   rc.my = kp.slots + (size_t)group * G + gid;
   rc.peers = kp.slots + (size_t)group * G;
   rc.xseq = &xseq;
@@ -1602,7 +1622,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         atomic_st(&rc.my->x1[xp][3], (unsigned long long)__double_as_longlong(wsx));
       }
       const double lmp = minp ? log((double)P.min_p) : 0.0;  // min-p's guess, taken before the wait
-      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
+      group_barrier(sm, rc.gc);
       // ---- exchange 2, merged by every workgroup of the row alike: the
       // records and the first histogram pairs in one batch of 16-byte reads,
       // the row max, each slice's bin shift and mass scale, integer LDS adds
@@ -1813,6 +1833,12 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       }
       __syncthreads();
     }
+    // A row without exchanges meets its peers only in the final exchange; a
+    // group that walks several rows then passes one barrier first, so that
+    // no workgroup arrives at the next row's final exchange (or rewrites its
+    // record of this row, two rows on) before this row's last arrival has
+    // read the records.
+    if (!need_x && kp.n_rows > kp.n_groups) row_barrier(sm, rc);
     const float mf = (float)m;
 
     // ---- 4. exact thresholds from the gathered candidates (exchange 3,
@@ -1962,7 +1988,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         po[j] = 2 * (pj - pg[j] * pps);
         pp[j] = &peers[min(pg[j], G - 1)].cand[xq][pg[j] < G ? po[j] : 0];
       }
-      group_barrier(sm, rc.gsync, G, rc.abort_word, rc.epoch);
+      group_barrier(sm, rc.gc);
       // ---- exchange 3, in every workgroup alike: wave 0 reads the counts and
       // the first candidates of every slice in one batch (pairs of keys; a
       // slot's array has room past an odd count), places them in the list
@@ -2480,12 +2506,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       order_release();
       uint32_t last = 0;
       if (lane == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&rc.gsync->fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        last = old == (uint32_t)G - 1u ? 1u : 0u;
-        if (last) {
-          __hip_atomic_store(&rc.gsync->fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          order_acquire();
-        }
+        last = final_arrive(rc.gc) ? 1u : 0u;
+        if (last) order_acquire();
       }
       if (__builtin_amdgcn_readfirstlane(last)) {
         if (lane < G) {
@@ -2496,7 +2518,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           sm.gk[lane] = u64_of(r1.x, r1.y);
         }
         __builtin_amdgcn_wave_barrier();
-        if (lane == 0) finish_row(sm, kp, row, G, gumbel, icdf);
+        if (lane == 0) finish_row(sm, kp, rc.gc.epoch, row, G, gumbel, icdf);
       }
     };
 
@@ -2645,12 +2667,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       order_release();
       __syncthreads();
       if (tid == 0) {
-        const uint32_t old = __hip_atomic_fetch_add(&rc.gsync->fin, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const bool last = old == (uint32_t)G - 1u;
-        if (last) {
-          __hip_atomic_store(&rc.gsync->fin, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          order_acquire();
-        }
+        const bool last = final_arrive(rc.gc);
+        if (last) order_acquire();
         sm.bu[15] = last ? 1u : 0u;
       }
       __syncthreads();
@@ -2663,7 +2681,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           sm.gk[tid] = u64_of(r1.x, r1.y);
         }
         __syncthreads();
-        if (tid == 0) finish_row(sm, kp, row, G, gumbel, icdf);
+        if (tid == 0) finish_row(sm, kp, rc.gc.epoch, row, G, gumbel, icdf);
         // merge the G local top-logprob lists (keys are distinct: each holds
         // its index): an entry's rank among all entries is its output slot
         unsigned long long *ent = reinterpret_cast<unsigned long long *>(region);
@@ -2754,6 +2772,22 @@ hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool coo
                      : launch_t<float, false>(ka, cooperative, stream, ev0, ev1);
   return penalties ? launch_t<uint16_t, true>(ka, cooperative, stream, ev0, ev1)
                    : launch_t<uint16_t, false>(ka, cooperative, stream, ev0, ev1);
+}
+
+hipError_t kernel_lds_static(size_t *out) {
+  const void *fns[] = {reinterpret_cast<const void *>(&row_kernel<float, true>),
+                       reinterpret_cast<const void *>(&row_kernel<float, false>),
+                       reinterpret_cast<const void *>(&row_kernel<uint16_t, true>),
+                       reinterpret_cast<const void *>(&row_kernel<uint16_t, false>)};
+  size_t m = 0;
+  for (const void *f : fns) {
+    hipFuncAttributes attr;
+    const hipError_t e = hipFuncGetAttributes(&attr, f);
+    if (e != hipSuccess) return e;
+    m = attr.sharedSizeBytes > m ? attr.sharedSizeBytes : m;
+  }
+  *out = m;
+  return hipSuccess;
 }
 
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out) {

@@ -3,8 +3,7 @@
 // Validation, per-row normalisation, the batch predicate, the per-row
 // records (in the kernel arguments for batches of up to kArgRows rows, so a
 // step is one launch and no copy; otherwise through a pinned staging ring
-// and one copy), launch planning (workgroups per row) and the cooperative
-// launch.
+// and one copy), launch planning (workgroups per row) and the launch.
 //
 // Sources (page titles; sections named where used):
 //   [A] "SGLang's +75% sampler speedup skips Qwen3 chat requests"
@@ -45,16 +44,31 @@ void set_msg(std::string &dst, const char *fmt, ...) {
   dst = buf;
 }
 
+// What a launch needs besides its arguments: the row kernel's limits on the
+// device (resident workgroups, LDS plan) and the exchange workspace (group
+// words, per-workgroup exchange slots, the abort word), which holds
+// `resident` workgroups.
+struct Workspace {
+  int device = 0;
+  int resident = 0;       // workgroups of the row kernel that fit at once (and slots of the workspace)
+  int slice_cap = 0;      // largest slice a workgroup holds in LDS
+  int det_slice_cap = 0;  // the slice cap of the largest history and bias hashes (deterministic launches)
+  int hash_slots = 0;     // LDS hash slots for history counts
+  int bias_slots = 0;     // LDS hash slots for logit_bias / stop entries (0: none)
+  GroupSync *sync = nullptr;       // [resident]
+  WgSlots *slots = nullptr;        // [resident]
+  uint32_t *abort_word = nullptr;  // device word: epoch of an aborted launch
+  uint32_t *epoch_dev = nullptr;   // device word: epoch of graph-path launches (advanced on the device), or null
+  uint32_t epoch = 0;              // epoch of the last host-path launch (1 .. 2^31 - 1)
+  // limits the workspace was planned for
+  int32_t max_history_per_row = 0, max_bias_per_row = 0, max_top_logprobs = 0, max_vocab = 0;
+};
+
 }  // namespace
 
 struct sampler_handle {
   sampler_config cfg{};
-  int device = 0;
-  int n_cu = 0;
-  int resident = 0;  // workgroups of the row kernel that fit at once
-  int slice_cap = 0;  // largest slice a workgroup holds in LDS
-  int hash_slots = 0; // LDS hash slots for history counts
-  int bias_slots = 0; // LDS hash slots for logit_bias / stop entries (0: none)
+  Workspace ws;
   RowParam *host_ring = nullptr;   // pinned, kRing slots of max_rows records
   RowParam *dev_ring = nullptr;    // device, kRing slots
   KernelArgs *args = nullptr;      // host: the launch's argument block
@@ -64,10 +78,6 @@ struct sampler_handle {
   hipEvent_t slot_done[kRing] = {};
   bool slot_used[kRing] = {};
   int next_slot = 0;
-  GroupSync *sync = nullptr;
-  WgSlots *slots = nullptr;
-  uint32_t *abort_word = nullptr;  // device word: epoch of an aborted launch
-  uint32_t epoch = 0;
   std::vector<hipEvent_t> prof;  // 2 per recorded step
   int prof_cap = 0;
   int prof_n = 0;
@@ -243,30 +253,27 @@ sampler_status validate_params(const sampler_config *cfg, const sampler_step_arg
   return SAMPLER_OK;
 }
 
-// [A] "One request with top_p takes the whole batch off the fast path":
-// normalize each row, then is_all_greedy / need_top_p / need_top_k /
-// need_min_p decide the path.
+// The path table of [A] "One request with top_p takes the whole batch off
+// the fast path", as two properties of the batch: whether any row samples
+// (top_k > 1 after normalisation; otherwise the batch is greedy), and
+// whether any row truncates (top-k below the whole vocabulary -- greedy rows
+// included, their top_k is 1 -- top-p or min-p), which makes it filtered.
 int choose_path(const sampler_step_args *a, uint32_t flags) {
-  bool all_greedy = true, need_p = false, need_k = false, need_minp = false;
+  bool samples = false, truncates = false;
   for (int r = 0; r < a->n_rows; ++r) {
     const float t = a->temperature ? a->temperature[r] : 1.0f;
-    int32_t k = a->top_k ? a->top_k[r] : -1;
-    if (row_is_greedy(t)) k = 1;
-    else if (k == -1) k = kTopKAll;
-    const float p = a->top_p ? a->top_p[r] : 1.0f;
-    const float mp = a->min_p ? a->min_p[r] : 0.0f;
-    if (!(k <= 1)) all_greedy = false;
-    if (p != 1.0f) need_p = true;
-    if (k != kTopKAll) need_k = true;
-    if (mp > 0.0f) need_minp = true;
+    const int32_t raw = a->top_k ? a->top_k[r] : -1;
+    const int32_t k = row_is_greedy(t) ? 1 : (raw == -1 ? kTopKAll : raw);
+    samples = samples || k > 1;
+    truncates = truncates || k != kTopKAll || (a->top_p && a->top_p[r] != 1.0f) || (a->min_p && a->min_p[r] > 0.0f);
   }
-  if (all_greedy) return PATH_GREEDY;
-  if (!(need_p || need_k || need_minp)) return (flags & SAMPLER_DETERMINISTIC) ? PATH_DETERMINISTIC : PATH_GUMBEL;
-  return PATH_FILTERED;
+  if (!samples) return PATH_GREEDY;
+  if (truncates) return PATH_FILTERED;
+  return (flags & SAMPLER_DETERMINISTIC) ? PATH_DETERMINISTIC : PATH_GUMBEL;
 }
 
-sampler_status hip_fail(sampler_handle *h, hipError_t e, const char *what) {
-  set_msg(h->err, "%s failed: %s", what, hipGetErrorString(e));
+sampler_status hip_fail(std::string &err, hipError_t e, const char *what) {
+  set_msg(err, "%s failed: %s", what, hipGetErrorString(e));
   return SAMPLER_EHIP;
 }
 
@@ -299,48 +306,97 @@ void free_handle(sampler_handle *h) {
   if (h->dev_ring) (void)hipFree(h->dev_ring);
   if (h->graph_rows) (void)hipFree(h->graph_rows);
   delete h->args;
-  if (h->sync) (void)hipFree(h->sync);
-  if (h->slots) (void)hipFree(h->slots);
-  if (h->abort_word) (void)hipFree(h->abort_word);
+  if (h->ws.sync) (void)hipFree(h->ws.sync);
+  if (h->ws.slots) (void)hipFree(h->ws.slots);
+  if (h->ws.abort_word) (void)hipFree(h->ws.abort_word);
+  if (h->ws.epoch_dev) (void)hipFree(h->ws.epoch_dev);
   delete h;
 }
 
-}  // namespace
+int next_pow2_at_least(int v, int lo) {
+  int s = lo;
+  while (s < v) s *= 2;
+  return s;
+}
 
-namespace {
+// The LDS plan of the row kernel for a history and bias limit, and the
+// workgroups that fit on the device at once.  Returns SAMPLER_OK, or a
+// status with a message in err.
+sampler_status plan_workspace(Workspace &ws, int device, int32_t max_hist, int32_t max_bias, int32_t max_vocab,
+                              int32_t max_top_lp, std::string &err) {
+  hipDeviceProp_t prop;
+  hipError_t e = hipGetDeviceProperties(&prop, device);
+  if (e != hipSuccess) return hip_fail(err, e, "hipGetDeviceProperties");
+  ws.device = device;
+  ws.max_history_per_row = max_hist;
+  ws.max_bias_per_row = max_bias;
+  ws.max_vocab = max_vocab;
+  ws.max_top_logprobs = max_top_lp;
+  // LDS plan: fixed part + slice of fp32 values + hash of history counts
+  ws.hash_slots = next_pow2_at_least(2 * max_hist, 64);
+  ws.bias_slots = max_bias > 0 ? next_pow2_at_least(2 * max_bias, 64) : 0;
+  // the dynamic request may use what the kernel's own static LDS leaves
+  size_t lds_static = 0;
+  if ((e = kernel_lds_static(&lds_static)) != hipSuccess) return hip_fail(err, e, "hipFuncGetAttributes");
+  const size_t lds_max = prop.sharedMemPerBlock > lds_static ? prop.sharedMemPerBlock - lds_static : 0;
+  const size_t fixed = kernel_lds_fixed() + kernel_lds_region(kMaxSlice, ws.hash_slots, ws.bias_slots, true);
+  if (lds_max <= fixed + 16 * kBlock) {
+    set_msg(err, "device LDS per workgroup (%zu B) too small", lds_max);
+    return SAMPLER_EHIP;
+  }
+  size_t cap = (lds_max - fixed) / sizeof(float);
+  if (cap > (size_t)kMaxSlice) cap = kMaxSlice;
+  ws.slice_cap = (int)(cap & ~(size_t)3);
+  const size_t fixed_max = kernel_lds_fixed() + kernel_lds_region(kMaxSlice, kMaxHashSlots, 2 * kMaxBiasPerRow, true);
+  size_t dcap = lds_max > fixed_max ? (lds_max - fixed_max) / sizeof(float) : 0;
+  if (dcap > (size_t)kMaxSlice) dcap = kMaxSlice;
+  ws.det_slice_cap = (int)(dcap & ~(size_t)3);
+  if (ws.det_slice_cap < 4) ws.det_slice_cap = ws.slice_cap;
+  if ((int64_t)ws.slice_cap * kMaxG < max_vocab) {
+    set_msg(err, "max_vocab %d exceeds %d (%d workgroups x %d values; lower max_history_per_row to free LDS)",
+            max_vocab, ws.slice_cap * kMaxG, kMaxG, ws.slice_cap);
+    return SAMPLER_ECAPACITY;
+  }
+  e = resident_blocks(device, kernel_lds_bytes(ws.slice_cap, ws.hash_slots, ws.bias_slots, true), &ws.resident);
+  if (e != hipSuccess) return hip_fail(err, e, "the row kernel's occupancy query");
+  if (ws.resident < 1) {
+    err = "the row kernel does not fit on this device";
+    return SAMPLER_EHIP;
+  }
+  return SAMPLER_OK;
+}
 
-// Launch plan (G workgroups per row, rows strided over groups), the kernel
-// parameters and the launch, shared by both step entry points.  `dp`: the
-// device records, or null (records in ka.rows); `dev`: per-row arrays in
-// device memory that the kernel normalises itself (sampler_step_graph).
 // The launch plan: G workgroups of `slice` values per row, `groups` row
 // groups (rows strided over them).
-sampler_status plan_groups(sampler_handle *h, int n, int V, int *G_out, int *slice_out, int *groups_out) {
-  const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
-  const int g_min = (V + h->slice_cap - 1) / h->slice_cap;
-  if (g_min > kMaxG || g_min > h->resident) {
-    set_msg(h->err, "vocab %d needs %d workgroups per row (max %d)", V, g_min,
-            kMaxG < h->resident ? kMaxG : h->resident);
+sampler_status plan_groups(const Workspace &ws, bool det, int n, int V, int *G_out, int *slice_out, int *groups_out,
+                           std::string &err) {
+  // deterministic launches cut every row by the slice cap of the largest
+  // hashes any handle may have, so that the cut -- and with it each row's
+  // reduction order -- depends on V alone, not on the handle's limits
+  const int cap = det ? ws.det_slice_cap : ws.slice_cap;
+  const int g_min = (V + cap - 1) / cap;
+  if (g_min > kMaxG || g_min > ws.resident) {
+    set_msg(err, "vocab %d needs %d workgroups per row (max %d)", V, g_min, kMaxG < ws.resident ? kMaxG : ws.resident);
     return SAMPLER_ECAPACITY;
   }
   int G;
   if (det) {
     G = g_min;  // depends on V only: a row's reduction order is batch invariant
   } else {
-    const int fill = h->resident / n;
+    const int fill = ws.resident / n;
     // at least ~32 values per thread: a row's steps are latency-bound, and
     // fewer workgroups per row exchange faster (measured on MI355X at N=8,
     // V=151,936: 10 workgroups per row 34.7 us, 32 workgroups 41.9 us)
     const int by_work = (V + 32 * kBlock - 1) / (32 * kBlock);
     G = fill < by_work ? fill : by_work;
     if (G > kMaxG) G = kMaxG;
-    if (G > h->resident) G = h->resident;
+    if (G > ws.resident) G = ws.resident;
     if (G < g_min) G = g_min;
   }
   int slice = (V + G - 1) / G;
   slice = (slice + 3) & ~3;
   G = (V + slice - 1) / slice;  // every workgroup gets a non-empty slice
-  const int groups = h->resident / G;
+  const int groups = ws.resident / G;
   *G_out = G;
   *slice_out = slice;
   *groups_out = groups < n ? groups : n;
@@ -374,260 +430,16 @@ int row_cost(const RowParam &p) {
   return 2 * c + ((p.flags & (RF_PEN | RF_SPEC)) ? 1 : 0);
 }
 
-sampler_status plan_and_launch(sampler_handle *h, const sampler_step_args *a, KernelArgs &ka, const RowParam *dp,
-                               bool any_pen, int path, hipStream_t stream, const DevRowArrays *dev = nullptr) {
-  const int n = a->n_rows, V = a->vocab;
-  const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
-  hipError_t e;
-  int G, slice, groups;
-  sampler_status st = plan_groups(h, n, V, &G, &slice, &groups);
-  if (st != SAMPLER_OK) return st;
-  KernelParams &kp = ka.kp;
-  kp = KernelParams{};
-  kp.logits = a->logits;
-  kp.row_stride = a->row_stride;
-  kp.n_rows = n;
-  kp.vocab = V;
-  kp.rows = dp;
-  kp.history_ids = a->history_ids;
-  kp.token_ids = a->token_ids;
-  kp.probs = a->probs;
-  kp.logprobs = a->logprobs;
-  kp.top_lp = a->top_logprobs;
-  kp.top_lp_vals = a->top_logprob_vals;
-  kp.top_lp_ids = a->top_logprob_ids;
-  kp.row_status = a->row_status;
-  kp.G = G;
-  kp.n_groups = groups;
-  kp.slice = slice;
-  kp.hash_slots = h->hash_slots;
-  kp.bias_slots = h->bias_slots;
-  kp.vocab_mask = a->vocab_mask;
-  kp.mask_stride = a->mask_stride;
-  kp.bias_ids = a->bias_ids;
-  kp.bias_vals = a->bias_vals;
-  kp.stop_ids = a->stop_ids;
-  kp.lp_mode = a->logprob_mode != SAMPLER_LOGPROB_PROCESSED ? 1 : 0;
-  kp.icdf = (h->cfg.flags & SAMPLER_INVERSE_CDF) ? 1 : 0;
-  if (dev) {
-    kp.dev = *dev;
-    kp.rows = h->graph_rows;
-  }
-  kp.det = det ? 1 : 0;
-  kp.max_hist = h->cfg.max_history_per_row;
-  kp.max_bias = h->cfg.max_bias_per_row;
-  kp.seed = a->seed;
-  kp.offset = a->offset;
-  const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
-  const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
-  const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);
-  kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0);
-  kp.path = path;
-  kp.sync = h->sync;
-  kp.slots = h->slots;
-  kp.abort_word = h->abort_word;
-  if (++h->epoch == 0) h->epoch = 1;
-  kp.epoch = h->epoch;
-  if (dev && (e = launch_rows(kp, h->graph_rows, stream)) != hipSuccess) return hip_fail(h, e, "rows kernel launch");
-  const bool prof = h->prof_n < h->prof_cap;
-  e = launch_step(ka, a->dtype, any_pen, (h->cfg.flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream,
-                  prof ? h->prof[2 * h->prof_n] : nullptr, prof ? h->prof[2 * h->prof_n + 1] : nullptr);
-  if (e != hipSuccess) return hip_fail(h, e, "kernel launch");
-  if (prof) ++h->prof_n;
-  return SAMPLER_OK;
-}
-
-}  // namespace
-
-extern "C" {
-
-sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
-  if (!out) {
-    g_create_error = "out is NULL";
-    return SAMPLER_EINVAL;
-  }
-  *out = nullptr;
-  if (!cfg) {
-    g_create_error = "cfg is NULL";
-    return SAMPLER_EINVAL;
-  }
-  if (cfg->max_rows < 1 || cfg->max_vocab < 1 || cfg->max_vocab > kMaxVocab || cfg->max_history_per_row < 0 ||
-      cfg->max_history_per_row > kMaxHistPerRow || cfg->max_top_logprobs < 0 ||
-      cfg->max_top_logprobs > kMaxTopLogprobs || cfg->max_bias_per_row < 0 ||
-      cfg->max_bias_per_row > kMaxBiasPerRow ||
-      (cfg->flags &
-       ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH | SAMPLER_INVERSE_CDF))) {
-    set_msg(g_create_error,
-            "bad config: need max_rows >= 1, 1 <= max_vocab <= %d, 0 <= max_history_per_row <= %d, "
-            "0 <= max_top_logprobs <= %d, 0 <= max_bias_per_row <= %d and known flags",
-            kMaxVocab, kMaxHistPerRow, kMaxTopLogprobs, kMaxBiasPerRow);
-    return SAMPLER_EINVAL;
-  }
-  int n_dev = 0;
-  hipError_t e = hipGetDeviceCount(&n_dev);
-  if (e != hipSuccess || n_dev <= 0) {
-    set_msg(g_create_error, "no usable HIP device (%s)", e == hipSuccess ? "none found" : hipGetErrorString(e));
-    (void)hipGetLastError();
-    return SAMPLER_EHIP;
-  }
-  if (cfg->device < 0 || cfg->device >= n_dev) {
-    set_msg(g_create_error, "device %d out of range (0..%d)", cfg->device, n_dev - 1);
-    return SAMPLER_EINVAL;
-  }
-  DeviceGuard guard(cfg->device);
-  if (!guard.ok) {
-    g_create_error = "hipSetDevice failed";
-    return SAMPLER_EHIP;
-  }
-  sampler_handle *h = new (std::nothrow) sampler_handle();
-  if (!h) {
-    g_create_error = "out of host memory";
-    return SAMPLER_EHIP;
-  }
-  h->cfg = *cfg;
-  h->device = cfg->device;
-  hipDeviceProp_t prop;
-  if ((e = hipGetDeviceProperties(&prop, cfg->device)) != hipSuccess) goto fail;
-  h->n_cu = prop.multiProcessorCount;
-  {
-    // LDS plan: fixed part + slice of fp32 values + hash of history counts
-    int slots = 64;
-    while (slots < 2 * cfg->max_history_per_row) slots *= 2;
-    h->hash_slots = slots;
-    int bslots = 0;
-    if (cfg->max_bias_per_row > 0) {
-      bslots = 64;
-      while (bslots < 2 * cfg->max_bias_per_row) bslots *= 2;
-    }
-    h->bias_slots = bslots;
-    const size_t lds_max = prop.sharedMemPerBlock;
-    const size_t fixed = kernel_lds_fixed() + kernel_lds_region(kMaxSlice, slots, bslots, true);
-    if (lds_max <= fixed + 16 * kBlock) {
-      set_msg(g_create_error, "device LDS per workgroup (%zu B) too small", lds_max);
-      free_handle(h);
-      return SAMPLER_EHIP;
-    }
-    size_t cap = (lds_max - fixed) / sizeof(float);
-    if (cap > (size_t)kMaxSlice) cap = kMaxSlice;
-    h->slice_cap = (int)(cap & ~(size_t)3);
-    if ((int64_t)h->slice_cap * kMaxG < cfg->max_vocab) {
-      set_msg(g_create_error, "max_vocab %d exceeds %d (%d workgroups x %d values; lower max_history_per_row "
-              "to free LDS)", cfg->max_vocab, h->slice_cap * kMaxG, kMaxG, h->slice_cap);
-      free_handle(h);
-      return SAMPLER_ECAPACITY;
-    }
-  }
-  if ((e = resident_blocks(cfg->device, kernel_lds_bytes(h->slice_cap, h->hash_slots, h->bias_slots, true),
-                           &h->resident)) !=
-      hipSuccess)
-    goto fail;
-  if (h->resident < 1) {
-    g_create_error = "the row kernel does not fit on this device";
-    free_handle(h);
-    return SAMPLER_EHIP;
-  }
-  {
-    const size_t ring_bytes = sizeof(RowParam) * (size_t)cfg->max_rows * kRing;
-    if ((e = hipHostMalloc((void **)&h->host_ring, ring_bytes, hipHostMallocDefault)) != hipSuccess) goto fail;
-    if ((e = hipMalloc((void **)&h->dev_ring, ring_bytes)) != hipSuccess) goto fail;
-    if ((e = hipMalloc((void **)&h->graph_rows, sizeof(RowParam) * (size_t)cfg->max_rows)) != hipSuccess) goto fail;
-    try {
-      h->recs.resize((size_t)cfg->max_rows);
-      h->rank.resize((size_t)cfg->max_rows);
-      h->order.resize((size_t)cfg->max_rows);
-    } catch (...) {
-      g_create_error = "out of host memory";
-      free_handle(h);
-      return SAMPLER_EHIP;
-    }
-    h->args = new (std::nothrow) KernelArgs();
-    if (!h->args) {
-      g_create_error = "out of host memory";
-      free_handle(h);
-      return SAMPLER_EHIP;
-    }
-    const size_t n_groups_max = (size_t)h->resident;  // one group per resident workgroup at most
-    if ((e = hipMalloc((void **)&h->sync, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
-    if ((e = hipMemset(h->sync, 0, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
-    if ((e = hipMalloc((void **)&h->slots, sizeof(WgSlots) * (size_t)h->resident)) != hipSuccess) goto fail;
-    if ((e = hipMemset(h->slots, 0, sizeof(WgSlots) * (size_t)h->resident)) != hipSuccess) goto fail;
-    if ((e = hipMalloc((void **)&h->abort_word, 256)) != hipSuccess) goto fail;
-    if ((e = hipMemset(h->abort_word, 0, 256)) != hipSuccess) goto fail;
-    for (int s = 0; s < kRing; ++s)
-      if ((e = hipEventCreateWithFlags(&h->slot_done[s], hipEventDisableTiming)) != hipSuccess) goto fail;
-    if ((e = hipDeviceSynchronize()) != hipSuccess) goto fail;
-  }
-  *out = h;
-  return SAMPLER_OK;
-fail:
-  set_msg(g_create_error, "HIP error during create: %s", hipGetErrorString(e));
-  free_handle(h);
-  return SAMPLER_EHIP;
-}
-
-sampler_status sampler_validate(const sampler_config *cfg, const sampler_step_args *args, char *msg,
-                                int32_t msg_len) {
-  std::string m;
-  sampler_status st = validate(cfg, args, m);
-  if (msg && msg_len > 0) {
-    std::snprintf(msg, (size_t)msg_len, "%s", m.c_str());
-  }
-  return st;
-}
-
-sampler_status sampler_select_path(const sampler_step_args *args, uint32_t flags, int32_t *path_out) {
-  std::string m;
-  if (!path_out || !args) return SAMPLER_EINVAL;
-  if (args->n_rows <= 0) return SAMPLER_EINVAL;  // [A]: an empty batch has no path
-  sampler_status st = validate_params(nullptr, args, m);
-  if (st != SAMPLER_OK) return st;
-  *path_out = choose_path(args, flags);
-  return SAMPLER_OK;
-}
-
-sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void *stream_ptr) {
-  if (!h) return SAMPLER_EINVAL;
-  h->err.clear();
-  sampler_status st = validate(&h->cfg, a, h->err);
-  if (st != SAMPLER_OK) return st;
-  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
-  DeviceGuard guard(h->device);
-  if (!guard.ok) {
-    h->err = "hipSetDevice failed";
-    return SAMPLER_EHIP;
-  }
-
-  const int n = a->n_rows, V = a->vocab;
-  const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
-  int path = choose_path(a, h->cfg.flags);
-  if (a->path_out) *a->path_out = path;
-  if (h->cfg.flags & SAMPLER_FORCE_FILTERED) path = PATH_FILTERED;
-
-  // ---- per-row records: in the kernel arguments, or in a staging slot
-  // (waits only when the ring wraps onto a slot whose copy is in flight)
-  const bool inline_rows = n <= kArgRows;
-  KernelArgs &ka = *h->args;
-  int slot = -1;
-  RowParam *rp = ka.rows, *dp = nullptr;
-  if (!inline_rows) {
-    slot = h->next_slot;
-    h->next_slot = (slot + 1) % kRing;
-    if (h->slot_used[slot]) {
-      hipError_t e = hipEventSynchronize(h->slot_done[slot]);
-      if (e != hipSuccess) return hip_fail(h, e, "hipEventSynchronize");
-    }
-    rp = h->host_ring + (size_t)slot * h->cfg.max_rows;
-    dp = h->dev_ring + (size_t)slot * h->cfg.max_rows;
-  }
-  int G, slice, groups;
-  {
-    sampler_status pst = plan_groups(h, n, V, &G, &slice, &groups);
-    if (pst != SAMPLER_OK) return pst;
-  }
-  RowParam *recs = h->recs.data();  // records in row order, placed below
+// The normalised records of rows [r0, r0 + n) of a step, in row order
+// ([A] "One request with top_p ...": 0 <= T < 1e-6 is greedy, T := 1 and
+// top_k := 1; -1 means the whole vocabulary).  Returns whether any row needs
+// the history / bias machinery.
+bool build_records(const sampler_step_args *a, bool det, int r0, int n, RowParam *recs) {
+  const int V = a->vocab;
   bool any_pen = false;
-  for (int r = 0; r < n; ++r) {
-    RowParam &p = recs[r];
+  for (int i = 0; i < n; ++i) {
+    const int r = r0 + i;
+    RowParam &p = recs[i];
     const float t = a->temperature ? a->temperature[r] : 1.0f;
     const bool greedy = row_is_greedy(t);
     int32_t k = a->top_k ? a->top_k[r] : -1;
@@ -679,33 +491,284 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
     p.stream = a->row_stream ? a->row_stream[r] : (det ? 0u : (uint32_t)r);
     p.offset = a->row_offset ? a->row_offset[r] : a->offset;
   }
-  // Place the records: the rows expected to take longest on the groups
-  // whose workgroups start first (a stable counting sort by cost class);
-  // rows past the first pass keep their order.
-  {
-    int *rank = h->rank.data(), *ord = h->order.data();
-    group_start_order(groups, rank);
-    constexpr int kClasses = 12;
-    int start[kClasses] = {};
-    for (int r = 0; r < n; ++r) ++start[row_cost(recs[r])];
-    for (int c = kClasses - 1, acc = 0; c >= 0; --c) {
-      const int cnt = start[c];
-      start[c] = acc;
-      acc += cnt;
-    }
-    for (int r = 0; r < n; ++r) ord[start[row_cost(recs[r])]++] = r;
-    for (int k = 0; k < n; ++k) rp[k < groups ? rank[k] : k] = recs[ord[k]];
+  return any_pen;
+}
+
+// Place n records: the rows expected to take longest on the groups whose
+// workgroups start first (a stable counting sort by cost class); rows past
+// the first pass keep their order.  rank and ord hold n ints each.
+void place_records(const RowParam *recs, int n, int groups, int *rank, int *ord, RowParam *out) {
+  group_start_order(groups, rank);
+  constexpr int kClasses = 12;
+  int start[kClasses] = {};
+  for (int r = 0; r < n; ++r) ++start[row_cost(recs[r])];
+  for (int c = kClasses - 1, acc = 0; c >= 0; --c) {
+    const int cnt = start[c];
+    start[c] = acc;
+    acc += cnt;
   }
+  for (int r = 0; r < n; ++r) ord[start[row_cost(recs[r])]++] = r;
+  for (int k = 0; k < n; ++k) out[k < groups ? rank[k] : k] = recs[ord[k]];
+}
+
+// Kernel parameters for n rows of a step and the launch.  `dp`: the device
+// records, or null (records in ka.rows); `dev`: per-row arrays in device
+// memory that rows_kernel normalises into `graph_rows` first
+// (sampler_step_graph).
+sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_limit, const sampler_step_args *a,
+                               int n, KernelArgs &ka, const RowParam *dp, bool any_pen, int path, hipStream_t stream,
+                               std::string &err, const DevRowArrays *dev = nullptr, RowParam *graph_rows = nullptr,
+                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+  const int V = a->vocab;
+  const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
+  hipError_t e;
+  int G, slice, groups;
+  sampler_status st = plan_groups(ws, det, n, V, &G, &slice, &groups, err);
+  if (st != SAMPLER_OK) return st;
+  KernelParams &kp = ka.kp;
+  kp = KernelParams{};
+  kp.logits = a->logits;
+  kp.row_stride = a->row_stride;
+  kp.n_rows = n;
+  kp.vocab = V;
+  kp.rows = dp;
+  kp.history_ids = a->history_ids;
+  kp.token_ids = a->token_ids;
+  kp.probs = a->probs;
+  kp.logprobs = a->logprobs;
+  kp.top_lp = a->top_logprobs;
+  kp.top_lp_vals = a->top_logprob_vals;
+  kp.top_lp_ids = a->top_logprob_ids;
+  kp.row_status = a->row_status;
+  kp.G = G;
+  kp.n_groups = groups;
+  kp.slice = slice;
+  kp.hash_slots = ws.hash_slots;
+  kp.bias_slots = ws.bias_slots;
+  kp.vocab_mask = a->vocab_mask;
+  kp.mask_stride = a->mask_stride;
+  kp.bias_ids = a->bias_ids;
+  kp.bias_vals = a->bias_vals;
+  kp.stop_ids = a->stop_ids;
+  kp.lp_mode = a->logprob_mode != SAMPLER_LOGPROB_PROCESSED ? 1 : 0;
+  kp.icdf = (flags & SAMPLER_INVERSE_CDF) ? 1 : 0;
+  if (dev) {
+    kp.dev = *dev;
+    kp.rows = graph_rows;
+  }
+  kp.det = det ? 1 : 0;
+  kp.max_hist = ws.max_history_per_row;
+  kp.max_bias = ws.max_bias_per_row;
+  kp.seed = a->seed;
+  kp.offset = a->offset;
+  const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
+  const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
+  const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);
+  kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0);
+  kp.path = path;
+  kp.sync = ws.sync;
+  kp.slots = ws.slots;
+  kp.abort_word = ws.abort_word;
+  // every launch has its own epoch: host launches count up through
+  // 1 .. 2^31 - 1; graph-path launches read theirs from a device word that
+  // rows_kernel advances (bit 31 set), so each replay of a captured graph is
+  // a launch of its own
+  ws.epoch = (ws.epoch & 0x7FFFFFFFu) + 1u;
+  if (ws.epoch == 0x80000000u) ws.epoch = 1;
+  kp.epoch = ws.epoch;
+  kp.epoch_dev = dev ? ws.epoch_dev : nullptr;
+  kp.spin_limit = (uint32_t)wait_spin_limit;
+  if (dev && (e = launch_rows(kp, graph_rows, stream)) != hipSuccess) return hip_fail(err, e, "rows kernel launch");
+  e = launch_step(ka, a->dtype, any_pen, (flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream, ev0, ev1);
+  if (e != hipSuccess) return hip_fail(err, e, "kernel launch");
+  return SAMPLER_OK;
+}
+
+// The path a step runs under: the predicate's, unless a SAMPLER_FORCE_*
+// flag names another.
+int run_path(int predicate_path, uint32_t flags) {
+  if (flags & SAMPLER_FORCE_FILTERED) return PATH_FILTERED;
+  if (flags & SAMPLER_FORCE_PATH_GUMBEL) return PATH_GUMBEL;
+  if (flags & SAMPLER_FORCE_PATH_GREEDY) return PATH_GREEDY;
+  return predicate_path;
+}
+
+bool flags_ok(uint32_t flags) {
+  return !(flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH |
+                     SAMPLER_INVERSE_CDF | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL)) &&
+         __builtin_popcount(flags & (SAMPLER_FORCE_FILTERED | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL)) <= 1;
+}
+
+}  // namespace
+
+extern "C" {
+
+sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
+  if (!out) {
+    g_create_error = "out is NULL";
+    return SAMPLER_EINVAL;
+  }
+  *out = nullptr;
+  if (!cfg) {
+    g_create_error = "cfg is NULL";
+    return SAMPLER_EINVAL;
+  }
+  if (cfg->max_rows < 1 || cfg->max_vocab < 1 || cfg->max_vocab > kMaxVocab || cfg->max_history_per_row < 0 ||
+      cfg->max_history_per_row > kMaxHistPerRow || cfg->max_top_logprobs < 0 ||
+      cfg->max_top_logprobs > kMaxTopLogprobs || cfg->max_bias_per_row < 0 ||
+      cfg->max_bias_per_row > kMaxBiasPerRow || cfg->wait_spin_limit < 0 || !flags_ok(cfg->flags)) {
+    set_msg(g_create_error,
+            "bad config: need max_rows >= 1, 1 <= max_vocab <= %d, 0 <= max_history_per_row <= %d, "
+            "0 <= max_top_logprobs <= %d, 0 <= max_bias_per_row <= %d, wait_spin_limit >= 0, known flags and "
+            "at most one SAMPLER_FORCE_* flag",
+            kMaxVocab, kMaxHistPerRow, kMaxTopLogprobs, kMaxBiasPerRow);
+    return SAMPLER_EINVAL;
+  }
+  int n_dev = 0;
+  hipError_t e = hipGetDeviceCount(&n_dev);
+  if (e != hipSuccess || n_dev <= 0) {
+    set_msg(g_create_error, "no usable HIP device (%s)", e == hipSuccess ? "none found" : hipGetErrorString(e));
+    (void)hipGetLastError();
+    return SAMPLER_EHIP;
+  }
+  if (cfg->device < 0 || cfg->device >= n_dev) {
+    set_msg(g_create_error, "device %d out of range (0..%d)", cfg->device, n_dev - 1);
+    return SAMPLER_EINVAL;
+  }
+  DeviceGuard guard(cfg->device);
+  if (!guard.ok) {
+    g_create_error = "hipSetDevice failed";
+    return SAMPLER_EHIP;
+  }
+  sampler_handle *h = new (std::nothrow) sampler_handle();
+  if (!h) {
+    g_create_error = "out of host memory";
+    return SAMPLER_EHIP;
+  }
+  h->cfg = *cfg;
+  {
+    const sampler_status st = plan_workspace(h->ws, cfg->device, cfg->max_history_per_row, cfg->max_bias_per_row,
+                                             cfg->max_vocab, cfg->max_top_logprobs, g_create_error);
+    if (st != SAMPLER_OK) {
+      free_handle(h);
+      return st;
+    }
+  }
+  {
+    Workspace &ws = h->ws;
+    const size_t ring_bytes = sizeof(RowParam) * (size_t)cfg->max_rows * kRing;
+    if ((e = hipHostMalloc((void **)&h->host_ring, ring_bytes, hipHostMallocDefault)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&h->dev_ring, ring_bytes)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&h->graph_rows, sizeof(RowParam) * (size_t)cfg->max_rows)) != hipSuccess) goto fail;
+    try {
+      h->recs.resize((size_t)cfg->max_rows);
+      h->rank.resize((size_t)cfg->max_rows);
+      h->order.resize((size_t)cfg->max_rows);
+    } catch (...) {
+      g_create_error = "out of host memory";
+      free_handle(h);
+      return SAMPLER_EHIP;
+    }
+    h->args = new (std::nothrow) KernelArgs();
+    if (!h->args) {
+      g_create_error = "out of host memory";
+      free_handle(h);
+      return SAMPLER_EHIP;
+    }
+    const size_t n_groups_max = (size_t)ws.resident;  // one group per resident workgroup at most
+    if ((e = hipMalloc((void **)&ws.sync, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
+    if ((e = hipMemset(ws.sync, 0, sizeof(GroupSync) * n_groups_max)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&ws.slots, sizeof(WgSlots) * (size_t)ws.resident)) != hipSuccess) goto fail;
+    if ((e = hipMemset(ws.slots, 0, sizeof(WgSlots) * (size_t)ws.resident)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&ws.abort_word, 256)) != hipSuccess) goto fail;
+    if ((e = hipMemset(ws.abort_word, 0, 256)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&ws.epoch_dev, 256)) != hipSuccess) goto fail;
+    if ((e = hipMemset(ws.epoch_dev, 0, 256)) != hipSuccess) goto fail;
+    for (int s = 0; s < kRing; ++s)
+      if ((e = hipEventCreateWithFlags(&h->slot_done[s], hipEventDisableTiming)) != hipSuccess) goto fail;
+    if ((e = hipDeviceSynchronize()) != hipSuccess) goto fail;
+  }
+  *out = h;
+  return SAMPLER_OK;
+fail:
+  set_msg(g_create_error, "HIP error during create: %s", hipGetErrorString(e));
+  free_handle(h);
+  return SAMPLER_EHIP;
+}
+
+sampler_status sampler_validate(const sampler_config *cfg, const sampler_step_args *args, char *msg,
+                                int32_t msg_len) {
+  std::string m;
+  sampler_status st = validate(cfg, args, m);
+  if (msg && msg_len > 0) {
+    std::snprintf(msg, (size_t)msg_len, "%s", m.c_str());
+  }
+  return st;
+}
+
+sampler_status sampler_select_path(const sampler_step_args *args, uint32_t flags, int32_t *path_out) {
+  std::string m;
+  if (!path_out || !args) return SAMPLER_EINVAL;
+  if (args->n_rows <= 0) return SAMPLER_EINVAL;  // [A]: an empty batch has no path
+  sampler_status st = validate_params(nullptr, args, m);
+  if (st != SAMPLER_OK) return st;
+  *path_out = choose_path(args, flags);
+  return SAMPLER_OK;
+}
+
+sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void *stream_ptr) {
+  if (!h) return SAMPLER_EINVAL;
+  h->err.clear();
+  sampler_status st = validate(&h->cfg, a, h->err);
+  if (st != SAMPLER_OK) return st;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  DeviceGuard guard(h->ws.device);
+  if (!guard.ok) {
+    h->err = "hipSetDevice failed";
+    return SAMPLER_EHIP;
+  }
+
+  const int n = a->n_rows, V = a->vocab;
+  const bool det = (h->cfg.flags & SAMPLER_DETERMINISTIC) != 0;
+  const int pred = choose_path(a, h->cfg.flags);
+  if (a->path_out) *a->path_out = pred;
+  const int path = run_path(pred, h->cfg.flags);
+
+  // ---- per-row records: in the kernel arguments, or in a staging slot
+  // (waits only when the ring wraps onto a slot whose copy is in flight)
+  const bool inline_rows = n <= kArgRows;
+  KernelArgs &ka = *h->args;
+  int slot = -1;
+  RowParam *rp = ka.rows, *dp = nullptr;
+  if (!inline_rows) {
+    slot = h->next_slot;
+    h->next_slot = (slot + 1) % kRing;
+    if (h->slot_used[slot]) {
+      hipError_t e = hipEventSynchronize(h->slot_done[slot]);
+      if (e != hipSuccess) return hip_fail(h->err, e, "hipEventSynchronize");
+    }
+    rp = h->host_ring + (size_t)slot * h->cfg.max_rows;
+    dp = h->dev_ring + (size_t)slot * h->cfg.max_rows;
+  }
+  int G, slice, groups;
+  st = plan_groups(h->ws, det, n, V, &G, &slice, &groups, h->err);
+  if (st != SAMPLER_OK) return st;
+  const bool any_pen = build_records(a, det, 0, n, h->recs.data());
+  place_records(h->recs.data(), n, groups, h->rank.data(), h->order.data(), rp);
   hipError_t e;
   if (!inline_rows) {
     e = hipMemcpyAsync(dp, rp, sizeof(RowParam) * (size_t)n, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) return hip_fail(h, e, "hipMemcpyAsync");
+    if (e != hipSuccess) return hip_fail(h->err, e, "hipMemcpyAsync");
     e = hipEventRecord(h->slot_done[slot], stream);
-    if (e != hipSuccess) return hip_fail(h, e, "hipEventRecord");
+    if (e != hipSuccess) return hip_fail(h->err, e, "hipEventRecord");
     h->slot_used[slot] = true;
   }
-
-  return plan_and_launch(h, a, ka, dp, any_pen, path, stream);
+  const bool prof = h->prof_n < h->prof_cap;
+  st = plan_and_launch(h->ws, h->cfg.flags, h->cfg.wait_spin_limit, a, n, ka, dp, any_pen, path, stream, h->err,
+                       nullptr, nullptr, prof ? h->prof[2 * h->prof_n] : nullptr,
+                       prof ? h->prof[2 * h->prof_n + 1] : nullptr);
+  if (st == SAMPLER_OK && prof) ++h->prof_n;
+  return st;
 }
 
 sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a, const sampler_device_params *dp,
@@ -736,7 +799,7 @@ sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a,
   // checked on the device)
   sampler_status st = validate(&h->cfg, a, h->err);
   if (st != SAMPLER_OK) return st;
-  DeviceGuard guard(h->device);
+  DeviceGuard guard(h->ws.device);
   if (!guard.ok) {
     h->err = "hipSetDevice failed";
     return SAMPLER_EHIP;
@@ -763,13 +826,24 @@ sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a,
   dev.output_len = dp->output_len;
   // the penalty / bias machinery whenever a row could use it
   const bool any_pen = (dp->history_len && a->history_ids) || dp->bias_len || (dp->min_tokens && dp->stop_len);
-  return plan_and_launch(h, a, *h->args, nullptr, any_pen, PATH_FILTERED, reinterpret_cast<hipStream_t>(stream_ptr),
-                         &dev);
+  const bool prof = h->prof_n < h->prof_cap;
+  sampler_status lst = plan_and_launch(h->ws, h->cfg.flags, h->cfg.wait_spin_limit, a, a->n_rows, *h->args, nullptr,
+                                       any_pen, PATH_FILTERED, reinterpret_cast<hipStream_t>(stream_ptr), h->err, &dev,
+                                       h->graph_rows, prof ? h->prof[2 * h->prof_n] : nullptr,
+                                       prof ? h->prof[2 * h->prof_n + 1] : nullptr);
+  if (lst == SAMPLER_OK && prof) ++h->prof_n;
+  return lst;
+}
+
+sampler_status sampler_set_wait_spin_limit(sampler_handle *h, int32_t limit) {
+  if (!h || limit < 0) return SAMPLER_EINVAL;
+  h->cfg.wait_spin_limit = limit;
+  return SAMPLER_OK;
 }
 
 sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity) {
   if (!h || capacity < 1) return SAMPLER_EINVAL;
-  DeviceGuard guard(h->device);
+  DeviceGuard guard(h->ws.device);
   free_profile(h);
   h->prof.resize(2 * (size_t)capacity);
   for (auto &ev : h->prof) {
@@ -777,7 +851,7 @@ sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity) {
     if (e != hipSuccess) {
       ev = nullptr;
       free_profile(h);
-      return hip_fail(h, e, "hipEventCreate");
+      return hip_fail(h->err, e, "hipEventCreate");
     }
   }
   h->prof_cap = capacity;
@@ -787,14 +861,14 @@ sampler_status sampler_profile_start(sampler_handle *h, int32_t capacity) {
 
 sampler_status sampler_profile_stop(sampler_handle *h, float *ms, int32_t cap, int32_t *n) {
   if (!h || !n || (cap > 0 && !ms)) return SAMPLER_EINVAL;
-  DeviceGuard guard(h->device);
+  DeviceGuard guard(h->ws.device);
   int k = 0;
   for (int i = 0; i < h->prof_n && i < cap; ++i) {
     hipError_t e = hipEventSynchronize(h->prof[2 * i + 1]);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms[k], h->prof[2 * i], h->prof[2 * i + 1]);
     if (e != hipSuccess) {
       free_profile(h);
-      return hip_fail(h, e, "hipEventElapsedTime");
+      return hip_fail(h->err, e, "hipEventElapsedTime");
     }
     ++k;
   }
@@ -805,7 +879,7 @@ sampler_status sampler_profile_stop(sampler_handle *h, float *ms, int32_t cap, i
 
 void sampler_destroy(sampler_handle *h) {
   if (!h) return;
-  DeviceGuard guard(h->device);
+  DeviceGuard guard(h->ws.device);
   free_handle(h);
 }
 

@@ -88,6 +88,18 @@ typedef enum sampler_dtype {
  * unchanged.  With SAMPLER_DETERMINISTIC the result of a row does not
  * depend on its batch. */
 #define SAMPLER_INVERSE_CDF (1u << 3)
+/* A/B switches of the selection path (the role of the page's
+ * SGLANG_OPT_USE_GUMBEL_SAMPLE switch, [A] "Nine lines, and exactly one call
+ * site"), at most one SAMPLER_FORCE_* flag per handle; path_out still
+ * reports the predicate's choice:
+ *   SAMPLER_FORCE_PATH_GREEDY: every row takes the first argmax, the greedy
+ *     path's selection, whatever its parameters; probs, logprobs and top
+ *     logprobs still follow each row's own parameters.
+ *   SAMPLER_FORCE_PATH_GUMBEL: the step runs under the Gumbel label; the
+ *     kernel selects per row (argmax for top_k == 1, Gumbel-max over the
+ *     kept set otherwise), so the outputs equal the unforced step's. */
+#define SAMPLER_FORCE_PATH_GREEDY (1u << 4)
+#define SAMPLER_FORCE_PATH_GUMBEL (1u << 5)
 
 typedef struct sampler_config {
   int32_t max_rows;            /* largest n_rows a step may pass (>= 1) */
@@ -95,9 +107,16 @@ typedef struct sampler_config {
   int32_t max_history_per_row; /* largest history_len of one row (0..4096) */
   int32_t max_top_logprobs;    /* largest top_logprobs (0..32) */
   int32_t device;              /* HIP device ordinal */
-  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH |
-                                  SAMPLER_INVERSE_CDF */
+  uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_COOPERATIVE_LAUNCH | SAMPLER_INVERSE_CDF |
+                                  one of SAMPLER_FORCE_FILTERED, SAMPLER_FORCE_PATH_GREEDY,
+                                  SAMPLER_FORCE_PATH_GUMBEL */
   int32_t max_bias_per_row;    /* largest bias_len + active stop_len of one row (0..512) */
+  /* Bound of every wait of one workgroup for another, in polls of the group
+   * word: 0 (the default) is ~2 s.  A wait that expires marks the step
+   * aborted: its rows get row_status 3 (outputs not valid) and every later
+   * wait of that step returns at once; later steps are unaffected.  Values
+   * of 1 force that path (tests of the failure handling). */
+  int32_t wait_spin_limit;
 } sampler_config;
 
 typedef struct sampler_handle sampler_handle;
@@ -308,6 +327,11 @@ sampler_status sampler_select_path(const sampler_step_args *args, uint32_t flags
  * message into msg (when non-NULL, msg_len > 0). */
 sampler_status sampler_validate(const sampler_config *cfg, const sampler_step_args *args, char *msg,
                                 int32_t msg_len);
+
+/* Change the handle's wait bound (sampler_config.wait_spin_limit; 0 is the
+ * default ~2 s) for the steps enqueued from now on.  A captured graph keeps
+ * the bound it was captured with.  SAMPLER_EINVAL for limit < 0. */
+sampler_status sampler_set_wait_spin_limit(sampler_handle *h, int32_t limit);
 
 /* Profiling: from now on each step records a HIP event pair that brackets
  * its sampling kernel's execution on the step's stream (hipExtLaunchKernel's

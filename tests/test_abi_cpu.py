@@ -58,7 +58,7 @@ def test_predicate_agrees_with_oracle_on_random_batches(lib):
     for _ in range(300):
         n = int(rng.integers(1, 9))
         T = rng.choice(np.array([0.0, 5e-7, 0.5, 1.0, 1.3], np.float32), n)
-        k = rng.choice(np.array([-1, -1, -1, 1, 5, 50], np.int32), n)
+        k = rng.choice(np.array([-1, -1, -1, 1, 5, 50, 1 << 30], np.int32), n)
         p = rng.choice(np.array([1.0, 1.0, 0.9], np.float32), n)
         mp = rng.choice(np.array([0.0, 0.0, 0.05], np.float32), n)
         det = bool(rng.integers(0, 2))
@@ -185,3 +185,37 @@ def test_create_rejects_bad_config(lib):
     bad = dsts.Config(max_rows=0, max_vocab=1024, max_history_per_row=0, max_top_logprobs=0, device=0, flags=0)
     assert lib.sampler_create(ctypes.byref(bad), ctypes.byref(h)) in (dsts.SAMPLER_EINVAL, dsts.SAMPLER_EHIP)
     assert not h.value
+
+
+def test_create_rejects_two_force_flags(lib):
+    h = ctypes.c_void_p()
+    for flags in (dsts.FLAG_FORCE_FILTERED | dsts.FLAG_FORCE_PATH_GREEDY,
+                  dsts.FLAG_FORCE_PATH_GREEDY | dsts.FLAG_FORCE_PATH_GUMBEL, 1 << 9):
+        cfg = dsts.Config(max_rows=4, max_vocab=1024, max_history_per_row=0, max_top_logprobs=0, device=0,
+                          flags=flags)
+        assert lib.sampler_create(ctypes.byref(cfg), ctypes.byref(h)) == dsts.SAMPLER_EINVAL
+        assert not h.value
+    cfg = dsts.Config(max_rows=4, max_vocab=1024, device=0, wait_spin_limit=-1)
+    assert lib.sampler_create(ctypes.byref(cfg), ctypes.byref(h)) == dsts.SAMPLER_EINVAL
+
+
+def test_set_wait_spin_limit_rejects_bad_arguments(lib):
+    assert lib.sampler_set_wait_spin_limit(None, 0) == dsts.SAMPLER_EINVAL
+
+
+def test_binding_checks_device_tensors():
+    # the binding refuses tensors the kernel would misread: wrong dtype,
+    # wrong device, non-contiguous, wrong shape, spans past the buffer
+    import torch
+    from decode_step_token_sampler_amd import _check_spans, _check_tensor
+    dev = torch.device("cuda", 0)
+    with pytest.raises(ValueError, match="CUDA"):
+        _check_tensor(torch.zeros(4, dtype=torch.int32), "history_ids", torch.int32, dev)
+    starts, lens = np.array([0, 6], np.int64), np.array([4, 4], np.int32)
+    with pytest.raises(ValueError, match="outside"):
+        _check_spans("history_ids", 8, starts, lens)
+    _check_spans("history_ids", 10, starts, lens)
+    _check_spans("history_ids", 8, starts, np.array([4, 0], np.int32))  # empty spans may point anywhere
+    with pytest.raises(ValueError, match="outside"):
+        _check_spans("bias_ids", 8, np.array([-1], np.int64), np.array([1], np.int32))
+
