@@ -37,7 +37,7 @@ FLAG_FORCE_PATH_GUMBEL = 1 << 5
 # symbols the header declares
 EXPORTS = ("sampler_create", "sampler_step", "sampler_step_graph", "sampler_select_path", "sampler_validate",
            "sampler_destroy", "sampler_last_error", "sampler_profile_start", "sampler_profile_stop",
-           "sampler_set_wait_spin_limit")
+           "sampler_set_wait_spin_limit", "sampler_step_noalloc", "sampler_noalloc_last_error")
 
 
 class SamplerError(RuntimeError):
@@ -154,6 +154,10 @@ def load_library(path: str = LIB_PATH):
     L.sampler_profile_stop.restype = ctypes.c_int
     L.sampler_set_wait_spin_limit.argtypes = [ctypes.c_void_p, ctypes.c_int32]
     L.sampler_set_wait_spin_limit.restype = ctypes.c_int
+    L.sampler_step_noalloc.argtypes = [ctypes.POINTER(StepArgs), ctypes.c_uint32, ctypes.c_int32, ctypes.c_void_p]
+    L.sampler_step_noalloc.restype = ctypes.c_int
+    L.sampler_noalloc_last_error.argtypes = []
+    L.sampler_noalloc_last_error.restype = ctypes.c_char_p
     L.sampler_last_error.argtypes = [ctypes.c_void_p]
     L.sampler_last_error.restype = ctypes.c_char_p
     _lib = L
@@ -347,6 +351,21 @@ def _prepare_step(logits, *, vocab: Optional[int] = None, temperature=None, top_
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
     return a, o, path, (m, path), s
 
+
+
+def step_noalloc(logits, *, flags: int = 0, **kw) -> dict:
+    """One decode step through sampler_step_noalloc (no handle; the library's
+    fixed scratch array on the logits' GPU).  Keywords as for Sampler.step;
+    ``flags``: FLAG_DETERMINISTIC, FLAG_INVERSE_CDF and at most one FORCE
+    flag."""
+    L = load_library()
+    a, o, path, keep, s = _prepare_step(logits, **kw)
+    st = L.sampler_step_noalloc(ctypes.byref(a), int(flags), int(logits.device.index or 0), ctypes.c_void_p(s))
+    if st != SAMPLER_OK:
+        raise SamplerError(st, L.sampler_noalloc_last_error().decode())
+    o["path"] = PATH_NAMES[path.value]
+    del keep
+    return o
 
 
 class Sampler:

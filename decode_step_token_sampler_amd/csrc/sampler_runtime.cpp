@@ -3,7 +3,9 @@
 // Validation, per-row normalisation, the batch predicate, the per-row
 // records (in the kernel arguments for batches of up to kArgRows rows, so a
 // step is one launch and no copy; otherwise through a pinned staging ring
-// and one copy), launch planning (workgroups per row) and the launch.
+// and one copy), launch planning (workgroups per row) and the launch.  A
+// step's exchange workspace is a handle's allocation, or, for
+// sampler_step_noalloc, the library's fixed scratch array.
 //
 // Sources (page titles; sections named where used):
 //   [A] "SGLang's +75% sampler speedup skips Qwen3 chat requests"
@@ -15,6 +17,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -599,6 +602,66 @@ bool flags_ok(uint32_t flags) {
          __builtin_popcount(flags & (SAMPLER_FORCE_FILTERED | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL)) <= 1;
 }
 
+// ---------------------------------------------------------------- no-alloc scratch
+// The exchange workspace of sampler_step_noalloc, for callers that cannot
+// allocate: group words, exchange slots and the abort word of kScratchWgs
+// workgroups (one per compute unit of an MI355X), in one file-scope device
+// array.  Every GPU the library runs on holds its own copy until the process
+// ends; host code reaches a device's copy only through the address that
+// hipGetSymbolAddress gave for that device, never through the array's name.
+constexpr int kScratchWgs = 256;
+constexpr size_t kScratchSync = 0;
+constexpr size_t kScratchSlots = ((sizeof(GroupSync) * kScratchWgs + 255) / 256) * 256;
+constexpr size_t kScratchAbort = kScratchSlots + ((sizeof(WgSlots) * kScratchWgs + 255) / 256) * 256;
+constexpr size_t kScratchBytes = kScratchAbort + 256;
+
+}  // namespace
+
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+struct StaticDevice {
+  bool ready = false;
+  Workspace ws;
+  sampler_status st = SAMPLER_OK;
+  std::string err;  // the set-up failure, if any
+};
+std::mutex g_static_mu;
+StaticDevice g_static[kMaxDevices];
+thread_local std::string g_static_error;
+thread_local KernelArgs g_static_args;  // the launch's argument block (copied at launch)
+
+// Set up device `dev` for sampler_step_noalloc once: its scratch address and
+// the row kernel's plan for the largest history, bias and top-logprob
+// limits.  Called with g_static_mu held and `dev` current.
+sampler_status static_setup(int dev) {
+  StaticDevice &sd = g_static[dev];
+  if (sd.ready) return sd.st;
+  sd.ready = true;
+  unsigned char *ptr = nullptr;
+  hipError_t e = hipGetSymbolAddress(reinterpret_cast<void **>(&ptr), HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !ptr) {
+    set_msg(sd.err, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    return sd.st = SAMPLER_EHIP;
+  }
+  Workspace &ws = sd.ws;
+  sd.st = plan_workspace(ws, dev, kMaxHistPerRow, kMaxBiasPerRow, kMaxVocab, kMaxTopLogprobs, sd.err);
+  if (sd.st == SAMPLER_ECAPACITY) {
+    // the largest vocabulary the plan allows
+    const int V = ws.slice_cap * kMaxG;
+    sd.st = plan_workspace(ws, dev, kMaxHistPerRow, kMaxBiasPerRow, V, kMaxTopLogprobs, sd.err);
+  }
+  if (sd.st != SAMPLER_OK) return sd.st;
+  if (ws.resident > kScratchWgs) ws.resident = kScratchWgs;
+  ws.sync = reinterpret_cast<GroupSync *>(ptr + kScratchSync);
+  ws.slots = reinterpret_cast<WgSlots *>(ptr + kScratchSlots);
+  ws.abort_word = reinterpret_cast<uint32_t *>(ptr + kScratchAbort);
+  ws.epoch_dev = nullptr;
+  return SAMPLER_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -770,6 +833,71 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   if (st == SAMPLER_OK && prof) ++h->prof_n;
   return st;
 }
+
+sampler_status sampler_step_noalloc(const sampler_step_args *a, uint32_t flags, int32_t device, void *stream_ptr) {
+  g_static_error.clear();
+  if (!flags_ok(flags) || (flags & SAMPLER_COOPERATIVE_LAUNCH)) {
+    g_static_error = "flags: SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF and at most one SAMPLER_FORCE_* flag";
+    return SAMPLER_EINVAL;
+  }
+  int n_dev = 0;
+  hipError_t e = hipGetDeviceCount(&n_dev);
+  if (e != hipSuccess || n_dev <= 0) {
+    set_msg(g_static_error, "no usable HIP device (%s)", e == hipSuccess ? "none found" : hipGetErrorString(e));
+    (void)hipGetLastError();
+    return SAMPLER_EHIP;
+  }
+  if (device < 0 || device >= n_dev || device >= kMaxDevices) {
+    set_msg(g_static_error, "device %d out of range (0..%d)", device, (n_dev < kMaxDevices ? n_dev : kMaxDevices) - 1);
+    return SAMPLER_EINVAL;
+  }
+  DeviceGuard guard(device);
+  if (!guard.ok) {
+    g_static_error = "hipSetDevice failed";
+    return SAMPLER_EHIP;
+  }
+  std::lock_guard<std::mutex> lock(g_static_mu);
+  sampler_status st = static_setup(device);
+  if (st != SAMPLER_OK) {
+    g_static_error = g_static[device].err;
+    return st;
+  }
+  Workspace &ws = g_static[device].ws;
+  // the limits of the scratch plan; any number of rows (launched in pieces)
+  sampler_config cfg{};
+  cfg.max_rows = a ? (a->n_rows > 0 ? a->n_rows : 1) : 1;
+  cfg.max_vocab = ws.max_vocab;
+  cfg.max_history_per_row = ws.max_history_per_row;
+  cfg.max_top_logprobs = ws.max_top_logprobs;
+  cfg.max_bias_per_row = ws.max_bias_per_row;
+  cfg.device = device;
+  cfg.flags = flags;
+  st = validate(&cfg, a, g_static_error);
+  if (st != SAMPLER_OK) return st;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
+  const int pred = choose_path(a, flags);
+  if (a->path_out) *a->path_out = pred;
+  const int path = run_path(pred, flags);
+  // rows in pieces of up to kArgRows, each one launch with its records in
+  // the kernel arguments; the pieces share the scratch in stream order
+  for (int r0 = 0; r0 < a->n_rows; r0 += kArgRows) {
+    const int n = a->n_rows - r0 < kArgRows ? a->n_rows - r0 : kArgRows;
+    int G, slice, groups;
+    st = plan_groups(ws, det, n, a->vocab, &G, &slice, &groups, g_static_error);
+    if (st != SAMPLER_OK) return st;
+    RowParam recs[kArgRows];
+    int rank[kArgRows], ord[kArgRows];
+    KernelArgs &ka = g_static_args;
+    const bool any_pen = build_records(a, det, r0, n, recs);
+    place_records(recs, n, groups, rank, ord, ka.rows);
+    st = plan_and_launch(ws, flags, 0, a, n, ka, nullptr, any_pen, path, stream, g_static_error);
+    if (st != SAMPLER_OK) return st;
+  }
+  return SAMPLER_OK;
+}
+
+const char *sampler_noalloc_last_error(void) { return g_static_error.c_str(); }
 
 sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a, const sampler_device_params *dp,
                                   void *stream_ptr) {

@@ -315,6 +315,35 @@ typedef struct sampler_device_params {
 sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *args, const sampler_device_params *dp,
                                   void *stream);
 
+/* For callers that cannot allocate device memory -- code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc: one decode
+ * step without a handle.  Arguments, outputs and results are those of
+ * sampler_step on a handle created with the same flags and the largest
+ * limits (max_history_per_row 4096, max_bias_per_row 512,
+ * max_top_logprobs 32); n_rows may be any positive number (batches above
+ * 72 rows run as several launches on `stream`).  `flags` takes
+ * SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF and at most one
+ * SAMPLER_FORCE_* flag.
+ *   Workspace: a fixed array of the library in device memory, about 8 MB
+ *   (group words and exchange slots of 256 workgroups), one copy per GPU,
+ *   held until the process ends.  The call allocates nothing: no hipMalloc,
+ *   no hipFree, no allocating library routine; the first call on a device
+ *   looks up that device's copy (hipGetSymbolAddress) and plans the row
+ *   kernel for it.
+ *   Every call on a GPU shares that GPU's array: calls that overlap on one
+ *   GPU (other streams, other host threads) race and give wrong results.
+ *   Calls in stream order on one GPU are safe, as are calls on different
+ *   GPUs.
+ *   Errors: SAMPLER_EINVAL / SAMPLER_ECAPACITY for arguments beyond those
+ *   limits (vocab beyond what 32 workgroups hold at those limits, about
+ *   950,000), SAMPLER_EHIP for device errors; the message of the calling
+ *   thread's last failure is sampler_noalloc_last_error(). */
+sampler_status sampler_step_noalloc(const sampler_step_args *args, uint32_t flags, int32_t device, void *stream);
+
+/* Message of the calling thread's last failed sampler_step_noalloc ("" when
+ * none). */
+const char *sampler_noalloc_last_error(void);
+
 /* The batch predicate alone ([A] "One request with top_p takes the whole
  * batch off the fast path": normalize, then is_all_greedy / need_top_p /
  * need_top_k / need_min_p).  Pure host code: works without a GPU.  `flags`

@@ -219,3 +219,14 @@ def test_binding_checks_device_tensors():
     with pytest.raises(ValueError, match="outside"):
         _check_spans("bias_ids", 8, np.array([-1], np.int64), np.array([1], np.int32))
 
+
+def test_noalloc_without_gpu_reports_ehip(lib):
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    a = dsts.StepArgs()
+    a.n_rows, a.vocab, a.row_stride = 1, 16, 16
+    assert lib.sampler_step_noalloc(ctypes.byref(a), 0, 0, None) == dsts.SAMPLER_EHIP
+    assert "device" in lib.sampler_noalloc_last_error().decode()
+    # flags are checked before the device
+    assert lib.sampler_step_noalloc(ctypes.byref(a), dsts.FLAG_COOPERATIVE_LAUNCH, 0, None) == dsts.SAMPLER_EINVAL
