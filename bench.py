@@ -111,9 +111,87 @@ def calibrate_copy():
     print(json.dumps({"copy_bytes": COPY_BYTES, "launches": 10}))
 
 
+def host_cpu():
+    """The host's CPU model and logical core count."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"model": model, "logical_cores": os.cpu_count()}
+
+
+def stream_rates(dev, nbytes=COPY_BYTES, reps=10):
+    """Plain device streams in the same run, as context for the roofline:
+    a copy (read + write), a read-only reduction and a write-only fill of
+    nbytes each, GB/s of bytes moved (best of reps)."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    out = {}
+    for name, fn, moved in (("copy", lambda: b.copy_(a), 2 * nbytes), ("read", lambda: a.sum(), nbytes),
+                            ("write", lambda: b.fill_(0.5), nbytes)):
+        fn()
+        best = None
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            e1.synchronize()
+            ms = e0.elapsed_time(e1)
+            best = ms if best is None else min(best, ms)
+        out[name + "_gbs"] = moved / (best * 1e-3) / 1e9
+    del a, b
+    torch.cuda.empty_cache()
+    out["bytes"] = nbytes
+    return out
+
+
+def batch_record(b):
+    """The batch fields of the xbrilliance.ai note's cost record ("记录字段"):
+    its batch switches, whether rows mix parameters, and the bytes of the two
+    fp32 [N, V] outputs (8 N V)."""
+    n, V = b.n_rows, b.vocab
+    k = np.asarray(b.top_k)
+    pen = [x for x in (b.repetition_penalty, b.presence_penalty, b.frequency_penalty) if x is not None]
+    params = np.stack([np.asarray(b.temperature, np.float64), np.asarray(b.top_p, np.float64), k.astype(np.float64),
+                       np.asarray(b.min_p, np.float64)] + [np.asarray(x, np.float64) for x in pen], axis=1)
+    return {
+        "num_seqs": n, "vocab_size": V,
+        "do_top_p_top_k": bool(np.any(np.asarray(b.top_p) < 1.0) or np.any(k != -1)),
+        "do_min_p": bool(np.any(np.asarray(b.min_p) > 0.0)),
+        "do_penalties": bool((b.repetition_penalty is not None and np.any(b.repetition_penalty != 1.0))
+                             or (b.presence_penalty is not None and np.any(b.presence_penalty != 0.0))
+                             or (b.frequency_penalty is not None and np.any(b.frequency_penalty != 0.0))),
+        "param_mixed": bool(np.any(params != params[0])),
+        "sampling_tensor_bytes": 8 * n * V,
+    }
+
+
+def parity_summary(b, offset, gpu_out):
+    """One timed step's GPU outputs against the oracle on its inputs, under
+    the parity rules of tests/parity.py (part of the CPU-baseline leg)."""
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    from parity import compare, run_oracle
+    import dataclasses
+    b = dataclasses.replace(b, seed=0, offset=offset)
+    g = {k: v.cpu().numpy() for k, v in gpu_out.items()}
+    r = compare(g, run_oracle(b, n_threads=min(os.cpu_count() or 1, 16)))
+    return {"step_offset": offset, "rows": r.rows, "ok": r.ok(), "token_mismatches": len(r.token_mismatch),
+            "flagged_rows": r.flagged, "flagged_by_class": r.flagged_by_class,
+            "flagged_rows_failed": len(r.flagged_failed), "max_prob_err": r.max_prob_err,
+            "max_logprob_err": r.max_logprob_err, "max_logprob_ulps": r.max_logprob_ulps}
+
+
 def cpu_baseline(batches, budget_s, threads=None):
     """The oracle, as it stands, on whole steps of the same workload (one
-    thread per host core, at most 16, unless threads is given)."""
+    thread per host core, at most 16 -- the host CPU share of one GPU --
+    unless threads is given)."""
     import oracle
     if threads is None:
         threads = min(os.cpu_count() or 1, 16)
@@ -134,7 +212,8 @@ def cpu_baseline(batches, budget_s, threads=None):
             break
     return {"value": rows / dt, "unit": "rows/s", "cores": threads, "kind": "oracle",
             "sample": f"{steps} whole steps of the N=64, V=128,000 full-chain workload "
-                      f"({rows} rows, {dt:.1f} s, probs and logprobs materialised)"}
+                      f"({rows} rows, {dt:.1f} s, probs and logprobs materialised)",
+            "host": dict(host_cpu(), thread_cap=16)}
 
 
 def main():
@@ -228,6 +307,9 @@ def main():
         torch.cuda.synchronize()
         sync_us.append((time.perf_counter() - t1) * 1e6)
 
+    # the last step that wrote set 0's outputs (for the parity summary)
+    parity_offset = max(i for i in range(50) if i % n_sets == 0)
+    streams = stream_rates(dev)
     ms_per_step = wall * 1e3 / args.steps
     rows_per_s = n * args.steps / wall
     alg_bytes = b0.algorithmic_bytes()
@@ -245,9 +327,12 @@ def main():
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": b0.dtype,
-        "data": "synthetic (seeded Zipf-biased Gaussian logits%s; %d rotating sets, %d MB)" % (
+        "data": "synthetic (seeded Zipf-biased Gaussian logits%s; %d rotating sets: %d MB of logits, %d MB "
+                "with their outputs)" % (
             ", Zipf(1.1) histories" if b0.history_ids is not None else "", n_sets,
-            sum(int(t["logits"].numel() * t["logits"].element_size()) for t in sets) // 10**6),
+            sum(int(t["logits"].numel() * t["logits"].element_size()) for t in sets) // 10**6,
+            sum(int(v.numel() * v.element_size()) for t in sets for v in [t["logits"]] + list(t["out"].values()))
+            // 10**6),
         "config": {"workload": desc, "n_rows": n, "vocab": V,
                    "history_per_row": 2048 if b0.history_ids is not None else 0, "path": r["path"],
                    "algorithmic_bytes_per_step": alg_bytes},
@@ -261,10 +346,13 @@ def main():
         "host_call_us_iqr": [float(np.percentile(host_us, 25)), float(np.percentile(host_us, 75))],
         "sync_step_us_median": float(np.median(sync_us)),
         "sync_step_us_iqr": [float(np.percentile(sync_us, 25)), float(np.percentile(sync_us, 75))],
+        "stream_gbs": streams,
+        "record": batch_record(b0),
     }
     if stage is not None:
         line["config"]["ablation_stage"] = stage
     if not args.no_cpu_baseline and headline:
+        line["parity"] = parity_summary(batches[0], parity_offset, sets[0]["out"])
         line["cpu_baseline"] = cpu_baseline(batches, args.cpu_seconds)
         # the same oracle on one host thread (rows are independent, so this
         # is the per-core rate)

@@ -58,6 +58,13 @@ constexpr float kLnInvEmin = 22.8738570f;  // 33 ln 2 = -ln of the least E
 constexpr float kSlack = 1.0009765625f;
 constexpr double kMassScale = 17592186044416.0;  // 2^44 (general-path radix masses)
 constexpr double kWinScale = 2147483648.0;        // 2^31 (window masses)
+// A top-p crossing found from window masses must lie farther than this
+// from its target (relative to the mass it is a fraction of) on each side
+// where moving it one tie group would change the kept set, else the row
+// takes the exact path.  The window sums' error is ~1e-8 (independent
+// per-value errors of ~1e-7), so a decision this far from its target is
+// the exact one.
+constexpr double kTopPMarginRel = 1e-7;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 constexpr uint32_t kNone = 0xFFFFFFFFu;
@@ -639,12 +646,15 @@ DEV float win_floor_z(float A, float h, float wsc) {
 }
 
 // Window histogram entry of one value at distance d = max - z: a count of
-// one in bits 48.. and the mass exp(-d) in 2^-31 units (2^(31 - d log2 e)
-// by the hardware exp2, relative error ~1e-6, rounded to an integer) below;
-// a workgroup's bin holds at most 2^15 values, so neither field overflows.
-// These masses only place thresholds in bins and sum the bins above a
-// threshold.
-DEV float mass_scaled(float d) { return __builtin_amdgcn_exp2f(__builtin_fmaf(-d, kLog2e, 31.0f)); }
+// one in bits 48.. and the mass exp(-d) in 2^-31 units below (rounded to an
+// integer); a workgroup's bin holds at most 2^15 values, so neither field
+// overflows.  The mass is the hardware exp2 of the small argument -d log2 e,
+// then scaled by 2^31 exactly.  Its relative error is at most about
+// 1.2e-7 (exp2) + 1.2e-7 d (the fp32 roundings of d and of d log2 e), and
+// the rounding to units adds 2^-32 of the max's mass; these masses place
+// thresholds in bins, and sum the bins above a threshold (a top-p decision
+// closer to its target than kTopPMarginRel is taken by the exact path).
+DEV float mass_scaled(float d) { return __builtin_amdgcn_exp2f(-d * kLog2e) * 2147483648.0f; }
 DEV unsigned long long hist_entry(float a) {
   return (1ull << 48) | (unsigned long long)(uint32_t)__builtin_rintf(a);
 }
@@ -990,8 +1000,28 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
       const unsigned long long bal = __ballot(has[s] && p >= fp_p0 && p < fp_p1 && end && base + pj[s] >= target);
       if (e < 0 && bal) e = 64 * s + __ffsll((long long)bal) - 1;
     }
-    if (e < 0) flags |= 1u;
-    else t = max(t, keyof(e));
+    if (e < 0) {
+      flags |= 1u;
+    } else {
+      // the crossing's distance from the target on both sides (the
+      // cumulative mass at the end of its tie group and before the group)
+      const uint32_t ke = keyof(e);
+      int gs = 0;  // the group's first position: the count of larger keys
+#pragma unroll
+      for (int s = 0; s < kE3Slots; ++s)
+        if (64 * s < n) gs += __popcll(__ballot(has[s] && kj[s] > ke));
+      const double c_new = base + pre_at(e), c_prev = base + (gs > 0 ? pre_at(gs - 1) : 0.0);
+      // a side matters when moving the crossing there changes max(t_p,
+      // t_k, t_m): one group later lowers t_p below ke, one group earlier
+      // raises it to the previous group's key (a bin above when the group
+      // opens the list)
+      const uint32_t tkm = max(t, in.minp ? in.t_m : 0u);
+      const uint32_t kprev = gs > 0 ? keyof(gs - 1) : 0xFFFFFFFFu;
+      const bool close_lo = c_new - target < kTopPMarginRel * ctot && ke > tkm;
+      const bool close_hi = target - c_prev < kTopPMarginRel * ctot && kprev > tkm;
+      if (close_lo || close_hi) flags |= 1u;
+      else t = max(t, ke);
+    }
   }
   if (in.minp) t = max(t, in.t_m);
   // the kept set: positions [0, et); its sum and the top logprobs
@@ -2219,8 +2249,29 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           }
           __syncthreads();
           const uint32_t e = sm.bu[24];
-          if (e == 0x7FFFFFFFu) flags |= 1u;
-          else t = max(t, keyof((int)e));
+          if (e == 0x7FFFFFFFu) {
+            flags |= 1u;
+          } else {
+            // the crossing's distance from the target on both sides (the
+            // cumulative mass at the end of its tie group and before the
+            // group, whose first position is found in parallel)
+            const uint32_t ke = keyof((int)e);
+            if (tid == 0) sm.bu[22] = 0u;
+            __syncthreads();
+            for (int j = tid; j <= (int)e; j += kBlock)
+              if (keyof(j) == ke && (j == 0 || keyof(j - 1) != ke)) sm.bu[22] = (uint32_t)j;
+            __syncthreads();
+            const int gs = (int)sm.bu[22];
+            const double c_new = base + pre[e], c_prev = base + (gs > 0 ? pre[gs - 1] : 0.0);
+            // a side matters when moving the crossing there changes the
+            // kept set's threshold (as in the wave form)
+            const uint32_t tkm = max(t, minp ? t_m : 0u);
+            const uint32_t kprev = gs > 0 ? keyof(gs - 1) : 0xFFFFFFFFu;
+            const bool close_lo = c_new - target < kTopPMarginRel * ctot && ke > tkm;
+            const bool close_hi = target - c_prev < kTopPMarginRel * ctot && kprev > tkm;
+            if (close_lo || close_hi) flags |= 1u;
+            else t = max(t, ke);
+          }
         }
         if (minp) t = max(t, t_m);
         // the kept set: positions [0, et); its sum and the top logprobs

@@ -61,3 +61,18 @@ def test_more_than_one_gpu_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
                        text=True, timeout=120)
     assert r.returncode == 2 and "one GPU" in r.stdout
+
+
+def test_batch_record_fields():
+    # the note's batch switches for the full chain, and for a Gumbel-only batch
+    full = bench.batch_record(workloads.config(4, set_id=0, n_rows=64, vocab=128_000 // 100))
+    assert full["do_top_p_top_k"] and full["do_min_p"] and full["do_penalties"] and full["param_mixed"]
+    assert full["sampling_tensor_bytes"] == 8 * 64 * 1280
+    g = bench.batch_record(workloads.config(1))
+    assert not (g["do_top_p_top_k"] or g["do_min_p"] or g["do_penalties"] or g["param_mixed"])
+    assert g["num_seqs"] == 4 and g["vocab_size"] == 1024
+
+
+def test_host_cpu_reports_cores():
+    h = bench.host_cpu()
+    assert h["logical_cores"] == os.cpu_count()
