@@ -163,7 +163,9 @@ struct KernelParams {
   WgSlots *slots;     // [n_groups * G]
   uint32_t *abort_word;  // equals the epoch once a barrier wait of this launch expired
   uint32_t epoch;        // the launch's epoch (host launches: 1 .. 2^31 - 1)
-  uint32_t *epoch_dev;   // or null; else the launch's epoch lives here (advanced by rows_kernel)
+  uint32_t *epoch_dev;   // or null; else the launch's epoch is *epoch_dev + epoch_dev_add (rows_kernel
+                         // advances the word by 2 per step: the row kernel adds 0, the raw-logprob kernel 1)
+  uint32_t epoch_dev_add;
   uint32_t spin_limit;   // bound of every cross-workgroup wait in spins (0: the default, ~2 s)
   // logits processors
   const uint32_t *vocab_mask;  // [n_rows, mask_stride] allowed bits, or null
@@ -196,6 +198,9 @@ static_assert(sizeof(KernelArgs) <= 8192, "kernel argument block");
 // Normalise the per-row device arrays of kp.dev into records at `out`
 // (one thread per row).
 hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream);
+// The raw logprobs of the rows whose effective temperature is not 1, after
+// the row kernel of the same step (same arguments, its own epoch).
+hipError_t launch_raw_lp(const KernelArgs &ka, int dtype, hipStream_t stream);
 // Launch one step.  The grid never exceeds the workgroups the device holds at
 // once; `cooperative` launches through hipLaunchCooperativeKernel, which
 // also has the runtime check that they are all resident.

@@ -1150,15 +1150,36 @@ DEV RowParam row_from_device(const KernelParams &kp, int r) {
 
 // One thread per row: the records of a step whose per-row parameters live
 // in device memory (the row kernel then reads them like copied records).
-// Thread 0 also advances the device epoch word that the row kernel launched
-// after it reads (bit 31 set: never a host epoch), so that a captured graph's
-// replays are distinct launches.
+// Thread 0 also advances the device epoch word that the kernels launched after
+// it read (bit 31 set: never a host epoch), by two: the row kernel takes the
+// new value and the raw-logprob kernel the one after it, so that a captured
+// graph's replays are distinct launches.
 __global__ __launch_bounds__(256) void rows_kernel(KernelParams kp, RowParam *out) {
   const int r = blockIdx.x * blockDim.x + threadIdx.x;
   if (r < kp.n_rows) out[r] = row_from_device(kp, r);
   if (r == 0 && kp.epoch_dev) {
     const uint32_t e = *kp.epoch_dev;
-    __hip_atomic_store(kp.epoch_dev, ((e + 1u) & 0x7FFFFFFFu) | 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(kp.epoch_dev, ((e + 2u) & 0x7FFFFFFEu) | 0x80000000u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+// Block b runs on XCD b % 8 (the dispatcher deals blocks round-robin over
+// the eight XCDs), so the G workgroups of a group are taken from one
+// residue class: their exchanges then stay on one XCD (a group barrier
+// measures ~0.86 us there against ~1.16 us across XCDs).  Only speed
+// depends on this; every exchange is coherent device-wide either way.
+// Groups beyond a multiple of 8 take consecutive blocks.
+DEV void block_group(const KernelParams &kp, int &group, int &gid) {
+  const int b = blockIdx.x, G = kp.G;
+  const int gpx = kp.n_groups / 8;  // groups per XCD in the XCD-aware part
+  const int nbx = gpx * 8 * G;
+  if (b < nbx) {
+    const int q = b / 8;
+    group = (b % 8) * gpx + q / G;
+    gid = q % G;
+  } else {
+    group = gpx * 8 + (b - nbx) / G;
+    gid = (b - nbx) % G;
   }
 }
 
@@ -1185,26 +1206,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   double *sq = reinterpret_cast<double *>(regB + 8 * kCandCap);
 
   const int G = kp.G;
-  // Block b runs on XCD b % 8 (the dispatcher deals blocks round-robin over
-  // the eight XCDs), so the G workgroups of a group are taken from one
-  // residue class: their exchanges then stay on one XCD (a group barrier
-  // measures ~0.86 us there against ~1.16 us across XCDs).  Only speed
-  // depends on this; every exchange is coherent device-wide either way.
-  // Groups beyond a multiple of 8 take consecutive blocks.
   int group, gid;
-  {
-    const int b = blockIdx.x;
-    const int gpx = kp.n_groups / 8;  // groups per XCD in the XCD-aware part
-    const int nbx = gpx * 8 * G;
-    if (b < nbx) {
-      const int q = b / 8;
-      group = (b % 8) * gpx + q / G;
-      gid = q % G;
-    } else {
-      group = gpx * 8 + (b - nbx) / G;
-      gid = (b - nbx) % G;
-    }
-  }
+  block_group(kp, group, gid);
   const int V = kp.vocab;
   const uint32_t hslots = (uint32_t)kp.hash_slots;
   const uint32_t bslots = (uint32_t)kp.bias_slots;
@@ -1214,7 +1217,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   rc.G = G;
   // the launch's epoch: from the host, or from the device word that the
   // records kernel ahead of this launch advanced
-  const uint32_t epoch = kp.epoch_dev ? atomic_ld(kp.epoch_dev) : kp.epoch;
+  const uint32_t epoch = kp.epoch_dev ? atomic_ld(kp.epoch_dev) + kp.epoch_dev_add : kp.epoch;
   rc.gc.s = kp.sync + group;
   rc.gc.abort_word = kp.abort_word;
   rc.gc.epoch = epoch;
@@ -2764,6 +2767,178 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   }
 }
 
+// ---------------------------------------------------------------- raw logprobs
+// [B] "Logprobs are temperature-scaled": with the original-logprob switch
+// the returned logprobs are log_softmax of the processed logits x' (logits
+// processors and penalties applied, no temperature).  The row kernel holds
+// z = x' / T, from which x' cannot be recovered exactly, so for the rows
+// whose effective temperature is not 1 this kernel runs after it: each
+// workgroup of a row group rebuilds x' for its slice (the raw logits again,
+// NaN -> -inf, the grammar mask, then the owners of history and bias
+// entries recompute their tokens as the row kernel does), takes the slice's
+// max and exact fp64 sum, exchanges them with its peers, and overwrites the
+// row's logprobs and the values of its top logprobs (whose ids and order
+// the row kernel chose, by z over all tokens).  Rows at temperature 1 are
+// already right (z = x').
+template <typename TIn>
+__global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
+  const KernelParams &kp = ka.kp;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  SmemBase &sm = *reinterpret_cast<SmemBase *>(lds_raw);
+  float *xs = reinterpret_cast<float *>(lds_raw + sizeof(SmemBase));
+  unsigned char *region = reinterpret_cast<unsigned char *>(xs + kp.slice);
+  uint32_t *hash = reinterpret_cast<uint32_t *>(region);
+  unsigned long long *bhash = reinterpret_cast<unsigned long long *>(region + 4 * (size_t)kp.hash_slots);
+  const int G = kp.G, V = kp.vocab;
+  int group, gid;
+  block_group(kp, group, gid);
+  const uint32_t hslots = (uint32_t)kp.hash_slots, bslots = (uint32_t)kp.bias_slots;
+  GroupCtx gc;
+  gc.s = kp.sync + group;
+  gc.abort_word = kp.abort_word;
+  gc.epoch = kp.epoch_dev ? atomic_ld(kp.epoch_dev) + kp.epoch_dev_add : kp.epoch;
+  gc.spin_limit = kp.spin_limit ? kp.spin_limit : kSpinLimit;
+  gc.G = G;
+  gc.claimed = false;
+  const int s0 = gid * kp.slice, s1 = min(V, s0 + kp.slice), ln = s1 - s0;
+  for (int j = tidx(); j < 64; j += kBlock) sm.exp_tab[j] = exp2((double)j * (1.0 / 64.0));
+  unsigned it = 0;
+  for (int ri = group; ri < kp.n_rows; ri += kp.n_groups) {
+    const RowParam P = kp.rows ? kp.rows[ri] : ka.rows[ri];
+    if ((P.flags & RF_BAD) || P.temperature == 1.0f) continue;  // the same on every workgroup of the row
+    const int tid = tidx(), row = P.row;
+    const bool pen = (P.flags & RF_PEN) != 0, spec = (P.flags & RF_SPEC) != 0;
+    const int64_t rbase = (int64_t)row * kp.row_stride + s0;
+    // x' = the sanitised raw logit, -inf where the grammar mask clears it
+    const uint32_t *mrow = kp.vocab_mask ? kp.vocab_mask + (int64_t)row * kp.mask_stride : nullptr;
+    for (int l = tid; l < ln; l += kBlock) {
+      float x = Loader<TIn>::load1(kp.logits, rbase + l);
+      if (x != x) x = -INFINITY;
+      if (mrow && !((mrow[(s0 + l) >> 5] >> ((s0 + l) & 31)) & 1u)) x = -INFINITY;
+      xs[l] = x;
+    }
+    // the history and bias hashes of the slice, as in the row kernel
+    if (pen)
+      for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+    if (spec)
+      for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;
+    __syncthreads();
+    int32_t bid = -1;
+    float bval = 0.0f;
+    if (spec) {
+      if (tid < P.bias_len) {
+        bid = kp.bias_ids[P.bias_start + tid];
+        bval = kp.bias_vals[P.bias_start + tid];
+      } else if (tid < P.bias_len + P.stop_len) {
+        bid = kp.stop_ids[P.stop_start + (tid - P.bias_len)];
+        bval = -INFINITY;
+      }
+    }
+    if (spec && bid >= s0 && bid < s1) {
+      const uint32_t local = (uint32_t)(bid - s0);
+      uint32_t sl = hash_slot(local, bslots);
+      uint32_t *lo = reinterpret_cast<uint32_t *>(bhash);
+      while (true) {
+        const uint32_t prev = atomicCAS(&lo[2 * sl], kEmpty, local);
+        if (prev == kEmpty || prev == local) {
+          atomicAdd(reinterpret_cast<float *>(&lo[2 * sl + 1]), bval);
+          break;
+        }
+        sl = (sl + 1u) & (bslots - 1u);
+      }
+    }
+    if (pen) {
+      const int32_t *hist = kp.history_ids + P.hist_start;
+      for (int h = tid; h < P.hist_len; h += kBlock) {
+        const int32_t id = hist[h];
+        if (id >= s0 && id < s1) {
+          const uint32_t local = (uint32_t)(id - s0);
+          uint32_t sl = hash_slot(local, hslots);
+          while (true) {
+            const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (local << 13) | 1u);
+            if (prev == kEmpty) break;
+            if ((prev >> 13) == local) {
+              atomicAdd(&hash[sl], 1u);
+              break;
+            }
+            sl = (sl + 1u) & (hslots - 1u);
+          }
+        }
+      }
+    }
+    __syncthreads();
+    // every occupied slot's token is recomputed from its raw logit: bias,
+    // then the penalties with the final count (masked tokens stay -inf)
+    if (pen)
+      for (int t = tid; t < (int)hslots; t += kBlock) {
+        const uint32_t e = hash[t];
+        if (e == kEmpty) continue;
+        const uint32_t local = e >> 13;
+        float x = Loader<TIn>::load1(kp.logits, rbase + local), b;
+        x = x == x ? x : -INFINITY;
+        if (spec && bias_lookup(bhash, bslots, local, b)) x = add_bias(x, b);
+        const bool masked = mrow && !((mrow[(s0 + local) >> 5] >> ((s0 + local) & 31)) & 1u);
+        xs[local] = masked ? -INFINITY : apply_penalty(x, e & 0x1FFFu, P);
+      }
+    if (spec)
+      for (int t = tid; t < (int)bslots; t += kBlock) {
+        const unsigned long long e = bhash[t];
+        const uint32_t local = (uint32_t)e;
+        if (local == kEmpty || (pen && hist_contains(hash, hslots, local))) continue;
+        float x = Loader<TIn>::load1(kp.logits, rbase + local);
+        x = x == x ? x : -INFINITY;
+        const bool masked = mrow && !((mrow[(s0 + local) >> 5] >> ((s0 + local) & 31)) & 1u);
+        xs[local] = masked ? -INFINITY : add_bias(x, __uint_as_float((uint32_t)(e >> 32)));
+      }
+    __syncthreads();
+    // the slice's max, then its exact sum relative to it
+    float lm = -INFINITY;
+    for (int l = tid; l < ln; l += kBlock) lm = fmaxf(lm, xs[l]);
+    const unsigned long long mkey = wg_max_u(sm, (unsigned long long)fkey(lm));
+    const float mg = key_to_float((uint32_t)mkey);
+    double ls = 0.0;
+    if (mg > -INFINITY && mg < INFINITY)
+      for (int l = tid; l < ln; l += kBlock) ls += exp_nonpos(sm.exp_tab, (double)xs[l] - (double)mg);
+    const double sg = wg_sum_d(sm, ls);
+    const unsigned par = it++ & 1u;
+    WgSlots *my = kp.slots + (size_t)group * G + gid;
+    if (tid == 0) {
+      atomic_st(&my->x1[par][0], (unsigned long long)__float_as_uint(mg));
+      atomic_st(&my->x1[par][1], (unsigned long long)__double_as_longlong(sg));
+    }
+    group_barrier(sm, gc);
+    if (tid == 0) {
+      // every workgroup combines the slices in the same order
+      float m = -INFINITY;
+      for (int g = 0; g < G; ++g)
+        m = fmaxf(m, __uint_as_float((uint32_t)atomic_ld(&kp.slots[(size_t)group * G + g].x1[par][0])));
+      double S = 0.0;
+      for (int g = 0; g < G; ++g) {
+        const WgSlots &pg = kp.slots[(size_t)group * G + g];
+        const float mgg = __uint_as_float((uint32_t)atomic_ld(&pg.x1[par][0]));
+        const double sgg = __longlong_as_double((long long)atomic_ld(&pg.x1[par][1]));
+        if (mgg > -INFINITY && m < INFINITY) S += sgg * exp_nonpos(sm.exp_tab, (double)mgg - (double)m);
+      }
+      sm.bd[0] = (double)m;
+      sm.bd[1] = log(S);
+      sm.bu[0] = (m > -INFINITY && m < INFINITY && atomic_ld(kp.abort_word) != gc.epoch) ? 1u : 0u;
+      if (gid == 0 && atomic_ld(kp.abort_word) == gc.epoch && kp.row_status) kp.row_status[row] = 3;
+    }
+    __syncthreads();
+    // rows without a finite value keep the row kernel's outputs (status 1 or 2)
+    if (sm.bu[0]) {
+      const double m = sm.bd[0], lns = sm.bd[1];
+      if (kp.logprobs)
+        for (int l = tid; l < ln; l += kBlock) kp.logprobs[(int64_t)row * V + s0 + l] = (float)(((double)xs[l] - m) - lns);
+      for (int j = tid; j < kp.top_lp; j += kBlock) {
+        const int id = kp.top_lp_ids[(int64_t)row * kp.top_lp + j];
+        if (id >= s0 && id < s1) kp.top_lp_vals[(int64_t)row * kp.top_lp + j] = (float)(((double)xs[id - s0] - m) - lns);
+      }
+    }
+    __syncthreads();
+  }
+}
+
 template <typename TIn, bool PEN>
 hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const KernelParams &kp = ka.kp;
@@ -2811,6 +2986,16 @@ size_t kernel_lds_bytes(int slice, int hash_slots, int bias_slots, bool penaltie
          kernel_lds_region(slice, hash_slots, bias_slots, penalties);
 }
 
+hipError_t launch_raw_lp(const KernelArgs &ka, int dtype, hipStream_t stream) {
+  const KernelParams &kp = ka.kp;
+  const size_t lds = kernel_lds_bytes(kp.slice, kp.hash_slots, kp.bias_slots, true);
+  const dim3 grid(kp.n_groups * kp.G), block(kBlock);
+  void *args[] = {const_cast<KernelArgs *>(&ka)};
+  const void *fn = dtype == 0 ? reinterpret_cast<const void *>(&raw_lp_kernel<float>)
+                              : reinterpret_cast<const void *>(&raw_lp_kernel<uint16_t>);
+  return hipExtLaunchKernel(fn, grid, block, args, lds, stream, nullptr, nullptr, 0);
+}
+
 hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream) {
   hipLaunchKernelGGL(rows_kernel, dim3((kp.n_rows + 255) / 256), dim3(256), 0, stream, kp, out);
   return hipGetLastError();
@@ -2847,6 +3032,12 @@ hipError_t resident_blocks(int device, size_t lds_bytes, int *out) {
   if ((e = set_lds_attr<float, false>(lds_bytes)) != hipSuccess) return e;
   if ((e = set_lds_attr<uint16_t, true>(lds_bytes)) != hipSuccess) return e;
   if ((e = set_lds_attr<uint16_t, false>(lds_bytes)) != hipSuccess) return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&raw_lp_kernel<float>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&raw_lp_kernel<uint16_t>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes)) != hipSuccess)
+    return e;
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&row_kernel<float, true>),
                                                    kBlock, lds_bytes);

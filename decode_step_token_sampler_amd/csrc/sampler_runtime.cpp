@@ -151,16 +151,6 @@ sampler_status validate(const sampler_config *cfg, const sampler_step_args *a, s
     set_msg(msg, "unknown logprob_mode %d", a->logprob_mode);
     return SAMPLER_EINVAL;
   }
-  if (a->logprob_mode == SAMPLER_LOGPROB_RAW) {
-    for (int r = 0; r < a->n_rows; ++r) {
-      const float t = a->temperature ? a->temperature[r] : 1.0f;
-      if (!(row_is_greedy(t) || t == 1.0f)) {
-        set_msg(msg, "row %d: the raw logprob mode is supported only at effective temperature 1 (got %g)", r,
-                (double)t);
-        return SAMPLER_ENOTSUP;
-      }
-    }
-  }
   if ((a->min_tokens != nullptr) != (a->output_len != nullptr)) {
     msg = "min_tokens and output_len go together";
     return SAMPLER_EINVAL;
@@ -584,6 +574,27 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   if (dev && (e = launch_rows(kp, graph_rows, stream)) != hipSuccess) return hip_fail(err, e, "rows kernel launch");
   e = launch_step(ka, a->dtype, any_pen, (flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream, ev0, ev1);
   if (e != hipSuccess) return hip_fail(err, e, "kernel launch");
+  // [B] "Logprobs are temperature-scaled", the original-logprob switch: the
+  // rows whose effective temperature is not 1 get log_softmax of their
+  // processed logits from a second kernel (on device-side parameters the
+  // kernel itself skips the rows at temperature 1)
+  bool raw = a->logprob_mode == SAMPLER_LOGPROB_RAW && (a->logprobs || a->top_logprobs > 0);
+  if (raw && !dev) {
+    raw = false;
+    for (int r = 0; r < a->n_rows && !raw; ++r) {
+      const float t = a->temperature ? a->temperature[r] : 1.0f;
+      raw = !row_is_greedy(t) && t != 1.0f;
+    }
+  }
+  if (raw) {
+    ws.epoch = (ws.epoch & 0x7FFFFFFFu) + 1u;
+    if (ws.epoch == 0x80000000u) ws.epoch = 1;
+    kp.epoch = ws.epoch;
+    kp.epoch_dev_add = 1;
+    e = launch_raw_lp(ka, a->dtype, stream);
+    kp.epoch_dev_add = 0;
+    if (e != hipSuccess) return hip_fail(err, e, "raw-logprob kernel launch");
+  }
   return SAMPLER_OK;
 }
 
@@ -874,6 +885,18 @@ sampler_status sampler_step_noalloc(const sampler_step_args *a, uint32_t flags, 
   cfg.flags = flags;
   st = validate(&cfg, a, g_static_error);
   if (st != SAMPLER_OK) return st;
+  // the raw logprobs of rows whose temperature is not 1 come from a second
+  // kernel that carries a small private (scratch) segment, which the runtime
+  // may back with memory at its first launch: not offered here
+  if (a->logprob_mode == SAMPLER_LOGPROB_RAW)
+    for (int r = 0; r < a->n_rows; ++r) {
+      const float t = a->temperature ? a->temperature[r] : 1.0f;
+      if (!row_is_greedy(t) && t != 1.0f) {
+        set_msg(g_static_error, "row %d: the raw logprob mode at temperature %g needs a handle (sampler_step)", r,
+                (double)t);
+        return SAMPLER_ENOTSUP;
+      }
+    }
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
   const int pred = choose_path(a, flags);
@@ -918,10 +941,6 @@ sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a,
   if ((dp->min_tokens != nullptr) != (dp->output_len != nullptr)) {
     h->err = "min_tokens and output_len go together";
     return SAMPLER_EINVAL;
-  }
-  if (a->logprob_mode == SAMPLER_LOGPROB_RAW) {
-    h->err = "the raw logprob mode needs host temperatures (sampler_step)";
-    return SAMPLER_ENOTSUP;
   }
   // the host checks of sizes, pointers and modes (per-row values are
   // checked on the device)

@@ -235,10 +235,11 @@ typedef struct sampler_step_args {
    *     of the processed logits, untruncated: every token gets a value and
    *     top logprobs list the largest over all tokens;
    *   SAMPLER_LOGPROB_RAW (2): log_softmax of the processed logits without
-   *     temperature (the page's original-logprob switch).  This build
-   *     supports it when every row's effective temperature is 1 (greedy
-   *     rows and T = 1), where it equals mode 1; otherwise the step returns
-   *     SAMPLER_ENOTSUP without launching.
+   *     temperature (the page's original-logprob switch); top logprobs list
+   *     the largest over all tokens, ordered as in mode 1.  Where a row's
+   *     effective temperature is 1 (greedy rows, T = 1) it equals mode 1;
+   *     the other rows take a second kernel after the sampling kernel,
+   *     which reads their logits again and rewrites their logprobs.
    * probs and the sampled tokens do not depend on the mode. */
   int32_t logprob_mode;
 } sampler_step_args;
@@ -323,7 +324,10 @@ sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *ar
  * max_top_logprobs 32); n_rows may be any positive number (batches above
  * 72 rows run as several launches on `stream`).  `flags` takes
  * SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF and at most one
- * SAMPLER_FORCE_* flag.
+ * SAMPLER_FORCE_* flag.  The raw logprob mode is offered where every row's
+ * effective temperature is 1 (SAMPLER_ENOTSUP otherwise: the kernel that
+ * serves the other rows carries a private segment, which the runtime may
+ * back with memory at its first launch).
  *   Workspace: a fixed array of the library in device memory, about 8 MB
  *   (group words and exchange slots of 256 workgroups), one copy per GPU,
  *   held until the process ends.  The call allocates nothing: no hipMalloc,

@@ -137,7 +137,6 @@ CFG = dsts.Config(max_rows=8, max_vocab=1024, max_history_per_row=64, max_top_lo
     (dict(min_tokens=np.array([3, 3], np.int32)), dsts.SAMPLER_EINVAL),      # without output_len
     # logprob modes
     (dict(logprob_mode=3), dsts.SAMPLER_EINVAL),
-    (dict(logprob_mode=2, temperature=np.array([1.0, 0.7], np.float32)), dsts.SAMPLER_ENOTSUP),
 ])
 def test_validation_errors(lib, change, status):
     a, keep = _args(**change)
@@ -230,3 +229,9 @@ def test_noalloc_without_gpu_reports_ehip(lib):
     assert "device" in lib.sampler_noalloc_last_error().decode()
     # flags are checked before the device
     assert lib.sampler_step_noalloc(ctypes.byref(a), dsts.FLAG_COOPERATIVE_LAUNCH, 0, None) == dsts.SAMPLER_EINVAL
+
+
+def test_validation_accepts_raw_logprobs_at_any_temperature(lib):
+    a, keep = _args(logprob_mode=2, temperature=np.array([1.0, 0.7], np.float32))
+    st, msg = dsts.validate(CFG, a)
+    assert st == dsts.SAMPLER_OK, msg

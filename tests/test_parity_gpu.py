@@ -271,10 +271,40 @@ def test_logprob_mode_raw_at_unit_temperature(sampler):
     o = run_oracle(b, logprob_mode="raw")
     r = compare(g, o)
     assert r.ok(), r
+
+
+@pytest.mark.parametrize("T", [0.5, 1.3])
+@pytest.mark.parametrize("seed,n,V,dtype", [(45, 10, 9000, "bf16"), (46, 7, 70_001, "f32"), (47, 13, 257, "f32")])
+def test_logprob_mode_raw_at_other_temperatures(sampler, T, seed, n, V, dtype):
+    # log_softmax of the processed logits (penalties, grammar mask, bias and
+    # stop lists applied, no temperature) at T = 0.5 and 1.3, beside greedy
+    # rows and rows at T = 1
+    b = workloads.random_small(seed, n, V, dtype, penalties=True)
+    b.temperature = np.where(np.arange(n) % 4 == 0, 0.0, np.where(np.arange(n) % 4 == 1, 1.0, T)).astype(np.float32)
+    p = workloads.processors(seed, b, max_entries=64)
+    kw = p.kwargs()
+    L, H = to_device(b)
+    dk = {k: (torch.from_numpy(np.ascontiguousarray(v)).to("cuda:0") if k in ("vocab_mask", "bias_ids", "bias_vals",
+                                                                             "stop_ids") else v)
+          for k, v in kw.items()}
     import decode_step_token_sampler_amd as dsts
-    b.temperature[1] = 0.7
-    with pytest.raises(dsts.SamplerError):
-        run_gpu(sampler, b, logprob_mode="raw")
+    s = dsts.Sampler(16, 80_000, max_history_per_row=64, max_top_logprobs=8, max_bias_per_row=64)
+    g = run_gpu(s, b, logits=L, history=H, logprob_mode="raw", **dk)
+    o = run_oracle(b, logprob_mode="raw", **kw)
+    r = compare(g, o)
+    assert r.ok(), r
+    s.close()
+
+
+def test_logprob_mode_raw_workloads(sampler):
+    # the mixed filtered batch and the full chain, every row's logprobs raw
+    for cfg in (3, 4):
+        b = workloads.config(cfg, n_rows=16, vocab=60_000, history_len=512)
+        b.top_logprobs = 5
+        g = run_gpu(sampler, b, logprob_mode="raw")
+        o = run_oracle(b, logprob_mode="raw")
+        r = compare(g, o)
+        assert r.ok(), (cfg, r)
 
 
 # ------------------------------------------------------------ invariants
@@ -468,6 +498,37 @@ def test_step_graph_eager_matches_host_step(sampler):
         np.testing.assert_array_equal(g[k], h[k])
     r = compare(g, run_oracle(b))
     assert r.ok(), r
+
+
+def test_step_graph_raw_logprobs_and_replays():
+    # the raw logprob mode on device-side parameters: the raw kernel follows
+    # the row kernel in the captured graph, and each replay (its own pair of
+    # launches) equals the host-path step and the oracle
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(16, 30_000, max_history_per_row=200, max_top_logprobs=8)
+    b = workloads.random_small(72, 12, 30_000, "f32", penalties=True, history_len=200)
+    b.temperature = np.where(np.arange(12) % 3 == 0, 1.0, 0.6).astype(np.float32)
+    L, H = to_device(b)
+    params = _device_params(b)
+    out = _outputs(b.n_rows, b.vocab, b.top_logprobs)
+    s.step_graph(L, params, history_ids=H, out=out, top_logprobs=b.top_logprobs, logprob_mode="raw")
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        s.step_graph(L, params, history_ids=H, out=out, top_logprobs=b.top_logprobs, logprob_mode="raw")
+    torch.cuda.synchronize()
+    o = run_oracle(b, logprob_mode="raw")
+    for rep in range(3):
+        graph.replay()
+        torch.cuda.synchronize()
+        g = _host(out)
+        r = compare(g, o)
+        assert r.ok(), (rep, r)
+        h = run_gpu(s, b, logits=L, history=H, logprob_mode="raw")
+        for k in ("token_ids", "probs", "logprobs", "top_logprob_ids", "top_logprob_vals", "row_status"):
+            np.testing.assert_array_equal(g[k], h[k], err_msg=k)
+    s.close()
 
 
 def test_step_graph_bad_rows_get_status_4(sampler):

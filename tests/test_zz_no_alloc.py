@@ -81,3 +81,17 @@ def test_noalloc_rejects_bad_arguments():
     with pytest.raises(dsts.SamplerError) as e:
         dsts.step_noalloc(L, temperature=b.temperature, top_logprobs=33)
     assert e.value.status == dsts.SAMPLER_ECAPACITY
+
+
+def test_noalloc_raw_logprobs_only_at_unit_temperature():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import decode_step_token_sampler_amd as dsts
+    b = workloads.random_small(43, 4, 1000, "f32", penalties=False)
+    L, _ = to_device(b)
+    with pytest.raises(dsts.SamplerError) as e:
+        dsts.step_noalloc(L, temperature=[0.5, 1.0, 1.0, 1.0], want_logprobs=True, logprob_mode="raw")
+    assert e.value.status == dsts.SAMPLER_ENOTSUP
+    out = dsts.step_noalloc(L, temperature=[0.0, 1.0, 1.0, 1.0], want_logprobs=True, logprob_mode="raw")
+    torch.cuda.synchronize()
+    assert out["token_ids"].shape == (4,)
