@@ -15,11 +15,17 @@ constexpr int32_t kTopKAll = 1 << 30;
 constexpr int kMaxG = 32;
 // Largest top-logprob list per row.
 constexpr int kMaxTopLogprobs = 32;
-// Largest history of one row.  Its counts live in an LDS hash table of
-// next_pow2(2 * max_history_per_row) slots, each packing a slice-local index
-// (15 bits) and a count (13 bits) into one word.
+// Largest history the row kernel counts by itself.  Its counts live in an
+// LDS hash table of next_pow2(2 * max_history_per_row) slots (at most
+// kMaxHashSlots), each packing a slice-local index (15 bits) and a count
+// (13 bits) into one word.
 constexpr int kMaxHistPerRow = 4096;
 constexpr int kMaxHashSlots = 8192;
+// Largest history of one row.  A longer history than kMaxHistPerRow is
+// counted ahead of the row kernel by hist_list_kernel: one workgroup per
+// (row, slice) counts the slice's ids in a dense LDS array and writes the
+// nonzero ones in index order as slice-local index << 17 | count.
+constexpr int32_t kMaxHistLong = (1 << 17) - 1;
 // Largest list of logit_bias plus active stop entries of one row: one per
 // thread.  They live in a second LDS hash of next_pow2(2 * max) 8-byte
 // slots (slice-local index, summed bias).
@@ -182,6 +188,12 @@ struct KernelParams {
   int32_t max_hist, max_bias;
   uint64_t seed, offset;
   DevRowArrays dev;
+  // counts of the histories longer than kMaxHistPerRow (hist_list_kernel):
+  // the (row, slice) list starts at hist_list + (row G + gid) hist_list_cap
+  // and holds hist_list_n[row G + gid] entries; null when no row is that long
+  uint32_t *hist_list;
+  int32_t *hist_list_n;
+  int64_t hist_list_cap;
 };
 
 // Batches of up to kArgRows rows carry their per-row records in the kernel
@@ -201,6 +213,11 @@ hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream
 // The raw logprobs of the rows whose effective temperature is not 1, after
 // the row kernel of the same step (same arguments, its own epoch).
 hipError_t launch_raw_lp(const KernelArgs &ka, int dtype, hipStream_t stream);
+// Count the histories longer than kMaxHistPerRow into kp.hist_list (one
+// workgroup per record and slice), ahead of the row kernel of the same step.
+hipError_t launch_hist_list(const KernelArgs &ka, hipStream_t stream);
+// Dynamic LDS bytes of hist_list_kernel for a slice.
+size_t hist_list_lds_bytes(int slice);
 // Launch one step.  The grid never exceeds the workgroups the device holds at
 // once; `cooperative` launches through hipLaunchCooperativeKernel, which
 // also has the runtime check that they are all resident.

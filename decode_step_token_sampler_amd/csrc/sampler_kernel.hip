@@ -1299,12 +1299,28 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     constexpr int kHistPer = kMaxHistPerRow / kBlock;
     int32_t hv[kHistPer];
     float xr[kHistPer];  // raw logit of each in-slice history entry
+    // a history longer than the hash holds arrives counted, as this slice's
+    // list of (local << 17 | count) entries; hv then holds its first ones
+    const bool longh = pen && P.hist_len > kMaxHistPerRow;
+    const uint32_t *hl = nullptr;
+    int hl_n = 0;
     if (pen) {
-      const int32_t *hist = kp.history_ids + P.hist_start;
+      if (longh) {
+        const int64_t li = (int64_t)row * G + gid;
+        hl = kp.hist_list + li * kp.hist_list_cap;
+        hl_n = kp.hist_list_n[li];
 #pragma unroll
-      for (int q = 0; q < kHistPer; ++q) {
-        const int h = tid + q * kBlock;
-        hv[q] = h < P.hist_len ? hist[h] : -1;
+        for (int q = 0; q < kHistPer; ++q) {
+          const int h = tid + q * kBlock;
+          hv[q] = h < hl_n ? (int32_t)hl[h] : -1;
+        }
+      } else {
+        const int32_t *hist = kp.history_ids + P.hist_start;
+#pragma unroll
+        for (int q = 0; q < kHistPer; ++q) {
+          const int h = tid + q * kBlock;
+          hv[q] = h < P.hist_len ? hist[h] : -1;
+        }
       }
     }
     // this thread's logit_bias or stop entry (one per thread): the bias
@@ -1412,7 +1428,24 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         }
         if (bsl >= 0) xbr = Loader<TIn>::load1(kp.logits, rbase + (bid - s0));
       }
-      if (pen) {
+      if (longh) {
+        // the entries' tokens are marked in a bitmap over the slice (for the
+        // bias entries below) and their raw logits read
+#pragma unroll
+        for (int q = 0; q < kHistPer; ++q) {
+          osl[q] = -1;
+          xr[q] = 0.0f;
+          if (hv[q] != -1) {
+            const uint32_t local = (uint32_t)hv[q] >> 17;
+            atomicOr(&hash[local >> 5], 1u << (local & 31u));
+            xr[q] = Loader<TIn>::load1(kp.logits, rbase + local);
+          }
+        }
+        for (int h = kHistPer * kBlock + tid; h < hl_n; h += kBlock) {
+          const uint32_t local = hl[h] >> 17;
+          atomicOr(&hash[local >> 5], 1u << (local & 31u));
+        }
+      } else if (pen) {
 #pragma unroll
         for (int q = 0; q < kHistPer; ++q) {
           const int32_t id = hv[q];
@@ -1453,7 +1486,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         __builtin_amdgcn_sched_barrier(0);
       }
       if (pen)
-        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = longh ? 0u : kEmpty;
       if (spec)
         for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;  // free, bias +0
       transform(0, kBatch / 2);
@@ -1466,7 +1499,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
 #pragma unroll
         for (int c = 0; c < 4; ++c) v[b][c] = Loader<TIn>::load1(kp.logits, rbase + min(4 * tid + 4 * kBlock * b + c, ln - 1));
       if (pen)
-        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = longh ? 0u : kEmpty;
       if (spec)
         for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;  // free, bias +0
       transform(0, kBatch / 2);
@@ -1480,7 +1513,30 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       // final count.  A bias entry whose token has no history entry is
       // recomputed by the thread that created it.
       __syncthreads();
-      if (pen) {
+      if (longh) {
+#pragma unroll
+        for (int q = 0; q < kHistPer; ++q) {
+          if (hv[q] != -1) {
+            const uint32_t local = (uint32_t)hv[q] >> 17;
+            float x = xr[q] == xr[q] ? xr[q] : -INFINITY;
+            if (spec) {
+              float b;
+              if (bias_lookup(bhash, bslots, local, b)) x = add_bias(x, b);
+            }
+            zs[local] = div_temp(apply_penalty(x, (uint32_t)hv[q] & 0x1FFFFu, P), T, rT);
+          }
+        }
+        for (int h = kHistPer * kBlock + tid; h < hl_n; h += kBlock) {
+          const uint32_t e = hl[h], local = e >> 17;
+          float x = Loader<TIn>::load1(kp.logits, rbase + local);
+          x = x == x ? x : -INFINITY;
+          if (spec) {
+            float b;
+            if (bias_lookup(bhash, bslots, local, b)) x = add_bias(x, b);
+          }
+          zs[local] = div_temp(apply_penalty(x, e & 0x1FFFFu, P), T, rT);
+        }
+      } else if (pen) {
 #pragma unroll
         for (int q = 0; q < kHistPer; ++q) {
           if (osl[q] >= 0) {
@@ -1497,7 +1553,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       if (spec && bsl >= 0) {
         const unsigned long long e = bhash[bsl];
         const uint32_t local = (uint32_t)e;
-        if (!(pen && hist_contains(hash, hslots, local))) {
+        const bool in_hist =
+            pen && (longh ? ((hash[local >> 5] >> (local & 31u)) & 1u) != 0u : hist_contains(hash, hslots, local));
+        if (!in_hist) {
           const float x = xbr == xbr ? xbr : -INFINITY;
           zs[local] = div_temp(add_bias(x, __uint_as_float((uint32_t)(e >> 32))), T, rT);
         }
@@ -2767,6 +2825,52 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   }
 }
 
+// ---------------------------------------------------------------- long histories
+// [C] "解码一步里采样做什么" (_apply_penalties): the penalties take each
+// token's count in the sequence so far.  A history longer than the row
+// kernel's LDS hash holds is counted here, ahead of the row kernel:
+// workgroup (record, slice) counts the ids that fall in its slice in a
+// dense LDS array, then writes the nonzero counts in index order as
+// local << 17 | count, and their number.  Each thread compacts a contiguous
+// run of the slice, so the list's order is fixed.  Rows that do not need it
+// leave at once.
+__global__ __launch_bounds__(kBlock) void hist_list_kernel(KernelArgs ka) {
+  const KernelParams &kp = ka.kp;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  uint32_t *cnt = reinterpret_cast<uint32_t *>(lds_raw);
+  __shared__ uint32_t wave_tot[kWaves];
+  const int G = kp.G;
+  const int ri = (int)blockIdx.x / G, gid = (int)blockIdx.x % G;
+  const RowParam *pp = kp.rows ? kp.rows + ri : ka.rows + ri;
+  const uint32_t flags = pp->flags;
+  const int32_t hist_len = pp->hist_len;
+  if ((flags & RF_BAD) || !(flags & RF_PEN) || hist_len <= kMaxHistPerRow) return;
+  const int64_t hist_start = pp->hist_start;
+  const int row = pp->row;
+  const int tid = (int)threadIdx.x;
+  const int s0 = gid * kp.slice, s1 = min(kp.vocab, s0 + kp.slice), ln = s1 - s0;
+  for (int l = tid; l < ln; l += kBlock) cnt[l] = 0u;
+  __syncthreads();
+  const int32_t *hist = kp.history_ids + hist_start;
+#pragma unroll 8
+  for (int h = tid; h < hist_len; h += kBlock) {
+    const int32_t id = hist[h];
+    if (id >= s0 && id < s1) atomicAdd(&cnt[id - s0], 1u);
+  }
+  __syncthreads();
+  const int per = (ln + kBlock - 1) / kBlock;
+  const int l0 = min(ln, tid * per), l1 = min(ln, l0 + per);
+  uint32_t c = 0;
+  for (int l = l0; l < l1; ++l) c += cnt[l] != 0u ? 1u : 0u;
+  const uint32_t incl = block_scan_incl(c, wave_tot);
+  const int64_t li = (int64_t)row * G + gid;
+  uint32_t *out = kp.hist_list + li * kp.hist_list_cap;
+  uint32_t k = incl - c;
+  for (int l = l0; l < l1; ++l)
+    if (cnt[l] != 0u) out[k++] = ((uint32_t)l << 17) | cnt[l];
+  if (tid == kBlock - 1) kp.hist_list_n[li] = (int32_t)incl;
+}
+
 // ---------------------------------------------------------------- raw logprobs
 // [B] "Logprobs are temperature-scaled": with the original-logprob switch
 // the returned logprobs are log_softmax of the processed logits x' (logits
@@ -2817,9 +2921,14 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
       if (mrow && !((mrow[(s0 + l) >> 5] >> ((s0 + l) & 31)) & 1u)) x = -INFINITY;
       xs[l] = x;
     }
-    // the history and bias hashes of the slice, as in the row kernel
+    // the history and bias hashes of the slice, as in the row kernel (a
+    // history longer than the hash holds: its counted list and a bitmap)
+    const bool longh = pen && P.hist_len > kMaxHistPerRow;
+    const int64_t li = (int64_t)row * G + gid;
+    const uint32_t *hl = longh ? kp.hist_list + li * kp.hist_list_cap : nullptr;
+    const int hl_n = longh ? kp.hist_list_n[li] : 0;
     if (pen)
-      for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+      for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = longh ? 0u : kEmpty;
     if (spec)
       for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;
     __syncthreads();
@@ -2847,7 +2956,11 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
         sl = (sl + 1u) & (bslots - 1u);
       }
     }
-    if (pen) {
+    for (int h = tid; h < hl_n; h += kBlock) {
+      const uint32_t local = hl[h] >> 17;
+      atomicOr(&hash[local >> 5], 1u << (local & 31u));
+    }
+    if (pen && !longh) {
       const int32_t *hist = kp.history_ids + P.hist_start;
       for (int h = tid; h < P.hist_len; h += kBlock) {
         const int32_t id = hist[h];
@@ -2869,7 +2982,7 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
     __syncthreads();
     // every occupied slot's token is recomputed from its raw logit: bias,
     // then the penalties with the final count (masked tokens stay -inf)
-    if (pen)
+    if (pen && !longh)
       for (int t = tid; t < (int)hslots; t += kBlock) {
         const uint32_t e = hash[t];
         if (e == kEmpty) continue;
@@ -2880,11 +2993,21 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
         const bool masked = mrow && !((mrow[(s0 + local) >> 5] >> ((s0 + local) & 31)) & 1u);
         xs[local] = masked ? -INFINITY : apply_penalty(x, e & 0x1FFFu, P);
       }
+    for (int h = tid; h < hl_n; h += kBlock) {
+      const uint32_t e = hl[h], local = e >> 17;
+      float x = Loader<TIn>::load1(kp.logits, rbase + local), b;
+      x = x == x ? x : -INFINITY;
+      if (spec && bias_lookup(bhash, bslots, local, b)) x = add_bias(x, b);
+      const bool masked = mrow && !((mrow[(s0 + local) >> 5] >> ((s0 + local) & 31)) & 1u);
+      xs[local] = masked ? -INFINITY : apply_penalty(x, e & 0x1FFFFu, P);
+    }
     if (spec)
       for (int t = tid; t < (int)bslots; t += kBlock) {
         const unsigned long long e = bhash[t];
         const uint32_t local = (uint32_t)e;
-        if (local == kEmpty || (pen && hist_contains(hash, hslots, local))) continue;
+        if (local == kEmpty) continue;
+        if (pen && (longh ? ((hash[local >> 5] >> (local & 31u)) & 1u) != 0u : hist_contains(hash, hslots, local)))
+          continue;
         float x = Loader<TIn>::load1(kp.logits, rbase + local);
         x = x == x ? x : -INFINITY;
         const bool masked = mrow && !((mrow[(s0 + local) >> 5] >> ((s0 + local) & 31)) & 1u);
@@ -2966,6 +3089,17 @@ hipError_t set_lds_attr(size_t lds) {
 
 }  // namespace
 
+size_t hist_list_lds_bytes(int slice) { return sizeof(uint32_t) * (size_t)slice; }
+
+hipError_t launch_hist_list(const KernelArgs &ka, hipStream_t stream) {
+  const KernelParams &kp = ka.kp;
+  const size_t lds = hist_list_lds_bytes(kp.slice);  // the attribute allows any slice (resident_blocks)
+  void *args[] = {const_cast<KernelArgs *>(&ka)};
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(&hist_list_kernel), dim3(kp.n_rows * kp.G), dim3(kBlock),
+                            args, lds, stream, nullptr, nullptr, 0);
+}
+
+
 size_t kernel_lds_fixed() { return sizeof(SmemBase); }
 
 size_t kernel_lds_region(int slice, int hash_slots, int bias_slots, bool penalties) {
@@ -3037,6 +3171,10 @@ hipError_t resident_blocks(int device, size_t lds_bytes, int *out) {
     return e;
   if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&raw_lp_kernel<uint16_t>),
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes)) != hipSuccess)
+    return e;
+  if ((e = hipFuncSetAttribute(reinterpret_cast<const void *>(&hist_list_kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)hist_list_lds_bytes(kMaxSlice))) !=
+      hipSuccess)
     return e;
   int per_cu = 0;
   e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&row_kernel<float, true>),

@@ -63,6 +63,10 @@ struct Workspace {
   uint32_t *abort_word = nullptr;  // device word: epoch of an aborted launch
   uint32_t *epoch_dev = nullptr;   // device word: epoch of graph-path launches (advanced on the device), or null
   uint32_t epoch = 0;              // epoch of the last host-path launch (1 .. 2^31 - 1)
+  // counted histories longer than kMaxHistPerRow (handles planned for them)
+  uint32_t *hist_list = nullptr;  // [max_rows * hist_list_row] entries
+  int32_t *hist_list_n = nullptr; // [max_rows * kMaxG]
+  int64_t hist_list_row = 0;      // entries per row: min(kMaxG max_history, max_vocab + kMaxSlice)
   // limits the workspace was planned for
   int32_t max_history_per_row = 0, max_bias_per_row = 0, max_top_logprobs = 0, max_vocab = 0;
 };
@@ -303,6 +307,8 @@ void free_handle(sampler_handle *h) {
   if (h->ws.slots) (void)hipFree(h->ws.slots);
   if (h->ws.abort_word) (void)hipFree(h->ws.abort_word);
   if (h->ws.epoch_dev) (void)hipFree(h->ws.epoch_dev);
+  if (h->ws.hist_list) (void)hipFree(h->ws.hist_list);
+  if (h->ws.hist_list_n) (void)hipFree(h->ws.hist_list_n);
   delete h;
 }
 
@@ -326,7 +332,9 @@ sampler_status plan_workspace(Workspace &ws, int device, int32_t max_hist, int32
   ws.max_vocab = max_vocab;
   ws.max_top_logprobs = max_top_lp;
   // LDS plan: fixed part + slice of fp32 values + hash of history counts
-  ws.hash_slots = next_pow2_at_least(2 * max_hist, 64);
+  // (longer histories than the hash holds arrive counted: the hash area
+  // then serves as a bitmap over the slice)
+  ws.hash_slots = next_pow2_at_least(2 * (max_hist < kMaxHistPerRow ? max_hist : kMaxHistPerRow), 64);
   ws.bias_slots = max_bias > 0 ? next_pow2_at_least(2 * max_bias, 64) : 0;
   // the dynamic request may use what the kernel's own static LDS leaves
   size_t lds_static = 0;
@@ -554,6 +562,17 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   kp.max_bias = ws.max_bias_per_row;
   kp.seed = a->seed;
   kp.offset = a->offset;
+  // a history longer than the row kernel's hash holds is counted first
+  bool long_hist = false;
+  if (ws.hist_list) {
+    long_hist = dev != nullptr;  // device-side lengths: the list kernel checks each row
+    for (int r = 0; r < a->n_rows && !long_hist && a->history_len; ++r) long_hist = a->history_len[r] > kMaxHistPerRow;
+  }
+  if (long_hist) {
+    kp.hist_list = ws.hist_list;
+    kp.hist_list_n = ws.hist_list_n;
+    kp.hist_list_cap = ws.max_history_per_row < slice ? ws.max_history_per_row : slice;
+  }
   const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
   const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
   const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);
@@ -572,6 +591,8 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   kp.epoch_dev = dev ? ws.epoch_dev : nullptr;
   kp.spin_limit = (uint32_t)wait_spin_limit;
   if (dev && (e = launch_rows(kp, graph_rows, stream)) != hipSuccess) return hip_fail(err, e, "rows kernel launch");
+  if (long_hist && (e = launch_hist_list(ka, stream)) != hipSuccess)
+    return hip_fail(err, e, "history count kernel launch");
   e = launch_step(ka, a->dtype, any_pen, (flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream, ev0, ev1);
   if (e != hipSuccess) return hip_fail(err, e, "kernel launch");
   // [B] "Logprobs are temperature-scaled", the original-logprob switch: the
@@ -688,14 +709,14 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     return SAMPLER_EINVAL;
   }
   if (cfg->max_rows < 1 || cfg->max_vocab < 1 || cfg->max_vocab > kMaxVocab || cfg->max_history_per_row < 0 ||
-      cfg->max_history_per_row > kMaxHistPerRow || cfg->max_top_logprobs < 0 ||
+      cfg->max_history_per_row > kMaxHistLong || cfg->max_top_logprobs < 0 ||
       cfg->max_top_logprobs > kMaxTopLogprobs || cfg->max_bias_per_row < 0 ||
       cfg->max_bias_per_row > kMaxBiasPerRow || cfg->wait_spin_limit < 0 || !flags_ok(cfg->flags)) {
     set_msg(g_create_error,
             "bad config: need max_rows >= 1, 1 <= max_vocab <= %d, 0 <= max_history_per_row <= %d, "
             "0 <= max_top_logprobs <= %d, 0 <= max_bias_per_row <= %d, wait_spin_limit >= 0, known flags and "
             "at most one SAMPLER_FORCE_* flag",
-            kMaxVocab, kMaxHistPerRow, kMaxTopLogprobs, kMaxBiasPerRow);
+            kMaxVocab, kMaxHistLong, kMaxTopLogprobs, kMaxBiasPerRow);
     return SAMPLER_EINVAL;
   }
   int n_dev = 0;
@@ -758,6 +779,19 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     if ((e = hipMemset(ws.abort_word, 0, 256)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&ws.epoch_dev, 256)) != hipSuccess) goto fail;
     if ((e = hipMemset(ws.epoch_dev, 0, 256)) != hipSuccess) goto fail;
+    if (cfg->max_history_per_row > kMaxHistPerRow) {
+      // list (row, slice) of a launch of G slices of `slice` values holds at
+      // most min(max_history, slice) entries, and G min(max_history, slice)
+      // <= min(kMaxG max_history, V + slice)
+      const int64_t by_hist = (int64_t)kMaxG * cfg->max_history_per_row;
+      const int64_t by_vocab = (int64_t)cfg->max_vocab + kMaxSlice;
+      ws.hist_list_row = by_hist < by_vocab ? by_hist : by_vocab;
+      if ((e = hipMalloc((void **)&ws.hist_list, sizeof(uint32_t) * (size_t)ws.hist_list_row * cfg->max_rows)) !=
+          hipSuccess)
+        goto fail;
+      if ((e = hipMalloc((void **)&ws.hist_list_n, sizeof(int32_t) * (size_t)kMaxG * cfg->max_rows)) != hipSuccess)
+        goto fail;
+    }
     for (int s = 0; s < kRing; ++s)
       if ((e = hipEventCreateWithFlags(&h->slot_done[s], hipEventDisableTiming)) != hipSuccess) goto fail;
     if ((e = hipDeviceSynchronize()) != hipSuccess) goto fail;

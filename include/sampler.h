@@ -104,7 +104,13 @@ typedef enum sampler_dtype {
 typedef struct sampler_config {
   int32_t max_rows;            /* largest n_rows a step may pass (>= 1) */
   int32_t max_vocab;           /* largest vocab (>= 1, <= 1,048,576) */
-  int32_t max_history_per_row; /* largest history_len of one row (0..4096) */
+  int32_t max_history_per_row; /* largest history_len of one row (0..131,071).  Up to
+                                  4096 the row kernel counts a history itself; a
+                                  handle planned for more holds a count list of
+                                  4 * max_rows * min(32 * max_history_per_row,
+                                  max_vocab + 32768) bytes, which a short kernel
+                                  fills ahead of the row kernel in steps where a
+                                  row's history is longer than 4096 */
   int32_t max_top_logprobs;    /* largest top_logprobs (0..32) */
   int32_t device;              /* HIP device ordinal */
   uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_COOPERATIVE_LAUNCH | SAMPLER_INVERSE_CDF |
@@ -320,7 +326,8 @@ sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *ar
  * capture, tight serving loops, harnesses that forbid hipMalloc: one decode
  * step without a handle.  Arguments, outputs and results are those of
  * sampler_step on a handle created with the same flags and the largest
- * limits (max_history_per_row 4096, max_bias_per_row 512,
+ * limits the row kernel serves alone (max_history_per_row 4096,
+ * max_bias_per_row 512,
  * max_top_logprobs 32); n_rows may be any positive number (batches above
  * 72 rows run as several launches on `stream`).  `flags` takes
  * SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF and at most one

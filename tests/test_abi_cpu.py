@@ -186,6 +186,24 @@ def test_create_rejects_bad_config(lib):
     assert not h.value
 
 
+def test_create_history_cap(lib):
+    # histories up to 2^17 - 1 ids per row (longer than 4,096: counted ahead
+    # of the row kernel); beyond that the config is rejected before any
+    # device is touched
+    h = ctypes.c_void_p()
+    cfg = dsts.Config(max_rows=4, max_vocab=1024, max_history_per_row=131_072, max_top_logprobs=0, device=0)
+    assert lib.sampler_create(ctypes.byref(cfg), ctypes.byref(h)) == dsts.SAMPLER_EINVAL
+    lib.sampler_last_error.restype = ctypes.c_char_p
+    assert b"131071" in lib.sampler_last_error(None)
+    assert not h.value
+    cfg = dsts.Config(max_rows=4, max_vocab=1024, max_history_per_row=131_071, max_top_logprobs=0, device=0)
+    st = lib.sampler_create(ctypes.byref(cfg), ctypes.byref(h))
+    if st == dsts.SAMPLER_OK:  # a GPU is present
+        lib.sampler_destroy(h)
+    else:
+        assert st == dsts.SAMPLER_EHIP
+
+
 def test_create_rejects_two_force_flags(lib):
     h = ctypes.c_void_p()
     for flags in (dsts.FLAG_FORCE_FILTERED | dsts.FLAG_FORCE_PATH_GREEDY,

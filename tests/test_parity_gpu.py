@@ -651,3 +651,62 @@ def test_cooperative_launch_is_identical():
     assert np.all(ga["row_status"] == 0)
     a.close()
     c.close()
+
+
+# ------------------------------------------------------------ long histories
+@pytest.fixture(scope="module")
+def sampler_long():
+    _need_gpu()
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(64, 131_072, max_history_per_row=16_384, max_top_logprobs=32, max_bias_per_row=512)
+    yield s
+    s.close()
+
+
+def test_full_chain_with_16384_id_histories(sampler_long):
+    """The full-chain workload (N=64, V=128,000, fp32) with 16,384-id Zipf(1.1)
+    histories: counted ahead of the row kernel, penalties as for short ones."""
+    b = workloads.config(4, history_len=16_384)
+    check(b, sampler_long)
+
+
+@pytest.mark.parametrize("seed,n,V,dtype", [(81, 6, 30_000, "f32"), (82, 9, 70_001, "bf16")])
+def test_long_uniform_histories_mixed_with_short(sampler_long, seed, n, V, dtype):
+    """Uniform histories of up to 16,384 ids: slices with more than 4,096
+    distinct ids (the list's second pass), in batches that mix long rows with
+    rows the row kernel's own hash counts."""
+    b = workloads.random_small(seed, n, V, dtype, penalties=True, history_len=16_384)
+    b.history_len[0] = 16_384
+    b.history_len[1] = 4096
+    b.history_len[2] = 4097
+    check(b, sampler_long)
+
+
+def test_long_histories_with_processors_and_raw_logprobs(sampler_long):
+    """Long histories with logit_bias / stop lists (bias entries on tokens with
+    and without history) and a grammar mask, in the processed and the raw
+    logprob modes."""
+    b = workloads.random_small(83, 10, 40_000, "f32", penalties=True, history_len=12_000)
+    p = workloads.processors(83, b)
+    g = run_gpu(sampler_long, b, **_processors_on_device(p))
+    r = compare(g, run_oracle(b, **p.kwargs()))
+    assert r.ok(), r
+    g = run_gpu(sampler_long, b, logprob_mode="raw", **_processors_on_device(p))
+    r = compare(g, run_oracle(b, logprob_mode="raw", **p.kwargs()))
+    assert r.ok(), r
+
+
+def test_long_histories_on_device_params(sampler_long):
+    """sampler_step_graph with long histories: the count kernel runs on every
+    step of a handle planned for them; outputs equal the host-path step."""
+    b = workloads.random_small(84, 12, 30_000, "bf16", penalties=True, history_len=9000)
+    L, H = to_device(b)
+    out = _outputs(b.n_rows, b.vocab, b.top_logprobs)
+    sampler_long.step_graph(L, _device_params(b), history_ids=H, out=out, top_logprobs=b.top_logprobs)
+    torch.cuda.synchronize()
+    g = _host(out)
+    h = run_gpu(sampler_long, b, logits=L, history=H)
+    for k in ("token_ids", "probs", "logprobs", "top_logprob_ids", "top_logprob_vals", "row_status"):
+        np.testing.assert_array_equal(g[k], h[k], err_msg=k)
+    r = compare(g, run_oracle(b))
+    assert r.ok(), r
