@@ -67,6 +67,10 @@ def parse():
                     help="full-chain (default): N=64, V=128,000 with every option; the others time the "
                          "remaining synthetic workloads and the full chain's per-feature ablation "
                          "(no CPU baseline)")
+    ap.add_argument("--phase-stamps", action="store_true",
+                    help="load the library built with the stamps option (decode_step_token_sampler_amd/build.py "
+                         "--stamps), run the workload's warm-up and --steps steps one at a time, and print the "
+                         "row kernel's phase timeline (first row of each workgroup) as one JSON line")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -216,6 +220,34 @@ def cpu_baseline(batches, budget_s, threads=None):
             "host": dict(host_cpu(), thread_cap=16)}
 
 
+PHASES = ("start", "row", "loaded", "max", "hist", "x2", "decided", "gathered", "x3", "thresholds", "select",
+          "token", "end", "gumbel", "released", "arrived")
+
+
+def phase_timeline(stamps_runs, khz):
+    """Per phase: the median over steps of the median and the maximum over
+    workgroups of the time since the kernel's first stamp (us), and the
+    number of workgroups that passed it.  A phase a row skipped has no
+    stamp."""
+    per = {name: {"median_us": [], "max_us": [], "workgroups": 0} for name in PHASES}
+    for st in stamps_runs:
+        used = st[:, 0] != 0
+        if not used.any():
+            continue
+        t0 = st[used, 0].min()
+        for k, name in enumerate(PHASES):
+            col = st[used, k]
+            col = col[col != 0]
+            if col.size == 0:
+                continue
+            us = (col.astype(np.float64) - float(t0)) * 1e3 / khz
+            per[name]["median_us"].append(float(np.median(us)))
+            per[name]["max_us"].append(float(us.max()))
+            per[name]["workgroups"] = int(col.size)
+    return {name: {"median_us": float(np.median(v["median_us"])), "max_us": float(np.median(v["max_us"])),
+                   "workgroups": v["workgroups"]} for name, v in per.items() if v["median_us"]}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -256,6 +288,9 @@ def main():
         sets.append(dict(logits=L, out=out,
                          hist=None if b.history_ids is None else torch.from_numpy(b.history_ids).to(dev)))
     torch.cuda.synchronize()
+    if args.phase_stamps:
+        from decode_step_token_sampler_amd import build as libbuild
+        dsts.load_library(libbuild.LIB_STAMPS)
     S = dsts.Sampler(n, V, max_history_per_row=2048, max_top_logprobs=K)
 
     def step(i):
@@ -266,6 +301,18 @@ def main():
                       history_len=b.history_len, row_stream=b.row_stream, seed=0, offset=i,
                       want_probs=b.want_probs, want_logprobs=b.want_logprobs, top_logprobs=K, out=t["out"])
 
+    if args.phase_stamps:
+        runs, khz = [], 0
+        for i in range(args.warmup + args.steps):
+            r = step(i)
+            torch.cuda.synchronize()
+            st, khz = dsts.phase_stamps()
+            if i >= args.warmup:
+                runs.append(st)
+        print(json.dumps({"workload": desc, "path": r["path"], "steps": args.steps, "clock_khz": khz,
+                          "phases_us_since_kernel_start": phase_timeline(runs, khz)}), flush=True)
+        S.close()
+        return
     for i in range(args.warmup):
         r = step(i)
     if headline:

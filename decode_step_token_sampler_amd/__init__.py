@@ -37,7 +37,8 @@ FLAG_FORCE_PATH_GUMBEL = 1 << 5
 # symbols the header declares
 EXPORTS = ("sampler_create", "sampler_step", "sampler_step_graph", "sampler_select_path", "sampler_validate",
            "sampler_destroy", "sampler_last_error", "sampler_profile_start", "sampler_profile_stop",
-           "sampler_set_wait_spin_limit", "sampler_step_noalloc", "sampler_noalloc_last_error")
+           "sampler_set_wait_spin_limit", "sampler_step_noalloc", "sampler_noalloc_last_error",
+           "sampler_phase_stamps")
 
 
 class SamplerError(RuntimeError):
@@ -160,8 +161,26 @@ def load_library(path: str = LIB_PATH):
     L.sampler_noalloc_last_error.restype = ctypes.c_char_p
     L.sampler_last_error.argtypes = [ctypes.c_void_p]
     L.sampler_last_error.restype = ctypes.c_char_p
+    L.sampler_phase_stamps.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.POINTER(ctypes.c_int32),
+                                       ctypes.POINTER(ctypes.c_int32), ctypes.POINTER(ctypes.c_int32)]
+    L.sampler_phase_stamps.restype = ctypes.c_int
     _lib = L
     return L
+
+
+def phase_stamps():
+    """The phase stamps of the last launches on the current device (a library
+    built with the `stamps` option), cleared after reading: (uint64 array
+    [blocks, slots], clock rate in kHz).  Raises SamplerError elsewhere."""
+    L = load_library()
+    blocks, slots, khz = ctypes.c_int32(), ctypes.c_int32(), ctypes.c_int32()
+    st = L.sampler_phase_stamps(None, 0, ctypes.byref(blocks), ctypes.byref(slots), None)
+    out = np.zeros((blocks.value, slots.value), dtype=np.uint64)
+    st = L.sampler_phase_stamps(out.ctypes.data, out.size, ctypes.byref(blocks), ctypes.byref(slots),
+                                ctypes.byref(khz))
+    if st != SAMPLER_OK:
+        raise SamplerError(st, "phase stamps need a library built with the stamps option")
+    return out, khz.value
 
 
 def _host(a, dtype, n):

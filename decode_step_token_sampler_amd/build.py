@@ -14,6 +14,9 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "libdsts_sampler.so")
+# the same library with the row kernel's phase stamps compiled in (for
+# performance work only; the stamps' stores perturb the timings a little)
+LIB_STAMPS = os.path.join(PKG, "libdsts_sampler_stamps.so")
 SOURCES = [os.path.join(CSRC, "sampler_kernel.hip"), os.path.join(CSRC, "sampler_runtime.cpp")]
 HEADERS = [os.path.join(CSRC, "sampler_internal.h"), os.path.join(INCLUDE, "sampler.h")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -24,16 +27,17 @@ FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared", "-ffp
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops", "-I", INCLUDE]
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp%d" % os.getpid()
-    cmd = [HIPCC, *FLAGS, *SOURCES, "-o", tmp]
+def build(verbose: bool = False, stamps: bool = False) -> str:
+    lib = LIB_STAMPS if stamps else LIB
+    tmp = lib + ".tmp%d" % os.getpid()
+    cmd = [HIPCC, *FLAGS, *(["-DDSTS_PHASE_STAMPS"] if stamps else []), *SOURCES, "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("hipcc failed:\n" + res.stdout + res.stderr)
     if verbose:
         print(res.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def ensure_built() -> str:
@@ -44,4 +48,5 @@ def ensure_built() -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    import sys
+    print(build(verbose=True, stamps="--stamps" in sys.argv[1:]))

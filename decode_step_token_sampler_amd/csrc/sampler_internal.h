@@ -129,6 +129,30 @@ static_assert(offsetof(WgSlots, x1) % 16 == 0 && offsetof(WgSlots, fin) % 16 == 
 
 enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINISTIC = 3 };
 
+// Phase stamps (builds with DSTS_PHASE_STAMPS): slot k of a workgroup's
+// record holds the real-time clock at the end of phase k of its first row
+// (0 where the row skipped the phase).
+constexpr int kStampBlocks = 2048;
+constexpr int kStampSlots = 20;
+enum : int {
+  kStampStart = 0,       // the kernel starts
+  kStampRow = 1,         // the row's record is read
+  kStampLoaded = 2,      // the slice is in LDS (loads, temperature, penalties, processors)
+  kStampMax = 3,         // the slice's max and first argmax
+  kStampHist = 4,        // the window histogram and the exchange-2 record are stored
+  kStampX2 = 5,          // the exchange-2 barrier is passed
+  kStampDecided = 6,     // exchange 2 is merged: row max, threshold bins
+  kStampGathered = 7,    // the candidates are gathered and stored
+  kStampX3 = 8,          // the exchange-3 barrier is passed
+  kStampThresholds = 9,  // thresholds and the kept-set sum are exact
+  kStampSelect = 10,     // selection and output stores start (after the general path)
+  kStampToken = 11,      // the last workgroup to arrive has written the token
+  kStampEnd = 12,        // the row's outputs are issued
+  kStampGumbel = 13,     // this workgroup's Gumbel-max winner is known (thread 0's wave)
+  kStampReleased = 14,   // final exchange: this workgroup's record is stored
+  kStampArrived = 15,    // final exchange: this workgroup has arrived
+};
+
 // Per-row parameters in device memory (one entry per row, or null for the
 // default), normalised by the kernel itself.
 struct DevRowArrays {
@@ -216,6 +240,10 @@ hipError_t launch_raw_lp(const KernelArgs &ka, int dtype, hipStream_t stream);
 // Count the histories longer than kMaxHistPerRow into kp.hist_list (one
 // workgroup per record and slice), ahead of the row kernel of the same step.
 hipError_t launch_hist_list(const KernelArgs &ka, hipStream_t stream);
+// Builds with DSTS_PHASE_STAMPS: copy the first n stamp words of the
+// current device to host (synchronously), then clear them; other builds
+// return hipErrorNotSupported.
+hipError_t phase_stamps_take(unsigned long long *host, size_t n);
 // Dynamic LDS bytes of hist_list_kernel for a slice.
 size_t hist_list_lds_bytes(int slice);
 // Launch one step.  The grid never exceeds the workgroups the device holds at

@@ -503,9 +503,14 @@ DEV void order_acquire() {
 // bits 32..63, the epoch of the launch that last used them; every launch has
 // its own epoch (host launches count up from 1, launches whose epoch lives
 // in device memory have bit 31 set).  A launch therefore never inherits an
-// earlier launch's count, also after that launch aborted mid-count: its
-// first arrival at a word claims the word by a compare-and-swap from the old
-// epoch, as if it were clear; later arrivals add one.
+// earlier launch's count, also after that launch aborted mid-count.  At its
+// start a launch claims its groups' words with a fire-and-forget atomic max
+// of epoch << 32 (epochs mostly increase, so the max resets a word to this
+// launch's epoch with zero counts, and leaves a word it already claimed as
+// it is).  An arrival adds one; an arrival that still finds an older epoch
+// (the claim has not landed, or the epochs went back) claims the word by a
+// compare-and-swap from what it holds, as if it were clear, or adds again
+// once another arrival has claimed it.
 //   barrier word: epoch << 32 | generation << 8 | arrivals
 //   final word:   epoch << 32 | arrivals
 // The last arrival at a barrier resets the count and advances the
@@ -516,20 +521,28 @@ struct GroupCtx {
   uint32_t epoch;
   uint32_t spin_limit;
   int G;
-  bool claimed;  // this workgroup has seen its launch's epoch on the barrier word (thread 0 only)
 };
+
+// The launch's claim of a group's two words (one thread per group).
+DEV void claim_words(GroupSync *s, uint32_t epoch) {
+  const unsigned long long mine = (unsigned long long)epoch << 32;
+  __hip_atomic_fetch_max(&s->word, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_fetch_max(&s->fin, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // One arrival at a group word; returns the word's value before it (the
 // count of an older epoch reads as 0).
-DEV unsigned long long arrive_word(unsigned long long *w, uint32_t epoch, bool claimed) {
+DEV unsigned long long arrive_word(unsigned long long *w, uint32_t epoch) {
   const unsigned long long mine = (unsigned long long)epoch << 32;
-  if (!claimed) {
-    unsigned long long cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    while ((uint32_t)(cur >> 32) != epoch) {
-      if (__hip_atomic_compare_exchange_strong(w, &cur, mine | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
-                                               __HIP_MEMORY_SCOPE_AGENT))
-        return mine;
-    }
+  const unsigned long long old = __hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if ((uint32_t)(old >> 32) == epoch) return old;
+  // an older epoch's word (the add above went to its count, which the claim
+  // discards)
+  unsigned long long cur = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while ((uint32_t)(cur >> 32) != epoch) {
+    if (__hip_atomic_compare_exchange_strong(w, &cur, mine | 1ull, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                             __HIP_MEMORY_SCOPE_AGENT))
+      return mine;
   }
   return __hip_atomic_fetch_add(w, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -563,9 +576,13 @@ DEV void spin_gen(const GroupCtx &gc, uint32_t g0) {
 DEV void group_barrier(SmemBase &sm, GroupCtx &gc) {
   order_release();
   __syncthreads();
+  if (gc.G == 1) {  // a one-workgroup group: its own stores are all there is to wait for
+    if (tidx() == 0) order_acquire();
+    __syncthreads();
+    return;
+  }
   if (tidx() == 0) {
-    const unsigned long long old = arrive_word(&gc.s->word, gc.epoch, gc.claimed);
-    gc.claimed = true;
+    const unsigned long long old = arrive_word(&gc.s->word, gc.epoch);
     const uint32_t g0 = ((uint32_t)old >> 8) & 0xFFFFFFu;
     if ((old & 0xFFull) == (unsigned long long)gc.G - 1ull)
       __hip_atomic_store(&gc.s->word, ((unsigned long long)gc.epoch << 32) | ((unsigned long long)((g0 + 1u) & 0xFFFFFFu) << 8),
@@ -579,7 +596,8 @@ DEV void group_barrier(SmemBase &sm, GroupCtx &gc) {
 // Arrival at the final exchange of a row: true in the last workgroup to
 // arrive, which resets the count (one lane calls it).
 DEV bool final_arrive(const GroupCtx &gc) {
-  const unsigned long long old = arrive_word(&gc.s->fin, gc.epoch, false);
+  if (gc.G == 1) return true;
+  const unsigned long long old = arrive_word(&gc.s->fin, gc.epoch);
   const bool last = (old & 0xFFull) == (unsigned long long)gc.G - 1ull;
   if (last) __hip_atomic_store(&gc.s->fin, (unsigned long long)gc.epoch << 32, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   return last;
@@ -1053,32 +1071,48 @@ DEV E3Out e3_decide(SmemBase &sm, const int n, const double *sq, uint32_t *lc, c
   return E3Out{(flags & 1u) != 0u, t, lns};
 }
 
-// The last workgroup of a row writes it: the row max and first argmax over
-// the slices' max keys (sm.gk; rows that skipped exchange 2 get their
-// status here) and, with Gumbel-max, the best of the slices' best scores
-// (sm.gd) and their indices (sm.gi), ties to the lower index.
-DEV void finish_row(const SmemBase &sm, const KernelParams &kp, uint32_t epoch, int row, int G, bool gumbel,
-                    bool token_set) {
-  unsigned long long mk = 0;
-  for (int g = 0; g < G; ++g) mk = sm.gk[g] > mk ? sm.gk[g] : mk;
+// The last workgroup of a row writes it: the row max and first argmax (the
+// largest of the slices' max keys; rows that skipped exchange 2 get their
+// status here) and, with Gumbel-max, the best of the slices' best scores,
+// ties to the lower index.  With `reduce`, one whole wave calls it: lane g
+// < G holds slice g's record (max key mk, best score bg, its index bi), the
+// other lanes the identities (0, -inf, 0x7FFFFFFF); the reductions run
+// across the wave and lane 0 writes.  Without, lane 0 alone calls it with
+// the row's only record.  aborted: lane 0's reading of the abort word.
+DEV void finish_row(const KernelParams &kp, bool aborted, int row, bool gumbel, bool token_set, unsigned long long mk,
+                    double bg, int bi, bool reduce) {
+  if (reduce) {
+    mk = wave_max_u(mk);
+    wave_best(bg, bi);
+    if ((tidx() & 63) != 0) return;
+  }
   const float mx = key_to_float((uint32_t)(mk >> 32));
   const int status = (mx > -INFINITY && mx < INFINITY) ? 0 : (mx == INFINITY ? 2 : 1);
   int token = (int)(0xFFFFFFFFu - (uint32_t)(mk & 0xFFFFFFFFu));
-  if (gumbel) {
-    double bg = -INFINITY;
-    int bi = 0x7FFFFFFF;
-    for (int g = 0; g < G; ++g) {
-      if (sm.gd[g] > bg || (sm.gd[g] == bg && sm.gi[g] < bi)) {
-        bg = sm.gd[g];
-        bi = sm.gi[g];
-      }
-    }
-    if (bi != 0x7FFFFFFF) token = bi;
-  }
-  const bool aborted = atomic_ld(kp.abort_word) == epoch;
+  if (gumbel && bi != 0x7FFFFFFF) token = bi;
   // token_set: the inverse-CDF selection already wrote the token
   if (!token_set || aborted || status != 0) kp.token_ids[row] = (aborted || status != 0) ? -1 : token;
   if (kp.row_status) kp.row_status[row] = aborted ? 3 : status;
+}
+
+// The final-exchange records of a row's G workgroups and the abort word, read
+// by one wave (lane g < G: slice g's record), then finish_row.
+DEV void merge_final(const KernelParams &kp, const WgSlots *peers, unsigned fpar, uint32_t epoch, int row, int G,
+                     bool gumbel, bool token_set) {
+  const int lane = tidx() & 63;
+  unsigned long long k = 0;
+  double g = -INFINITY;
+  int i = 0x7FFFFFFF;
+  bool ab = false;
+  if (lane < G) {
+    u32x4 r0, r1, ra;
+    coh_load16x3(&peers[lane].fin[fpar][0], &peers[lane].fin[fpar][2], kp.abort_word, r0, r1, ra);
+    g = f64_of(r0.x, r0.y);
+    i = (int)r0.z;
+    k = u64_of(r1.x, r1.y);
+    ab = ra.x == epoch;
+  }
+  finish_row(kp, ab, row, gumbel, token_set, k, g, i, true);
 }
 
 // A row's record from per-row arrays in device memory, normalised and
@@ -1183,6 +1217,32 @@ DEV void block_group(const KernelParams &kp, int &group, int &gid) {
   }
 }
 
+// ---------------------------------------------------------------- phase stamps
+// Builds with DSTS_PHASE_STAMPS record the real-time clock (s_memrealtime,
+// a constant-rate counter shared by the whole device) at the phase
+// boundaries of the first row each workgroup walks: thread 0 stores it to
+// g_phase_stamps[block][k].  Other builds compile the stamps out.
+#ifdef DSTS_PHASE_STAMPS
+__device__ unsigned long long g_phase_stamps[kStampBlocks * kStampSlots];
+#define PHASE_STAMP(k)                                                                                        \
+  do {                                                                                                        \
+    if (tidx() == 0 && it == 0u && blockIdx.x < (unsigned)kStampBlocks)                                       \
+      g_phase_stamps[blockIdx.x * kStampSlots + (k)] = wall_clock64();                                        \
+  } while (0)
+// a stamp taken by whichever single thread reaches it (the caller ensures one)
+#define PHASE_STAMP_ONE(k)                                                                                    \
+  do {                                                                                                        \
+    if (it == 0u && blockIdx.x < (unsigned)kStampBlocks) g_phase_stamps[blockIdx.x * kStampSlots + (k)] = wall_clock64(); \
+  } while (0)
+#else
+#define PHASE_STAMP(k) \
+  do {                 \
+  } while (0)
+#define PHASE_STAMP_ONE(k) \
+  do {                     \
+  } while (0)
+#endif
+
 // ---------------------------------------------------------------- the kernel
 template <typename TIn, bool PEN>
 __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
@@ -1223,7 +1283,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   rc.gc.epoch = epoch;
   rc.gc.spin_limit = kp.spin_limit ? kp.spin_limit : kSpinLimit;
   rc.gc.G = G;
-  rc.gc.claimed = false;
+  if (gid == 0 && G > 1 && tidx() == 0) claim_words(rc.gc.s, epoch);
   rc.my = kp.slots + (size_t)group * G + gid;
   rc.peers = kp.slots + (size_t)group * G;
   rc.xseq = &xseq;
@@ -1242,10 +1302,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   rc.s0 = s0;
   rc.n = s1 - s0;
   rc.n4 = (rc.n + 3) & ~3;
+  unsigned it = 0;
+  PHASE_STAMP(kStampStart);
   for (int j = tidx(); j < 64; j += kBlock) sm.exp_tab[j] = exp2((double)j * (1.0 / 64.0));
   __syncthreads();
 
-  unsigned it = 0;
   // Record ri describes batch row rows[ri].row: the host puts the rows it
   // expects to take longest on the groups whose workgroups are dispatched
   // first.
@@ -1265,6 +1326,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const RowParam P = kp.rows ? kp.rows[ri] : ka.rows[ri];
     const int row = P.row;
     rc.row = row;
+    PHASE_STAMP(kStampRow);
     if (P.flags & RF_BAD) {
       // device-side parameters that break the rules: status 4
       if (want_out)
@@ -1608,10 +1670,12 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       lidx = s0 + lgrp + (zv[0] == lmax ? 0 : zv[1] == lmax ? 1 : zv[2] == lmax ? 2 : 3);
     }
 
+    PHASE_STAMP(kStampLoaded);
     // ---- 2. this slice's max and first argmax as one order key (value key
     // << 32 | ~index: the largest key is the first argmax)
     const unsigned long long lkey = wg_max_u(sm, ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx));
     const float mg = key_to_float((uint32_t)(lkey >> 32));  // -inf: no finite value in this slice
+    PHASE_STAMP(kStampMax);
     const unsigned par = it & 1u;
     const float wsc = T < 1.0f ? T : 1.0f;  // bin scale (see abin)
     const bool need_sel = topk || topp || K > 0 || (truncated && want_S);  // window + candidates
@@ -1713,7 +1777,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         atomic_st(&rc.my->x1[xp][3], (unsigned long long)__double_as_longlong(wsx));
       }
       const double lmp = minp ? log((double)P.min_p) : 0.0;  // min-p's guess, taken before the wait
+      PHASE_STAMP(kStampHist);
       group_barrier(sm, rc.gc);
+      PHASE_STAMP(kStampX2);
       // ---- exchange 2, merged by every workgroup of the row alike: the
       // records and the first histogram pairs in one batch of 16-byte reads,
       // the row max, each slice's bin shift and mass scale, integer LDS adds
@@ -1929,6 +1995,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // no workgroup arrives at the next row's final exchange (or rewrites its
     // record of this row, two rows on) before this row's last arrival has
     // read the records.
+    PHASE_STAMP(kStampDecided);
     if (!need_x && kp.n_rows > kp.n_groups) row_barrier(sm, rc);
     const float mf = (float)m;
 
@@ -2079,7 +2146,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         po[j] = 2 * (pj - pg[j] * pps);
         pp[j] = &peers[min(pg[j], G - 1)].cand[xq][pg[j] < G ? po[j] : 0];
       }
+      PHASE_STAMP(kStampGathered);
       group_barrier(sm, rc.gc);
+      PHASE_STAMP(kStampX3);
       // ---- exchange 3, in every workgroup alike: wave 0 reads the counts and
       // the first candidates of every slice in one batch (pairs of keys; a
       // slot's array has room past an odd count), places them in the list
@@ -2372,6 +2441,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       __syncthreads();
     }
 
+    PHASE_STAMP(kStampThresholds);
     // ---- general path: radix selects and an exact kept-set sum
     if (general) {
       tau = 0;
@@ -2610,27 +2680,30 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const unsigned fpar = it & 1u;
     const bool late_fin = general && K > 0;
     auto final_exchange = [&]() __attribute__((always_inline)) {  // one wave
+      if (G == 1) {  // the row's only workgroup: the exchange stays in registers
+        // (a one-workgroup launch never waits, so it cannot have aborted)
+        if (lane == 0) {
+          finish_row(kp, false, row, gumbel, icdf, lkey, best_g, best_i, false);
+          PHASE_STAMP_ONE(kStampToken);
+        }
+        return;
+      }
       if (lane == 0) {
         atomic_st(&rc.my->fin[fpar][0], (unsigned long long)__double_as_longlong(best_g));
         atomic_st(&rc.my->fin[fpar][1], (unsigned long long)(uint32_t)best_i);
         atomic_st(&rc.my->fin[fpar][2], lkey);
       }
       order_release();
+      if (lane == 0) PHASE_STAMP_ONE(kStampReleased);
       uint32_t last = 0;
       if (lane == 0) {
         last = final_arrive(rc.gc) ? 1u : 0u;
         if (last) order_acquire();
+        PHASE_STAMP_ONE(kStampArrived);
       }
       if (__builtin_amdgcn_readfirstlane(last)) {
-        if (lane < G) {
-          u32x4 r0, r1;
-          coh_load16x2(&rc.peers[lane].fin[fpar][0], &rc.peers[lane].fin[fpar][2], r0, r1);
-          sm.gd[lane] = f64_of(r0.x, r0.y);
-          sm.gi[lane] = (int)r0.z;
-          sm.gk[lane] = u64_of(r1.x, r1.y);
-        }
-        __builtin_amdgcn_wave_barrier();
-        if (lane == 0) finish_row(sm, kp, rc.gc.epoch, row, G, gumbel, icdf);
+        merge_final(kp, rc.peers, fpar, rc.gc.epoch, row, G, gumbel, icdf);
+        if (lane == 0) PHASE_STAMP_ONE(kStampToken);
       }
     };
 
@@ -2715,6 +2788,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     using I2 = std::integral_constant<int, 2>;
     using B0 = std::integral_constant<bool, false>;
     using B1 = std::integral_constant<bool, true>;
+    PHASE_STAMP(kStampSelect);
     if (omode != 0 && !late_fin && tau != 0) {
       // A truncated row: waves 4..7 write the outputs from the start; waves
       // 0..3 run Gumbel-max over the whole slice meanwhile (the kept set is
@@ -2727,6 +2801,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           gumbel_pass(NT256{});
           wave_best(best_g, best_i);
         }
+        PHASE_STAMP(kStampGumbel);
         if (lane == 0) {
           sm.red_d[wave] = best_g;
           sm.red_i[wave] = best_i;
@@ -2758,6 +2833,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         gumbel_pass(NT512{});
         wg_best(sm, best_g, best_i);
       }
+      PHASE_STAMP(kStampGumbel);
       if (!late_fin && wave == 0) final_exchange();
       if (lp_all) {
         if (omode == 1) emit_loop(I1{}, NT512{}, B1{});
@@ -2785,15 +2861,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       }
       __syncthreads();
       if (sm.bu[15]) {
-        if (tid < G) {
-          u32x4 r0, r1;
-          coh_load16x2(&rc.peers[tid].fin[fpar][0], &rc.peers[tid].fin[fpar][2], r0, r1);
-          sm.gd[tid] = f64_of(r0.x, r0.y);
-          sm.gi[tid] = (int)r0.z;
-          sm.gk[tid] = u64_of(r1.x, r1.y);
-        }
-        __syncthreads();
-        if (tid == 0) finish_row(sm, kp, rc.gc.epoch, row, G, gumbel, icdf);
+        if (wave == 0) merge_final(kp, rc.peers, fpar, rc.gc.epoch, row, G, gumbel, icdf);
         // merge the G local top-logprob lists (keys are distinct: each holds
         // its index): an entry's rank among all entries is its output slot
         unsigned long long *ent = reinterpret_cast<unsigned long long *>(region);
@@ -2822,6 +2890,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       }
     }
     __syncthreads();
+    PHASE_STAMP(kStampEnd);
   }
 }
 
@@ -2903,7 +2972,7 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
   gc.epoch = kp.epoch_dev ? atomic_ld(kp.epoch_dev) + kp.epoch_dev_add : kp.epoch;
   gc.spin_limit = kp.spin_limit ? kp.spin_limit : kSpinLimit;
   gc.G = G;
-  gc.claimed = false;
+  if (gid == 0 && G > 1 && tidx() == 0) claim_words(gc.s, gc.epoch);
   const int s0 = gid * kp.slice, s1 = min(V, s0 + kp.slice), ln = s1 - s0;
   for (int j = tidx(); j < 64; j += kBlock) sm.exp_tab[j] = exp2((double)j * (1.0 / 64.0));
   unsigned it = 0;
@@ -3088,6 +3157,23 @@ hipError_t set_lds_attr(size_t lds) {
 }
 
 }  // namespace
+
+hipError_t phase_stamps_take(unsigned long long *host, size_t n) {
+#ifdef DSTS_PHASE_STAMPS
+  const size_t total = (size_t)kStampBlocks * kStampSlots;
+  if (n > total) n = total;
+  hipError_t e = hipMemcpyFromSymbol(host, HIP_SYMBOL(g_phase_stamps), n * sizeof(unsigned long long), 0,
+                                     hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return e;
+  void *p = nullptr;
+  if ((e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_phase_stamps))) != hipSuccess) return e;
+  return hipMemset(p, 0, total * sizeof(unsigned long long));
+#else
+  (void)host;
+  (void)n;
+  return hipErrorNotSupported;
+#endif
+}
 
 size_t hist_list_lds_bytes(int slice) { return sizeof(uint32_t) * (size_t)slice; }
 

@@ -33,6 +33,11 @@ constexpr int kRing = 4;
 // [A] "One request with top_p takes the whole batch off the fast path":
 // temperatures in [0, 1e-6) are greedy.
 constexpr double kGreedyEps = 1e-6;
+// Values per thread of a launch whose rows exchange only at the end (see
+// launch_is_light).  Measured on MI355X, batch-1 Gumbel at V=151,936 (ids
+// only), kernel time: 16 values per thread (19 workgroups) 18.0 us, 8 (32
+// workgroups, the cap) 16.8 us, 4 (also 32) 16.7 us.
+constexpr int kLightValuesPerThread = 8;
 // [B] "What the flag switches": requests without a seed use 42.
 constexpr uint64_t kDeterministicSeed = 42;
 
@@ -369,8 +374,8 @@ sampler_status plan_workspace(Workspace &ws, int device, int32_t max_hist, int32
 
 // The launch plan: G workgroups of `slice` values per row, `groups` row
 // groups (rows strided over them).
-sampler_status plan_groups(const Workspace &ws, bool det, int n, int V, int *G_out, int *slice_out, int *groups_out,
-                           std::string &err) {
+sampler_status plan_groups(const Workspace &ws, bool det, bool light, int n, int V, int *G_out, int *slice_out,
+                           int *groups_out, std::string &err) {
   // deterministic launches cut every row by the slice cap of the largest
   // hashes any handle may have, so that the cut -- and with it each row's
   // reduction order -- depends on V alone, not on the handle's limits
@@ -387,8 +392,11 @@ sampler_status plan_groups(const Workspace &ws, bool det, int n, int V, int *G_o
     const int fill = ws.resident / n;
     // at least ~32 values per thread: a row's steps are latency-bound, and
     // fewer workgroups per row exchange faster (measured on MI355X at N=8,
-    // V=151,936: 10 workgroups per row 34.7 us, 32 workgroups 41.9 us)
-    const int by_work = (V + 32 * kBlock - 1) / (32 * kBlock);
+    // V=151,936: 10 workgroups per row 34.7 us, 32 workgroups 41.9 us).
+    // Light launches exchange once, at the end, and spend their time in
+    // Philox and the loads: kLightValuesPerThread.
+    const int vpt = light ? kLightValuesPerThread : 32;
+    const int by_work = (V + vpt * kBlock - 1) / (vpt * kBlock);
     G = fill < by_work ? fill : by_work;
     if (G > kMaxG) G = kMaxG;
     if (G > ws.resident) G = ws.resident;
@@ -402,6 +410,21 @@ sampler_status plan_groups(const Workspace &ws, bool det, int n, int V, int *G_o
   *slice_out = slice;
   *groups_out = groups < n ? groups : n;
   return SAMPLER_OK;
+}
+
+// Whether no row of a step needs its row's merged max: no outputs besides
+// the token, no top-k / top-p / min-p, no inverse-CDF selection (rows that
+// keep every token, and greedy rows).  Such rows meet their peers only in
+// the final exchange, so the launch spreads them over more workgroups.
+bool launch_is_light(const sampler_step_args *a, uint32_t flags) {
+  if ((flags & SAMPLER_INVERSE_CDF) || a->probs || a->logprobs || a->top_logprobs > 0) return false;
+  for (int r = 0; r < a->n_rows; ++r) {
+    if (row_is_greedy(a->temperature ? a->temperature[r] : 1.0f)) continue;
+    const int32_t k = a->top_k ? a->top_k[r] : -1;
+    if ((k != -1 && k < a->vocab) || (a->top_p && a->top_p[r] < 1.0f) || (a->min_p && a->min_p[r] > 0.0f))
+      return false;
+  }
+  return true;
 }
 
 // The order in which the kernel's row groups start: block b of the grid is
@@ -524,7 +547,7 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
   hipError_t e;
   int G, slice, groups;
-  sampler_status st = plan_groups(ws, det, n, V, &G, &slice, &groups, err);
+  sampler_status st = plan_groups(ws, det, !dev && launch_is_light(a, flags), n, V, &G, &slice, &groups, err);
   if (st != SAMPLER_OK) return st;
   KernelParams &kp = ka.kp;
   kp = KernelParams{};
@@ -859,7 +882,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
     dp = h->dev_ring + (size_t)slot * h->cfg.max_rows;
   }
   int G, slice, groups;
-  st = plan_groups(h->ws, det, n, V, &G, &slice, &groups, h->err);
+  st = plan_groups(h->ws, det, launch_is_light(a, h->cfg.flags), n, V, &G, &slice, &groups, h->err);
   if (st != SAMPLER_OK) return st;
   const bool any_pen = build_records(a, det, 0, n, h->recs.data());
   place_records(h->recs.data(), n, groups, h->rank.data(), h->order.data(), rp);
@@ -941,7 +964,7 @@ sampler_status sampler_step_noalloc(const sampler_step_args *a, uint32_t flags, 
   for (int r0 = 0; r0 < a->n_rows; r0 += kArgRows) {
     const int n = a->n_rows - r0 < kArgRows ? a->n_rows - r0 : kArgRows;
     int G, slice, groups;
-    st = plan_groups(ws, det, n, a->vocab, &G, &slice, &groups, g_static_error);
+    st = plan_groups(ws, det, launch_is_light(a, flags), n, a->vocab, &G, &slice, &groups, g_static_error);
     if (st != SAMPLER_OK) return st;
     RowParam recs[kArgRows];
     int rank[kArgRows], ord[kArgRows];
@@ -955,6 +978,21 @@ sampler_status sampler_step_noalloc(const sampler_step_args *a, uint32_t flags, 
 }
 
 const char *sampler_noalloc_last_error(void) { return g_static_error.c_str(); }
+
+sampler_status sampler_phase_stamps(uint64_t *host_out, int32_t cap, int32_t *blocks_out, int32_t *slots_out,
+                                    int32_t *clock_khz_out) {
+  if (blocks_out) *blocks_out = kStampBlocks;
+  if (slots_out) *slots_out = kStampSlots;
+  if (!host_out || cap < 0) return SAMPLER_EINVAL;
+  int dev = 0, khz = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev);
+  if (e != hipSuccess) return SAMPLER_EHIP;
+  if (clock_khz_out) *clock_khz_out = khz;
+  e = phase_stamps_take(reinterpret_cast<unsigned long long *>(host_out), (size_t)cap);
+  if (e == hipErrorNotSupported) return SAMPLER_ENOTSUP;
+  return e == hipSuccess ? SAMPLER_OK : SAMPLER_EHIP;
+}
 
 sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a, const sampler_device_params *dp,
                                   void *stream_ptr) {

@@ -395,6 +395,19 @@ void sampler_destroy(sampler_handle *h);
  * stays valid until the next call on the handle. */
 const char *sampler_last_error(const sampler_handle *h);
 
+/* Phase timeline of the row kernel, for performance work.  A library built
+ * with -DDSTS_PHASE_STAMPS (build option `stamps`) records the device's
+ * real-time clock at the phase boundaries of the first row each workgroup
+ * walks, in a device array of *blocks_out x *slots_out words (workgroup
+ * b's stamps at [b * slots ..], one slot per phase, 0 where a phase did not
+ * run; the phases are those of the row kernel's description).  This call
+ * copies the first `cap` words of the current device's array to host_out,
+ * synchronously, then clears the array; *clock_khz_out receives the
+ * clock's rate.  Other builds return SAMPLER_ENOTSUP (after setting
+ * *blocks_out and *slots_out). */
+sampler_status sampler_phase_stamps(uint64_t *host_out, int32_t cap, int32_t *blocks_out, int32_t *slots_out,
+                                    int32_t *clock_khz_out);
+
 #ifdef __cplusplus
 }
 #endif
