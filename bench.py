@@ -224,13 +224,56 @@ PHASES = ("start", "row", "loaded", "max", "hist", "x2", "decided", "gathered", 
           "token", "end", "gumbel", "released", "arrived")
 
 
+ROW_INDEX_SLOT = 19
+
+
+def row_class(b, r):
+    """The cost class of row r of batch b, as the phase table groups rows."""
+    t = float(b.temperature[r])
+    if 0.0 <= t < 1e-6:
+        return "greedy"
+    k = int(b.top_k[r])
+    topk = k != -1 and k < b.vocab
+    topp = float(b.top_p[r]) < 1.0
+    minp = float(b.min_p[r]) > 0.0
+    if k == 1:
+        return "top-1"
+    if not (topk or topp or minp):
+        return "keep-all"
+    return "+".join(n for n, on in (("top-k", topk), ("top-p", topp), ("min-p", minp)) if on)
+
+
+def phase_by_class(stamps_runs, khz):
+    """Per row class: the median over steps and workgroups of the time since
+    the kernel's first stamp at which the workgroups' rows reach selection
+    and their end (us).  stamps_runs: (stamps, batch) of each step."""
+    acc = {}
+    for st, b in stamps_runs:
+        used = st[:, 0] != 0
+        if not used.any():
+            continue
+        t0 = float(st[used, 0].min())
+        for blk in np.flatnonzero(used):
+            r = int(st[blk, ROW_INDEX_SLOT]) - 1
+            if r < 0:
+                continue
+            c = acc.setdefault(row_class(b, r), {"select": [], "end": [], "rows": set()})
+            c["rows"].add(r)
+            for name, k in (("select", PHASES.index("select")), ("end", PHASES.index("end"))):
+                if st[blk, k]:
+                    c[name].append((float(st[blk, k]) - t0) * 1e3 / khz)
+    return {cls: {"rows": len(v["rows"]), "select_us": float(np.median(v["select"])) if v["select"] else None,
+                  "end_us": float(np.median(v["end"])) if v["end"] else None,
+                  "end_max_us": float(np.max(v["end"])) if v["end"] else None} for cls, v in sorted(acc.items())}
+
+
 def phase_timeline(stamps_runs, khz):
     """Per phase: the median over steps of the median and the maximum over
     workgroups of the time since the kernel's first stamp (us), and the
     number of workgroups that passed it.  A phase a row skipped has no
     stamp."""
     per = {name: {"median_us": [], "max_us": [], "workgroups": 0} for name in PHASES}
-    for st in stamps_runs:
+    for st, _ in stamps_runs:
         used = st[:, 0] != 0
         if not used.any():
             continue
@@ -308,9 +351,10 @@ def main():
             torch.cuda.synchronize()
             st, khz = dsts.phase_stamps()
             if i >= args.warmup:
-                runs.append(st)
+                runs.append((st, batches[i % n_sets]))
         print(json.dumps({"workload": desc, "path": r["path"], "steps": args.steps, "clock_khz": khz,
-                          "phases_us_since_kernel_start": phase_timeline(runs, khz)}), flush=True)
+                          "phases_us_since_kernel_start": phase_timeline(runs, khz),
+                          "by_row_class": phase_by_class(runs, khz)}), flush=True)
         S.close()
         return
     for i in range(args.warmup):

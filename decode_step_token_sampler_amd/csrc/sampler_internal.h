@@ -151,6 +151,7 @@ enum : int {
   kStampGumbel = 13,     // this workgroup's Gumbel-max winner is known (thread 0's wave)
   kStampReleased = 14,   // final exchange: this workgroup's record is stored
   kStampArrived = 15,    // final exchange: this workgroup has arrived
+  kStampRowIndex = 19,   // not a time: 1 + the index of the row the stamps describe
 };
 
 // Per-row parameters in device memory (one entry per row, or null for the

@@ -1234,7 +1234,16 @@ __device__ unsigned long long g_phase_stamps[kStampBlocks * kStampSlots];
   do {                                                                                                        \
     if (it == 0u && blockIdx.x < (unsigned)kStampBlocks) g_phase_stamps[blockIdx.x * kStampSlots + (k)] = wall_clock64(); \
   } while (0)
+// a value instead of the clock (the row's index)
+#define PHASE_RECORD(k, v)                                                                                    \
+  do {                                                                                                        \
+    if (tidx() == 0 && it == 0u && blockIdx.x < (unsigned)kStampBlocks)                                       \
+      g_phase_stamps[blockIdx.x * kStampSlots + (k)] = (unsigned long long)(v);                               \
+  } while (0)
 #else
+#define PHASE_RECORD(k, v) \
+  do {                     \
+  } while (0)
 #define PHASE_STAMP(k) \
   do {                 \
   } while (0)
@@ -1327,6 +1336,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const int row = P.row;
     rc.row = row;
     PHASE_STAMP(kStampRow);
+    PHASE_RECORD(kStampRowIndex, row + 1);
     if (P.flags & RF_BAD) {
       // device-side parameters that break the rules: status 4
       if (want_out)
