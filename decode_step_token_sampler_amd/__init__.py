@@ -20,7 +20,9 @@ from typing import Optional
 import numpy as np
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libdsts_sampler.so")
+# DSTS_LIBRARY: the same library built elsewhere (the sanitizer test loads
+# one whose host code carries address and UB checks)
+LIB_PATH = os.environ.get("DSTS_LIBRARY") or os.path.join(_PKG, "libdsts_sampler.so")
 
 SAMPLER_OK, SAMPLER_EINVAL, SAMPLER_ECAPACITY, SAMPLER_EHIP, SAMPLER_ENOTSUP = 0, -1, -2, -3, -4
 STATUS_NAMES = {0: "OK", -1: "EINVAL", -2: "ECAPACITY", -3: "EHIP", -4: "ENOTSUP"}

@@ -110,7 +110,9 @@ def lib():
     global _lib
     with _lock:
         if _lib is None:
-            path = build()
+            # ORACLE_LIBRARY: an oracle built elsewhere from the same source
+            # (the sanitizer test builds one with address and UB checks)
+            path = os.environ.get("ORACLE_LIBRARY") or build()
             L = ctypes.CDLL(path)
             L.orc_step.argtypes = [ctypes.POINTER(_Args)]
             L.orc_step.restype = ctypes.c_int
