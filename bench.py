@@ -71,6 +71,10 @@ def parse():
                     help="load the library built with the stamps option (decode_step_token_sampler_amd/build.py "
                          "--stamps), run the workload's warm-up and --steps steps one at a time, and print the "
                          "row kernel's phase timeline (first row of each workgroup) as one JSON line")
+    ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV", "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="write the row kernel's HBM traffic per launch (the counter_collection.csv files of "
+                         "rocprofv3 --pmc FETCH_SIZE / WRITE_SIZE runs of this benchmark and of --calibrate-copy) to "
+                         + os.path.relpath(os.path.join("profiles", "row_kernel_N64_V128000_traffic.json")) + " and exit")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain 256 MiB device copy 10 times (the reference kernel for scaling "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
@@ -103,6 +107,46 @@ def measured_traffic():
     if t.get("kernel_sha256") != kernel_digest():
         return None
     return t.get("traffic_bytes")
+
+
+def _counter_means(path, kernel_pred):
+    """Mean Counter_Value over the dispatches of the kernels kernel_pred
+    accepts in a rocprofv3 counter_collection.csv, and their count."""
+    import csv
+    vals = []
+    with open(path, newline="") as f:
+        for row in csv.DictReader(f):
+            if kernel_pred(row["Kernel_Name"]):
+                vals.append(float(row["Counter_Value"]))
+    if not vals:
+        raise SystemExit(f"{path}: no dispatch of the kernel")
+    return float(np.mean(vals)), len(vals)
+
+
+def traffic_summary(fetch_csv, write_csv, cfetch_csv, cwrite_csv):
+    """HBM bytes per launch of the row kernel: each counter (KiB per
+    dispatch) scaled by what the same counter reads for a plain copy of
+    COPY_BYTES (read COPY_BYTES, write COPY_BYTES)."""
+    import workloads
+    row_k = lambda name: "row_kernel" in name
+    copy_k = lambda name: "copyBuffer" in name  # the runtime's device-to-device copy kernel
+    fetch, n_f = _counter_means(fetch_csv, row_k)
+    write, n_w = _counter_means(write_csv, row_k)
+    cfetch, _ = _counter_means(cfetch_csv, copy_k)
+    cwrite, _ = _counter_means(cwrite_csv, copy_k)
+    f_scale = COPY_BYTES / 1024.0 / cfetch
+    w_scale = COPY_BYTES / 1024.0 / cwrite
+    traffic = int(round((fetch * f_scale + write * w_scale) * 1024.0))
+    out = {"kernel": "row_kernel<float, true>", "workload": "N=64 V=128000 fp32 full chain (bench.py default)",
+           "fetch_kib_per_launch": round(fetch, 1), "write_kib_per_launch": round(write, 1),
+           "copy_bytes": COPY_BYTES, "copy_fetch_kib": round(cfetch, 1), "copy_write_kib": round(cwrite, 1),
+           "fetch_factor": round(f_scale, 4), "write_factor": round(w_scale, 4), "traffic_bytes": traffic,
+           "algorithmic_bytes": workloads.config(4).algorithmic_bytes(), "launches_counted": min(n_f, n_w),
+           "kernel_sha256": kernel_digest()}
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(out, f, indent=1)
+        f.write("\n")
+    print(json.dumps(out))
 
 
 def calibrate_copy():
@@ -298,6 +342,9 @@ def main():
         sys.exit(2)
     if args.calibrate_copy:
         calibrate_copy()
+        return
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
         return
     import torch
     import decode_step_token_sampler_amd as dsts

@@ -266,8 +266,12 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out);
  * a negative status without launching if one is wrong.  Allocates nothing,
  * never synchronises the device and never reads device memory back; waits on
  * the host only when the 4-slot staging ring wraps onto a slot whose copy is
- * still in flight (batches of up to 96 rows pass their per-row records in
- * the kernel arguments and use no staging slot).  Outputs are valid when the stream reaches this point. */
+ * still in flight (batches of up to 72 rows pass their per-row records in
+ * the kernel arguments and use no staging slot).  The step is the row
+ * kernel, preceded by a history-count kernel when a row's history is longer
+ * than 4096 ids and followed by the raw-logprob kernel in the raw mode when a
+ * row's effective temperature is not 1.  Outputs are valid when the stream
+ * reaches this point. */
 sampler_status sampler_step(sampler_handle *h, const sampler_step_args *args, void *stream);
 
 /* Per-row parameters in device memory, for sampler_step_graph.  Each array
