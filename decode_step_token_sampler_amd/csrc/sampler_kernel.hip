@@ -414,6 +414,21 @@ DEV double exp_nonpos(const double *tab, double y) {
   return ldexp(tab[k & 63] * p, k >> 6);
 }
 
+// A summand exp(z - m) (z <= m, m finite) of a normaliser that only scales
+// outputs: t = (z - m) log2 e in fp64 (the difference of two fp32 values is
+// exact, the product's error is below 1e-13 absolute), split into an
+// integer k and a fraction f in [-1/2, 1/2]; 2^f by the hardware exp2 of f
+// rounded to fp32 (1 ulp, and 2^-25 ln 2 from the rounding of f); 2^k
+// exactly.  Relative error below 1.5e-7; -inf (and anything below 2^-1070)
+// gives 0.
+DEV double exp_term(float z, double m) {
+  const double t = ((double)z - m) * 1.4426950408889634;
+  if (!(t > -1070.0)) return 0.0;
+  const double k = rint(t);
+  const float e = __builtin_amdgcn_exp2f((float)(t - k));
+  return ldexp((double)e, (int)k);
+}
+
 // Penalties on one logit ([C] "解码一步里采样做什么", _apply_penalties):
 // repetition divides positive and multiplies non-positive logits, then
 // frequency subtracts f * count, then presence subtracts p; each operation
@@ -1755,7 +1770,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
                     if (near) atomicAdd(&wh[(int)lb], hist_entry(a));
                     if (deep) dsum += near ? 0.0f : a;
                   }
-                  if (exact) sx += exp_nonpos(sm.exp_tab, (double)zz - (double)mg);
+                  if (exact) sx += exp_term(zz, (double)mg);
                 }
                 if (deep) deep_a += (double)dsum;
               }
