@@ -265,7 +265,7 @@ def cpu_baseline(batches, budget_s, threads=None):
 
 
 PHASES = ("start", "row", "loaded", "max", "hist", "x2", "decided", "gathered", "x3", "thresholds", "select",
-          "token", "end", "gumbel", "released", "arrived")
+          "token", "end", "gumbel", "released", "arrived", "g_bound", "g_listed")
 
 
 ROW_INDEX_SLOT = 19
@@ -289,8 +289,9 @@ def row_class(b, r):
 
 def phase_by_class(stamps_runs, khz):
     """Per row class: the median over steps and workgroups of the time since
-    the kernel's first stamp at which the workgroups' rows reach selection
-    and their end (us).  stamps_runs: (stamps, batch) of each step."""
+    the kernel's first stamp at which the workgroups' rows pass each phase
+    (us), the largest end time, and the number of distinct rows seen.
+    stamps_runs: (stamps, batch) of each step."""
     acc = {}
     for st, b in stamps_runs:
         used = st[:, 0] != 0
@@ -301,14 +302,20 @@ def phase_by_class(stamps_runs, khz):
             r = int(st[blk, ROW_INDEX_SLOT]) - 1
             if r < 0:
                 continue
-            c = acc.setdefault(row_class(b, r), {"select": [], "end": [], "rows": set()})
+            c = acc.setdefault(row_class(b, r), {"rows": set(), "phases": {}})
             c["rows"].add(r)
-            for name, k in (("select", PHASES.index("select")), ("end", PHASES.index("end"))):
+            for k, name in enumerate(PHASES):
                 if st[blk, k]:
-                    c[name].append((float(st[blk, k]) - t0) * 1e3 / khz)
-    return {cls: {"rows": len(v["rows"]), "select_us": float(np.median(v["select"])) if v["select"] else None,
-                  "end_us": float(np.median(v["end"])) if v["end"] else None,
-                  "end_max_us": float(np.max(v["end"])) if v["end"] else None} for cls, v in sorted(acc.items())}
+                    c["phases"].setdefault(name, []).append((float(st[blk, k]) - t0) * 1e3 / khz)
+    out = {}
+    for cls, v in sorted(acc.items()):
+        ph = v["phases"]
+        out[cls] = {"rows": len(v["rows"]),
+                    "select_us": float(np.median(ph["select"])) if "select" in ph else None,
+                    "end_us": float(np.median(ph["end"])) if "end" in ph else None,
+                    "end_max_us": float(np.max(ph["end"])) if "end" in ph else None,
+                    "phases_median_us": {name: float(np.median(ph[name])) for name in PHASES if name in ph}}
+    return out
 
 
 def phase_timeline(stamps_runs, khz):

@@ -151,6 +151,9 @@ enum : int {
   kStampGumbel = 13,     // this workgroup's Gumbel-max winner is known (thread 0's wave)
   kStampReleased = 14,   // final exchange: this workgroup's record is stored
   kStampArrived = 15,    // final exchange: this workgroup has arrived
+  kStampGumbelBound = 16,   // Gumbel-max: the argmax's draw and the listing cut are known
+  kStampGumbelListed = 17,  // Gumbel-max: the candidate groups are listed
+  kStampGumbelListedCount = 18,  // not a time: groups thread 0's wave listed
   kStampRowIndex = 19,   // not a time: 1 + the index of the row the stamps describe
 };
 

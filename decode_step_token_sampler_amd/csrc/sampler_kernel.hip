@@ -2671,6 +2671,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       philox4x32_10((uint32_t)argmax_idx >> 2, P.stream, off0, off1, key0, key1, w4);
       bound = (float)(1.0 / exp1_f64(w4[argmax_idx & 3])) * 0.99999f;
       cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
+      PHASE_STAMP(kStampGumbelBound);
       const int its = (ln4 + 4 * NT - 1) / (4 * NT);
       constexpr int kStep = 8;  // groups read before any is tested
       for (int q0 = 0; q0 < its; q0 += kStep) {
@@ -2694,6 +2695,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
           }
         }
       }
+      PHASE_STAMP(kStampGumbelListed);
+      PHASE_RECORD(kStampGumbelListedCount, qt);
       for (; qh < qt;) gumbel_batch(min(qt - qh, 64u));
     };
 

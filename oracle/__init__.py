@@ -12,11 +12,12 @@ What each part follows (page titles; the C file names the sections):
       "What the flag switches")
   [C] "采样参数对解码开销的影响：temperature、top_p 与采样核路径"
 
-Parity unpinned: the frequency and presence terms of the penalty formula and
-the order of the three penalties (the pages name the three penalties and
-their defaults but print no formula); only their identity at the defaults,
-their locality and a hand-worked example are pinned.  The repetition term is
-pinned against the transformers library's repetition-penalty processor.
+Parity unpinned: the order of the three penalties (the pages name the three
+penalties and their defaults but print no formula).  The repetition term is
+pinned against the transformers library's repetition-penalty processor, the
+frequency and presence terms by invariants (count-independence of presence,
+linearity of frequency in the count, additivity), the whole by its identity
+at the defaults, its locality and a hand-worked example.
 """
 from __future__ import annotations
 

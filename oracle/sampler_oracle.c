@@ -44,9 +44,10 @@
  *
  * Parity pins: see tests/test_oracle_*.py.  The penalty formula is not
  * fixed by the pages: its repetition term is pinned against the transformers
- * library's repetition-penalty processor; the frequency and presence terms
- * and the order of the three are "parity unpinned" (only their identity at
- * the defaults, their locality and a hand-worked example are pinned).
+ * library's repetition-penalty processor, and the frequency and presence
+ * terms by invariants (presence lowers a seen token by a constant whatever
+ * its count, frequency lowers it linearly in the count, the two add).  The
+ * order of the three is a reading the pages leave open: "parity unpinned".
  */
 #include <float.h>
 #include <math.h>

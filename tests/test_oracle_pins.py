@@ -452,6 +452,41 @@ def test_penalty_hand_worked_example():
     np.testing.assert_allclose(o["logprobs"][0], scipy.special.log_softmax(z), rtol=1e-7)
 
 
+def _penalised_shift(x, tok, ref, counts, rep=1.0, freq=0.0, pres=0.0):
+    """Logit of token `tok` minus that of the untouched token `ref` after the
+    penalties, read from the oracle's logprobs at T = 1, with `tok` seen
+    `counts` times in the history."""
+    hist = np.full(max(counts, 1), tok, np.int32) if counts else np.zeros(1, np.int32)
+    o = run(x, temperature=[1.0], repetition_penalty=[rep], frequency_penalty=[freq], presence_penalty=[pres],
+            history_ids=hist, history_start=[0], history_len=[counts])
+    return float(o["logprobs"][0, tok]) - float(o["logprobs"][0, ref])
+
+
+def test_frequency_and_presence_invariants():
+    # The pages name the frequency and presence penalties and their defaults
+    # ([C] "哪些参数会额外打开一趟全词表计算") but print no formula; these
+    # invariants pin the terms: presence moves a seen token by a constant
+    # whatever its count, frequency moves it linearly in the count, both
+    # lower it, and the two add.  Dyadic values keep every step exact.
+    x = np.array([0.5, 1.0, -0.75, 0.25, 2.0, -1.5, 0.0, 0.125], np.float32)
+    tok, ref = 1, 0
+    base = _penalised_shift(x, tok, ref, 0, freq=0.125, pres=0.375)
+    assert base == pytest.approx(0.5, abs=1e-6)              # an unseen token does not move
+    pres = [_penalised_shift(x, tok, ref, c, pres=0.375) for c in (1, 2, 7)]
+    assert pres[0] == pytest.approx(0.5 - 0.375, abs=1e-6)   # lowered once ...
+    assert pres[1] == pres[0] and pres[2] == pres[0]         # ... whatever the count
+    freq = [_penalised_shift(x, tok, ref, c, freq=0.125) for c in (1, 2, 3, 4)]
+    steps = np.diff([0.5] + freq)
+    np.testing.assert_allclose(steps, -0.125, atol=1e-6)     # linear in the count, downwards
+    both = [_penalised_shift(x, tok, ref, c, freq=0.125, pres=0.375) for c in (1, 3)]
+    np.testing.assert_allclose(both, [0.5 - 0.375 - 0.125, 0.5 - 0.375 - 0.375], atol=1e-6)
+    # with a repetition penalty the frequency and presence terms act on the
+    # repetition-adjusted logit (the order of reading 4): a positive logit
+    # 1.0 with rep 2 becomes 0.5, then - 2 * 0.125 - 0.375
+    assert _penalised_shift(x, tok, ref, 2, rep=2.0, freq=0.125, pres=0.375) == pytest.approx(
+        (1.0 / 2.0 - 0.25 - 0.375) - 0.5, abs=1e-6)
+
+
 def test_repetition_penalty_matches_transformers_processor():
     # The repetition part of the reading is the CTRL rule as the transformers
     # library applies it (RepetitionPenaltyLogitsProcessor): each token seen
