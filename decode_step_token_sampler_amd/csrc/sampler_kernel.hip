@@ -1792,10 +1792,11 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       const double wdm = need_deep ? wg_sum_d(sm, deep_a) : 0.0;
       const double wsx = need_exact ? wg_sum_d(sm, sx) : 0.0;
       __syncthreads();
-      // this workgroup's record and histogram -> its exchange slot
+      // this workgroup's record and histogram -> its exchange slot (a row's
+      // only workgroup keeps them: the merge reads registers and LDS)
       const unsigned xp = xseq++ & 1u;
-      if (need_sel) atomic_st(&rc.my->whist[xp][tid], wh[tid]);
-      if (tid == 0) {
+      if (need_sel && G > 1) atomic_st(&rc.my->whist[xp][tid], wh[tid]);
+      if (tid == 0 && G > 1) {
         atomic_st(&rc.my->x1[xp][0], lkey);
         atomic_st(&rc.my->x1[xp][1], (unsigned long long)__float_as_uint(Ag));
         atomic_st(&rc.my->x1[xp][2], (unsigned long long)__double_as_longlong(wdm));
@@ -1813,7 +1814,21 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       constexpr int kPairs = kWinBins / 2;
       const int npairs = need_sel ? G * kPairs : 0;
       u32x4 hr[4];
-      {
+      if (G == 1) {
+        // the local histogram is still in LDS (region B), the record in
+        // registers
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int pk = min(tid + k * kBlock, max(npairs - 1, 0));
+          hr[k] = *reinterpret_cast<const u32x4 *>(&wh[2 * (pk % kPairs)]);
+        }
+        if (tid == 0) {
+          sm.gk[0] = lkey;
+          sm.ga[0] = Ag;
+          sm.gf[0] = wdm;
+          sm.gd[0] = wsx;
+        }
+      } else {
         const int g1 = tid < G ? tid : G - 1;
         u32x4 r0, r1;
         if (npairs > 0) {
@@ -2631,20 +2646,30 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         const int i0 = s0 + l;
         uint32_t w[4];
         philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
+        // the values of the group that may still beat the bound (bit c)
+        uint32_t surv = 0;
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           if (zv[c] >= tauf && (mf - zv[c] <= cut)) {
             // lower bound of w: (float)x rounds to nearest
             const float wl = (float)w[c] * 0x1.fffffcp-33f;
             const float qv = __builtin_amdgcn_exp2f((zv[c] - mf) * kLog2e);
-            if (wl * bound <= qv * kSlack) {
-              const double ge = (double)zv[c] - log(exp1_f64(w[c]));
-              if (ge > best_g || (ge == best_g && i0 + c < best_i)) {
-                best_g = ge;
-                best_i = i0 + c;
-                improved = true;
-              }
-            }
+            if (wl * bound <= qv * kSlack) surv |= 1u << c;
+          }
+        }
+        // their exact fp64 scores, one survivor per lane per round (in
+        // index order): the wave runs as many rounds as its busiest lane
+        // has survivors, not one per position that any lane needs
+        while (surv) {
+          const int c = __builtin_ctz(surv);
+          surv &= surv - 1u;
+          const float zc = c == 0 ? zv[0] : c == 1 ? zv[1] : c == 2 ? zv[2] : zv[3];
+          const uint32_t wc = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
+          const double ge = (double)zc - log(exp1_f64(wc));
+          if (ge > best_g || (ge == best_g && i0 + c < best_i)) {
+            best_g = ge;
+            best_i = i0 + c;
+            improved = true;
           }
         }
       }
