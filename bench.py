@@ -265,10 +265,12 @@ def cpu_baseline(batches, budget_s, threads=None):
 
 
 PHASES = ("start", "row", "loaded", "max", "hist", "x2", "decided", "gathered", "x3", "thresholds", "select",
-          "token", "end", "gumbel", "released", "arrived", "g_bound", "g_listed")
+          "token", "end", "gumbel", "released", "arrived", "g_bound", "g_listed", "listed_n", "row_index",
+          "g_batched", "g_rounds", "table")
+NOT_TIMES = ("listed_n", "row_index", "g_rounds")
 
 
-ROW_INDEX_SLOT = 19
+ROW_INDEX_SLOT = 19  # PHASES[19]
 
 
 def row_class(b, r):
@@ -305,8 +307,9 @@ def phase_by_class(stamps_runs, khz):
             c = acc.setdefault(row_class(b, r), {"rows": set(), "phases": {}})
             c["rows"].add(r)
             for k, name in enumerate(PHASES):
-                if st[blk, k]:
-                    c["phases"].setdefault(name, []).append((float(st[blk, k]) - t0) * 1e3 / khz)
+                if st[blk, k] and name != "row_index":
+                    v = float(st[blk, k]) if name in NOT_TIMES else (float(st[blk, k]) - t0) * 1e3 / khz
+                    c["phases"].setdefault(name, []).append(v)
     out = {}
     for cls, v in sorted(acc.items()):
         ph = v["phases"]
@@ -332,7 +335,7 @@ def phase_timeline(stamps_runs, khz):
         for k, name in enumerate(PHASES):
             col = st[used, k]
             col = col[col != 0]
-            if col.size == 0:
+            if col.size == 0 or name in NOT_TIMES:
                 continue
             us = (col.astype(np.float64) - float(t0)) * 1e3 / khz
             per[name]["median_us"].append(float(np.median(us)))

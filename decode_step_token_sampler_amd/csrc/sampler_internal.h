@@ -13,6 +13,10 @@ namespace dsts {
 constexpr int32_t kTopKAll = 1 << 30;
 // Largest number of workgroups that cooperate on one row.
 constexpr int kMaxG = 32;
+// The same for a launch whose rows exchange only in the final merge (no
+// merged max, thresholds or sums): that merge reads one record per lane of
+// one wave, and no per-workgroup LDS array is involved.
+constexpr int kMaxLightG = 64;
 // Largest top-logprob list per row.
 constexpr int kMaxTopLogprobs = 32;
 // Largest history the row kernel counts by itself.  Its counts live in an
@@ -133,7 +137,7 @@ enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINI
 // record holds the real-time clock at the end of phase k of its first row
 // (0 where the row skipped the phase).
 constexpr int kStampBlocks = 2048;
-constexpr int kStampSlots = 20;
+constexpr int kStampSlots = 24;
 enum : int {
   kStampStart = 0,       // the kernel starts
   kStampRow = 1,         // the row's record is read
@@ -155,6 +159,9 @@ enum : int {
   kStampGumbelListed = 17,  // Gumbel-max: the candidate groups are listed
   kStampGumbelListedCount = 18,  // not a time: groups thread 0's wave listed
   kStampRowIndex = 19,   // not a time: 1 + the index of the row the stamps describe
+  kStampGumbelBatched = 20,  // Gumbel-max: thread 0's wave has scored its listed groups
+  kStampGumbelRounds = 21,   // not a time: fp64 scoring rounds of thread 0's wave
+  kStampTable = 22,          // the kernel's fp64 exp table is built (before the first row)
 };
 
 // Per-row parameters in device memory (one entry per row, or null for the

@@ -1330,6 +1330,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   PHASE_STAMP(kStampStart);
   for (int j = tidx(); j < 64; j += kBlock) sm.exp_tab[j] = exp2((double)j * (1.0 / 64.0));
   __syncthreads();
+  PHASE_STAMP(kStampTable);
 
   // Record ri describes batch row rows[ri].row: the host puts the rows it
   // expects to take longest on the groups whose workgroups are dispatched
@@ -2638,8 +2639,14 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // waves: Philox and the filter.
     uint16_t *ring = reinterpret_cast<uint16_t *>(regB);  // this wave's list (set by the pass)
     uint32_t qh = 0, qt = 0;  // wave-uniform head and tail
+#ifdef DSTS_PHASE_STAMPS
+    uint32_t g_rounds = 0;  // fp64 scoring rounds of this wave (stamps builds)
+#endif
     auto gumbel_batch = [&](uint32_t cnt) __attribute__((always_inline)) {  // one queued group per lane, cnt <= 64
       bool improved = false;
+#ifdef DSTS_PHASE_STAMPS
+      uint32_t surv_n = 0;
+#endif
       if ((uint32_t)lane < cnt) {
         const int l = 4 * (int)ring[qh + lane];
         const f32x4 zv = *reinterpret_cast<const f32x4 *>(zs + l);
@@ -2660,6 +2667,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         // their exact fp64 scores, one survivor per lane per round (in
         // index order): the wave runs as many rounds as its busiest lane
         // has survivors, not one per position that any lane needs
+#ifdef DSTS_PHASE_STAMPS
+        surv_n = (uint32_t)__popc(surv);
+#endif
         while (surv) {
           const int c = __builtin_ctz(surv);
           surv &= surv - 1u;
@@ -2674,6 +2684,9 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         }
       }
       qh += cnt;
+#ifdef DSTS_PHASE_STAMPS
+      g_rounds += lane63_u32(wave_scanmax_u32(surv_n));  // the wave's scoring rounds in this batch
+#endif
       if (__ballot(improved)) {
         float mb = improved ? (float)exp(best_g - m) * 0.99999f : 0.0f;
         mb = wave_max_nonneg_f(mb);
@@ -2723,6 +2736,8 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       PHASE_STAMP(kStampGumbelListed);
       PHASE_RECORD(kStampGumbelListedCount, qt);
       for (; qh < qt;) gumbel_batch(min(qt - qh, 64u));
+      PHASE_STAMP(kStampGumbelBatched);
+      PHASE_RECORD(kStampGumbelRounds, g_rounds);
     };
 
     // ---- 6. final exchange: the last workgroup to arrive writes the row.

@@ -35,9 +35,9 @@ constexpr int kRing = 4;
 constexpr double kGreedyEps = 1e-6;
 // Values per thread of a launch whose rows exchange only at the end (see
 // launch_is_light).  Measured on MI355X, batch-1 Gumbel at V=151,936 (ids
-// only), kernel time: 16 values per thread (19 workgroups) 18.0 us, 8 (32
-// workgroups, the cap) 16.8 us, 4 (also 32) 16.7 us.
-constexpr int kLightValuesPerThread = 8;
+// only), kernel time: 16 values per thread (19 workgroups) 18.0 us, 8 (38
+// workgroups) 16.1 us, 4 (64, the cap for such launches) 15.0 us.
+constexpr int kLightValuesPerThread = 4;
 // [B] "What the flag switches": requests without a seed use 42.
 constexpr uint64_t kDeterministicSeed = 42;
 
@@ -70,8 +70,8 @@ struct Workspace {
   uint32_t epoch = 0;              // epoch of the last host-path launch (1 .. 2^31 - 1)
   // counted histories longer than kMaxHistPerRow (handles planned for them)
   uint32_t *hist_list = nullptr;  // [max_rows * hist_list_row] entries
-  int32_t *hist_list_n = nullptr; // [max_rows * kMaxG]
-  int64_t hist_list_row = 0;      // entries per row: min(kMaxG max_history, max_vocab + kMaxSlice)
+  int32_t *hist_list_n = nullptr; // [max_rows * kMaxLightG]
+  int64_t hist_list_row = 0;      // entries per row: min(kMaxLightG max_history, max_vocab + kMaxSlice)
   // limits the workspace was planned for
   int32_t max_history_per_row = 0, max_bias_per_row = 0, max_top_logprobs = 0, max_vocab = 0;
 };
@@ -398,7 +398,8 @@ sampler_status plan_groups(const Workspace &ws, bool det, bool light, int n, int
     const int vpt = light ? kLightValuesPerThread : 32;
     const int by_work = (V + vpt * kBlock - 1) / (vpt * kBlock);
     G = fill < by_work ? fill : by_work;
-    if (G > kMaxG) G = kMaxG;
+    const int gcap = light ? kMaxLightG : kMaxG;
+    if (G > gcap) G = gcap;
     if (G > ws.resident) G = ws.resident;
     if (G < g_min) G = g_min;
   }
@@ -805,14 +806,15 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     if (cfg->max_history_per_row > kMaxHistPerRow) {
       // list (row, slice) of a launch of G slices of `slice` values holds at
       // most min(max_history, slice) entries, and G min(max_history, slice)
-      // <= min(kMaxG max_history, V + slice)
-      const int64_t by_hist = (int64_t)kMaxG * cfg->max_history_per_row;
+      // <= min(kMaxLightG max_history, V + slice) (G never exceeds kMaxLightG)
+      const int64_t by_hist = (int64_t)kMaxLightG * cfg->max_history_per_row;
       const int64_t by_vocab = (int64_t)cfg->max_vocab + kMaxSlice;
       ws.hist_list_row = by_hist < by_vocab ? by_hist : by_vocab;
       if ((e = hipMalloc((void **)&ws.hist_list, sizeof(uint32_t) * (size_t)ws.hist_list_row * cfg->max_rows)) !=
           hipSuccess)
         goto fail;
-      if ((e = hipMalloc((void **)&ws.hist_list_n, sizeof(int32_t) * (size_t)kMaxG * cfg->max_rows)) != hipSuccess)
+      if ((e = hipMalloc((void **)&ws.hist_list_n, sizeof(int32_t) * (size_t)kMaxLightG * cfg->max_rows)) !=
+          hipSuccess)
         goto fail;
     }
     for (int s = 0; s < kRing; ++s)

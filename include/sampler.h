@@ -107,7 +107,7 @@ typedef struct sampler_config {
   int32_t max_history_per_row; /* largest history_len of one row (0..131,071).  Up to
                                   4096 the row kernel counts a history itself; a
                                   handle planned for more holds a count list of
-                                  4 * max_rows * min(32 * max_history_per_row,
+                                  4 * max_rows * min(64 * max_history_per_row,
                                   max_vocab + 32768) bytes, which a short kernel
                                   fills ahead of the row kernel in steps where a
                                   row's history is longer than 4096 */
