@@ -137,7 +137,7 @@ enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINI
 // record holds the real-time clock at the end of phase k of its first row
 // (0 where the row skipped the phase).
 constexpr int kStampBlocks = 2048;
-constexpr int kStampSlots = 24;
+constexpr int kStampSlots = 28;
 enum : int {
   kStampStart = 0,       // the kernel starts
   kStampRow = 1,         // the row's record is read
@@ -162,6 +162,9 @@ enum : int {
   kStampGumbelBatched = 20,  // Gumbel-max: thread 0's wave has scored its listed groups
   kStampGumbelRounds = 21,   // not a time: fp64 scoring rounds of thread 0's wave
   kStampTable = 22,          // the kernel's fp64 exp table is built (before the first row)
+  kStampX3Read = 23,         // exchange 3: wave 0 has read and placed the candidates
+  kStampX3Ranked = 24,       // exchange 3: the candidates are sorted
+  kStampX3Decided = 25,      // exchange 3: wave 0 has decided (short lists)
 };
 
 // Per-row parameters in device memory (one entry per row, or null for the

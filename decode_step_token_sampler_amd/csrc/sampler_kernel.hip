@@ -2232,6 +2232,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         }
         if (lane == 0) sm.bu[13] = fast ? 1u : 0u;
       }
+      PHASE_STAMP(kStampX3Read);
       __syncthreads();
       // rank of each key: the number of larger keys (keys are distinct:
       // each holds its index), so the list is in (value desc, index asc)
@@ -2266,6 +2267,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
         const int n = (int)sm.goff[G];
         rank_place(n, reinterpret_cast<unsigned long long *>(sq));
         __syncthreads();
+        PHASE_STAMP(kStampX3Ranked);
         if (wave == 0) {
           E3In in;
           in.top_k = P.top_k;
@@ -2296,6 +2298,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
             sm.bu[27] = o.tau;
             sm.bd[5] = o.lnS;
           }
+          PHASE_STAMP(kStampX3Decided);
         }
         __syncthreads();
         general = sm.bu[26] != 0u;
