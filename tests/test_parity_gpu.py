@@ -710,3 +710,22 @@ def test_long_histories_on_device_params(sampler_long):
         np.testing.assert_array_equal(g[k], h[k], err_msg=k)
     r = compare(g, run_oracle(b))
     assert r.ok(), r
+
+
+# ------------------------------------------------------------ light launches
+def test_light_launch_with_penalties_processors_and_long_histories(sampler_long):
+    """A launch whose rows only meet in the final merge (ids only; rows greedy
+    or keeping every token) spreads each row over up to 64 workgroups: with
+    penalties over short and long histories, logit_bias, stop lists and a
+    grammar mask, its tokens equal the oracle's."""
+    b = workloads.random_small(85, 6, 131_000, "bf16", penalties=True, history_len=6000, mix="plain")
+    b.temperature[1] = 0.0                     # a greedy row
+    b.history_len[2] = 6000                    # longer than the row kernel's own hash
+    b.want_probs = b.want_logprobs = False
+    b.top_logprobs = 0
+    p = workloads.processors(85, b)
+    g = run_gpu(sampler_long, b, **_processors_on_device(p))
+    o = run_oracle(b, **p.kwargs())
+    r = compare(g, o)
+    print(b.name, r)
+    assert r.ok(), r
