@@ -266,7 +266,8 @@ def cpu_baseline(batches, budget_s, threads=None):
 
 PHASES = ("start", "row", "loaded", "max", "hist", "x2", "decided", "gathered", "x3", "thresholds", "select",
           "token", "end", "gumbel", "released", "arrived", "g_bound", "g_listed", "listed_n", "row_index",
-          "g_batched", "g_rounds", "table", "x3_read", "x3_ranked", "x3_decided")
+          "g_batched", "g_rounds", "table", "x3_read", "x3_ranked", "x3_decided",
+          "half", "hashed", "transformed")
 NOT_TIMES = ("listed_n", "row_index", "g_rounds")
 
 

@@ -137,7 +137,7 @@ enum : int { PATH_GREEDY = 0, PATH_GUMBEL = 1, PATH_FILTERED = 2, PATH_DETERMINI
 // record holds the real-time clock at the end of phase k of its first row
 // (0 where the row skipped the phase).
 constexpr int kStampBlocks = 2048;
-constexpr int kStampSlots = 28;
+constexpr int kStampSlots = 32;
 enum : int {
   kStampStart = 0,       // the kernel starts
   kStampRow = 1,         // the row's record is read
@@ -165,6 +165,9 @@ enum : int {
   kStampX3Read = 23,         // exchange 3: wave 0 has read and placed the candidates
   kStampX3Ranked = 24,       // exchange 3: the candidates are sorted
   kStampX3Decided = 25,      // exchange 3: wave 0 has decided (short lists)
+  kStampHalf = 26,           // load phase: the first half of the slice is transformed (vector loads)
+  kStampHashed = 27,         // load phase: the history and bias hashes are built
+  kStampTransformed = 28,    // load phase: the whole slice is transformed
 };
 
 // Per-row parameters in device memory (one entry per row, or null for the

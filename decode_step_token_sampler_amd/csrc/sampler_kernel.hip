@@ -1578,9 +1578,12 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
       if (spec)
         for (int t = tid; t < (int)bslots; t += kBlock) bhash[t] = 0xFFFFFFFFull;  // free, bias +0
       transform(0, kBatch / 2);
+      PHASE_STAMP(kStampHalf);
       build_hash();
+      PHASE_STAMP(kStampHashed);
       transform(kBatch / 2, kBatch);
       transform_slow();
+      PHASE_STAMP(kStampTransformed);
     } else {
 #pragma unroll
       for (int b = 0; b < kBatch; ++b)
