@@ -729,3 +729,27 @@ def test_light_launch_with_penalties_processors_and_long_histories(sampler_long)
     r = compare(g, o)
     print(b.name, r)
     assert r.ok(), r
+
+
+# ------------------------------------------------------------ extreme parameters
+@pytest.mark.parametrize("V,dtype", [(100_003, "f32"), (4097, "bf16")])
+def test_extreme_parameters(sampler, V, dtype):
+    """Temperatures at the greedy boundary and far above 1, top-p down to
+    1e-6, min-p near 1, top-k of V - 1 and 1, logits of large and tiny
+    magnitude: every row against the oracle."""
+    rng = np.random.default_rng(V)
+    n = 12
+    x = (rng.standard_normal((n, V)) * 3.0).astype(np.float32)
+    x[6] *= 3000.0                                  # large magnitudes
+    x[7] *= 1e-30                                   # tiny magnitudes (near-uniform row)
+    x[8, rng.integers(0, V, 40)] = 25.0             # a plateau of equal maxima
+    T = np.array([1e-6, 1e-5, 50.0, 1e4, 1.0, 1.0, 0.7, 1.0, 1.0, 0.3, 2.0, 1.0], np.float32)
+    top_k = np.array([-1, -1, -1, -1, V - 1, 1, 20, -1, 5, -1, 3, -1], np.int32)
+    top_p = np.array([1, 0.5, 0.9, 1, 1e-6, 1, 0.99, 0.5, 1, 1e-3, 0.7, 1], np.float32)
+    min_p = np.array([0, 0, 0.5, 0.999, 0, 0, 0, 0.01, 0, 0.9, 0, 0.3], np.float32)
+    L = workloads.f32_to_bf16_bits(x) if dtype == "bf16" else x
+    b = workloads.Batch("extreme parameters V=%d %s" % (V, dtype), dtype, L, temperature=T, top_k=top_k,
+                        top_p=top_p, min_p=min_p, seed=123, offset=7, want_probs=True, want_logprobs=True,
+                        top_logprobs=8)
+    g, o, r = check(b, sampler)
+    assert np.all(g["row_status"] == 0)
