@@ -10,28 +10,39 @@
 // G workgroups of 512 threads (a "row group") own one slice each and keep
 // their slice's processed logits z = penalised(x) / T in LDS, so the logits
 // are read from HBM once.  The G workgroups of a group cooperate through
-// per-group barrier words and exchange slots in device memory (the launch
-// is cooperative, so all workgroups are resident).  A group walks rows
-// group, group + n_groups, ...
+// per-group barrier words and exchange slots in device memory; the grid
+// never exceeds the workgroups the device holds at once, and every wait is
+// bounded.  A group walks rows group, group + n_groups, ...
 //
-// Per row:
-//   1. load, NaN -> -inf, z = x / T as the loads land; penalties from an LDS
-//      hash of history counts, applied once per distinct id
-//   2. exchange 1: row max and first argmax; min-p's boundary key
-//   3. exchange 2: a histogram of d = max - z in 1/32-nat bins over 16 nats
-//      (counts, 2^-44 fixed-point masses; deeper masses summed per
-//      workgroup), merged by the last workgroup to arrive, which picks in
-//      parallel the bins holding each threshold
-//   4. exchange 3: the values of those bins are gathered, sorted by the last
-//      workgroup to arrive, which fixes top-k, top-p, the kept-set sum and
-//      the top logprobs exactly (rows whose thresholds fall outside the
-//      window take the general path: a radix select with one exchange per
-//      8-bit digit)
-//   5. emit probs / logprobs of the kept set; Gumbel-max with an in-kernel
-//      Philox draw, a linear-domain bound that skips elements which cannot
-//      win, and an fp64 score for every element that still can
-//   6. the last workgroup to arrive merges the Gumbel winners and writes
-//      the token and status
+// Per row (row_kernel):
+//   1. load, NaN -> -inf, z = x / T as the loads land; logits processors and
+//      penalties from LDS hashes of the bias/stop entries and of the history
+//      counts (or from a counted list, for histories longer than the hash
+//      holds), applied once per distinct id
+//   2. the slice's max and first argmax; a histogram of the values on an
+//      absolute grid of 1/32-nat bins over a 16-nat window below the slice
+//      max (counts, 2^-31 fixed-point masses; deeper masses summed), or the
+//      exact sum where every value is kept
+//   3. exchange 2: every workgroup of the row merges the records and
+//      histograms alike: the row max, status and argmax, min-p's boundary,
+//      and in parallel the bins holding each threshold
+//   4. exchange 3: the values of those bins are gathered, and every
+//      workgroup sorts the merged list alike and fixes top-k, top-p, the
+//      kept-set sum and the top logprobs exactly (rows whose thresholds fall
+//      outside the window take the general path: a radix select with one
+//      exchange per 8-bit digit)
+//   5. Gumbel-max over the kept set with an in-kernel Philox draw, a
+//      linear-domain bound that skips elements which cannot win, and an
+//      fp64 score for every element that still can (or the seeded inverse
+//      CDF); probs / logprobs of the kept set are written meanwhile
+//   6. final exchange: the last workgroup to arrive merges the G winners
+//      across one wave and writes the token and status
+// Rows that need no merged max (ids only, no truncation) skip steps 2-4;
+// a row held by one workgroup exchanges through registers and LDS only.
+//
+// Other kernels: rows_kernel (per-row parameters from device arrays),
+// hist_list_kernel (counts of long histories, ahead of the row kernel) and
+// raw_lp_kernel (the raw logprob mode at T != 1, after it).
 #include <float.h>
 #include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
@@ -1730,10 +1741,10 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     int r0hi = -1, r1lo = 1, r1hi = 0, rklo = 1, rkhi = 0, bm = -1;
     if (need_x) {
       // ---- 3. window histogram of this slice on the absolute bin grid,
-      // anchored at its own max, masses relative to its own max; the exact
-      // fp64 sum when every token is kept.  Exchange 2: the last workgroup
-      // to arrive finds the row max, shifts each histogram by whole bins,
-      // rescales its masses and decides in parallel.
+      // anchored at its own max, masses relative to its own max; the fp64
+      // sum when every token is kept.  Exchange 2: every workgroup of the
+      // row finds the row max, shifts each histogram by whole bins,
+      // rescales its masses and decides in parallel, alike.
       const bool finite_g = mg > -INFINITY && mg < INFINITY;
       const float Ag = finite_g ? abin(mg, wsc) : 0.0f;
       if (need_sel) {
@@ -2044,7 +2055,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     const float mf = (float)m;
 
     // ---- 4. exact thresholds from the gathered candidates (exchange 3,
-    // sorted and decided by the last workgroup to arrive)
+    // sorted and decided by every workgroup of the row alike)
     if (need_sel && !general) {
       // compact this slice's candidates into per-wave LDS staging (ballot
       // order: deterministic), then copy them to this workgroup's slot
