@@ -35,6 +35,8 @@ FLAG_COOPERATIVE_LAUNCH = 1 << 2
 FLAG_INVERSE_CDF = 1 << 3
 FLAG_FORCE_PATH_GREEDY = 1 << 4
 FLAG_FORCE_PATH_GUMBEL = 1 << 5
+FLAG_FORCE_STREAM = 1 << 6
+FLAG_NO_STREAM = 1 << 7
 
 # symbols the header declares
 EXPORTS = ("sampler_create", "sampler_step", "sampler_step_graph", "sampler_select_path", "sampler_validate",
@@ -104,6 +106,7 @@ class StepArgs(ctypes.Structure):
         ("min_tokens", ctypes.c_void_p),
         ("output_len", ctypes.c_void_p),
         ("logprob_mode", ctypes.c_int32),
+        ("kernel_out", ctypes.c_void_p),
     ]
 
 
@@ -369,8 +372,10 @@ def _prepare_step(logits, *, vocab: Optional[int] = None, temperature=None, top_
     a.row_status = o["row_status"].data_ptr() if "row_status" in o else None
     path = ctypes.c_int32(-1)
     a.path_out = ctypes.addressof(path)
+    kern = ctypes.c_int32(0)
+    a.kernel_out = ctypes.addressof(kern)
     s = torch.cuda.current_stream(dev).cuda_stream if stream is None else int(stream)
-    return a, o, path, (m, path), s
+    return a, o, path, (m, path, kern), s
 
 
 
@@ -395,7 +400,8 @@ class Sampler:
     def __init__(self, max_rows: int, max_vocab: int, *, max_history_per_row: int = 4096,
                  max_top_logprobs: int = 32, device: int = 0, deterministic: bool = False,
                  force_filtered: bool = False, cooperative_launch: bool = False, max_bias_per_row: int = 0,
-                 inverse_cdf: bool = False, wait_spin_limit: int = 0, force_path: Optional[str] = None):
+                 inverse_cdf: bool = False, wait_spin_limit: int = 0, force_path: Optional[str] = None,
+                 stream_rows: Optional[str] = None):
         L = load_library()
         self._L = L
         cfg = Config(max_rows=max_rows, max_vocab=max_vocab, max_history_per_row=max_history_per_row,
@@ -405,7 +411,8 @@ class Sampler:
                            | (FLAG_COOPERATIVE_LAUNCH if cooperative_launch else 0)
                            | (FLAG_INVERSE_CDF if inverse_cdf else 0)
                            | {None: 0, "greedy": FLAG_FORCE_PATH_GREEDY, "gumbel": FLAG_FORCE_PATH_GUMBEL,
-                              "filtered": FLAG_FORCE_FILTERED}[force_path])
+                              "filtered": FLAG_FORCE_FILTERED}[force_path]
+                           | {None: 0, "force": FLAG_FORCE_STREAM, "off": FLAG_NO_STREAM}[stream_rows])
         self.config = cfg
         h = ctypes.c_void_p()
         st = L.sampler_create(ctypes.byref(cfg), ctypes.byref(h))
@@ -470,6 +477,7 @@ class Sampler:
         if st != SAMPLER_OK:
             raise SamplerError(st, self.last_error())
         o["path"] = PATH_NAMES[path.value]
+        o["kernel"] = "stream" if keep[2].value == 1 else "row"
         del keep
         return o
 

@@ -36,6 +36,11 @@ constexpr int32_t kMaxHistLong = (1 << 17) - 1;
 constexpr int kMaxBiasPerRow = 512;
 // Largest vocabulary (masses are summed as 2^-44 fixed point in 64 bits).
 constexpr int32_t kMaxVocab = 1 << 20;
+// The streaming kernel packs a token and a count into one hash word (19 + 13
+// bits), so it takes vocabularies up to 2^19; its bitmap of the tokens that
+// have history holds one bit per token, in whole 16-byte units.
+constexpr int32_t kStreamMaxVocab = 1 << 19;
+__host__ __device__ inline int stream_bitmap_words(int vocab) { return (((vocab + 31) / 32) + 3) & ~3; }
 
 // Workgroup shape of the row kernel: 512 threads (8 wave64s; LDS allows one
 // workgroup per CU, so each thread may use 256 VGPRs).  Each
@@ -168,6 +173,9 @@ enum : int {
   kStampHalf = 26,           // load phase: the first half of the slice is transformed (vector loads)
   kStampHashed = 27,         // load phase: the history and bias hashes are built
   kStampTransformed = 28,    // load phase: the whole slice is transformed
+  kStampStreamStart = 29,    // the streaming kernel starts (its other stamps reuse the row kernel's
+                             // slots: row read 1, history hashed 27, pass A 3, pass B 4, ranges 6,
+                             // pass C 7, list sorted 24, decisions 9, end 12, row index 19)
 };
 
 // Per-row parameters in device memory (one entry per row, or null for the
@@ -204,7 +212,8 @@ struct KernelParams {
   int32_t n_groups;   // row groups (rows are strided over groups)
   int32_t slice;      // elements per workgroup slice (multiple of 4)
   int32_t hash_slots; // LDS hash slots (power of two) when penalties are on
-  int32_t vec_ok;     // bit 0: logits rows aligned for vector loads; bit 1: outputs for vector stores
+  int32_t vec_ok;     // bit 0: logits rows aligned for vector loads of four values; bit 1: outputs for
+                      // vector stores; bit 2: logits rows aligned for 16-byte loads
   int32_t path;
   GroupSync *sync;    // [n_groups]
   WgSlots *slots;     // [n_groups * G]
@@ -235,6 +244,14 @@ struct KernelParams {
   uint32_t *hist_list;
   int32_t *hist_list_n;
   int64_t hist_list_cap;
+  // rows the streaming kernel leaves to the row kernel: their records and
+  // a word epoch << 32 | count (arrivals of the streaming kernel's epoch)
+  RowParam *defer_rows;
+  unsigned long long *defer_word;
+  // the row kernel launched after it reads its row count from that word
+  // (count of epoch n_rows_epoch, else 0) instead of n_rows
+  const unsigned long long *n_rows_word;
+  uint32_t n_rows_epoch;
 };
 
 // Batches of up to kArgRows rows carry their per-row records in the kernel
@@ -269,6 +286,15 @@ size_t hist_list_lds_bytes(int slice);
 // ev0 / ev1 (or null): an event pair that brackets the kernel's execution.
 hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool cooperative, hipStream_t stream,
                        hipEvent_t ev0, hipEvent_t ev1);
+// The streaming kernel (batches of many rows that want only tokens and top
+// logprobs): one workgroup per row, `grid` workgroups walking the rows; rows
+// it cannot settle go to kp.defer_rows for a row-kernel launch after it.
+hipError_t launch_stream(const KernelArgs &ka, int dtype, bool penalties, int grid, hipStream_t stream, hipEvent_t ev0,
+                         hipEvent_t ev1);
+// Its dynamic LDS bytes for a vocabulary, and the workgroups of it that fit on
+// the device at once.
+size_t stream_lds_bytes(int hash_slots, bool penalties, int vocab);
+hipError_t stream_resident(int device, size_t lds_bytes, int *out);
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);

@@ -1319,6 +1319,12 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   rc.gc.spin_limit = kp.spin_limit ? kp.spin_limit : kSpinLimit;
   rc.gc.G = G;
   if (gid == 0 && G > 1 && tidx() == 0) claim_words(rc.gc.s, epoch);
+  // after the streaming kernel: the rows it left, counted in its epoch
+  int n_rows = kp.n_rows;
+  if (kp.n_rows_word) {
+    const unsigned long long w = atomic_ld(kp.n_rows_word);
+    n_rows = (uint32_t)(w >> 32) == kp.n_rows_epoch ? (int)(uint32_t)w : 0;
+  }
   rc.my = kp.slots + (size_t)group * G + gid;
   rc.peers = kp.slots + (size_t)group * G;
   rc.xseq = &xseq;
@@ -1346,7 +1352,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
   // Record ri describes batch row rows[ri].row: the host puts the rows it
   // expects to take longest on the groups whose workgroups are dispatched
   // first.
-  for (int ri = group; ri < kp.n_rows; ri += kp.n_groups, ++it) {
+  for (int ri = group; ri < n_rows; ri += kp.n_groups, ++it) {
     // the slice bounds, opaque per row: keeps per-element offsets and
     // compares from being hoisted out of the row loop (they would stay
     // live across it)
@@ -2051,7 +2057,7 @@ __global__ __launch_bounds__(kBlock) void row_kernel(KernelArgs ka) {
     // record of this row, two rows on) before this row's last arrival has
     // read the records.
     PHASE_STAMP(kStampDecided);
-    if (!need_x && kp.n_rows > kp.n_groups) row_barrier(sm, rc);
+    if (!need_x && n_rows > kp.n_groups) row_barrier(sm, rc);
     const float mf = (float)m;
 
     // ---- 4. exact thresholds from the gathered candidates (exchange 3,
@@ -3216,6 +3222,917 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
   }
 }
 
+// ---------------------------------------------------------------- streaming rows
+// Batches of many rows that want only tokens and top logprobs (no probs or
+// logprobs), [C] "best_of 与 n 的放大": forks multiply the rows of a step.
+// The row kernel holds a row's slices in LDS, so such a batch walks each
+// row group through many rows one after the other.  Here one workgroup
+// owns a whole row (two workgroups per CU) and reads it from memory in up
+// to three passes, recomputing z = penalised(x) / T each time, so every row
+// of the batch is in flight at once:
+//   A. the row max and its first index;
+//   B. (rows with thresholds or a top-logprob list) the window histogram of
+//      the row kernel -- absolute bins of 1/32 nat, counts and approximate
+//      masses -- which places each threshold in a range of values;
+//   C. values in those ranges are gathered into LDS; values above them
+//      (certainly kept) are counted, their masses summed exactly and their
+//      Gumbel scores taken on the way (Philox, the linear-domain bound,
+//      fp64 scores).
+// The gathered list is then sorted and every decision taken exactly on it:
+// the k-th value and its tie group, the top-p crossing on exact fp64
+// cumulative masses, min-p's boundary key, tau, the kept-set sum, the top
+// logprobs and the Gumbel scores of the kept values in the list.  A row
+// whose thresholds lie outside the window, whose ranges hold more than
+// kSCap values, or whose exact decision falls outside the ranges the
+// histogram chose is not written: its record goes to a list that the row
+// kernel, launched after this one, samples in full.
+constexpr int kSCap = 1024;       // values gathered per row
+constexpr int kSLoads = 4;        // 16-byte chunks each thread loads per step (one more step in flight)
+static_assert(kSCap % kBlock == 0, "gathered values per thread");
+
+// Window histogram entry of the streaming kernel: a count in bits 44.. (a
+// row of up to 2^19 values fits) and the mass exp(z - max) in 2^-24 units
+// below (a bin of 2^19 values at most 2^43).  These masses only place the
+// top-p crossing in a range of bins; the decision itself is exact.
+DEV unsigned long long hist_entry_s(float a) {
+  return (1ull << 44) | (unsigned long long)(uint32_t)__builtin_rintf(a * 16777216.0f);
+}
+
+// A token's history count from the row's hash (token << 13 | count), or 0.
+DEV uint32_t hist_count(const uint32_t *hash, uint32_t slots, uint32_t tok) {
+  uint32_t sl = hash_slot(tok, slots);
+  while (true) {
+    const uint32_t e = hash[sl];
+    if (e == kEmpty) return 0u;
+    if ((e >> 13) == tok) return e & 0x1FFFu;
+    sl = (sl + 1u) & (slots - 1u);
+  }
+}
+
+// A 16-byte chunk of a row (16-byte aligned): kGroups groups of four
+// values (one of fp32, two of bf16).  Ordinary loads: the passes read a row
+// again soon after, so it should stay in the caches.
+template <typename TIn>
+struct Chunk16;
+template <>
+struct Chunk16<float> {
+  static constexpr int kGroups = 1;
+  static DEV u32x4 load(const void *base, int64_t off) {
+    return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const float *>(base) + off);
+  }
+  static DEV u32x4 load_scalar(const void *base, int64_t rbase, int i0, int V) {
+    const float *p = reinterpret_cast<const float *>(base) + rbase;
+    u32x4 r;
+    r.x = __float_as_uint(p[min(i0, V - 1)]);
+    r.y = __float_as_uint(p[min(i0 + 1, V - 1)]);
+    r.z = __float_as_uint(p[min(i0 + 2, V - 1)]);
+    r.w = __float_as_uint(p[min(i0 + 3, V - 1)]);
+    return r;
+  }
+  static DEV void unpack(const u32x4 &t, int j, float v[4]) {
+    (void)j;
+    v[0] = __uint_as_float(t.x);
+    v[1] = __uint_as_float(t.y);
+    v[2] = __uint_as_float(t.z);
+    v[3] = __uint_as_float(t.w);
+  }
+};
+template <>
+struct Chunk16<uint16_t> {
+  static constexpr int kGroups = 2;
+  static DEV u32x4 load(const void *base, int64_t off) {
+    return *reinterpret_cast<const u32x4 *>(reinterpret_cast<const uint16_t *>(base) + off);
+  }
+  static DEV u32x4 load_scalar(const void *base, int64_t rbase, int i0, int V) {
+    const uint16_t *p = reinterpret_cast<const uint16_t *>(base) + rbase;
+    uint32_t w[4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      w[k] = (uint32_t)p[min(i0 + 2 * k, V - 1)] | ((uint32_t)p[min(i0 + 2 * k + 1, V - 1)] << 16);
+    return u32x4{w[0], w[1], w[2], w[3]};
+  }
+  static DEV void unpack(const u32x4 &t, int j, float v[4]) {
+    const uint32_t a = j == 0 ? t.x : t.z, b = j == 0 ? t.y : t.w;
+    v[0] = __uint_as_float(a << 16);
+    v[1] = __uint_as_float(a & 0xFFFF0000u);
+    v[2] = __uint_as_float(b << 16);
+    v[3] = __uint_as_float(b & 0xFFFF0000u);
+  }
+};
+// One value (rows not aligned for vector loads).
+DEV float load1_cached(const float *base, int64_t off) { return base[off]; }
+DEV float load1_cached(const uint16_t *base, int64_t off) { return __uint_as_float((uint32_t)base[off] << 16); }
+
+template <typename TIn, bool PEN>
+__global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
+  const KernelParams &kp = ka.kp;
+  extern __shared__ __align__(16) unsigned char lds_raw[];
+  SmemBase &sm = *reinterpret_cast<SmemBase *>(lds_raw);
+  const uint32_t hslots = PEN ? (uint32_t)kp.hash_slots : 0u;
+  const int bwords = PEN ? stream_bitmap_words(kp.vocab) : 0;
+  // LDS: with penalties, a bitmap of the tokens that have history, the hash
+  // of their counts (token << 13 | count) and each entry's penalised value;
+  // then the gathered keys sk (later their prefix masses) and the sorted
+  // keys srt; the window histogram and its prefix sums use the same bytes
+  // before the gather
+  uint32_t *bmap = reinterpret_cast<uint32_t *>(lds_raw + sizeof(SmemBase));
+  uint32_t *hash = bmap + bwords;
+  float *hz = reinterpret_cast<float *>(hash + hslots);
+  unsigned long long *sk = reinterpret_cast<unsigned long long *>(hz + hslots);
+  unsigned long long *srt = sk + kSCap;
+  double *pre = reinterpret_cast<double *>(sk);
+  unsigned long long *wh = sk;                                     // [kWinBins]
+  unsigned long long *lm = sk + kWinBins;                          // [kWinBins] inclusive masses
+  uint32_t *lc = reinterpret_cast<uint32_t *>(sk + 2 * kWinBins);  // [kWinBins] inclusive counts
+  static_assert(8 * 2 * kWinBins + 4 * kWinBins <= 16 * kSCap, "the histogram fits the list region");
+
+  const int V = kp.vocab;
+  const int n4 = (V + 3) >> 2;
+  const int K = kp.top_lp;
+  unsigned it = 0;  // (the phase stamps describe a workgroup's first row)
+  PHASE_STAMP(kStampStreamStart);
+  for (int j = tidx(); j < 64; j += kBlock) sm.exp_tab[j] = exp2((double)j * (1.0 / 64.0));
+  __syncthreads();
+
+  for (int ri = blockIdx.x; ri < kp.n_rows; ri += gridDim.x, ++it) {
+    const int tid = tidx();
+    const int lane = tid & 63;
+    const RowParam P = kp.rows ? kp.rows[ri] : ka.rows[ri];
+    const int row = P.row;
+    PHASE_STAMP(kStampRow);
+    PHASE_RECORD(kStampRowIndex, row + 1);
+    // outputs of a row without a token (status 1, 2 or 4)
+    auto write_status = [&](int status) {
+      if (tid == 0) {
+        kp.token_ids[row] = -1;
+        if (kp.row_status) kp.row_status[row] = status;
+      }
+      for (int t = tid; t < K; t += kBlock) {
+        kp.top_lp_vals[(int64_t)row * K + t] = -INFINITY;
+        kp.top_lp_ids[(int64_t)row * K + t] = -1;
+      }
+    };
+    // the row goes to the row kernel launched after this one (its record
+    // is read again: keeping P live across the row would cost registers)
+    auto defer_row = [&]() {
+      if (tid == 0) {
+        const uint32_t slot = (uint32_t)arrive_word(kp.defer_word, kp.epoch);
+        kp.defer_rows[slot] = kp.rows ? kp.rows[ri] : ka.rows[ri];
+      }
+    };
+    auto row_body = [&]() __attribute__((always_inline)) {
+      if (P.flags & RF_BAD) {
+        write_status(4);
+        return;
+      }
+      const bool greedy = P.flags & RF_GREEDY;
+      const bool top1 = P.flags & RF_TOP1;
+      const bool pen = PEN && (P.flags & RF_PEN);
+      const bool topk = !greedy && (P.flags & RF_TOPK);
+      const bool topp = !greedy && (P.flags & RF_TOPP);
+      const bool minp = !greedy && (P.flags & RF_MINP);
+      const bool truncated = topk || topp || minp;
+      const bool gumbel = !top1 && kp.path != PATH_GREEDY;
+      const float T = P.temperature;
+      const float rT = 1.0f / T;
+      const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
+      const uint32_t xhi_b = min(__float_as_uint(T * 0x1p99f), 0x7F7FFFFFu);
+      const int64_t rbase = (int64_t)row * kp.row_stride;
+      const bool vec = kp.vec_ok & 4;  // rows aligned for 16-byte loads
+
+      // ---- history counts: the hash, the bitmap, and each token's
+      // penalised value (computed once, by the thread that created the entry,
+      // from the token's raw logit).  The passes take the history tokens out
+      // of the stream (their bits make them -inf there) and then visit them
+      // from the hash: the "patch" step of each pass.
+      if (pen) {
+        for (int t = tid; t < bwords; t += kBlock) bmap[t] = 0u;
+        for (int t = tid; t < (int)hslots; t += kBlock) hash[t] = kEmpty;
+        __syncthreads();
+        const int32_t *hist = kp.history_ids + P.hist_start;
+        for (int h = tid; h < P.hist_len; h += kBlock) {
+          const int32_t id = hist[h];
+          if (id >= 0 && id < V) {
+            const uint32_t tok = (uint32_t)id;
+            uint32_t sl = hash_slot(tok, hslots);
+            while (true) {
+              const uint32_t prev = atomicCAS(&hash[sl], kEmpty, (tok << 13) | 1u);
+              if (prev == kEmpty) {
+                atomicOr(&bmap[tok >> 5], 1u << (tok & 31u));
+                break;
+              }
+              if ((prev >> 13) == tok) {
+                atomicAdd(&hash[sl], 1u);
+                break;
+              }
+              sl = (sl + 1u) & (hslots - 1u);
+            }
+          }
+        }
+        __syncthreads();
+        for (int t = tid; t < (int)hslots; t += kBlock) {
+          const uint32_t e = hash[t];
+          if (e != kEmpty) {
+            float x = load1_cached(reinterpret_cast<const TIn *>(kp.logits), rbase + (e >> 13));
+            x = x == x ? x : -INFINITY;
+            hz[t] = div_temp(apply_penalty(x, e & 0x1FFFu, P), T, rT);
+          }
+        }
+        __syncthreads();
+      }
+      PHASE_STAMP(kStampHashed);
+      // the patch step: f(token, z) for every history token of the row
+      auto patches = [&](auto &&f) __attribute__((always_inline)) {
+        if (pen)
+          for (int t = tid; t < (int)hslots; t += kBlock) {
+            const uint32_t e = hash[t];
+            if (e != kEmpty) f((int)(e >> 13), hz[t]);
+          }
+      };
+
+      // The passes see every token without history: pass A and B its z =
+      // x / T correctly rounded (Markstein while |x| lies in [T 2^-99,
+      // T 2^99], else the IEEE division), NaN -> -inf, -0 -> +0; pass C its
+      // raw logit, compared with thresholds mapped to the logits.  History
+      // tokens and slots past the row are masked (they read -inf).
+      // A chunk is a 16-byte load: kGPL groups of four values.
+      constexpr int kGPL = Chunk16<TIn>::kGroups;
+      constexpr int kCV = 4 * kGPL;  // values per chunk
+      const int nch = (V + kCV - 1) / kCV;
+      // the chunk's history bits (bit j: value j of the chunk)
+      auto chunk_bits = [&](int c) -> uint32_t {
+        if (!pen) return 0u;
+        const uint32_t i0 = (uint32_t)(kCV * c);
+        return (bmap[i0 >> 5] >> (i0 & 31u)) & ((1u << kCV) - 1u);
+      };
+      // z of an unmasked value: the Markstein form when the step is known
+      // to lie in its range, else the general division
+      auto zval = [&](float x, bool fast) __attribute__((always_inline)) {
+        if (fast) {
+          const float qq = x * rT;
+          return __builtin_fmaf(__builtin_fmaf(-qq, T, x), rT, qq);
+        }
+        return div_temp(x == x ? x : -INFINITY, T, rT);
+      };
+      // One pass over the row: fstep(gi, v, mk, fast) for each step of kNG
+      // groups per thread (their indices, raw values and masks of masked
+      // values; fast: every value of the step is finite and in the Markstein
+      // range, tested only when the pass asks for it).  Threads take chunks;
+      // each workgroup starts at its own point of its row (rows lie at
+      // multiples of one stride) and wraps around.  Loads run one step ahead
+      // (the next step's chunks are in flight while this step's are
+      // processed).  Lanes past the row's end see masked values, so
+      // cross-lane operations in fstep run in uniform control flow.
+      const int shift = (int)(((int64_t)blockIdx.x * nch) / (int64_t)gridDim.x);
+      auto cmap = [&](int x) {  // x in [0, nch): the chunk it stands for
+        const int y = x + shift;
+        return y >= nch ? y - nch : y;
+      };
+      constexpr int kSL = kSLoads;  // loads per step
+      constexpr int kNG = kSL * kGPL;  // groups per thread and step
+      auto stream_pass = [&](auto NEEDZ, auto &&fstep) __attribute__((always_inline)) {
+        constexpr bool needz = decltype(NEEDZ)::value;
+        const int lastc = nch - 1;
+        constexpr int kStep = kBlock * kSL;
+        // a step: group indices, masks and the fast flag; values are
+        // unpacked from the raw chunks where the pass uses them
+        auto step = [&](int s0, const u32x4 (&ch)[kSL], const uint32_t (&bb)[kSL]) __attribute__((always_inline)) {
+          int gi[kNG];
+          uint32_t mk[kNG];
+          uint32_t amax = 0u, amin = 0xFFFFFFFFu;
+#pragma unroll
+          for (int u = 0; u < kSL; ++u) {
+            const int x = s0 + tid + u * kBlock;
+            const int c = cmap(min(x, lastc));
+#pragma unroll
+            for (int j = 0; j < kGPL; ++j) {
+              const int t = u * kGPL + j;
+              gi[t] = kGPL * c + j;
+              const int i0 = kCV * c + 4 * j;
+              uint32_t m4 = (bb[u] >> (4 * j)) & 0xFu;
+              if (x >= nch) m4 = 0xFu;
+              if (i0 + 4 > V) m4 |= (0xFu << (V - i0 > 0 ? V - i0 : 0)) & 0xFu;
+              mk[t] = m4;
+              if (needz) {
+                float v[4];
+                Chunk16<TIn>::unpack(ch[u], j, v);
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  const uint32_t ab = ((m4 >> q) & 1u) ? __float_as_uint(1.0f) : __float_as_uint(v[q]) & 0x7FFFFFFFu;
+                  amax = max(amax, ab);
+                  amin = min(amin, ab);
+                }
+              }
+            }
+          }
+          // (1.0 stands in for masked values: in range whenever T is)
+          const bool fast = needz && (__float_as_uint(1.0f) <= xhi_b) && (__float_as_uint(1.0f) >= xlo_b) &&
+                            __ballot(!((amax <= xhi_b) & (amin >= xlo_b))) == 0ull;  // (wave-uniform)
+          fstep(gi, ch, mk, fast);
+        };
+        if (vec) {
+          u32x4 cur[kSL];
+#pragma unroll
+          for (int u = 0; u < kSL; ++u)
+            cur[u] = Chunk16<TIn>::load(kp.logits, rbase + kCV * (int64_t)cmap(min(tid + u * kBlock, lastc)));
+          for (int s0 = 0; s0 < nch; s0 += kStep) {  // (workgroup-uniform trip count)
+            u32x4 nxt[kSL];  // (clamped: the last step loads in bounds, unused)
+#pragma unroll
+            for (int u = 0; u < kSL; ++u)
+              nxt[u] = Chunk16<TIn>::load(kp.logits, rbase + kCV * (int64_t)cmap(min(s0 + kStep + tid + u * kBlock, lastc)));
+            uint32_t bb[kSL];
+#pragma unroll
+            for (int u = 0; u < kSL; ++u) bb[u] = chunk_bits(cmap(min(s0 + tid + u * kBlock, lastc)));
+            step(s0, cur, bb);
+#pragma unroll
+            for (int u = 0; u < kSL; ++u) cur[u] = nxt[u];
+          }
+        } else {  // clamped scalar loads, packed into chunks
+          for (int s0 = 0; s0 < nch; s0 += kStep) {
+            u32x4 ch[kSL];
+            uint32_t bb[kSL];
+#pragma unroll
+            for (int u = 0; u < kSL; ++u) {
+              const int c = cmap(min(s0 + tid + u * kBlock, lastc));
+              bb[u] = chunk_bits(c);
+              ch[u] = Chunk16<TIn>::load_scalar(kp.logits, rbase, kCV * c, V);
+            }
+            step(s0, ch, bb);
+          }
+        }
+      };
+      // value q of group t of a step's raw chunks
+      auto rawv = [&](const u32x4 (&ch)[kSL], int t, int q) __attribute__((always_inline)) {
+        float v[4];
+        Chunk16<TIn>::unpack(ch[t / kGPL], t % kGPL, v);
+        return v[q];
+      };
+      // a pass whose work is per group of processed values: f(g, z)
+      auto group_pass = [&](auto &&f) __attribute__((always_inline)) {
+        stream_pass(std::true_type{}, [&](const int (&gi)[kNG], const u32x4 (&ch)[kSL], const uint32_t (&mk)[kNG], bool fast)
+                                          __attribute__((always_inline)) {
+          if (fast) {
+#pragma unroll
+            for (int t = 0; t < kNG; ++t) {
+              float z[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) z[q] = ((mk[t] >> q) & 1u) ? -INFINITY : zval(rawv(ch, t, q), true);
+              f(gi[t], z);
+            }
+          } else {
+#pragma unroll
+            for (int t = 0; t < kNG; ++t) {
+              float z[4];
+#pragma unroll
+              for (int q = 0; q < 4; ++q) z[q] = ((mk[t] >> q) & 1u) ? -INFINITY : zval(rawv(ch, t, q), false);
+              f(gi[t], z);
+            }
+          }
+        });
+      };
+      // the smallest logit whose z has a key of at least kz (z is monotone in
+      // the logit), or NaN when none has: "key(z) >= kz" is then "x >= it"
+      // for every unmasked value (NaN compares false, as -inf would)
+      auto x_at_least = [&](uint32_t kz) -> float {
+        if (kz > fkey(INFINITY)) return __uint_as_float(0x7FC00000u);
+        uint32_t lo = fkey(-INFINITY), hi = fkey(INFINITY);  // key(z(lo)) < kz <= key(z(hi)) once lo is excluded
+        if (fkey(div_temp(-INFINITY, T, rT)) >= kz) return -INFINITY;
+        while (hi - lo > 1u) {
+          const uint32_t mid = lo + (hi - lo) / 2u;
+          if (fkey(div_temp(key_to_float(mid), T, rT)) >= kz) hi = mid;
+          else lo = mid;
+        }
+        return key_to_float(hi);
+      };
+
+      // ---- A. the row max and its first index (the best group of four, the
+      // earlier group on a tie, then the first match in it)
+      float lmax = -INFINITY;
+      int lgrp = -1;
+      float lz[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
+      group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
+        const float gm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        const bool take = gm > lmax || (gm == lmax && gm > -INFINITY && g < lgrp);
+        lmax = take ? gm : lmax;
+        lgrp = take ? g : lgrp;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) lz[c] = take ? z[c] : lz[c];
+      });
+      int lidx = 0x7FFFFFFF;
+      if (lgrp >= 0) lidx = 4 * lgrp + (lz[0] == lmax ? 0 : lz[1] == lmax ? 1 : lz[2] == lmax ? 2 : 3);
+      unsigned long long lkey = ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx);
+      patches([&](int i, float zz) {
+        const unsigned long long k2 = ((unsigned long long)fkey(zz) << 32) | (0xFFFFFFFFu - (uint32_t)i);
+        lkey = k2 > lkey ? k2 : lkey;
+      });
+      const unsigned long long mk = wg_max_u(sm, lkey);
+      const float mf = key_to_float((uint32_t)(mk >> 32));
+      const int argmax = (int)(0xFFFFFFFFu - (uint32_t)mk);
+      PHASE_STAMP(kStampMax);
+      if (!(mf > -INFINITY && mf < INFINITY)) {
+        write_status(mf == INFINITY ? 2 : 1);  // a +inf value, or no finite value
+        return;
+      }
+      if ((!gumbel || top1) && K == 0) {  // the first argmax is all the row needs
+        if (tid == 0) {
+          kp.token_ids[row] = argmax;
+          if (kp.row_status) kp.row_status[row] = 0;
+        }
+        return;
+      }
+      const double m = (double)mf;
+      const float wsc = T < 1.0f ? T : 1.0f;
+      uint32_t t_m = 0;
+      if (minp) t_m = min_p_key(sm, m, log((double)P.min_p), P.min_p);
+
+      // Value ranges, as order keys.  Values with key >= T_hi are certainly
+      // kept ("above"), values with key in [T_lo, T_hi) may hold tau and are
+      // gathered, values below T_lo are dropped; values with key >= K_lo
+      // (the top-logprob range) are gathered too.  Without truncation every
+      // finite value is above; min-p alone gives tau exactly.
+      const uint32_t kFinite = fkey(-INFINITY) + 1u;
+      uint32_t T_lo = kFinite, T_hi = kFinite, K_lo = 0xFFFFFFFFu;
+      bool topk_on = topk;
+      uint32_t lo_max = 0, hi_max = 0;  // the threshold ranges' bounds (pass B)
+      uint32_t klo_bin = 0xFFFFFFFFu;   // the top-logprob range's lower bound (pass B)
+      uint32_t klo_k = 0;               // the lower bound of the top-k value's bin (pass B)
+      double C_all = 0.0;  // top-p without top-k: the row's whole mass (window masses, fp64 sum)
+
+      // ---- B. window histogram (the row kernel's bins), when a threshold
+      // or the top-logprob list needs placing
+      if (topk || topp || K > 0) {
+        const float A = abin(mf, wsc);
+        if (!(A > -INFINITY && A < INFINITY)) {  // the bin grid overflows for |m / T| beyond ~1e37
+          defer_row();
+          return;
+        }
+        wh[tid] = 0;
+        __syncthreads();
+        const bool need_c = topp && !topk;
+        double csum = 0.0;
+        group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
+          float dsum = 0.0f;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float lb = win_pos(A, z[c], wsc);  // -inf: +inf
+            const float a = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
+            if (lb < (float)kWinBins) atomicAdd(&wh[(int)lb], hist_entry_s(a));
+            dsum += a;
+          }
+          if (need_c) csum += (double)dsum;
+        });
+        patches([&](int i, float zz) {
+          const float lb = win_pos(A, zz, wsc);
+          const float a = __builtin_amdgcn_exp2f((zz - mf) * kLog2e);
+          if (lb < (float)kWinBins) atomicAdd(&wh[(int)lb], hist_entry_s(a));
+          if (need_c) csum += (double)a;
+        });
+        C_all = need_c ? wg_sum_d(sm, csum) : 0.0;
+        __syncthreads();
+        PHASE_STAMP(kStampHist);
+        const int b = tid;
+        const unsigned long long e = wh[b];
+        uint32_t runc = (uint32_t)(e >> 44);
+        unsigned long long runm = e & ((1ull << 44) - 1ull);
+        block_scan_incl2(runc, runm, sm.red_c, sm.red_u);
+        lc[b] = runc;
+        lm[b] = runm;
+        if (tid == 0) {
+          sm.bu[16] = kNone;
+          sm.bu[17] = kNone;
+          sm.bu[18] = kNone;
+          sm.bu[19] = kNone;
+        }
+        __syncthreads();
+        // bins of the k-th and the K-th value
+        const uint32_t cprev = b > 0 ? lc[b - 1] : 0u;
+        if (topk && cprev < (uint32_t)P.top_k && runc >= (uint32_t)P.top_k) sm.bu[16] = (uint32_t)b;
+        if (K > 0 && cprev < (uint32_t)K && runc >= (uint32_t)K) sm.bu[17] = (uint32_t)b;
+        __syncthreads();
+        const uint32_t bk = sm.bu[16], r0 = sm.bu[17];
+        bool gen = false;
+        if (topk && bk == kNone) {
+          // the k-th value is deeper than the window: it decides unless
+          // min-p's boundary lies inside the window (and so above it)
+          const bool minp_in = minp && win_bin(A, key_to_float(t_m), wsc) < kWinBins;
+          if (topp || !minp_in) gen = true;
+          else topk_on = false;
+        }
+        // top-p: the bins where the cumulative mass crosses p times the
+        // total mass of the top-k set (bounded below and above), or of the
+        // row
+        double tlo = 0.0, thi = 0.0;
+        if (topp && !gen) {
+          if (topk) {
+            tlo = (double)P.top_p * (bk > 0 ? (double)lm[bk - 1] : 0.0);
+            thi = (double)P.top_p * (double)lm[bk];
+          } else {
+            tlo = thi = (double)P.top_p * C_all * 16777216.0;
+          }
+          const double mprev = b > 0 ? (double)lm[b - 1] : 0.0, mcur = (double)lm[b];
+          if (mprev < tlo && mcur >= tlo) sm.bu[18] = (uint32_t)b;
+          if (mprev < thi && mcur >= thi) sm.bu[19] = (uint32_t)b;
+        }
+        __syncthreads();
+        int plo = 0, phi = -1;
+        if (topp && !gen) {
+          const uint32_t lo = tlo <= 0.0 ? 0u : sm.bu[18], hi = sm.bu[19];
+          if (hi == kNone) {
+            gen = true;  // the crossing lies deeper than the window
+          } else {
+            // one bin of slack on each side (the masses are approximate;
+            // the decision on the gathered values is exact)
+            plo = max((int)(lo == kNone ? hi : lo) - 1, 0);
+            phi = min((int)hi + 1, kWinBins - 1);
+            if (topk) {
+              plo = min(plo, (int)bk);
+              phi = min(phi, (int)bk);
+            }
+          }
+        }
+        int r0hi = -1;
+        if (K > 0 && !gen) {
+          if (r0 != kNone) r0hi = (int)r0;
+          else if (truncated) r0hi = kWinBins - 1;  // fewer than K values in the window: all of them
+          else gen = true;                          // the list reaches below the window
+        }
+        if (gen) {
+          __syncthreads();
+          defer_row();
+          return;
+        }
+        // the key bounds of those bins: bins 0..h hold the values with key
+        // >= lo(h); bin h the values in [lo(h), lo(h - 1))
+        if (tid < 5) {
+          const int h = tid == 0 ? (int)bk : tid == 1 ? (int)bk - 1 : tid == 2 ? phi : tid == 3 ? plo - 1 : r0hi;
+          const bool act = tid <= 1 ? topk_on : tid <= 3 ? topp : K > 0;
+          uint32_t k = 0xFFFFFFFFu;  // (no bin above bin 0)
+          if (act && h >= 0) k = fkey(win_floor_z(A, (float)h, wsc));
+          sm.bu[20 + tid] = k;
+        }
+        __syncthreads();
+        if (topk_on) {
+          lo_max = max(lo_max, sm.bu[20]);
+          hi_max = max(hi_max, sm.bu[21]);
+          klo_k = sm.bu[20];
+        }
+        if (topp) {
+          lo_max = max(lo_max, sm.bu[22]);
+          hi_max = max(hi_max, sm.bu[23]);
+        }
+        if (minp) {
+          lo_max = max(lo_max, t_m);
+          hi_max = max(hi_max, t_m + 1u);
+        }
+        klo_bin = sm.bu[24];
+        __syncthreads();  // the histogram's bytes are reused by the gather
+        PHASE_STAMP(kStampDecided);
+      }
+      if (truncated) {
+        if (topk_on || topp) {
+          T_lo = lo_max;
+          T_hi = hi_max;
+          // top-p takes its share of the top-k set's mass, so the values
+          // down to the k-th one are gathered too (those below tau drop out)
+          if (topk_on && topp) T_lo = klo_k;
+        } else {
+          T_lo = T_hi = t_m;  // min-p alone: tau exactly
+        }
+      }
+      if (K > 0) K_lo = truncated ? max(klo_bin, T_lo) : klo_bin;
+
+      // ---- C. gather the ranges; above them: count, exact masses, Gumbel
+      const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
+      const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
+      double best_g = -INFINITY;
+      int best_i = 0x7FFFFFFF;
+      float bound = 0.0f, cut = kPruneNats;
+      if (gumbel) {
+        // the argmax (always kept) scores 1 / E; a value more than 33 ln 2 -
+        // ln(bound) nats below the max cannot beat it (as in the row kernel)
+        uint32_t w4[4];
+        philox4x32_10((uint32_t)argmax >> 2, P.stream, off0, off1, key0, key1, w4);
+        bound = (float)(1.0 / exp1_f64(w4[argmax & 3])) * 0.99999f;
+        cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
+      }
+      const bool need_s = topp || K > 0;  // the kept mass (crossing, normaliser)
+      double s_above = 0.0;
+      uint32_t n_above = 0;
+      if (tid == 0) sm.bu[25] = 0u;
+      __syncthreads();
+      // whether a value is gathered, or above the gathered ranges (kept)
+      auto is_gat = [&](uint32_t k) { return (k >= K_lo) | ((k >= T_lo) & (k < T_hi)); };
+      auto is_abv = [&](uint32_t k, float z) { return !is_gat(k) & (k >= T_hi) & (z > -INFINITY); };
+      // the ranges as logit thresholds (threads 0..2, by bisection)
+      if (tid < 3) {
+        const float xt = x_at_least(tid == 0 ? K_lo : tid == 1 ? T_lo : T_hi);
+        sm.bu[32 + tid] = __float_as_uint(xt);
+      }
+      __syncthreads();
+      const float xK = __uint_as_float(sm.bu[32]), xTlo = __uint_as_float(sm.bu[33]), xThi = __uint_as_float(sm.bu[34]);
+      stream_pass(std::false_type{}, [&](const int (&gi)[kNG], const u32x4 (&ch)[kSL], const uint32_t (&mk)[kNG], bool)
+                                         __attribute__((always_inline)) {
+        // cheap per-group part on the raw logits: gathered values (their z
+        // taken exactly) appended per wave in ballot order; groups holding a
+        // value above the ranges marked in hv
+        uint32_t hv = 0;
+#pragma unroll
+        for (int t = 0; t < kNG; ++t) {
+          bool anya = false;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float x = ((mk[t] >> c) & 1u) ? -INFINITY : rawv(ch, t, c);  // (NaN compares false)
+            const bool below_hi = !(x >= xThi);
+            const bool gt = (x >= xK) | ((x >= xTlo) & below_hi);
+            anya |= !gt & !below_hi & (x > -INFINITY);
+            const unsigned long long bal = __ballot(gt);
+            if (bal) {
+              uint32_t base = 0;
+              if (lane == 0) base = atomicAdd(&sm.bu[25], (uint32_t)__popcll(bal));
+              base = (uint32_t)__builtin_amdgcn_readfirstlane((int)base);
+              const uint32_t off = __builtin_amdgcn_mbcnt_hi((uint32_t)(bal >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)bal, 0u));
+              if (gt && base + off < (uint32_t)kSCap) sk[base + off] = cand_key(zval(x, false), 4 * gi[t] + c);
+            }
+          }
+          hv |= anya ? 1u << t : 0u;
+        }
+        // the groups above the ranges, one per lane per round (one copy of
+        // the heavy code): count, exact masses, Philox, the linear-domain
+        // bound and the fp64 scores of the values that can still win
+        bool improved = false;
+        while (hv) {
+          const int t0 = __builtin_ctz(hv);
+          hv &= hv - 1u;
+          int g = 0;
+          float xr[4];
+          uint32_t m4 = 0;
+#pragma unroll
+          for (int t = 0; t < kNG; ++t)
+            if (t == t0) {
+              g = gi[t];
+              m4 = mk[t];
+#pragma unroll
+              for (int c = 0; c < 4; ++c) xr[c] = rawv(ch, t, c);
+            }
+          bool cand = false;
+          uint32_t am = 0;
+          float z[4];
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            const float x = ((m4 >> c) & 1u) ? -INFINITY : xr[c];
+            const bool ab = (x >= xThi) & !(x >= xK) & (x > -INFINITY);
+            z[c] = ab ? zval(x, false) : -INFINITY;
+            am |= ab ? 1u << c : 0u;
+            cand |= ab && (mf - z[c] <= cut);
+          }
+          n_above += (uint32_t)__popc(am);
+          if (need_s) {
+            for (uint32_t mm = am; mm; mm &= mm - 1u) {
+              const int c = __builtin_ctz(mm);
+              const float zc = c == 0 ? z[0] : c == 1 ? z[1] : c == 2 ? z[2] : z[3];
+              s_above += truncated ? exp_nonpos(sm.exp_tab, (double)zc - m) : exp_term(zc, m);
+            }
+          }
+          if (gumbel && cand) {
+            uint32_t w[4];
+            philox4x32_10((uint32_t)g, P.stream, off0, off1, key0, key1, w);
+            // lower bound of E (E >= w) against the best score so far
+            uint32_t surv = 0;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float wl = (float)w[c] * 0x1.fffffcp-33f;
+              const float qv = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
+              surv |= (((am >> c) & 1u) && (mf - z[c] <= cut) && wl * bound <= qv * kSlack) ? 1u << c : 0u;
+            }
+            while (surv) {
+              const int c = __builtin_ctz(surv);
+              surv &= surv - 1u;
+              const float zc = c == 0 ? z[0] : c == 1 ? z[1] : c == 2 ? z[2] : z[3];
+              const uint32_t wc = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
+              const double ge = (double)zc - log(exp1_f64(wc));
+              if (ge > best_g || (ge == best_g && 4 * g + c < best_i)) {
+                best_g = ge;
+                best_i = 4 * g + c;
+                improved = true;
+              }
+            }
+          }
+        }
+        if (gumbel && __ballot(improved)) {
+          float mb = improved ? (float)exp(best_g - m) * 0.99999f : 0.0f;
+          mb = wave_max_nonneg_f(mb);
+          bound = fmaxf(bound, mb);
+        }
+      });
+      patches([&](int i, float zz) {
+        const uint32_t k = fkey(zz);
+        if (is_gat(k)) {
+          const uint32_t slot = atomicAdd(&sm.bu[25], 1u);
+          if (slot < (uint32_t)kSCap) sk[slot] = cand_key(zz, i);
+        } else if (is_abv(k, zz)) {
+          ++n_above;
+          if (need_s) s_above += truncated ? exp_nonpos(sm.exp_tab, (double)zz - m) : exp_term(zz, m);
+          if (gumbel) {
+            uint32_t w[4];
+            philox4x32_10((uint32_t)i >> 2, P.stream, off0, off1, key0, key1, w);
+            const uint32_t wc = (i & 3) == 0 ? w[0] : (i & 3) == 1 ? w[1] : (i & 3) == 2 ? w[2] : w[3];
+            const double ge = (double)zz - log(exp1_f64(wc));
+            if (ge > best_g || (ge == best_g && i < best_i)) {
+              best_g = ge;
+              best_i = i;
+            }
+          }
+        }
+      });
+      const uint32_t cnt_above = (uint32_t)wg_sum_u(sm, n_above);  // (its barriers also order the appends)
+      const double S_above = need_s ? wg_sum_d(sm, s_above) : 0.0;
+      const uint32_t n_g = sm.bu[25];
+      PHASE_STAMP(kStampGathered);
+      if (n_g > (uint32_t)kSCap) {
+        defer_row();
+        return;
+      }
+      const int n = (int)n_g;
+
+      // ---- the gathered list, sorted by (value desc, index asc): a key's
+      // position is the number of larger keys (keys are distinct)
+      for (int j = tid; j < n; j += kBlock) {
+        const unsigned long long c = sk[j];
+        uint32_t r = 0;
+        int i = 0;
+        for (; i + 8 <= n; i += 8) {
+          unsigned long long kk[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) kk[u] = sk[i + u];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) r += kk[u] > c ? 1u : 0u;
+        }
+        for (; i < n; ++i) r += sk[i] > c ? 1u : 0u;
+        srt[r] = c;
+      }
+      __syncthreads();
+      PHASE_STAMP(kStampX3Ranked);
+      auto keyof = [&](int j) { return (uint32_t)(srt[j] >> 32); };
+      auto zof = [&](int j) { return key_to_float(keyof(j)); };
+      auto idxof = [&](int j) { return (int)(~(uint32_t)srt[j]); };
+      // inclusive prefix of exact masses exp(z - m) along the list (each
+      // thread owns kSCap / kBlock consecutive positions)
+      {
+        constexpr int kPer = kSCap / kBlock;
+        double qv[kPer];
+        double own = 0.0;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int j = tid * kPer + u;
+          qv[u] = j < n ? exp_nonpos(sm.exp_tab, (double)zof(j) - m) : 0.0;
+          own += qv[u];
+        }
+        double run = block_scan_incl<double>(own, sm.red_d) - own;
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+          const int j = tid * kPer + u;
+          run += qv[u];
+          if (j < n) pre[j] = run;
+        }
+      }
+      // the list's head (keys >= K_lo) lies above the above-range, the rest
+      // below it; nK = the head's length (the whole list when nothing is above)
+      const bool has_above = cnt_above > 0u;
+      if (tid == 0) {
+        sm.bu[26] = (uint32_t)n;  // nK
+        sm.bu[27] = (uint32_t)n;  // end of the top-k tie group
+        sm.bu[28] = 0x7FFFFFFFu;  // top-p crossing
+        sm.bu[29] = 0u;           // first position of the crossing's tie group
+        sm.bu[30] = (uint32_t)n;  // end of the kept list
+      }
+      __syncthreads();
+      if (has_above)
+        for (int j = tid; j < n; j += kBlock)
+          if (keyof(j) < K_lo && (j == 0 || keyof(j - 1) >= K_lo)) sm.bu[26] = (uint32_t)j;
+      __syncthreads();
+      const int nK = (int)sm.bu[26];
+      const double ab = has_above ? S_above : 0.0;
+      auto cum = [&](int j) { return pre[j] + (j >= nK ? ab : 0.0); };               // mass up to and with j
+      auto cumb = [&](int j) { return (j > 0 ? pre[j - 1] : 0.0) + (j >= nK ? ab : 0.0); };  // mass before j
+      bool bad = false;
+      // top-k: the value of rank k (values above the list's tail count too);
+      // past the list's end it lies below T_lo, under another threshold's
+      // range, and does not bind (kout)
+      uint32_t tk = 0;
+      bool kout = false;
+      if (topk_on) {
+        const int r = P.top_k - 1;
+        const int j = (!has_above || r < nK) ? r : (r < nK + (int)cnt_above ? -1 : r - (int)cnt_above);
+        if (j < 0) bad = true;
+        else if (j >= n) kout = true;
+        else tk = keyof(j);
+        if (!bad && !kout)
+          for (int q = tid; q < n; q += kBlock)
+            if (keyof(q) < tk && (q == 0 || keyof(q - 1) >= tk)) sm.bu[27] = (uint32_t)q;
+      }
+      __syncthreads();
+      const int ek = (int)sm.bu[27];
+      // top-p: the first tie-group end whose cumulative mass reaches p times
+      // the top-k set's mass (exact) or the row's (window masses)
+      uint32_t tp = 0;
+      double ctot = 0.0, target = 0.0;
+      if (topp && topk_on && kout) bad = true;  // (the list reaches down to the k-th value's bin)
+      if (topp && !bad) {
+        ctot = topk_on ? (ek > 0 ? cum(ek - 1) : 0.0) : C_all;
+        target = (double)P.top_p * ctot;
+        for (int e = tid; e < n; e += kBlock) {
+          const bool end = (e == n - 1) || (keyof(e + 1) != keyof(e));
+          const unsigned long long bal = __ballot(end && cum(e) >= target);
+          if (bal && lane == __ffsll((long long)bal) - 1) atomicMin(&sm.bu[28], (uint32_t)e);
+        }
+      }
+      __syncthreads();
+      if (topp && !bad) {
+        const uint32_t e = sm.bu[28];
+        if (e == 0x7FFFFFFFu) {
+          // no tie-group end reaches the target: the crossing lies below
+          // T_lo, where another threshold's range keeps tau above it -- if
+          // the mass of everything from T_lo up is short of the target by
+          // more than the total's error
+          const double tot = n > 0 ? cum(n - 1) : ab;
+          if (tot >= target || target - tot < kTopPMarginRel * ctot) bad = true;
+        } else {
+          const uint32_t ke = keyof((int)e);
+          for (int j = tid; j <= (int)e; j += kBlock)
+            if (keyof(j) == ke && (j == 0 || keyof(j - 1) != ke)) sm.bu[29] = (uint32_t)j;
+          __syncthreads();
+          const int gs = (int)sm.bu[29];
+          const double c_new = cum((int)e), c_prev = cumb(gs);
+          if (c_prev >= target) bad = true;  // the crossing lies among the values above the list
+          if (!topk_on) {
+            // the row's mass is approximate: a crossing this close to its
+            // target, on a side where moving it would change tau, goes to
+            // the row kernel
+            const uint32_t tkm = minp ? t_m : 0u;
+            const uint32_t kprev = (gs > 0 && !(has_above && gs == nK)) ? keyof(gs - 1) : 0xFFFFFFFFu;
+            const bool close_lo = c_new - target < kTopPMarginRel * ctot && ke > tkm;
+            const bool close_hi = target - c_prev < kTopPMarginRel * ctot && kprev > tkm;
+            if (close_lo || close_hi) bad = true;
+          }
+          tp = ke;
+        }
+      }
+      // tau, the kept list [0, et), and the checks that the ranges held it
+      uint32_t tau = truncated ? 0u : kFinite;
+      if (topk_on) tau = max(tau, tk);
+      if (topp) tau = max(tau, tp);
+      if (minp) tau = max(tau, t_m);
+      if (truncated && (tau < T_lo || (has_above && tau > T_hi))) bad = true;
+      if (!bad)
+        for (int j = tid; j < n; j += kBlock)
+          if (keyof(j) < tau && (j == 0 || keyof(j - 1) >= tau)) sm.bu[30] = (uint32_t)j;
+      __syncthreads();
+      const int et = (int)sm.bu[30];
+      // the top-logprob list must come from the head when values lie above
+      if (K > 0 && has_above && et > nK && nK < K) bad = true;
+      if (__syncthreads_or(bad)) {
+        defer_row();
+        return;
+      }
+      PHASE_STAMP(kStampThresholds);
+      const double lnS = need_s ? log(cumb(et)) : 0.0;
+      for (int q = tid; q < K; q += kBlock) {
+        const int64_t o = (int64_t)row * K + q;
+        if (q < et) {
+          kp.top_lp_vals[o] = (float)(((double)zof(q) - m) - lnS);
+          kp.top_lp_ids[o] = idxof(q);
+        } else {
+          kp.top_lp_vals[o] = -INFINITY;
+          kp.top_lp_ids[o] = -1;
+        }
+      }
+      // Gumbel-max: the kept values of the list, then the best over the
+      // workgroup (ties to the smaller index)
+      if (gumbel) {
+        for (int j = tid; j < et; j += kBlock) {
+          const int i = idxof(j);
+          uint32_t w[4];
+          philox4x32_10((uint32_t)i >> 2, P.stream, off0, off1, key0, key1, w);
+          const uint32_t wc = (i & 3) == 0 ? w[0] : (i & 3) == 1 ? w[1] : (i & 3) == 2 ? w[2] : w[3];
+          const double ge = (double)zof(j) - log(exp1_f64(wc));
+          if (ge > best_g || (ge == best_g && i < best_i)) {
+            best_g = ge;
+            best_i = i;
+          }
+        }
+        wg_best(sm, best_g, best_i);
+      }
+      if (tid == 0) {
+        kp.token_ids[row] = gumbel ? best_i : argmax;
+        if (kp.row_status) kp.row_status[row] = 0;
+      }
+    };
+    row_body();
+    __syncthreads();
+    PHASE_STAMP(kStampEnd);
+  }
+}
+
 template <typename TIn, bool PEN>
 hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const KernelParams &kp = ka.kp;
@@ -3299,6 +4216,46 @@ hipError_t launch_raw_lp(const KernelArgs &ka, int dtype, hipStream_t stream) {
   const void *fn = dtype == 0 ? reinterpret_cast<const void *>(&raw_lp_kernel<float>)
                               : reinterpret_cast<const void *>(&raw_lp_kernel<uint16_t>);
   return hipExtLaunchKernel(fn, grid, block, args, lds, stream, nullptr, nullptr, 0);
+}
+
+size_t stream_lds_bytes(int hash_slots, bool penalties, int vocab) {
+  return sizeof(SmemBase) +
+         (penalties ? sizeof(uint32_t) * (size_t)stream_bitmap_words(vocab) + 8 * (size_t)hash_slots : 0) +
+         2 * sizeof(unsigned long long) * (size_t)kSCap;
+}
+
+namespace {
+template <typename TIn, bool PEN>
+const void *stream_fn() {
+  return reinterpret_cast<const void *>(&stream_kernel<TIn, PEN>);
+}
+}  // namespace
+
+hipError_t launch_stream(const KernelArgs &ka, int dtype, bool penalties, int grid, hipStream_t stream, hipEvent_t ev0,
+                         hipEvent_t ev1) {
+  const KernelParams &kp = ka.kp;
+  const size_t lds = stream_lds_bytes(kp.hash_slots, penalties, kp.vocab);
+  const void *fn = dtype == 0 ? (penalties ? stream_fn<float, true>() : stream_fn<float, false>())
+                              : (penalties ? stream_fn<uint16_t, true>() : stream_fn<uint16_t, false>());
+  void *args[] = {const_cast<KernelArgs *>(&ka)};
+  return hipExtLaunchKernel(fn, dim3(grid), dim3(kBlock), args, lds, stream, ev0, ev1, 0);
+}
+
+hipError_t stream_resident(int device, size_t lds_bytes, int *out) {
+  const void *fns[] = {stream_fn<float, true>(), stream_fn<float, false>(), stream_fn<uint16_t, true>(),
+                       stream_fn<uint16_t, false>()};
+  hipError_t e;
+  int pc = 1 << 30;
+  for (const void *f : fns) {
+    if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes)) != hipSuccess) return e;
+    int per_cu = 0;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kBlock, lds_bytes)) != hipSuccess) return e;
+    pc = per_cu < pc ? per_cu : pc;
+  }
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return e;
+  *out = pc * prop.multiProcessorCount;
+  return hipSuccess;
 }
 
 hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream) {

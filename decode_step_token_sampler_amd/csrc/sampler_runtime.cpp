@@ -40,6 +40,10 @@ constexpr double kGreedyEps = 1e-6;
 constexpr int kLightValuesPerThread = 4;
 // [B] "What the flag switches": requests without a seed use 42.
 constexpr uint64_t kDeterministicSeed = 42;
+// Steps whose rows outnumber the row kernel's row groups by more than this
+// factor run on the streaming kernel (measured on MI355X: see the design
+// notes' streaming section).
+constexpr int kStreamRowsPerGroup = 1;
 
 thread_local std::string g_create_error;
 
@@ -72,6 +76,11 @@ struct Workspace {
   uint32_t *hist_list = nullptr;  // [max_rows * hist_list_row] entries
   int32_t *hist_list_n = nullptr; // [max_rows * kMaxLightG]
   int64_t hist_list_row = 0;      // entries per row: min(kMaxLightG max_history, max_vocab + kMaxSlice)
+  // the streaming kernel: workgroups that fit at once, and the rows it
+  // leaves to the row kernel (records and the epoch-tagged count word)
+  int stream_resident = 0;
+  RowParam *defer_rows = nullptr;           // [max_rows]
+  unsigned long long *defer_word = nullptr;
   // limits the workspace was planned for
   int32_t max_history_per_row = 0, max_bias_per_row = 0, max_top_logprobs = 0, max_vocab = 0;
 };
@@ -314,6 +323,8 @@ void free_handle(sampler_handle *h) {
   if (h->ws.epoch_dev) (void)hipFree(h->ws.epoch_dev);
   if (h->ws.hist_list) (void)hipFree(h->ws.hist_list);
   if (h->ws.hist_list_n) (void)hipFree(h->ws.hist_list_n);
+  if (h->ws.defer_rows) (void)hipFree(h->ws.defer_rows);
+  if (h->ws.defer_word) (void)hipFree(h->ws.defer_word);
   delete h;
 }
 
@@ -536,6 +547,48 @@ void place_records(const RowParam *recs, int n, int groups, int *rank, int *ord,
   for (int k = 0; k < n; ++k) out[k < groups ? rank[k] : k] = recs[ord[k]];
 }
 
+// Whether a step may run on the streaming kernel: ids and top logprobs of
+// the sampled distribution only, no logits processors, Gumbel-max (or
+// argmax) selection, histories the hash holds, rows short enough for its
+// hash packing.  recs: the step's records.
+bool stream_eligible(const Workspace &ws, uint32_t flags, const sampler_step_args *a, const RowParam *recs, int n) {
+  if (flags & (SAMPLER_NO_STREAM | SAMPLER_DETERMINISTIC | SAMPLER_INVERSE_CDF)) return false;
+  if (a->probs || a->logprobs || a->vocab_mask) return false;
+  if (a->top_logprobs > 0 && a->logprob_mode != SAMPLER_LOGPROB_PROCESSED) return false;
+  if (a->vocab > kStreamMaxVocab || ws.stream_resident < 1) return false;
+  for (int r = 0; r < n; ++r) {
+    if (recs[r].flags & RF_SPEC) return false;
+    if ((recs[r].flags & RF_PEN) && recs[r].hist_len > kMaxHistPerRow) return false;
+  }
+  return true;
+}
+
+// Cost class of a row on the streaming kernel (larger: longer): rows that
+// keep every value run Philox over the whole row; top-p without top-k keeps
+// the most values; argmax rows read the row once.
+int stream_cost(const RowParam &p) {
+  if (p.flags & (RF_GREEDY | RF_TOP1)) return 0;
+  if (!(p.flags & (RF_TOPK | RF_TOPP | RF_MINP))) return 4;
+  if ((p.flags & RF_TOPP) && !(p.flags & RF_TOPK)) return 3;
+  if (p.flags & RF_TOPK) return 1;
+  return 2;
+}
+
+// The streaming kernel's order: costlier rows first (workgroup b starts on
+// row b), a stable counting sort.  ord holds n ints.
+void stream_records(const RowParam *recs, int n, int *ord, RowParam *out) {
+  constexpr int kClasses = 5;
+  int start[kClasses] = {};
+  for (int r = 0; r < n; ++r) ++start[stream_cost(recs[r])];
+  for (int c = kClasses - 1, acc = 0; c >= 0; --c) {
+    const int cnt = start[c];
+    start[c] = acc;
+    acc += cnt;
+  }
+  for (int r = 0; r < n; ++r) ord[start[stream_cost(recs[r])]++] = r;
+  for (int k = 0; k < n; ++k) out[k] = recs[ord[k]];
+}
+
 // Kernel parameters for n rows of a step and the launch.  `dp`: the device
 // records, or null (records in ka.rows); `dev`: per-row arrays in device
 // memory that rows_kernel normalises into `graph_rows` first
@@ -543,7 +596,7 @@ void place_records(const RowParam *recs, int n, int groups, int *rank, int *ord,
 sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_limit, const sampler_step_args *a,
                                int n, KernelArgs &ka, const RowParam *dp, bool any_pen, int path, hipStream_t stream,
                                std::string &err, const DevRowArrays *dev = nullptr, RowParam *graph_rows = nullptr,
-                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr) {
+                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool streamed = false) {
   const int V = a->vocab;
   const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
   hipError_t e;
@@ -600,7 +653,8 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   const size_t esz = a->dtype == SAMPLER_DTYPE_F32 ? 4 : 2;
   const bool lvec = ((uintptr_t)a->logits % (4 * esz) == 0) && (a->row_stride % 4 == 0);
   const bool ovec = ((V & 3) == 0) && ((uintptr_t)a->probs % 16 == 0) && ((uintptr_t)a->logprobs % 16 == 0);
-  kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0);
+  const bool lvec16 = ((uintptr_t)a->logits % 16 == 0) && ((a->row_stride * (int64_t)esz) % 16 == 0);
+  kp.vec_ok = (lvec ? 1 : 0) | (ovec ? 2 : 0) | (lvec16 ? 4 : 0);
   kp.path = path;
   kp.sync = ws.sync;
   kp.slots = ws.slots;
@@ -617,6 +671,24 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   if (dev && (e = launch_rows(kp, graph_rows, stream)) != hipSuccess) return hip_fail(err, e, "rows kernel launch");
   if (long_hist && (e = launch_hist_list(ka, stream)) != hipSuccess)
     return hip_fail(err, e, "history count kernel launch");
+  if (streamed) {
+    // the streaming kernel, then the row kernel on the rows it left (their
+    // count read on the device; nothing to do when it left none)
+    kp.defer_rows = ws.defer_rows;
+    kp.defer_word = ws.defer_word;
+    const int grid = n < ws.stream_resident ? n : ws.stream_resident;
+    e = launch_stream(ka, a->dtype, any_pen, grid, stream, ev0, nullptr);
+    if (e != hipSuccess) return hip_fail(err, e, "streaming kernel launch");
+    kp.n_rows_epoch = kp.epoch;
+    kp.n_rows_word = ws.defer_word;
+    kp.rows = ws.defer_rows;
+    ws.epoch = (ws.epoch & 0x7FFFFFFFu) + 1u;
+    if (ws.epoch == 0x80000000u) ws.epoch = 1;
+    kp.epoch = ws.epoch;
+    e = launch_step(ka, a->dtype, any_pen, (flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream, nullptr, ev1);
+    if (e != hipSuccess) return hip_fail(err, e, "kernel launch");
+    return SAMPLER_OK;
+  }
   e = launch_step(ka, a->dtype, any_pen, (flags & SAMPLER_COOPERATIVE_LAUNCH) != 0, stream, ev0, ev1);
   if (e != hipSuccess) return hip_fail(err, e, "kernel launch");
   // [B] "Logprobs are temperature-scaled", the original-logprob switch: the
@@ -654,8 +726,10 @@ int run_path(int predicate_path, uint32_t flags) {
 
 bool flags_ok(uint32_t flags) {
   return !(flags & ~(SAMPLER_DETERMINISTIC | SAMPLER_FORCE_FILTERED | SAMPLER_COOPERATIVE_LAUNCH |
-                     SAMPLER_INVERSE_CDF | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL)) &&
-         __builtin_popcount(flags & (SAMPLER_FORCE_FILTERED | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL)) <= 1;
+                     SAMPLER_INVERSE_CDF | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL |
+                     SAMPLER_FORCE_STREAM | SAMPLER_NO_STREAM)) &&
+         __builtin_popcount(flags & (SAMPLER_FORCE_FILTERED | SAMPLER_FORCE_PATH_GREEDY | SAMPLER_FORCE_PATH_GUMBEL)) <= 1 &&
+         __builtin_popcount(flags & (SAMPLER_FORCE_STREAM | SAMPLER_NO_STREAM)) <= 1;
 }
 
 // ---------------------------------------------------------------- no-alloc scratch
@@ -817,6 +891,14 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
           hipSuccess)
         goto fail;
     }
+    if ((e = hipMalloc((void **)&ws.defer_rows, sizeof(RowParam) * (size_t)cfg->max_rows)) != hipSuccess) goto fail;
+    if ((e = hipMalloc((void **)&ws.defer_word, 256)) != hipSuccess) goto fail;
+    if ((e = hipMemset(ws.defer_word, 0, 256)) != hipSuccess) goto fail;
+    if ((e = stream_resident(cfg->device,
+                             stream_lds_bytes(ws.hash_slots, true,
+                                              cfg->max_vocab < kStreamMaxVocab ? cfg->max_vocab : kStreamMaxVocab),
+                             &ws.stream_resident)) != hipSuccess)
+      goto fail;
     for (int s = 0; s < kRing; ++s)
       if ((e = hipEventCreateWithFlags(&h->slot_done[s], hipEventDisableTiming)) != hipSuccess) goto fail;
     if ((e = hipDeviceSynchronize()) != hipSuccess) goto fail;
@@ -887,7 +969,13 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   st = plan_groups(h->ws, det, launch_is_light(a, h->cfg.flags), n, V, &G, &slice, &groups, h->err);
   if (st != SAMPLER_OK) return st;
   const bool any_pen = build_records(a, det, 0, n, h->recs.data());
-  place_records(h->recs.data(), n, groups, h->rank.data(), h->order.data(), rp);
+  // the streaming kernel when forced, or when the row kernel would walk its
+  // row groups through several rows each
+  const bool streamed = stream_eligible(h->ws, h->cfg.flags, a, h->recs.data(), n) &&
+                        ((h->cfg.flags & SAMPLER_FORCE_STREAM) || n > kStreamRowsPerGroup * groups);
+  if (a->kernel_out) *a->kernel_out = streamed ? 1 : 0;
+  if (streamed) stream_records(h->recs.data(), n, h->order.data(), rp);
+  else place_records(h->recs.data(), n, groups, h->rank.data(), h->order.data(), rp);
   hipError_t e;
   if (!inline_rows) {
     e = hipMemcpyAsync(dp, rp, sizeof(RowParam) * (size_t)n, hipMemcpyHostToDevice, stream);
@@ -899,7 +987,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   const bool prof = h->prof_n < h->prof_cap;
   st = plan_and_launch(h->ws, h->cfg.flags, h->cfg.wait_spin_limit, a, n, ka, dp, any_pen, path, stream, h->err,
                        nullptr, nullptr, prof ? h->prof[2 * h->prof_n] : nullptr,
-                       prof ? h->prof[2 * h->prof_n + 1] : nullptr);
+                       prof ? h->prof[2 * h->prof_n + 1] : nullptr, streamed);
   if (st == SAMPLER_OK && prof) ++h->prof_n;
   return st;
 }
@@ -960,6 +1048,7 @@ sampler_status sampler_step_noalloc(const sampler_step_args *a, uint32_t flags, 
   const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
   const int pred = choose_path(a, flags);
   if (a->path_out) *a->path_out = pred;
+  if (a->kernel_out) *a->kernel_out = 0;
   const int path = run_path(pred, flags);
   // rows in pieces of up to kArgRows, each one launch with its records in
   // the kernel arguments; the pieces share the scratch in stream order
@@ -1026,6 +1115,7 @@ sampler_status sampler_step_graph(sampler_handle *h, const sampler_step_args *a,
     return SAMPLER_EHIP;
   }
   if (a->path_out) *a->path_out = PATH_FILTERED;
+  if (a->kernel_out) *a->kernel_out = 0;
   DevRowArrays dev;
   dev.temperature = dp->temperature;
   dev.top_p = dp->top_p;

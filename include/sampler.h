@@ -100,6 +100,22 @@ typedef enum sampler_dtype {
  *     kept set otherwise), so the outputs equal the unforced step's. */
 #define SAMPLER_FORCE_PATH_GREEDY (1u << 4)
 #define SAMPLER_FORCE_PATH_GUMBEL (1u << 5)
+/* Kernel choice for steps that want only token ids and top logprobs of the
+ * sampled distribution (no probs, logprobs or logits processors, no
+ * SAMPLER_DETERMINISTIC or SAMPLER_INVERSE_CDF, vocab <= 524,288,
+ * histories of at most 4096 ids).  Such a step runs
+ * on a streaming kernel -- one workgroup per row, the row read from memory
+ * in passes instead of held in LDS, every row of the batch in flight at
+ * once -- when its rows outnumber the row kernel's row groups, which then
+ * would walk several rows each ([C] "best_of 与 n 的放大": forks multiply a
+ * step's rows).  A row that kernel cannot settle exactly is sampled by the
+ * row kernel in a second launch on the same stream.  The outputs follow the
+ * same definitions either way (the fp64 sums may round differently).
+ *   SAMPLER_FORCE_STREAM: use the streaming kernel for every such step.
+ *   SAMPLER_NO_STREAM: never use it.
+ * At most one of the two per handle. */
+#define SAMPLER_FORCE_STREAM (1u << 6)
+#define SAMPLER_NO_STREAM (1u << 7)
 
 typedef struct sampler_config {
   int32_t max_rows;            /* largest n_rows a step may pass (>= 1) */
@@ -115,7 +131,8 @@ typedef struct sampler_config {
   int32_t device;              /* HIP device ordinal */
   uint32_t flags;              /* SAMPLER_DETERMINISTIC | SAMPLER_COOPERATIVE_LAUNCH | SAMPLER_INVERSE_CDF |
                                   one of SAMPLER_FORCE_FILTERED, SAMPLER_FORCE_PATH_GREEDY,
-                                  SAMPLER_FORCE_PATH_GUMBEL */
+                                  SAMPLER_FORCE_PATH_GUMBEL | one of SAMPLER_FORCE_STREAM,
+                                  SAMPLER_NO_STREAM */
   int32_t max_bias_per_row;    /* largest bias_len + active stop_len of one row (0..512) */
   /* Bound of every wait of one workgroup for another, in polls of the group
    * word: 0 (the default) is ~2 s.  A wait that expires marks the step
@@ -248,6 +265,11 @@ typedef struct sampler_step_args {
    *     which reads their logits again and rewrites their logprobs.
    * probs and the sampled tokens do not depend on the mode. */
   int32_t logprob_mode;
+
+  /* Output (host, may be NULL): the kernel the step ran on: 0 the row
+   * kernel, 1 the streaming kernel, followed on the same stream by the row
+   * kernel for the rows it left (SAMPLER_FORCE_STREAM above). */
+  int32_t *kernel_out;
 } sampler_step_args;
 
 #define SAMPLER_LOGPROB_PROCESSED 0

@@ -207,7 +207,8 @@ def test_create_history_cap(lib):
 def test_create_rejects_two_force_flags(lib):
     h = ctypes.c_void_p()
     for flags in (dsts.FLAG_FORCE_FILTERED | dsts.FLAG_FORCE_PATH_GREEDY,
-                  dsts.FLAG_FORCE_PATH_GREEDY | dsts.FLAG_FORCE_PATH_GUMBEL, 1 << 9):
+                  dsts.FLAG_FORCE_PATH_GREEDY | dsts.FLAG_FORCE_PATH_GUMBEL,
+                  dsts.FLAG_FORCE_STREAM | dsts.FLAG_NO_STREAM, 1 << 9):
         cfg = dsts.Config(max_rows=4, max_vocab=1024, max_history_per_row=0, max_top_logprobs=0, device=0,
                           flags=flags)
         assert lib.sampler_create(ctypes.byref(cfg), ctypes.byref(h)) == dsts.SAMPLER_EINVAL
