@@ -676,8 +676,9 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
     // count read on the device; nothing to do when it left none)
     kp.defer_rows = ws.defer_rows;
     kp.defer_word = ws.defer_word;
-    const int grid = n < ws.stream_resident ? n : ws.stream_resident;
-    e = launch_stream(ka, a->dtype, any_pen, grid, stream, ev0, nullptr);
+    // one workgroup per row: the dispatcher starts each as a slot frees, so
+    // the costlier rows (placed first) do not hold up a fixed set of others
+    e = launch_stream(ka, a->dtype, any_pen, n, stream, ev0, nullptr);
     if (e != hipSuccess) return hip_fail(err, e, "streaming kernel launch");
     kp.n_rows_epoch = kp.epoch;
     kp.n_rows_word = ws.defer_word;
