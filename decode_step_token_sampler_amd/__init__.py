@@ -477,7 +477,7 @@ class Sampler:
         if st != SAMPLER_OK:
             raise SamplerError(st, self.last_error())
         o["path"] = PATH_NAMES[path.value]
-        o["kernel"] = "stream" if keep[2].value == 1 else "row"
+        o["kernel"] = {0: "row", 1: "stream", 2: "small"}[keep[2].value]
         del keep
         return o
 

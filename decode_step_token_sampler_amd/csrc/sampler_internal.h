@@ -295,6 +295,10 @@ hipError_t launch_stream(const KernelArgs &ka, int dtype, bool penalties, int gr
 // the device at once.
 size_t stream_lds_bytes(int hash_slots, bool penalties, int vocab);
 hipError_t stream_resident(int device, size_t lds_bytes, int *out);
+// Rows of at most kSmallV values that keep every value (no truncation,
+// penalties, processors or top-logprob list): one small workgroup per row.
+constexpr int kSmallV = 4096;
+hipError_t launch_small(const KernelArgs &ka, int dtype, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);

@@ -4133,6 +4133,206 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
   }
 }
 
+// ---------------------------------------------------------------- small rows
+// Rows of at most kSmallV values that keep every value -- Gumbel-max over
+// the whole row, or greedy ([A] "Nine lines, and exactly one call site": the
+// path with no truncation) -- with no penalties, logits processors or
+// top-logprob list.  The row kernel's general machinery (tables, exchanges,
+// candidate lists) is all latency for them: here one workgroup of
+// kSmallBlock threads takes a row with every value in registers, and the
+// row's steps meet at a handful of workgroup barriers.  The arithmetic is
+// the row kernel's: z = x / T correctly rounded, the first argmax, the fp64
+// sum of exp(z - m) (in another order, so it may round differently), the
+// linear-domain bound, fp64 Gumbel scores, lp = fl32(z - m - ln S) and
+// p = 2^(lp log2 e).
+constexpr int kSmallBlock = 256;
+constexpr int kSmallG = kSmallV / 4 / kSmallBlock;  // groups of four per thread
+static_assert(kSmallV % (4 * kSmallBlock) == 0, "whole groups per thread");
+
+template <typename TIn>
+__global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
+  const KernelParams &kp = ka.kp;
+  constexpr int kW = kSmallBlock / 64;
+  __shared__ unsigned long long red_u[kW];
+  __shared__ double red_d[kW];
+  __shared__ int red_i[kW];
+  const int tid = tidx();
+  const int lane = tid & 63, wave = tid >> 6;
+  const RowParam P = kp.rows ? kp.rows[blockIdx.x] : ka.rows[blockIdx.x];
+  const int row = P.row;
+  const int V = kp.vocab;
+  const float T = P.temperature;
+  const float rT = 1.0f / T;
+  const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
+  const uint32_t xhi_b = min(__float_as_uint(T * 0x1p99f), 0x7F7FFFFFu);
+  const int64_t rbase = (int64_t)row * kp.row_stride;
+  const bool vec = kp.vec_ok & 1;
+  const bool gumbel = !(P.flags & RF_TOP1) && kp.path != PATH_GREEDY;
+  const int lastg = (V - 1) & ~3;
+  // the values: group u of this thread starts at 4 (tid + kSmallBlock u)
+  float z[kSmallG][4];
+#pragma unroll
+  for (int u = 0; u < kSmallG; ++u) {
+    const int l = 4 * (tid + kSmallBlock * u);
+    if (vec) {
+      Loader<TIn>::load4(kp.logits, rbase + min(l, lastg), z[u]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) z[u][c] = Loader<TIn>::load1(kp.logits, rbase + min(l + c, V - 1));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kSmallG; ++u) {
+    const int l = 4 * (tid + kSmallBlock * u);
+    uint32_t a[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(z[u][c]) & 0x7FFFFFFFu;
+    const bool fast = (max(max(a[0], a[1]), max(a[2], a[3])) <= xhi_b) & (min(min(a[0], a[1]), min(a[2], a[3])) >= xlo_b);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const float x = z[u][c];
+      const float q = x * rT;
+      float zz = __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q);
+      if (!fast) zz = (x == x ? x : -INFINITY) / T + 0.0f;
+      z[u][c] = l + c < V ? zz : -INFINITY;
+    }
+  }
+  // the row max and its first index (the best group by a strict compare,
+  // groups in index order, then the first match in it)
+  float lmax = -INFINITY;
+  int lidx = 0x7FFFFFFF;
+#pragma unroll
+  for (int u = 0; u < kSmallG; ++u) {
+    const float gm = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
+    if (gm > lmax) {
+      lmax = gm;
+      lidx = 4 * (tid + kSmallBlock * u) + (z[u][0] == gm ? 0 : z[u][1] == gm ? 1 : z[u][2] == gm ? 2 : 3);
+    }
+  }
+  unsigned long long mk = wave_max_u(((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx));
+  if (lane == 0) red_u[wave] = mk;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW; ++w) mk = red_u[w] > mk ? red_u[w] : mk;
+  const float mf = key_to_float((uint32_t)(mk >> 32));
+  const int argmax = (int)(0xFFFFFFFFu - (uint32_t)mk);
+  const bool want_out = kp.probs != nullptr || kp.logprobs != nullptr;
+  if (!(mf > -INFINITY && mf < INFINITY)) {  // no finite value (status 1) or a +inf value (status 2)
+    if (want_out)
+      for (int l = tid; l < V; l += kSmallBlock) {
+        if (kp.probs) kp.probs[(int64_t)row * V + l] = 0.0f;
+        if (kp.logprobs) kp.logprobs[(int64_t)row * V + l] = -INFINITY;
+      }
+    if (tid == 0) {
+      kp.token_ids[row] = -1;
+      if (kp.row_status) kp.row_status[row] = mf == INFINITY ? 2 : 1;
+    }
+    return;
+  }
+  const double m = (double)mf;
+  // the normaliser: the fp64 sum of exp(z - m) (per thread in index order,
+  // then across the wave and the waves in a fixed order)
+  double lnS = 0.0;
+  if (want_out) {
+    double sx = 0.0;
+#pragma unroll
+    for (int u = 0; u < kSmallG; ++u)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) sx += exp_term(z[u][c], m);
+    sx = wave_sum_d(sx);
+    if (lane == 0) red_d[wave] = sx;
+    __syncthreads();
+    double t = red_d[0];
+#pragma unroll
+    for (int w = 1; w < kW; ++w) t += red_d[w];
+    lnS = log(t);
+  }
+  // Gumbel-max: the argmax's draw seeds the bound (the argmax scores 1 / E);
+  // groups within the listing cut draw, values that pass the linear-domain
+  // bound get the exact fp64 score; ties go to the smaller index
+  double best_g = -INFINITY;
+  int best_i = 0x7FFFFFFF;
+  if (gumbel) {
+    const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
+    const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
+    uint32_t w4[4];
+    philox4x32_10((uint32_t)argmax >> 2, P.stream, off0, off1, key0, key1, w4);
+    float bound = (float)(1.0 / exp1_f64(w4[argmax & 3])) * 0.99999f;
+    const float cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
+#pragma unroll
+    for (int u = 0; u < kSmallG; ++u) {
+      const int i0 = 4 * (tid + kSmallBlock * u);
+      const float gm = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
+      if (i0 < V && mf - gm <= cut) {
+        uint32_t w[4];
+        philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
+        uint32_t surv = 0;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const float wl = (float)w[c] * 0x1.fffffcp-33f;
+          const float qv = __builtin_amdgcn_exp2f((z[u][c] - mf) * kLog2e);
+          surv |= (mf - z[u][c] <= cut && wl * bound <= qv * kSlack) ? 1u << c : 0u;
+        }
+        while (surv) {
+          const int c = __builtin_ctz(surv);
+          surv &= surv - 1u;
+          const float zc = c == 0 ? z[u][0] : c == 1 ? z[u][1] : c == 2 ? z[u][2] : z[u][3];
+          const uint32_t wc = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
+          const double ge = (double)zc - log(exp1_f64(wc));
+          if (ge > best_g || (ge == best_g && i0 + c < best_i)) {
+            best_g = ge;
+            best_i = i0 + c;
+            bound = fmaxf(bound, (float)exp(best_g - m) * 0.99999f);
+          }
+        }
+      }
+    }
+    wave_best(best_g, best_i);
+    if (lane == 0) {
+      red_d[wave] = best_g;
+      red_i[wave] = best_i;
+    }
+    __syncthreads();
+    best_g = red_d[0];
+    best_i = red_i[0];
+#pragma unroll
+    for (int w = 1; w < kW; ++w)
+      if (red_d[w] > best_g || (red_d[w] == best_g && red_i[w] < best_i)) {
+        best_g = red_d[w];
+        best_i = red_i[w];
+      }
+  }
+  if (tid == 0) {
+    kp.token_ids[row] = gumbel ? best_i : argmax;
+    if (kp.row_status) kp.row_status[row] = 0;
+  }
+  // outputs: every value is kept
+  if (want_out) {
+#pragma unroll
+    for (int u = 0; u < kSmallG; ++u) {
+      const int l = 4 * (tid + kSmallBlock * u);
+      float lv[4], pv[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        lv[c] = z[u][c] > -INFINITY ? (float)(((double)z[u][c] - m) - lnS) : -INFINITY;
+        pv[c] = z[u][c] > -INFINITY ? __builtin_amdgcn_exp2f(lv[c] * kLog2e) : 0.0f;
+      }
+      const int64_t o = (int64_t)row * V + l;
+      if ((kp.vec_ok & 2) && l + 3 < V) {
+        if (kp.probs) *reinterpret_cast<f32x4 *>(kp.probs + o) = f32x4{pv[0], pv[1], pv[2], pv[3]};
+        if (kp.logprobs) *reinterpret_cast<f32x4 *>(kp.logprobs + o) = f32x4{lv[0], lv[1], lv[2], lv[3]};
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+          if (l + c < V) {
+            if (kp.probs) kp.probs[o + c] = pv[c];
+            if (kp.logprobs) kp.logprobs[o + c] = lv[c];
+          }
+      }
+    }
+  }
+}
+
 template <typename TIn, bool PEN>
 hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const KernelParams &kp = ka.kp;
@@ -4256,6 +4456,13 @@ hipError_t stream_resident(int device, size_t lds_bytes, int *out) {
   if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return e;
   *out = pc * prop.multiProcessorCount;
   return hipSuccess;
+}
+
+hipError_t launch_small(const KernelArgs &ka, int dtype, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const void *fn = dtype == 0 ? reinterpret_cast<const void *>(&small_kernel<float>)
+                              : reinterpret_cast<const void *>(&small_kernel<uint16_t>);
+  void *args[] = {const_cast<KernelArgs *>(&ka)};
+  return hipExtLaunchKernel(fn, dim3(ka.kp.n_rows), dim3(kSmallBlock), args, 0, stream, ev0, ev1, 0);
 }
 
 hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream) {

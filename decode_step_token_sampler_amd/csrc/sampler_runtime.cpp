@@ -13,6 +13,7 @@
 //   [C] "采样参数对解码开销的影响：temperature、top_p 与采样核路径"
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -563,6 +564,20 @@ bool stream_eligible(const Workspace &ws, uint32_t flags, const sampler_step_arg
   return true;
 }
 
+// Whether a step may run on the small-row kernel: at most kSmallV values per
+// row, every row keeping every value (Gumbel-max or greedy), no penalties,
+// processors or top-logprob list, logprobs of the sampled distribution
+// (the raw mode differs at T != 1).  The forced-filtered A/B switch and the
+// deterministic and inverse-CDF modes keep the row kernel.
+bool small_eligible(uint32_t flags, const sampler_step_args *a, const RowParam *recs, int n) {
+  if (flags & (SAMPLER_DETERMINISTIC | SAMPLER_INVERSE_CDF | SAMPLER_FORCE_FILTERED)) return false;
+  if (a->vocab > kSmallV || a->top_logprobs > 0 || a->vocab_mask) return false;
+  if (a->logprobs && a->logprob_mode == SAMPLER_LOGPROB_RAW) return false;
+  for (int r = 0; r < n; ++r)
+    if (recs[r].flags & (RF_TOPK | RF_TOPP | RF_MINP | RF_PEN | RF_SPEC)) return false;
+  return true;
+}
+
 // Cost class of a row on the streaming kernel (larger: longer): rows that
 // keep every value run Philox over the whole row; top-p without top-k keeps
 // the most values; argmax rows read the row once.
@@ -596,7 +611,8 @@ void stream_records(const RowParam *recs, int n, int *ord, RowParam *out) {
 sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_limit, const sampler_step_args *a,
                                int n, KernelArgs &ka, const RowParam *dp, bool any_pen, int path, hipStream_t stream,
                                std::string &err, const DevRowArrays *dev = nullptr, RowParam *graph_rows = nullptr,
-                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool streamed = false) {
+                               hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool streamed = false,
+                               bool small = false) {
   const int V = a->vocab;
   const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
   hipError_t e;
@@ -671,6 +687,11 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   if (dev && (e = launch_rows(kp, graph_rows, stream)) != hipSuccess) return hip_fail(err, e, "rows kernel launch");
   if (long_hist && (e = launch_hist_list(ka, stream)) != hipSuccess)
     return hip_fail(err, e, "history count kernel launch");
+  if (small) {
+    e = launch_small(ka, a->dtype, stream, ev0, ev1);
+    if (e != hipSuccess) return hip_fail(err, e, "small-row kernel launch");
+    return SAMPLER_OK;
+  }
   if (streamed) {
     // the streaming kernel, then the row kernel on the rows it left (their
     // count read on the device; nothing to do when it left none)
@@ -972,10 +993,12 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   const bool any_pen = build_records(a, det, 0, n, h->recs.data());
   // the streaming kernel when forced, or when the row kernel would walk its
   // row groups through several rows each
-  const bool streamed = stream_eligible(h->ws, h->cfg.flags, a, h->recs.data(), n) &&
+  const bool small = small_eligible(h->cfg.flags, a, h->recs.data(), n);
+  const bool streamed = !small && stream_eligible(h->ws, h->cfg.flags, a, h->recs.data(), n) &&
                         ((h->cfg.flags & SAMPLER_FORCE_STREAM) || n > kStreamRowsPerGroup * groups);
-  if (a->kernel_out) *a->kernel_out = streamed ? 1 : 0;
+  if (a->kernel_out) *a->kernel_out = small ? 2 : streamed ? 1 : 0;
   if (streamed) stream_records(h->recs.data(), n, h->order.data(), rp);
+  else if (small) std::copy(h->recs.data(), h->recs.data() + n, rp);
   else place_records(h->recs.data(), n, groups, h->rank.data(), h->order.data(), rp);
   hipError_t e;
   if (!inline_rows) {
@@ -988,7 +1011,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   const bool prof = h->prof_n < h->prof_cap;
   st = plan_and_launch(h->ws, h->cfg.flags, h->cfg.wait_spin_limit, a, n, ka, dp, any_pen, path, stream, h->err,
                        nullptr, nullptr, prof ? h->prof[2 * h->prof_n] : nullptr,
-                       prof ? h->prof[2 * h->prof_n + 1] : nullptr, streamed);
+                       prof ? h->prof[2 * h->prof_n + 1] : nullptr, streamed, small);
   if (st == SAMPLER_OK && prof) ++h->prof_n;
   return st;
 }

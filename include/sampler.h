@@ -268,7 +268,12 @@ typedef struct sampler_step_args {
 
   /* Output (host, may be NULL): the kernel the step ran on: 0 the row
    * kernel, 1 the streaming kernel, followed on the same stream by the row
-   * kernel for the rows it left (SAMPLER_FORCE_STREAM above). */
+   * kernel for the rows it left (SAMPLER_FORCE_STREAM above), 2 the
+   * small-row kernel: steps of at most 4096 values per row whose every row
+   * keeps every value (Gumbel-max or greedy; no penalties, logits
+   * processors or top_logprobs; not the raw logprob mode, not
+   * SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF or SAMPLER_FORCE_FILTERED)
+   * take one small workgroup per row. */
   int32_t *kernel_out;
 } sampler_step_args;
 
