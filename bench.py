@@ -272,6 +272,11 @@ NOT_TIMES = ("listed_n", "row_index", "g_rounds")
 
 
 ROW_INDEX_SLOT = 19  # PHASES[19]
+ROW_SLOTS = tuple((name, k) for k, name in enumerate(PHASES))
+# the streaming kernel's stamps: its own start slot, the rest in slots of
+# the row kernel's list
+STREAM_SLOTS = (("start", 29), ("row", 1), ("hashed", 27), ("pass_a", 3), ("pass_b", 4), ("ranges", 6),
+                ("pass_c", 7), ("sorted", 24), ("decided", 9), ("end", 12), ("row_index", 19))
 
 
 def row_class(b, r):
@@ -290,24 +295,26 @@ def row_class(b, r):
     return "+".join(n for n, on in (("top-k", topk), ("top-p", topp), ("min-p", minp)) if on)
 
 
-def phase_by_class(stamps_runs, khz):
+def phase_by_class(stamps_runs, khz, slots=ROW_SLOTS):
     """Per row class: the median over steps and workgroups of the time since
     the kernel's first stamp at which the workgroups' rows pass each phase
     (us), the largest end time, and the number of distinct rows seen.
-    stamps_runs: (stamps, batch) of each step."""
+    stamps_runs: (stamps, batch) of each step; slots: (phase, slot) pairs,
+    the kernel's start first."""
     acc = {}
+    s0 = slots[0][1]
     for st, b in stamps_runs:
-        used = st[:, 0] != 0
+        used = st[:, s0] != 0
         if not used.any():
             continue
-        t0 = float(st[used, 0].min())
+        t0 = float(st[used, s0].min())
         for blk in np.flatnonzero(used):
             r = int(st[blk, ROW_INDEX_SLOT]) - 1
             if r < 0:
                 continue
             c = acc.setdefault(row_class(b, r), {"rows": set(), "phases": {}})
             c["rows"].add(r)
-            for k, name in enumerate(PHASES):
+            for name, k in slots:
                 if st[blk, k] and name != "row_index":
                     v = float(st[blk, k]) if name in NOT_TIMES else (float(st[blk, k]) - t0) * 1e3 / khz
                     c["phases"].setdefault(name, []).append(v)
@@ -318,22 +325,23 @@ def phase_by_class(stamps_runs, khz):
                     "select_us": float(np.median(ph["select"])) if "select" in ph else None,
                     "end_us": float(np.median(ph["end"])) if "end" in ph else None,
                     "end_max_us": float(np.max(ph["end"])) if "end" in ph else None,
-                    "phases_median_us": {name: float(np.median(ph[name])) for name in PHASES if name in ph}}
+                    "phases_median_us": {name: float(np.median(ph[name])) for name, _ in slots if name in ph}}
     return out
 
 
-def phase_timeline(stamps_runs, khz):
+def phase_timeline(stamps_runs, khz, slots=ROW_SLOTS):
     """Per phase: the median over steps of the median and the maximum over
     workgroups of the time since the kernel's first stamp (us), and the
     number of workgroups that passed it.  A phase a row skipped has no
-    stamp."""
-    per = {name: {"median_us": [], "max_us": [], "workgroups": 0} for name in PHASES}
+    stamp.  slots: (phase, slot) pairs, the kernel's start first."""
+    per = {name: {"median_us": [], "max_us": [], "workgroups": 0} for name, _ in slots}
+    s0 = slots[0][1]
     for st, _ in stamps_runs:
-        used = st[:, 0] != 0
+        used = st[:, s0] != 0
         if not used.any():
             continue
-        t0 = st[used, 0].min()
-        for k, name in enumerate(PHASES):
+        t0 = st[used, s0].min()
+        for name, k in slots:
             col = st[used, k]
             col = col[col != 0]
             if col.size == 0 or name in NOT_TIMES:
@@ -410,9 +418,10 @@ def main():
             st, khz = dsts.phase_stamps()
             if i >= args.warmup:
                 runs.append((st, batches[i % n_sets]))
-        print(json.dumps({"workload": desc, "path": r["path"], "steps": args.steps, "clock_khz": khz,
-                          "phases_us_since_kernel_start": phase_timeline(runs, khz),
-                          "by_row_class": phase_by_class(runs, khz)}), flush=True)
+        slots = STREAM_SLOTS if r["kernel"] == "stream" else ROW_SLOTS
+        print(json.dumps({"workload": desc, "path": r["path"], "kernel": r["kernel"] + "_kernel", "steps": args.steps, "clock_khz": khz,
+                          "phases_us_since_kernel_start": phase_timeline(runs, khz, slots),
+                          "by_row_class": phase_by_class(runs, khz, slots)}), flush=True)
         S.close()
         return
     for i in range(args.warmup):
@@ -484,6 +493,7 @@ def main():
             // 10**6),
         "config": {"workload": desc, "n_rows": n, "vocab": V,
                    "history_per_row": 2048 if b0.history_ids is not None else 0, "path": r["path"],
+                   "kernel": r["kernel"] + "_kernel",
                    "algorithmic_bytes_per_step": alg_bytes},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": achieved / HBM_PEAK_GBS, "traffic": measured_traffic() if headline else None},

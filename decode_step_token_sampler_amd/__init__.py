@@ -477,7 +477,7 @@ class Sampler:
         if st != SAMPLER_OK:
             raise SamplerError(st, self.last_error())
         o["path"] = PATH_NAMES[path.value]
-        o["kernel"] = {0: "row", 1: "stream", 2: "small"}[keep[2].value]
+        o["kernel"] = {0: "row", 1: "stream", 2: "small", 3: "chunk"}[keep[2].value]
         del keep
         return o
 

@@ -194,6 +194,7 @@ struct DevRowArrays {
   const int32_t *min_tokens, *output_len;
 };
 
+struct ChunkRec;
 struct KernelParams {
   const void *logits;
   int64_t row_stride;
@@ -252,6 +253,12 @@ struct KernelParams {
   // (count of epoch n_rows_epoch, else 0) instead of n_rows
   const unsigned long long *n_rows_word;
   uint32_t n_rows_epoch;
+  // chunked rows (chunk_kernel): chunk_n chunks of 4 kChunkBlock chunk_u
+  // values per row; record r's chunk c result at chunk_recs[r chunk_stride +
+  // c], its arrival word at chunk_words[kChunkWordStride r]
+  ChunkRec *chunk_recs;
+  unsigned long long *chunk_words;
+  int32_t chunk_n, chunk_u, chunk_stride;
 };
 
 // Batches of up to kArgRows rows carry their per-row records in the kernel
@@ -299,6 +306,24 @@ hipError_t stream_resident(int device, size_t lds_bytes, int *out);
 // penalties, processors or top-logprob list): one small workgroup per row.
 constexpr int kSmallV = 4096;
 hipError_t launch_small(const KernelArgs &ka, int dtype, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
+// Longer rows of that kind in a step that wants only token ids: one
+// workgroup of kChunkBlock threads per chunk of 4 kChunkBlock U values
+// (U = 1, 2 or 4), at most kChunkMax chunks per row; the last chunk of a row
+// to arrive merges the chunks' results.
+constexpr int kChunkBlock = 256;
+constexpr int kChunkMaxU = 4;
+constexpr int kChunkMax = 256;
+constexpr int kChunkMaxV = 4 * kChunkBlock * kChunkMaxU * kChunkMax;
+constexpr int kChunkWordStride = 16;  // arrival words 128 bytes apart
+// One chunk's result.  Gumbel-max rows: a = its best score (fp64 bits), b =
+// status << 32 | that score's index (status 1: no finite value in the
+// chunk, 2: a +inf value).  Greedy rows: a = the order key of its max
+// (order key << 32 | ~first index).
+struct alignas(16) ChunkRec {
+  unsigned long long a;
+  unsigned long long b;
+};
+hipError_t launch_chunk(const KernelArgs &ka, int dtype, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1);
 // Workgroups of the row kernel that fit on the device at once for a given
 // dynamic LDS size.
 hipError_t resident_blocks(int device, size_t lds_bytes, int *out);

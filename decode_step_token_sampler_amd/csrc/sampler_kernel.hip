@@ -4149,6 +4149,25 @@ constexpr int kSmallBlock = 256;
 constexpr int kSmallG = kSmallV / 4 / kSmallBlock;  // groups of four per thread
 static_assert(kSmallV % (4 * kSmallBlock) == 0, "whole groups per thread");
 
+// z = x / T, correctly rounded, of the group of four raw values at index l
+// (in place); NaN gives -inf, indices from V on give -inf.  Values whose
+// magnitude lies in [T 2^-99, T 2^99] (xlo_b, xhi_b: those bounds' bits)
+// take one reciprocal product and one fma correction, others the division.
+DEV void temper4(float (&v)[4], int l, int V, float T, float rT, uint32_t xlo_b, uint32_t xhi_b) {
+  uint32_t a[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(v[c]) & 0x7FFFFFFFu;
+  const bool fast = (max(max(a[0], a[1]), max(a[2], a[3])) <= xhi_b) & (min(min(a[0], a[1]), min(a[2], a[3])) >= xlo_b);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float x = v[c];
+    const float q = x * rT;
+    float zz = __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q);
+    if (!fast) zz = (x == x ? x : -INFINITY) / T + 0.0f;
+    v[c] = l + c < V ? zz : -INFINITY;
+  }
+}
+
 template <typename TIn>
 __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   const KernelParams &kp = ka.kp;
@@ -4182,21 +4201,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < kSmallG; ++u) {
-    const int l = 4 * (tid + kSmallBlock * u);
-    uint32_t a[4];
-#pragma unroll
-    for (int c = 0; c < 4; ++c) a[c] = __float_as_uint(z[u][c]) & 0x7FFFFFFFu;
-    const bool fast = (max(max(a[0], a[1]), max(a[2], a[3])) <= xhi_b) & (min(min(a[0], a[1]), min(a[2], a[3])) >= xlo_b);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const float x = z[u][c];
-      const float q = x * rT;
-      float zz = __builtin_fmaf(__builtin_fmaf(-q, T, x), rT, q);
-      if (!fast) zz = (x == x ? x : -INFINITY) / T + 0.0f;
-      z[u][c] = l + c < V ? zz : -INFINITY;
-    }
-  }
+  for (int u = 0; u < kSmallG; ++u) temper4(z[u], 4 * (tid + kSmallBlock * u), V, T, rT, xlo_b, xhi_b);
   // the row max and its first index (the best group by a strict compare,
   // groups in index order, then the first match in it)
   float lmax = -INFINITY;
@@ -4333,6 +4338,235 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   }
 }
 
+// ---------------------------------------------------------------- chunked rows
+// Rows longer than kSmallV of the same kind (every value kept, Gumbel-max or
+// greedy, no penalties, processors or top-logprob list) in a step that wants
+// only token ids.  Neither the normaliser nor the row max is needed for
+// that: the Gumbel-max winner is the first index of the largest fp64 score
+// z - ln E ([A] "Nine lines, and exactly one call site"), greedy's the first
+// index of the largest z.  So each workgroup scores one chunk of the row on
+// its own and the last chunk of the row to arrive merges the chunks' bests.
+// No workgroup waits for another.
+// ln E in fp32 for the word x, E = -ln(1 - w), w = (x + 1/2) 2^-32 (the
+// draw of exp1_f64), for ranking only: below w = 1/16 by the series of
+// -ln(1 - w) to w^6 (relative truncation below 1e-8), above it from 1 - w
+// taken from the complement of x (relative error 6e-8, so E's relative error
+// stays below 3e-6 where -ln(1 - w) >= 1/16).  The result is within 1e-5 of
+// ln E; kChunkMargin leaves a hundredfold slack for two scores' errors.
+DEV float ln_exp1_f32(uint32_t x) {
+  const float w = ((float)x + 0.5f) * 0x1p-32f;
+  const float q = ((float)(0xFFFFFFFFu - x) + 0.5f) * 0x1p-32f;
+  const float es = w * (1.0f + w * (0.5f + w * (1.0f / 3.0f + w * (0.25f + w * (0.2f + w * (1.0f / 6.0f))))));
+  const float el = -__logf(q);
+  return __logf(w < 0.0625f ? es : el);  // (both sides computed: no branch)
+}
+constexpr float kChunkMargin = 0x1p-10f;
+// Order keys of fp64 values (larger value, larger key; -0 < +0), and back.
+DEV unsigned long long dkey(double d) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+DEV double key_to_double(unsigned long long k) {
+  return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
+template <typename TIn>
+__global__ __launch_bounds__(kChunkBlock) void chunk_kernel(KernelArgs ka) {
+  const KernelParams &kp = ka.kp;
+  constexpr int kW = kChunkBlock / 64;
+  __shared__ unsigned long long red_u[kW];
+  __shared__ int red_i[kW];
+  __shared__ uint32_t last_s;
+  __shared__ unsigned long long best_key_s;
+  __shared__ int best_idx_s;
+  const int tid = tidx();
+  const int lane = tid & 63, wave = tid >> 6;
+  const int ri = blockIdx.y;   // the record
+  const int ch = blockIdx.x;   // the chunk
+  const int U = kp.chunk_u;
+  const unsigned it = blockIdx.y;  // (stamps: the first row's chunks)
+  PHASE_STAMP(kStampStart);
+  const RowParam P = kp.rows ? kp.rows[ri] : ka.rows[ri];
+  const int row = P.row;
+  PHASE_STAMP(kStampRow);
+  PHASE_RECORD(kStampRowIndex, row + 1);
+  const int V = kp.vocab;
+  const float T = P.temperature;
+  const float rT = 1.0f / T;
+  const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
+  const uint32_t xhi_b = min(__float_as_uint(T * 0x1p99f), 0x7F7FFFFFu);
+  const int64_t rbase = (int64_t)row * kp.row_stride;
+  const bool vec = kp.vec_ok & 1;
+  const bool gumbel = !(P.flags & RF_TOP1) && kp.path != PATH_GREEDY;
+  const int lastg = (V - 1) & ~3;
+  const int c0 = ch * 4 * kChunkBlock * U;  // the chunk's first index
+  // group u of this thread starts at c0 + 4 (tid + kChunkBlock u)
+  float z[kChunkMaxU][4];
+#pragma unroll
+  for (int u = 0; u < kChunkMaxU; ++u) {
+    if (u >= U) break;
+    const int l = c0 + 4 * (tid + kChunkBlock * u);
+    if (vec) {
+      Loader<TIn>::load4(kp.logits, rbase + min(l, lastg), z[u]);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) z[u][c] = Loader<TIn>::load1(kp.logits, rbase + min(l + c, V - 1));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kChunkMaxU; ++u) {
+    if (u >= U) break;
+    temper4(z[u], c0 + 4 * (tid + kChunkBlock * u), V, T, rT, xlo_b, xhi_b);
+  }
+  PHASE_STAMP(kStampLoaded);
+  // the chunk's max and its first index
+  float lmax = -INFINITY;
+  int lidx = 0x7FFFFFFF;
+#pragma unroll
+  for (int u = 0; u < kChunkMaxU; ++u) {
+    if (u >= U) break;
+    const float gm = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
+    if (gm > lmax) {
+      lmax = gm;
+      lidx = c0 + 4 * (tid + kChunkBlock * u) + (z[u][0] == gm ? 0 : z[u][1] == gm ? 1 : z[u][2] == gm ? 2 : 3);
+    }
+  }
+  unsigned long long mk = wave_max_u(((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx));
+  if (lane == 0) red_u[wave] = mk;
+  __syncthreads();
+#pragma unroll
+  for (int w = 0; w < kW; ++w) mk = red_u[w] > mk ? red_u[w] : mk;
+  const float mf = key_to_float((uint32_t)(mk >> 32));
+  const int amax = (int)(0xFFFFFFFFu - (uint32_t)mk);
+  PHASE_STAMP(kStampMax);
+  // Gumbel-max within the chunk: every finite value gets an fp32 score, and
+  // the values within kChunkMargin of the chunk's best fp32 score get the
+  // exact fp64 score z - ln E; the best of those (ties: the smaller index)
+  // through two LDS atomics
+  double best_g = -INFINITY;
+  int best_i = 0x7FFFFFFF;
+  const uint32_t cst = mf == INFINITY ? 2u : mf > -INFINITY ? 0u : 1u;  // +inf / no finite value
+  if (gumbel && cst == 0u) {
+    const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
+    const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
+    float g32[kChunkMaxU][4];
+    uint32_t wv[kChunkMaxU][4];
+    float gmx = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < kChunkMaxU; ++u) {
+      if (u >= U) break;
+      const int i0 = c0 + 4 * (tid + kChunkBlock * u);
+      const float gm = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
+      if (i0 < V && gm > -INFINITY) {
+        philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, wv[u]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          g32[u][c] = z[u][c] - ln_exp1_f32(wv[u][c]);  // (-inf stays -inf)
+          gmx = fmaxf(gmx, g32[u][c]);
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g32[u][c] = -INFINITY;
+      }
+    }
+    PHASE_STAMP(kStampGumbelListed);
+    // the chunk's best fp32 score (finite: the chunk max is finite)
+    uint32_t gk = lane63_u32(wave_scanmax_u32(fkey(gmx)));
+    if (lane == 0) red_i[wave] = (int)gk;
+    if (tid == 0) {
+      best_key_s = 0ull;
+      best_idx_s = 0x7FFFFFFF;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kW; ++w) gk = max(gk, (uint32_t)red_i[w]);
+    const float G32 = key_to_float(gk);
+    const float thr = G32 - (kChunkMargin + fabsf(G32) * 0x1p-20f);
+    double tg = -INFINITY;
+    int ti = 0x7FFFFFFF;
+#pragma unroll
+    for (int u = 0; u < kChunkMaxU; ++u) {
+      if (u >= U) break;
+      const int i0 = c0 + 4 * (tid + kChunkBlock * u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (g32[u][c] >= thr) {
+          const double ge = ((double)z[u][c] - log(exp1_f64(wv[u][c]))) + 0.0;  // (+0 for -0)
+          if (ge > tg || (ge == tg && i0 + c < ti)) {
+            tg = ge;
+            ti = i0 + c;
+          }
+        }
+    }
+    PHASE_STAMP(kStampGumbelBatched);
+    const unsigned long long tk = dkey(tg);
+    if (ti != 0x7FFFFFFF) atomicMax(&best_key_s, tk);
+    __syncthreads();
+    const unsigned long long bk = best_key_s;
+    if (ti != 0x7FFFFFFF && tk == bk) atomicMin(&best_idx_s, ti);
+    __syncthreads();
+    best_g = key_to_double(bk);
+    best_i = best_idx_s;
+  }
+  PHASE_STAMP(kStampGumbel);
+  // the chunk's result (Gumbel-max rows: best fp64 score, its index and the
+  // chunk's status; greedy rows: the max's order key), then its arrival: one
+  // atomic add on the row's word, whose count the last chunk to arrive resets
+  // to zero for the next launch (every launch runs to its end: no chunk
+  // waits for another)
+  ChunkRec *recs = kp.chunk_recs + (int64_t)ri * kp.chunk_stride;
+  if (tid == 0) {
+    if (gumbel) {
+      atomic_st(&recs[ch].a, (unsigned long long)__double_as_longlong(best_g));
+      atomic_st(&recs[ch].b, ((unsigned long long)cst << 32) | (uint32_t)best_i);
+    } else {
+      atomic_st(&recs[ch].a, mk);
+    }
+    order_release();
+    PHASE_STAMP(kStampReleased);
+    unsigned long long *word = kp.chunk_words + (int64_t)kChunkWordStride * ri;
+    const unsigned long long old = __hip_atomic_fetch_add(word, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const bool last = old == (unsigned long long)(kp.chunk_n - 1);
+    if (last) {
+      atomic_st(word, 0ull);
+      order_acquire();
+    }
+    last_s = last ? 1u : 0u;
+    PHASE_STAMP(kStampArrived);
+  }
+  __syncthreads();
+  if (!last_s || wave != 0) return;
+  // the merge (one wave): lane l holds chunks l, l + 64, l + 128, l + 192,
+  // read in one round trip
+  const int C = kp.chunk_n;
+  u32x4 r[4];
+  coh_load16x4(&recs[min(lane, C - 1)], &recs[min(lane + 64, C - 1)], &recs[min(lane + 128, C - 1)],
+               &recs[min(lane + 192, C - 1)], r[0], r[1], r[2], r[3]);
+  unsigned long long k = 0;  // greedy: the max's order key; Gumbel-max: the row's status as a key
+  double g = -INFINITY;
+  int gi = 0x7FFFFFFF;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if (lane + 64 * t >= C) break;
+    if (gumbel) {
+      const double gj = f64_of(r[t].x, r[t].y);
+      const int ij = (int)r[t].z;
+      if (gj > g || (gj == g && ij < gi)) {
+        g = gj;
+        gi = ij;
+      }
+      const unsigned long long sk = (unsigned long long)fkey(r[t].w == 2u ? INFINITY : r[t].w == 1u ? -INFINITY : 0.0f)
+                                    << 32;
+      k = sk > k ? sk : k;
+    } else {
+      const unsigned long long kj = u64_of(r[t].x, r[t].y);
+      k = kj > k ? kj : k;
+    }
+  }
+  finish_row(kp, false, row, gumbel, false, k, g, gi, true);
+  if (lane == 0) PHASE_STAMP_ONE(kStampToken);
+}
+
 template <typename TIn, bool PEN>
 hipError_t launch_t(const KernelArgs &ka, bool cooperative, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
   const KernelParams &kp = ka.kp;
@@ -4463,6 +4697,13 @@ hipError_t launch_small(const KernelArgs &ka, int dtype, hipStream_t stream, hip
                               : reinterpret_cast<const void *>(&small_kernel<uint16_t>);
   void *args[] = {const_cast<KernelArgs *>(&ka)};
   return hipExtLaunchKernel(fn, dim3(ka.kp.n_rows), dim3(kSmallBlock), args, 0, stream, ev0, ev1, 0);
+}
+
+hipError_t launch_chunk(const KernelArgs &ka, int dtype, hipStream_t stream, hipEvent_t ev0, hipEvent_t ev1) {
+  const void *fn = dtype == 0 ? reinterpret_cast<const void *>(&chunk_kernel<float>)
+                              : reinterpret_cast<const void *>(&chunk_kernel<uint16_t>);
+  void *args[] = {const_cast<KernelArgs *>(&ka)};
+  return hipExtLaunchKernel(fn, dim3(ka.kp.chunk_n, ka.kp.n_rows), dim3(kChunkBlock), args, 0, stream, ev0, ev1, 0);
 }
 
 hipError_t launch_rows(const KernelParams &kp, RowParam *out, hipStream_t stream) {

@@ -45,6 +45,8 @@ constexpr uint64_t kDeterministicSeed = 42;
 // factor run on the streaming kernel (measured on MI355X: see the design
 // notes' streaming section).
 constexpr int kStreamRowsPerGroup = 1;
+// chunked rows: the chunks a launch aims at, above which chunks grow
+constexpr int64_t kChunkBatchGroups = 4096;
 
 thread_local std::string g_create_error;
 
@@ -82,6 +84,10 @@ struct Workspace {
   int stream_resident = 0;
   RowParam *defer_rows = nullptr;           // [max_rows]
   unsigned long long *defer_word = nullptr;
+  // chunked rows: per record chunk_cap chunk results and one arrival word
+  ChunkRec *chunk_recs = nullptr;           // [max_rows * chunk_cap]
+  unsigned long long *chunk_words = nullptr;  // [max_rows * kChunkWordStride]
+  int chunk_cap = 0;
   // limits the workspace was planned for
   int32_t max_history_per_row = 0, max_bias_per_row = 0, max_top_logprobs = 0, max_vocab = 0;
 };
@@ -326,6 +332,8 @@ void free_handle(sampler_handle *h) {
   if (h->ws.hist_list_n) (void)hipFree(h->ws.hist_list_n);
   if (h->ws.defer_rows) (void)hipFree(h->ws.defer_rows);
   if (h->ws.defer_word) (void)hipFree(h->ws.defer_word);
+  if (h->ws.chunk_recs) (void)hipFree(h->ws.chunk_recs);
+  if (h->ws.chunk_words) (void)hipFree(h->ws.chunk_words);
   delete h;
 }
 
@@ -578,6 +586,30 @@ bool small_eligible(uint32_t flags, const sampler_step_args *a, const RowParam *
   return true;
 }
 
+// Whether a step may run on the chunked-row kernel: rows longer than kSmallV
+// of the small-row kernel's kind, in a step that wants token ids (and row
+// status) only.  *U: groups of four per thread, *C: chunks per row (more
+// values per thread for batches of many chunks).
+bool chunk_eligible(const Workspace &ws, uint32_t flags, const sampler_step_args *a, const RowParam *recs, int n,
+                    int *U, int *C) {
+  if (flags & (SAMPLER_DETERMINISTIC | SAMPLER_INVERSE_CDF | SAMPLER_FORCE_FILTERED | SAMPLER_FORCE_STREAM))
+    return false;
+  if (!ws.chunk_recs || a->vocab <= kSmallV || a->vocab > kChunkMaxV) return false;
+  if (a->probs || a->logprobs || a->top_logprobs > 0 || a->vocab_mask) return false;
+  for (int r = 0; r < n; ++r)
+    if (recs[r].flags & (RF_TOPK | RF_TOPP | RF_MINP | RF_PEN | RF_SPEC)) return false;
+  const int64_t V = a->vocab;
+  auto chunks = [&](int uu) { return (V + 4 * kChunkBlock * uu - 1) / (4 * kChunkBlock * uu); };
+  // one group per thread up to 64 chunks a row, else at least two (the
+  // merge reads fewer records; measured on batch-1 rows of 151,936 values)
+  int u = chunks(1) > 64 ? 2 : 1;
+  while (u < kChunkMaxU && (chunks(u) > ws.chunk_cap || (int64_t)n * chunks(u) > kChunkBatchGroups)) u *= 2;
+  if (chunks(u) > ws.chunk_cap) return false;
+  *U = u;
+  *C = (int)chunks(u);
+  return true;
+}
+
 // Cost class of a row on the streaming kernel (larger: longer): rows that
 // keep every value run Philox over the whole row; top-p without top-k keeps
 // the most values; argmax rows read the row once.
@@ -612,7 +644,7 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
                                int n, KernelArgs &ka, const RowParam *dp, bool any_pen, int path, hipStream_t stream,
                                std::string &err, const DevRowArrays *dev = nullptr, RowParam *graph_rows = nullptr,
                                hipEvent_t ev0 = nullptr, hipEvent_t ev1 = nullptr, bool streamed = false,
-                               bool small = false) {
+                               bool small = false, int chunk_u = 0, int chunk_c = 0) {
   const int V = a->vocab;
   const bool det = (flags & SAMPLER_DETERMINISTIC) != 0;
   hipError_t e;
@@ -690,6 +722,16 @@ sampler_status plan_and_launch(Workspace &ws, uint32_t flags, int32_t wait_spin_
   if (small) {
     e = launch_small(ka, a->dtype, stream, ev0, ev1);
     if (e != hipSuccess) return hip_fail(err, e, "small-row kernel launch");
+    return SAMPLER_OK;
+  }
+  if (chunk_u > 0) {
+    kp.chunk_recs = ws.chunk_recs;
+    kp.chunk_words = ws.chunk_words;
+    kp.chunk_u = chunk_u;
+    kp.chunk_n = chunk_c;
+    kp.chunk_stride = ws.chunk_cap;
+    e = launch_chunk(ka, a->dtype, stream, ev0, ev1);
+    if (e != hipSuccess) return hip_fail(err, e, "chunked-row kernel launch");
     return SAMPLER_OK;
   }
   if (streamed) {
@@ -916,6 +958,17 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
     if ((e = hipMalloc((void **)&ws.defer_rows, sizeof(RowParam) * (size_t)cfg->max_rows)) != hipSuccess) goto fail;
     if ((e = hipMalloc((void **)&ws.defer_word, 256)) != hipSuccess) goto fail;
     if ((e = hipMemset(ws.defer_word, 0, 256)) != hipSuccess) goto fail;
+    if (cfg->max_vocab > kSmallV) {
+      // at most min(kChunkMax, ceil(V / (4 kChunkBlock))) chunks per row
+      const int64_t by_vocab = ((int64_t)cfg->max_vocab + 4 * kChunkBlock - 1) / (4 * kChunkBlock);
+      ws.chunk_cap = (int)(by_vocab < kChunkMax ? by_vocab : kChunkMax);
+      if ((e = hipMalloc((void **)&ws.chunk_recs, sizeof(ChunkRec) * (size_t)ws.chunk_cap * cfg->max_rows)) !=
+          hipSuccess)
+        goto fail;
+      const size_t wbytes = sizeof(unsigned long long) * kChunkWordStride * (size_t)cfg->max_rows;
+      if ((e = hipMalloc((void **)&ws.chunk_words, wbytes)) != hipSuccess) goto fail;
+      if ((e = hipMemset(ws.chunk_words, 0, wbytes)) != hipSuccess) goto fail;
+    }
     if ((e = stream_resident(cfg->device,
                              stream_lds_bytes(ws.hash_slots, true,
                                               cfg->max_vocab < kStreamMaxVocab ? cfg->max_vocab : kStreamMaxVocab),
@@ -994,11 +1047,13 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   // the streaming kernel when forced, or when the row kernel would walk its
   // row groups through several rows each
   const bool small = small_eligible(h->cfg.flags, a, h->recs.data(), n);
-  const bool streamed = !small && stream_eligible(h->ws, h->cfg.flags, a, h->recs.data(), n) &&
+  int chunk_u = 0, chunk_c = 0;
+  const bool chunked = !small && chunk_eligible(h->ws, h->cfg.flags, a, h->recs.data(), n, &chunk_u, &chunk_c);
+  const bool streamed = !small && !chunked && stream_eligible(h->ws, h->cfg.flags, a, h->recs.data(), n) &&
                         ((h->cfg.flags & SAMPLER_FORCE_STREAM) || n > kStreamRowsPerGroup * groups);
-  if (a->kernel_out) *a->kernel_out = small ? 2 : streamed ? 1 : 0;
+  if (a->kernel_out) *a->kernel_out = small ? 2 : chunked ? 3 : streamed ? 1 : 0;
   if (streamed) stream_records(h->recs.data(), n, h->order.data(), rp);
-  else if (small) std::copy(h->recs.data(), h->recs.data() + n, rp);
+  else if (small || chunked) std::copy(h->recs.data(), h->recs.data() + n, rp);
   else place_records(h->recs.data(), n, groups, h->rank.data(), h->order.data(), rp);
   hipError_t e;
   if (!inline_rows) {
@@ -1011,7 +1066,7 @@ sampler_status sampler_step(sampler_handle *h, const sampler_step_args *a, void 
   const bool prof = h->prof_n < h->prof_cap;
   st = plan_and_launch(h->ws, h->cfg.flags, h->cfg.wait_spin_limit, a, n, ka, dp, any_pen, path, stream, h->err,
                        nullptr, nullptr, prof ? h->prof[2 * h->prof_n] : nullptr,
-                       prof ? h->prof[2 * h->prof_n + 1] : nullptr, streamed, small);
+                       prof ? h->prof[2 * h->prof_n + 1] : nullptr, streamed, small, chunk_u, chunk_c);
   if (st == SAMPLER_OK && prof) ++h->prof_n;
   return st;
 }

@@ -273,7 +273,12 @@ typedef struct sampler_step_args {
    * keeps every value (Gumbel-max or greedy; no penalties, logits
    * processors or top_logprobs; not the raw logprob mode, not
    * SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF or SAMPLER_FORCE_FILTERED)
-   * take one small workgroup per row. */
+   * take one small workgroup per row, 3 the chunked-row kernel: steps of
+   * longer rows of that kind that want only token_ids and row_status (no
+   * probs, logprobs or top_logprobs; not SAMPLER_FORCE_STREAM either) take
+   * one workgroup per chunk of 1024 to 4096 values, and the last chunk of a
+   * row to finish merges the row.  sampler_step only: the graph and
+   * no-allocation entry points always report 0. */
   int32_t *kernel_out;
 } sampler_step_args;
 
