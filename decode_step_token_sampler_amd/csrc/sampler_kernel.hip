@@ -4133,6 +4133,29 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
   }
 }
 
+// ln E in fp32 for the word x, E = -ln(1 - w), w = (x + 1/2) 2^-32 (the
+// draw of exp1_f64), for ranking only: below w = 1/16 by the series of
+// -ln(1 - w) to w^6 (relative truncation below 1e-8), above it from 1 - w
+// taken from the complement of x (relative error 6e-8, so E's relative error
+// stays below 3e-6 where -ln(1 - w) >= 1/16).  The result is within 1e-5 of
+// ln E; kChunkMargin leaves a hundredfold slack for two scores' errors.
+DEV float ln_exp1_f32(uint32_t x) {
+  const float w = ((float)x + 0.5f) * 0x1p-32f;
+  const float q = ((float)(0xFFFFFFFFu - x) + 0.5f) * 0x1p-32f;
+  const float es = w * (1.0f + w * (0.5f + w * (1.0f / 3.0f + w * (0.25f + w * (0.2f + w * (1.0f / 6.0f))))));
+  const float el = -__logf(q);
+  return __logf(w < 0.0625f ? es : el);  // (both sides computed: no branch)
+}
+constexpr float kChunkMargin = 0x1p-10f;
+// Order keys of fp64 values (larger value, larger key; -0 < +0), and back.
+DEV unsigned long long dkey(double d) {
+  const unsigned long long u = (unsigned long long)__double_as_longlong(d);
+  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
+}
+DEV double key_to_double(unsigned long long k) {
+  return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
 // ---------------------------------------------------------------- small rows
 // Rows of at most kSmallV values that keep every value -- Gumbel-max over
 // the whole row, or greedy ([A] "Nine lines, and exactly one call site": the
@@ -4143,8 +4166,9 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
 // row's steps meet at a handful of workgroup barriers.  The arithmetic is
 // the row kernel's: z = x / T correctly rounded, the first argmax, the fp64
 // sum of exp(z - m) (in another order, so it may round differently), the
-// linear-domain bound, fp64 Gumbel scores, lp = fl32(z - m - ln S) and
-// p = 2^(lp log2 e).
+// fp64 Gumbel scores z - ln E (here only for the values whose fp32 score is
+// near the best, which provably holds the winner), lp = fl32(z - m - ln S)
+// and p = 2^(lp log2 e).
 constexpr int kSmallBlock = 256;
 constexpr int kSmallG = kSmallV / 4 / kSmallBlock;  // groups of four per thread
 static_assert(kSmallV % (4 * kSmallBlock) == 0, "whole groups per thread");
@@ -4175,11 +4199,19 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   __shared__ unsigned long long red_u[kW];
   __shared__ double red_d[kW];
   __shared__ int red_i[kW];
+  __shared__ unsigned long long best_key_s;
+  __shared__ int best_idx_s;
   const int tid = tidx();
   const int lane = tid & 63, wave = tid >> 6;
+  const unsigned it = 0;  // (stamps)
+  PHASE_STAMP(kStampStart);
   const RowParam P = kp.rows ? kp.rows[blockIdx.x] : ka.rows[blockIdx.x];
   const int row = P.row;
   const int V = kp.vocab;
+  PHASE_STAMP(kStampRow);
+  PHASE_RECORD(kStampRowIndex, row + 1);
+  // groups of four per thread that the row fills (the same for every thread)
+  const int ng = min(kSmallG, (V + 4 * kSmallBlock - 1) / (4 * kSmallBlock));
   const float T = P.temperature;
   const float rT = 1.0f / T;
   const uint32_t xlo_b = __float_as_uint(T * 0x1p-99f);
@@ -4192,6 +4224,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   float z[kSmallG][4];
 #pragma unroll
   for (int u = 0; u < kSmallG; ++u) {
+    if (u >= ng) break;
     const int l = 4 * (tid + kSmallBlock * u);
     if (vec) {
       Loader<TIn>::load4(kp.logits, rbase + min(l, lastg), z[u]);
@@ -4201,13 +4234,15 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
     }
   }
 #pragma unroll
-  for (int u = 0; u < kSmallG; ++u) temper4(z[u], 4 * (tid + kSmallBlock * u), V, T, rT, xlo_b, xhi_b);
+  for (int u = 0; u < kSmallG && u < ng; ++u) temper4(z[u], 4 * (tid + kSmallBlock * u), V, T, rT, xlo_b, xhi_b);
+  PHASE_STAMP(kStampLoaded);
   // the row max and its first index (the best group by a strict compare,
   // groups in index order, then the first match in it)
   float lmax = -INFINITY;
   int lidx = 0x7FFFFFFF;
 #pragma unroll
   for (int u = 0; u < kSmallG; ++u) {
+    if (u >= ng) break;
     const float gm = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
     if (gm > lmax) {
       lmax = gm;
@@ -4221,6 +4256,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   for (int w = 0; w < kW; ++w) mk = red_u[w] > mk ? red_u[w] : mk;
   const float mf = key_to_float((uint32_t)(mk >> 32));
   const int argmax = (int)(0xFFFFFFFFu - (uint32_t)mk);
+  PHASE_STAMP(kStampMax);
   const bool want_out = kp.probs != nullptr || kp.logprobs != nullptr;
   if (!(mf > -INFINITY && mf < INFINITY)) {  // no finite value (status 1) or a +inf value (status 2)
     if (want_out)
@@ -4241,7 +4277,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   if (want_out) {
     double sx = 0.0;
 #pragma unroll
-    for (int u = 0; u < kSmallG; ++u)
+    for (int u = 0; u < kSmallG && u < ng; ++u)
 #pragma unroll
       for (int c = 0; c < 4; ++c) sx += exp_term(z[u][c], m);
     sx = wave_sum_d(sx);
@@ -4252,61 +4288,70 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
     for (int w = 1; w < kW; ++w) t += red_d[w];
     lnS = log(t);
   }
-  // Gumbel-max: the argmax's draw seeds the bound (the argmax scores 1 / E);
-  // groups within the listing cut draw, values that pass the linear-domain
-  // bound get the exact fp64 score; ties go to the smaller index
-  double best_g = -INFINITY;
+  PHASE_STAMP(kStampThresholds);
+  // Gumbel-max: every finite value gets an fp32 score z - ln E, the values
+  // within kChunkMargin of the best fp32 score the exact fp64 score; the
+  // best of those (ties: the smaller index) through two LDS atomics
   int best_i = 0x7FFFFFFF;
   if (gumbel) {
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
     const uint32_t off0 = (uint32_t)P.offset, off1 = (uint32_t)(P.offset >> 32);
-    uint32_t w4[4];
-    philox4x32_10((uint32_t)argmax >> 2, P.stream, off0, off1, key0, key1, w4);
-    float bound = (float)(1.0 / exp1_f64(w4[argmax & 3])) * 0.99999f;
-    const float cut = fminf(kPruneNats, kLnInvEmin + (kPruneNats - 26.004f) - logf(bound));
+    float g32[kSmallG][4];
+    uint32_t wv[kSmallG][4];
+    float gmx = -INFINITY;
 #pragma unroll
     for (int u = 0; u < kSmallG; ++u) {
+      if (u >= ng) break;
       const int i0 = 4 * (tid + kSmallBlock * u);
       const float gm = fmaxf(fmaxf(z[u][0], z[u][1]), fmaxf(z[u][2], z[u][3]));
-      if (i0 < V && mf - gm <= cut) {
-        uint32_t w[4];
-        philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, w);
-        uint32_t surv = 0;
+      if (i0 < V && gm > -INFINITY) {
+        philox4x32_10((uint32_t)i0 >> 2, P.stream, off0, off1, key0, key1, wv[u]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const float wl = (float)w[c] * 0x1.fffffcp-33f;
-          const float qv = __builtin_amdgcn_exp2f((z[u][c] - mf) * kLog2e);
-          surv |= (mf - z[u][c] <= cut && wl * bound <= qv * kSlack) ? 1u << c : 0u;
+          g32[u][c] = z[u][c] - ln_exp1_f32(wv[u][c]);  // (-inf stays -inf)
+          gmx = fmaxf(gmx, g32[u][c]);
         }
-        while (surv) {
-          const int c = __builtin_ctz(surv);
-          surv &= surv - 1u;
-          const float zc = c == 0 ? z[u][0] : c == 1 ? z[u][1] : c == 2 ? z[u][2] : z[u][3];
-          const uint32_t wc = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
-          const double ge = (double)zc - log(exp1_f64(wc));
-          if (ge > best_g || (ge == best_g && i0 + c < best_i)) {
-            best_g = ge;
-            best_i = i0 + c;
-            bound = fmaxf(bound, (float)exp(best_g - m) * 0.99999f);
-          }
-        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 4; ++c) g32[u][c] = -INFINITY;
       }
     }
-    wave_best(best_g, best_i);
-    if (lane == 0) {
-      red_d[wave] = best_g;
-      red_i[wave] = best_i;
+    uint32_t gk = lane63_u32(wave_scanmax_u32(fkey(gmx)));
+    if (lane == 0) red_i[wave] = (int)gk;
+    if (tid == 0) {
+      best_key_s = 0ull;
+      best_idx_s = 0x7FFFFFFF;
     }
     __syncthreads();
-    best_g = red_d[0];
-    best_i = red_i[0];
 #pragma unroll
-    for (int w = 1; w < kW; ++w)
-      if (red_d[w] > best_g || (red_d[w] == best_g && red_i[w] < best_i)) {
-        best_g = red_d[w];
-        best_i = red_i[w];
-      }
+    for (int w = 0; w < kW; ++w) gk = max(gk, (uint32_t)red_i[w]);
+    const float G32 = key_to_float(gk);
+    const float thr = G32 - (kChunkMargin + fabsf(G32) * 0x1p-20f);
+    double tg = -INFINITY;
+    int ti = 0x7FFFFFFF;
+#pragma unroll
+    for (int u = 0; u < kSmallG; ++u) {
+      if (u >= ng) break;
+      const int i0 = 4 * (tid + kSmallBlock * u);
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        if (g32[u][c] >= thr) {
+          const double ge = ((double)z[u][c] - log(exp1_f64(wv[u][c]))) + 0.0;  // (+0 for -0)
+          if (ge > tg || (ge == tg && i0 + c < ti)) {
+            tg = ge;
+            ti = i0 + c;
+          }
+        }
+    }
+    const unsigned long long tk = dkey(tg);
+    if (ti != 0x7FFFFFFF) atomicMax(&best_key_s, tk);
+    __syncthreads();
+    const unsigned long long bk = best_key_s;
+    if (ti != 0x7FFFFFFF && tk == bk) atomicMin(&best_idx_s, ti);
+    __syncthreads();
+    best_i = best_idx_s;
   }
+  PHASE_STAMP(kStampGumbel);
   if (tid == 0) {
     kp.token_ids[row] = gumbel ? best_i : argmax;
     if (kp.row_status) kp.row_status[row] = 0;
@@ -4315,6 +4360,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   if (want_out) {
 #pragma unroll
     for (int u = 0; u < kSmallG; ++u) {
+    if (u >= ng) break;
       const int l = 4 * (tid + kSmallBlock * u);
       float lv[4], pv[4];
 #pragma unroll
@@ -4336,6 +4382,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
       }
     }
   }
+  PHASE_STAMP(kStampEnd);
 }
 
 // ---------------------------------------------------------------- chunked rows
@@ -4347,29 +4394,6 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
 // index of the largest z.  So each workgroup scores one chunk of the row on
 // its own and the last chunk of the row to arrive merges the chunks' bests.
 // No workgroup waits for another.
-// ln E in fp32 for the word x, E = -ln(1 - w), w = (x + 1/2) 2^-32 (the
-// draw of exp1_f64), for ranking only: below w = 1/16 by the series of
-// -ln(1 - w) to w^6 (relative truncation below 1e-8), above it from 1 - w
-// taken from the complement of x (relative error 6e-8, so E's relative error
-// stays below 3e-6 where -ln(1 - w) >= 1/16).  The result is within 1e-5 of
-// ln E; kChunkMargin leaves a hundredfold slack for two scores' errors.
-DEV float ln_exp1_f32(uint32_t x) {
-  const float w = ((float)x + 0.5f) * 0x1p-32f;
-  const float q = ((float)(0xFFFFFFFFu - x) + 0.5f) * 0x1p-32f;
-  const float es = w * (1.0f + w * (0.5f + w * (1.0f / 3.0f + w * (0.25f + w * (0.2f + w * (1.0f / 6.0f))))));
-  const float el = -__logf(q);
-  return __logf(w < 0.0625f ? es : el);  // (both sides computed: no branch)
-}
-constexpr float kChunkMargin = 0x1p-10f;
-// Order keys of fp64 values (larger value, larger key; -0 < +0), and back.
-DEV unsigned long long dkey(double d) {
-  const unsigned long long u = (unsigned long long)__double_as_longlong(d);
-  return (u >> 63) ? ~u : (u | 0x8000000000000000ull);
-}
-DEV double key_to_double(unsigned long long k) {
-  return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
-}
-
 template <typename TIn>
 __global__ __launch_bounds__(kChunkBlock) void chunk_kernel(KernelArgs ka) {
   const KernelParams &kp = ka.kp;
