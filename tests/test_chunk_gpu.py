@@ -96,8 +96,8 @@ def test_unaligned_rows(sampler_chunk):
 
 
 def test_repeated_steps_of_other_shapes(sampler_chunk):
-    # the arrival words carry each launch's epoch: steps of other row counts
-    # and chunk counts in a row, each checked
+    # the last chunk of a row resets the row's arrival count for the next
+    # launch: steps of other row counts and chunk counts in a row, each checked
     for seed, n, V in [(181, 40, 151_936), (182, 3, 20_000), (183, 40, 151_936), (184, 1, 4097)]:
         check(ids_only(seed, n, V, "bf16"), sampler_chunk)
 
