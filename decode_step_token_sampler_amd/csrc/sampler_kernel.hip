@@ -3860,60 +3860,123 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
         // the heavy code): count, exact masses, Philox, the linear-domain
         // bound and the fp64 scores of the values that can still win
         bool improved = false;
-        while (hv) {
-          const int t0 = __builtin_ctz(hv);
-          hv &= hv - 1u;
-          int g = 0;
-          float xr[4];
-          uint32_t m4 = 0;
+        if (!truncated) {
+          // a row that keeps every value: nearly every group is above the
+          // ranges, so the step's groups run unrolled (their Philox chains
+          // interleave); the values that pass the linear-domain bound are
+          // marked (bit 4 t + c) and scored in fp64 after the step, one
+          // copy of that code
+          uint32_t sv = 0;
 #pragma unroll
-          for (int t = 0; t < kNG; ++t)
-            if (t == t0) {
-              g = gi[t];
-              m4 = mk[t];
-#pragma unroll
-              for (int c = 0; c < 4; ++c) xr[c] = rawv(ch, t, c);
-            }
-          bool cand = false;
-          uint32_t am = 0;
-          float z[4];
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float x = ((m4 >> c) & 1u) ? -INFINITY : xr[c];
-            const bool ab = (x >= xThi) & !(x >= xK) & (x > -INFINITY);
-            z[c] = ab ? zval(x, false) : -INFINITY;
-            am |= ab ? 1u << c : 0u;
-            cand |= ab && (mf - z[c] <= cut);
-          }
-          n_above += (uint32_t)__popc(am);
-          if (need_s) {
-            for (uint32_t mm = am; mm; mm &= mm - 1u) {
-              const int c = __builtin_ctz(mm);
-              const float zc = c == 0 ? z[0] : c == 1 ? z[1] : c == 2 ? z[2] : z[3];
-              s_above += truncated ? exp_nonpos(sm.exp_tab, (double)zc - m) : exp_term(zc, m);
-            }
-          }
-          if (gumbel && cand) {
-            uint32_t w[4];
-            philox4x32_10((uint32_t)g, P.stream, off0, off1, key0, key1, w);
-            // lower bound of E (E >= w) against the best score so far
-            uint32_t surv = 0;
+          for (int t = 0; t < kNG; ++t) {
+            if (!((hv >> t) & 1u)) continue;
+            uint32_t am = 0;
+            bool cand = false;
+            float z[4];
 #pragma unroll
             for (int c = 0; c < 4; ++c) {
-              const float wl = (float)w[c] * 0x1.fffffcp-33f;
-              const float qv = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
-              surv |= (((am >> c) & 1u) && (mf - z[c] <= cut) && wl * bound <= qv * kSlack) ? 1u << c : 0u;
+              const float x = ((mk[t] >> c) & 1u) ? -INFINITY : rawv(ch, t, c);
+              const bool ab = (x >= xThi) & !(x >= xK) & (x > -INFINITY);
+              z[c] = ab ? zval(x, false) : -INFINITY;
+              am |= ab ? 1u << c : 0u;
+              cand |= ab && (mf - z[c] <= cut);
             }
-            while (surv) {
-              const int c = __builtin_ctz(surv);
-              surv &= surv - 1u;
-              const float zc = c == 0 ? z[0] : c == 1 ? z[1] : c == 2 ? z[2] : z[3];
-              const uint32_t wc = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
-              const double ge = (double)zc - log(exp1_f64(wc));
-              if (ge > best_g || (ge == best_g && 4 * g + c < best_i)) {
-                best_g = ge;
-                best_i = 4 * g + c;
-                improved = true;
+            n_above += (uint32_t)__popc(am);
+            if (need_s) {
+#pragma unroll
+              for (int c = 0; c < 4; ++c) s_above += exp_term(z[c], m);  // (0 for -inf)
+            }
+            if (gumbel && cand) {
+              uint32_t w[4];
+              philox4x32_10((uint32_t)gi[t], P.stream, off0, off1, key0, key1, w);
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const float wl = (float)w[c] * 0x1.fffffcp-33f;
+                const float qv = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
+                sv |= (((am >> c) & 1u) && (mf - z[c] <= cut) && wl * bound <= qv * kSlack) ? 1u << (4 * t + c) : 0u;
+              }
+            }
+          }
+          while (sv) {
+            const int bit = __builtin_ctz(sv);
+            sv &= sv - 1u;
+            const int t0 = bit >> 2, c0 = bit & 3;
+            int g = 0;
+            float xv[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int t = 0; t < kNG; ++t)
+              if (t == t0) {
+                g = gi[t];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xv[c] = rawv(ch, t, c);
+              }
+            const float zc = zval(c0 == 0 ? xv[0] : c0 == 1 ? xv[1] : c0 == 2 ? xv[2] : xv[3], false);
+            uint32_t w[4];
+            philox4x32_10((uint32_t)g, P.stream, off0, off1, key0, key1, w);
+            const uint32_t wc = c0 == 0 ? w[0] : c0 == 1 ? w[1] : c0 == 2 ? w[2] : w[3];
+            const double ge = (double)zc - log(exp1_f64(wc));
+            if (ge > best_g || (ge == best_g && 4 * g + c0 < best_i)) {
+              best_g = ge;
+              best_i = 4 * g + c0;
+              improved = true;
+            }
+          }
+        } else {
+          while (hv) {
+            const int t0 = __builtin_ctz(hv);
+            hv &= hv - 1u;
+            int g = 0;
+            float xr[4];
+            uint32_t m4 = 0;
+#pragma unroll
+            for (int t = 0; t < kNG; ++t)
+              if (t == t0) {
+                g = gi[t];
+                m4 = mk[t];
+#pragma unroll
+                for (int c = 0; c < 4; ++c) xr[c] = rawv(ch, t, c);
+              }
+            bool cand = false;
+            uint32_t am = 0;
+            float z[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float x = ((m4 >> c) & 1u) ? -INFINITY : xr[c];
+              const bool ab = (x >= xThi) & !(x >= xK) & (x > -INFINITY);
+              z[c] = ab ? zval(x, false) : -INFINITY;
+              am |= ab ? 1u << c : 0u;
+              cand |= ab && (mf - z[c] <= cut);
+            }
+            n_above += (uint32_t)__popc(am);
+            if (need_s) {
+              for (uint32_t mm = am; mm; mm &= mm - 1u) {
+                const int c = __builtin_ctz(mm);
+                const float zc = c == 0 ? z[0] : c == 1 ? z[1] : c == 2 ? z[2] : z[3];
+                s_above += truncated ? exp_nonpos(sm.exp_tab, (double)zc - m) : exp_term(zc, m);
+              }
+            }
+            if (gumbel && cand) {
+              uint32_t w[4];
+              philox4x32_10((uint32_t)g, P.stream, off0, off1, key0, key1, w);
+              // lower bound of E (E >= w) against the best score so far
+              uint32_t surv = 0;
+#pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const float wl = (float)w[c] * 0x1.fffffcp-33f;
+                const float qv = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
+                surv |= (((am >> c) & 1u) && (mf - z[c] <= cut) && wl * bound <= qv * kSlack) ? 1u << c : 0u;
+              }
+              while (surv) {
+                const int c = __builtin_ctz(surv);
+                surv &= surv - 1u;
+                const float zc = c == 0 ? z[0] : c == 1 ? z[1] : c == 2 ? z[2] : z[3];
+                const uint32_t wc = c == 0 ? w[0] : c == 1 ? w[1] : c == 2 ? w[2] : w[3];
+                const double ge = (double)zc - log(exp1_f64(wc));
+                if (ge > best_g || (ge == best_g && 4 * g + c < best_i)) {
+                  best_g = ge;
+                  best_i = 4 * g + c;
+                  improved = true;
+                }
               }
             }
           }
