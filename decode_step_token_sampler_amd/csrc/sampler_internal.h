@@ -299,7 +299,8 @@ hipError_t launch_step(const KernelArgs &ka, int dtype, bool penalties, bool coo
 hipError_t launch_stream(const KernelArgs &ka, int dtype, bool penalties, int grid, hipStream_t stream, hipEvent_t ev0,
                          hipEvent_t ev1);
 // Its dynamic LDS bytes for a vocabulary, and the workgroups of it that fit on
-// the device at once.
+// the device at once (0 when those bytes exceed a workgroup's LDS: such a
+// handle never streams).
 size_t stream_lds_bytes(int hash_slots, bool penalties, int vocab);
 hipError_t stream_resident(int device, size_t lds_bytes, int *out);
 // Rows of at most kSmallV values that keep every value (no truncation,

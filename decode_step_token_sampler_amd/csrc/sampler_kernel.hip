@@ -3246,7 +3246,7 @@ __global__ __launch_bounds__(kBlock) void raw_lp_kernel(KernelArgs ka) {
 // kSCap values, or whose exact decision falls outside the ranges the
 // histogram chose is not written: its record goes to a list that the row
 // kernel, launched after this one, samples in full.
-constexpr int kSCap = 1024;       // values gathered per row
+constexpr int kSCap = 2048;       // values gathered per row (one workgroup per CU has room)
 constexpr int kSLoads = 4;        // 16-byte chunks each thread loads per step (one more step in flight)
 static_assert(kSCap % kBlock == 0, "gathered values per thread");
 
@@ -4766,6 +4766,12 @@ hipError_t stream_resident(int device, size_t lds_bytes, int *out) {
   const void *fns[] = {stream_fn<float, true>(), stream_fn<float, false>(), stream_fn<uint16_t, true>(),
                        stream_fn<uint16_t, false>()};
   hipError_t e;
+  hipDeviceProp_t prop;
+  if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return e;
+  if (lds_bytes > prop.sharedMemPerBlock) {  // (the largest vocabularies with the longest histories)
+    *out = 0;
+    return hipSuccess;
+  }
   int pc = 1 << 30;
   for (const void *f : fns) {
     if ((e = hipFuncSetAttribute(f, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_bytes)) != hipSuccess) return e;
@@ -4773,8 +4779,6 @@ hipError_t stream_resident(int device, size_t lds_bytes, int *out) {
     if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kBlock, lds_bytes)) != hipSuccess) return e;
     pc = per_cu < pc ? per_cu : pc;
   }
-  hipDeviceProp_t prop;
-  if ((e = hipGetDeviceProperties(&prop, device)) != hipSuccess) return e;
   *out = pc * prop.multiProcessorCount;
   return hipSuccess;
 }

@@ -113,7 +113,9 @@ typedef enum sampler_dtype {
  * same definitions either way (the fp64 sums may round differently).
  *   SAMPLER_FORCE_STREAM: use the streaming kernel for every such step.
  *   SAMPLER_NO_STREAM: never use it.
- * At most one of the two per handle. */
+ * At most one of the two per handle.  A handle whose largest vocabulary and
+ * history need more LDS than a workgroup has (max_vocab near 2^19 with
+ * histories over 2,048 ids) never streams, forced or not. */
 #define SAMPLER_FORCE_STREAM (1u << 6)
 #define SAMPLER_NO_STREAM (1u << 7)
 

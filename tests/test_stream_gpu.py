@@ -186,3 +186,17 @@ def test_unaligned_rows(sampler_stream, dtype):
     assert g["kernel"] == "stream"
     r = compare(g, run_oracle(b))
     assert r.ok(), r
+
+
+def test_handle_too_large_for_streaming_takes_the_row_kernel():
+    """A handle whose largest vocabulary and histories (2^19 values, 4,096-id
+    histories) need more LDS than the streaming kernel's workgroup has never
+    streams, even forced: its steps run on the row kernel and still equal
+    the oracle."""
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(8, 1 << 19, max_history_per_row=4096, max_top_logprobs=8, stream_rows="force")
+    try:
+        b = ids_only(workloads.random_small(132, 6, 1 << 19, "bf16", history_len=3000), 4)
+        check(b, s, kernel="row")
+    finally:
+        s.close()
