@@ -316,6 +316,7 @@ constexpr int kChunkMaxU = 4;
 constexpr int kChunkMax = 256;
 constexpr int kChunkMaxV = 4 * kChunkBlock * kChunkMaxU * kChunkMax;
 constexpr int kChunkWordStride = 16;  // arrival words 128 bytes apart
+constexpr int kChunkMaxRows = 4096;   // rows of a chunked step (the grid's y extent; workspace)
 // One chunk's result.  Gumbel-max rows: a = its best score (fp64 bits), b =
 // status << 32 | that score's index (status 1: no finite value in the
 // chunk, 2: a +inf value).  Greedy rows: a = the order key of its max

@@ -85,8 +85,8 @@ struct Workspace {
   RowParam *defer_rows = nullptr;           // [max_rows]
   unsigned long long *defer_word = nullptr;
   // chunked rows: per record chunk_cap chunk results and one arrival word
-  ChunkRec *chunk_recs = nullptr;           // [max_rows * chunk_cap]
-  unsigned long long *chunk_words = nullptr;  // [max_rows * kChunkWordStride]
+  ChunkRec *chunk_recs = nullptr;           // [min(max_rows, kChunkMaxRows) * chunk_cap]
+  unsigned long long *chunk_words = nullptr;  // [min(max_rows, kChunkMaxRows) * kChunkWordStride]
   int chunk_cap = 0;
   // limits the workspace was planned for
   int32_t max_history_per_row = 0, max_bias_per_row = 0, max_top_logprobs = 0, max_vocab = 0;
@@ -594,7 +594,7 @@ bool chunk_eligible(const Workspace &ws, uint32_t flags, const sampler_step_args
                     int *U, int *C) {
   if (flags & (SAMPLER_DETERMINISTIC | SAMPLER_INVERSE_CDF | SAMPLER_FORCE_FILTERED | SAMPLER_FORCE_STREAM))
     return false;
-  if (!ws.chunk_recs || a->vocab <= kSmallV || a->vocab > kChunkMaxV) return false;
+  if (!ws.chunk_recs || a->vocab <= kSmallV || a->vocab > kChunkMaxV || n > kChunkMaxRows) return false;
   if (a->probs || a->logprobs || a->top_logprobs > 0 || a->vocab_mask) return false;
   for (int r = 0; r < n; ++r)
     if (recs[r].flags & (RF_TOPK | RF_TOPP | RF_MINP | RF_PEN | RF_SPEC)) return false;
@@ -962,10 +962,10 @@ sampler_status sampler_create(const sampler_config *cfg, sampler_handle **out) {
       // at most min(kChunkMax, ceil(V / (4 kChunkBlock))) chunks per row
       const int64_t by_vocab = ((int64_t)cfg->max_vocab + 4 * kChunkBlock - 1) / (4 * kChunkBlock);
       ws.chunk_cap = (int)(by_vocab < kChunkMax ? by_vocab : kChunkMax);
-      if ((e = hipMalloc((void **)&ws.chunk_recs, sizeof(ChunkRec) * (size_t)ws.chunk_cap * cfg->max_rows)) !=
-          hipSuccess)
+      const size_t crows = (size_t)(cfg->max_rows < kChunkMaxRows ? cfg->max_rows : kChunkMaxRows);
+      if ((e = hipMalloc((void **)&ws.chunk_recs, sizeof(ChunkRec) * (size_t)ws.chunk_cap * crows)) != hipSuccess)
         goto fail;
-      const size_t wbytes = sizeof(unsigned long long) * kChunkWordStride * (size_t)cfg->max_rows;
+      const size_t wbytes = sizeof(unsigned long long) * kChunkWordStride * crows;
       if ((e = hipMalloc((void **)&ws.chunk_words, wbytes)) != hipSuccess) goto fail;
       if ((e = hipMemset(ws.chunk_words, 0, wbytes)) != hipSuccess) goto fail;
     }

@@ -276,8 +276,9 @@ typedef struct sampler_step_args {
    * processors or top_logprobs; not the raw logprob mode, not
    * SAMPLER_DETERMINISTIC, SAMPLER_INVERSE_CDF or SAMPLER_FORCE_FILTERED)
    * take one small workgroup per row, 3 the chunked-row kernel: steps of
-   * longer rows of that kind that want only token_ids and row_status (no
-   * probs, logprobs or top_logprobs; not SAMPLER_FORCE_STREAM either) take
+   * up to 4,096 longer rows of that kind that want only token_ids and
+   * row_status (no probs, logprobs or top_logprobs; not
+   * SAMPLER_FORCE_STREAM either) take
    * one workgroup per chunk of 1024 to 4096 values, and the last chunk of a
    * row to finish merges the row.  sampler_step only: the graph and
    * no-allocation entry points always report 0. */

@@ -62,6 +62,12 @@ def test_random_rows(sampler_chunk, seed, n, V, dtype):
     check(ids_only(seed, n, V, dtype), sampler_chunk)
 
 
+def test_many_long_rows(sampler_chunk):
+    # 96 rows of 262,144 values: four groups per thread, 64 chunks a row,
+    # 6,144 workgroups in the launch
+    check(ids_only(179, 96, 262_144, "bf16"), sampler_chunk)
+
+
 def test_edge_rows(sampler_chunk):
     V = 5000
     x = np.random.default_rng(5).standard_normal((8, V)).astype(np.float32)
