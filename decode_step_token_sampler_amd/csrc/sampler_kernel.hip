@@ -3670,21 +3670,37 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
         __syncthreads();
         const bool need_c = topp && !topk;
         double csum = 0.0;
-        group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
-          float dsum = 0.0f;
+        if (topp) {  // counts and masses (only the top-p crossing reads the masses)
+          group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
+            float dsum = 0.0f;
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            const float lb = win_pos(A, z[c], wsc);  // -inf: +inf
-            const float a = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
-            if (lb < (float)kWinBins) atomicAdd(&wh[(int)lb], hist_entry_s(a));
-            dsum += a;
-          }
-          if (need_c) csum += (double)dsum;
-        });
+            for (int c = 0; c < 4; ++c) {
+              const float lb = win_pos(A, z[c], wsc);  // -inf: +inf
+              const float a = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
+              if (lb < (float)kWinBins) atomicAdd(&wh[(int)lb], hist_entry_s(a));
+              dsum += a;
+            }
+            if (need_c) csum += (double)dsum;
+          });
+        } else {  // counts only: a 32-bit add to the bin's high word (count bits 44 and up)
+          uint32_t *whc = reinterpret_cast<uint32_t *>(wh);
+          group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const float lb = win_pos(A, z[c], wsc);  // -inf: +inf
+              if (lb < (float)kWinBins) atomicAdd(&whc[2 * (int)lb + 1], 1u << 12);
+            }
+          });
+        }
+        // (the same atomic width as the pass above: the passes of other
+        // waves may still run)
         patches([&](int i, float zz) {
           const float lb = win_pos(A, zz, wsc);
           const float a = __builtin_amdgcn_exp2f((zz - mf) * kLog2e);
-          if (lb < (float)kWinBins) atomicAdd(&wh[(int)lb], hist_entry_s(a));
+          if (lb < (float)kWinBins) {
+            if (topp) atomicAdd(&wh[(int)lb], hist_entry_s(a));
+            else atomicAdd(reinterpret_cast<uint32_t *>(wh) + 2 * (int)lb + 1, 1u << 12);
+          }
           if (need_c) csum += (double)a;
         });
         C_all = need_c ? wg_sum_d(sm, csum) : 0.0;
