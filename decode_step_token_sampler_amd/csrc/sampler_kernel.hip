@@ -3898,9 +3898,14 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
               cand |= ab && (mf - z[c] <= cut);
             }
             n_above += (uint32_t)__popc(am);
+            // each value's mass exp(z - m) in fp32 (0 for -inf), for the sum
+            // and the bound alike
+            float qv[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) qv[c] = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
             if (need_s) {
 #pragma unroll
-              for (int c = 0; c < 4; ++c) s_above += exp_term(z[c], m);  // (0 for -inf)
+              for (int c = 0; c < 4; ++c) s_above += (double)qv[c];
             }
             if (gumbel && cand) {
               uint32_t w[4];
@@ -3908,8 +3913,7 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
 #pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const float wl = (float)w[c] * 0x1.fffffcp-33f;
-                const float qv = __builtin_amdgcn_exp2f((z[c] - mf) * kLog2e);
-                sv |= (((am >> c) & 1u) && (mf - z[c] <= cut) && wl * bound <= qv * kSlack) ? 1u << (4 * t + c) : 0u;
+                sv |= (((am >> c) & 1u) && (mf - z[c] <= cut) && wl * bound <= qv[c] * kSlack) ? 1u << (4 * t + c) : 0u;
               }
             }
           }
