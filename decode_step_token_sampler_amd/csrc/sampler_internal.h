@@ -317,10 +317,12 @@ constexpr int kChunkMax = 256;
 constexpr int kChunkMaxV = 4 * kChunkBlock * kChunkMaxU * kChunkMax;
 constexpr int kChunkWordStride = 16;  // arrival words 128 bytes apart
 constexpr int kChunkMaxRows = 4096;   // rows of a chunked step (the grid's y extent; workspace)
-// One chunk's result.  Gumbel-max rows: a = its best score (fp64 bits), b =
-// status << 32 | that score's index (status 1: no finite value in the
-// chunk, 2: a +inf value).  Greedy rows: a = the order key of its max
-// (order key << 32 | ~first index).
+// One chunk's result.  Gumbel-max rows: b = the winner's fp32 score bits
+// << 32 | flags << 28 | the winner's index (flags bits 0-1: status, 1 no
+// finite value in the chunk, 2 a +inf value; bit 2: exact), a = the
+// winner's z bits << 32 | its Philox word, or with the exact flag its fp64
+// score (several values were near the chunk's best fp32 score).  Greedy
+// rows: a = the order key of its max (order key << 32 | ~first index).
 struct alignas(16) ChunkRec {
   unsigned long long a;
   unsigned long long b;

@@ -4230,6 +4230,7 @@ DEV float ln_exp1_f32(uint32_t x) {
   return __logf(w < 0.0625f ? es : el);  // (both sides computed: no branch)
 }
 constexpr float kChunkMargin = 0x1p-10f;
+constexpr uint32_t kChunkExact = 4u;  // chunk record: the score word holds an exact fp64 score
 // Order keys of fp64 values (larger value, larger key; -0 < +0), and back.
 DEV unsigned long long dkey(double d) {
   const unsigned long long u = (unsigned long long)__double_as_longlong(d);
@@ -4237,6 +4238,77 @@ DEV unsigned long long dkey(double d) {
 }
 DEV double key_to_double(unsigned long long k) {
   return __longlong_as_double((long long)((k >> 63) ? (k & 0x7FFFFFFFFFFFFFFFull) : ~k));
+}
+
+// A workgroup's Gumbel-max pick among its values whose fp32 score is at
+// least thr (a set that holds the exact winner, thr lying within
+// kChunkMargin of the best fp32 score).  Most often the set has one value:
+// then it is the winner, found without any fp64 work (single; its index,
+// z and word in pk).  Otherwise the set's exact fp64 scores z - ln E decide
+// (ties: the smaller index) through two LDS atomics (pk.best_key,
+// pk.best_idx).  NG groups of four per thread, ng of them used, value c of
+// group u at index base + 4 (tid + NT u) + c.  The caller clears pk.n,
+// pk.best_key and pk.best_idx before the barrier that follows thr's inputs.
+struct PickLds {
+  unsigned long long best_key;
+  int best_idx;
+  uint32_t n;  // values in the set
+  int idx;     // the set's value, when it has one
+  uint32_t w;
+  float z;
+};
+template <int NG, int NT>
+DEV bool pick_candidate(const float (&z)[NG][4], const float (&g32)[NG][4], const uint32_t (&wv)[NG][4], int ng,
+                        int base, float thr, PickLds &pk) {
+  const int tid = tidx();
+  uint32_t myc = 0;
+  int myi = 0x7FFFFFFF;
+  uint32_t myw = 0;
+  float myz = 0.0f;
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    if (u >= ng) break;
+    const int i0 = base + 4 * (tid + NT * u);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (g32[u][c] >= thr) {
+        ++myc;
+        myi = i0 + c;
+        myw = wv[u][c];
+        myz = z[u][c];
+      }
+  }
+  if (myc != 0u) atomicAdd(&pk.n, myc);
+  if (myc == 1u) {  // (read only when no other thread has a value in the set)
+    pk.idx = myi;
+    pk.w = myw;
+    pk.z = myz;
+  }
+  __syncthreads();
+  if (pk.n == 1u) return true;  // (workgroup-uniform)
+  double tg = -INFINITY;
+  int ti = 0x7FFFFFFF;
+#pragma unroll
+  for (int u = 0; u < NG; ++u) {
+    if (u >= ng) break;
+    const int i0 = base + 4 * (tid + NT * u);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (g32[u][c] >= thr) {
+        const double ge = ((double)z[u][c] - log(exp1_f64(wv[u][c]))) + 0.0;  // (+0 for -0)
+        if (ge > tg || (ge == tg && i0 + c < ti)) {
+          tg = ge;
+          ti = i0 + c;
+        }
+      }
+  }
+  const unsigned long long tk = dkey(tg);
+  if (ti != 0x7FFFFFFF) atomicMax(&pk.best_key, tk);
+  __syncthreads();
+  const unsigned long long bk = pk.best_key;
+  if (ti != 0x7FFFFFFF && tk == bk) atomicMin(&pk.best_idx, ti);
+  __syncthreads();
+  return false;
 }
 
 // ---------------------------------------------------------------- small rows
@@ -4282,8 +4354,7 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
   __shared__ unsigned long long red_u[kW];
   __shared__ double red_d[kW];
   __shared__ int red_i[kW];
-  __shared__ unsigned long long best_key_s;
-  __shared__ int best_idx_s;
+  __shared__ PickLds pk;
   const int tid = tidx();
   const int lane = tid & 63, wave = tid >> 6;
   const unsigned it = 0;  // (stamps)
@@ -4372,9 +4443,8 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
     lnS = log(t);
   }
   PHASE_STAMP(kStampThresholds);
-  // Gumbel-max: every finite value gets an fp32 score z - ln E, the values
-  // within kChunkMargin of the best fp32 score the exact fp64 score; the
-  // best of those (ties: the smaller index) through two LDS atomics
+  // Gumbel-max: every finite value gets an fp32 score z - ln E; the values
+  // within kChunkMargin of the best one hold the winner (pick_candidate)
   int best_i = 0x7FFFFFFF;
   if (gumbel) {
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
@@ -4402,37 +4472,16 @@ __global__ __launch_bounds__(kSmallBlock) void small_kernel(KernelArgs ka) {
     uint32_t gk = lane63_u32(wave_scanmax_u32(fkey(gmx)));
     if (lane == 0) red_i[wave] = (int)gk;
     if (tid == 0) {
-      best_key_s = 0ull;
-      best_idx_s = 0x7FFFFFFF;
+      pk.best_key = 0ull;
+      pk.best_idx = 0x7FFFFFFF;
+      pk.n = 0u;
     }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kW; ++w) gk = max(gk, (uint32_t)red_i[w]);
     const float G32 = key_to_float(gk);
     const float thr = G32 - (kChunkMargin + fabsf(G32) * 0x1p-20f);
-    double tg = -INFINITY;
-    int ti = 0x7FFFFFFF;
-#pragma unroll
-    for (int u = 0; u < kSmallG; ++u) {
-      if (u >= ng) break;
-      const int i0 = 4 * (tid + kSmallBlock * u);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (g32[u][c] >= thr) {
-          const double ge = ((double)z[u][c] - log(exp1_f64(wv[u][c]))) + 0.0;  // (+0 for -0)
-          if (ge > tg || (ge == tg && i0 + c < ti)) {
-            tg = ge;
-            ti = i0 + c;
-          }
-        }
-    }
-    const unsigned long long tk = dkey(tg);
-    if (ti != 0x7FFFFFFF) atomicMax(&best_key_s, tk);
-    __syncthreads();
-    const unsigned long long bk = best_key_s;
-    if (ti != 0x7FFFFFFF && tk == bk) atomicMin(&best_idx_s, ti);
-    __syncthreads();
-    best_i = best_idx_s;
+    best_i = pick_candidate<kSmallG, kSmallBlock>(z, g32, wv, ng, 0, thr, pk) ? pk.idx : pk.best_idx;
   }
   PHASE_STAMP(kStampGumbel);
   if (tid == 0) {
@@ -4484,8 +4533,7 @@ __global__ __launch_bounds__(kChunkBlock) void chunk_kernel(KernelArgs ka) {
   __shared__ unsigned long long red_u[kW];
   __shared__ int red_i[kW];
   __shared__ uint32_t last_s;
-  __shared__ unsigned long long best_key_s;
-  __shared__ int best_idx_s;
+  __shared__ PickLds pk;
   const int tid = tidx();
   const int lane = tid & 63, wave = tid >> 6;
   const int ri = blockIdx.y;   // the record
@@ -4546,12 +4594,13 @@ __global__ __launch_bounds__(kChunkBlock) void chunk_kernel(KernelArgs ka) {
   const float mf = key_to_float((uint32_t)(mk >> 32));
   const int amax = (int)(0xFFFFFFFFu - (uint32_t)mk);
   PHASE_STAMP(kStampMax);
-  // Gumbel-max within the chunk: every finite value gets an fp32 score, and
-  // the values within kChunkMargin of the chunk's best fp32 score get the
-  // exact fp64 score z - ln E; the best of those (ties: the smaller index)
-  // through two LDS atomics
+  // Gumbel-max within the chunk: every finite value gets an fp32 score; the
+  // values within kChunkMargin of the chunk's best one hold its winner
+  // (pick_candidate: usually one value, else settled by fp64 scores)
   double best_g = -INFINITY;
   int best_i = 0x7FFFFFFF;
+  bool single = false;  // the chunk's winner is its one value near the best fp32 score (pk)
+  float win32 = -INFINITY;  // then its fp32 score
   const uint32_t cst = mf == INFINITY ? 2u : mf > -INFINITY ? 0u : 1u;  // +inf / no finite value
   if (gumbel && cst == 0u) {
     const uint32_t key0 = (uint32_t)P.seed, key1 = (uint32_t)(P.seed >> 32);
@@ -4581,51 +4630,43 @@ __global__ __launch_bounds__(kChunkBlock) void chunk_kernel(KernelArgs ka) {
     uint32_t gk = lane63_u32(wave_scanmax_u32(fkey(gmx)));
     if (lane == 0) red_i[wave] = (int)gk;
     if (tid == 0) {
-      best_key_s = 0ull;
-      best_idx_s = 0x7FFFFFFF;
+      pk.best_key = 0ull;
+      pk.best_idx = 0x7FFFFFFF;
+      pk.n = 0u;
     }
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kW; ++w) gk = max(gk, (uint32_t)red_i[w]);
     const float G32 = key_to_float(gk);
     const float thr = G32 - (kChunkMargin + fabsf(G32) * 0x1p-20f);
-    double tg = -INFINITY;
-    int ti = 0x7FFFFFFF;
-#pragma unroll
-    for (int u = 0; u < kChunkMaxU; ++u) {
-      if (u >= U) break;
-      const int i0 = c0 + 4 * (tid + kChunkBlock * u);
-#pragma unroll
-      for (int c = 0; c < 4; ++c)
-        if (g32[u][c] >= thr) {
-          const double ge = ((double)z[u][c] - log(exp1_f64(wv[u][c]))) + 0.0;  // (+0 for -0)
-          if (ge > tg || (ge == tg && i0 + c < ti)) {
-            tg = ge;
-            ti = i0 + c;
-          }
-        }
-    }
+    single = pick_candidate<kChunkMaxU, kChunkBlock>(z, g32, wv, U, c0, thr, pk);
+    win32 = G32;
     PHASE_STAMP(kStampGumbelBatched);
-    const unsigned long long tk = dkey(tg);
-    if (ti != 0x7FFFFFFF) atomicMax(&best_key_s, tk);
-    __syncthreads();
-    const unsigned long long bk = best_key_s;
-    if (ti != 0x7FFFFFFF && tk == bk) atomicMin(&best_idx_s, ti);
-    __syncthreads();
-    best_g = key_to_double(bk);
-    best_i = best_idx_s;
+    if (!single) {
+      best_g = key_to_double(pk.best_key);
+      best_i = pk.best_idx;
+    }
   }
   PHASE_STAMP(kStampGumbel);
-  // the chunk's result (Gumbel-max rows: best fp64 score, its index and the
-  // chunk's status; greedy rows: the max's order key), then its arrival: one
-  // atomic add on the row's word, whose count the last chunk to arrive resets
-  // to zero for the next launch (every launch runs to its end: no chunk
-  // waits for another)
+  // the chunk's result (Gumbel-max rows: its winner's z and word, or its
+  // exact fp64 score when several values were near its best, with the
+  // winner's index and the chunk's status; greedy rows: the max's order
+  // key), then its arrival: one atomic add on the row's word, whose count the
+  // last chunk to arrive resets to zero for the next launch (every launch
+  // runs to its end: no chunk waits for another)
   ChunkRec *recs = kp.chunk_recs + (int64_t)ri * kp.chunk_stride;
   if (tid == 0) {
     if (gumbel) {
-      atomic_st(&recs[ch].a, (unsigned long long)__double_as_longlong(best_g));
-      atomic_st(&recs[ch].b, ((unsigned long long)cst << 32) | (uint32_t)best_i);
+      // b: the winner's fp32 score << 32 | flags << 28 | its index (< 2^20)
+      if (single) {
+        atomic_st(&recs[ch].a, ((unsigned long long)__float_as_uint(pk.z) << 32) | pk.w);
+        atomic_st(&recs[ch].b, ((unsigned long long)__float_as_uint(cst == 0u ? win32 : -INFINITY) << 32) |
+                                   (cst << 28) | (uint32_t)pk.idx);
+      } else {
+        atomic_st(&recs[ch].a, (unsigned long long)__double_as_longlong(best_g));
+        atomic_st(&recs[ch].b, ((unsigned long long)__float_as_uint(cst == 0u ? (float)best_g : -INFINITY) << 32) |
+                                   ((cst | kChunkExact) << 28) | ((uint32_t)best_i & 0x0FFFFFFFu));
+      }
     } else {
       atomic_st(&recs[ch].a, mk);
     }
@@ -4652,20 +4693,45 @@ __global__ __launch_bounds__(kChunkBlock) void chunk_kernel(KernelArgs ka) {
   unsigned long long k = 0;  // greedy: the max's order key; Gumbel-max: the row's status as a key
   double g = -INFINITY;
   int gi = 0x7FFFFFFF;
+  if (gumbel) {
+    // each chunk's best score in fp32 (its fp32 score, or its exact score
+    // rounded): the chunks within kChunkMargin of the best hold the row's
+    // winner; one such chunk is the winner, several are settled by their
+    // exact fp64 scores
+    float a32[4];
 #pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    if (lane + 64 * t >= C) break;
-    if (gumbel) {
-      const double gj = f64_of(r[t].x, r[t].y);
-      const int ij = (int)r[t].z;
-      if (gj > g || (gj == g && ij < gi)) {
-        g = gj;
-        gi = ij;
-      }
-      const unsigned long long sk = (unsigned long long)fkey(r[t].w == 2u ? INFINITY : r[t].w == 1u ? -INFINITY : 0.0f)
-                                    << 32;
+    for (int t = 0; t < 4; ++t) {
+      a32[t] = -INFINITY;
+      if (lane + 64 * t >= C) continue;
+      const uint32_t st = (r[t].z >> 28) & 3u;
+      const unsigned long long sk = (unsigned long long)fkey(st == 2u ? INFINITY : st == 1u ? -INFINITY : 0.0f) << 32;
       k = sk > k ? sk : k;
-    } else {
+      if (st == 0u) a32[t] = __uint_as_float(r[t].w);
+    }
+    const float G = key_to_float(lane63_u32(wave_scanmax_u32(fkey(fmaxf(fmaxf(a32[0], a32[1]), fmaxf(a32[2], a32[3]))))));
+    if (G > -INFINITY) {
+      const float thr = G - (kChunkMargin + fabsf(G) * 0x1p-20f);
+      uint32_t nc = 0;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) nc += (uint32_t)__popcll(__ballot(a32[t] >= thr));
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        if (a32[t] >= thr) {
+          const int ij = (int)(r[t].z & 0x0FFFFFFFu);
+          double gj = 0.0;  // one candidate: any finite score
+          if (nc > 1u)
+            gj = ((r[t].z >> 28) & kChunkExact) ? f64_of(r[t].x, r[t].y)
+                                                : ((double)__uint_as_float(r[t].y) - log(exp1_f64(r[t].x))) + 0.0;
+          if (gj > g || (gj == g && ij < gi)) {
+            g = gj;
+            gi = ij;
+          }
+        }
+    }
+  } else {
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      if (lane + 64 * t >= C) break;
       const unsigned long long kj = u64_of(r[t].x, r[t].y);
       k = kj > k ? kj : k;
     }
