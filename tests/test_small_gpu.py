@@ -53,6 +53,17 @@ def test_random_plain_rows(sampler_small, seed, n, V, dtype):
     check(plain(seed, n, V, dtype), sampler_small)
 
 
+def test_many_rows_through_the_record_ring():
+    # more rows than the kernel arguments carry (72): the records go through
+    # the pinned ring to device memory
+    import decode_step_token_sampler_amd as dsts
+    s = dsts.Sampler(300, 4096, max_history_per_row=0)
+    try:
+        check(plain(158, 300, 777, "bf16"), s)
+    finally:
+        s.close()
+
+
 @pytest.mark.parametrize("probs,logprobs", [(False, False), (True, False), (False, True)])
 def test_output_subsets(sampler_small, probs, logprobs):
     check(plain(160, 12, 3000, "f32", probs, logprobs), sampler_small)
