@@ -3610,16 +3610,39 @@ __global__ __launch_bounds__(kBlock, 2) void stream_kernel(KernelArgs ka) {
       float lmax = -INFINITY;
       int lgrp = -1;
       float lz[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
-      group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
-        const float gm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        const bool take = gm > lmax || (gm == lmax && gm > -INFINITY && g < lgrp);
-        lmax = take ? gm : lmax;
-        lgrp = take ? g : lgrp;
+      if (gumbel && !top1) {
+        // Gumbel-max rows need the max z and any index holding it (its draw
+        // seeds the bound), not the first: z is monotone in the logit, so
+        // the pass takes the max of the raw logits (NaN never wins) and
+        // divides only each thread's largest
+        stream_pass(std::false_type{}, [&](const int (&gi)[kNG], const u32x4 (&ch)[kSL], const uint32_t (&mk)[kNG], bool)
+                                           __attribute__((always_inline)) {
 #pragma unroll
-        for (int c = 0; c < 4; ++c) lz[c] = take ? z[c] : lz[c];
-      });
+          for (int t = 0; t < kNG; ++t) {
+            float x[4];
+#pragma unroll
+            for (int c = 0; c < 4; ++c) x[c] = ((mk[t] >> c) & 1u) ? -INFINITY : rawv(ch, t, c);
+            const float gm = fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3]));
+            const bool take = gm > lmax || (gm == lmax && gm > -INFINITY && gi[t] < lgrp);
+            lmax = take ? gm : lmax;
+            lgrp = take ? gi[t] : lgrp;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) lz[c] = take ? x[c] : lz[c];
+          }
+        });
+      } else {
+        group_pass([&](int g, const float z[4]) __attribute__((always_inline)) {
+          const float gm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+          const bool take = gm > lmax || (gm == lmax && gm > -INFINITY && g < lgrp);
+          lmax = take ? gm : lmax;
+          lgrp = take ? g : lgrp;
+#pragma unroll
+          for (int c = 0; c < 4; ++c) lz[c] = take ? z[c] : lz[c];
+        });
+      }
       int lidx = 0x7FFFFFFF;
       if (lgrp >= 0) lidx = 4 * lgrp + (lz[0] == lmax ? 0 : lz[1] == lmax ? 1 : lz[2] == lmax ? 2 : 3);
+      if (gumbel && !top1) lmax = zval(lmax, false);  // (the raw maximum's z; -inf stays -inf)
       unsigned long long lkey = ((unsigned long long)fkey(lmax) << 32) | (0xFFFFFFFFu - (uint32_t)lidx);
       patches([&](int i, float zz) {
         const unsigned long long k2 = ((unsigned long long)fkey(zz) << 32) | (0xFFFFFFFFu - (uint32_t)i);
